@@ -1,0 +1,437 @@
+"""e-means CPU oracle (reference semantics for the GPU library).
+
+TEST INFRASTRUCTURE ONLY. This package is the plain, slow checker that the GPU
+path is compared against. It shares no code with the library: only the tests,
+the package's smoke check and the benchmark's CPU-baseline leg may import it,
+and the library never does.
+
+What it computes, and where each step comes from (pages: the faiss
+``contrib/e_means`` README, "e-means: outperforming k-means in one-tenth the
+epochs"; the jecision.com blog "k-means Reads Your Data 25 Times. Two Would
+Do."):
+
+* recipe            README "Scaling laws" equations (1)-(3) and their
+                    constraints; "Parameters" (batch_law, note on low
+                    dimension), "Manual overrides", "Settings" table.
+* exact assignment  blog, section on Lloyd's algorithm: a(i) = argmin_j
+                    ||x_i - c_j||^2 (``emeans_ref.c``, fp64 brute force).
+* EMA update        README "How the centroid updates work" and blog "four
+                    things e-means changes", first item:
+                    N_j <- (1-a) N_j + a n_j,  S_j <- (1-a) S_j + a s_j,
+                    c_j = S_j / N_j.
+* cosine schedule   blog, second item; README "How the centroid updates
+                    work": the step decays along a cosine to a tenth of its
+                    starting value.
+* revival           blog, third item (every five batches, clusters below 10%
+                    of the mean count are refilled by splitting a big
+                    cluster); README "Settings" (unused_threshold).
+* batch order       README "Data too big for memory": fresh random order every
+                    pass, batches of exactly B except the last of each pass,
+                    every vector once per pass.
+* finalisation      README "How the centroid updates work", last item: each
+                    centroid becomes the exact mean of the points the last pass
+                    assigned to it; README "Quick start": labels come from the
+                    last pass.
+* precision         README "Data precision": centroids and running sums are
+                    stored in fp32; only the nearest-centroid search uses the
+                    smaller format for bf16 data.
+
+Readings where the pages are silent (each listed in the design notes):
+power-of-two rounding in log2 space; cap = largest power of two <= n/2;
+N = S = 0 at start and c_j kept while N_j = 0; the cosine runs over all update
+steps, endpoints included; revival mechanics (global step counter, strict <,
+donors drawn one dead cluster at a time in index order with probability
+proportional to N among the clusters that were alive at the check, donor
+halves, +/-2^-10 hashed-sign perturbation); finalisation over the last pass,
+keeping the EMA centroid where that pass gave no point; labels of rows the last
+pass did not visit are -1; random streams from Philox4x64-10.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+import subprocess
+from dataclasses import dataclass, field
+from typing import Callable, Optional
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "emeans_ref.c")
+_LIB = os.path.join(_HERE, "libemeans_ref.so")
+
+STREAM_INIT = 1
+STREAM_PERM = 2
+STREAM_REVIVE = 3
+STREAM_SIGN = 4
+
+SPLIT_EPS = 2.0 ** -10       # relative perturbation of a split (reading)
+REVIVE_EVERY = 5             # blog: checked every five batches
+
+
+def build(force: bool = False) -> str:
+    """Compile the C half of the oracle with gcc (fp64, OpenMP)."""
+    if force or not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
+        subprocess.check_call(["gcc", "-O2", "-fopenmp", "-fno-fast-math", "-shared", "-fPIC",
+                               "-o", _LIB, _SRC])
+    return _LIB
+
+
+_lib = None
+
+
+def lib():
+    global _lib
+    if _lib is None:
+        L = ctypes.CDLL(build())
+        u64, i64, i32, vp = ctypes.c_uint64, ctypes.c_int64, ctypes.c_int32, ctypes.c_void_p
+        L.ref_philox4x64.argtypes = [vp, vp, vp]
+        L.ref_perm_at.argtypes = [u64, u64, u64, u64, u64]
+        L.ref_perm_at.restype = i64
+        L.ref_perm_range.argtypes = [u64, u64, u64, u64, u64, u64, vp]
+        L.ref_assign.argtypes = [vp, ctypes.c_int, i64, vp, i32, vp, i32, vp, vp, vp, ctypes.c_int]
+        L.ref_dist_to.argtypes = [vp, ctypes.c_int, i64, vp, i32, vp, vp, vp]
+        L.ref_group.argtypes = [vp, ctypes.c_int, i64, vp, vp, i32, i32, vp, vp]
+        _lib = L
+    return _lib
+
+
+def _p(a: Optional[np.ndarray]):
+    return None if a is None else a.ctypes.data_as(ctypes.c_void_p)
+
+
+# ----------------------------------------------------------------------------
+# random streams
+# ----------------------------------------------------------------------------
+
+def philox4x64(ctr, key) -> np.ndarray:
+    c = np.ascontiguousarray(np.array(ctr, dtype=np.uint64))
+    k = np.ascontiguousarray(np.array(key, dtype=np.uint64))
+    o = np.zeros(4, dtype=np.uint64)
+    lib().ref_philox4x64(_p(c), _p(k), _p(o))
+    return o
+
+
+def perm_range(n: int, seed: int, stream: int, pass_: int, start: int, count: int) -> np.ndarray:
+    out = np.empty(count, dtype=np.int64)
+    if count:
+        lib().ref_perm_range(n, seed, stream, pass_, start, count, _p(out))
+    return out
+
+
+def uniform01(seed: int, t: int, j: int) -> float:
+    """Revival draw for dead cluster j at step t: 53 random bits in [0, 1)."""
+    w = philox4x64((j, t, 0, STREAM_REVIVE), (seed, 0))
+    return float(int(w[0]) >> 11) * 2.0 ** -53
+
+
+def split_signs(seed: int, t: int, j: int, d: int) -> np.ndarray:
+    """+1/-1 per coordinate for the split of step t that refills cluster j."""
+    s = np.empty(d, dtype=np.float32)
+    for blk in range(0, d, 256):
+        w = philox4x64((j, t, blk >> 8, STREAM_SIGN), (seed, 0))
+        for u in range(blk, min(d, blk + 256)):
+            bit = (int(w[(u >> 6) & 3]) >> (u & 63)) & 1
+            s[u] = -1.0 if bit else 1.0
+    return s
+
+
+# ----------------------------------------------------------------------------
+# recipe: scaling laws (README "Scaling laws")
+# ----------------------------------------------------------------------------
+
+LAW_THROUGHPUT = 1
+LAW_QUALITY = 2
+
+
+def recipe(n: int, d: int, k: int, T: float, batch_law: int = 0, batch_size: int = 0,
+           alpha0: float = 0.0, unused_threshold: float = -1.0) -> dict:
+    law = batch_law if batch_law in (LAW_THROUGHPUT, LAW_QUALITY) else (
+        LAW_QUALITY if d <= 16 else LAW_THROUGHPUT)
+    if batch_size and batch_size > 0:
+        B = min(int(batch_size), n)
+    else:
+        c = 0.00439175 if law == LAW_QUALITY else 0.035134                   # eq. (2) / (1)
+        braw = c * math.pow(k, 0.134749) * math.pow(n, 0.876473) * math.pow(T, 0.813344)
+        B = 2 ** int(math.floor(math.log2(braw) + 0.5))                        # nearest power of two
+        cap = 2 ** int(math.floor(math.log2(n / 2.0))) if n >= 2 else 1        # "capped at ~n/2"
+        B = max(1, min(B, cap))
+    if alpha0 and alpha0 > 0:
+        a0 = float(alpha0)
+    else:
+        a0 = (0.8244 * math.pow(k, -0.4617) * math.pow(B, 0.9003) * math.pow(n, -0.4498)
+              * math.pow(T, -0.1057))                                          # eq. (3)
+        a0 = min(max(a0, 1e-4), 1.0)
+    full = int(math.floor(T))
+    rows = [n] * full
+    frac_rows = int(math.floor((T - full) * n))
+    if frac_rows > 0:
+        rows.append(frac_rows)
+    steps = [(r + B - 1) // B for r in rows]
+    if unused_threshold is None or unused_threshold < 0:
+        thr = 0.0 if d <= 2 else 0.1
+    else:
+        thr = float(unused_threshold)
+    return dict(law=law, batch_size=B, alpha0=a0, epoch_rows=rows, steps_per_pass=steps,
+                total_steps=sum(steps), unused_threshold=thr)
+
+
+def alphas(alpha0: float, S: int) -> np.ndarray:
+    """Cosine decay from alpha0 to alpha0/10 over the S update steps (fp32)."""
+    out = np.empty(S, dtype=np.float32)
+    for t in range(S):
+        if S == 1:
+            a = alpha0
+        else:
+            a = alpha0 * (0.1 + 0.45 * (1.0 + math.cos(math.pi * t / (S - 1))))
+        out[t] = np.float32(a)
+    return out
+
+
+# ----------------------------------------------------------------------------
+# assignment and grouping
+# ----------------------------------------------------------------------------
+
+def _dtype_code(X: np.ndarray) -> int:
+    if X.dtype == np.float32:
+        return 0
+    if X.dtype == np.uint16:      # bf16 bit patterns
+        return 1
+    raise TypeError(f"unsupported data type {X.dtype}")
+
+
+def to_f32(X: np.ndarray) -> np.ndarray:
+    if X.dtype == np.uint16:
+        return (X.astype(np.uint32) << 16).view(np.float32)
+    return X
+
+
+def bf16_round(C: np.ndarray) -> np.ndarray:
+    """fp32 -> nearest bf16 (ties to even), returned as fp32 values."""
+    b = np.ascontiguousarray(C, dtype=np.float32).view(np.uint32).astype(np.uint64)
+    b = ((b + 0x7FFF + ((b >> 16) & 1)) >> 16) << 16
+    return b.astype(np.uint32).view(np.float32)
+
+
+def search_centroids(C: np.ndarray, X: np.ndarray) -> np.ndarray:
+    """Centroids in the search format: bf16 for bf16 data, fp32 otherwise."""
+    return bf16_round(C) if X.dtype == np.uint16 else np.ascontiguousarray(C, dtype=np.float32)
+
+
+def assign(X: np.ndarray, C: np.ndarray, rows: Optional[np.ndarray] = None, nthreads: int = 0):
+    """Nearest centroid of each (selected) row: labels, best and runner-up distance (fp64).
+
+    C is used as given (the caller converts it to the search format)."""
+    X = np.ascontiguousarray(X)
+    C = np.ascontiguousarray(C, dtype=np.float32)
+    d = X.shape[1]
+    k = C.shape[0]
+    m = X.shape[0] if rows is None else len(rows)
+    r = None if rows is None else np.ascontiguousarray(rows, dtype=np.int64)
+    lab = np.empty(m, dtype=np.int32)
+    d1 = np.empty(m, dtype=np.float64)
+    d2 = np.empty(m, dtype=np.float64)
+    if m:
+        lib().ref_assign(_p(X), _dtype_code(X), m, _p(r), d, _p(C), k, _p(lab), _p(d1), _p(d2),
+                         int(nthreads))
+    return lab, d1, d2
+
+
+def dist_to(X: np.ndarray, C: np.ndarray, labels: np.ndarray, rows: Optional[np.ndarray] = None):
+    X = np.ascontiguousarray(X)
+    C = np.ascontiguousarray(C, dtype=np.float32)
+    labels = np.ascontiguousarray(labels, dtype=np.int32)
+    m = len(labels)
+    r = None if rows is None else np.ascontiguousarray(rows, dtype=np.int64)
+    out = np.empty(m, dtype=np.float64)
+    if m:
+        lib().ref_dist_to(_p(X), _dtype_code(X), m, _p(r), X.shape[1], _p(C), _p(labels), _p(out))
+    return out
+
+
+def group(X: np.ndarray, rows: Optional[np.ndarray], labels: np.ndarray, k: int):
+    """Per-cluster count n_j (int64) and sum s_j (fp64) of the selected rows."""
+    X = np.ascontiguousarray(X)
+    d = X.shape[1]
+    labels = np.ascontiguousarray(labels, dtype=np.int32)
+    m = len(labels)
+    r = None if rows is None else np.ascontiguousarray(rows, dtype=np.int64)
+    sums = np.zeros((k, d), dtype=np.float64)
+    counts = np.zeros(k, dtype=np.int64)
+    lib().ref_group(_p(X), _dtype_code(X), m, _p(r), _p(labels), d, k, _p(sums), _p(counts))
+    return counts, sums
+
+
+def mse(X: np.ndarray, C: np.ndarray, nthreads: int = 0) -> float:
+    """Mean over rows of the squared distance to the nearest centroid (not / d)."""
+    _, d1, _ = assign(X, search_centroids(C, X), nthreads=nthreads)
+    return float(d1.mean())
+
+
+# ----------------------------------------------------------------------------
+# training
+# ----------------------------------------------------------------------------
+
+@dataclass
+class TrainResult:
+    centroids: np.ndarray           # k x d fp32 (finalised unless finalize=False)
+    ema_centroids: np.ndarray       # k x d fp32 before finalisation
+    labels: np.ndarray              # n int32, last-pass label, -1 if not visited
+    N: np.ndarray                   # k fp32 running counts at the end
+    S: np.ndarray                   # k x d fp32 running sums at the end
+    recipe: dict
+    alphas: np.ndarray
+    obj: list = field(default_factory=list)        # per pass: mean distance while moving
+    split_log: list = field(default_factory=list)  # (t, dead j, donor i)
+    dead_at_end: int = 0
+    label_checks: list = field(default_factory=list)  # per step, lockstep validation results
+
+
+def init_rows(n: int, k: int, seed: int) -> np.ndarray:
+    """k distinct starting rows: the first k entries of the init permutation."""
+    return perm_range(n, seed, STREAM_INIT, 0, 0, k)
+
+
+def _revive(t: int, seed: int, thr: float, N: np.ndarray, S: np.ndarray, C: np.ndarray,
+            log: list) -> None:
+    k, d = S.shape
+    total = float(np.sum(N.astype(np.float64)))
+    th = thr * (total / k)
+    dead = np.nonzero(N.astype(np.float64) < th)[0]
+    if len(dead) == 0:
+        return
+    live = np.ones(k, dtype=bool)
+    live[dead] = False
+    for j in dead:
+        u = uniform01(seed, t, int(j))
+        w = np.where(live, N.astype(np.float64), 0.0)
+        cum = np.cumsum(w)
+        target = u * cum[-1]
+        i = int(np.searchsorted(cum, target, side="right"))
+        if i >= k or not live[i]:
+            i = int(np.nonzero(live)[0][-1])
+        sig = split_signs(seed, t, int(j), d)
+        half = S[i] * np.float32(0.5)
+        N[i] = N[i] * np.float32(0.5)
+        N[j] = N[i]
+        S[j] = half * (np.float32(1.0) + np.float32(SPLIT_EPS) * sig)
+        S[i] = half * (np.float32(1.0) - np.float32(SPLIT_EPS) * sig)
+        C[i] = (S[i].astype(np.float64) / float(N[i])).astype(np.float32)
+        C[j] = (S[j].astype(np.float64) / float(N[j])).astype(np.float32)
+        log.append((t, int(j), i))
+
+
+def train(X: np.ndarray, k: int, T: float, seed: int = 1234, *, batch_law: int = 0,
+          batch_size: int = 0, alpha0: float = 0.0, unused_threshold: float = -1.0,
+          finalize: bool = True,
+          labels_for_step: Optional[Callable[[int, np.ndarray], np.ndarray]] = None,
+          check_slots: Optional[Callable[[int, int], Optional[np.ndarray]]] = None,
+          check_hook: Optional[Callable[[dict], None]] = None,
+          nthreads: int = 0) -> TrainResult:
+    """e-means on X (n x d, fp32 or bf16 bits), step by step.
+
+    labels_for_step(t, rows) may supply the labels of step t from elsewhere
+    (lockstep replay). The oracle then checks them on the slots that
+    check_slots(t, B_t) names (all slots when it returns None) against its
+    own fp64 assignment, hands the check to check_hook (or keeps it in
+    label_checks), and adopts them.
+    """
+    n, d = X.shape
+    rc = recipe(n, d, k, T, batch_law, batch_size, alpha0, unused_threshold)
+    B = rc["batch_size"]
+    S_tot = rc["total_steps"]
+    al = alphas(rc["alpha0"], S_tot)
+    thr = rc["unused_threshold"]
+    Xf = X  # searched as stored
+
+    C = np.ascontiguousarray(to_f32(X[init_rows(n, k, seed)]), dtype=np.float32)
+    N = np.zeros(k, dtype=np.float32)
+    S = np.zeros((k, d), dtype=np.float32)
+    LN = np.zeros(k, dtype=np.int64)
+    LS = np.zeros((k, d), dtype=np.float64)
+    labels_out = np.full(n, -1, dtype=np.int32)
+    res = TrainResult(centroids=C, ema_centroids=C, labels=labels_out, N=N, S=S, recipe=rc,
+                      alphas=al)
+
+    t = 0
+    n_pass = len(rc["epoch_rows"])
+    for e, rows_e in enumerate(rc["epoch_rows"]):
+        last = e == n_pass - 1
+        obj = 0.0
+        for s in range(rc["steps_per_pass"][e]):
+            Bt = min(B, rows_e - s * B)
+            rows = perm_range(n, seed, STREAM_PERM, e, s * B, Bt)
+            Cs = search_centroids(C, X)
+            if labels_for_step is None:
+                lab, d1, _ = assign(Xf, Cs, rows, nthreads)
+                dist = d1
+            else:
+                lab = np.ascontiguousarray(labels_for_step(t, rows), dtype=np.int32)
+                slots = None if check_slots is None else check_slots(t, Bt)
+                sel = rows if slots is None else rows[slots]
+                olab, od1, od2 = assign(Xf, Cs, sel, nthreads)
+                glab = lab if slots is None else lab[slots]
+                gd = dist_to(Xf, Cs, glab, sel)
+                chk = dict(t=t, slots=slots, oracle=olab, d1=od1, d2=od2, given=glab,
+                           given_dist=gd, rows=sel, C=Cs)
+                if check_hook is not None:
+                    check_hook(chk)
+                else:
+                    res.label_checks.append(chk)
+                dist = dist_to(Xf, Cs, lab, rows)
+            obj += float(np.sum(dist))
+            counts, sums = group(Xf, rows, lab, k)
+            a = al[t]
+            b = np.float32(1.0) - a
+            # running count in fp32, fixed operation order: fl(fl(b*N) + fl(a*n))
+            N[:] = (b * N) + (a * counts.astype(np.float32))
+            # running sum: fp64 arithmetic, fp32 storage
+            S[:] = (np.float64(b) * S.astype(np.float64) + np.float64(a) * sums).astype(np.float32)
+            pos = N > 0
+            C[pos] = (S[pos].astype(np.float64) / N[pos].astype(np.float64)[:, None]).astype(np.float32)
+            if last:
+                LN += counts
+                LS += sums
+                labels_out[rows] = lab
+            if thr > 0 and (t + 1) % REVIVE_EVERY == 0:
+                _revive(t, seed, thr, N, S, C, res.split_log)
+            t += 1
+        res.obj.append(obj / rows_e)
+
+    res.ema_centroids = C.copy()
+    if finalize:
+        pos = LN > 0
+        C[pos] = (LS[pos] / LN[pos].astype(np.float64)[:, None]).astype(np.float32)
+    res.centroids = C
+    if thr > 0:
+        th = thr * float(np.sum(N.astype(np.float64))) / k
+        res.dead_at_end = int(np.sum(N.astype(np.float64) < th))
+    return res
+
+
+def lloyd(X: np.ndarray, k: int, iters: int, seed: int = 1234, nthreads: int = 0):
+    """Plain Lloyd from the same k starting rows: assign all rows, move each
+    centroid to the exact mean of its rows (a centroid with no row stays).
+    Returns the centroids after `iters` updates and the MSE seen at each assign."""
+    n, d = X.shape
+    C = np.ascontiguousarray(to_f32(X[init_rows(n, k, seed)]), dtype=np.float32)
+    hist = []
+    for _ in range(iters):
+        lab, d1, _ = assign(X, search_centroids(C, X), nthreads=nthreads)
+        hist.append(float(d1.mean()))
+        counts, sums = group(X, None, lab, k)
+        pos = counts > 0
+        C[pos] = (sums[pos] / counts[pos].astype(np.float64)[:, None]).astype(np.float32)
+    return C, hist
+
+
+def rel_gap(X: np.ndarray, C: np.ndarray, rows: Optional[np.ndarray], labels: np.ndarray,
+            d1: np.ndarray, d2: np.ndarray) -> np.ndarray:
+    """(runner-up - best) / (||x||^2 + ||c_best||^2): how decided each label is,
+    relative to the size of the quantities the distance is computed from."""
+    Xf = to_f32(X if rows is None else X[rows]).astype(np.float64)
+    xn = np.einsum("ij,ij->i", Xf, Xf)
+    Cb = C[labels].astype(np.float64)
+    cn = np.einsum("ij,ij->i", Cb, Cb)
+    return (d2 - d1) / np.maximum(xn + cn, 1e-300)

@@ -1,0 +1,202 @@
+/*
+ * e-means CPU oracle: the direct-definition loops.
+ *
+ * TEST INFRASTRUCTURE ONLY. This file is the slow, plain checker that the GPU
+ * library is compared against. Only the tests, the package smoke check and the
+ * benchmark's CPU-baseline leg may load it; the library never does.
+ *
+ * Everything here is written from the definitions, in fp64, with no blocking,
+ * tiling or algebraic rewriting:
+ *   - squared Euclidean distance  sum_t (x_t - c_t)^2  and its argmin
+ *     (k-means objective, blog "k-means Reads Your Data 25 Times", section on
+ *     Lloyd's 1957 algorithm, MSE formula);
+ *   - per-cluster count n_j and sum s_j of a batch (faiss e_means README,
+ *     "How the centroid updates work");
+ *   - Philox4x64-10, the counter-based generator of Salmon, Moraes, Dror and
+ *     Shaw, "Parallel Random Numbers: As Easy as 1, 2, 3" (SC'11);
+ *   - a keyed bijection on [0, n): a 4-round balanced Feistel network
+ *     (Luby-Rackoff) whose round function is Philox, restricted to [0, n) by
+ *     cycle-walking (Black and Rogaway, "Ciphers with Arbitrary Finite
+ *     Domains", 2002). It stands for the "fresh random order every pass" of
+ *     the README's batch loop ("Data too big for memory").
+ *
+ * Build: gcc -O2 -fopenmp -shared -fPIC -o libemeans_ref.so emeans_ref.c
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+/* ------------------------------------------------------------------------ */
+/* Philox4x64-10 (Salmon et al. 2011): multipliers, Weyl key increments and */
+/* the round S-box as published.                                            */
+/* ------------------------------------------------------------------------ */
+static const uint64_t PH_M0 = 0xD2E7470EE14C6C93ULL;
+static const uint64_t PH_M1 = 0xCA5A826395121157ULL;
+static const uint64_t PH_W0 = 0x9E3779B97F4A7C15ULL;
+static const uint64_t PH_W1 = 0xBB67AE8584CAA73BULL;
+
+void ref_philox4x64(const uint64_t ctr_in[4], const uint64_t key_in[2], uint64_t out[4]) {
+  uint64_t c0 = ctr_in[0], c1 = ctr_in[1], c2 = ctr_in[2], c3 = ctr_in[3];
+  uint64_t k0 = key_in[0], k1 = key_in[1];
+  for (int round = 0; round < 10; ++round) {
+    if (round > 0) {
+      k0 += PH_W0;
+      k1 += PH_W1;
+    }
+    unsigned __int128 p0 = (unsigned __int128)PH_M0 * c0;
+    unsigned __int128 p1 = (unsigned __int128)PH_M1 * c2;
+    uint64_t hi0 = (uint64_t)(p0 >> 64), lo0 = (uint64_t)p0;
+    uint64_t hi1 = (uint64_t)(p1 >> 64), lo1 = (uint64_t)p1;
+    uint64_t n0 = hi1 ^ c1 ^ k0;
+    uint64_t n1 = lo1;
+    uint64_t n2 = hi0 ^ c3 ^ k1;
+    uint64_t n3 = lo0;
+    c0 = n0; c1 = n1; c2 = n2; c3 = n3;
+  }
+  out[0] = c0; out[1] = c1; out[2] = c2; out[3] = c3;
+}
+
+/* ------------------------------------------------------------------------ */
+/* Keyed permutation of [0, n).                                              */
+/*   half width h = max(1, ceil(bits(n-1) / 2)), domain 2^(2h) >= n          */
+/*   round r (0..3): F = Philox(ctr=(R, r, pass, stream), key=(seed, 0))[0]  */
+/*                   (L, R) <- (R, L xor (F mod 2^h))                        */
+/*   cycle-walk: re-encrypt while the value is >= n.                         */
+/* ------------------------------------------------------------------------ */
+static int ref_half_bits(uint64_t n) {
+  int m = 0;
+  while (m < 64 && (n - 1) >> m) ++m; /* bits needed for n-1 (0 when n == 1) */
+  int h = (m + 1) / 2;
+  return h < 1 ? 1 : h;
+}
+
+static uint64_t ref_feistel(uint64_t v, int h, uint64_t seed, uint64_t stream, uint64_t pass) {
+  const uint64_t mask = (h >= 64) ? ~0ULL : ((1ULL << h) - 1);
+  uint64_t L = v >> h, R = v & mask;
+  for (uint64_t r = 0; r < 4; ++r) {
+    uint64_t ctr[4] = {R, r, pass, stream};
+    uint64_t key[2] = {seed, 0};
+    uint64_t o[4];
+    ref_philox4x64(ctr, key, o);
+    uint64_t nl = R;
+    uint64_t nr = L ^ (o[0] & mask);
+    L = nl;
+    R = nr;
+  }
+  return (L << h) | R;
+}
+
+int64_t ref_perm_at(uint64_t n, uint64_t seed, uint64_t stream, uint64_t pass, uint64_t i) {
+  int h = ref_half_bits(n);
+  uint64_t v = ref_feistel(i, h, seed, stream, pass);
+  while (v >= n) v = ref_feistel(v, h, seed, stream, pass);
+  return (int64_t)v;
+}
+
+void ref_perm_range(uint64_t n, uint64_t seed, uint64_t stream, uint64_t pass, uint64_t start,
+                    uint64_t count, int64_t* out) {
+#pragma omp parallel for schedule(static)
+  for (int64_t i = 0; i < (int64_t)count; ++i) out[i] = ref_perm_at(n, seed, stream, pass, start + (uint64_t)i);
+}
+
+/* ------------------------------------------------------------------------ */
+/* Element access: dtype 0 = fp32, 1 = bf16 (stored as the high 16 bits of  */
+/* an fp32).                                                                 */
+/* ------------------------------------------------------------------------ */
+static inline double ref_elem(const void* X, int dtype, int64_t row, int32_t d, int32_t t) {
+  if (dtype == 0) return (double)((const float*)X)[row * (int64_t)d + t];
+  uint32_t bits = (uint32_t)((const uint16_t*)X)[row * (int64_t)d + t] << 16;
+  float f;
+  memcpy(&f, &bits, 4);
+  return (double)f;
+}
+
+/* Nearest centroid by brute force: for each selected row, the squared       */
+/* distance to every centroid, written out as the sum over coordinates; ties */
+/* go to the lowest index. Also returns the runner-up distance (used by the  */
+/* tests to tell decided labels from near-ties).                             */
+void ref_assign(const void* X, int dtype, int64_t nrows, const int64_t* rows, int32_t d,
+                const float* C, int32_t k, int32_t* labels, double* d1, double* d2,
+                int nthreads) {
+#ifdef _OPENMP
+  if (nthreads > 0) omp_set_num_threads(nthreads);
+#endif
+#pragma omp parallel
+  {
+    double* x = (double*)malloc(sizeof(double) * (size_t)d);
+#pragma omp for schedule(dynamic, 16)
+    for (int64_t i = 0; i < nrows; ++i) {
+      int64_t row = rows ? rows[i] : i;
+      for (int32_t t = 0; t < d; ++t) x[t] = ref_elem(X, dtype, row, d, t);
+      double best = INFINITY, second = INFINITY;
+      int32_t arg = -1;
+      for (int32_t j = 0; j < k; ++j) {
+        const float* c = C + (int64_t)j * d;
+        double s = 0.0;
+        for (int32_t t = 0; t < d; ++t) {
+          double diff = x[t] - (double)c[t];
+          s += diff * diff;
+        }
+        if (s < best) {
+          second = best;
+          best = s;
+          arg = j;
+        } else if (s < second) {
+          second = s;
+        }
+      }
+      labels[i] = arg;
+      d1[i] = best;
+      if (d2) d2[i] = second;
+    }
+    free(x);
+  }
+}
+
+/* Squared distance of each selected row to one given centroid each.        */
+void ref_dist_to(const void* X, int dtype, int64_t nrows, const int64_t* rows, int32_t d,
+                 const float* C, const int32_t* labels, double* out) {
+#pragma omp parallel for schedule(static)
+  for (int64_t i = 0; i < nrows; ++i) {
+    int64_t row = rows ? rows[i] : i;
+    const float* c = C + (int64_t)labels[i] * d;
+    double s = 0.0;
+    for (int32_t t = 0; t < d; ++t) {
+      double diff = ref_elem(X, dtype, row, d, t) - (double)c[t];
+      s += diff * diff;
+    }
+    out[i] = s;
+  }
+}
+
+/* Per-cluster count and sum of the selected rows, in fp64. Each cluster's  */
+/* sum is taken in row order (the order of a sequential loop over the rows);  */
+/* rows are bucketed by label first only so clusters can run in parallel.     */
+void ref_group(const void* X, int dtype, int64_t nrows, const int64_t* rows,
+               const int32_t* labels, int32_t d, int32_t k, double* sums, int64_t* counts) {
+  memset(counts, 0, sizeof(int64_t) * (size_t)k);
+  for (int64_t i = 0; i < nrows; ++i) counts[labels[i]] += 1;
+  int64_t* start = (int64_t*)malloc(sizeof(int64_t) * ((size_t)k + 1));
+  int64_t* cursor = (int64_t*)malloc(sizeof(int64_t) * (size_t)k);
+  int64_t* order = (int64_t*)malloc(sizeof(int64_t) * (size_t)(nrows > 0 ? nrows : 1));
+  start[0] = 0;
+  for (int32_t j = 0; j < k; ++j) start[j + 1] = start[j] + counts[j];
+  for (int32_t j = 0; j < k; ++j) cursor[j] = start[j];
+  for (int64_t i = 0; i < nrows; ++i) order[cursor[labels[i]]++] = i;
+#pragma omp parallel for schedule(dynamic, 16)
+  for (int32_t j = 0; j < k; ++j) {
+    double* s = sums + (int64_t)j * d;
+    for (int32_t t = 0; t < d; ++t) s[t] = 0.0;
+    for (int64_t p = start[j]; p < start[j + 1]; ++p) {
+      int64_t row = rows ? rows[order[p]] : order[p];
+      for (int32_t t = 0; t < d; ++t) s[t] += ref_elem(X, dtype, row, d, t);
+    }
+  }
+  free(order);
+  free(cursor);
+  free(start);
+}
