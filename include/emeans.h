@@ -1,0 +1,160 @@
+/*
+ * emeans.h -- C ABI of the MI355X e-means library (libemeans.so).
+ *
+ * e-means is mini-batch k-means whose centroid statistics are exponential
+ * moving averages (faiss contrib/e_means README, "How the centroid updates
+ * work"): for each batch, every vector goes to its exact nearest centroid,
+ * then for every cluster j
+ *     N_j <- (1 - alpha) N_j + alpha n_j,   S_j <- (1 - alpha) S_j + alpha s_j,
+ *     c_j  = S_j / N_j,
+ * where n_j, s_j are the count and sum of the batch's vectors assigned to j.
+ * The batch size and the starting step alpha0 come from the README's scaling
+ * laws ("Scaling laws", equations (1)-(3)); alpha decays along a cosine to
+ * alpha0/10; clusters whose running count falls under a fraction of the mean
+ * are revived every 5 batches by splitting a cluster drawn in proportion to
+ * its size; at the end each centroid becomes the exact mean of the vectors
+ * the last pass assigned to it (README "How the centroid updates work";
+ * blog "k-means Reads Your Data 25 Times. Two Would Do.", section on the four
+ * things e-means changes).
+ *
+ * Conventions for every entry point:
+ *   - X, centroids, labels and dists are DEVICE pointers (HIP device memory on
+ *     the current device), row-major and contiguous, owned by the caller. The
+ *     library never copies data between host and device for the caller.
+ *   - X is n x d, either fp32 or bf16 (opts->dtype). Centroids are always
+ *     k x d fp32. Labels are int32 in [0, k). Distances are fp32 squared L2.
+ *   - Work is queued on opts->stream (a hipStream_t; NULL = the null stream).
+ *     emeans_train synchronises that stream before it returns (its statistics
+ *     are host values); emeans_assign and emeans_batch_rows are asynchronous.
+ *   - The library allocates its working memory stream-ordered on that stream
+ *     and releases it before returning (emeans_train) or stream-ordered after
+ *     the queued work (emeans_assign).
+ *   - Return value: EMEANS_OK (0) or a negative emeans_status. On error,
+ *     emeans_last_error() gives a message (thread-local). Arguments are checked
+ *     before any work is queued; a failed HIP call returns EMEANS_EHIP.
+ *   - Inputs are not checked for NaN or infinity (README "Data and centroids
+ *     fit on 1 GPU"): such values give undefined labels, never a fault.
+ */
+#ifndef EMEANS_H
+#define EMEANS_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define EMEANS_MAX_PASSES 64
+
+enum emeans_dtype { EMEANS_F32 = 0, EMEANS_BF16 = 1 };
+
+enum emeans_status {
+  EMEANS_OK = 0,
+  EMEANS_EINVAL = -1,     /* a size, pointer or option is out of range */
+  EMEANS_EDTYPE = -2,     /* unsupported element type */
+  EMEANS_ENOMEM = -3,     /* device allocation failed */
+  EMEANS_EHIP = -4,       /* a HIP call or kernel launch failed */
+  EMEANS_ENOTDEVICE = -5  /* a pointer is not device memory */
+};
+
+enum emeans_law { EMEANS_LAW_AUTO = 0, EMEANS_LAW_THROUGHPUT = 1, EMEANS_LAW_QUALITY = 2 };
+
+/* Options. A zero-initialised struct (or a NULL pointer) means the defaults
+ * of the README's "Settings" table. */
+typedef struct emeans_opts {
+  int32_t dtype;              /* emeans_dtype of X (default fp32) */
+  int32_t batch_law;          /* emeans_law: auto = quality for d <= 16, else throughput */
+  int64_t batch_size;         /* 0: from the batch law; > 0: this batch (capped at n),
+                                 and alpha0 then follows equation (3) for it */
+  double alpha0;              /* 0: equation (3), clamped to [1e-4, 1]; > 0: this value */
+  double unused_threshold;    /* 0: default (0.1, or no revival when d <= 2);
+                                 < 0: no revival; > 0: revive clusters whose running
+                                 count is below this fraction of the mean count */
+  int32_t no_finalize;        /* 0: last-pass exact means (default); 1: return the
+                                 EMA centroids c = S / N */
+  int32_t profile;            /* 1: time kernel classes with HIP events (stats->ms_*) */
+  void* stream;               /* hipStream_t, NULL = null stream */
+  /* Optional outputs for inspection and testing (NULL = not produced). */
+  int32_t* trace_labels;      /* device, sum of all batch sizes: the label of every
+                                 batch slot of every step, in step order */
+  float* out_counts;          /* device, k: running counts N at the end */
+  int32_t* split_log;         /* host, 3 * split_log_cap: (step, dead j, donor i) */
+  int64_t split_log_cap;
+} emeans_opts;
+
+/* Recipe and statistics of a run (README "Settings and results": recipe, obj,
+ * iteration_stats, n_splits). */
+typedef struct emeans_stats {
+  int64_t batch_size;
+  int64_t total_steps;
+  int64_t n_splits;                 /* dead clusters revived */
+  int64_t n_logged;                 /* entries written to opts->split_log */
+  int64_t dead_at_end;              /* clusters under the revival threshold at the end */
+  double alpha0;
+  double unused_threshold;          /* the threshold in effect (0 = no revival) */
+  int32_t law;                      /* emeans_law actually used */
+  int32_t n_passes;
+  int64_t rows_per_pass[EMEANS_MAX_PASSES];
+  int64_t steps_per_pass[EMEANS_MAX_PASSES];
+  double obj[EMEANS_MAX_PASSES];       /* mean squared distance of the pass's vectors to
+                                          the centroids they were assigned to, while
+                                          the centroids move */
+  double imbalance[EMEANS_MAX_PASSES]; /* k * sum n_j^2 / (sum n_j)^2 over the pass */
+  int64_t splits[EMEANS_MAX_PASSES];   /* revivals during the pass */
+  double ms_total;                     /* emeans_train wall clock */
+  double ms_assign, ms_group, ms_update, ms_revive;  /* with opts->profile */
+} emeans_stats;
+
+/* Scaling-law recipe for (n, d, k, T) and the given options; host only, no
+ * device work (README "Scaling laws", "Parameters", "Manual overrides").
+ * Fills batch_size, alpha0, law, unused_threshold, n_passes, rows_per_pass,
+ * steps_per_pass and total_steps of *out. Errors: EINVAL if n < 1, d < 1,
+ * k < 1, k > n, T <= 0, or more than EMEANS_MAX_PASSES passes. */
+int emeans_recipe(int64_t n, int32_t d, int32_t k, double T, const emeans_opts* opts,
+                  emeans_stats* out);
+
+/* Train e-means for T passes (T may be fractional: the last pass then visits
+ * floor(frac(T) * n) vectors) starting from k distinct rows of X chosen from
+ * `seed`.
+ *   X          device, n x d, opts->dtype
+ *   centroids  device, k x d fp32, output (also the working centroids)
+ *   labels     device, n int32, output or NULL: each vector's label from the
+ *              last pass (README "Quick start"); -1 for vectors that pass
+ *              did not visit
+ *   stats      host, output or NULL
+ * Errors: EINVAL (sizes as for emeans_recipe, n >= 2^31, NULL X/centroids),
+ * EDTYPE, ENOTDEVICE, ENOMEM, EHIP. Synchronises opts->stream. */
+int emeans_train(const void* X, int64_t n, int32_t d, int32_t k, double T, uint64_t seed,
+                 float* centroids, int32_t* labels, const emeans_opts* opts,
+                 emeans_stats* stats);
+
+/* Nearest centroid of each row of X (README "Settings and results":
+ * em.assign): labels[i] = argmin_j ||x_i - c_j||^2 (lowest j on ties) and
+ * dists[i] = that squared distance (fp32, >= 0). For bf16 X the centroids
+ * are searched in bf16 (README "Data precision").
+ *   X        device, n x d, opts->dtype      C       device, k x d fp32
+ *   labels   device, n int32 output          dists   device, n fp32 output or NULL
+ * Errors: EINVAL (n < 0, d < 1, k < 1, n >= 2^31, NULL pointers), EDTYPE,
+ * ENOTDEVICE, ENOMEM, EHIP. Asynchronous on opts->stream. */
+int emeans_assign(const void* X, int64_t n, int32_t d, const float* C, int32_t k,
+                  int32_t* labels, float* dists, const emeans_opts* opts);
+
+/* Rows visited by batch slots [start, start + count) of pass `pass` of a
+ * training run with this seed (README "Data too big for memory": a fresh
+ * order every pass, every vector once). rows_out: device, count int32.
+ * Errors: EINVAL (n < 1, n >= 2^31, start + count > n, NULL), ENOTDEVICE, EHIP.
+ * Asynchronous on `stream`. */
+int emeans_batch_rows(int64_t n, uint64_t seed, int32_t pass, int64_t start, int64_t count,
+                      int32_t* rows_out, void* stream);
+
+/* Message for the last non-zero return on this thread ("" if none). */
+const char* emeans_last_error(void);
+
+/* ABI version (major * 100 + minor). */
+int emeans_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* EMEANS_H */

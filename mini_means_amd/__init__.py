@@ -1,0 +1,239 @@
+"""e-means on MI355X: Python binding of libemeans.so.
+
+Argument marshalling only: every step of the training and assignment runs in
+the HIP kernels of ``libemeans.so``. PyTorch provides the device memory and the
+stream; there is no CPU fallback. If the library is not built, every call
+raises.
+
+    import torch, mini_means_amd as mm
+    x = torch.randn(100_000, 64, device="cuda")
+    out = mm.train(x, k=1024)               # 5 passes, scaling-law recipe
+    labels, dists = mm.assign(x, out.centroids)
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import re
+from dataclasses import dataclass
+from typing import Optional
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "_lib", "libemeans.so")
+HEADER = os.path.join(os.path.dirname(_PKG), "include", "emeans.h")
+
+MAX_PASSES = 64
+F32, BF16 = 0, 1
+LAWS = {"auto": 0, "throughput": 1, "quality": 2}
+STATUS = {0: "OK", -1: "EINVAL", -2: "EDTYPE", -3: "ENOMEM", -4: "EHIP", -5: "ENOTDEVICE"}
+
+c_i32, c_i64, c_dbl, c_vp = ctypes.c_int32, ctypes.c_int64, ctypes.c_double, ctypes.c_void_p
+
+
+class Opts(ctypes.Structure):
+    _fields_ = [
+        ("dtype", c_i32), ("batch_law", c_i32), ("batch_size", c_i64), ("alpha0", c_dbl),
+        ("unused_threshold", c_dbl), ("no_finalize", c_i32), ("profile", c_i32),
+        ("stream", c_vp), ("trace_labels", c_vp), ("out_counts", c_vp), ("split_log", c_vp),
+        ("split_log_cap", c_i64),
+    ]
+
+
+class Stats(ctypes.Structure):
+    _fields_ = [
+        ("batch_size", c_i64), ("total_steps", c_i64), ("n_splits", c_i64), ("n_logged", c_i64),
+        ("dead_at_end", c_i64), ("alpha0", c_dbl), ("unused_threshold", c_dbl),
+        ("law", c_i32), ("n_passes", c_i32),
+        ("rows_per_pass", c_i64 * MAX_PASSES), ("steps_per_pass", c_i64 * MAX_PASSES),
+        ("obj", c_dbl * MAX_PASSES), ("imbalance", c_dbl * MAX_PASSES),
+        ("splits", c_i64 * MAX_PASSES),
+        ("ms_total", c_dbl), ("ms_assign", c_dbl), ("ms_group", c_dbl), ("ms_update", c_dbl),
+        ("ms_revive", c_dbl),
+    ]
+
+
+class EmeansError(RuntimeError):
+    pass
+
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    """Load libemeans.so (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise EmeansError(f"{LIB_PATH} is missing: build it with "
+                              "`python -m mini_means_amd.build` (there is no CPU fallback)")
+        L = ctypes.CDLL(LIB_PATH)
+        L.emeans_recipe.argtypes = [c_i64, c_i32, c_i32, c_dbl, ctypes.POINTER(Opts),
+                                    ctypes.POINTER(Stats)]
+        L.emeans_train.argtypes = [c_vp, c_i64, c_i32, c_i32, c_dbl, ctypes.c_uint64, c_vp, c_vp,
+                                   ctypes.POINTER(Opts), ctypes.POINTER(Stats)]
+        L.emeans_assign.argtypes = [c_vp, c_i64, c_i32, c_vp, c_i32, c_vp, c_vp,
+                                    ctypes.POINTER(Opts)]
+        L.emeans_batch_rows.argtypes = [c_i64, ctypes.c_uint64, c_i32, c_i64, c_i64, c_vp, c_vp]
+        L.emeans_last_error.restype = ctypes.c_char_p
+        L.emeans_last_error.argtypes = []
+        L.emeans_version.argtypes = []
+        for f in ("emeans_recipe", "emeans_train", "emeans_assign", "emeans_batch_rows",
+                  "emeans_version"):
+            getattr(L, f).restype = ctypes.c_int
+        _lib = L
+    return _lib
+
+
+def declared_functions() -> list:
+    """Function names the C header declares."""
+    with open(HEADER) as f:
+        text = f.read()
+    return re.findall(r"^\s*(?:int|const char\*)\s+(emeans_\w+)\s*\(", text, flags=re.M)
+
+
+def _check(rc: int) -> None:
+    if rc != 0:
+        msg = lib().emeans_last_error().decode(errors="replace")
+        raise EmeansError(f"{STATUS.get(rc, rc)}: {msg}")
+
+
+def _opts(dtype=F32, batch_law="auto", batch_size=0, alpha0=0.0, unused_threshold=None,
+          finalize=True, profile=False, stream=None) -> Opts:
+    o = Opts()
+    o.dtype = dtype
+    o.batch_law = LAWS[batch_law] if isinstance(batch_law, str) else int(batch_law)
+    o.batch_size = int(batch_size or 0)
+    o.alpha0 = float(alpha0 or 0.0)
+    # ABI: 0 = default, < 0 = off, > 0 = value; Python: None = default, 0 = off
+    if unused_threshold is None:
+        o.unused_threshold = 0.0
+    elif unused_threshold <= 0:
+        o.unused_threshold = -1.0
+    else:
+        o.unused_threshold = float(unused_threshold)
+    o.no_finalize = 0 if finalize else 1
+    o.profile = 1 if profile else 0
+    o.stream = stream
+    return o
+
+
+def _stats_dict(s: Stats) -> dict:
+    P = s.n_passes
+    return dict(batch_size=s.batch_size, alpha0=s.alpha0, law=s.law, total_steps=s.total_steps,
+                n_passes=P, epoch_rows=list(s.rows_per_pass[:P]),
+                steps_per_pass=list(s.steps_per_pass[:P]), unused_threshold=s.unused_threshold,
+                obj=list(s.obj[:P]), imbalance=list(s.imbalance[:P]), splits=list(s.splits[:P]),
+                n_splits=s.n_splits, dead_at_end=s.dead_at_end, ms_total=s.ms_total,
+                ms_assign=s.ms_assign, ms_group=s.ms_group, ms_update=s.ms_update,
+                ms_revive=s.ms_revive)
+
+
+def recipe(n: int, d: int, k: int, T: float = 5.0, **kw) -> dict:
+    """Scaling-law recipe (host only): batch size, alpha0, passes and steps."""
+    s = Stats()
+    o = _opts(**kw)
+    _check(lib().emeans_recipe(int(n), int(d), int(k), float(T), ctypes.byref(o), ctypes.byref(s)))
+    return _stats_dict(s)
+
+
+def _dtype_of(X) -> int:
+    import torch
+    if X.dtype == torch.float32:
+        return F32
+    if X.dtype == torch.bfloat16:
+        return BF16
+    raise EmeansError(f"EDTYPE: {X.dtype} not supported (float32 or bfloat16)")
+
+
+def _stream_ptr(X, stream):
+    import torch
+    s = stream if stream is not None else torch.cuda.current_stream(X.device)
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _require_device(X) -> None:
+    if not getattr(X, "is_cuda", False):
+        raise EmeansError("ENOTDEVICE: X must be a tensor on the GPU")
+    if not X.is_contiguous():
+        raise EmeansError("EINVAL: X must be contiguous")
+
+
+@dataclass
+class TrainOutput:
+    centroids: object          # k x d float32 tensor
+    labels: object             # n int32 tensor or None
+    stats: dict
+    trace: object = None       # int32 tensor of every step's labels, or None
+    counts: object = None      # k float32 running counts at the end, or None
+    split_log: Optional[list] = None
+
+
+def train(X, k: int, T: float = 5.0, seed: int = 1234, *, batch_law="auto", batch_size: int = 0,
+          alpha0: float = 0.0, unused_threshold=None, finalize: bool = True,
+          capture_labels: bool = True, trace: bool = False, counts: bool = False,
+          split_log_cap: int = 0, profile: bool = False, stream=None) -> TrainOutput:
+    import torch
+    _require_device(X)
+    n, d = X.shape
+    dev = X.device
+    with torch.cuda.device(dev):
+        o = _opts(_dtype_of(X), batch_law, batch_size, alpha0, unused_threshold, finalize,
+                  profile, _stream_ptr(X, stream))
+        rc = recipe(n, d, k, T, batch_law=batch_law, batch_size=batch_size, alpha0=alpha0,
+                    unused_threshold=unused_threshold)
+        C = torch.empty((k, d), dtype=torch.float32, device=dev)
+        labels = torch.empty((n,), dtype=torch.int32, device=dev) if capture_labels else None
+        tr = torch.empty((sum(rc["epoch_rows"]),), dtype=torch.int32, device=dev) if trace else None
+        cn = torch.empty((k,), dtype=torch.float32, device=dev) if counts else None
+        log = (ctypes.c_int32 * (3 * split_log_cap))() if split_log_cap > 0 else None
+        if tr is not None:
+            o.trace_labels = tr.data_ptr()
+        if cn is not None:
+            o.out_counts = cn.data_ptr()
+        if log is not None:
+            o.split_log = ctypes.cast(log, c_vp)
+            o.split_log_cap = split_log_cap
+        s = Stats()
+        _check(lib().emeans_train(X.data_ptr(), n, d, int(k), float(T), int(seed) & (2**64 - 1),
+                                  C.data_ptr(), labels.data_ptr() if labels is not None else None,
+                                  ctypes.byref(o), ctypes.byref(s)))
+        st = _stats_dict(s)
+        splits = None
+        if log is not None:
+            m = min(s.n_logged, split_log_cap)
+            splits = [(log[3 * i], log[3 * i + 1], log[3 * i + 2]) for i in range(m)]
+        return TrainOutput(C, labels, st, tr, cn, splits)
+
+
+def assign(X, C, *, with_dists: bool = True, stream=None):
+    """Nearest centroid (int32 labels) and squared distance (float32) of each row."""
+    import torch
+    _require_device(X)
+    if not (getattr(C, "is_cuda", False) and C.dtype == torch.float32 and C.is_contiguous()):
+        raise EmeansError("EINVAL: C must be a contiguous float32 tensor on the GPU")
+    n, d = X.shape
+    k = C.shape[0]
+    if C.shape[1] != d:
+        raise EmeansError("EINVAL: C and X differ in dimension")
+    with torch.cuda.device(X.device):
+        labels = torch.empty((n,), dtype=torch.int32, device=X.device)
+        dists = torch.empty((n,), dtype=torch.float32, device=X.device) if with_dists else None
+        o = _opts(_dtype_of(X), stream=_stream_ptr(X, stream))
+        if n:
+            _check(lib().emeans_assign(X.data_ptr(), n, d, C.data_ptr(), k, labels.data_ptr(),
+                                       dists.data_ptr() if dists is not None else None,
+                                       ctypes.byref(o)))
+    return labels, dists
+
+
+def batch_rows(n: int, seed: int, pass_: int, start: int, count: int, device="cuda", stream=None):
+    """Rows visited by slots [start, start+count) of a pass of a training run."""
+    import torch
+    out = torch.empty((count,), dtype=torch.int32, device=device)
+    with torch.cuda.device(out.device):
+        s = stream if stream is not None else torch.cuda.current_stream(out.device)
+        if count:
+            _check(lib().emeans_batch_rows(int(n), int(seed) & (2**64 - 1), int(pass_),
+                                           int(start), int(count), out.data_ptr(),
+                                           ctypes.c_void_p(s.cuda_stream)))
+    return out

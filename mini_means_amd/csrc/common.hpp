@@ -1,0 +1,171 @@
+// Device-side building blocks shared by the e-means kernels (gfx950, wave64).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace emk {
+
+constexpr int kWave = 64;
+
+// Random streams (distinct Philox counter words).
+constexpr uint64_t kStreamInit = 1;
+constexpr uint64_t kStreamPerm = 2;
+constexpr uint64_t kStreamRevive = 3;
+constexpr uint64_t kStreamSign = 4;
+
+// ---------------------------------------------------------------------------
+// Philox4x64-10, Salmon, Moraes, Dror, Shaw, "Parallel Random Numbers: As Easy
+// as 1, 2, 3" (SC'11): ten rounds of two 64x64->128 multiplies, key bumped by
+// the Weyl increments between rounds.
+// ---------------------------------------------------------------------------
+struct U64x4 {
+  uint64_t w0, w1, w2, w3;
+};
+
+__host__ __device__ __forceinline__ uint64_t mulhi64(uint64_t a, uint64_t b) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  return __umul64hi(a, b);
+#else
+  return (uint64_t)(((unsigned __int128)a * b) >> 64);
+#endif
+}
+
+__host__ __device__ __forceinline__ U64x4 philox(uint64_t c0, uint64_t c1, uint64_t c2,
+                                                 uint64_t c3, uint64_t k0, uint64_t k1) {
+  constexpr uint64_t kM0 = 0xD2E7470EE14C6C93ull, kM1 = 0xCA5A826395121157ull;
+  constexpr uint64_t kW0 = 0x9E3779B97F4A7C15ull, kW1 = 0xBB67AE8584CAA73Bull;
+#pragma unroll
+  for (int r = 0; r < 10; ++r) {
+    if (r) {
+      k0 += kW0;
+      k1 += kW1;
+    }
+    const uint64_t lo0 = kM0 * c0, hi0 = mulhi64(kM0, c0);
+    const uint64_t lo1 = kM1 * c2, hi1 = mulhi64(kM1, c2);
+    const uint64_t n0 = hi1 ^ c1 ^ k0;
+    const uint64_t n2 = hi0 ^ c3 ^ k1;
+    c0 = n0;
+    c1 = lo1;
+    c2 = n2;
+    c3 = lo0;
+  }
+  return {c0, c1, c2, c3};
+}
+
+// ---------------------------------------------------------------------------
+// Keyed permutation of [0, n): balanced 4-round Feistel network on 2h bits
+// with Philox as round function (Luby-Rackoff), cycle-walked onto [0, n)
+// (Black-Rogaway). Every pass draws a fresh order with its own pass word.
+// ---------------------------------------------------------------------------
+struct PermKey {
+  uint64_t n, seed, stream, pass;
+  uint32_t h;
+  uint64_t mask;
+};
+
+inline PermKey make_perm_key(uint64_t n, uint64_t seed, uint64_t stream, uint64_t pass) {
+  uint32_t m = 0;
+  while (m < 64 && ((n - 1) >> m)) ++m;
+  uint32_t h = (m + 1) / 2;
+  if (h < 1) h = 1;
+  PermKey k{n, seed, stream, pass, h, (h >= 64) ? ~0ull : ((1ull << h) - 1)};
+  return k;
+}
+
+__host__ __device__ __forceinline__ uint64_t feistel(uint64_t v, const PermKey& k) {
+  uint64_t L = v >> k.h, R = v & k.mask;
+#pragma unroll
+  for (uint64_t r = 0; r < 4; ++r) {
+    const uint64_t f = philox(R, r, k.pass, k.stream, k.seed, 0).w0 & k.mask;
+    const uint64_t nl = R;
+    R = L ^ f;
+    L = nl;
+  }
+  return (L << k.h) | R;
+}
+
+__host__ __device__ __forceinline__ uint64_t perm_at(uint64_t i, const PermKey& k) {
+  uint64_t v = feistel(i, k);
+  while (v >= k.n) v = feistel(v, k);
+  return v;
+}
+
+// 53 random bits in [0, 1) for the revival draw of dead cluster j at step t.
+__device__ __forceinline__ double revive_uniform(uint64_t seed, uint64_t t, uint64_t j) {
+  const U64x4 w = philox(j, t, 0, kStreamRevive, seed, 0);
+  return (double)(w.w0 >> 11) * 0x1.0p-53;
+}
+
+// Sign (+1 / -1) of coordinate e for the split at step t that refills j.
+__device__ __forceinline__ float split_sign(uint64_t seed, uint64_t t, uint64_t j, uint32_t e) {
+  const U64x4 w = philox(j, t, e >> 8, kStreamSign, seed, 0);
+  const uint32_t q = (e >> 6) & 3;
+  const uint64_t word = q == 0 ? w.w0 : q == 1 ? w.w1 : q == 2 ? w.w2 : w.w3;
+  return ((word >> (e & 63)) & 1) ? -1.0f : 1.0f;
+}
+
+// ---------------------------------------------------------------------------
+// bf16 storage
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
+  const uint32_t b = __float_as_uint(f);
+  return (uint16_t)((b + 0x7FFFu + ((b >> 16) & 1u)) >> 16);
+}
+
+__device__ __forceinline__ float bf16_to_f32(uint16_t h) { return __uint_as_float((uint32_t)h << 16); }
+
+// ---------------------------------------------------------------------------
+// reductions
+// ---------------------------------------------------------------------------
+template <typename T>
+__device__ __forceinline__ T wave_sum(T v) {
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off, kWave);
+  return v;
+}
+
+// Inclusive scan across the 64 lanes of a wave.
+template <typename T>
+__device__ __forceinline__ T wave_incl_scan(T v) {
+  const int lane = threadIdx.x & (kWave - 1);
+#pragma unroll
+  for (int off = 1; off < kWave; off <<= 1) {
+    const T o = __shfl_up(v, off, kWave);
+    if (lane >= off) v += o;
+  }
+  return v;
+}
+
+// Inclusive scan across a block of NT threads (NT a multiple of 64, <= 1024).
+// `tmp` must hold NT/64 elements of shared memory. Ends with a barrier.
+template <typename T, int NT>
+__device__ __forceinline__ T block_incl_scan(T v, T* tmp) {
+  const int lane = threadIdx.x & (kWave - 1), w = threadIdx.x / kWave;
+  v = wave_incl_scan(v);
+  if (lane == kWave - 1) tmp[w] = v;
+  __syncthreads();
+  if (w == 0) {
+    T t = lane < NT / kWave ? tmp[lane] : T(0);
+    t = wave_incl_scan(t);
+    if (lane < NT / kWave) tmp[lane] = t;
+  }
+  __syncthreads();
+  if (w > 0) v += tmp[w - 1];
+  __syncthreads();
+  return v;
+}
+
+template <typename T, int NT>
+__device__ __forceinline__ T block_sum(T v, T* tmp) {
+  const int lane = threadIdx.x & (kWave - 1), w = threadIdx.x / kWave;
+  v = wave_sum(v);
+  if (lane == 0) tmp[w] = v;
+  __syncthreads();
+  T t = T(0);
+  for (int i = 0; i < NT / kWave; ++i) t += tmp[i];
+  __syncthreads();
+  return t;
+}
+
+}  // namespace emk

@@ -1,0 +1,80 @@
+// Host-side launchers of the e-means kernels (internal to libemeans.so).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "common.hpp"
+
+namespace emk {
+
+// Assign: for batch slot r (row = rows ? rows[r] : r) of X, the nearest
+// centroid by maximal score x.c - |c|^2/2 (equivalent to minimal squared
+// distance). `Cs` is the search-format centroid table (fp32 C, or bf16 C-hat
+// for bf16 X) and `bias` = -|c|^2/2 computed from it. Writes labels[r],
+// dists[r] (optional), counts[label] += 1 (optional) and obj[0] += sum of
+// distances (optional).
+hipError_t launch_assign(bool bf16, const void* X, int d, const uint32_t* rows, int nrows,
+                         const void* Cs, const float* bias, int k, int32_t* labels, float* dists,
+                         int32_t* counts, double* obj, hipStream_t st);
+
+// rows[r] = pi(start + r) for the keyed permutation pk.
+hipError_t launch_sample_rows(const PermKey& pk, uint64_t start, int count, uint32_t* rows,
+                              hipStream_t st);
+hipError_t launch_sample_rows_i32(const PermKey& pk, uint64_t start, int count, int32_t* rows,
+                                  hipStream_t st);
+
+// C[j] = X[pi(j)] as fp32, j < k.
+hipError_t launch_init_centroids(bool bf16, const void* X, int d, const PermKey& pk, int k,
+                                 float* C, hipStream_t st);
+
+// bias[j] = -|c_j|^2 / 2 in the search format; Chat = bf16(C) when non-null.
+hipError_t launch_prep(const float* C, int k, int d, float* bias, uint16_t* Chat, hipStream_t st);
+
+// off = exclusive scan of counts (k+1 entries), cursor = off[0..k),
+// item_off = exclusive scan of ceil(counts / R).
+hipError_t launch_scan(const int32_t* counts, int k, int R, int32_t* off, int32_t* cursor,
+                       int32_t* item_off, hipStream_t st);
+
+// Bucket the batch by label: order[cursor[label]++] = rows[r]; when
+// out_labels is non-null also out_labels[rows[r]] = label.
+hipError_t launch_scatter(const int32_t* labels, const uint32_t* rows, int nb, int32_t* cursor,
+                          uint32_t* order, int32_t* out_labels, hipStream_t st);
+
+// s_acc[j] += sum of X rows of cluster j (work items of at most R rows).
+hipError_t launch_group(bool bf16, const void* X, int d, const uint32_t* order,
+                        const int32_t* off, const int32_t* item_off, int k, int R, int nb,
+                        float* s_acc, hipStream_t st);
+
+// EMA update of every cluster; resets counts and s_acc for the next step;
+// pass_counts += counts; LS += s when LS is non-null; refreshes bias/Chat.
+hipError_t launch_ema(int k, int d, float a, float b, int32_t* counts, float* s_acc, float* N,
+                      float* S, float* C, float* bias, uint16_t* Chat, int32_t* pass_counts,
+                      float* LS, hipStream_t st);
+
+struct ReviveArgs {
+  int k, d;
+  float* N;
+  float* S;
+  float* C;
+  float* bias;
+  uint16_t* Chat;
+  double thr;
+  uint64_t seed, step;
+  int32_t* flags;     // k scratch
+  int32_t* dead;      // k scratch
+  int64_t* counters;  // [0] splits, [1] logged, [2] dead count, [3] splits this pass
+  int32_t* log;       // 3 * log_cap
+  int64_t log_cap;
+  int count_only;
+};
+hipError_t launch_revive(const ReviveArgs& a, hipStream_t st);
+
+// sums[0] += sum n_j^2, sums[1] += sum n_j over pass_counts; zeroes them if `reset`.
+hipError_t launch_pass_stats(int32_t* pass_counts, int k, double* sums, int reset, hipStream_t st);
+
+// C[j] = LS[j] / pass_counts[j] where pass_counts[j] > 0.
+hipError_t launch_finalize(int k, int d, const int32_t* pass_counts, const float* LS, float* C,
+                           hipStream_t st);
+
+}  // namespace emk

@@ -1,0 +1,551 @@
+// Everything of an e-means step after the assignment: batch sampling, the
+// bucketing of the batch by label, the per-cluster sums, the EMA update of the
+// running statistics, dead-cluster revival and the closing mean.
+//
+// Precision (faiss e_means README, "Data precision"): running counts, running
+// sums and centroids are fp32. The running count update is written as
+// fl(fl(b*N) + fl(a*n)) with b = fl(1 - a) and no fused multiply-add, so that
+// given the same labels it is reproducible bit for bit.
+#include "kernels.hpp"
+
+namespace emk {
+
+namespace {
+
+constexpr float kSplitEps = 0x1.0p-10f;  // relative perturbation of a split
+
+__global__ void sample_rows_kernel(PermKey pk, uint64_t start, int count, uint32_t* rows) {
+  const int r = blockIdx.x * blockDim.x + threadIdx.x;
+  if (r < count) rows[r] = (uint32_t)perm_at(start + (uint64_t)r, pk);
+}
+
+__global__ void sample_rows_i32_kernel(PermKey pk, uint64_t start, int count, int32_t* rows) {
+  const int r = blockIdx.x * blockDim.x + threadIdx.x;
+  if (r < count) rows[r] = (int32_t)perm_at(start + (uint64_t)r, pk);
+}
+
+// One wave per centroid: C[j] = X[pi(j)] converted to fp32.
+__global__ __launch_bounds__(256) void init_centroids_kernel(const unsigned char* X, int bf16,
+                                                             int d, PermKey pk, int k, float* C) {
+  const int j = blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  if (j >= k) return;
+  uint64_t row = 0;
+  if (lane == 0) row = perm_at((uint64_t)j, pk);
+  row = __shfl(row, 0, 64);
+  for (int e = lane; e < d; e += 64) {
+    float v;
+    if (bf16)
+      v = bf16_to_f32(reinterpret_cast<const uint16_t*>(X)[row * (uint64_t)d + e]);
+    else
+      v = reinterpret_cast<const float*>(X)[row * (uint64_t)d + e];
+    C[(size_t)j * d + e] = v;
+  }
+}
+
+// One wave per centroid: bias = -|c|^2/2 in the search format, Chat = bf16(c).
+__global__ __launch_bounds__(256) void prep_kernel(const float* C, int k, int d, float* bias,
+                                                   uint16_t* Chat) {
+  const int j = blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  if (j >= k) return;
+  float nrm = 0.0f;
+  for (int e = lane; e < d; e += 64) {
+    float c = C[(size_t)j * d + e];
+    if (Chat) {
+      const uint16_t h = f32_to_bf16_rne(c);
+      Chat[(size_t)j * d + e] = h;
+      c = bf16_to_f32(h);
+    }
+    nrm += c * c;
+  }
+  nrm = wave_sum(nrm);
+  if (lane == 0) bias[j] = -0.5f * nrm;
+}
+
+// Single workgroup: exclusive scans of counts and of ceil(counts / R).
+__global__ __launch_bounds__(1024) void scan_kernel(const int32_t* counts, int k, int R,
+                                                    int32_t* off, int32_t* cursor,
+                                                    int32_t* item_off) {
+  __shared__ int tmp[16];
+  const int tid = threadIdx.x;
+  const int cs = (k + 1023) / 1024;
+  const int j0 = min(k, tid * cs), j1 = min(k, j0 + cs);
+  int c = 0, it = 0;
+  for (int j = j0; j < j1; ++j) {
+    const int n = counts[j];
+    c += n;
+    it += (n + R - 1) / R;
+  }
+  const int ci = block_incl_scan<int, 1024>(c, tmp);
+  const int ii = block_incl_scan<int, 1024>(it, tmp);
+  int oc = ci - c, oi = ii - it;
+  for (int j = j0; j < j1; ++j) {
+    const int n = counts[j];
+    off[j] = oc;
+    cursor[j] = oc;
+    item_off[j] = oi;
+    oc += n;
+    oi += (n + R - 1) / R;
+  }
+  if (tid == 1023) {
+    off[k] = ci;
+    item_off[k] = ii;
+  }
+}
+
+__global__ void scatter_kernel(const int32_t* labels, const uint32_t* rows, int nb,
+                               int32_t* cursor, uint32_t* order, int32_t* out_labels) {
+  const int r = blockIdx.x * blockDim.x + threadIdx.x;
+  if (r >= nb) return;
+  const int j = labels[r];
+  const uint32_t row = rows[r];
+  const int pos = atomicAdd(&cursor[j], 1);
+  order[pos] = row;
+  if (out_labels) out_labels[row] = j;
+}
+
+// One workgroup per work item: up to R rows of one cluster (rows taken from
+// the bucketed order). Columns are 16-byte chunks when the rows allow it.
+// Threads are arranged as rpar row groups x ncol columns; row groups are
+// folded through LDS; a cluster held by a single item is stored, otherwise
+// its partial sums are added atomically.
+template <bool BF16, bool VEC>
+__global__ __launch_bounds__(256) void group_kernel(const unsigned char* __restrict__ X, int d,
+                                                    const uint32_t* __restrict__ order,
+                                                    const int32_t* __restrict__ off,
+                                                    const int32_t* __restrict__ item_off, int k,
+                                                    int R, float* __restrict__ s_acc) {
+  constexpr int ES = BF16 ? 2 : 4;
+  constexpr int EPV = VEC ? 16 / ES : 1;  // elements per column unit
+  __shared__ float red[256 * EPV];
+  const int w = blockIdx.x;
+  const int nitems = item_off[k];
+  if (w >= nitems) return;
+  int lo = 0, hi = k;  // largest j with item_off[j] <= w
+  while (hi - lo > 1) {
+    const int mid = (lo + hi) >> 1;
+    if (item_off[mid] <= w) lo = mid; else hi = mid;
+  }
+  const int j = lo;
+  const int p = w - item_off[j];
+  const int beg = off[j] + p * R;
+  const int end = min(off[j + 1], beg + R);
+  const bool single = (item_off[j + 1] - item_off[j]) == 1;
+  const int tid = threadIdx.x;
+  const int ncol = d / EPV;
+  const size_t rowbytes = (size_t)d * ES;
+  float* dst = s_acc + (size_t)j * d;
+
+  auto load_unit = [&](uint32_t row, int col, float* v) {
+    const unsigned char* base = X + (size_t)row * rowbytes;
+    if constexpr (VEC) {
+      typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+      const u32x4 q = *reinterpret_cast<const u32x4*>(base + (size_t)col * 16);
+      if constexpr (BF16) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          v[2 * e] = __uint_as_float(q[e] << 16);
+          v[2 * e + 1] = __uint_as_float(q[e] & 0xFFFF0000u);
+        }
+      } else {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) v[e] = __uint_as_float(q[e]);
+      }
+    } else {
+      if constexpr (BF16)
+        v[0] = bf16_to_f32(reinterpret_cast<const uint16_t*>(base)[col]);
+      else
+        v[0] = reinterpret_cast<const float*>(base)[col];
+    }
+  };
+
+  auto write_out = [&](int col, const float* acc) {
+#pragma unroll
+    for (int e = 0; e < EPV; ++e) {
+      if (single)
+        dst[col * EPV + e] = acc[e];
+      else
+        atomicAdd(&dst[col * EPV + e], acc[e]);
+    }
+  };
+
+  if (ncol >= 256) {
+    for (int col = tid; col < ncol; col += 256) {
+      float acc[EPV];
+#pragma unroll
+      for (int e = 0; e < EPV; ++e) acc[e] = 0.0f;
+      int pos = beg;
+      for (; pos + 4 <= end; pos += 4) {
+        float v0[EPV], v1[EPV], v2[EPV], v3[EPV];
+        load_unit(order[pos], col, v0);
+        load_unit(order[pos + 1], col, v1);
+        load_unit(order[pos + 2], col, v2);
+        load_unit(order[pos + 3], col, v3);
+#pragma unroll
+        for (int e = 0; e < EPV; ++e) acc[e] += v0[e] + v1[e] + v2[e] + v3[e];
+      }
+      for (; pos < end; ++pos) {
+        float v[EPV];
+        load_unit(order[pos], col, v);
+#pragma unroll
+        for (int e = 0; e < EPV; ++e) acc[e] += v[e];
+      }
+      write_out(col, acc);
+    }
+    return;
+  }
+
+  const int rpar = 256 / ncol;
+  const int rg = tid / ncol;
+  const int col = tid - rg * ncol;
+  float acc[EPV];
+#pragma unroll
+  for (int e = 0; e < EPV; ++e) acc[e] = 0.0f;
+  if (rg < rpar) {
+    int pos = beg + rg;
+    for (; pos + 3 * rpar < end; pos += 4 * rpar) {
+      float v0[EPV], v1[EPV], v2[EPV], v3[EPV];
+      load_unit(order[pos], col, v0);
+      load_unit(order[pos + rpar], col, v1);
+      load_unit(order[pos + 2 * rpar], col, v2);
+      load_unit(order[pos + 3 * rpar], col, v3);
+#pragma unroll
+      for (int e = 0; e < EPV; ++e) acc[e] += v0[e] + v1[e] + v2[e] + v3[e];
+    }
+    for (; pos < end; pos += rpar) {
+      float v[EPV];
+      load_unit(order[pos], col, v);
+#pragma unroll
+      for (int e = 0; e < EPV; ++e) acc[e] += v[e];
+    }
+#pragma unroll
+    for (int e = 0; e < EPV; ++e) red[(rg * ncol + col) * EPV + e] = acc[e];
+  }
+  __syncthreads();
+  if (rg == 0) {
+    for (int g = 1; g < rpar; ++g)
+#pragma unroll
+      for (int e = 0; e < EPV; ++e) acc[e] += red[(g * ncol + col) * EPV + e];
+    write_out(col, acc);
+  }
+}
+
+// One wave per cluster: EMA of the running count and sum, centroid S/N,
+// search-format refresh, last-pass accumulation; resets counts and s_acc.
+template <bool BF16S>
+__global__ __launch_bounds__(256) void ema_kernel(int k, int d, float a, float b,
+                                                  int32_t* counts, float* s_acc, float* N,
+                                                  float* S, float* C, float* bias,
+                                                  uint16_t* Chat, int32_t* pass_counts,
+                                                  float* LS) {
+  const int j = blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  if (j >= k) return;
+  const int n = counts[j];
+  const float Nn = __fadd_rn(__fmul_rn(b, N[j]), __fmul_rn(a, (float)n));
+  float nrm = 0.0f;
+  const size_t base = (size_t)j * d;
+  for (int e = lane; e < d; e += 64) {
+    const size_t idx = base + e;
+    float s = 0.0f;
+    if (n) {
+      s = s_acc[idx];
+      s_acc[idx] = 0.0f;
+    }
+    const float Sv = __fadd_rn(__fmul_rn(b, S[idx]), __fmul_rn(a, s));
+    S[idx] = Sv;
+    float c;
+    if (Nn > 0.0f) {
+      c = __fdiv_rn(Sv, Nn);
+      C[idx] = c;
+    } else {
+      c = C[idx];
+    }
+    if (LS && n) LS[idx] += s;
+    if constexpr (BF16S) {
+      const uint16_t h = f32_to_bf16_rne(c);
+      Chat[idx] = h;
+      c = bf16_to_f32(h);
+    }
+    nrm += c * c;
+  }
+  nrm = wave_sum(nrm);
+  if (lane == 0) {
+    N[j] = Nn;
+    bias[j] = -0.5f * nrm;
+    pass_counts[j] += n;
+    counts[j] = 0;
+  }
+}
+
+// Single workgroup. Mean running count m = sum N / k (fp64); dead set D =
+// {j : N_j < thr * m} in index order. For each dead j in turn: u from Philox,
+// donor i = first live index whose fp64 prefix sum of N over live clusters
+// exceeds u * (sum of live N); the donor keeps half of its count and sum,
+// cluster j takes the other half, and both sums are perturbed by
+// -/+ 2^-10 * sign per coordinate. Live prefix sums are kept as per-thread
+// chunk sums so a draw costs one block scan plus one chunk walk.
+__global__ __launch_bounds__(1024) void revive_kernel(ReviveArgs A) {
+  __shared__ double dtmp[16];
+  __shared__ int itmp[16];
+  __shared__ double bs[1024];
+  __shared__ float ftmp[16];
+  __shared__ int s_ndead, s_donor, s_last;
+  __shared__ double s_tot;
+  const int tid = threadIdx.x;
+  const int k = A.k, d = A.d;
+
+  double loc = 0.0;
+  for (int j = tid; j < k; j += 1024) loc += (double)A.N[j];
+  const double total = block_sum<double, 1024>(loc, dtmp);
+  const double th = A.thr * (total / (double)k);
+
+  const int cs = (k + 1023) / 1024;
+  const int j0 = min(k, tid * cs), j1 = min(k, j0 + cs);
+  int cnt = 0;
+  for (int j = j0; j < j1; ++j) {
+    const int dd = ((double)A.N[j] < th) ? 1 : 0;
+    A.flags[j] = dd;
+    cnt += dd;
+  }
+  const int incl = block_incl_scan<int, 1024>(cnt, itmp);
+  if (tid == 1023) s_ndead = incl;
+  int wpos = incl - cnt;
+  for (int j = j0; j < j1; ++j)
+    if (A.flags[j]) A.dead[wpos++] = j;
+  __threadfence_block();
+  __syncthreads();
+  const int ndead = s_ndead;
+  if (A.count_only) {
+    if (tid == 0) A.counters[2] = ndead;
+    return;
+  }
+  if (ndead == 0) return;
+
+  double mys = 0.0;
+  int mylast = -1;
+  for (int j = j0; j < j1; ++j)
+    if (!A.flags[j]) {
+      mys += (double)A.N[j];
+      mylast = j;
+    }
+  bs[tid] = mys;
+  if (tid == 0) s_last = -1;
+  __syncthreads();
+  if (mylast >= 0) atomicMax(&s_last, mylast);
+  __syncthreads();
+  const int last_live = s_last;
+  if (last_live < 0) return;  // no donor exists (every cluster under the threshold)
+
+  for (int q = 0; q < ndead; ++q) {
+    const int j = A.dead[q];
+    const double u = revive_uniform(A.seed, A.step, (uint64_t)j);
+    const double v = bs[tid];
+    const double inc = block_incl_scan<double, 1024>(v, dtmp);
+    if (tid == 1023) s_tot = inc;
+    if (tid == 0) s_donor = last_live;
+    __syncthreads();
+    const double target = u * s_tot;
+    const double ex = inc - v;
+    if (v > 0.0 && ex <= target && target < inc) {
+      double acc = ex;
+      int donor = -1, lastl = -1;
+      for (int jj = j0; jj < j1; ++jj) {
+        if (A.flags[jj]) continue;
+        lastl = jj;
+        acc += (double)A.N[jj];
+        if (acc > target) {
+          donor = jj;
+          break;
+        }
+      }
+      s_donor = donor >= 0 ? donor : lastl;
+    }
+    __syncthreads();
+    const int i = s_donor;
+    const float Ni = A.N[i] * 0.5f;
+    __syncthreads();
+    if (tid == 0) {
+      A.N[i] = Ni;
+      A.N[j] = Ni;
+      const int64_t c = A.counters[1];
+      if (A.log && c < A.log_cap) {
+        A.log[3 * c] = (int32_t)A.step;
+        A.log[3 * c + 1] = j;
+        A.log[3 * c + 2] = i;
+        A.counters[1] = c + 1;
+      }
+    }
+    float ni = 0.0f, nj = 0.0f;
+    for (int e = tid; e < d; e += 1024) {
+      const size_t ii = (size_t)i * d + e, jj = (size_t)j * d + e;
+      const float half = A.S[ii] * 0.5f;
+      const float sg = split_sign(A.seed, A.step, (uint64_t)j, (uint32_t)e);
+      const float sj = __fmul_rn(half, 1.0f + kSplitEps * sg);
+      const float si = __fmul_rn(half, 1.0f - kSplitEps * sg);
+      A.S[jj] = sj;
+      A.S[ii] = si;
+      float cj = __fdiv_rn(sj, Ni), ci = __fdiv_rn(si, Ni);
+      A.C[jj] = cj;
+      A.C[ii] = ci;
+      if (A.Chat) {
+        const uint16_t hj = f32_to_bf16_rne(cj), hi = f32_to_bf16_rne(ci);
+        A.Chat[jj] = hj;
+        A.Chat[ii] = hi;
+        cj = bf16_to_f32(hj);
+        ci = bf16_to_f32(hi);
+      }
+      ni += ci * ci;
+      nj += cj * cj;
+    }
+    ni = block_sum<float, 1024>(ni, ftmp);
+    nj = block_sum<float, 1024>(nj, ftmp);
+    if (tid == 0) {
+      A.bias[i] = -0.5f * ni;
+      A.bias[j] = -0.5f * nj;
+    }
+    __threadfence_block();
+    __syncthreads();
+    if (tid == i / cs) {
+      double s2 = 0.0;
+      for (int jj = j0; jj < j1; ++jj)
+        if (!A.flags[jj]) s2 += (double)A.N[jj];
+      bs[tid] = s2;
+    }
+    __syncthreads();
+  }
+  if (tid == 0) {
+    A.counters[0] += ndead;
+    A.counters[3] += ndead;
+  }
+}
+
+__global__ __launch_bounds__(1024) void pass_stats_kernel(int32_t* pass_counts, int k,
+                                                          double* sums, int reset) {
+  __shared__ double tmp[16];
+  double s2 = 0.0, s1 = 0.0;
+  for (int j = threadIdx.x; j < k; j += 1024) {
+    const double n = (double)pass_counts[j];
+    s2 += n * n;
+    s1 += n;
+    if (reset) pass_counts[j] = 0;
+  }
+  s2 = block_sum<double, 1024>(s2, tmp);
+  s1 = block_sum<double, 1024>(s1, tmp);
+  if (threadIdx.x == 0) {
+    sums[0] += s2;
+    sums[1] += s1;
+  }
+}
+
+__global__ void finalize_kernel(int k, int d, const int32_t* pass_counts, const float* LS,
+                                float* C) {
+  const size_t total = (size_t)k * d;
+  for (size_t idx = blockIdx.x * (size_t)blockDim.x + threadIdx.x; idx < total;
+       idx += (size_t)gridDim.x * blockDim.x) {
+    const int j = (int)(idx / d);
+    const int n = pass_counts[j];
+    if (n > 0) C[idx] = __fdiv_rn(LS[idx], (float)n);
+  }
+}
+
+}  // namespace
+
+hipError_t launch_sample_rows(const PermKey& pk, uint64_t start, int count, uint32_t* rows,
+                              hipStream_t st) {
+  if (count <= 0) return hipSuccess;
+  sample_rows_kernel<<<(count + 255) / 256, 256, 0, st>>>(pk, start, count, rows);
+  return hipGetLastError();
+}
+
+hipError_t launch_sample_rows_i32(const PermKey& pk, uint64_t start, int count, int32_t* rows,
+                                  hipStream_t st) {
+  if (count <= 0) return hipSuccess;
+  sample_rows_i32_kernel<<<(count + 255) / 256, 256, 0, st>>>(pk, start, count, rows);
+  return hipGetLastError();
+}
+
+hipError_t launch_init_centroids(bool bf16, const void* X, int d, const PermKey& pk, int k,
+                                 float* C, hipStream_t st) {
+  init_centroids_kernel<<<(k + 3) / 4, 256, 0, st>>>(static_cast<const unsigned char*>(X),
+                                                     bf16 ? 1 : 0, d, pk, k, C);
+  return hipGetLastError();
+}
+
+hipError_t launch_prep(const float* C, int k, int d, float* bias, uint16_t* Chat,
+                       hipStream_t st) {
+  prep_kernel<<<(k + 3) / 4, 256, 0, st>>>(C, k, d, bias, Chat);
+  return hipGetLastError();
+}
+
+hipError_t launch_scan(const int32_t* counts, int k, int R, int32_t* off, int32_t* cursor,
+                       int32_t* item_off, hipStream_t st) {
+  scan_kernel<<<1, 1024, 0, st>>>(counts, k, R, off, cursor, item_off);
+  return hipGetLastError();
+}
+
+hipError_t launch_scatter(const int32_t* labels, const uint32_t* rows, int nb, int32_t* cursor,
+                          uint32_t* order, int32_t* out_labels, hipStream_t st) {
+  if (nb <= 0) return hipSuccess;
+  scatter_kernel<<<(nb + 255) / 256, 256, 0, st>>>(labels, rows, nb, cursor, order, out_labels);
+  return hipGetLastError();
+}
+
+hipError_t launch_group(bool bf16, const void* X, int d, const uint32_t* order,
+                        const int32_t* off, const int32_t* item_off, int k, int R, int nb,
+                        float* s_acc, hipStream_t st) {
+  if (nb <= 0) return hipSuccess;
+  // upper bound on work items: one per non-empty cluster plus one per R rows
+  const long long items = (long long)(k < nb ? k : nb) + (nb + R - 1) / R;
+  const dim3 grid((unsigned)items), block(256);
+  const auto* x = static_cast<const unsigned char*>(X);
+  const bool aligned = (uintptr_t)X % 16 == 0;
+  if (bf16) {
+    if (aligned && d % 8 == 0)
+      group_kernel<true, true><<<grid, block, 0, st>>>(x, d, order, off, item_off, k, R, s_acc);
+    else
+      group_kernel<true, false><<<grid, block, 0, st>>>(x, d, order, off, item_off, k, R, s_acc);
+  } else {
+    if (aligned && d % 4 == 0)
+      group_kernel<false, true><<<grid, block, 0, st>>>(x, d, order, off, item_off, k, R, s_acc);
+    else
+      group_kernel<false, false><<<grid, block, 0, st>>>(x, d, order, off, item_off, k, R, s_acc);
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_ema(int k, int d, float a, float b, int32_t* counts, float* s_acc, float* N,
+                      float* S, float* C, float* bias, uint16_t* Chat, int32_t* pass_counts,
+                      float* LS, hipStream_t st) {
+  const dim3 grid((k + 3) / 4), block(256);
+  if (Chat)
+    ema_kernel<true><<<grid, block, 0, st>>>(k, d, a, b, counts, s_acc, N, S, C, bias, Chat,
+                                             pass_counts, LS);
+  else
+    ema_kernel<false><<<grid, block, 0, st>>>(k, d, a, b, counts, s_acc, N, S, C, bias, Chat,
+                                              pass_counts, LS);
+  return hipGetLastError();
+}
+
+hipError_t launch_revive(const ReviveArgs& a, hipStream_t st) {
+  revive_kernel<<<1, 1024, 0, st>>>(a);
+  return hipGetLastError();
+}
+
+hipError_t launch_pass_stats(int32_t* pass_counts, int k, double* sums, int reset,
+                             hipStream_t st) {
+  pass_stats_kernel<<<1, 1024, 0, st>>>(pass_counts, k, sums, reset);
+  return hipGetLastError();
+}
+
+hipError_t launch_finalize(int k, int d, const int32_t* pass_counts, const float* LS, float* C,
+                           hipStream_t st) {
+  const size_t total = (size_t)k * d;
+  const size_t want = (total + 255) / 256;
+  const unsigned blocks = (unsigned)(want < 65536 ? want : 65536);
+  finalize_kernel<<<blocks, 256, 0, st>>>(k, d, pass_counts, LS, C);
+  return hipGetLastError();
+}
+
+}  // namespace emk

@@ -1,0 +1,113 @@
+"""Helpers for the GPU-vs-oracle parity tests.
+
+Tolerances (the parity bar):
+  * labels: equal to the oracle's wherever the oracle's runner-up gap
+    (d2 - d1) exceeds 1e-5 relative to |x|^2 + |c_best|^2, the size of the
+    quantities a distance is computed from; elsewhere the label must be one
+    of the near-tied centroids (its distance within that band of the best);
+  * distances: within 1e-5 * (|x|^2 + |c|^2) of the oracle's fp64 distance
+    to the same centroid;
+  * centroids: relative L2 error 1e-4 (fp32 data) or 1e-2 (bf16 data);
+  * running counts: bit-exact given the same labels;
+  * final MSE: 1e-3 relative.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+import oracle
+
+GAP_TOL = 1e-5
+DIST_TOL = 1e-5
+
+
+def to_device(X: np.ndarray, device="cuda"):
+    import torch
+    if X.dtype == np.uint16:
+        return torch.from_numpy(X.view(np.int16)).to(device).view(torch.bfloat16)
+    return torch.from_numpy(X).to(device)
+
+
+def scale_of(X, C, rows, labels):
+    Xf = oracle.to_f32(X if rows is None else X[rows]).astype(np.float64)
+    Cb = C[labels].astype(np.float64)
+    return np.einsum("ij,ij->i", Xf, Xf) + np.einsum("ij,ij->i", Cb, Cb)
+
+
+def check_labels(X, Cs, rows, given, olab, d1, d2, given_dist=None, what=""):
+    """Check labels `given` against the oracle's (olab, d1, d2) on the same rows."""
+    given = np.asarray(given)
+    if given_dist is None:
+        given_dist = oracle.dist_to(X, Cs, given, rows)
+    sc = scale_of(X, Cs, rows, olab)
+    gap = (d2 - d1) / np.maximum(sc, 1e-300)
+    decided = gap > GAP_TOL
+    bad = decided & (given != olab)
+    assert not bad.any(), (
+        f"{what}: {int(bad.sum())} decided labels differ, e.g. slot {int(np.argmax(bad))}: "
+        f"gpu {given[bad][:5]} oracle {olab[bad][:5]} gap {gap[bad][:5]}")
+    und = ~decided
+    band_ok = given_dist[und] <= d1[und] + GAP_TOL * sc[und]
+    assert band_ok.all(), f"{what}: near-tie labels outside the tie band"
+    assert np.all((given >= 0) & (given < Cs.shape[0]))
+    return int(decided.sum()), int(und.sum()), int((und & (given != olab)).sum())
+
+
+def check_dists(X, Cs, rows, labels, dists, what=""):
+    ref = oracle.dist_to(X, Cs, labels, rows)
+    sc = scale_of(X, Cs, rows, labels)
+    err = np.abs(dists.astype(np.float64) - ref)
+    assert np.all(err <= DIST_TOL * sc + 1e-30), (
+        f"{what}: distance error {err.max():.3e} (scale {sc[np.argmax(err)]:.3e})")
+    assert np.all(dists >= 0)
+
+
+def rel_l2(a, b) -> float:
+    a = np.asarray(a, np.float64)
+    b = np.asarray(b, np.float64)
+    return float(np.linalg.norm(a - b) / max(np.linalg.norm(b), 1e-300))
+
+
+def step_offsets(rc: dict) -> np.ndarray:
+    B = rc["batch_size"]
+    sizes = []
+    for rows_e, steps in zip(rc["epoch_rows"], rc["steps_per_pass"]):
+        for s in range(steps):
+            sizes.append(min(B, rows_e - s * B))
+    return np.concatenate([[0], np.cumsum(sizes)]).astype(np.int64)
+
+
+def lockstep(X: np.ndarray, out, k: int, T: float, seed: int, sample: int = 0,
+             rng_seed: int = 0, **opts):
+    """Replay a GPU training run in the oracle, adopting the GPU's labels after
+    checking them (all slots, or `sample` random slots per step), and return
+    the oracle's result and the check summary."""
+    trace = out.trace.cpu().numpy()
+    rc = oracle.recipe(X.shape[0], X.shape[1], k, T, opts.get("batch_law", 0),
+                       opts.get("batch_size", 0), opts.get("alpha0", 0.0),
+                       opts.get("unused_threshold", -1.0))
+    offs = step_offsets(rc)
+    assert offs[-1] == len(trace)
+    rng = np.random.default_rng(rng_seed)
+    summary = dict(decided=0, undecided=0, undecided_differ=0, steps=0)
+
+    def labels_for_step(t, rows):
+        return trace[offs[t]:offs[t + 1]]
+
+    def check_slots(t, Bt):
+        if not sample or sample >= Bt:
+            return None
+        return np.sort(rng.choice(Bt, size=sample, replace=False))
+
+    def hook(chk):
+        dec, und, diff = check_labels(X, chk["C"], chk["rows"], chk["given"], chk["oracle"],
+                                      chk["d1"], chk["d2"], chk["given_dist"],
+                                      what=f"step {chk['t']}")
+        summary["decided"] += dec
+        summary["undecided"] += und
+        summary["undecided_differ"] += diff
+        summary["steps"] += 1
+
+    res = oracle.train(X, k, T, seed, labels_for_step=labels_for_step, check_slots=check_slots,
+                       check_hook=hook, **opts)
+    return res, summary

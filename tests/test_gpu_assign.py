@@ -1,0 +1,133 @@
+"""emeans_assign and emeans_batch_rows on the GPU against the oracle."""
+import numpy as np
+import pytest
+
+import oracle
+from mini_means_amd import datagen
+
+from parity import check_dists, check_labels, to_device
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def mm():
+    import torch
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import mini_means_amd
+    mini_means_amd.lib()
+    return mini_means_amd
+
+
+def _centroids(X, k, seed):
+    rng = np.random.default_rng(seed)
+    Xf = oracle.to_f32(X)
+    idx = rng.choice(len(X), size=k, replace=len(X) < k)
+    C = Xf[idx].astype(np.float32) + 0.05 * rng.standard_normal((k, X.shape[1])).astype(np.float32) \
+        * np.float32(np.abs(Xf).mean() + 1e-3)
+    return np.ascontiguousarray(C, dtype=np.float32)
+
+
+def _run(mm, X, C):
+    import torch
+    Xd = to_device(X)
+    Cd = torch.from_numpy(C).cuda()
+    lab, dist = mm.assign(Xd, Cd)
+    torch.cuda.synchronize()
+    return lab.cpu().numpy(), dist.cpu().numpy()
+
+
+CASES_F32 = [
+    # (generator, n, d, k): several tiles, ragged tails in n, k and d
+    ("tiny", 1000, 16, 64),
+    ("tiny", 3001, 16, 130),
+    ("embedding", 1000, 768, 257),
+    ("embedding", 700, 100, 300),
+    ("deep", 5000, 96, 1000),
+    ("sift", 2000, 128, 513),
+    ("tiny", 257, 5, 3),
+    ("tiny", 130, 33, 200),
+    ("tiny", 100, 1, 1),
+    ("tiny", 129, 7, 129),
+    ("sift", 300, 250, 17),
+]
+
+
+@pytest.mark.parametrize("gen,n,d,k", CASES_F32)
+def test_assign_fp32(mm, gen, n, d, k):
+    X = datagen.make(gen, n, d, seed=11)
+    C = _centroids(X, k, 5)
+    lab, dist = _run(mm, X, C)
+    olab, d1, d2 = oracle.assign(X, C)
+    check_labels(X, C, None, lab, olab, d1, d2, what=f"{gen} {n}x{d} k={k}")
+    check_dists(X, C, None, lab, dist, what=f"{gen} {n}x{d} k={k}")
+
+
+CASES_BF16 = [(2000, 128, 300), (1000, 64, 129), (777, 40, 50), (500, 37, 20), (300, 256, 1)]
+
+
+@pytest.mark.parametrize("n,d,k", CASES_BF16)
+def test_assign_bf16(mm, n, d, k):
+    X = datagen.large_host(n, d=d, m=64, seed=13)
+    C = _centroids(X, k, 6)
+    lab, dist = _run(mm, X, C)
+    Cs = oracle.bf16_round(C)                # bf16 data is searched with bf16 centroids
+    olab, d1, d2 = oracle.assign(X, Cs)
+    check_labels(X, Cs, None, lab, olab, d1, d2, what=f"bf16 {n}x{d} k={k}")
+    check_dists(X, Cs, None, lab, dist, what=f"bf16 {n}x{d} k={k}")
+
+
+def test_assign_ties_lowest_index(mm):
+    rng = np.random.default_rng(3)
+    X = rng.standard_normal((500, 24)).astype(np.float32)
+    base = rng.standard_normal((40, 24)).astype(np.float32)
+    C = np.concatenate([base, base, base[:7]])  # exact duplicates: the first copy must win
+    lab, _ = _run(mm, X, C)
+    olab, _, _ = oracle.assign(X, C)
+    assert np.array_equal(lab, olab)
+    assert lab.max() < 40
+
+
+def test_assign_exact_hits(mm):
+    """Rows equal to a centroid get that centroid and distance ~0."""
+    X = datagen.sift(n=600, d=128, seed=2)
+    C = np.ascontiguousarray(X[::7][:80])
+    lab, dist = _run(mm, X, C)
+    hit = np.arange(0, 600, 7)[:80]
+    assert np.array_equal(lab[hit], oracle.assign(X[hit], C)[0])
+    assert np.all(dist[hit] <= 1e-5 * 2 * np.einsum("ij,ij->i", X[hit], X[hit]))
+
+
+def test_assign_empty_and_single(mm):
+    import torch
+    X = torch.zeros((0, 8), device="cuda")
+    lab, dist = mm.assign(X, torch.zeros((3, 8), device="cuda"))
+    assert lab.numel() == 0
+    Xs = datagen.tiny(n=1, d=8)
+    C = _centroids(datagen.tiny(n=50, d=8), 5, 1)
+    lab, _ = _run(mm, Xs, C)
+    assert lab[0] == oracle.assign(Xs, C)[0][0]
+
+
+def test_assign_rejects_bad_args(mm):
+    import torch
+    with pytest.raises(mm.EmeansError):
+        mm.assign(torch.zeros((10, 4), device="cuda", dtype=torch.float64),
+                  torch.zeros((3, 4), device="cuda"))
+    with pytest.raises(mm.EmeansError):
+        mm.assign(torch.zeros((10, 4), device="cuda"), torch.zeros((3, 5), device="cuda"))
+
+
+@pytest.mark.parametrize("n", [1, 2, 10, 1000, 10007, 65536, 1_000_000])
+def test_batch_rows_bit_exact(mm, n):
+    seed = 1234
+    for pass_ in (0, 3):
+        count = min(n, 50_000)
+        start = (n - count) // 2
+        got = mm.batch_rows(n, seed, pass_, start, count).cpu().numpy()
+        want = oracle.perm_range(n, seed, oracle.STREAM_PERM, pass_, start, count)
+        assert np.array_equal(got, want)
+    if n <= 65536:
+        full = mm.batch_rows(n, seed, 1, 0, n).cpu().numpy()
+        assert np.array_equal(np.sort(full), np.arange(n))

@@ -1,0 +1,163 @@
+"""emeans_train on the GPU against the oracle.
+
+Lockstep: the oracle replays the GPU run step by step, checks every label the
+GPU produced against its own fp64 assignment on its own centroids, adopts
+them, and the two states are then compared (running counts bit for bit, the
+split log exactly, centroids to 1e-4 relative L2, final MSE to 1e-3).
+Free run: the two run independently from the same seed.
+"""
+import numpy as np
+import pytest
+
+import oracle
+from mini_means_amd import datagen
+
+from parity import lockstep, rel_l2, to_device
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def mm():
+    import torch
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import mini_means_amd
+    mini_means_amd.lib()
+    return mini_means_amd
+
+
+def _gpu_train(mm, X, k, T, seed, **o):
+    """mm.train with oracle-style options (unused_threshold: -1 default, 0 off)."""
+    import torch
+    ut = o.pop("unused_threshold", -1.0)
+    out = mm.train(to_device(X), k, T, seed, unused_threshold=None if ut < 0 else ut,
+                   trace=True, counts=True, split_log_cap=1 << 16, **o)
+    torch.cuda.synchronize()
+    return out
+
+
+# (name, generator, n, d, k, T, extra options)
+LOCKSTEP = [
+    ("tiny", "tiny", 10_000, 16, 64, 5.0, {}),
+    ("emb-small", "embedding", 12_000, 768, 256, 2.0, {}),
+    ("deep-small", "deep", 30_000, 96, 1024, 3.0, {}),
+    ("sift-small", "sift", 20_000, 128, 1024, 2.0, {}),
+    ("large-small", "large", 40_000, 128, 1024, 2.0, {}),
+    ("ragged", "tiny", 5_003, 37, 77, 1.5, dict(batch_size=700)),
+    ("no-revival", "deep", 8_000, 96, 300, 2.0, dict(unused_threshold=0.0)),
+    ("alpha1-lloyd", "tiny", 4_000, 16, 32, 1.0, dict(batch_size=4000, alpha0=1.0)),
+]
+
+
+@pytest.mark.parametrize("name,gen,n,d,k,T,o", LOCKSTEP, ids=[c[0] for c in LOCKSTEP])
+def test_train_lockstep(mm, name, gen, n, d, k, T, o):
+    seed = 1234
+    X = datagen.make(gen, n, d, seed=21)
+    out = _gpu_train(mm, X, k, T, seed, **dict(o))
+    res, summ = lockstep(X, out, k, T, seed, **o)
+    assert summ["steps"] == res.recipe["total_steps"]
+    assert out.stats["batch_size"] == res.recipe["batch_size"]
+    # running counts: same labels -> bit-identical fp32 recurrence
+    assert np.array_equal(out.counts.cpu().numpy(), res.N), "running counts differ"
+    # revivals: identical decisions
+    assert out.split_log == [tuple(s) for s in res.split_log]
+    assert out.stats["n_splits"] == len(res.split_log)
+    assert out.stats["dead_at_end"] == res.dead_at_end
+    # last-pass labels are the adopted trace
+    assert np.array_equal(out.labels.cpu().numpy(), res.labels)
+    tol = 1e-2 if X.dtype == np.uint16 else 1e-4
+    C = out.centroids.cpu().numpy()
+    err = rel_l2(C, res.centroids)
+    assert err <= tol, f"centroids rel L2 {err:.3e}"
+    m_gpu = oracle.mse(X, C)
+    m_ref = oracle.mse(X, res.centroids)
+    assert abs(m_gpu - m_ref) <= 1e-3 * m_ref
+    np.testing.assert_allclose(out.stats["obj"], res.obj, rtol=1e-4)
+
+
+FREERUN = [
+    ("tiny", "tiny", 10_000, 16, 64, 5.0),
+    ("deep-small", "deep", 20_000, 96, 512, 3.0),
+    ("emb-small", "embedding", 12_000, 768, 256, 2.0),
+]
+
+
+@pytest.mark.parametrize("name,gen,n,d,k,T", FREERUN, ids=[c[0] for c in FREERUN])
+def test_train_free_run(mm, name, gen, n, d, k, T):
+    seed = 1234
+    X = datagen.make(gen, n, d, seed=22)
+    Xh = datagen.make(gen, n // 2, d, seed=22, split=1)
+    out = _gpu_train(mm, X, k, T, seed)
+    res = oracle.train(X, k, T, seed)
+    C = out.centroids.cpu().numpy()
+    m_gpu, m_ref = oracle.mse(X, C), oracle.mse(X, res.centroids)
+    assert abs(m_gpu - m_ref) <= 1e-3 * m_ref, (m_gpu, m_ref)
+    h_gpu, h_ref = oracle.mse(Xh, C), oracle.mse(Xh, res.centroids)
+    assert abs(h_gpu - h_ref) <= 1e-3 * h_ref, (h_gpu, h_ref)
+    agree = np.mean(out.labels.cpu().numpy() == res.labels)
+    assert agree > 0.99
+    if agree == 1.0:
+        assert rel_l2(C, res.centroids) <= 1e-4
+
+
+def test_train_finalisation_identity(mm):
+    """Each returned centroid is the exact mean of the rows whose last-pass
+    label it is (README: the closing mean costs nothing extra)."""
+    X = datagen.deep(n=30_000, d=96, seed=5)
+    out = _gpu_train(mm, X, 700, 2.0, 99)
+    lab = out.labels.cpu().numpy()
+    C = out.centroids.cpu().numpy()
+    assert lab.min() >= 0
+    cnt = np.bincount(lab, minlength=700)
+    sums = np.zeros((700, 96))
+    np.add.at(sums, lab, X.astype(np.float64))
+    nz = cnt > 0
+    means = sums[nz] / cnt[nz, None]
+    assert rel_l2(C[nz], means) <= 1e-5
+
+
+def test_train_every_row_once_per_pass(mm):
+    X = datagen.tiny(n=3_000, d=16, seed=8)
+    out = _gpu_train(mm, X, 20, 3.0, 5, batch_size=256)
+    rc = oracle.recipe(3000, 16, 20, 3.0, batch_size=256)
+    for e in range(3):
+        rows = mm.batch_rows(3000, 5, e, 0, 3000).cpu().numpy()
+        assert np.array_equal(np.sort(rows), np.arange(3000))
+    assert out.trace.numel() == sum(rc["epoch_rows"])
+
+
+def test_train_no_finalize_returns_ema(mm):
+    X = datagen.tiny(n=4_000, d=16, seed=9)
+    out = _gpu_train(mm, X, 32, 2.0, 3, finalize=False)
+    res, _ = lockstep(X, out, 32, 2.0, 3, finalize=False)
+    assert rel_l2(out.centroids.cpu().numpy(), res.ema_centroids) <= 1e-4
+
+
+def test_train_k_equals_n_and_k1(mm):
+    X = datagen.tiny(n=300, d=16, seed=4)
+    out = _gpu_train(mm, X, 300, 1.0, 1, batch_size=300, alpha0=1.0, unused_threshold=0.0)
+    # one Lloyd step from all rows as centroids: each row is its own centroid
+    assert np.array_equal(np.sort(out.labels.cpu().numpy()), np.arange(300))
+    out1 = _gpu_train(mm, X, 1, 2.0, 1)
+    assert np.allclose(out1.centroids.cpu().numpy()[0], X.astype(np.float64).mean(0), atol=1e-5)
+
+
+def test_train_deterministic_labels(mm):
+    X = datagen.deep(n=20_000, d=96, seed=6)
+    a = _gpu_train(mm, X, 256, 2.0, 7)
+    b = _gpu_train(mm, X, 256, 2.0, 7)
+    # same seed: same batches; labels may only differ through fp32 sum order
+    assert np.mean(a.labels.cpu().numpy() == b.labels.cpu().numpy()) > 0.999
+    assert rel_l2(a.centroids.cpu().numpy(), b.centroids.cpu().numpy()) <= 1e-4
+
+
+def test_train_rejects_bad_args(mm):
+    import torch
+    X = torch.zeros((100, 8), device="cuda")
+    with pytest.raises(mm.EmeansError):
+        mm.train(X, 101)
+    with pytest.raises(mm.EmeansError):
+        mm.train(X, 10, T=0.0)
+    with pytest.raises(mm.EmeansError):
+        mm.train(X.double(), 10)
