@@ -1,0 +1,250 @@
+#!/usr/bin/env python3
+"""e-means training-step benchmark on one MI355X.
+
+    python bench.py [--steps K] [--warmup W] [--workload embedding]
+
+A step is one batch through the whole hot path: batch sampling, fused
+assignment, bucketing, per-cluster sums, EMA update (and the revival check
+every fifth step). The timed region is one emeans_train call that runs
+exactly K steps of the workload's schedule (K = all steps of the 5-pass run
+by default), with the data resident in HBM; a separate run with event
+profiling gives each kernel class's device time. Prints one JSON line.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, HERE)
+
+METRIC = "assign TFLOP/s (% MFMA peak) + s to Lloyd-25 MSE, 1M×768 k=4096"
+MFMA_PEAK_TFLOPS = {"f32": 157.3, "bf16": 2516.6}   # MI355X dense MFMA
+HBM_PEAK_GBS = 8000.0
+
+DESCR = {
+    "tiny": "tiny: 10k x 16 fp32, 64-component mixture (sigma 0.3), k=64, T=5",
+    "embedding": "embedding-like: 1M x 768 fp32, unit-normalised 4096-component mixture, "
+                 "Zipf(1.1) weights, sigma 0.5; k=4096, T=5",
+    "deep": "deep-descriptor-like: 1M x 96 fp32, unit-normalised rank-32 Gaussian + noise 0.1; "
+            "k=16384, T=5",
+    "sift": "local-descriptor-like: 1M x 128 fp32 integers in [0,255], 30% zeros; k=16384, T=5",
+    "large": "large: 100M x 128 bf16, unit-normalised 65536-component mixture (sigma 0.4); "
+             "k=65536, T=3",
+}
+
+
+def log(msg: str) -> None:
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def batch_sizes(rc: dict) -> list:
+    out = []
+    for rows_e, steps in zip(rc["epoch_rows"], rc["steps_per_pass"]):
+        out += [min(rc["batch_size"], rows_e - s * rc["batch_size"]) for s in range(steps)]
+    return out
+
+
+def make_data(name: str, W: dict, torch):
+    from mini_means_amd import datagen
+    t0 = time.time()
+    if W["dtype"] == "bf16":
+        X = datagen.large_device(n=W["n"], d=W["d"])
+        Xh = datagen.large_device(n=W["heldout"], d=W["d"], split=1)
+        Xhost = None
+    else:
+        Xhost = datagen.make(W["gen"], W["n"], W["d"])
+        X = torch.from_numpy(Xhost).cuda()
+        Xh = torch.from_numpy(datagen.make(W["gen"], W["heldout"], W["d"], split=1)).cuda()
+    torch.cuda.synchronize()
+    log(f"data {tuple(X.shape)} {X.dtype} + held-out {tuple(Xh.shape)} in {time.time() - t0:.1f}s")
+    return X, Xh, Xhost
+
+
+def heldout_mse(mm, Xh, C, torch) -> float:
+    _, dist = mm.assign(Xh, C)
+    return float(dist.double().mean().item())
+
+
+def time_to_target(mm, X, Xh, k, target, seeds, Ts, torch) -> dict:
+    """Smallest median wall-clock among pass counts whose finalised held-out MSE
+    reaches the Lloyd-25 held-out MSE (median over training seeds)."""
+    import statistics
+    rows = []
+    best = None
+    for T in Ts:
+        walls, mses = [], []
+        for s in seeds:
+            torch.cuda.synchronize()
+            t0 = time.perf_counter()
+            out = mm.train(X, k, T, s, capture_labels=True)
+            torch.cuda.synchronize()
+            walls.append(time.perf_counter() - t0)
+            mses.append(heldout_mse(mm, Xh, out.centroids, torch))
+        w, m = statistics.median(walls), statistics.median(mses)
+        rows.append(dict(T=T, seconds=round(w, 4), heldout_mse=m))
+        log(f"T={T}: {w:.3f}s held-out MSE {m:.6f} (target {target:.6f})")
+        if m <= target and (best is None or w < best["seconds"]):
+            best = dict(T=T, seconds=w)
+    return dict(target_heldout_mse=target, sweep=rows,
+                seconds=None if best is None else round(best["seconds"], 4),
+                T=None if best is None else best["T"])
+
+
+def cpu_baseline(Xhost, C, k, d, budget_s: float) -> dict:
+    """The CPU oracle's assignment (fp64 brute force, OpenMP over rows) on a
+    bounded sample of the workload's rows, in the metric's unit."""
+    import numpy as np
+    import oracle
+    rng = np.random.default_rng(0)
+    cores = int(os.environ.get("OMP_NUM_THREADS", "0")) or len(os.sched_getaffinity(0))
+    probe = Xhost[rng.choice(len(Xhost), 128, replace=False)]
+    t0 = time.perf_counter()
+    oracle.assign(probe, C, nthreads=cores)
+    per_row = (time.perf_counter() - t0) / 128
+    rows = int(max(256, min(len(Xhost), budget_s / max(per_row, 1e-9))))
+    sample = Xhost[rng.choice(len(Xhost), rows, replace=False)]
+    t0 = time.perf_counter()
+    oracle.assign(sample, C, nthreads=cores)
+    dt = time.perf_counter() - t0
+    tflops = 2.0 * rows * k * d / dt / 1e12
+    return dict(value=round(tflops, 6), unit="TFLOP/s", cores=cores, kind="oracle",
+                sample=f"{rows} random training rows x all {k} centroids (fp64 brute force, "
+                       f"{dt:.1f}s)")
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=0, help="timed steps (0 = the whole run)")
+    ap.add_argument("--warmup", type=int, default=16)
+    ap.add_argument("--workload", default="embedding")
+    ap.add_argument("--seed", type=int, default=1234)
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--no-ttt", action="store_true", help="skip the time-to-target sweep")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--ttt-seeds", type=int, default=3)
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py runs on one GPU only: this build has no multi-GPU path "
+              f"(asked for --gpus {args.gpus}, WORLD_SIZE {world}).", file=sys.stderr)
+        return 2
+
+    import torch
+
+    import mini_means_amd as mm
+    from mini_means_amd import datagen
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        return 2
+    mm.lib()
+    W = datagen.WORKLOADS[args.workload]
+    n, d, k, T = W["n"], W["d"], W["k"], W["T"]
+    rc = mm.recipe(n, d, k, T)
+    S = rc["total_steps"]
+    K = args.steps if args.steps > 0 else S
+    K = min(K, S)
+    Wm = min(args.warmup, S)
+    sizes = batch_sizes(rc)[:K]
+    es = 2 if W["dtype"] == "bf16" else 4
+    flops = float(sum(2.0 * b * k * d for b in sizes))
+
+    X, Xh, Xhost = make_data(args.workload, W, torch)
+
+    # warm-up (untimed)
+    if Wm > 0:
+        mm.train(X, k, T, args.seed, max_steps=Wm)
+        torch.cuda.synchronize()
+
+    # timed: exactly K steps of the schedule
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    out = mm.train(X, k, T, args.seed, max_steps=K)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    value = flops / wall / 1e12
+    log(f"timed {K} steps in {wall:.4f}s -> {value:.2f} assign TFLOP/s (whole step)")
+
+    # profiled run: device time per kernel class (HIP events on the launch stream)
+    prof = mm.train(X, k, T, args.seed, max_steps=K, profile=True).stats
+    torch.cuda.synchronize()
+    a_ms = prof["ms_assign"]
+    assign_tflops = flops / (a_ms / 1e3) / 1e12 if a_ms > 0 else None
+    peak = MFMA_PEAK_TFLOPS[W["dtype"]]
+    group_bytes = float(sum(b * d * es + 4 * b + 4 * k * d for b in sizes))
+    update_bytes = float(K * (4 * 4 * k * d))   # read s, S, C; write S, C (+ counts, small)
+    g_ms = prof["ms_group"]
+    u_ms = prof["ms_update"]
+    log(f"device ms: assign {a_ms:.2f} bucket {prof['ms_bucket']:.2f} group {g_ms:.2f} "
+        f"update {u_ms:.2f} revive {prof['ms_revive']:.2f} sample {prof['ms_sample']:.2f}")
+
+    line = {
+        "metric": METRIC,
+        "value": round(value, 3),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": Wm,
+        "ms_per_step": round(wall * 1e3 / K, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": W["dtype"],
+        "data": "synthetic",
+        "config": {"workload": DESCR[args.workload], "n": n, "d": d, "k": k, "T": T,
+                   "batch": rc["batch_size"], "alpha0": round(rc["alpha0"], 6),
+                   "steps_per_run": S},
+        "mfma_peak_frac": round(value / peak, 4),
+        "roofline": {
+            "kernel": "assign_kernel (fused MFMA assign)",
+            "bound": "mfma",
+            "achieved": round(assign_tflops, 3) if assign_tflops else None,
+            "peak": peak,
+            "unit": "TFLOP/s",
+            "frac": round(assign_tflops / peak, 4) if assign_tflops else None,
+            "traffic": None,
+            "launches": K,
+            "avg_launch_ms": round(a_ms / K, 4),
+        },
+        "grouping": {
+            "group_GBs": round(group_bytes / (g_ms / 1e3) / 1e9, 1) if g_ms > 0 else None,
+            "update_GBs": round(update_bytes / (u_ms / 1e3) / 1e9, 1) if u_ms > 0 else None,
+            "hbm_peak_GBs": HBM_PEAK_GBS,
+            "group_avg_launch_ms": round(g_ms / K, 4),
+            "update_avg_launch_ms": round(u_ms / K, 4),
+        },
+        "device_ms": {c: round(prof[f"ms_{c}"], 3) for c in
+                      ("assign", "bucket", "group", "update", "revive", "sample")},
+    }
+
+    if not args.no_ttt and args.workload == "embedding":
+        path = os.path.join(HERE, "tests", "golden", f"lloyd25_{args.workload}.json")
+        if os.path.exists(path):
+            with open(path) as f:
+                target = json.load(f)["heldout_mse"]
+            seeds = [args.seed + i for i in range(args.ttt_seeds)]
+            ttt = time_to_target(mm, X, Xh, k, target, seeds, [1.0, 1.5, 2.0, 2.5, 3.0, 5.0],
+                                 torch)
+            line["s_to_lloyd25"] = ttt["seconds"]
+            line["time_to_target"] = ttt
+        else:
+            line["s_to_lloyd25"] = None
+            log(f"no Lloyd-25 target at {path}")
+
+    if not args.no_cpu and Xhost is not None:
+        C = out.centroids.cpu().numpy()
+        line["cpu_baseline"] = cpu_baseline(Xhost, C, k, d, args.cpu_seconds)
+        log(f"cpu baseline {line['cpu_baseline']}")
+
+    print(json.dumps(line), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -80,6 +80,9 @@ typedef struct emeans_opts {
   float* out_counts;          /* device, k: running counts N at the end */
   int32_t* split_log;         /* host, 3 * split_log_cap: (step, dead j, donor i) */
   int64_t split_log_cap;
+  int64_t max_steps;          /* 0: all steps; > 0: stop after this many update steps
+                                 (the schedule stays that of the full run); the
+                                 closing mean is taken only if the last pass began */
 } emeans_opts;
 
 /* Recipe and statistics of a run (README "Settings and results": recipe, obj,
@@ -102,7 +105,10 @@ typedef struct emeans_stats {
   double imbalance[EMEANS_MAX_PASSES]; /* k * sum n_j^2 / (sum n_j)^2 over the pass */
   int64_t splits[EMEANS_MAX_PASSES];   /* revivals during the pass */
   double ms_total;                     /* emeans_train wall clock */
-  double ms_assign, ms_group, ms_update, ms_revive;  /* with opts->profile */
+  /* with opts->profile: summed device time of each kernel class, from HIP
+     events recorded on opts->stream around the launches */
+  double ms_assign, ms_bucket, ms_group, ms_update, ms_revive, ms_sample;
+  int64_t steps_run;                   /* update steps executed */
 } emeans_stats;
 
 /* Scaling-law recipe for (n, d, k, T) and the given options; host only, no

@@ -35,7 +35,7 @@ class Opts(ctypes.Structure):
         ("dtype", c_i32), ("batch_law", c_i32), ("batch_size", c_i64), ("alpha0", c_dbl),
         ("unused_threshold", c_dbl), ("no_finalize", c_i32), ("profile", c_i32),
         ("stream", c_vp), ("trace_labels", c_vp), ("out_counts", c_vp), ("split_log", c_vp),
-        ("split_log_cap", c_i64),
+        ("split_log_cap", c_i64), ("max_steps", c_i64),
     ]
 
 
@@ -47,8 +47,9 @@ class Stats(ctypes.Structure):
         ("rows_per_pass", c_i64 * MAX_PASSES), ("steps_per_pass", c_i64 * MAX_PASSES),
         ("obj", c_dbl * MAX_PASSES), ("imbalance", c_dbl * MAX_PASSES),
         ("splits", c_i64 * MAX_PASSES),
-        ("ms_total", c_dbl), ("ms_assign", c_dbl), ("ms_group", c_dbl), ("ms_update", c_dbl),
-        ("ms_revive", c_dbl),
+        ("ms_total", c_dbl), ("ms_assign", c_dbl), ("ms_bucket", c_dbl), ("ms_group", c_dbl),
+        ("ms_update", c_dbl),
+        ("ms_revive", c_dbl), ("ms_sample", c_dbl), ("steps_run", c_i64),
     ]
 
 
@@ -124,8 +125,9 @@ def _stats_dict(s: Stats) -> dict:
                 steps_per_pass=list(s.steps_per_pass[:P]), unused_threshold=s.unused_threshold,
                 obj=list(s.obj[:P]), imbalance=list(s.imbalance[:P]), splits=list(s.splits[:P]),
                 n_splits=s.n_splits, dead_at_end=s.dead_at_end, ms_total=s.ms_total,
-                ms_assign=s.ms_assign, ms_group=s.ms_group, ms_update=s.ms_update,
-                ms_revive=s.ms_revive)
+                ms_assign=s.ms_assign, ms_bucket=s.ms_bucket, ms_group=s.ms_group,
+                ms_update=s.ms_update,
+                ms_revive=s.ms_revive, ms_sample=s.ms_sample, steps_run=s.steps_run)
 
 
 def recipe(n: int, d: int, k: int, T: float = 5.0, **kw) -> dict:
@@ -171,7 +173,8 @@ class TrainOutput:
 def train(X, k: int, T: float = 5.0, seed: int = 1234, *, batch_law="auto", batch_size: int = 0,
           alpha0: float = 0.0, unused_threshold=None, finalize: bool = True,
           capture_labels: bool = True, trace: bool = False, counts: bool = False,
-          split_log_cap: int = 0, profile: bool = False, stream=None) -> TrainOutput:
+          split_log_cap: int = 0, profile: bool = False, max_steps: int = 0,
+          stream=None) -> TrainOutput:
     import torch
     _require_device(X)
     n, d = X.shape
@@ -193,6 +196,7 @@ def train(X, k: int, T: float = 5.0, seed: int = 1234, *, batch_law="auto", batc
         if log is not None:
             o.split_log = ctypes.cast(log, c_vp)
             o.split_log_cap = split_log_cap
+        o.max_steps = int(max_steps)
         s = Stats()
         _check(lib().emeans_train(X.data_ptr(), n, d, int(k), float(T), int(seed) & (2**64 - 1),
                                   C.data_ptr(), labels.data_ptr() if labels is not None else None,

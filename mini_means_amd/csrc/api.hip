@@ -38,7 +38,7 @@ int fail(int code, const char* fmt, ...) {
     }                                                                                     \
   } while (0)
 
-constexpr int kGroupRows = 256;  // rows per grouping work item
+constexpr int kGroupRows = 64;   // rows per grouping work item
 constexpr int kReviveEvery = 5;  // blog: dead clusters are checked every five batches
 
 struct Recipe {
@@ -277,15 +277,21 @@ int emeans_train(const void* X, int64_t n, int32_t d, int32_t k, double T, uint6
   uint32_t *rows = nullptr, *order = nullptr;
   int32_t *blab = nullptr, *counts = nullptr, *cursor = nullptr, *off = nullptr,
           *item_off = nullptr, *pass_counts = nullptr, *flags = nullptr, *dead = nullptr,
-          *dlog = nullptr;
+          *dlog = nullptr, *pair_i = nullptr, *rv_pos = nullptr, *rv_head = nullptr,
+          *rv_cbase = nullptr, *rv_clen = nullptr, *rv_heads = nullptr, *rv_list = nullptr,
+          *rv_nheads = nullptr;
+  double* rv_u = nullptr;
   float *bdist = nullptr, *s_acc = nullptr, *S = nullptr, *N = nullptr, *LS = nullptr,
-        *bias = nullptr;
+        *bias = nullptr, *n0 = nullptr, *pair_n = nullptr;
   uint16_t* chat = nullptr;
   // per pass: [0, P) sum of distances, [P, 3P) sum n^2 and sum n, [3P, 4P) splits (int64)
   double* dstat = nullptr;
   int64_t* counters = nullptr;
-  std::vector<hipEvent_t> evs;
-  std::vector<int> ev_class;
+  struct Span {
+    int cls;
+    hipEvent_t a, b;
+  };
+  std::vector<Span> spans;
   double host_stat[4 * EMEANS_MAX_PASSES];
   int64_t host_counters[4] = {0, 0, 0, 0};
   int64_t trace_off = 0;
@@ -303,6 +309,17 @@ int emeans_train(const void* X, int64_t n, int32_t d, int32_t k, double T, uint6
   ar.want(&pass_counts, (size_t)k);
   ar.want(&flags, (size_t)k);
   ar.want(&dead, (size_t)k);
+  ar.want(&n0, (size_t)k);
+  ar.want(&pair_i, (size_t)k);
+  ar.want(&pair_n, (size_t)k);
+  ar.want(&rv_u, (size_t)k);
+  ar.want(&rv_pos, (size_t)k);
+  ar.want(&rv_head, (size_t)k);
+  ar.want(&rv_cbase, (size_t)k);
+  ar.want(&rv_clen, (size_t)k);
+  ar.want(&rv_heads, (size_t)k);
+  ar.want(&rv_list, (size_t)k);
+  ar.want(&rv_nheads, 1);
   ar.want(&s_acc, kd);
   ar.want(&S, kd);
   ar.want(&N, (size_t)k);
@@ -313,15 +330,23 @@ int emeans_train(const void* X, int64_t n, int32_t d, int32_t k, double T, uint6
   ar.want(&counters, 4);
   if (log_cap > 0) ar.want(&dlog, (size_t)3 * log_cap);
 
-  auto mark = [&](int cls) -> hipError_t {
-    if (!profile) return hipSuccess;
-    hipEvent_t e;
-    hipError_t er = hipEventCreate(&e);
+  // Device time of a kernel class: events recorded on the launch stream around it.
+  enum { kAssign = 0, kBucket, kGroup, kUpdate, kRevive, kSample, kClasses };
+  auto timed = [&](int cls, auto&& launch) -> hipError_t {
+    if (!profile) return launch();
+    Span sp{cls, nullptr, nullptr};
+    hipError_t er = hipEventCreate(&sp.a);
+    if (er == hipSuccess) er = hipEventCreate(&sp.b);
     if (er != hipSuccess) return er;
-    evs.push_back(e);
-    ev_class.push_back(cls);
-    return hipEventRecord(e, st);
+    spans.push_back(sp);
+    if ((er = hipEventRecord(sp.a, st)) != hipSuccess) return er;
+    if ((er = launch()) != hipSuccess) return er;
+    return hipEventRecord(sp.b, st);
   };
+  const int64_t max_steps = opts ? opts->max_steps : 0;
+  if (max_steps < 0) return fail(EMEANS_EINVAL, "max_steps must be >= 0");
+  const int64_t run_steps = (max_steps > 0 && max_steps < r.S) ? max_steps : r.S;
+  bool last_pass_begun = false;
 
   HIP_TRY(ar.alloc(&base, st));
   // zero the statistics and every accumulator the step loop expects at zero
@@ -340,37 +365,43 @@ int emeans_train(const void* X, int64_t n, int32_t d, int32_t k, double T, uint6
                                 centroids, st));
   HIP_TRY(launch_prep(centroids, k, d, bias, chat, st));
 
-  for (int e = 0; e < r.npass; ++e) {
+  for (int e = 0; e < r.npass && t < run_steps; ++e) {
     const bool last = e == r.npass - 1;
+    last_pass_begun = last;
     const PermKey pk = make_perm_key((uint64_t)n, seed, kStreamPerm, (uint64_t)e);
-    for (int64_t s = 0; s < r.steps[e]; ++s, ++t) {
+    for (int64_t s = 0; s < r.steps[e] && t < run_steps; ++s, ++t) {
       const int64_t rem = r.rows[e] - s * B;
       const int nb = (int)(rem < B ? rem : B);
       const float a = alpha_at(r.alpha0, t, r.S);
       const float b = 1.0f - a;
-      HIP_TRY(mark(0));
-      HIP_TRY(launch_sample_rows(pk, (uint64_t)(s * B), nb, rows, st));
-      HIP_TRY(launch_assign(bf16, X, d, rows, nb, bf16 ? (const void*)chat : (const void*)centroids,
-                            bias, k, blab, bdist, counts, dstat + e, st));
+      HIP_TRY(timed(kSample, [&] { return launch_sample_rows(pk, (uint64_t)(s * B), nb, rows, st); }));
+      HIP_TRY(timed(kAssign, [&] {
+        return launch_assign(bf16, X, d, rows, nb, bf16 ? (const void*)chat : (const void*)centroids,
+                             bias, k, blab, bdist, counts, dstat + e, st);
+      }));
       if (opts && opts->trace_labels) {
         HIP_TRY(hipMemcpyAsync(opts->trace_labels + trace_off, blab, sizeof(int32_t) * nb,
                                hipMemcpyDeviceToDevice, st));
         trace_off += nb;
       }
-      HIP_TRY(mark(1));
-      HIP_TRY(launch_scan(counts, k, kGroupRows, off, cursor, item_off, st));
-      HIP_TRY(launch_scatter(blab, rows, nb, cursor, order, (last && labels) ? labels : nullptr, st));
-      HIP_TRY(launch_group(bf16, X, d, order, off, item_off, k, kGroupRows, nb, s_acc, st));
-      HIP_TRY(mark(2));
-      HIP_TRY(launch_ema(k, d, a, b, counts, s_acc, N, S, centroids, bias, chat, pass_counts,
-                         last ? LS : nullptr, st));
-      HIP_TRY(mark(3));
+      HIP_TRY(timed(kBucket, [&] {
+        hipError_t er = launch_scan(counts, k, kGroupRows, off, cursor, item_off, st);
+        if (er != hipSuccess) return er;
+        return launch_scatter(blab, rows, nb, cursor, order, (last && labels) ? labels : nullptr, st);
+      }));
+      HIP_TRY(timed(kGroup, [&] {
+        return launch_group(bf16, X, d, order, off, item_off, k, kGroupRows, nb, s_acc, st);
+      }));
+      HIP_TRY(timed(kUpdate, [&] {
+        return launch_ema(k, d, a, b, counts, s_acc, N, S, centroids, bias, chat, pass_counts,
+                          last ? LS : nullptr, st);
+      }));
       if (r.thr > 0.0 && (t + 1) % kReviveEvery == 0) {
         ReviveArgs ra{k, d, N, S, centroids, bias, chat, r.thr, seed, (uint64_t)t, flags, dead,
-                      counters, dlog, log_cap, 0};
-        HIP_TRY(launch_revive(ra, st));
+                      n0, rv_u, pair_i, pair_n, rv_pos, rv_head, rv_cbase, rv_clen, rv_heads,
+                      rv_list, rv_nheads, counters, dlog, log_cap, 0};
+        HIP_TRY(timed(kRevive, [&] { return launch_revive(ra, st); }));
       }
-      HIP_TRY(mark(4));
     }
     HIP_TRY(launch_pass_stats(pass_counts, k, dstat + EMEANS_MAX_PASSES + 2 * e, last ? 0 : 1, st));
     // per-pass split count: snapshot counters[3] then reset it
@@ -381,12 +412,14 @@ int emeans_train(const void* X, int64_t n, int32_t d, int32_t k, double T, uint6
 
   if (r.thr > 0.0) {
     ReviveArgs ra{k, d, N, S, centroids, bias, chat, r.thr, seed, (uint64_t)t, flags, dead,
-                  counters, nullptr, 0, 1};
+                  n0, rv_u, pair_i, pair_n, rv_pos, rv_head, rv_cbase, rv_clen, rv_heads,
+                  rv_list, rv_nheads, counters, nullptr, 0, 1};
     HIP_TRY(launch_revive(ra, st));
   }
   if (opts && opts->out_counts)
     HIP_TRY(hipMemcpyAsync(opts->out_counts, N, sizeof(float) * k, hipMemcpyDeviceToDevice, st));
-  if (!(opts && opts->no_finalize)) HIP_TRY(launch_finalize(k, d, pass_counts, LS, centroids, st));
+  if (!(opts && opts->no_finalize) && last_pass_begun)
+    HIP_TRY(launch_finalize(k, d, pass_counts, LS, centroids, st));
 
   HIP_TRY(hipMemcpyAsync(host_stat, dstat, sizeof host_stat, hipMemcpyDeviceToHost, st));
   HIP_TRY(hipMemcpyAsync(host_counters, counters, sizeof host_counters, hipMemcpyDeviceToHost, st));
@@ -408,23 +441,29 @@ int emeans_train(const void* X, int64_t n, int32_t d, int32_t k, double T, uint6
     stats->n_splits = host_counters[0];
     stats->n_logged = host_counters[1] < log_cap ? host_counters[1] : log_cap;
     stats->dead_at_end = r.thr > 0.0 ? host_counters[2] : 0;
-    if (profile && !evs.empty()) {
-      double cls_ms[5] = {0, 0, 0, 0, 0};
-      for (size_t i = 0; i + 1 < evs.size(); ++i) {
+    if (profile) {
+      double cls_ms[kClasses] = {};
+      for (const Span& sp : spans) {
         float ms = 0.0f;
-        if (hipEventElapsedTime(&ms, evs[i], evs[i + 1]) == hipSuccess) cls_ms[ev_class[i]] += ms;
+        if (hipEventElapsedTime(&ms, sp.a, sp.b) == hipSuccess) cls_ms[sp.cls] += ms;
       }
-      stats->ms_assign = cls_ms[0];
-      stats->ms_group = cls_ms[1];
-      stats->ms_update = cls_ms[2];
-      stats->ms_revive = cls_ms[3];
+      stats->ms_assign = cls_ms[kAssign];
+      stats->ms_bucket = cls_ms[kBucket];
+      stats->ms_group = cls_ms[kGroup];
+      stats->ms_update = cls_ms[kUpdate];
+      stats->ms_revive = cls_ms[kRevive];
+      stats->ms_sample = cls_ms[kSample];
     }
+    stats->steps_run = t;
     stats->ms_total =
         std::chrono::duration<double, std::milli>(std::chrono::steady_clock::now() - t_start).count();
   }
 
 done:
-  for (auto e : evs) (void)hipEventDestroy(e);
+  for (const Span& sp : spans) {
+    (void)hipEventDestroy(sp.a);
+    (void)hipEventDestroy(sp.b);
+  }
   if (base) {
     const hipError_t e = hipFreeAsync(base, st);
     if (e != hipSuccess && rc == EMEANS_OK)

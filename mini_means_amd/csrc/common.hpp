@@ -168,4 +168,35 @@ __device__ __forceinline__ T block_sum(T v, T* tmp) {
   return t;
 }
 
+// ---------------------------------------------------------------------------
+// fp64 wave scan on DPP lane moves (no LDS round trip): row shifts 1, 2, 4, 8
+// scan each row of 16 lanes, then row broadcasts 15 and 31 carry the row
+// totals across the wave. Lanes outside a move's source range add zero.
+// ---------------------------------------------------------------------------
+template <int CTRL, int ROWMASK>
+__device__ __forceinline__ double dpp_move_f64(double v) {
+  const uint64_t b = (uint64_t)__double_as_longlong(v);
+  int lo = (int)(uint32_t)b, hi = (int)(uint32_t)(b >> 32);
+  lo = __builtin_amdgcn_update_dpp(0, lo, CTRL, ROWMASK, 0xF, false);
+  hi = __builtin_amdgcn_update_dpp(0, hi, CTRL, ROWMASK, 0xF, false);
+  return __longlong_as_double((long long)(((uint64_t)(uint32_t)hi << 32) | (uint32_t)lo));
+}
+
+__device__ __forceinline__ double wave_scan_f64(double v) {
+  v += dpp_move_f64<0x111, 0xF>(v);  // row_shr:1
+  v += dpp_move_f64<0x112, 0xF>(v);  // row_shr:2
+  v += dpp_move_f64<0x114, 0xF>(v);  // row_shr:4
+  v += dpp_move_f64<0x118, 0xF>(v);  // row_shr:8
+  v += dpp_move_f64<0x142, 0xA>(v);  // row_bcast:15 into rows 1 and 3
+  v += dpp_move_f64<0x143, 0xC>(v);  // row_bcast:31 into rows 2 and 3
+  return v;
+}
+
+__device__ __forceinline__ double readlane_f64(double v, int lane) {
+  const uint64_t b = (uint64_t)__double_as_longlong(v);
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)b, lane);
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(b >> 32), lane);
+  return __longlong_as_double((long long)(((uint64_t)hi << 32) | lo));
+}
+
 }  // namespace emk

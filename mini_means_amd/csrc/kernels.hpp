@@ -61,13 +61,27 @@ struct ReviveArgs {
   uint16_t* Chat;
   double thr;
   uint64_t seed, step;
-  int32_t* flags;     // k scratch
-  int32_t* dead;      // k scratch
+  // k-sized scratch
+  int32_t* flags;     // 1 = under the threshold at this check
+  int32_t* dead;      // dead clusters in index order (q-th dead = dead[q])
+  float* n0;          // running counts at the check
+  double* udraw;      // the q-th dead cluster's uniform draw
+  int32_t* pair_i;    // donor of the q-th dead cluster
+  float* pair_n;      // donor's count right after that split
+  int32_t* pos;       // place of split q in its donor's chain
+  int32_t* head_of;   // first split of a donor
+  int32_t* cbase;     // start of a chain (indexed by its first split)
+  int32_t* clen;      // length of a chain (indexed by its first split)
+  int32_t* heads;     // first splits, compacted
+  int32_t* list;      // splits grouped by chain, in chain order
+  int32_t* nheads;    // [1]: number of chains
   int64_t* counters;  // [0] splits, [1] logged, [2] dead count, [3] splits this pass
   int32_t* log;       // 3 * log_cap
   int64_t log_cap;
   int count_only;
 };
+// Dead-cluster check and donor draws (one workgroup), then the splits of the
+// running sums, one wave per donor chain.
 hipError_t launch_revive(const ReviveArgs& a, hipStream_t st);
 
 // sums[0] += sum n_j^2, sums[1] += sum n_j over pass_counts; zeroes them if `reset`.

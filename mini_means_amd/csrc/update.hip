@@ -107,9 +107,11 @@ __global__ void scatter_kernel(const int32_t* labels, const uint32_t* rows, int 
 
 // One workgroup per work item: up to R rows of one cluster (rows taken from
 // the bucketed order). Columns are 16-byte chunks when the rows allow it.
-// Threads are arranged as rpar row groups x ncol columns; row groups are
-// folded through LDS; a cluster held by a single item is stored, otherwise
-// its partial sums are added atomically.
+// Threads are arranged as rpar row groups x ncol columns (blockDim.x =
+// rpar * ncol rounded up to whole waves, at most 256); row groups are folded
+// through LDS; a cluster held by a single item is stored, otherwise its
+// partial sums are added atomically. Eight row loads are kept in flight per
+// thread.
 template <bool BF16, bool VEC>
 __global__ __launch_bounds__(256) void group_kernel(const unsigned char* __restrict__ X, int d,
                                                     const uint32_t* __restrict__ order,
@@ -118,6 +120,7 @@ __global__ __launch_bounds__(256) void group_kernel(const unsigned char* __restr
                                                     int R, float* __restrict__ s_acc) {
   constexpr int ES = BF16 ? 2 : 4;
   constexpr int EPV = VEC ? 16 / ES : 1;  // elements per column unit
+  constexpr int U = 8;                    // rows in flight per thread
   __shared__ float red[256 * EPV];
   const int w = blockIdx.x;
   const int nitems = item_off[k];
@@ -133,6 +136,7 @@ __global__ __launch_bounds__(256) void group_kernel(const unsigned char* __restr
   const int end = min(off[j + 1], beg + R);
   const bool single = (item_off[j + 1] - item_off[j]) == 1;
   const int tid = threadIdx.x;
+  const int NT = blockDim.x;
   const int ncol = d / EPV;
   const size_t rowbytes = (size_t)d * ES;
   float* dst = s_acc + (size_t)j * d;
@@ -160,6 +164,29 @@ __global__ __launch_bounds__(256) void group_kernel(const unsigned char* __restr
     }
   };
 
+  // sum rows beg+first, beg+first+stride, ... < end of column col into acc
+  auto sum_rows = [&](int first, int stride, int col, float* acc) {
+    int pos = beg + first;
+    for (; pos + (U - 1) * stride < end; pos += U * stride) {
+      uint32_t rr[U];
+#pragma unroll
+      for (int u = 0; u < U; ++u) rr[u] = order[pos + u * stride];
+      float v[U][EPV];
+#pragma unroll
+      for (int u = 0; u < U; ++u) load_unit(rr[u], col, v[u]);
+#pragma unroll
+      for (int u = 0; u < U; ++u)
+#pragma unroll
+        for (int e = 0; e < EPV; ++e) acc[e] += v[u][e];
+    }
+    for (; pos < end; pos += stride) {
+      float v[EPV];
+      load_unit(order[pos], col, v);
+#pragma unroll
+      for (int e = 0; e < EPV; ++e) acc[e] += v[e];
+    }
+  };
+
   auto write_out = [&](int col, const float* acc) {
 #pragma unroll
     for (int e = 0; e < EPV; ++e) {
@@ -170,59 +197,31 @@ __global__ __launch_bounds__(256) void group_kernel(const unsigned char* __restr
     }
   };
 
-  if (ncol >= 256) {
-    for (int col = tid; col < ncol; col += 256) {
+  if (ncol >= NT) {
+    for (int col = tid; col < ncol; col += NT) {
       float acc[EPV];
 #pragma unroll
       for (int e = 0; e < EPV; ++e) acc[e] = 0.0f;
-      int pos = beg;
-      for (; pos + 4 <= end; pos += 4) {
-        float v0[EPV], v1[EPV], v2[EPV], v3[EPV];
-        load_unit(order[pos], col, v0);
-        load_unit(order[pos + 1], col, v1);
-        load_unit(order[pos + 2], col, v2);
-        load_unit(order[pos + 3], col, v3);
-#pragma unroll
-        for (int e = 0; e < EPV; ++e) acc[e] += v0[e] + v1[e] + v2[e] + v3[e];
-      }
-      for (; pos < end; ++pos) {
-        float v[EPV];
-        load_unit(order[pos], col, v);
-#pragma unroll
-        for (int e = 0; e < EPV; ++e) acc[e] += v[e];
-      }
+      sum_rows(0, 1, col, acc);
       write_out(col, acc);
     }
     return;
   }
 
-  const int rpar = 256 / ncol;
+  const int rpar = NT / ncol;
   const int rg = tid / ncol;
   const int col = tid - rg * ncol;
   float acc[EPV];
 #pragma unroll
   for (int e = 0; e < EPV; ++e) acc[e] = 0.0f;
   if (rg < rpar) {
-    int pos = beg + rg;
-    for (; pos + 3 * rpar < end; pos += 4 * rpar) {
-      float v0[EPV], v1[EPV], v2[EPV], v3[EPV];
-      load_unit(order[pos], col, v0);
-      load_unit(order[pos + rpar], col, v1);
-      load_unit(order[pos + 2 * rpar], col, v2);
-      load_unit(order[pos + 3 * rpar], col, v3);
+    sum_rows(rg, rpar, col, acc);
+    if (rpar > 1) {
 #pragma unroll
-      for (int e = 0; e < EPV; ++e) acc[e] += v0[e] + v1[e] + v2[e] + v3[e];
+      for (int e = 0; e < EPV; ++e) red[(rg * ncol + col) * EPV + e] = acc[e];
     }
-    for (; pos < end; pos += rpar) {
-      float v[EPV];
-      load_unit(order[pos], col, v);
-#pragma unroll
-      for (int e = 0; e < EPV; ++e) acc[e] += v[e];
-    }
-#pragma unroll
-    for (int e = 0; e < EPV; ++e) red[(rg * ncol + col) * EPV + e] = acc[e];
   }
-  __syncthreads();
+  if (rpar > 1) __syncthreads();
   if (rg == 0) {
     for (int g = 1; g < rpar; ++g)
 #pragma unroll
@@ -279,114 +278,258 @@ __global__ __launch_bounds__(256) void ema_kernel(int k, int d, float a, float b
   }
 }
 
-// Single workgroup. Mean running count m = sum N / k (fp64); dead set D =
-// {j : N_j < thr * m} in index order. For each dead j in turn: u from Philox,
-// donor i = first live index whose fp64 prefix sum of N over live clusters
-// exceeds u * (sum of live N); the donor keeps half of its count and sum,
-// cluster j takes the other half, and both sums are perturbed by
-// -/+ 2^-10 * sign per coordinate. Live prefix sums are kept as per-thread
-// chunk sums so a draw costs one block scan plus one chunk walk.
+// Dead-cluster revival. Mean running count m = sum N / k (fp64); dead set
+// D = {j : N_j < thr * m} in index order. For each dead j in turn: u from
+// Philox, donor i = first live index whose fp64 prefix sum of N over live
+// clusters exceeds u * (sum of live N); the donor keeps half of its count and
+// sum, cluster j takes the other half, and both sums are perturbed by
+// -/+ 2^-10 * sign per coordinate.
+//
+// revive_kernel (one workgroup):
+//  A. all threads: threshold, dead list, uniform draws, live counts (in LDS
+//     when k <= kRvLdsN), fp64 live sums per chunk of CS clusters.
+//  B. wave 0 alone draws the donors in dead-list order. Each lane owns m
+//     consecutive chunks and keeps the inclusive prefix of the live total over
+//     lanes in a register; a draw reads it with one ballot, narrows to a chunk
+//     (one wave scan when m > 1) and to a cluster (one wave scan per 64
+//     clusters), then subtracts the donor's lost half from the prefixes. Only
+//     running counts change here.
+//  C. all threads: chain bookkeeping. A donor picked r times before split q
+//     had its count halved r times, so the recorded count after split q fixes
+//     q's place in the donor's chain and the final count the chain's length.
+// split_kernel (many workgroups): one wave per chain applies its splits of the
+// running sums in order (chains are independent: donors are never dead).
+constexpr int kRvLdsN = 32768;   // live counts kept in LDS up to this k
+constexpr int kRvChunks = 1024;  // at most this many chunks
+
+__device__ __forceinline__ int halvings(float from, float to) {
+  int m = 0;
+  while (from != to && m < 200) {
+    from *= 0.5f;
+    ++m;
+  }
+  return m;
+}
+
 __global__ __launch_bounds__(1024) void revive_kernel(ReviveArgs A) {
   __shared__ double dtmp[16];
   __shared__ int itmp[16];
-  __shared__ double bs[1024];
-  __shared__ float ftmp[16];
-  __shared__ int s_ndead, s_donor, s_last;
-  __shared__ double s_tot;
+  __shared__ double csum[kRvChunks];
+  __shared__ float wN[kRvLdsN];
+  __shared__ int s_ndead, s_last;
   const int tid = threadIdx.x;
-  const int k = A.k, d = A.d;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int k = A.k;
+  const bool lds_n = k <= kRvLdsN;
+  const int cb = (k + 64 * kRvChunks - 1) / (64 * kRvChunks);  // 64-blocks per chunk
+  const int CS = 64 * cb;
+  const int nch = (k + CS - 1) / CS;
+  const int m = (nch + 63) / 64;  // chunks per lane in phase B
+  if (tid == 0) A.nheads[0] = 0;
 
+  // ---- A --------------------------------------------------------------------
   double loc = 0.0;
   for (int j = tid; j < k; j += 1024) loc += (double)A.N[j];
   const double total = block_sum<double, 1024>(loc, dtmp);
   const double th = A.thr * (total / (double)k);
 
-  const int cs = (k + 1023) / 1024;
-  const int j0 = min(k, tid * cs), j1 = min(k, j0 + cs);
+  const int per = (k + 1023) / 1024;
+  const int j0 = min(k, tid * per), j1 = min(k, j0 + per);
   int cnt = 0;
   for (int j = j0; j < j1; ++j) {
-    const int dd = ((double)A.N[j] < th) ? 1 : 0;
+    const float nv = A.N[j];
+    const int dd = ((double)nv < th) ? 1 : 0;
     A.flags[j] = dd;
+    A.n0[j] = nv;
+    if (lds_n) wN[j] = dd ? 0.0f : nv;
     cnt += dd;
   }
   const int incl = block_incl_scan<int, 1024>(cnt, itmp);
   if (tid == 1023) s_ndead = incl;
+  if (tid == 0) s_last = -1;
   int wpos = incl - cnt;
-  for (int j = j0; j < j1; ++j)
-    if (A.flags[j]) A.dead[wpos++] = j;
+  int mylast = -1;
+  for (int j = j0; j < j1; ++j) {
+    if (A.flags[j])
+      A.dead[wpos++] = j;
+    else
+      mylast = j;
+  }
   __threadfence_block();
   __syncthreads();
+  if (mylast >= 0) atomicMax(&s_last, mylast);
   const int ndead = s_ndead;
   if (A.count_only) {
     if (tid == 0) A.counters[2] = ndead;
     return;
   }
   if (ndead == 0) return;
-
-  double mys = 0.0;
-  int mylast = -1;
-  for (int j = j0; j < j1; ++j)
-    if (!A.flags[j]) {
-      mys += (double)A.N[j];
-      mylast = j;
-    }
-  bs[tid] = mys;
-  if (tid == 0) s_last = -1;
-  __syncthreads();
-  if (mylast >= 0) atomicMax(&s_last, mylast);
+  for (int q = tid; q < ndead; q += 1024)
+    A.udraw[q] = revive_uniform(A.seed, A.step, (uint64_t)A.dead[q]);
+  for (int c = tid; c < nch; c += 1024) {  // live sum of each chunk, in index order
+    double sv = 0.0;
+    const int e1 = min(k, (c + 1) * CS);
+    for (int j = c * CS; j < e1; ++j)
+      if (!A.flags[j]) sv += (double)A.N[j];
+    csum[c] = sv;
+  }
+  __threadfence_block();
   __syncthreads();
   const int last_live = s_last;
   if (last_live < 0) return;  // no donor exists (every cluster under the threshold)
 
-  for (int q = 0; q < ndead; ++q) {
-    const int j = A.dead[q];
-    const double u = revive_uniform(A.seed, A.step, (uint64_t)j);
-    const double v = bs[tid];
-    const double inc = block_incl_scan<double, 1024>(v, dtmp);
-    if (tid == 1023) s_tot = inc;
-    if (tid == 0) s_donor = last_live;
-    __syncthreads();
-    const double target = u * s_tot;
-    const double ex = inc - v;
-    if (v > 0.0 && ex <= target && target < inc) {
-      double acc = ex;
-      int donor = -1, lastl = -1;
-      for (int jj = j0; jj < j1; ++jj) {
-        if (A.flags[jj]) continue;
-        lastl = jj;
-        acc += (double)A.N[jj];
-        if (acc > target) {
-          donor = jj;
-          break;
+  // ---- B: donor draws (wave 0) ----------------------------------------------
+  if (wave == 0) {
+    double lsum = 0.0;
+    for (int t = 0; t < m; ++t)
+      if (lane * m + t < nch) lsum += csum[lane * m + t];
+    double incA = wave_scan_f64(lsum);
+    double T = readlane_f64(incA, 63);
+    int64_t logc = A.counters[1];
+    int dl = 0;
+    double ul = 0.0;
+    for (int q = 0; q < ndead; ++q) {
+      const int ql = q & 63;
+      if (ql == 0) {
+        dl = (q + lane < ndead) ? A.dead[q + lane] : 0;
+        ul = (q + lane < ndead) ? A.udraw[q + lane] : 0.0;
+      }
+      const int j = __builtin_amdgcn_readlane(dl, ql);
+      const double target = readlane_f64(ul, ql) * T;
+      int donor = -1;
+      float nvd = 0.0f;
+      const uint64_t bA = __ballot(lane * m < nch && lsum > 0.0 && incA > target);
+      if (bA) {
+        const int L = __ffsll((unsigned long long)bA) - 1;
+        const double baseA = readlane_f64(incA - lsum, L);
+        int c = L;
+        double base = baseA;
+        if (m > 1) {
+          const int ci = L * m + lane;
+          const double v = (lane < m && ci < nch) ? csum[ci] : 0.0;
+          const double inc2 = baseA + wave_scan_f64(v);
+          const uint64_t b2 = __ballot(lane < m && ci < nch && v > 0.0 && inc2 > target);
+          if (b2) {
+            const int t2 = __ffsll((unsigned long long)b2) - 1;
+            c = L * m + t2;
+            base = readlane_f64(inc2 - v, t2);
+          } else {
+            c = -1;
+          }
+        }
+        for (int bb = 0; c >= 0 && bb < cb && donor < 0; ++bb) {
+          const int idx = c * CS + bb * 64 + lane;
+          float nv = 0.0f;
+          if (idx < k) nv = lds_n ? wN[idx] : (A.flags[idx] ? 0.0f : A.N[idx]);
+          const double inc3 = base + wave_scan_f64((double)nv);
+          const uint64_t b3 = __ballot(idx < k && nv > 0.0f && inc3 > target);
+          if (b3) {
+            const int t3 = __ffsll((unsigned long long)b3) - 1;
+            donor = c * CS + bb * 64 + t3;
+            nvd = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(nv), t3));
+          }
+          base = readlane_f64(inc3, 63);
         }
       }
-      s_donor = donor >= 0 ? donor : lastl;
-    }
-    __syncthreads();
-    const int i = s_donor;
-    const float Ni = A.N[i] * 0.5f;
-    __syncthreads();
-    if (tid == 0) {
-      A.N[i] = Ni;
-      A.N[j] = Ni;
-      const int64_t c = A.counters[1];
-      if (A.log && c < A.log_cap) {
-        A.log[3 * c] = (int32_t)A.step;
-        A.log[3 * c + 1] = j;
-        A.log[3 * c + 2] = i;
-        A.counters[1] = c + 1;
+      if (donor < 0) {
+        donor = last_live;
+        nvd = lds_n ? wN[donor] : A.N[donor];
       }
+      const int i = donor;
+      const float Nh = nvd * 0.5f;
+      if (lane == 0) {
+        A.N[i] = Nh;
+        A.N[j] = Nh;
+        A.pair_i[q] = i;
+        A.pair_n[q] = Nh;
+        if (lds_n) wN[i] = Nh;
+        if (A.log && logc < A.log_cap) {
+          A.log[3 * logc] = (int32_t)A.step;
+          A.log[3 * logc + 1] = j;
+          A.log[3 * logc + 2] = i;
+          ++logc;
+        }
+      }
+      // counts read from global memory by the next draw must see these stores
+      if (!lds_n) __threadfence_block();
+      // the donor's chunk lost Nh of live count: update the prefix state
+      const int Lo = (i / CS) / m;
+      if (lane == Lo) lsum -= (double)Nh;
+      if (lane >= Lo) incA -= (double)Nh;
+      T -= (double)Nh;
+      if (lane == 0 && m > 1) csum[i / CS] -= (double)Nh;
     }
+    if (lane == 0) A.counters[1] = logc;
+  }
+  __threadfence_block();
+  __syncthreads();
+
+  // ---- C: chain bookkeeping -------------------------------------------------
+  // per thread a contiguous run of splits; chain starts are counted with a
+  // block scan (chain lengths) and a second one (number of chains)
+  const int qper = (ndead + 1023) / 1024;
+  const int q0 = min(ndead, tid * qper), q1 = min(ndead, q0 + qper);
+  int lensum = 0, hcnt = 0;
+  for (int q = q0; q < q1; ++q) {
+    const int i = A.pair_i[q];
+    const int ps = halvings(A.n0[i] * 0.5f, A.pair_n[q]);
+    A.pos[q] = ps;
+    if (ps == 0) {
+      const int len = 1 + halvings(A.n0[i] * 0.5f, A.N[i]);
+      A.head_of[i] = q;
+      A.clen[q] = len;
+      lensum += len;
+      ++hcnt;
+    }
+  }
+  const int lincl = block_incl_scan<int, 1024>(lensum, itmp);
+  const int hincl = block_incl_scan<int, 1024>(hcnt, itmp);
+  int lb = lincl - lensum, hb = hincl - hcnt;
+  for (int q = q0; q < q1; ++q) {
+    if (A.pos[q] == 0) {
+      A.cbase[q] = lb;
+      lb += A.clen[q];
+      A.heads[hb++] = q;
+    }
+  }
+  if (tid == 1023) A.nheads[0] = hincl;
+  __threadfence_block();
+  __syncthreads();
+  for (int q = q0; q < q1; ++q) A.list[A.cbase[A.head_of[A.pair_i[q]]] + A.pos[q]] = q;
+  if (tid == 0) {
+    A.counters[0] += ndead;
+    A.counters[3] += ndead;
+  }
+}
+
+// One wave per donor chain: apply its splits of the running sums in order.
+__global__ __launch_bounds__(256) void split_kernel(ReviveArgs A) {
+  const int w = blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  if (w >= A.nheads[0]) return;
+  const int d = A.d;
+  const int qh = A.heads[w];
+  const int base = A.cbase[qh], len = A.clen[qh];
+  for (int r = 0; r < len; ++r) {
+    const int q = A.list[base + r];
+    const int i = A.pair_i[q];
+    const int j = A.dead[q];
+    const float Nh = A.pair_n[q];
     float ni = 0.0f, nj = 0.0f;
-    for (int e = tid; e < d; e += 1024) {
+    U64x4 wd = {0, 0, 0, 0};
+    for (int e = lane, it = 0; e < d; e += 64, ++it) {
+      if ((it & 3) == 0)
+        wd = philox((uint64_t)j, A.step, (uint64_t)(e >> 8), kStreamSign, A.seed, 0);
+      const uint64_t word = (it & 3) == 0 ? wd.w0 : (it & 3) == 1 ? wd.w1 : (it & 3) == 2 ? wd.w2 : wd.w3;
+      const float sg = ((word >> (e & 63)) & 1) ? -1.0f : 1.0f;
       const size_t ii = (size_t)i * d + e, jj = (size_t)j * d + e;
       const float half = A.S[ii] * 0.5f;
-      const float sg = split_sign(A.seed, A.step, (uint64_t)j, (uint32_t)e);
       const float sj = __fmul_rn(half, 1.0f + kSplitEps * sg);
       const float si = __fmul_rn(half, 1.0f - kSplitEps * sg);
       A.S[jj] = sj;
       A.S[ii] = si;
-      float cj = __fdiv_rn(sj, Ni), ci = __fdiv_rn(si, Ni);
+      float cj = __fdiv_rn(sj, Nh), ci = __fdiv_rn(si, Nh);
       A.C[jj] = cj;
       A.C[ii] = ci;
       if (A.Chat) {
@@ -399,25 +542,12 @@ __global__ __launch_bounds__(1024) void revive_kernel(ReviveArgs A) {
       ni += ci * ci;
       nj += cj * cj;
     }
-    ni = block_sum<float, 1024>(ni, ftmp);
-    nj = block_sum<float, 1024>(nj, ftmp);
-    if (tid == 0) {
+    ni = wave_sum(ni);
+    nj = wave_sum(nj);
+    if (lane == 0) {
       A.bias[i] = -0.5f * ni;
       A.bias[j] = -0.5f * nj;
     }
-    __threadfence_block();
-    __syncthreads();
-    if (tid == i / cs) {
-      double s2 = 0.0;
-      for (int jj = j0; jj < j1; ++jj)
-        if (!A.flags[jj]) s2 += (double)A.N[jj];
-      bs[tid] = s2;
-    }
-    __syncthreads();
-  }
-  if (tid == 0) {
-    A.counters[0] += ndead;
-    A.counters[3] += ndead;
   }
 }
 
@@ -498,16 +628,20 @@ hipError_t launch_group(bool bf16, const void* X, int d, const uint32_t* order,
   if (nb <= 0) return hipSuccess;
   // upper bound on work items: one per non-empty cluster plus one per R rows
   const long long items = (long long)(k < nb ? k : nb) + (nb + R - 1) / R;
-  const dim3 grid((unsigned)items), block(256);
   const auto* x = static_cast<const unsigned char*>(X);
   const bool aligned = (uintptr_t)X % 16 == 0;
+  const bool vec = aligned && d % (bf16 ? 8 : 4) == 0;
+  const int ncol = vec ? d / (bf16 ? 8 : 4) : d;
+  int nt = 256;
+  if (ncol < 256) nt = (((256 / ncol) * ncol + 63) / 64) * 64;
+  const dim3 grid((unsigned)items), block(nt);
   if (bf16) {
-    if (aligned && d % 8 == 0)
+    if (vec)
       group_kernel<true, true><<<grid, block, 0, st>>>(x, d, order, off, item_off, k, R, s_acc);
     else
       group_kernel<true, false><<<grid, block, 0, st>>>(x, d, order, off, item_off, k, R, s_acc);
   } else {
-    if (aligned && d % 4 == 0)
+    if (vec)
       group_kernel<false, true><<<grid, block, 0, st>>>(x, d, order, off, item_off, k, R, s_acc);
     else
       group_kernel<false, false><<<grid, block, 0, st>>>(x, d, order, off, item_off, k, R, s_acc);
@@ -530,6 +664,9 @@ hipError_t launch_ema(int k, int d, float a, float b, int32_t* counts, float* s_
 
 hipError_t launch_revive(const ReviveArgs& a, hipStream_t st) {
   revive_kernel<<<1, 1024, 0, st>>>(a);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || a.count_only) return e;
+  split_kernel<<<(a.k + 3) / 4, 256, 0, st>>>(a);
   return hipGetLastError();
 }
 

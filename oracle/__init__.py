@@ -73,7 +73,7 @@ REVIVE_EVERY = 5             # blog: checked every five batches
 def build(force: bool = False) -> str:
     """Compile the C half of the oracle with gcc (fp64, OpenMP)."""
     if force or not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
-        subprocess.check_call(["gcc", "-O2", "-fopenmp", "-fno-fast-math", "-shared", "-fPIC",
+        subprocess.check_call(["gcc", "-O2", "-fopenmp", "-fno-fast-math", "-ffp-contract=off", "-shared", "-fPIC",
                                "-o", _LIB, _SRC])
     return _LIB
 
@@ -410,7 +410,8 @@ def train(X: np.ndarray, k: int, T: float, seed: int = 1234, *, batch_law: int =
     return res
 
 
-def lloyd(X: np.ndarray, k: int, iters: int, seed: int = 1234, nthreads: int = 0):
+def lloyd(X: np.ndarray, k: int, iters: int, seed: int = 1234, nthreads: int = 0,
+          progress: Optional[Callable[[int, float], None]] = None):
     """Plain Lloyd from the same k starting rows: assign all rows, move each
     centroid to the exact mean of its rows (a centroid with no row stays).
     Returns the centroids after `iters` updates and the MSE seen at each assign."""
@@ -420,6 +421,8 @@ def lloyd(X: np.ndarray, k: int, iters: int, seed: int = 1234, nthreads: int = 0
     for _ in range(iters):
         lab, d1, _ = assign(X, search_centroids(C, X), nthreads=nthreads)
         hist.append(float(d1.mean()))
+        if progress is not None:
+            progress(len(hist), hist[-1])
         counts, sums = group(X, None, lab, k)
         pos = counts > 0
         C[pos] = (sums[pos] / counts[pos].astype(np.float64)[:, None]).astype(np.float32)
