@@ -1,17 +1,19 @@
 // Fused nearest-centroid assignment for gfx950 (MFMA, wave64).
 //
-// A workgroup owns a tile of TP points and sweeps every centroid in panels of
-// TC. For each (panel, d-chunk) the point rows and centroid rows are staged
-// through LDS (double buffered, one 128-byte slab per row); four waves each
-// compute a 64 x 64 block of scores with 16x16 MFMA tiles:
+// A workgroup of 8 waves owns a tile of 128 points and sweeps every centroid
+// in panels of 256. For each (panel, d-chunk) the point rows and centroid
+// rows are staged through LDS (double buffered, one 128-byte slab per row);
+// each wave computes a 64 x 64 block of scores with 16x16 MFMA tiles:
 //   fp32 X: v_mfma_f32_16x16x4_f32     bf16 X: v_mfma_f32_16x16x32_bf16.
 // Centroids sit on the MFMA M dimension and points on N, so after a tile each
 // lane holds four centroid scores of a single point; the running best score
 // and its index stay in registers across all panels and are merged across the
-// four lane groups with cross-lane shuffles and across the two M-waves through
-// LDS only once at the end. The score is x.c - |c|^2/2: the bias -|c|^2/2 is
-// the accumulator's initial value, so the argmax needs compares only, and the
-// squared distance is |x|^2 - 2 * best. No n x k distance matrix is formed.
+// four lane groups with cross-lane shuffles and across the four M-waves
+// through LDS only once at the end. The score is x.c - |c|^2/2: the bias
+// -|c|^2/2 is the accumulator's initial value, so the argmax needs compares
+// only, and the squared distance is |x|^2 - 2 * best. No n x k distance
+// matrix is formed. A 256-centroid panel means the gathered point rows, the
+// data least likely to sit in L2, are re-read k/256 times per batch.
 //
 // Ties: each lane visits its centroids in increasing index order and keeps
 // the first strict maximum; merges prefer the lower index on equal scores, so
@@ -26,21 +28,28 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 
-constexpr int kTP = 128;       // points per workgroup
-constexpr int kTC = 128;       // centroids per panel
-constexpr int kSlab = 128;     // bytes of one row per stage
-constexpr int kStride = 144;   // LDS row pitch in bytes (slab + 16 to spread banks)
-constexpr int kThreads = 256;
+constexpr int kWM = 4;               // waves along the centroid (M) dimension
+constexpr int kWN = 2;               // waves along the point (N) dimension
+constexpr int kTP = 64 * kWN;        // points per workgroup
+constexpr int kTC = 64 * kWM;        // centroids per panel
+constexpr int kThreads = 64 * kWM * kWN;
+constexpr int kSlab = 128;           // bytes of one row per stage
+constexpr int kStride = 144;         // LDS row pitch in bytes (slab + 16 to spread banks)
+constexpr int kChunks = kSlab / 16;  // 16-byte chunks per row slab
+constexpr int kRowsPerPass = kThreads / kChunks;
+constexpr int kXL = kTP / kRowsPerPass;     // point-row slabs per thread
+constexpr int kCL = kTC / kRowsPerPass;     // centroid-row slabs per thread
 
 template <bool BF16, bool VEC>
 __device__ __forceinline__ u32x4 load_slab16(const unsigned char* row, int col, int d) {
-  // 16 bytes of a row starting at element `col`; zero past the end of the row.
+  // 16 bytes of a row starting at element `col`. With whole 16-byte chunks
+  // per row (VEC) the address is clamped into the row and the caller zeroes
+  // chunks past the end when it stores them, so the load stays in flight
+  // across the MFMA work; otherwise elements past the end read as zero.
   constexpr int ES = BF16 ? 2 : 4;
   constexpr int EPV = 16 / ES;
-  u32x4 v = {0u, 0u, 0u, 0u};
-  if (row == nullptr) return v;
   if constexpr (VEC) {
-    if (col < d) v = *reinterpret_cast<const u32x4*>(row + (size_t)col * ES);
+    return *reinterpret_cast<const u32x4*>(row + (size_t)(col < d ? col : d - EPV) * ES);
   } else {
     if constexpr (BF16) {
       const uint16_t* p = reinterpret_cast<const uint16_t*>(row);
@@ -51,21 +60,37 @@ __device__ __forceinline__ u32x4 load_slab16(const unsigned char* row, int col, 
         const uint32_t h = c < d ? (uint32_t)p[c] : 0u;
         w[e >> 1] |= h << (16 * (e & 1));
       }
-      v = u32x4{w[0], w[1], w[2], w[3]};
+      return u32x4{w[0], w[1], w[2], w[3]};
     } else {
       const float* p = reinterpret_cast<const float*>(row);
       float f[4];
 #pragma unroll
       for (int e = 0; e < 4; ++e) f[e] = (col + e) < d ? p[col + e] : 0.0f;
-      v = u32x4{__float_as_uint(f[0]), __float_as_uint(f[1]), __float_as_uint(f[2]),
-                __float_as_uint(f[3])};
+      return u32x4{__float_as_uint(f[0]), __float_as_uint(f[1]), __float_as_uint(f[2]),
+                   __float_as_uint(f[3])};
     }
   }
-  return v;
+}
+
+template <bool BF16>
+__device__ __forceinline__ float sumsq16(u32x4 w) {
+  float s = 0.0f;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    if constexpr (BF16) {
+      const float lo = __uint_as_float(w[e] << 16);
+      const float hi = __uint_as_float(w[e] & 0xFFFF0000u);
+      s += lo * lo + hi * hi;
+    } else {
+      const float f = __uint_as_float(w[e]);
+      s += f * f;
+    }
+  }
+  return s;
 }
 
 template <bool BF16, bool VEC>
-__global__ __launch_bounds__(kThreads, 2) void assign_kernel(
+__global__ __launch_bounds__(kThreads, 1) void assign_kernel(
     const unsigned char* __restrict__ X, int d, const uint32_t* __restrict__ rows, int nrows,
     const unsigned char* __restrict__ Cs, const float* __restrict__ bias, int k,
     int32_t* __restrict__ labels, float* __restrict__ dists, int32_t* __restrict__ counts,
@@ -75,8 +100,8 @@ __global__ __launch_bounds__(kThreads, 2) void assign_kernel(
   constexpr int EPS = kSlab / ES;       // elements per stage
   __shared__ __attribute__((aligned(16))) unsigned char lx[2][kTP * kStride];
   __shared__ __attribute__((aligned(16))) unsigned char lc[2][kTC * kStride];
-  __shared__ float m_s[2][kTP];
-  __shared__ int m_j[2][kTP];
+  __shared__ float m_s[kWM][kTP];
+  __shared__ int m_j[kWM][kTP];
   __shared__ float xn_s[kTP];
   __shared__ double red[kThreads / 64];
 
@@ -87,45 +112,45 @@ __global__ __launch_bounds__(kThreads, 2) void assign_kernel(
   const int wn = wave & 1;   // which 64 points of the tile
   const int tile0 = blockIdx.x * kTP;
 
-  // Global->LDS mapping: 8 threads per 128-byte row slab, 32 rows per pass.
-  const int ch = tid & 7;
-  const int rb = tid >> 3;
+  // Global->LDS mapping: kChunks threads per row slab. Rows past the end read
+  // a valid row (their results are discarded or masked by the bias).
+  const int ch = tid % kChunks;
+  const int rb = tid / kChunks;
   const size_t rowbytes = (size_t)d * ES;
-  const unsigned char* xrow[4];
+  const unsigned char* xrow[kXL];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int slot = tile0 + rb + 32 * i;
-    if (slot < nrows) {
-      const size_t r = rows ? (size_t)rows[slot] : (size_t)slot;
-      xrow[i] = X + r * rowbytes;
-    } else {
-      xrow[i] = nullptr;
-    }
+  for (int i = 0; i < kXL; ++i) {
+    const int slot = min(tile0 + rb + kRowsPerPass * i, nrows - 1);
+    const size_t r = rows ? (size_t)rows[slot] : (size_t)slot;
+    xrow[i] = X + r * rowbytes;
   }
 
   const int nst = (d + EPS - 1) / EPS;
   const int npan = (k + kTC - 1) / kTC;
-  const int total = nst * npan;
 
-  u32x4 rx[4], rc[4];
-  auto gload = [&](int it) {
-    const int panel = it / nst;
-    const int s = it - panel * nst;
+  u32x4 rx[kXL], rc[kCL];
+  bool colin = true;  // this thread's chunk of the staged slab lies inside the row
+  auto gload = [&](int panel, int s) {
     const int col = s * EPS + ch * EPV;
+    colin = col < d;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) rx[i] = load_slab16<BF16, VEC>(xrow[i], col, d);
+    for (int i = 0; i < kXL; ++i) rx[i] = load_slab16<BF16, VEC>(xrow[i], col, d);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int j = panel * kTC + rb + 32 * i;
-      rc[i] = load_slab16<BF16, VEC>(j < k ? Cs + (size_t)j * rowbytes : nullptr, col, d);
+    for (int i = 0; i < kCL; ++i) {
+      const int j = min(panel * kTC + rb + kRowsPerPass * i, k - 1);
+      rc[i] = load_slab16<BF16, VEC>(Cs + (size_t)j * rowbytes, col, d);
     }
   };
   auto sstore = [&](int buf) {
+    const u32x4 z = {0u, 0u, 0u, 0u};
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      *reinterpret_cast<u32x4*>(&lx[buf][(rb + 32 * i) * kStride + ch * 16]) = rx[i];
-      *reinterpret_cast<u32x4*>(&lc[buf][(rb + 32 * i) * kStride + ch * 16]) = rc[i];
-    }
+    for (int i = 0; i < kXL; ++i)
+      *reinterpret_cast<u32x4*>(&lx[buf][(rb + kRowsPerPass * i) * kStride + ch * 16]) =
+          colin ? rx[i] : z;
+#pragma unroll
+    for (int i = 0; i < kCL; ++i)
+      *reinterpret_cast<u32x4*>(&lc[buf][(rb + kRowsPerPass * i) * kStride + ch * 16]) =
+          colin ? rc[i] : z;
   };
 
   f32x4 acc[4][4];
@@ -150,21 +175,31 @@ __global__ __launch_bounds__(kThreads, 2) void assign_kernel(
     best[nb] = -__builtin_inff();
     bidx[nb] = -1;
   }
-  float xpart = 0.0f;  // |x|^2 partial: point tid/2, half tid&1 of each slab
+  float xpart[kXL];  // |x|^2 partials of this thread's point-row slabs
+#pragma unroll
+  for (int i = 0; i < kXL; ++i) xpart[i] = 0.0f;
 
-  gload(0);
+  // Two LDS stages: the global loads of the next stage are in flight while
+  // the MFMAs consume the current one.
+  gload(0, 0);
+#pragma unroll
+  for (int i = 0; i < kXL; ++i) xpart[i] += colin ? sumsq16<BF16>(rx[i]) : 0.0f;
   sstore(0);
   __syncthreads();
   init_acc(0);
 
-  for (int it = 0; it < total; ++it) {
-    const int panel = it / nst;
-    const int s = it - panel * nst;
-    const int buf = it & 1;
-    if (it + 1 < total) gload(it + 1);
+  int panel = 0, s = 0, buf = 0;
+  while (true) {
+    int np = panel, ns = s + 1;
+    if (ns == nst) {
+      ns = 0;
+      ++np;
+    }
+    const bool more = np < npan;
+    if (more) gload(np, ns);
 
 #pragma unroll
-    for (int kk = 0; kk < 2; ++kk) {
+    for (int kk = 0; kk < kSlab / 64; ++kk) {
       u32x4 a[4], b[4];
 #pragma unroll
       for (int mb = 0; mb < 4; ++mb)
@@ -194,27 +229,8 @@ __global__ __launch_bounds__(kThreads, 2) void assign_kernel(
       }
     }
 
-    if (panel == 0) {
-      const unsigned char* p = &lx[buf][(tid >> 1) * kStride + (tid & 1) * 64];
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const u32x4 w = *reinterpret_cast<const u32x4*>(p + 16 * q);
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          if constexpr (BF16) {
-            const float lo = __uint_as_float(w[e] << 16);
-            const float hi = __uint_as_float(w[e] & 0xFFFF0000u);
-            xpart += lo * lo + hi * hi;
-          } else {
-            const float f = __uint_as_float(w[e]);
-            xpart += f * f;
-          }
-        }
-      }
-    }
-
-    if (s == nst - 1) {
-      // fold this panel into the running best (centroids in increasing order)
+    if (ns == 0) {
+      // panel complete: fold it into the running best (centroids in increasing order)
 #pragma unroll
       for (int nb = 0; nb < 4; ++nb)
 #pragma unroll
@@ -227,13 +243,28 @@ __global__ __launch_bounds__(kThreads, 2) void assign_kernel(
               bidx[nb] = panel * kTC + wm * 64 + mb * 16 + 4 * (lane >> 4) + v;
             }
           }
-      if (panel + 1 < npan) init_acc(panel + 1);
+      if (more) init_acc(np);
     }
-
-    if (it + 1 < total) sstore(buf ^ 1);
+    if (!more) break;
+    if (np == 0) {
+#pragma unroll
+      for (int i = 0; i < kXL; ++i) xpart[i] += colin ? sumsq16<BF16>(rx[i]) : 0.0f;
+    }
+    sstore(buf ^ 1);
     __syncthreads();
+    panel = np;
+    s = ns;
+    buf ^= 1;
   }
 
+  // |x|^2: fold the column-chunk threads of each point row (adjacent lanes)
+#pragma unroll
+  for (int i = 0; i < kXL; ++i) {
+    float v = xpart[i];
+#pragma unroll
+    for (int o = 1; o < kChunks; o <<= 1) v += __shfl_xor(v, o, 64);
+    if (ch == 0) xn_s[rb + kRowsPerPass * i] = v;
+  }
   // merge the four lane groups that share a point
 #pragma unroll
   for (int nb = 0; nb < 4; ++nb) {
@@ -253,8 +284,6 @@ __global__ __launch_bounds__(kThreads, 2) void assign_kernel(
       m_j[wm][wn * 64 + nb * 16 + lane] = j;
     }
   }
-  xpart += __shfl_xor(xpart, 1, 64);
-  if ((tid & 1) == 0) xn_s[tid >> 1] = xpart;
   __syncthreads();
 
   double dsum = 0.0;
@@ -262,11 +291,14 @@ __global__ __launch_bounds__(kThreads, 2) void assign_kernel(
     const int p = tid;
     float sc = m_s[0][p];
     int j = m_j[0][p];
-    const float s1 = m_s[1][p];
-    const int j1 = m_j[1][p];
-    if (s1 > sc || (s1 == sc && (unsigned)j1 < (unsigned)j)) {
-      sc = s1;
-      j = j1;
+#pragma unroll
+    for (int w = 1; w < kWM; ++w) {
+      const float s1 = m_s[w][p];
+      const int j1 = m_j[w][p];
+      if (s1 > sc || (s1 == sc && (unsigned)j1 < (unsigned)j)) {
+        sc = s1;
+        j = j1;
+      }
     }
     if (j < 0 || j >= k) j = 0;  // only reachable with non-finite data
     const int slot = tile0 + p;
@@ -282,7 +314,11 @@ __global__ __launch_bounds__(kThreads, 2) void assign_kernel(
     dsum = wave_sum(dsum);
     if (lane == 0) red[wave] = dsum;
     __syncthreads();
-    if (tid == 0) atomicAdd(obj, red[0] + red[1] + red[2] + red[3]);
+    if (tid == 0) {
+      double t = 0.0;
+      for (int w = 0; w < kThreads / 64; ++w) t += red[w];
+      atomicAdd(obj, t);
+    }
   }
 }
 
