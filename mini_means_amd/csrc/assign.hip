@@ -328,6 +328,9 @@ hipError_t launch_assign(bool bf16, const void* X, int d, const uint32_t* rows, 
                          const void* Cs, const float* bias, int k, int32_t* labels, float* dists,
                          int32_t* counts, double* obj, hipStream_t st) {
   if (nrows <= 0) return hipSuccess;
+  if (bf16 && assign_bf16_resident_ok(d, X, Cs))
+    return launch_assign_bf16_resident(X, d, rows, nrows, Cs, bias, k, labels, dists, counts, obj,
+                                       st);
   const dim3 grid((nrows + kTP - 1) / kTP), block(kThreads);
   const auto* x = static_cast<const unsigned char*>(X);
   const auto* c = static_cast<const unsigned char*>(Cs);

@@ -18,6 +18,14 @@ hipError_t launch_assign(bool bf16, const void* X, int d, const uint32_t* rows, 
                          const void* Cs, const float* bias, int k, int32_t* labels, float* dists,
                          int32_t* counts, double* obj, hipStream_t st);
 
+// bf16 data of dimension 32, 64, 96 or 128: points resident in registers,
+// 32x32x16 bf16 MFMA tiles (same contract as launch_assign).
+bool assign_bf16_resident_ok(int d, const void* X, const void* Chat);
+hipError_t launch_assign_bf16_resident(const void* X, int d, const uint32_t* rows, int nrows,
+                                       const void* Chat, const float* bias, int k,
+                                       int32_t* labels, float* dists, int32_t* counts,
+                                       double* obj, hipStream_t st);
+
 // rows[r] = pi(start + r) for the keyed permutation pk.
 hipError_t launch_sample_rows(const PermKey& pk, uint64_t start, int count, uint32_t* rows,
                               hipStream_t st);
