@@ -127,14 +127,15 @@ def uniform01(seed: int, t: int, j: int) -> float:
 
 
 def split_signs(seed: int, t: int, j: int, d: int) -> np.ndarray:
-    """+1/-1 per coordinate for the split of step t that refills cluster j."""
-    s = np.empty(d, dtype=np.float32)
-    for blk in range(0, d, 256):
-        w = philox4x64((j, t, blk >> 8, STREAM_SIGN), (seed, 0))
-        for u in range(blk, min(d, blk + 256)):
-            bit = (int(w[(u >> 6) & 3]) >> (u & 63)) & 1
-            s[u] = -1.0 if bit else 1.0
-    return s
+    """+1/-1 per coordinate for the split of step t that refills cluster j.
+
+    Coordinate u takes bit (u mod 64) of word (u // 64) mod 4 of the Philox
+    block with counter word 2 = u // 256; a set bit means -1."""
+    nblk = (d + 255) // 256
+    words = np.concatenate([philox4x64((j, t, b, STREAM_SIGN), (seed, 0)) for b in range(nblk)])
+    bits = (words[:, None] >> np.arange(64, dtype=np.uint64)[None, :]) & np.uint64(1)
+    bits = bits.reshape(-1)[:d]
+    return np.where(bits == 1, np.float32(-1.0), np.float32(1.0)).astype(np.float32)
 
 
 # ----------------------------------------------------------------------------
@@ -374,7 +375,7 @@ def train(X: np.ndarray, k: int, T: float, seed: int = 1234, *, batch_law: int =
                 glab = lab if slots is None else lab[slots]
                 gd = dist_to(Xf, Cs, glab, sel)
                 chk = dict(t=t, slots=slots, oracle=olab, d1=od1, d2=od2, given=glab,
-                           given_dist=gd, rows=sel, C=Cs)
+                           given_dist=gd, rows=sel, C=Cs, C32=C.copy())
                 if check_hook is not None:
                     check_hook(chk)
                 else:
