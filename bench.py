@@ -13,6 +13,7 @@ profiling gives each kernel class's device time. Prints one JSON line.
 from __future__ import annotations
 
 import argparse
+import hashlib
 import json
 import os
 import sys
@@ -35,6 +36,34 @@ DESCR = {
     "large": "large: 100M x 128 bf16, unit-normalised 65536-component mixture (sigma 0.4); "
              "k=65536, T=3",
 }
+
+
+def kernel_source_sha() -> str:
+    """Hash of the assign kernels' sources: counter readings are only reused
+    while it is unchanged."""
+    h = hashlib.sha256()
+    for f in ("assign.hip", "assign_bf16.hip", "common.hpp", "kernels.hpp"):
+        with open(os.path.join(HERE, "mini_means_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
+def committed_traffic(workload: str):
+    """HBM bytes per assign launch from the committed counter summary
+    (rocprofv3 FETCH_SIZE + WRITE_SIZE, scaled by a plain copy of known size),
+    or None when there is none or the kernel changed since it was taken."""
+    path = os.path.join(HERE, "profiles", f"assign_{workload}_traffic.md")
+    if not os.path.exists(path):
+        return None, "no counter summary"
+    vals = {}
+    with open(path) as fh:
+        for line in fh:
+            if ":" in line and line.strip().startswith("- "):
+                key, val = line.strip()[2:].split(":", 1)
+                vals[key.strip()] = val.strip().strip("`")
+    if vals.get("source_sha256") != kernel_source_sha():
+        return None, "kernel changed since the counters were taken"
+    return float(vals["hbm_bytes_per_launch"]), path
 
 
 def log(msg: str) -> None:
@@ -127,7 +156,13 @@ def main() -> int:
     ap.add_argument("--no-ttt", action="store_true", help="skip the time-to-target sweep")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--ttt-seeds", type=int, default=3)
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
+                    help="also run a plain device copy of BYTES (counter calibration)")
+    ap.add_argument("--print-source-sha", action="store_true")
     args = ap.parse_args()
+    if args.print_source_sha:
+        print(kernel_source_sha())
+        return 0
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -171,6 +206,16 @@ def main() -> int:
     value = flops / wall / 1e12
     log(f"timed {K} steps in {wall:.4f}s -> {value:.2f} assign TFLOP/s (whole step)")
 
+    if args.copy_calibration > 0:
+        # a plain copy of known size, for scaling the HBM byte counters
+        src = torch.empty(args.copy_calibration // 4, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+        log(f"copied {args.copy_calibration} bytes x3 for counter calibration")
+
     # profiled run: device time per kernel class (HIP events on the launch stream)
     prof = mm.train(X, k, T, args.seed, max_steps=K, profile=True).stats
     torch.cuda.synchronize()
@@ -183,6 +228,9 @@ def main() -> int:
     u_ms = prof["ms_update"]
     log(f"device ms: assign {a_ms:.2f} bucket {prof['ms_bucket']:.2f} group {g_ms:.2f} "
         f"update {u_ms:.2f} revive {prof['ms_revive']:.2f} sample {prof['ms_sample']:.2f}")
+
+    traffic, tsrc = committed_traffic(args.workload)
+    log(f"traffic: {traffic} ({tsrc})")
 
     line = {
         "metric": METRIC,
@@ -208,7 +256,7 @@ def main() -> int:
             "peak": peak,
             "unit": "TFLOP/s",
             "frac": round(assign_tflops / peak, 4) if assign_tflops else None,
-            "traffic": None,
+            "traffic": traffic,
             "launches": K,
             "avg_launch_ms": round(a_ms / K, 4),
         },

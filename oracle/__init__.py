@@ -45,6 +45,12 @@ proportional to N among the clusters that were alive at the check, donor
 halves, +/-2^-10 hashed-sign perturbation); finalisation over the last pass,
 keeping the EMA centroid where that pass gave no point; labels of rows the last
 pass did not visit are -1; random streams from Philox4x64-10.
+
+Parity unpinned: the split geometry of a revival (halving, the +/-2^-10
+hashed-sign perturbation, the sequential donor draws) is this build's reading
+of "split a busy cluster in two"; the pages fix no values for it. It is pinned
+only by properties (donor frequency proportional to N, the split identities,
+fewer dead clusters than without revival).
 """
 from __future__ import annotations
 
