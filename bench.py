@@ -130,10 +130,11 @@ def cpu_baseline(Xhost, C, k, d, budget_s: float) -> dict:
     import oracle
     rng = np.random.default_rng(0)
     cores = int(os.environ.get("OMP_NUM_THREADS", "0")) or len(os.sched_getaffinity(0))
-    probe = Xhost[rng.choice(len(Xhost), 128, replace=False)]
+    npr = 2048
+    probe = Xhost[rng.choice(len(Xhost), npr, replace=False)]
     t0 = time.perf_counter()
     oracle.assign(probe, C, nthreads=cores)
-    per_row = (time.perf_counter() - t0) / 128
+    per_row = (time.perf_counter() - t0) / npr
     rows = int(max(256, min(len(Xhost), budget_s / max(per_row, 1e-9))))
     sample = Xhost[rng.choice(len(Xhost), rows, replace=False)]
     t0 = time.perf_counter()
