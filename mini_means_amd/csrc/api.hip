@@ -276,11 +276,12 @@ int emeans_train(const void* X, int64_t n, int32_t d, int32_t k, double T, uint6
   void* base = nullptr;
   uint32_t *rows = nullptr, *order = nullptr;
   int32_t *blab = nullptr, *counts = nullptr, *cursor = nullptr, *off = nullptr,
-          *item_off = nullptr, *pass_counts = nullptr, *flags = nullptr, *dead = nullptr,
+          *ovf_n = nullptr, *pass_counts = nullptr, *flags = nullptr, *dead = nullptr,
           *dlog = nullptr, *pair_i = nullptr, *rv_pos = nullptr, *rv_head = nullptr,
           *rv_cbase = nullptr, *rv_clen = nullptr, *rv_heads = nullptr, *rv_list = nullptr,
           *rv_nheads = nullptr;
   double* rv_u = nullptr;
+  int2* ovf = nullptr;
   float *bdist = nullptr, *s_acc = nullptr, *S = nullptr, *N = nullptr, *LS = nullptr,
         *bias = nullptr, *n0 = nullptr, *pair_n = nullptr;
   uint16_t* chat = nullptr;
@@ -305,7 +306,8 @@ int emeans_train(const void* X, int64_t n, int32_t d, int32_t k, double T, uint6
   ar.want(&counts, (size_t)k);
   ar.want(&cursor, (size_t)k);
   ar.want(&off, (size_t)k + 1);
-  ar.want(&item_off, (size_t)k + 1);
+  ar.want(&ovf, (size_t)(B / kGroupRows) + 1);
+  ar.want(&ovf_n, 1);
   ar.want(&pass_counts, (size_t)k);
   ar.want(&flags, (size_t)k);
   ar.want(&dead, (size_t)k);
@@ -385,12 +387,12 @@ int emeans_train(const void* X, int64_t n, int32_t d, int32_t k, double T, uint6
         trace_off += nb;
       }
       HIP_TRY(timed(kBucket, [&] {
-        hipError_t er = launch_scan(counts, k, kGroupRows, off, cursor, item_off, st);
+        hipError_t er = launch_scan(counts, k, kGroupRows, off, cursor, ovf, ovf_n, st);
         if (er != hipSuccess) return er;
         return launch_scatter(blab, rows, nb, cursor, order, (last && labels) ? labels : nullptr, st);
       }));
       HIP_TRY(timed(kGroup, [&] {
-        return launch_group(bf16, X, d, order, off, item_off, k, kGroupRows, nb, s_acc, st);
+        return launch_group(bf16, X, d, order, off, ovf, ovf_n, k, kGroupRows, nb, s_acc, st);
       }));
       HIP_TRY(timed(kUpdate, [&] {
         return launch_ema(k, d, a, b, counts, s_acc, N, S, centroids, bias, chat, pass_counts,

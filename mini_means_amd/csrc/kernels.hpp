@@ -39,10 +39,11 @@ hipError_t launch_init_centroids(bool bf16, const void* X, int d, const PermKey&
 // bias[j] = -|c_j|^2 / 2 in the search format; Chat = bf16(C) when non-null.
 hipError_t launch_prep(const float* C, int k, int d, float* bias, uint16_t* Chat, hipStream_t st);
 
-// off = exclusive scan of counts (k+1 entries), cursor = off[0..k),
-// item_off = exclusive scan of ceil(counts / R).
+// off = exclusive scan of counts (k+1 entries), cursor = off[0..k); ovf lists
+// the grouping work items beyond the first R rows of each cluster as
+// (cluster, part) pairs, *ovf_n of them (room for rows / R pairs).
 hipError_t launch_scan(const int32_t* counts, int k, int R, int32_t* off, int32_t* cursor,
-                       int32_t* item_off, hipStream_t st);
+                       int2* ovf, int32_t* ovf_n, hipStream_t st);
 
 // Bucket the batch by label: order[cursor[label]++] = rows[r]; when
 // out_labels is non-null also out_labels[rows[r]] = label.
@@ -51,8 +52,8 @@ hipError_t launch_scatter(const int32_t* labels, const uint32_t* rows, int nb, i
 
 // s_acc[j] += sum of X rows of cluster j (work items of at most R rows).
 hipError_t launch_group(bool bf16, const void* X, int d, const uint32_t* order,
-                        const int32_t* off, const int32_t* item_off, int k, int R, int nb,
-                        float* s_acc, hipStream_t st);
+                        const int32_t* off, const int2* ovf, const int32_t* ovf_n, int k, int R,
+                        int nb, float* s_acc, hipStream_t st);
 
 // EMA update of every cluster; resets counts and s_acc for the next step;
 // pass_counts += counts; LS += s when LS is non-null; refreshes bias/Chat.

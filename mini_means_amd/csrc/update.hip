@@ -14,9 +14,27 @@ namespace {
 
 constexpr float kSplitEps = 0x1.0p-10f;  // relative perturbation of a split
 
-__global__ void sample_rows_kernel(PermKey pk, uint64_t start, int count, uint32_t* rows) {
-  const int r = blockIdx.x * blockDim.x + threadIdx.x;
-  if (r < count) rows[r] = (uint32_t)perm_at(start + (uint64_t)r, pk);
+// Each thread produces q consecutive slots of the batch. A loop trip takes one
+// Feistel evaluation of the slot in hand; the thread moves on to its next slot
+// as soon as the value lands in [0, n). A wave therefore runs for the largest
+// sum of q cycle-walk lengths among its lanes rather than q times the longest
+// single walk (walks are geometric, with mean up to 4 when n is just above a
+// power of four).
+__global__ __launch_bounds__(256) void sample_rows_kernel(PermKey pk, uint64_t start, int count,
+                                                          int q, uint32_t* rows) {
+  const int64_t base = ((int64_t)blockIdx.x * blockDim.x + threadIdx.x) * q;
+  if (base >= count) return;
+  const int qn = (int)(count - base < q ? count - base : q);
+  int i = 0;
+  uint64_t v = start + (uint64_t)base;
+  while (i < qn) {
+    v = feistel(v, pk);
+    if (v < pk.n) {
+      rows[base + i] = (uint32_t)v;
+      ++i;
+      v = start + (uint64_t)(base + i);
+    }
+  }
 }
 
 __global__ void sample_rows_i32_kernel(PermKey pk, uint64_t start, int count, int32_t* rows) {
@@ -63,35 +81,102 @@ __global__ __launch_bounds__(256) void prep_kernel(const float* C, int k, int d,
   if (lane == 0) bias[j] = -0.5f * nrm;
 }
 
-// Single workgroup: exclusive scans of counts and of ceil(counts / R).
-__global__ __launch_bounds__(1024) void scan_kernel(const int32_t* counts, int k, int R,
-                                                    int32_t* off, int32_t* cursor,
-                                                    int32_t* item_off) {
-  __shared__ int tmp[16];
+// Single workgroup: exclusive scan of the counts (row offsets of the buckets)
+// and the list of overflow work items. Work item j < k of the grouping is the
+// first R rows of cluster j; a cluster with n > R rows also gets (n - 1) / R
+// overflow items, listed here as (cluster, part) pairs. Clusters are taken in
+// tiles of 1024 x 16: counts are loaded coalesced (the next tile's loads are
+// in flight during this tile's scan) and transposed through LDS so that each
+// thread owns 16 consecutive clusters; one block scan of the packed pair (rows
+// in the high word, overflow items in the low word) serves both sums, and the
+// row offsets go back through LDS to be stored coalesced.
+__global__ __launch_bounds__(1024) void scan_kernel(const int32_t* __restrict__ counts, int k,
+                                                    int R, int32_t* __restrict__ off,
+                                                    int32_t* __restrict__ cursor,
+                                                    int2* __restrict__ ovf,
+                                                    int32_t* __restrict__ ovf_n) {
+  constexpr int V = 16, kTile = 1024 * V;
+  __shared__ int lds[kTile + kTile / 16];
+  __shared__ uint64_t tmp[16];
+  const auto at = [](int i) { return i + (i >> 4); };  // odd stride: no bank conflicts
   const int tid = threadIdx.x;
-  const int cs = (k + 1023) / 1024;
-  const int j0 = min(k, tid * cs), j1 = min(k, j0 + cs);
-  int c = 0, it = 0;
-  for (int j = j0; j < j1; ++j) {
-    const int n = counts[j];
-    c += n;
-    it += (n + R - 1) / R;
+  uint64_t carry = 0;
+  int nx[V];
+#pragma unroll
+  for (int v = 0; v < V; ++v) {
+    const int j = v * 1024 + tid;
+    nx[v] = j < k ? counts[j] : 0;
   }
-  const int ci = block_incl_scan<int, 1024>(c, tmp);
-  const int ii = block_incl_scan<int, 1024>(it, tmp);
-  int oc = ci - c, oi = ii - it;
-  for (int j = j0; j < j1; ++j) {
-    const int n = counts[j];
-    off[j] = oc;
-    cursor[j] = oc;
-    item_off[j] = oi;
-    oc += n;
-    oi += (n + R - 1) / R;
+  for (int t0 = 0; t0 < k; t0 += kTile) {
+#pragma unroll
+    for (int v = 0; v < V; ++v) lds[at(v * 1024 + tid)] = nx[v];
+    __syncthreads();
+    int n[V];
+#pragma unroll
+    for (int v = 0; v < V; ++v) n[v] = lds[at(tid * V + v)];
+    const int t1 = t0 + kTile;
+#pragma unroll
+    for (int v = 0; v < V; ++v) {
+      const int j = t1 + v * 1024 + tid;
+      nx[v] = j < k ? counts[j] : 0;
+    }
+    uint64_t loc = 0;
+#pragma unroll
+    for (int v = 0; v < V; ++v)
+      loc += ((uint64_t)(uint32_t)n[v] << 32) | (uint32_t)(n[v] > R ? (n[v] - 1) / R : 0);
+    // ends with a barrier: every thread has read its counts from lds
+    const uint64_t incl = block_incl_scan<uint64_t, 1024>(loc, tmp);
+    const uint64_t total = tmp[15];
+    const uint64_t ex = carry + incl - loc;
+    int oc = (int)(ex >> 32), ov = (int)(uint32_t)ex;
+#pragma unroll
+    for (int v = 0; v < V; ++v) {
+      lds[at(tid * V + v)] = oc;
+      const int extra = n[v] > R ? (n[v] - 1) / R : 0;
+      for (int q = 0; q < extra; ++q) ovf[ov + q] = make_int2(t0 + tid * V + v, q + 1);
+      oc += n[v];
+      ov += extra;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int v = 0; v < V; ++v) {
+      const int j = t0 + v * 1024 + tid;
+      if (j < k) {
+        const int o = lds[at(v * 1024 + tid)];
+        off[j] = o;
+        cursor[j] = o;
+      }
+    }
+    carry += total;
+    __syncthreads();  // lds and tmp are rewritten by the next tile
   }
-  if (tid == 1023) {
-    off[k] = ci;
-    item_off[k] = ii;
+  if (tid == 0) {
+    off[k] = (int)(carry >> 32);
+    *ovf_n = (int)(uint32_t)carry;
   }
+}
+
+// Rows [beg, end) of the bucketed order that work item w sums, the cluster j,
+// and whether the cluster is held by this item alone. False for an empty item.
+__device__ __forceinline__ bool group_item(int w, int k, int R, const int32_t* __restrict__ off,
+                                           const int2* __restrict__ ovf,
+                                           const int32_t* __restrict__ ovf_n, int& j, int& beg,
+                                           int& end, bool& single) {
+  int p = 0;
+  if (w < k) {
+    j = w;
+  } else {
+    if (w - k >= *ovf_n) return false;
+    const int2 e = ovf[w - k];
+    j = e.x;
+    p = e.y;
+  }
+  const int o0 = off[j], o1 = off[j + 1];
+  beg = o0 + p * R;
+  if (beg >= o1) return false;
+  end = min(o1, beg + R);
+  single = o1 - o0 <= R;
+  return true;
 }
 
 __global__ void scatter_kernel(const int32_t* labels, const uint32_t* rows, int nb,
@@ -116,25 +201,16 @@ template <bool BF16, bool VEC>
 __global__ __launch_bounds__(256) void group_kernel(const unsigned char* __restrict__ X, int d,
                                                     const uint32_t* __restrict__ order,
                                                     const int32_t* __restrict__ off,
-                                                    const int32_t* __restrict__ item_off, int k,
+                                                    const int2* __restrict__ ovf,
+                                                    const int32_t* __restrict__ ovf_n, int k,
                                                     int R, float* __restrict__ s_acc) {
   constexpr int ES = BF16 ? 2 : 4;
   constexpr int EPV = VEC ? 16 / ES : 1;  // elements per column unit
   constexpr int U = 8;                    // rows in flight per thread
   __shared__ float red[256 * EPV];
-  const int w = blockIdx.x;
-  const int nitems = item_off[k];
-  if (w >= nitems) return;
-  int lo = 0, hi = k;  // largest j with item_off[j] <= w
-  while (hi - lo > 1) {
-    const int mid = (lo + hi) >> 1;
-    if (item_off[mid] <= w) lo = mid; else hi = mid;
-  }
-  const int j = lo;
-  const int p = w - item_off[j];
-  const int beg = off[j] + p * R;
-  const int end = min(off[j + 1], beg + R);
-  const bool single = (item_off[j + 1] - item_off[j]) == 1;
+  int j, beg, end;
+  bool single;
+  if (!group_item(blockIdx.x, k, R, off, ovf, ovf_n, j, beg, end, single)) return;
   const int tid = threadIdx.x;
   const int NT = blockDim.x;
   const int ncol = d / EPV;
@@ -227,6 +303,99 @@ __global__ __launch_bounds__(256) void group_kernel(const unsigned char* __restr
 #pragma unroll
       for (int e = 0; e < EPV; ++e) acc[e] += red[(g * ncol + col) * EPV + e];
     write_out(col, acc);
+  }
+}
+
+// Narrow rows (at most 64 column units of 16 bytes, e.g. d <= 256 fp32 or
+// d <= 512 bf16): one wave per work item, four items per workgroup. The 64
+// lanes form 64 / ncol row groups; row groups are folded with cross-lane
+// shuffles, so a wave needs no LDS and no barrier.
+template <bool BF16, bool VEC>
+__global__ __launch_bounds__(256) void group_wave_kernel(const unsigned char* __restrict__ X,
+                                                         int d, const uint32_t* __restrict__ order,
+                                                         const int32_t* __restrict__ off,
+                                                         const int2* __restrict__ ovf,
+                                                         const int32_t* __restrict__ ovf_n,
+                                                         int k, int R, float* __restrict__ s_acc) {
+  constexpr int ES = BF16 ? 2 : 4;
+  constexpr int EPV = VEC ? 16 / ES : 1;  // elements per column unit
+  constexpr int U = 8;                    // rows in flight per lane
+  const int lane = threadIdx.x & 63;
+  int j, beg, end;
+  bool single;
+  if (!group_item(blockIdx.x * 4 + (threadIdx.x >> 6), k, R, off, ovf, ovf_n, j, beg, end, single))
+    return;
+  const int ncol = d / EPV;
+  const int rpar = 64 / ncol;
+  const int rg = lane / ncol;
+  const int col = lane - rg * ncol;
+  const size_t rowbytes = (size_t)d * ES;
+
+  auto load_unit = [&](uint32_t row, float* v) {
+    const unsigned char* base = X + (size_t)row * rowbytes;
+    if constexpr (VEC) {
+      typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+      const u32x4 q = *reinterpret_cast<const u32x4*>(base + (size_t)col * 16);
+      if constexpr (BF16) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          v[2 * e] = __uint_as_float(q[e] << 16);
+          v[2 * e + 1] = __uint_as_float(q[e] & 0xFFFF0000u);
+        }
+      } else {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) v[e] = __uint_as_float(q[e]);
+      }
+    } else {
+      if constexpr (BF16)
+        v[0] = bf16_to_f32(reinterpret_cast<const uint16_t*>(base)[col]);
+      else
+        v[0] = reinterpret_cast<const float*>(base)[col];
+    }
+  };
+
+  float acc[EPV];
+#pragma unroll
+  for (int e = 0; e < EPV; ++e) acc[e] = 0.0f;
+  if (rg < rpar) {
+    int pos = beg + rg;
+    for (; pos + (U - 1) * rpar < end; pos += U * rpar) {
+      uint32_t rr[U];
+#pragma unroll
+      for (int u = 0; u < U; ++u) rr[u] = order[pos + u * rpar];
+      float v[U][EPV];
+#pragma unroll
+      for (int u = 0; u < U; ++u) load_unit(rr[u], v[u]);
+#pragma unroll
+      for (int u = 0; u < U; ++u)
+#pragma unroll
+        for (int e = 0; e < EPV; ++e) acc[e] += v[u][e];
+    }
+    for (; pos < end; pos += rpar) {
+      float v[EPV];
+      load_unit(order[pos], v);
+#pragma unroll
+      for (int e = 0; e < EPV; ++e) acc[e] += v[e];
+    }
+  }
+  // fold the row groups into row group 0 (lanes 0 .. ncol-1)
+  for (int g = 1; g < rpar; ++g) {
+    const int src = col + g * ncol;
+#pragma unroll
+    for (int e = 0; e < EPV; ++e) {
+      const float o = __shfl(acc[e], src, 64);
+      if (rg == 0) acc[e] += o;
+    }
+  }
+  if (rg == 0) {
+    float* dst = s_acc + (size_t)j * d + (size_t)col * EPV;
+#pragma unroll
+    for (int e = 0; e < EPV; ++e) {
+      if (single)
+        dst[e] = acc[e];
+      else
+        atomicAdd(&dst[e], acc[e]);
+    }
   }
 }
 
@@ -585,7 +754,11 @@ __global__ void finalize_kernel(int k, int d, const int32_t* pass_counts, const 
 hipError_t launch_sample_rows(const PermKey& pk, uint64_t start, int count, uint32_t* rows,
                               hipStream_t st) {
   if (count <= 0) return hipSuccess;
-  sample_rows_kernel<<<(count + 255) / 256, 256, 0, st>>>(pk, start, count, rows);
+  // several slots per thread only once the batch keeps 2^18 threads busy
+  int q = count >> 18;
+  q = q < 1 ? 1 : (q > 8 ? 8 : q);
+  const int threads = (count + q - 1) / q;
+  sample_rows_kernel<<<(threads + 255) / 256, 256, 0, st>>>(pk, start, count, q, rows);
   return hipGetLastError();
 }
 
@@ -610,8 +783,8 @@ hipError_t launch_prep(const float* C, int k, int d, float* bias, uint16_t* Chat
 }
 
 hipError_t launch_scan(const int32_t* counts, int k, int R, int32_t* off, int32_t* cursor,
-                       int32_t* item_off, hipStream_t st) {
-  scan_kernel<<<1, 1024, 0, st>>>(counts, k, R, off, cursor, item_off);
+                       int2* ovf, int32_t* ovf_n, hipStream_t st) {
+  scan_kernel<<<1, 1024, 0, st>>>(counts, k, R, off, cursor, ovf, ovf_n);
   return hipGetLastError();
 }
 
@@ -623,28 +796,43 @@ hipError_t launch_scatter(const int32_t* labels, const uint32_t* rows, int nb, i
 }
 
 hipError_t launch_group(bool bf16, const void* X, int d, const uint32_t* order,
-                        const int32_t* off, const int32_t* item_off, int k, int R, int nb,
-                        float* s_acc, hipStream_t st) {
+                        const int32_t* off, const int2* ovf, const int32_t* ovf_n, int k, int R,
+                        int nb, float* s_acc, hipStream_t st) {
   if (nb <= 0) return hipSuccess;
-  // upper bound on work items: one per non-empty cluster plus one per R rows
-  const long long items = (long long)(k < nb ? k : nb) + (nb + R - 1) / R;
+  // work items: one per cluster plus at most nb / R overflow items
+  const long long items = (long long)k + nb / R;
   const auto* x = static_cast<const unsigned char*>(X);
   const bool aligned = (uintptr_t)X % 16 == 0;
   const bool vec = aligned && d % (bf16 ? 8 : 4) == 0;
   const int ncol = vec ? d / (bf16 ? 8 : 4) : d;
+  if (ncol <= 64) {
+    const dim3 wgrid((unsigned)((items + 3) / 4)), wblock(256);
+    if (bf16) {
+      if (vec)
+        group_wave_kernel<true, true><<<wgrid, wblock, 0, st>>>(x, d, order, off, ovf, ovf_n, k, R, s_acc);
+      else
+        group_wave_kernel<true, false><<<wgrid, wblock, 0, st>>>(x, d, order, off, ovf, ovf_n, k, R, s_acc);
+    } else {
+      if (vec)
+        group_wave_kernel<false, true><<<wgrid, wblock, 0, st>>>(x, d, order, off, ovf, ovf_n, k, R, s_acc);
+      else
+        group_wave_kernel<false, false><<<wgrid, wblock, 0, st>>>(x, d, order, off, ovf, ovf_n, k, R, s_acc);
+    }
+    return hipGetLastError();
+  }
   int nt = 256;
   if (ncol < 256) nt = (((256 / ncol) * ncol + 63) / 64) * 64;
   const dim3 grid((unsigned)items), block(nt);
   if (bf16) {
     if (vec)
-      group_kernel<true, true><<<grid, block, 0, st>>>(x, d, order, off, item_off, k, R, s_acc);
+      group_kernel<true, true><<<grid, block, 0, st>>>(x, d, order, off, ovf, ovf_n, k, R, s_acc);
     else
-      group_kernel<true, false><<<grid, block, 0, st>>>(x, d, order, off, item_off, k, R, s_acc);
+      group_kernel<true, false><<<grid, block, 0, st>>>(x, d, order, off, ovf, ovf_n, k, R, s_acc);
   } else {
     if (vec)
-      group_kernel<false, true><<<grid, block, 0, st>>>(x, d, order, off, item_off, k, R, s_acc);
+      group_kernel<false, true><<<grid, block, 0, st>>>(x, d, order, off, ovf, ovf_n, k, R, s_acc);
     else
-      group_kernel<false, false><<<grid, block, 0, st>>>(x, d, order, off, item_off, k, R, s_acc);
+      group_kernel<false, false><<<grid, block, 0, st>>>(x, d, order, off, ovf, ovf_n, k, R, s_acc);
   }
   return hipGetLastError();
 }
