@@ -48,6 +48,16 @@ def kernel_source_sha() -> str:
     return h.hexdigest()
 
 
+def assign_kernel_name(dtype: str, d: int) -> str:
+    """The assign kernel the library launches for 16-byte aligned rows of this
+    dtype and width (the dispatch rule of launch_assign in assign.hip)."""
+    if dtype == "bf16" and d in (32, 64, 96, 128):
+        return "assign_bf16_kernel (points resident in registers, 32x32x16 bf16 MFMA)"
+    if d % (8 if dtype == "bf16" else 4) == 0:
+        return "assign_ring_kernel (direct-to-LDS stage ring, 16x16 MFMA)"
+    return "assign_kernel (register-staged stages, 16x16 MFMA)"
+
+
 def committed_traffic(workload: str):
     """HBM bytes per assign launch from the committed counter summary
     (rocprofv3 FETCH_SIZE + WRITE_SIZE, scaled by a plain copy of known size),
@@ -251,7 +261,7 @@ def main() -> int:
                    "steps_per_run": S},
         "mfma_peak_frac": round(value / peak, 4),
         "roofline": {
-            "kernel": "assign_kernel (fused MFMA assign)",
+            "kernel": assign_kernel_name(W["dtype"], d),
             "bound": "mfma",
             "achieved": round(assign_tflops, 3) if assign_tflops else None,
             "peak": peak,

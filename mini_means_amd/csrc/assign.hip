@@ -322,6 +322,331 @@ __global__ __launch_bounds__(kThreads, 1) void assign_kernel(
   }
 }
 
+// ---------------------------------------------------------------------------
+// The same tiling for rows made of whole 16-byte chunks, with the stage data
+// moved by the direct global-to-LDS path of gfx950 (global_load_lds_dwordx4):
+// no register round trip and no LDS store instructions. Three stage buffers
+// form a ring, so the loads of stage t + 2 are in flight while the MFMAs
+// consume stage t, and one wait plus one barrier close each stage.
+//
+// A direct load writes the 64 lanes' 16-byte pieces to 1 KB of consecutive
+// LDS, i.e. 8 unpadded 128-byte rows per wave load. To keep the MFMA operand
+// reads (16 rows, one chunk each) free of bank conflicts the chunk positions
+// are swizzled: chunk c of row r sits at position c ^ (r % 8); each lane
+// fetches the chunk that belongs at its position. In the last stage of a
+// ragged row the chunks past the row end are zeroed in LDS before use, and
+// the loads for them read the row's first chunk (in bounds, finite).
+// ---------------------------------------------------------------------------
+typedef __attribute__((address_space(3))) void* lds_ptr_t;
+
+constexpr int kRing = 3;                         // stage buffers
+constexpr int kRowsStage = kTP + kTC;            // point rows, then centroid rows
+constexpr int kStageBytes = kRowsStage * kSlab;  // 48 KB
+constexpr int kLoadsPerWave = kRowsStage / 8 / (kThreads / 64);  // 8-row wave loads
+
+// Chunk position of chunk c in row r. Rows r and r + 8 use different
+// positions, so 8 or 16 consecutive rows read at one chunk index touch
+// distinct banks whether the LDS serves 8 lanes (32 banks) or 16 lanes (64
+// banks) of a 16-byte read per cycle.
+__device__ __forceinline__ int swz_pos(int r, int c) { return c ^ (r & 7) ^ ((r >> 3) & 1); }
+__device__ __forceinline__ int swz(int r, int c) { return r * kSlab + (swz_pos(r, c) << 4); }
+
+// One wave-wide direct load: lane i's 16 bytes at src go to LDS bytes
+// [lds + 16 i, lds + 16 i + 16); lds must be wave-uniform. Written as asm so
+// that the compiler does not treat every later LDS read as aliasing the load
+// (it would wait for all loads in flight before each one); the asm has no
+// register outputs, and completion is waited for with EMK_WAIT_VMCNT.
+// M0 is clobbered: the backend reserves it and sets it right before any
+// instruction that reads it, so no value of its own is live across the asm.
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+__device__ __forceinline__ void load_lds16(const void* src, void* lds) {
+  const uint32_t m0 = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(lds_ptr_t)lds);
+  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off" ::"s"(m0), "v"(src)
+               : "memory", "m0");
+}
+#pragma clang diagnostic pop
+
+// s_waitcnt immediate that waits for vmcnt <= n only (gfx9 encoding).
+#define EMK_WAIT_VMCNT(n) __builtin_amdgcn_s_waitcnt(((n) & 15) | (((n) >> 4) << 14) | (7 << 4) | (15 << 8))
+
+// Workgroup barrier that orders LDS accesses only. __syncthreads() also
+// orders global memory, which waits for every load in flight, the ring loads
+// of later stages included; their completion is waited for explicitly.
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
+template <bool BF16>
+__global__ __launch_bounds__(kThreads, 1) void assign_ring_kernel(
+    const unsigned char* __restrict__ X, int d, const uint32_t* __restrict__ rows, int nrows,
+    const unsigned char* __restrict__ Cs, const float* __restrict__ bias, int k,
+    int32_t* __restrict__ labels, float* __restrict__ dists, int32_t* __restrict__ counts,
+    double* __restrict__ obj) {
+  constexpr int ES = BF16 ? 2 : 4;
+  constexpr int EPV = 16 / ES;
+  constexpr int EPS = kSlab / ES;
+  __shared__ __attribute__((aligned(1024))) unsigned char ring[kRing * kStageBytes];
+  __shared__ float m_s[kWM][kTP];
+  __shared__ int m_j[kWM][kTP];
+  __shared__ float xn_s[kTP];
+  __shared__ double red[kThreads / 64];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int wm = wave >> 1;
+  const int wn = wave & 1;
+  const int tile0 = blockIdx.x * kTP;
+  const size_t rowbytes = (size_t)d * ES;
+  const int nst = (d + EPS - 1) / EPS;
+  const int npan = (k + kTC - 1) / kTC;
+  const int total = nst * npan;
+
+  // Wave loads of this wave: load i covers stage rows 8 g .. 8 g + 7 with
+  // g = wave * kLoadsPerWave + i; this lane fills LDS position lane % 8 of
+  // row 8 g + lane / 8, i.e. logical chunk swz_pos(row, lane % 8). Stages are
+  // issued in order; (ip, is) is the next stage to issue, islot its buffer.
+  // Source = row pointer (points: fixed; centroids: per panel) + the stage's
+  // column + the lane's chunk.
+  const int wv = __builtin_amdgcn_readfirstlane(wave);
+  const int lr = lane >> 3;
+  const bool ragged = d % EPS != 0;
+  const unsigned char* rowp[kLoadsPerWave];
+  int pcol[kLoadsPerWave];
+  auto centroid_row = [&](int panel, int g) {
+    const int j = min(panel * kTC + 8 * g - kTP + lr, k - 1);
+    return Cs + (size_t)j * rowbytes;
+  };
+#pragma unroll
+  for (int i = 0; i < kLoadsPerWave; ++i) {
+    const int g = wv * kLoadsPerWave + i;
+    pcol[i] = swz_pos(8 * g + lr, lane & 7) * EPV;
+    if (8 * g < kTP) {
+      const int slot = min(tile0 + 8 * g + lr, nrows - 1);
+      const size_t ri = rows ? (size_t)rows[slot] : (size_t)slot;
+      rowp[i] = X + ri * rowbytes;
+    } else {
+      rowp[i] = centroid_row(0, g);
+    }
+  }
+  int ip = 0, is = 0, islot = 0, issued = 0;
+  auto issue_next = [&]() {
+    unsigned char* dst = ring + islot * kStageBytes;
+#pragma unroll
+    for (int i = 0; i < kLoadsPerWave; ++i) {
+      const int col = is * EPS + pcol[i];
+      const int c = ragged && col >= d ? 0 : col;
+      load_lds16(rowp[i] + (size_t)c * ES, dst + 1024 * (wv * kLoadsPerWave + i));
+    }
+    islot = islot + 1 == kRing ? 0 : islot + 1;
+    if (issued + 1 < total) {  // past the end the last stage is loaded again
+      ++issued;
+      if (++is == nst) {
+        is = 0;
+        ++ip;
+#pragma unroll
+        for (int i = 0; i < kLoadsPerWave; ++i) {
+          const int g = wv * kLoadsPerWave + i;
+          if (8 * g >= kTP) rowp[i] = centroid_row(ip, g);
+        }
+      }
+    }
+  };
+
+  f32x4 acc[4][4];
+  f32x4 bnext[4];
+  auto load_bias = [&](int panel) {
+#pragma unroll
+    for (int mb = 0; mb < 4; ++mb)
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        const int j = panel * kTC + wm * 64 + mb * 16 + 4 * (lane >> 4) + v;
+        bnext[mb][v] = j < k ? bias[j] : -__builtin_inff();
+      }
+  };
+  auto init_acc = [&]() {
+#pragma unroll
+    for (int mb = 0; mb < 4; ++mb)
+#pragma unroll
+      for (int nb = 0; nb < 4; ++nb) acc[mb][nb] = bnext[mb];
+  };
+
+  float best[4];
+  int bidx[4];
+#pragma unroll
+  for (int nb = 0; nb < 4; ++nb) {
+    best[nb] = -__builtin_inff();
+    bidx[nb] = -1;
+  }
+  // |x|^2 partials: thread (rb, ch) covers chunk ch of point rows rb + 64 i
+  const int ch = tid & 7, rb = tid >> 3;
+  constexpr int kXR = kTP / (kThreads / 8);
+  float xpart[kXR];
+#pragma unroll
+  for (int i = 0; i < kXR; ++i) xpart[i] = 0.0f;
+
+  load_bias(0);
+  init_acc();
+  // Exactly kLoadsPerWave ring loads are issued per stage (the last stages
+  // reload the final stage into a buffer that is no longer read), so "the
+  // previous stage's loads are done" is always vmcnt <= kLoadsPerWave.
+  issue_next();
+  issue_next();
+  EMK_WAIT_VMCNT(kLoadsPerWave);
+  lds_barrier();
+
+  int panel = 0, s = 0, cslot = 0;
+  for (int t = 0; t < total; ++t) {
+    const bool last_s = s == nst - 1;
+    const bool more_p = panel + 1 < npan;
+    if (last_s && more_p) load_bias(panel + 1);  // before the ring loads: retired by the stage wait
+    unsigned char* cur = ring + cslot * kStageBytes;
+    if (ragged && last_s) {
+      // zero the chunks past the row end (points and centroids)
+      const u32x4 z = {0u, 0u, 0u, 0u};
+      for (int q = tid; q < kRowsStage * kChunks; q += kThreads) {
+        const int r = q >> 3, c = q & 7;
+        if (s * EPS + c * EPV >= d) *reinterpret_cast<u32x4*>(cur + swz(r, c)) = z;
+      }
+      lds_barrier();
+    }
+    if (panel == 0) {
+      const bool in = s * EPS + ch * EPV < d;
+#pragma unroll
+      for (int i = 0; i < kXR; ++i)
+        if (in) xpart[i] += sumsq16<BF16>(*reinterpret_cast<const u32x4*>(cur + swz(rb + 64 * i, ch)));
+    }
+#pragma unroll
+    for (int kk = 0; kk < kSlab / 64; ++kk) {
+      const int pc = swz_pos(lane & 15, kk * 4 + (lane >> 4)) << 4;  // rows are 16-aligned + lane % 16
+      u32x4 a[4], b[4];
+#pragma unroll
+      for (int mb = 0; mb < 4; ++mb)
+        a[mb] = *reinterpret_cast<const u32x4*>(
+            cur + (kTP + wm * 64 + mb * 16 + (lane & 15)) * kSlab + pc);
+#pragma unroll
+      for (int nb = 0; nb < 4; ++nb)
+        b[nb] = *reinterpret_cast<const u32x4*>(cur + (wn * 64 + nb * 16 + (lane & 15)) * kSlab + pc);
+      if constexpr (BF16) {
+#pragma unroll
+        for (int mb = 0; mb < 4; ++mb)
+#pragma unroll
+          for (int nb = 0; nb < 4; ++nb)
+            acc[mb][nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                __builtin_bit_cast(bf16x8, a[mb]), __builtin_bit_cast(bf16x8, b[nb]),
+                acc[mb][nb], 0, 0, 0);
+      } else {
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+#pragma unroll
+          for (int mb = 0; mb < 4; ++mb)
+#pragma unroll
+            for (int nb = 0; nb < 4; ++nb)
+              acc[mb][nb] = __builtin_amdgcn_mfma_f32_16x16x4f32(
+                  __uint_as_float(a[mb][q]), __uint_as_float(b[nb][q]), acc[mb][nb], 0, 0, 0);
+      }
+      // the loads of stage t + 2, issued while the matrix core works on this
+      // stage's first half
+      if (kk == 0) issue_next();
+    }
+    if (last_s) {
+      // panel complete: fold it into the running best (centroids in increasing order)
+#pragma unroll
+      for (int nb = 0; nb < 4; ++nb)
+#pragma unroll
+        for (int mb = 0; mb < 4; ++mb)
+#pragma unroll
+          for (int v = 0; v < 4; ++v) {
+            const float sc = acc[mb][nb][v];
+            if (sc > best[nb]) {
+              best[nb] = sc;
+              bidx[nb] = panel * kTC + wm * 64 + mb * 16 + 4 * (lane >> 4) + v;
+            }
+          }
+      if (more_p) init_acc();
+    }
+    // the next stage's loads have landed in LDS for this wave, then for all
+    EMK_WAIT_VMCNT(kLoadsPerWave);
+    lds_barrier();
+    cslot = cslot + 1 == kRing ? 0 : cslot + 1;
+    if (last_s) {
+      s = 0;
+      ++panel;
+    } else {
+      ++s;
+    }
+  }
+
+  EMK_WAIT_VMCNT(0);  // no ring load may still be writing LDS at exit
+
+  // |x|^2: fold the eight chunk threads of each point row (adjacent lanes)
+#pragma unroll
+  for (int i = 0; i < kXR; ++i) {
+    float v = xpart[i];
+#pragma unroll
+    for (int o = 1; o < 8; o <<= 1) v += __shfl_xor(v, o, 64);
+    if (ch == 0) xn_s[rb + 64 * i] = v;
+  }
+  // merge the four lane groups that share a point
+#pragma unroll
+  for (int nb = 0; nb < 4; ++nb) {
+    float sc = best[nb];
+    int j = bidx[nb];
+#pragma unroll
+    for (int off = 16; off <= 32; off <<= 1) {
+      const float os = __shfl_xor(sc, off, 64);
+      const int oj = __shfl_xor(j, off, 64);
+      if (os > sc || (os == sc && (unsigned)oj < (unsigned)j)) {
+        sc = os;
+        j = oj;
+      }
+    }
+    if ((lane >> 4) == 0) {
+      m_s[wm][wn * 64 + nb * 16 + lane] = sc;
+      m_j[wm][wn * 64 + nb * 16 + lane] = j;
+    }
+  }
+  __syncthreads();
+
+  double dsum = 0.0;
+  if (tid < kTP) {
+    const int p = tid;
+    float sc = m_s[0][p];
+    int j = m_j[0][p];
+#pragma unroll
+    for (int w = 1; w < kWM; ++w) {
+      const float s1 = m_s[w][p];
+      const int j1 = m_j[w][p];
+      if (s1 > sc || (s1 == sc && (unsigned)j1 < (unsigned)j)) {
+        sc = s1;
+        j = j1;
+      }
+    }
+    if (j < 0 || j >= k) j = 0;  // only reachable with non-finite data
+    const int slot = tile0 + p;
+    if (slot < nrows) {
+      const float dist = fmaxf(xn_s[p] - 2.0f * sc, 0.0f);
+      labels[slot] = j;
+      if (dists) dists[slot] = dist;
+      if (counts) atomicAdd(&counts[j], 1);
+      dsum = (double)dist;
+    }
+  }
+  if (obj) {
+    dsum = wave_sum(dsum);
+    if (lane == 0) red[wave] = dsum;
+    __syncthreads();
+    if (tid == 0) {
+      double t = 0.0;
+      for (int w = 0; w < kThreads / 64; ++w) t += red[w];
+      atomicAdd(obj, t);
+    }
+  }
+}
+
 }  // namespace
 
 hipError_t launch_assign(bool bf16, const void* X, int d, const uint32_t* rows, int nrows,
@@ -337,15 +662,15 @@ hipError_t launch_assign(bool bf16, const void* X, int d, const uint32_t* rows, 
   const bool aligned = ((uintptr_t)X % 16 == 0) && ((uintptr_t)Cs % 16 == 0);
   if (bf16) {
     if (aligned && d % 8 == 0)
-      assign_kernel<true, true><<<grid, block, 0, st>>>(x, d, rows, nrows, c, bias, k, labels,
-                                                        dists, counts, obj);
+      assign_ring_kernel<true><<<grid, block, 0, st>>>(x, d, rows, nrows, c, bias, k, labels,
+                                                       dists, counts, obj);
     else
       assign_kernel<true, false><<<grid, block, 0, st>>>(x, d, rows, nrows, c, bias, k, labels,
                                                          dists, counts, obj);
   } else {
     if (aligned && d % 4 == 0)
-      assign_kernel<false, true><<<grid, block, 0, st>>>(x, d, rows, nrows, c, bias, k, labels,
-                                                         dists, counts, obj);
+      assign_ring_kernel<false><<<grid, block, 0, st>>>(x, d, rows, nrows, c, bias, k, labels,
+                                                        dists, counts, obj);
     else
       assign_kernel<false, false><<<grid, block, 0, st>>>(x, d, rows, nrows, c, bias, k, labels,
                                                           dists, counts, obj);

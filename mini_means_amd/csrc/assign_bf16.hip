@@ -145,29 +145,32 @@ __global__ __launch_bounds__(kThreads, 1) void assign_bf16_kernel(
                                                           __builtin_bit_cast(bf16x8, pB[pb][ks]),
                                                           acc[pb], 0, 0, 0);
   };
-  // Fold a finished block into the running best: a max of the 16 scores per
-  // point; the exact walk over the 16 only when some lane improved.
+  // Fold a finished block into the running best: the max m of the 16 scores
+  // per point; only when some lane of the wave improves on its best does the
+  // wave locate, on those lanes, the first of the 16 slots holding m (slots
+  // are in increasing centroid order: row 8 * (v / 4) + (v % 4) + 4 * half),
+  // which is the lowest-index maximum, as an ordered strict-> walk finds.
   auto fold = [&](const f32x16* acc, int base) {
+    float m[kPB];
     bool imp[kPB];
 #pragma unroll
     for (int pb = 0; pb < kPB; ++pb) {
       const f32x16 c = acc[pb];
-      const float m = fmaxf(max3f(max3f(c[0], c[1], c[2]), max3f(c[3], c[4], c[5]),
-                                  max3f(c[6], c[7], c[8])),
-                            max3f(max3f(c[9], c[10], c[11]), max3f(c[12], c[13], c[14]), c[15]));
-      imp[pb] = m > best[pb];
+      m[pb] = fmaxf(max3f(max3f(c[0], c[1], c[2]), max3f(c[3], c[4], c[5]),
+                          max3f(c[6], c[7], c[8])),
+                    max3f(max3f(c[9], c[10], c[11]), max3f(c[12], c[13], c[14]), c[15]));
+      imp[pb] = m[pb] > best[pb];
     }
 #pragma unroll
     for (int pb = 0; pb < kPB; ++pb) {
       if (__builtin_amdgcn_ballot_w64(imp[pb])) {
         const f32x16 c = acc[pb];
-        // rows of this lane in increasing order: 8 * (v / 4) + (v % 4) + 4 * half
+        int v0 = 15;
 #pragma unroll
-        for (int v = 0; v < 16; ++v) {
-          if (c[v] > best[pb]) {
-            best[pb] = c[v];
-            bidx[pb] = base + 8 * (v >> 2) + (v & 3);
-          }
+        for (int v = 14; v >= 0; --v) v0 = c[v] == m[pb] ? v : v0;
+        if (imp[pb]) {
+          best[pb] = m[pb];
+          bidx[pb] = base + 8 * (v0 >> 2) + (v0 & 3);
         }
       }
     }

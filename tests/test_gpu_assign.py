@@ -51,6 +51,8 @@ CASES_F32 = [
     ("tiny", 100, 1, 1),
     ("tiny", 129, 7, 129),
     ("sift", 300, 250, 17),
+    ("embedding", 1500, 36, 700),
+    ("embedding", 513, 1028, 520),
 ]
 
 
@@ -64,7 +66,8 @@ def test_assign_fp32(mm, gen, n, d, k):
     check_dists(X, C, None, lab, dist, what=f"{gen} {n}x{d} k={k}")
 
 
-CASES_BF16 = [(2000, 128, 300), (1000, 64, 129), (777, 40, 50), (500, 37, 20), (300, 256, 1)]
+CASES_BF16 = [(2000, 128, 300), (1000, 64, 129), (777, 40, 50), (500, 37, 20), (300, 256, 1),
+              (900, 520, 300), (600, 1024, 257)]
 
 
 @pytest.mark.parametrize("n,d,k", CASES_BF16)
