@@ -34,7 +34,10 @@ Do."):
                     last pass.
 * precision         README "Data precision": centroids and running sums are
                     stored in fp32; only the nearest-centroid search uses the
-                    smaller format for bf16 data.
+                    smaller format: for bf16 data, and for fp32 data when
+                    bf16_search asks for the pages' GPU default (rows and
+                    centroids rounded to bf16 for the search, fp32 rows
+                    grouped).
 
 Readings where the pages are silent (each listed in the design notes):
 power-of-two rounding in log2 space; cap = largest power of two <= n/2;
@@ -221,6 +224,20 @@ def bf16_round(C: np.ndarray) -> np.ndarray:
     return b.astype(np.uint32).view(np.float32)
 
 
+def bf16_bits(X: np.ndarray) -> np.ndarray:
+    """fp32 -> nearest bf16 (ties to even), as bf16 bit patterns (uint16)."""
+    return (bf16_round(X).view(np.uint32) >> 16).astype(np.uint16)
+
+
+def search_data(X: np.ndarray, bf16_search: bool) -> np.ndarray:
+    """Data in the search format. README "Data precision": on a GPU, fp32 data
+    may be converted to bf16 for the nearest-centroid search only (the pages'
+    GPU default, opt-in here); bf16 data is searched as stored."""
+    if bf16_search and X.dtype == np.float32:
+        return bf16_bits(X)
+    return X
+
+
 def search_centroids(C: np.ndarray, X: np.ndarray) -> np.ndarray:
     """Centroids in the search format: bf16 for bf16 data, fp32 otherwise."""
     return bf16_round(C) if X.dtype == np.uint16 else np.ascontiguousarray(C, dtype=np.float32)
@@ -335,8 +352,13 @@ def train(X: np.ndarray, k: int, T: float, seed: int = 1234, *, batch_law: int =
           labels_for_step: Optional[Callable[[int, np.ndarray], np.ndarray]] = None,
           check_slots: Optional[Callable[[int, int], Optional[np.ndarray]]] = None,
           check_hook: Optional[Callable[[dict], None]] = None,
-          nthreads: int = 0) -> TrainResult:
+          nthreads: int = 0, bf16_search: bool = False) -> TrainResult:
     """e-means on X (n x d, fp32 or bf16 bits), step by step.
+
+    bf16_search: fp32 data is searched in bf16 (rows and centroids rounded to
+    bf16), while the grouping, the running sums and the centroids use the
+    fp32 rows (README "Data precision": only the search uses the smaller
+    format).
 
     labels_for_step(t, rows) may supply the labels of step t from elsewhere
     (lockstep replay). The oracle then checks them on the slots that
@@ -350,7 +372,7 @@ def train(X: np.ndarray, k: int, T: float, seed: int = 1234, *, batch_law: int =
     S_tot = rc["total_steps"]
     al = alphas(rc["alpha0"], S_tot)
     thr = rc["unused_threshold"]
-    Xf = X  # searched as stored
+    Xf = search_data(X, bf16_search)  # the search reads this; grouping reads X
 
     C = np.ascontiguousarray(to_f32(X[init_rows(n, k, seed)]), dtype=np.float32)
     N = np.zeros(k, dtype=np.float32)
@@ -369,7 +391,7 @@ def train(X: np.ndarray, k: int, T: float, seed: int = 1234, *, batch_law: int =
         for s in range(rc["steps_per_pass"][e]):
             Bt = min(B, rows_e - s * B)
             rows = perm_range(n, seed, STREAM_PERM, e, s * B, Bt)
-            Cs = search_centroids(C, X)
+            Cs = search_centroids(C, Xf)
             if labels_for_step is None:
                 lab, d1, _ = assign(Xf, Cs, rows, nthreads)
                 dist = d1
@@ -388,7 +410,7 @@ def train(X: np.ndarray, k: int, T: float, seed: int = 1234, *, batch_law: int =
                     res.label_checks.append(chk)
                 dist = dist_to(Xf, Cs, lab, rows)
             obj += float(np.sum(dist))
-            counts, sums = group(Xf, rows, lab, k)
+            counts, sums = group(X, rows, lab, k)
             a = al[t]
             b = np.float32(1.0) - a
             # running count in fp32, fixed operation order: fl(fl(b*N) + fl(a*n))

@@ -362,6 +362,41 @@ def test_finalisation_is_exact_mean_of_last_pass():
             assert np.array_equal(res.centroids[j], res.ema_centroids[j])
 
 
+def test_bf16_search_on_bf16_exact_values_is_the_bf16_data_path():
+    """README "Data precision": converting fp32 data to bf16 for the search is
+    the same search as storing the data in bf16. On fp32 data whose values are
+    bf16 numbers the two runs agree bit for bit (the bf16-data path is pinned
+    by the assignment and finalisation tests); an fp32 search of the same
+    data takes other decisions, so the option is not ignored."""
+    Xb = datagen.large_host(20000, d=32, m=64, seed=21)
+    Xf = datagen.bf16_bits_to_f32(Xb)
+    kw = dict(seed=7, batch_size=2048)
+    a = oracle.train(Xb, 64, 2.0, **kw)
+    b = oracle.train(Xf, 64, 2.0, bf16_search=True, **kw)
+    assert np.array_equal(a.labels, b.labels)
+    assert np.array_equal(a.N, b.N)
+    assert np.array_equal(a.centroids, b.centroids)
+    assert a.split_log == b.split_log
+    c = oracle.train(Xf, 64, 2.0, **kw)
+    assert not (np.array_equal(c.labels, b.labels) and np.array_equal(c.centroids, b.centroids))
+
+
+def test_bf16_search_groups_the_fp32_rows():
+    """Only the search uses bf16: the closing mean of every centroid is the
+    exact mean of the fp32 rows (not of their bf16 roundings) that the last
+    pass assigned to it."""
+    X = datagen.tiny(n=5000, d=16, seed=9)
+    assert not np.array_equal(oracle.bf16_round(X), X)
+    res = oracle.train(X, 64, 3.0, seed=5, bf16_search=True)
+    lab = res.labels
+    assert np.all(lab >= 0)
+    for j in range(64):
+        m = lab == j
+        if m.any():
+            np.testing.assert_allclose(res.centroids[j], X[m].astype(np.float64).mean(axis=0),
+                                       rtol=0, atol=1e-6)
+
+
 def test_fractional_last_pass_labels():
     X = datagen.tiny(n=2000, d=16, seed=3)
     res = oracle.train(X, 16, 1.5, seed=5, batch_size=256)
