@@ -108,7 +108,7 @@ def heldout_mse(mm, Xh, C, torch) -> float:
     return float(dist.double().mean().item())
 
 
-def time_to_target(mm, X, Xh, k, target, seeds, Ts, torch) -> dict:
+def time_to_target(mm, X, Xh, k, target, seeds, Ts, torch, bf16_search=False) -> dict:
     """Smallest median wall-clock among pass counts whose finalised held-out MSE
     reaches the Lloyd-25 held-out MSE (median over training seeds)."""
     import statistics
@@ -119,7 +119,7 @@ def time_to_target(mm, X, Xh, k, target, seeds, Ts, torch) -> dict:
         for s in seeds:
             torch.cuda.synchronize()
             t0 = time.perf_counter()
-            out = mm.train(X, k, T, s, capture_labels=True)
+            out = mm.train(X, k, T, s, capture_labels=True, bf16_search=bf16_search)
             torch.cuda.synchronize()
             walls.append(time.perf_counter() - t0)
             mses.append(heldout_mse(mm, Xh, out.centroids, torch))
@@ -169,6 +169,9 @@ def main() -> int:
     ap.add_argument("--ttt-seeds", type=int, default=3)
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
                     help="also run a plain device copy of BYTES (counter calibration)")
+    ap.add_argument("--bf16-search", action="store_true",
+                    help="search fp32 data in bf16 (README \"Data precision\": the pages' GPU "
+                         "default); the held-out MSE is still evaluated in fp32")
     ap.add_argument("--print-source-sha", action="store_true")
     args = ap.parse_args()
     if args.print_source_sha:
@@ -200,18 +203,21 @@ def main() -> int:
     sizes = batch_sizes(rc)[:K]
     es = 2 if W["dtype"] == "bf16" else 4
     flops = float(sum(2.0 * b * k * d for b in sizes))
+    bsearch = bool(args.bf16_search) and W["dtype"] == "f32"
+    sdtype = "bf16" if bsearch else W["dtype"]   # arithmetic type of the search
+    tag = args.workload + ("_bf16search" if bsearch else "")
 
     X, Xh, Xhost = make_data(args.workload, W, torch)
 
     # warm-up (untimed)
     if Wm > 0:
-        mm.train(X, k, T, args.seed, max_steps=Wm)
+        mm.train(X, k, T, args.seed, max_steps=Wm, bf16_search=bsearch)
         torch.cuda.synchronize()
 
     # timed: exactly K steps of the schedule
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    out = mm.train(X, k, T, args.seed, max_steps=K)
+    out = mm.train(X, k, T, args.seed, max_steps=K, bf16_search=bsearch)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     value = flops / wall / 1e12
@@ -228,11 +234,11 @@ def main() -> int:
         log(f"copied {args.copy_calibration} bytes x3 for counter calibration")
 
     # profiled run: device time per kernel class (HIP events on the launch stream)
-    prof = mm.train(X, k, T, args.seed, max_steps=K, profile=True).stats
+    prof = mm.train(X, k, T, args.seed, max_steps=K, profile=True, bf16_search=bsearch).stats
     torch.cuda.synchronize()
     a_ms = prof["ms_assign"]
     assign_tflops = flops / (a_ms / 1e3) / 1e12 if a_ms > 0 else None
-    peak = MFMA_PEAK_TFLOPS[W["dtype"]]
+    peak = MFMA_PEAK_TFLOPS[sdtype]
     group_bytes = float(sum(b * d * es + 4 * b + 4 * k * d for b in sizes))
     update_bytes = float(K * (4 * 4 * k * d))   # read s, S, C; write S, C (+ counts, small)
     g_ms = prof["ms_group"]
@@ -240,7 +246,7 @@ def main() -> int:
     log(f"device ms: assign {a_ms:.2f} bucket {prof['ms_bucket']:.2f} group {g_ms:.2f} "
         f"update {u_ms:.2f} revive {prof['ms_revive']:.2f} sample {prof['ms_sample']:.2f}")
 
-    traffic, tsrc = committed_traffic(args.workload)
+    traffic, tsrc = committed_traffic(tag)
     log(f"traffic: {traffic} ({tsrc})")
 
     line = {
@@ -254,14 +260,16 @@ def main() -> int:
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": W["dtype"],
+        "dtype": sdtype,
         "data": "synthetic",
         "config": {"workload": DESCR[args.workload], "n": n, "d": d, "k": k, "T": T,
                    "batch": rc["batch_size"], "alpha0": round(rc["alpha0"], 6),
-                   "steps_per_run": S},
+                   "steps_per_run": S,
+                   "search": "bf16 (fp32 rows rounded for the search; sums in fp32)" if bsearch
+                   else ("bf16" if W["dtype"] == "bf16" else "fp32 (exact)")},
         "mfma_peak_frac": round(value / peak, 4),
         "roofline": {
-            "kernel": assign_kernel_name(W["dtype"], d),
+            "kernel": assign_kernel_name(sdtype, d),
             "bound": "mfma",
             "achieved": round(assign_tflops, 3) if assign_tflops else None,
             "peak": peak,
@@ -289,7 +297,7 @@ def main() -> int:
                 target = json.load(f)["heldout_mse"]
             seeds = [args.seed + i for i in range(args.ttt_seeds)]
             ttt = time_to_target(mm, X, Xh, k, target, seeds, [1.0, 1.5, 2.0, 2.5, 3.0, 5.0],
-                                 torch)
+                                 torch, bsearch)
             line["s_to_lloyd25"] = ttt["seconds"]
             line["time_to_target"] = ttt
         else:

@@ -83,6 +83,13 @@ typedef struct emeans_opts {
   int64_t max_steps;          /* 0: all steps; > 0: stop after this many update steps
                                  (the schedule stays that of the full run); the
                                  closing mean is taken only if the last pass began */
+  int32_t bf16_search;        /* 1: fp32 X is searched in bf16 (README "Data precision":
+                                 the pages' GPU default): the rows and the centroids
+                                 are rounded to bf16 (nearest, ties to even) for the
+                                 nearest-centroid search only, and the distances are
+                                 those of the rounded vectors; grouping, running sums
+                                 and centroids use the fp32 rows. 0: fp32 X is searched
+                                 in fp32 (exact). Ignored for bf16 X. */
 } emeans_opts;
 
 /* Recipe and statistics of a run (README "Settings and results": recipe, obj,
@@ -108,6 +115,8 @@ typedef struct emeans_stats {
   /* with opts->profile: summed device time of each kernel class, from HIP
      events recorded on opts->stream around the launches */
   double ms_assign, ms_bucket, ms_group, ms_update, ms_revive, ms_sample;
+                                       /* ms_sample includes, with bf16_search, the
+                                          gather and bf16 rounding of the batch rows */
   int64_t steps_run;                   /* update steps executed */
 } emeans_stats;
 
@@ -137,7 +146,9 @@ int emeans_train(const void* X, int64_t n, int32_t d, int32_t k, double T, uint6
 /* Nearest centroid of each row of X (README "Settings and results":
  * em.assign): labels[i] = argmin_j ||x_i - c_j||^2 (lowest j on ties) and
  * dists[i] = that squared distance (fp32, >= 0). For bf16 X the centroids
- * are searched in bf16 (README "Data precision").
+ * are searched in bf16 (README "Data precision"); so are fp32 X and the
+ * centroids with opts->bf16_search (rows and centroids rounded to bf16, the
+ * distances those of the rounded vectors; workspace n x d bf16).
  *   X        device, n x d, opts->dtype      C       device, k x d fp32
  *   labels   device, n int32 output          dists   device, n fp32 output or NULL
  * Errors: EINVAL (n < 0, d < 1, k < 1, n >= 2^31, NULL pointers), EDTYPE,

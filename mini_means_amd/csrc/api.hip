@@ -222,17 +222,22 @@ int emeans_assign(const void* X, int64_t n, int32_t d, const float* C, int32_t k
     return rc;
   hipStream_t st = static_cast<hipStream_t>(opts ? opts->stream : nullptr);
   const bool bf16 = dtype == EMEANS_BF16;
+  const bool bsearch = !bf16 && opts && opts->bf16_search;  // fp32 rows searched in bf16
   void* base = nullptr;
   float* bias = nullptr;
   uint16_t* chat = nullptr;
+  uint16_t* xb = nullptr;
   Arena ar;
   ar.want(&bias, (size_t)k);
-  if (bf16) ar.want(&chat, (size_t)k * d);
+  if (bf16 || bsearch) ar.want(&chat, (size_t)k * d);
+  if (bsearch) ar.want(&xb, (size_t)n * d);
   rc = EMEANS_OK;
   HIP_TRY(ar.alloc(&base, st));
   HIP_TRY(launch_prep(C, k, d, bias, chat, st));
-  HIP_TRY(launch_assign(bf16, X, d, nullptr, (int)n, bf16 ? (const void*)chat : (const void*)C,
-                        bias, k, labels, dists, nullptr, nullptr, st));
+  if (bsearch) HIP_TRY(launch_cast_rows(static_cast<const float*>(X), d, nullptr, (int)n, xb, st));
+  HIP_TRY(launch_assign(bf16 || bsearch, bsearch ? (const void*)xb : X, d, nullptr, (int)n,
+                        (bf16 || bsearch) ? (const void*)chat : (const void*)C, bias, k, labels,
+                        dists, nullptr, nullptr, st));
 done:
   if (base) {
     const hipError_t e = hipFreeAsync(base, st);
@@ -268,6 +273,9 @@ int emeans_train(const void* X, int64_t n, int32_t d, int32_t k, double T, uint6
 
   hipStream_t st = static_cast<hipStream_t>(opts ? opts->stream : nullptr);
   const bool bf16 = dtype == EMEANS_BF16;
+  // fp32 rows searched in bf16: each batch is gathered and rounded into xb
+  const bool bsearch = !bf16 && opts && opts->bf16_search;
+  const bool sbf = bf16 || bsearch;  // the search runs in bf16 against chat
   const bool profile = opts && opts->profile;
   const size_t kd = (size_t)k * d;
   const int64_t B = r.B;
@@ -284,7 +292,7 @@ int emeans_train(const void* X, int64_t n, int32_t d, int32_t k, double T, uint6
   int2* ovf = nullptr;
   float *bdist = nullptr, *s_acc = nullptr, *S = nullptr, *N = nullptr, *LS = nullptr,
         *bias = nullptr, *n0 = nullptr, *pair_n = nullptr;
-  uint16_t* chat = nullptr;
+  uint16_t *chat = nullptr, *xb = nullptr;
   // per pass: [0, P) sum of distances, [P, 3P) sum n^2 and sum n, [3P, 4P) splits (int64)
   double* dstat = nullptr;
   int64_t* counters = nullptr;
@@ -327,7 +335,8 @@ int emeans_train(const void* X, int64_t n, int32_t d, int32_t k, double T, uint6
   ar.want(&N, (size_t)k);
   ar.want(&LS, kd);
   ar.want(&bias, (size_t)k);
-  if (bf16) ar.want(&chat, kd);
+  if (sbf) ar.want(&chat, kd);
+  if (bsearch) ar.want(&xb, (size_t)B * d);
   ar.want(&dstat, (size_t)4 * EMEANS_MAX_PASSES);
   ar.want(&counters, 4);
   if (log_cap > 0) ar.want(&dlog, (size_t)3 * log_cap);
@@ -376,8 +385,15 @@ int emeans_train(const void* X, int64_t n, int32_t d, int32_t k, double T, uint6
       const int nb = (int)(rem < B ? rem : B);
       const float a = alpha_at(r.alpha0, t, r.S);
       const float b = 1.0f - a;
-      HIP_TRY(timed(kSample, [&] { return launch_sample_rows(pk, (uint64_t)(s * B), nb, rows, st); }));
+      HIP_TRY(timed(kSample, [&] {
+        hipError_t er = launch_sample_rows(pk, (uint64_t)(s * B), nb, rows, st);
+        if (er != hipSuccess || !bsearch) return er;
+        return launch_cast_rows(static_cast<const float*>(X), d, rows, nb, xb, st);
+      }));
       HIP_TRY(timed(kAssign, [&] {
+        if (bsearch)
+          return launch_assign(true, xb, d, nullptr, nb, chat, bias, k, blab, bdist, counts,
+                               dstat + e, st);
         return launch_assign(bf16, X, d, rows, nb, bf16 ? (const void*)chat : (const void*)centroids,
                              bias, k, blab, bdist, counts, dstat + e, st);
       }));

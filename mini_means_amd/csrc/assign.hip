@@ -481,9 +481,9 @@ __global__ __launch_bounds__(kThreads, 1) void assign_ring_kernel(
     best[nb] = -__builtin_inff();
     bidx[nb] = -1;
   }
-  // |x|^2 partials: thread (rb, ch) covers chunk ch of point rows rb + 64 i
+  // |x|^2 partials: thread (rb, ch) covers chunk ch of point rows rb + kRowsPerPass i
   const int ch = tid & 7, rb = tid >> 3;
-  constexpr int kXR = kTP / (kThreads / 8);
+  constexpr int kXR = kTP / kRowsPerPass;
   float xpart[kXR];
 #pragma unroll
   for (int i = 0; i < kXR; ++i) xpart[i] = 0.0f;
@@ -517,7 +517,9 @@ __global__ __launch_bounds__(kThreads, 1) void assign_ring_kernel(
       const bool in = s * EPS + ch * EPV < d;
 #pragma unroll
       for (int i = 0; i < kXR; ++i)
-        if (in) xpart[i] += sumsq16<BF16>(*reinterpret_cast<const u32x4*>(cur + swz(rb + 64 * i, ch)));
+        if (in)
+          xpart[i] += sumsq16<BF16>(
+              *reinterpret_cast<const u32x4*>(cur + swz(rb + kRowsPerPass * i, ch)));
     }
 #pragma unroll
     for (int kk = 0; kk < kSlab / 64; ++kk) {
@@ -588,7 +590,7 @@ __global__ __launch_bounds__(kThreads, 1) void assign_ring_kernel(
     float v = xpart[i];
 #pragma unroll
     for (int o = 1; o < 8; o <<= 1) v += __shfl_xor(v, o, 64);
-    if (ch == 0) xn_s[rb + 64 * i] = v;
+    if (ch == 0) xn_s[rb + kRowsPerPass * i] = v;
   }
   // merge the four lane groups that share a point
 #pragma unroll

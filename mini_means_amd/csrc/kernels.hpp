@@ -39,6 +39,10 @@ hipError_t launch_init_centroids(bool bf16, const void* X, int d, const PermKey&
 // bias[j] = -|c_j|^2 / 2 in the search format; Chat = bf16(C) when non-null.
 hipError_t launch_prep(const float* C, int k, int d, float* bias, uint16_t* Chat, hipStream_t st);
 
+// out[r] = bf16(X[rows[r]]) for r < nrows (rows NULL: row r), row-major.
+hipError_t launch_cast_rows(const float* X, int d, const uint32_t* rows, int nrows,
+                            uint16_t* out, hipStream_t st);
+
 // off = exclusive scan of counts (k+1 entries), cursor = off[0..k); ovf lists
 // the grouping work items beyond the first R rows of each cluster as
 // (cluster, part) pairs, *ovf_n of them (room for rows / R pairs).

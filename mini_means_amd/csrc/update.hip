@@ -42,6 +42,34 @@ __global__ void sample_rows_i32_kernel(PermKey pk, uint64_t start, int count, in
   if (r < count) rows[r] = (int32_t)perm_at(start + (uint64_t)r, pk);
 }
 
+// out[r] = bf16(X[rows[r]]) (nearest, ties to even): the batch rows in the
+// bf16 search format, contiguous. Eight elements per thread when rows are
+// whole 32-byte chunks, else one.
+template <bool VEC>
+__global__ __launch_bounds__(256) void cast_rows_kernel(const float* __restrict__ X, int d,
+                                                        const uint32_t* __restrict__ rows,
+                                                        int nrows, uint16_t* __restrict__ out) {
+  constexpr int E = VEC ? 8 : 1;
+  const int per = d / E;
+  const int64_t q = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (q >= (int64_t)nrows * per) return;
+  const int r = (int)(q / per), c = (int)(q - (int64_t)r * per) * E;
+  const size_t src = (size_t)(rows ? rows[r] : (uint32_t)r) * d + c;
+  const size_t dst = (size_t)r * d + c;
+  if constexpr (VEC) {
+    const float4 a = *reinterpret_cast<const float4*>(X + src);
+    const float4 b = *reinterpret_cast<const float4*>(X + src + 4);
+    const float f[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+    uint32_t w[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+      w[e] = (uint32_t)f32_to_bf16_rne(f[2 * e]) | ((uint32_t)f32_to_bf16_rne(f[2 * e + 1]) << 16);
+    *reinterpret_cast<uint4*>(out + dst) = make_uint4(w[0], w[1], w[2], w[3]);
+  } else {
+    out[dst] = f32_to_bf16_rne(X[src]);
+  }
+}
+
 // One wave per centroid: C[j] = X[pi(j)] converted to fp32.
 __global__ __launch_bounds__(256) void init_centroids_kernel(const unsigned char* X, int bf16,
                                                              int d, PermKey pk, int k, float* C) {
@@ -759,6 +787,19 @@ hipError_t launch_sample_rows(const PermKey& pk, uint64_t start, int count, uint
   q = q < 1 ? 1 : (q > 8 ? 8 : q);
   const int threads = (count + q - 1) / q;
   sample_rows_kernel<<<(threads + 255) / 256, 256, 0, st>>>(pk, start, count, q, rows);
+  return hipGetLastError();
+}
+
+hipError_t launch_cast_rows(const float* X, int d, const uint32_t* rows, int nrows,
+                            uint16_t* out, hipStream_t st) {
+  if (nrows <= 0) return hipSuccess;
+  const bool vec = d % 8 == 0 && (uintptr_t)X % 16 == 0 && (uintptr_t)out % 16 == 0;
+  const int64_t work = (int64_t)nrows * (vec ? d / 8 : d);
+  const unsigned grid = (unsigned)((work + 255) / 256);
+  if (vec)
+    cast_rows_kernel<true><<<grid, 256, 0, st>>>(X, d, rows, nrows, out);
+  else
+    cast_rows_kernel<false><<<grid, 256, 0, st>>>(X, d, rows, nrows, out);
   return hipGetLastError();
 }
 

@@ -116,6 +116,7 @@ def lockstep(X: np.ndarray, out, k: int, T: float, seed: int, sample: int = 0,
     checking them (all slots, or `sample` random slots per step), and return
     the oracle's result and the check summary."""
     trace = out.trace.cpu().numpy()
+    Xs = oracle.search_data(X, opts.get("bf16_search", False))  # what the search reads
     rc = oracle.recipe(X.shape[0], X.shape[1], k, T, opts.get("batch_law", 0),
                        opts.get("batch_size", 0), opts.get("alpha0", 0.0),
                        opts.get("unused_threshold", -1.0))
@@ -133,10 +134,10 @@ def lockstep(X: np.ndarray, out, k: int, T: float, seed: int, sample: int = 0,
         return np.sort(rng.choice(Bt, size=sample, replace=False))
 
     def hook(chk):
-        dec, und, diff = check_labels(X, chk["C"], chk["rows"], chk["given"], chk["oracle"],
+        dec, und, diff = check_labels(Xs, chk["C"], chk["rows"], chk["given"], chk["oracle"],
                                       chk["d1"], chk["d2"], chk["given_dist"],
                                       what=f"step {chk['t']}",
-                                      C32=chk["C32"] if X.dtype == np.uint16 else None)
+                                      C32=chk["C32"] if Xs.dtype == np.uint16 else None)
         summary["decided"] += dec
         summary["undecided"] += und
         summary["undecided_differ"] += diff

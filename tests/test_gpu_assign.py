@@ -70,6 +70,26 @@ CASES_BF16 = [(2000, 128, 300), (1000, 64, 129), (777, 40, 50), (500, 37, 20), (
               (900, 520, 300), (600, 1024, 257)]
 
 
+CASES_BF16_SEARCH = [("sift", 2000, 128, 300), ("embedding", 1000, 768, 257),
+                     ("embedding", 700, 100, 40), ("tiny", 300, 37, 20), ("deep", 3000, 96, 1000)]
+
+
+@pytest.mark.parametrize("gen,n,d,k", CASES_BF16_SEARCH)
+def test_assign_bf16_search(mm, gen, n, d, k):
+    """fp32 rows searched in bf16: the oracle's assignment of the bf16-rounded
+    rows against the bf16-rounded centroids."""
+    import torch
+    X = datagen.make(gen, n, d, seed=17)
+    C = _centroids(X, k, 8)
+    lab, dist = mm.assign(to_device(X), torch.from_numpy(C).cuda(), bf16_search=True)
+    lab, dist = lab.cpu().numpy(), dist.cpu().numpy()
+    Xs = oracle.search_data(X, True)
+    Cs = oracle.bf16_round(C)
+    olab, d1, d2 = oracle.assign(Xs, Cs)
+    check_labels(Xs, Cs, None, lab, olab, d1, d2, what=f"bf16-search {gen} {n}x{d} k={k}")
+    check_dists(Xs, Cs, None, lab, dist, what=f"bf16-search {gen} {n}x{d} k={k}")
+
+
 @pytest.mark.parametrize("n,d,k", CASES_BF16)
 def test_assign_bf16(mm, n, d, k):
     X = datagen.large_host(n, d=d, m=64, seed=13)

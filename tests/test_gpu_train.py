@@ -47,6 +47,10 @@ LOCKSTEP = [
     ("ragged", "tiny", 5_003, 37, 77, 1.5, dict(batch_size=700)),
     ("no-revival", "deep", 8_000, 96, 300, 2.0, dict(unused_threshold=0.0)),
     ("alpha1-lloyd", "tiny", 4_000, 16, 32, 1.0, dict(batch_size=4000, alpha0=1.0)),
+    # fp32 data searched in bf16 (README "Data precision", the pages' GPU default)
+    ("emb-small-bf16s", "embedding", 12_000, 768, 256, 2.0, dict(bf16_search=True)),
+    ("deep-small-bf16s", "deep", 30_000, 96, 1024, 3.0, dict(bf16_search=True)),
+    ("ragged-bf16s", "tiny", 5_003, 37, 77, 1.5, dict(batch_size=700, bf16_search=True)),
 ]
 
 
