@@ -484,20 +484,21 @@ __global__ __launch_bounds__(256) void ema_kernel(int k, int d, float a, float b
 //
 // revive_kernel (one workgroup):
 //  A. all threads: threshold, dead list, uniform draws, live counts (in LDS
-//     when k <= kRvLdsN), fp64 live sums per chunk of CS clusters.
-//  B. wave 0 alone draws the donors in dead-list order. Each lane owns m
-//     consecutive chunks and keeps the inclusive prefix of the live total over
-//     lanes in a register; a draw reads it with one ballot, narrows to a chunk
-//     (one wave scan when m > 1) and to a cluster (one wave scan per 64
-//     clusters), then subtracts the donor's lost half from the prefixes. Only
-//     running counts change here.
+//     when k <= kRvLdsN), fp64 live sum of each of 64 chunks of CS = 64 V
+//     consecutive clusters.
+//  B. wave 0 alone draws the donors in dead-list order. Lane c owns chunk c
+//     and keeps its live sum and the inclusive prefix of the sums over lanes
+//     in registers. A draw finds the chunk with one ballot, then reads the
+//     chunk's live counts (V consecutive clusters per lane), takes the lane's
+//     running sums in registers plus one wave scan, and finds the cluster with
+//     a second ballot; then it subtracts the donor's lost half from the
+//     prefixes. Only running counts change here.
 //  C. all threads: chain bookkeeping. A donor picked r times before split q
 //     had its count halved r times, so the recorded count after split q fixes
 //     q's place in the donor's chain and the final count the chain's length.
 // split_kernel (many workgroups): one wave per chain applies its splits of the
 // running sums in order (chains are independent: donors are never dead).
-constexpr int kRvLdsN = 32768;   // live counts kept in LDS up to this k
-constexpr int kRvChunks = 1024;  // at most this many chunks
+constexpr int kRvLdsN = 32768;  // live counts kept in LDS up to this k
 
 __device__ __forceinline__ int halvings(float from, float to) {
   int m = 0;
@@ -508,21 +509,26 @@ __device__ __forceinline__ int halvings(float from, float to) {
   return m;
 }
 
+// VT > 0: VT clusters per lane per chunk (a power of two >= k / 4096), held in
+// registers during a draw; VT = 0: any k, counts re-read.
+template <int VT>
 __global__ __launch_bounds__(1024) void revive_kernel(ReviveArgs A) {
   __shared__ double dtmp[16];
   __shared__ int itmp[16];
-  __shared__ double csum[kRvChunks];
-  __shared__ float wN[kRvLdsN];
+  __shared__ double csum[64];
+  __shared__ __attribute__((aligned(16))) float wN[kRvLdsN];
   __shared__ int s_ndead, s_last;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
   const int k = A.k;
-  const bool lds_n = k <= kRvLdsN;
-  const int cb = (k + 64 * kRvChunks - 1) / (64 * kRvChunks);  // 64-blocks per chunk
-  const int CS = 64 * cb;
-  const int nch = (k + CS - 1) / CS;
-  const int m = (nch + 63) / 64;  // chunks per lane in phase B
+  // live counts in LDS exactly when VT <= 8 (k <= 32768); a compile-time
+  // choice keeps global loads, and waits on the draw's global stores, out of
+  // the LDS variant's draw loop
+  constexpr bool lds_n = VT >= 1 && VT <= 8;
+  static_assert(8 * 4096 <= kRvLdsN, "VT <= 8 must fit the LDS counts");
+  const int V = VT > 0 ? VT : (k + 4095) / 4096;  // clusters per lane per chunk
+  const int CS = 64 * V;  // clusters per chunk; chunk c = [c CS, (c + 1) CS)
   if (tid == 0) A.nheads[0] = 0;
 
   // ---- A --------------------------------------------------------------------
@@ -539,9 +545,11 @@ __global__ __launch_bounds__(1024) void revive_kernel(ReviveArgs A) {
     const int dd = ((double)nv < th) ? 1 : 0;
     A.flags[j] = dd;
     A.n0[j] = nv;
-    if (lds_n) wN[j] = dd ? 0.0f : nv;
+    if constexpr (lds_n) wN[j] = dd ? 0.0f : nv;
     cnt += dd;
   }
+  if constexpr (lds_n)  // zero counts past k up to the 64 chunks: no bounds test in a draw
+    for (int j = k + tid; j < 64 * CS; j += 1024) wN[j] = 0.0f;
   const int incl = block_incl_scan<int, 1024>(cnt, itmp);
   if (tid == 1023) s_ndead = incl;
   if (tid == 0) s_last = -1;
@@ -564,12 +572,16 @@ __global__ __launch_bounds__(1024) void revive_kernel(ReviveArgs A) {
   if (ndead == 0) return;
   for (int q = tid; q < ndead; q += 1024)
     A.udraw[q] = revive_uniform(A.seed, A.step, (uint64_t)A.dead[q]);
-  for (int c = tid; c < nch; c += 1024) {  // live sum of each chunk, in index order
+  {
+    // live sum of chunk c by the 16 consecutive threads 16 c .. 16 c + 15
+    const int c = tid >> 4, part = tid & 15;
     double sv = 0.0;
     const int e1 = min(k, (c + 1) * CS);
-    for (int j = c * CS; j < e1; ++j)
+    for (int j = c * CS + part; j < e1; j += 16)
       if (!A.flags[j]) sv += (double)A.N[j];
-    csum[c] = sv;
+#pragma unroll
+    for (int o = 1; o < 16; o <<= 1) sv += __shfl_xor(sv, o, 64);
+    if (part == 0) csum[c] = sv;
   }
   __threadfence_block();
   __syncthreads();
@@ -578,9 +590,12 @@ __global__ __launch_bounds__(1024) void revive_kernel(ReviveArgs A) {
 
   // ---- B: donor draws (wave 0) ----------------------------------------------
   if (wave == 0) {
-    double lsum = 0.0;
-    for (int t = 0; t < m; ++t)
-      if (lane * m + t < nch) lsum += csum[lane * m + t];
+    auto live_count = [&](int idx) -> float {
+      if constexpr (lds_n) return wN[idx];
+      if (idx >= k) return 0.0f;
+      return A.flags[idx] ? 0.0f : A.N[idx];
+    };
+    double lsum = csum[lane];
     double incA = wave_scan_f64(lsum);
     double T = readlane_f64(incA, 63);
     int64_t logc = A.counters[1];
@@ -596,42 +611,76 @@ __global__ __launch_bounds__(1024) void revive_kernel(ReviveArgs A) {
       const double target = readlane_f64(ul, ql) * T;
       int donor = -1;
       float nvd = 0.0f;
-      const uint64_t bA = __ballot(lane * m < nch && lsum > 0.0 && incA > target);
+      const uint64_t bA = __ballot(lsum > 0.0 && incA > target);
       if (bA) {
         const int L = __ffsll((unsigned long long)bA) - 1;
-        const double baseA = readlane_f64(incA - lsum, L);
-        int c = L;
-        double base = baseA;
-        if (m > 1) {
-          const int ci = L * m + lane;
-          const double v = (lane < m && ci < nch) ? csum[ci] : 0.0;
-          const double inc2 = baseA + wave_scan_f64(v);
-          const uint64_t b2 = __ballot(lane < m && ci < nch && v > 0.0 && inc2 > target);
-          if (b2) {
-            const int t2 = __ffsll((unsigned long long)b2) - 1;
-            c = L * m + t2;
-            base = readlane_f64(inc2 - v, t2);
+        const double base = readlane_f64(incA - lsum, L);
+        const int i0 = L * CS + lane * V;  // this lane's clusters of chunk L
+        int vl = -1;                        // this lane's first cluster past the target
+        double lp = 0.0;
+        float wl = 0.0f;
+        if constexpr (VT > 0) {
+          float w[VT];
+          double pv[VT];
+          if constexpr (lds_n) {
+            // VT consecutive counts, VT-aligned: one wide LDS read
+#pragma unroll
+            for (int v = 0; v < VT; v += (VT >= 4 ? 4 : VT)) {
+              if constexpr (VT >= 4) {
+                const float4 q4 = *reinterpret_cast<const float4*>(&wN[i0 + v]);
+                w[v] = q4.x;
+                w[v + 1] = q4.y;
+                w[v + 2] = q4.z;
+                w[v + 3] = q4.w;
+              } else if constexpr (VT == 2) {
+                const float2 q2 = *reinterpret_cast<const float2*>(&wN[i0 + v]);
+                w[v] = q2.x;
+                w[v + 1] = q2.y;
+              } else {
+                w[v] = wN[i0 + v];
+              }
+            }
           } else {
-            c = -1;
+#pragma unroll
+            for (int v = 0; v < VT; ++v) w[v] = live_count(i0 + v);
+          }
+#pragma unroll
+          for (int v = 0; v < VT; ++v) {
+            lp += (double)w[v];
+            pv[v] = lp;
+          }
+          const double ex = base + wave_scan_f64(lp) - lp;
+#pragma unroll
+          for (int v = VT - 1; v >= 0; --v)
+            if (w[v] > 0.0f && ex + pv[v] > target) {
+              vl = v;
+              wl = w[v];
+            }
+        } else {
+          for (int v = 0; v < V; ++v) lp += (double)live_count(i0 + v);
+          double run = base + wave_scan_f64(lp) - lp;
+          for (int v = 0; v < V && vl < 0; ++v) {
+            const float wv = live_count(i0 + v);
+            run += (double)wv;
+            if (wv > 0.0f && run > target) {
+              vl = v;
+              wl = wv;
+            }
           }
         }
-        for (int bb = 0; c >= 0 && bb < cb && donor < 0; ++bb) {
-          const int idx = c * CS + bb * 64 + lane;
-          float nv = 0.0f;
-          if (idx < k) nv = lds_n ? wN[idx] : (A.flags[idx] ? 0.0f : A.N[idx]);
-          const double inc3 = base + wave_scan_f64((double)nv);
-          const uint64_t b3 = __ballot(idx < k && nv > 0.0f && inc3 > target);
-          if (b3) {
-            const int t3 = __ffsll((unsigned long long)b3) - 1;
-            donor = c * CS + bb * 64 + t3;
-            nvd = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(nv), t3));
-          }
-          base = readlane_f64(inc3, 63);
+        const uint64_t b2 = __ballot(vl >= 0);
+        if (b2) {
+          const int t2 = __ffsll((unsigned long long)b2) - 1;
+          donor = L * CS + t2 * V + __builtin_amdgcn_readlane(vl, t2);
+          nvd = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(wl), t2));
         }
       }
       if (donor < 0) {
         donor = last_live;
-        nvd = lds_n ? wN[donor] : A.N[donor];
+        if constexpr (lds_n)
+          nvd = wN[donor];
+        else
+          nvd = A.N[donor];
       }
       const int i = donor;
       const float Nh = nvd * 0.5f;
@@ -640,7 +689,7 @@ __global__ __launch_bounds__(1024) void revive_kernel(ReviveArgs A) {
         A.N[j] = Nh;
         A.pair_i[q] = i;
         A.pair_n[q] = Nh;
-        if (lds_n) wN[i] = Nh;
+        if constexpr (lds_n) wN[i] = Nh;
         if (A.log && logc < A.log_cap) {
           A.log[3 * logc] = (int32_t)A.step;
           A.log[3 * logc + 1] = j;
@@ -649,13 +698,12 @@ __global__ __launch_bounds__(1024) void revive_kernel(ReviveArgs A) {
         }
       }
       // counts read from global memory by the next draw must see these stores
-      if (!lds_n) __threadfence_block();
+      if constexpr (!lds_n) __threadfence_block();
       // the donor's chunk lost Nh of live count: update the prefix state
-      const int Lo = (i / CS) / m;
+      const int Lo = i / CS;
       if (lane == Lo) lsum -= (double)Nh;
       if (lane >= Lo) incA -= (double)Nh;
       T -= (double)Nh;
-      if (lane == 0 && m > 1) csum[i / CS] -= (double)Nh;
     }
     if (lane == 0) A.counters[1] = logc;
   }
@@ -892,7 +940,19 @@ hipError_t launch_ema(int k, int d, float a, float b, int32_t* counts, float* s_
 }
 
 hipError_t launch_revive(const ReviveArgs& a, hipStream_t st) {
-  revive_kernel<<<1, 1024, 0, st>>>(a);
+  const int v = (a.k + 4095) / 4096;
+  if (v <= 1)
+    revive_kernel<1><<<1, 1024, 0, st>>>(a);
+  else if (v <= 2)
+    revive_kernel<2><<<1, 1024, 0, st>>>(a);
+  else if (v <= 4)
+    revive_kernel<4><<<1, 1024, 0, st>>>(a);
+  else if (v <= 8)
+    revive_kernel<8><<<1, 1024, 0, st>>>(a);
+  else if (v <= 16)
+    revive_kernel<16><<<1, 1024, 0, st>>>(a);
+  else
+    revive_kernel<0><<<1, 1024, 0, st>>>(a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || a.count_only) return e;
   split_kernel<<<(a.k + 3) / 4, 256, 0, st>>>(a);

@@ -80,6 +80,28 @@ def test_train_lockstep(mm, name, gen, n, d, k, T, o):
     np.testing.assert_allclose(out.stats["obj"], res.obj, rtol=1e-4)
 
 
+# Revival draws at larger k: 64 chunks of 64 V clusters, V = 2, 8 and the
+# register-free path (k > 65536), each with thousands of revivals.
+REVIVAL_K = [
+    ("k6000", 24_000, 8, 6_000, 4_096),
+    ("k20000", 60_000, 8, 20_000, 8_192),
+    ("k66000", 140_000, 4, 66_000, 16_384),
+]
+
+
+@pytest.mark.parametrize("name,n,d,k,bs", REVIVAL_K, ids=[c[0] for c in REVIVAL_K])
+def test_train_lockstep_revival_widths(mm, name, n, d, k, bs):
+    seed = 1234
+    X = datagen.make("tiny", n, d, seed=21)
+    out = _gpu_train(mm, X, k, 2.0, seed, batch_size=bs)
+    res, summ = lockstep(X, out, k, 2.0, seed, sample=256, rng_seed=2, batch_size=bs)
+    assert len(res.split_log) > 100
+    assert np.array_equal(out.counts.cpu().numpy(), res.N)
+    assert out.split_log == [tuple(s) for s in res.split_log]
+    assert np.array_equal(out.labels.cpu().numpy(), res.labels)
+    assert rel_l2(out.centroids.cpu().numpy(), res.centroids) <= 1e-4
+
+
 FREERUN = [
     ("tiny", "tiny", 10_000, 16, 64, 5.0),
     ("deep-small", "deep", 20_000, 96, 512, 3.0),
