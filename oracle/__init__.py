@@ -32,6 +32,11 @@ Do."):
                     centroid becomes the exact mean of the points the last pass
                     assigned to it; README "Quick start": labels come from the
                     last pass.
+* spherical         README "Spherical e-means": centroids rescaled to norm 1
+                    before every use (zero stays zero), assignment by the
+                    highest dot product (``emeans_ref.c``, fp64 brute force),
+                    closing mean rescaled to norm 1, error = sum of
+                    2 - 2 x similarity.
 * precision         README "Data precision": centroids and running sums are
                     stored in fp32; only the nearest-centroid search uses the
                     smaller format: for bf16 data, and for fp32 data when
@@ -101,6 +106,9 @@ def lib():
         L.ref_perm_range.argtypes = [u64, u64, u64, u64, u64, u64, vp]
         L.ref_assign.argtypes = [vp, ctypes.c_int, i64, vp, i32, vp, i32, vp, vp, vp, ctypes.c_int]
         L.ref_dist_to.argtypes = [vp, ctypes.c_int, i64, vp, i32, vp, vp, vp]
+        L.ref_assign_ip.argtypes = [vp, ctypes.c_int, i64, vp, i32, vp, i32, vp, vp, vp,
+                                    ctypes.c_int]
+        L.ref_dot_to.argtypes = [vp, ctypes.c_int, i64, vp, i32, vp, vp, vp]
         L.ref_group.argtypes = [vp, ctypes.c_int, i64, vp, vp, i32, i32, vp, vp]
         _lib = L
     return _lib
@@ -262,6 +270,46 @@ def assign(X: np.ndarray, C: np.ndarray, rows: Optional[np.ndarray] = None, nthr
     return lab, d1, d2
 
 
+def assign_ip(X: np.ndarray, C: np.ndarray, rows: Optional[np.ndarray] = None,
+              nthreads: int = 0):
+    """README "Spherical e-means": centroid with the highest dot product (lowest
+    index on ties): labels, best and runner-up dot product (fp64)."""
+    X = np.ascontiguousarray(X)
+    C = np.ascontiguousarray(C, dtype=np.float32)
+    d = X.shape[1]
+    k = C.shape[0]
+    m = X.shape[0] if rows is None else len(rows)
+    r = None if rows is None else np.ascontiguousarray(rows, dtype=np.int64)
+    lab = np.empty(m, dtype=np.int32)
+    s1 = np.empty(m, dtype=np.float64)
+    s2 = np.empty(m, dtype=np.float64)
+    if m:
+        lib().ref_assign_ip(_p(X), _dtype_code(X), m, _p(r), d, _p(C), k, _p(lab), _p(s1), _p(s2),
+                            int(nthreads))
+    return lab, s1, s2
+
+
+def dot_to(X: np.ndarray, C: np.ndarray, labels: np.ndarray, rows: Optional[np.ndarray] = None):
+    X = np.ascontiguousarray(X)
+    C = np.ascontiguousarray(C, dtype=np.float32)
+    labels = np.ascontiguousarray(labels, dtype=np.int32)
+    m = len(labels)
+    r = None if rows is None else np.ascontiguousarray(rows, dtype=np.int64)
+    out = np.empty(m, dtype=np.float64)
+    if m:
+        lib().ref_dot_to(_p(X), _dtype_code(X), m, _p(r), X.shape[1], _p(C), _p(labels), _p(out))
+    return out
+
+
+def normalize(C: np.ndarray) -> np.ndarray:
+    """Each row rescaled to norm 1 (norm and quotient in fp64, stored fp32); a
+    zero row stays zero (README "Spherical e-means")."""
+    c = np.asarray(C, dtype=np.float32).astype(np.float64)
+    nrm = np.sqrt(np.sum(c * c, axis=-1, keepdims=True))
+    out = np.where(nrm > 0, c / np.where(nrm > 0, nrm, 1.0), 0.0)
+    return out.astype(np.float32)
+
+
 def dist_to(X: np.ndarray, C: np.ndarray, labels: np.ndarray, rows: Optional[np.ndarray] = None):
     X = np.ascontiguousarray(X)
     C = np.ascontiguousarray(C, dtype=np.float32)
@@ -318,7 +366,7 @@ def init_rows(n: int, k: int, seed: int) -> np.ndarray:
 
 
 def _revive(t: int, seed: int, thr: float, N: np.ndarray, S: np.ndarray, C: np.ndarray,
-            log: list) -> None:
+            log: list, spherical: bool = False) -> None:
     k, d = S.shape
     total = float(np.sum(N.astype(np.float64)))
     th = thr * (total / k)
@@ -343,6 +391,9 @@ def _revive(t: int, seed: int, thr: float, N: np.ndarray, S: np.ndarray, C: np.n
         S[i] = half * (np.float32(1.0) - np.float32(SPLIT_EPS) * sig)
         C[i] = (S[i].astype(np.float64) / float(N[i])).astype(np.float32)
         C[j] = (S[j].astype(np.float64) / float(N[j])).astype(np.float32)
+        if spherical:
+            C[i] = normalize(C[i])
+            C[j] = normalize(C[j])
         log.append((t, int(j), i))
 
 
@@ -352,13 +403,21 @@ def train(X: np.ndarray, k: int, T: float, seed: int = 1234, *, batch_law: int =
           labels_for_step: Optional[Callable[[int, np.ndarray], np.ndarray]] = None,
           check_slots: Optional[Callable[[int, int], Optional[np.ndarray]]] = None,
           check_hook: Optional[Callable[[dict], None]] = None,
-          nthreads: int = 0, bf16_search: bool = False) -> TrainResult:
+          nthreads: int = 0, bf16_search: bool = False,
+          spherical: bool = False) -> TrainResult:
     """e-means on X (n x d, fp32 or bf16 bits), step by step.
 
     bf16_search: fp32 data is searched in bf16 (rows and centroids rounded to
     bf16), while the grouping, the running sums and the centroids use the
     fp32 rows (README "Data precision": only the search uses the smaller
     format).
+
+    spherical (README "Spherical e-means"): every centroid is its running
+    average rescaled to norm 1 before use (a zero centroid stays zero), each
+    vector goes to the centroid with the highest dot product, the closing step
+    rescales each cluster's exact mean to norm 1, and the reported error is
+    the sum of 2 - 2 x similarity. In label checks a dot product s enters as
+    -2 s (the squared distance up to a per-row constant for unit centroids).
 
     labels_for_step(t, rows) may supply the labels of step t from elsewhere
     (lockstep replay). The oracle then checks them on the slots that
@@ -375,6 +434,8 @@ def train(X: np.ndarray, k: int, T: float, seed: int = 1234, *, batch_law: int =
     Xf = search_data(X, bf16_search)  # the search reads this; grouping reads X
 
     C = np.ascontiguousarray(to_f32(X[init_rows(n, k, seed)]), dtype=np.float32)
+    if spherical:
+        C = normalize(C)
     N = np.zeros(k, dtype=np.float32)
     S = np.zeros((k, d), dtype=np.float32)
     LN = np.zeros(k, dtype=np.int64)
@@ -392,24 +453,31 @@ def train(X: np.ndarray, k: int, T: float, seed: int = 1234, *, batch_law: int =
             Bt = min(B, rows_e - s * B)
             rows = perm_range(n, seed, STREAM_PERM, e, s * B, Bt)
             Cs = search_centroids(C, Xf)
+            if spherical:
+                find = lambda r: (lambda l, a, b: (l, -2.0 * a, -2.0 * b))(*assign_ip(Xf, Cs, r, nthreads))
+                score_of = lambda l, r: -2.0 * dot_to(Xf, Cs, l, r)
+            else:
+                find = lambda r: assign(Xf, Cs, r, nthreads)
+                score_of = lambda l, r: dist_to(Xf, Cs, l, r)
             if labels_for_step is None:
-                lab, d1, _ = assign(Xf, Cs, rows, nthreads)
+                lab, d1, _ = find(rows)
                 dist = d1
             else:
                 lab = np.ascontiguousarray(labels_for_step(t, rows), dtype=np.int32)
                 slots = None if check_slots is None else check_slots(t, Bt)
                 sel = rows if slots is None else rows[slots]
-                olab, od1, od2 = assign(Xf, Cs, sel, nthreads)
+                olab, od1, od2 = find(sel)
                 glab = lab if slots is None else lab[slots]
-                gd = dist_to(Xf, Cs, glab, sel)
+                gd = score_of(glab, sel)
                 chk = dict(t=t, slots=slots, oracle=olab, d1=od1, d2=od2, given=glab,
-                           given_dist=gd, rows=sel, C=Cs, C32=C.copy())
+                           given_dist=gd, rows=sel, C=Cs, C32=C.copy(), spherical=spherical)
                 if check_hook is not None:
                     check_hook(chk)
                 else:
                     res.label_checks.append(chk)
-                dist = dist_to(Xf, Cs, lab, rows)
-            obj += float(np.sum(dist))
+                dist = score_of(lab, rows)
+            # spherical: sum of 2 - 2 x similarity (dist holds -2 x similarity)
+            obj += float(np.sum(dist)) + (2.0 * len(rows) if spherical else 0.0)
             counts, sums = group(X, rows, lab, k)
             a = al[t]
             b = np.float32(1.0) - a
@@ -419,12 +487,14 @@ def train(X: np.ndarray, k: int, T: float, seed: int = 1234, *, batch_law: int =
             S[:] = (np.float64(b) * S.astype(np.float64) + np.float64(a) * sums).astype(np.float32)
             pos = N > 0
             C[pos] = (S[pos].astype(np.float64) / N[pos].astype(np.float64)[:, None]).astype(np.float32)
+            if spherical:
+                C[pos] = normalize(C[pos])
             if last:
                 LN += counts
                 LS += sums
                 labels_out[rows] = lab
             if thr > 0 and (t + 1) % REVIVE_EVERY == 0:
-                _revive(t, seed, thr, N, S, C, res.split_log)
+                _revive(t, seed, thr, N, S, C, res.split_log, spherical)
             t += 1
         res.obj.append(obj / rows_e)
 
@@ -432,6 +502,8 @@ def train(X: np.ndarray, k: int, T: float, seed: int = 1234, *, batch_law: int =
     if finalize:
         pos = LN > 0
         C[pos] = (LS[pos] / LN[pos].astype(np.float64)[:, None]).astype(np.float32)
+        if spherical:
+            C[pos] = normalize(C[pos])
     res.centroids = C
     if thr > 0:
         th = thr * float(np.sum(N.astype(np.float64))) / k

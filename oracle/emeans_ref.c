@@ -201,6 +201,58 @@ void ref_dist_to(const void* X, int dtype, int64_t nrows, const int64_t* rows, i
   }
 }
 
+/* Spherical e-means (README "Spherical e-means"): each row goes to the      */
+/* centroid with the highest dot product, the lowest index on ties. Returns  */
+/* the label, the best and the runner-up dot product (fp64, summed over t in */
+/* order).                                                                    */
+void ref_assign_ip(const void* X, int dtype, int64_t nrows, const int64_t* rows, int32_t d,
+                   const float* C, int32_t k, int32_t* labels, double* s1, double* s2,
+                   int nthreads) {
+#ifdef _OPENMP
+  if (nthreads > 0) omp_set_num_threads(nthreads);
+#endif
+#pragma omp parallel
+  {
+    double* x = (double*)malloc(sizeof(double) * (size_t)d);
+#pragma omp for schedule(dynamic, 16)
+    for (int64_t i = 0; i < nrows; ++i) {
+      int64_t row = rows ? rows[i] : i;
+      for (int32_t t = 0; t < d; ++t) x[t] = ref_elem(X, dtype, row, d, t);
+      double best = -INFINITY, second = -INFINITY;
+      int32_t arg = -1;
+      for (int32_t j = 0; j < k; ++j) {
+        const float* c = C + (int64_t)j * d;
+        double s = 0.0;
+        for (int32_t t = 0; t < d; ++t) s += x[t] * (double)c[t];
+        if (s > best) {
+          second = best;
+          best = s;
+          arg = j;
+        } else if (s > second) {
+          second = s;
+        }
+      }
+      labels[i] = arg;
+      s1[i] = best;
+      s2[i] = second;
+    }
+    free(x);
+  }
+}
+
+/* Dot product of each selected row with the centroid of the given label.     */
+void ref_dot_to(const void* X, int dtype, int64_t nrows, const int64_t* rows, int32_t d,
+                const float* C, const int32_t* labels, double* out) {
+#pragma omp parallel for schedule(static)
+  for (int64_t i = 0; i < nrows; ++i) {
+    int64_t row = rows ? rows[i] : i;
+    const float* c = C + (int64_t)labels[i] * d;
+    double s = 0.0;
+    for (int32_t t = 0; t < d; ++t) s += ref_elem(X, dtype, row, d, t) * (double)c[t];
+    out[i] = s;
+  }
+}
+
 /* Per-cluster count and sum of the selected rows, in fp64. Each cluster's  */
 /* sum is taken in row order (the order of a sequential loop over the rows);  */
 /* rows are bucketed by label first only so clusters can run in parallel.     */

@@ -397,6 +397,100 @@ def test_bf16_search_groups_the_fp32_rows():
                                        rtol=0, atol=1e-6)
 
 
+# ---------------------------------------------------------------------------
+# spherical e-means (README "Spherical e-means")
+# ---------------------------------------------------------------------------
+
+def _unit(X):
+    X = X.astype(np.float64)
+    return (X / np.linalg.norm(X, axis=1, keepdims=True)).astype(np.float32)
+
+
+def test_assign_ip_matches_numpy_argmax():
+    """Highest dot product, lowest index on ties (duplicated centroids)."""
+    rng = np.random.default_rng(31)
+    X = rng.standard_normal((700, 24)).astype(np.float32)
+    C = rng.standard_normal((50, 24)).astype(np.float32)
+    C[17] = C[5]          # exact tie: index 5 must win
+    C[40] = C[33]
+    C[3] = 0.0            # a zero centroid scores 0 (by distance it would score |x|^2)
+    # numpy, summed over the dimension in order (so that tied centroids give
+    # bit-equal scores, which a blocked matrix product need not)
+    X64, C64 = X.astype(np.float64), C.astype(np.float64)
+    S = np.zeros((len(X), len(C)))
+    for t in range(X.shape[1]):
+        S += X64[:, t:t + 1] * C64[None, :, t]
+    lab, s1, s2 = oracle.assign_ip(X, C)
+    assert np.array_equal(lab, np.argmax(S, axis=1))
+    np.testing.assert_allclose(s1, S.max(axis=1), rtol=1e-12, atol=1e-12)
+    S2 = np.sort(S, axis=1)
+    np.testing.assert_allclose(s2, S2[:, -2], rtol=1e-12, atol=1e-12)
+    assert not np.any(np.isin(lab, [17, 40]))
+    # a zero centroid scores 0: x = (0.2, -0.98) goes to (1, 0) by dot product
+    # (0.2 > 0 > -0.66), while by distance the zero centroid would win
+    Cz = np.array([[1.0, 0.0], [0.0, 0.0], [0.6, 0.8]], np.float32)
+    xz = np.array([[0.2, -0.98], [-1.0, -0.2], [0.3, 0.954]], np.float32)
+    lz, sz, _ = oracle.assign_ip(xz, Cz)
+    assert lz.tolist() == [0, 1, 2]
+    np.testing.assert_allclose(sz, [0.2, 0.0, 0.6 * 0.3 + 0.8 * 0.954], rtol=1e-6)
+    assert oracle.assign(xz, Cz)[0].tolist() == [1, 1, 2]
+    rows = np.array([3, 699, 0, 350])
+    l2, _, _ = oracle.assign_ip(X, C, rows)
+    assert np.array_equal(l2, lab[rows])
+    np.testing.assert_allclose(oracle.dot_to(X, C, lab), s1, rtol=1e-12, atol=1e-12)
+
+
+def test_normalize_keeps_zero_rows():
+    C = np.array([[3.0, 4.0], [0.0, 0.0], [-1e-20, 0.0]], np.float32)
+    N = oracle.normalize(C)
+    np.testing.assert_allclose(N[0], [0.6, 0.8], rtol=1e-7)
+    assert np.array_equal(N[1], [0.0, 0.0])
+    np.testing.assert_allclose(N[2], [-1.0, 0.0])
+
+
+def test_spherical_one_step_is_spherical_kmeans():
+    """B = n, alpha = 1, no revival: one step is one spherical k-means step
+    (assign by the highest cosine to the unit-norm starting centroids, then
+    each centroid is its cluster's mean rescaled to norm 1); the reported
+    error is the mean of 2 - 2 x cosine, i.e. the mean squared distance on
+    the sphere."""
+    X = _unit(datagen.tiny(n=3000, d=16, seed=4))
+    k = 40
+    res = oracle.train(X, k, 1.0, seed=9, batch_size=3000, alpha0=1.0, unused_threshold=0,
+                       finalize=False, spherical=True)
+    C0 = X[oracle.init_rows(3000, k, 9)].astype(np.float64)
+    C0 /= np.linalg.norm(C0, axis=1, keepdims=True)
+    S = X.astype(np.float64) @ C0.T
+    lab = np.argmax(S, axis=1)
+    want = C0.copy()
+    for j in range(k):
+        m = lab == j
+        if m.any():
+            mu = X[m].astype(np.float64).mean(axis=0)
+            want[j] = mu / np.linalg.norm(mu)
+    np.testing.assert_allclose(res.centroids, want, rtol=0, atol=2e-6)
+    # fp32 unit vectors have norms 1 +- 1e-7, hence the tolerance
+    D = cdist(X.astype(np.float64), C0, "sqeuclidean").min(axis=1)
+    np.testing.assert_allclose(res.obj[0], D.mean(), rtol=1e-6)
+    np.testing.assert_allclose(res.obj[0], np.mean(2.0 - 2.0 * S.max(axis=1)), rtol=1e-6)
+
+
+def test_spherical_closing_step_is_normalised_mean():
+    X = _unit(datagen.deep(n=4000, d=32, seed=6))
+    res = oracle.train(X, 50, 2.0, seed=3, batch_size=512, spherical=True)
+    lab = res.labels
+    nrm = np.linalg.norm(res.centroids.astype(np.float64), axis=1)
+    np.testing.assert_allclose(nrm[nrm > 0], 1.0, atol=1e-6)
+    for j in range(50):
+        m = lab == j
+        if m.any():
+            mu = X[m].astype(np.float64).mean(axis=0)
+            np.testing.assert_allclose(res.centroids[j], mu / np.linalg.norm(mu), rtol=0, atol=2e-6)
+    # the EMA centroids are unit-norm too (rescaled before every use)
+    en = np.linalg.norm(res.ema_centroids.astype(np.float64), axis=1)
+    np.testing.assert_allclose(en[en > 0], 1.0, atol=1e-6)
+
+
 def test_fractional_last_pass_labels():
     X = datagen.tiny(n=2000, d=16, seed=3)
     res = oracle.train(X, 16, 1.5, seed=5, batch_size=256)
