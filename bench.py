@@ -172,6 +172,8 @@ def main() -> int:
     ap.add_argument("--bf16-search", action="store_true",
                     help="search fp32 data in bf16 (README \"Data precision\": the pages' GPU "
                          "default); the held-out MSE is still evaluated in fp32")
+    ap.add_argument("--spherical", action="store_true",
+                    help="spherical e-means (README \"Spherical e-means\"); no time-to-target")
     ap.add_argument("--print-source-sha", action="store_true")
     args = ap.parse_args()
     if args.print_source_sha:
@@ -205,19 +207,22 @@ def main() -> int:
     flops = float(sum(2.0 * b * k * d for b in sizes))
     bsearch = bool(args.bf16_search) and W["dtype"] == "f32"
     sdtype = "bf16" if bsearch else W["dtype"]   # arithmetic type of the search
-    tag = args.workload + ("_bf16search" if bsearch else "")
+    sph = bool(args.spherical)
+    tag = args.workload + ("_bf16search" if bsearch else "") + ("_spherical" if sph else "")
+    if sph:
+        args.no_ttt = True   # the Lloyd-25 target is Euclidean
 
     X, Xh, Xhost = make_data(args.workload, W, torch)
 
     # warm-up (untimed)
     if Wm > 0:
-        mm.train(X, k, T, args.seed, max_steps=Wm, bf16_search=bsearch)
+        mm.train(X, k, T, args.seed, max_steps=Wm, bf16_search=bsearch, spherical=sph)
         torch.cuda.synchronize()
 
     # timed: exactly K steps of the schedule
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    out = mm.train(X, k, T, args.seed, max_steps=K, bf16_search=bsearch)
+    out = mm.train(X, k, T, args.seed, max_steps=K, bf16_search=bsearch, spherical=sph)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     value = flops / wall / 1e12
@@ -234,7 +239,8 @@ def main() -> int:
         log(f"copied {args.copy_calibration} bytes x3 for counter calibration")
 
     # profiled run: device time per kernel class (HIP events on the launch stream)
-    prof = mm.train(X, k, T, args.seed, max_steps=K, profile=True, bf16_search=bsearch).stats
+    prof = mm.train(X, k, T, args.seed, max_steps=K, profile=True, bf16_search=bsearch,
+                    spherical=sph).stats
     torch.cuda.synchronize()
     a_ms = prof["ms_assign"]
     assign_tflops = flops / (a_ms / 1e3) / 1e12 if a_ms > 0 else None
@@ -266,7 +272,8 @@ def main() -> int:
                    "batch": rc["batch_size"], "alpha0": round(rc["alpha0"], 6),
                    "steps_per_run": S,
                    "search": "bf16 (fp32 rows rounded for the search; sums in fp32)" if bsearch
-                   else ("bf16" if W["dtype"] == "bf16" else "fp32 (exact)")},
+                   else ("bf16" if W["dtype"] == "bf16" else "fp32 (exact)"),
+                   "mode": "spherical" if sph else "euclidean"},
         "mfma_peak_frac": round(value / peak, 4),
         "roofline": {
             "kernel": assign_kernel_name(sdtype, d),

@@ -90,6 +90,16 @@ typedef struct emeans_opts {
                                  those of the rounded vectors; grouping, running sums
                                  and centroids use the fp32 rows. 0: fp32 X is searched
                                  in fp32 (exact). Ignored for bf16 X. */
+  int32_t spherical;          /* 1: spherical e-means (README "Spherical e-means"):
+                                 every centroid is its running average rescaled to
+                                 norm 1 before use (a zero centroid stays zero), each
+                                 vector goes to the centroid with the highest dot
+                                 product, the closing step rescales each cluster's
+                                 mean to norm 1, and stats->obj is the mean of
+                                 2 - 2 x similarity. Vectors are not normalised (nor
+                                 checked): pass unit-norm rows for cosine semantics.
+                                 emeans_assign: labels by the highest dot product with
+                                 C as given, dists[i] = that similarity. */
 } emeans_opts;
 
 /* Recipe and statistics of a run (README "Settings and results": recipe, obj,

@@ -36,6 +36,7 @@ class Opts(ctypes.Structure):
         ("unused_threshold", c_dbl), ("no_finalize", c_i32), ("profile", c_i32),
         ("stream", c_vp), ("trace_labels", c_vp), ("out_counts", c_vp), ("split_log", c_vp),
         ("split_log_cap", c_i64), ("max_steps", c_i64), ("bf16_search", c_i32),
+        ("spherical", c_i32),
     ]
 
 
@@ -174,7 +175,7 @@ def train(X, k: int, T: float = 5.0, seed: int = 1234, *, batch_law="auto", batc
           alpha0: float = 0.0, unused_threshold=None, finalize: bool = True,
           capture_labels: bool = True, trace: bool = False, counts: bool = False,
           split_log_cap: int = 0, profile: bool = False, max_steps: int = 0,
-          bf16_search: bool = False, stream=None) -> TrainOutput:
+          bf16_search: bool = False, spherical: bool = False, stream=None) -> TrainOutput:
     import torch
     _require_device(X)
     n, d = X.shape
@@ -198,6 +199,7 @@ def train(X, k: int, T: float = 5.0, seed: int = 1234, *, batch_law="auto", batc
             o.split_log_cap = split_log_cap
         o.max_steps = int(max_steps)
         o.bf16_search = 1 if bf16_search else 0
+        o.spherical = 1 if spherical else 0
         s = Stats()
         _check(lib().emeans_train(X.data_ptr(), n, d, int(k), float(T), int(seed) & (2**64 - 1),
                                   C.data_ptr(), labels.data_ptr() if labels is not None else None,
@@ -210,9 +212,11 @@ def train(X, k: int, T: float = 5.0, seed: int = 1234, *, batch_law="auto", batc
         return TrainOutput(C, labels, st, tr, cn, splits)
 
 
-def assign(X, C, *, with_dists: bool = True, bf16_search: bool = False, stream=None):
+def assign(X, C, *, with_dists: bool = True, bf16_search: bool = False, spherical: bool = False,
+           stream=None):
     """Nearest centroid (int32 labels) and squared distance (float32) of each row.
-    bf16_search: search fp32 rows in bf16 (rows and centroids rounded)."""
+    bf16_search: search fp32 rows in bf16 (rows and centroids rounded).
+    spherical: the centroid with the highest dot product, and that similarity."""
     import torch
     _require_device(X)
     if not (getattr(C, "is_cuda", False) and C.dtype == torch.float32 and C.is_contiguous()):
@@ -226,6 +230,7 @@ def assign(X, C, *, with_dists: bool = True, bf16_search: bool = False, stream=N
         dists = torch.empty((n,), dtype=torch.float32, device=X.device) if with_dists else None
         o = _opts(_dtype_of(X), stream=_stream_ptr(X, stream))
         o.bf16_search = 1 if bf16_search else 0
+        o.spherical = 1 if spherical else 0
         if n:
             _check(lib().emeans_assign(X.data_ptr(), n, d, C.data_ptr(), k, labels.data_ptr(),
                                        dists.data_ptr() if dists is not None else None,

@@ -223,6 +223,7 @@ int emeans_assign(const void* X, int64_t n, int32_t d, const float* C, int32_t k
   hipStream_t st = static_cast<hipStream_t>(opts ? opts->stream : nullptr);
   const bool bf16 = dtype == EMEANS_BF16;
   const bool bsearch = !bf16 && opts && opts->bf16_search;  // fp32 rows searched in bf16
+  const bool sph = opts && opts->spherical;  // highest dot product, similarity out
   void* base = nullptr;
   float* bias = nullptr;
   uint16_t* chat = nullptr;
@@ -233,11 +234,11 @@ int emeans_assign(const void* X, int64_t n, int32_t d, const float* C, int32_t k
   if (bsearch) ar.want(&xb, (size_t)n * d);
   rc = EMEANS_OK;
   HIP_TRY(ar.alloc(&base, st));
-  HIP_TRY(launch_prep(C, k, d, bias, chat, st));
+  HIP_TRY(launch_prep(C, k, d, bias, chat, sph, st));
   if (bsearch) HIP_TRY(launch_cast_rows(static_cast<const float*>(X), d, nullptr, (int)n, xb, st));
   HIP_TRY(launch_assign(bf16 || bsearch, bsearch ? (const void*)xb : X, d, nullptr, (int)n,
                         (bf16 || bsearch) ? (const void*)chat : (const void*)C, bias, k, labels,
-                        dists, nullptr, nullptr, st));
+                        dists, nullptr, nullptr, sph, st));
 done:
   if (base) {
     const hipError_t e = hipFreeAsync(base, st);
@@ -276,6 +277,7 @@ int emeans_train(const void* X, int64_t n, int32_t d, int32_t k, double T, uint6
   // fp32 rows searched in bf16: each batch is gathered and rounded into xb
   const bool bsearch = !bf16 && opts && opts->bf16_search;
   const bool sbf = bf16 || bsearch;  // the search runs in bf16 against chat
+  const bool sph = opts && opts->spherical;  // spherical e-means
   const bool profile = opts && opts->profile;
   const size_t kd = (size_t)k * d;
   const int64_t B = r.B;
@@ -373,8 +375,8 @@ int emeans_train(const void* X, int64_t n, int32_t d, int32_t k, double T, uint6
 
   // starting centroids: k distinct rows (first k entries of the init permutation)
   HIP_TRY(launch_init_centroids(bf16, X, d, make_perm_key((uint64_t)n, seed, kStreamInit, 0), k,
-                                centroids, st));
-  HIP_TRY(launch_prep(centroids, k, d, bias, chat, st));
+                                centroids, sph, st));
+  HIP_TRY(launch_prep(centroids, k, d, bias, chat, sph, st));
 
   for (int e = 0; e < r.npass && t < run_steps; ++e) {
     const bool last = e == r.npass - 1;
@@ -393,9 +395,9 @@ int emeans_train(const void* X, int64_t n, int32_t d, int32_t k, double T, uint6
       HIP_TRY(timed(kAssign, [&] {
         if (bsearch)
           return launch_assign(true, xb, d, nullptr, nb, chat, bias, k, blab, bdist, counts,
-                               dstat + e, st);
+                               dstat + e, sph, st);
         return launch_assign(bf16, X, d, rows, nb, bf16 ? (const void*)chat : (const void*)centroids,
-                             bias, k, blab, bdist, counts, dstat + e, st);
+                             bias, k, blab, bdist, counts, dstat + e, sph, st);
       }));
       if (opts && opts->trace_labels) {
         HIP_TRY(hipMemcpyAsync(opts->trace_labels + trace_off, blab, sizeof(int32_t) * nb,
@@ -412,12 +414,12 @@ int emeans_train(const void* X, int64_t n, int32_t d, int32_t k, double T, uint6
       }));
       HIP_TRY(timed(kUpdate, [&] {
         return launch_ema(k, d, a, b, counts, s_acc, N, S, centroids, bias, chat, pass_counts,
-                          last ? LS : nullptr, st);
+                          last ? LS : nullptr, sph, st);
       }));
       if (r.thr > 0.0 && (t + 1) % kReviveEvery == 0) {
         ReviveArgs ra{k, d, N, S, centroids, bias, chat, r.thr, seed, (uint64_t)t, flags, dead,
                       n0, rv_u, pair_i, pair_n, rv_pos, rv_head, rv_cbase, rv_clen, rv_heads,
-                      rv_list, rv_nheads, counters, dlog, log_cap, 0};
+                      rv_list, rv_nheads, counters, dlog, log_cap, 0, sph ? 1 : 0};
         HIP_TRY(timed(kRevive, [&] { return launch_revive(ra, st); }));
       }
     }
@@ -431,13 +433,13 @@ int emeans_train(const void* X, int64_t n, int32_t d, int32_t k, double T, uint6
   if (r.thr > 0.0) {
     ReviveArgs ra{k, d, N, S, centroids, bias, chat, r.thr, seed, (uint64_t)t, flags, dead,
                   n0, rv_u, pair_i, pair_n, rv_pos, rv_head, rv_cbase, rv_clen, rv_heads,
-                  rv_list, rv_nheads, counters, nullptr, 0, 1};
+                  rv_list, rv_nheads, counters, nullptr, 0, 1, sph ? 1 : 0};
     HIP_TRY(launch_revive(ra, st));
   }
   if (opts && opts->out_counts)
     HIP_TRY(hipMemcpyAsync(opts->out_counts, N, sizeof(float) * k, hipMemcpyDeviceToDevice, st));
   if (!(opts && opts->no_finalize) && last_pass_begun)
-    HIP_TRY(launch_finalize(k, d, pass_counts, LS, centroids, st));
+    HIP_TRY(launch_finalize(k, d, pass_counts, LS, centroids, sph, st));
 
   HIP_TRY(hipMemcpyAsync(host_stat, dstat, sizeof host_stat, hipMemcpyDeviceToHost, st));
   HIP_TRY(hipMemcpyAsync(host_counters, counters, sizeof host_counters, hipMemcpyDeviceToHost, st));

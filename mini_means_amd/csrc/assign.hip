@@ -94,7 +94,7 @@ __global__ __launch_bounds__(kThreads, 1) void assign_kernel(
     const unsigned char* __restrict__ X, int d, const uint32_t* __restrict__ rows, int nrows,
     const unsigned char* __restrict__ Cs, const float* __restrict__ bias, int k,
     int32_t* __restrict__ labels, float* __restrict__ dists, int32_t* __restrict__ counts,
-    double* __restrict__ obj) {
+    double* __restrict__ obj, int sim) {
   constexpr int ES = BF16 ? 2 : 4;
   constexpr int EPV = 16 / ES;          // elements per 16-byte chunk
   constexpr int EPS = kSlab / ES;       // elements per stage
@@ -303,11 +303,13 @@ __global__ __launch_bounds__(kThreads, 1) void assign_kernel(
     if (j < 0 || j >= k) j = 0;  // only reachable with non-finite data
     const int slot = tile0 + p;
     if (slot < nrows) {
+      // sim (spherical e-means): the score is the similarity x.c (zero bias);
+      // the error adds 2 - 2 x similarity
       const float dist = fmaxf(xn_s[p] - 2.0f * sc, 0.0f);
       labels[slot] = j;
-      if (dists) dists[slot] = dist;
+      if (dists) dists[slot] = sim ? sc : dist;
       if (counts) atomicAdd(&counts[j], 1);
-      dsum = (double)dist;
+      dsum = sim ? 2.0 - 2.0 * (double)sc : (double)dist;
     }
   }
   if (obj) {
@@ -384,7 +386,7 @@ __global__ __launch_bounds__(kThreads, 1) void assign_ring_kernel(
     const unsigned char* __restrict__ X, int d, const uint32_t* __restrict__ rows, int nrows,
     const unsigned char* __restrict__ Cs, const float* __restrict__ bias, int k,
     int32_t* __restrict__ labels, float* __restrict__ dists, int32_t* __restrict__ counts,
-    double* __restrict__ obj) {
+    double* __restrict__ obj, int sim) {
   constexpr int ES = BF16 ? 2 : 4;
   constexpr int EPV = 16 / ES;
   constexpr int EPS = kSlab / ES;
@@ -630,11 +632,13 @@ __global__ __launch_bounds__(kThreads, 1) void assign_ring_kernel(
     if (j < 0 || j >= k) j = 0;  // only reachable with non-finite data
     const int slot = tile0 + p;
     if (slot < nrows) {
+      // sim (spherical e-means): the score is the similarity x.c (zero bias);
+      // the error adds 2 - 2 x similarity
       const float dist = fmaxf(xn_s[p] - 2.0f * sc, 0.0f);
       labels[slot] = j;
-      if (dists) dists[slot] = dist;
+      if (dists) dists[slot] = sim ? sc : dist;
       if (counts) atomicAdd(&counts[j], 1);
-      dsum = (double)dist;
+      dsum = sim ? 2.0 - 2.0 * (double)sc : (double)dist;
     }
   }
   if (obj) {
@@ -653,11 +657,11 @@ __global__ __launch_bounds__(kThreads, 1) void assign_ring_kernel(
 
 hipError_t launch_assign(bool bf16, const void* X, int d, const uint32_t* rows, int nrows,
                          const void* Cs, const float* bias, int k, int32_t* labels, float* dists,
-                         int32_t* counts, double* obj, hipStream_t st) {
+                         int32_t* counts, double* obj, bool sim, hipStream_t st) {
   if (nrows <= 0) return hipSuccess;
   if (bf16 && assign_bf16_resident_ok(d, X, Cs))
     return launch_assign_bf16_resident(X, d, rows, nrows, Cs, bias, k, labels, dists, counts, obj,
-                                       st);
+                                       sim, st);
   const dim3 grid((nrows + kTP - 1) / kTP), block(kThreads);
   const auto* x = static_cast<const unsigned char*>(X);
   const auto* c = static_cast<const unsigned char*>(Cs);
@@ -665,17 +669,17 @@ hipError_t launch_assign(bool bf16, const void* X, int d, const uint32_t* rows, 
   if (bf16) {
     if (aligned && d % 8 == 0)
       assign_ring_kernel<true><<<grid, block, 0, st>>>(x, d, rows, nrows, c, bias, k, labels,
-                                                       dists, counts, obj);
+                                                       dists, counts, obj, sim ? 1 : 0);
     else
       assign_kernel<true, false><<<grid, block, 0, st>>>(x, d, rows, nrows, c, bias, k, labels,
-                                                         dists, counts, obj);
+                                                         dists, counts, obj, sim ? 1 : 0);
   } else {
     if (aligned && d % 4 == 0)
       assign_ring_kernel<false><<<grid, block, 0, st>>>(x, d, rows, nrows, c, bias, k, labels,
-                                                        dists, counts, obj);
+                                                        dists, counts, obj, sim ? 1 : 0);
     else
       assign_kernel<false, false><<<grid, block, 0, st>>>(x, d, rows, nrows, c, bias, k, labels,
-                                                          dists, counts, obj);
+                                                          dists, counts, obj, sim ? 1 : 0);
   }
   return hipGetLastError();
 }

@@ -39,7 +39,7 @@ __global__ __launch_bounds__(kThreads, 1) void assign_bf16_kernel(
     const uint16_t* __restrict__ X, const uint32_t* __restrict__ rows, int nrows,
     const uint16_t* __restrict__ Chat, const float* __restrict__ bias, int k,
     int32_t* __restrict__ labels, float* __restrict__ dists, int32_t* __restrict__ counts,
-    double* __restrict__ obj) {
+    double* __restrict__ obj, int sim) {
   constexpr int d = 16 * KS;
   constexpr int CPR = d * 2 / 16;              // 16-byte chunks per centroid row
   constexpr int PER = kTC * CPR / kThreads;    // chunk loads per thread per panel
@@ -220,11 +220,12 @@ __global__ __launch_bounds__(kThreads, 1) void assign_bf16_kernel(
     if (j < 0 || j >= k) j = 0;  // only reachable with non-finite data
     const int slot = tile0 + p;
     if (slot < nrows) {
+      // sim (spherical e-means): similarity out, error 2 - 2 x similarity
       const float dist = fmaxf(m_s[1][p] - 2.0f * m_s[0][p], 0.0f);
       labels[slot] = j;
-      if (dists) dists[slot] = dist;
+      if (dists) dists[slot] = sim ? m_s[0][p] : dist;
       if (counts) atomicAdd(&counts[j], 1);
-      dsum += (double)dist;
+      dsum += sim ? 2.0 - 2.0 * (double)m_s[0][p] : (double)dist;
     }
   }
   if (obj) {
@@ -249,23 +250,27 @@ bool assign_bf16_resident_ok(int d, const void* X, const void* Chat) {
 hipError_t launch_assign_bf16_resident(const void* X, int d, const uint32_t* rows, int nrows,
                                        const void* Chat, const float* bias, int k,
                                        int32_t* labels, float* dists, int32_t* counts,
-                                       double* obj, hipStream_t st) {
+                                       double* obj, bool sim, hipStream_t st) {
   if (nrows <= 0) return hipSuccess;
   const dim3 grid((nrows + kTP - 1) / kTP), block(kThreads);
   const auto* x = static_cast<const uint16_t*>(X);
   const auto* c = static_cast<const uint16_t*>(Chat);
   switch (d) {
     case 32:
-      assign_bf16_kernel<2><<<grid, block, 0, st>>>(x, rows, nrows, c, bias, k, labels, dists, counts, obj);
+      assign_bf16_kernel<2><<<grid, block, 0, st>>>(x, rows, nrows, c, bias, k, labels, dists, counts, obj,
+                                                     sim ? 1 : 0);
       break;
     case 64:
-      assign_bf16_kernel<4><<<grid, block, 0, st>>>(x, rows, nrows, c, bias, k, labels, dists, counts, obj);
+      assign_bf16_kernel<4><<<grid, block, 0, st>>>(x, rows, nrows, c, bias, k, labels, dists, counts, obj,
+                                                     sim ? 1 : 0);
       break;
     case 96:
-      assign_bf16_kernel<6><<<grid, block, 0, st>>>(x, rows, nrows, c, bias, k, labels, dists, counts, obj);
+      assign_bf16_kernel<6><<<grid, block, 0, st>>>(x, rows, nrows, c, bias, k, labels, dists, counts, obj,
+                                                     sim ? 1 : 0);
       break;
     default:
-      assign_bf16_kernel<8><<<grid, block, 0, st>>>(x, rows, nrows, c, bias, k, labels, dists, counts, obj);
+      assign_bf16_kernel<8><<<grid, block, 0, st>>>(x, rows, nrows, c, bias, k, labels, dists, counts, obj,
+                                                     sim ? 1 : 0);
       break;
   }
   return hipGetLastError();

@@ -13,10 +13,11 @@ namespace emk {
 // distance). `Cs` is the search-format centroid table (fp32 C, or bf16 C-hat
 // for bf16 X) and `bias` = -|c|^2/2 computed from it. Writes labels[r],
 // dists[r] (optional), counts[label] += 1 (optional) and obj[0] += sum of
-// distances (optional).
+// distances (optional). With `sim` (spherical e-means, bias = 0) dists[r] is
+// the similarity x.c and obj adds 2 - 2 x similarity.
 hipError_t launch_assign(bool bf16, const void* X, int d, const uint32_t* rows, int nrows,
                          const void* Cs, const float* bias, int k, int32_t* labels, float* dists,
-                         int32_t* counts, double* obj, hipStream_t st);
+                         int32_t* counts, double* obj, bool sim, hipStream_t st);
 
 // bf16 data of dimension 32, 64, 96 or 128: points resident in registers,
 // 32x32x16 bf16 MFMA tiles (same contract as launch_assign).
@@ -24,7 +25,7 @@ bool assign_bf16_resident_ok(int d, const void* X, const void* Chat);
 hipError_t launch_assign_bf16_resident(const void* X, int d, const uint32_t* rows, int nrows,
                                        const void* Chat, const float* bias, int k,
                                        int32_t* labels, float* dists, int32_t* counts,
-                                       double* obj, hipStream_t st);
+                                       double* obj, bool sim, hipStream_t st);
 
 // rows[r] = pi(start + r) for the keyed permutation pk.
 hipError_t launch_sample_rows(const PermKey& pk, uint64_t start, int count, uint32_t* rows,
@@ -32,12 +33,14 @@ hipError_t launch_sample_rows(const PermKey& pk, uint64_t start, int count, uint
 hipError_t launch_sample_rows_i32(const PermKey& pk, uint64_t start, int count, int32_t* rows,
                                   hipStream_t st);
 
-// C[j] = X[pi(j)] as fp32, j < k.
+// C[j] = X[pi(j)] as fp32, j < k (rescaled to norm 1 when sph).
 hipError_t launch_init_centroids(bool bf16, const void* X, int d, const PermKey& pk, int k,
-                                 float* C, hipStream_t st);
+                                 float* C, bool sph, hipStream_t st);
 
-// bias[j] = -|c_j|^2 / 2 in the search format; Chat = bf16(C) when non-null.
-hipError_t launch_prep(const float* C, int k, int d, float* bias, uint16_t* Chat, hipStream_t st);
+// bias[j] = -|c_j|^2 / 2 in the search format (0 when sph); Chat = bf16(C)
+// when non-null.
+hipError_t launch_prep(const float* C, int k, int d, float* bias, uint16_t* Chat, bool sph,
+                       hipStream_t st);
 
 // out[r] = bf16(X[rows[r]]) for r < nrows (rows NULL: row r), row-major.
 hipError_t launch_cast_rows(const float* X, int d, const uint32_t* rows, int nrows,
@@ -61,9 +64,10 @@ hipError_t launch_group(bool bf16, const void* X, int d, const uint32_t* order,
 
 // EMA update of every cluster; resets counts and s_acc for the next step;
 // pass_counts += counts; LS += s when LS is non-null; refreshes bias/Chat.
+// sph: the centroids are rescaled to norm 1 and the bias is 0.
 hipError_t launch_ema(int k, int d, float a, float b, int32_t* counts, float* s_acc, float* N,
                       float* S, float* C, float* bias, uint16_t* Chat, int32_t* pass_counts,
-                      float* LS, hipStream_t st);
+                      float* LS, bool sph, hipStream_t st);
 
 struct ReviveArgs {
   int k, d;
@@ -92,6 +96,7 @@ struct ReviveArgs {
   int32_t* log;       // 3 * log_cap
   int64_t log_cap;
   int count_only;
+  int sph;            // spherical e-means: split centroids rescaled to norm 1, bias 0
 };
 // Dead-cluster check and donor draws (one workgroup), then the splits of the
 // running sums, one wave per donor chain.
@@ -100,8 +105,9 @@ hipError_t launch_revive(const ReviveArgs& a, hipStream_t st);
 // sums[0] += sum n_j^2, sums[1] += sum n_j over pass_counts; zeroes them if `reset`.
 hipError_t launch_pass_stats(int32_t* pass_counts, int k, double* sums, int reset, hipStream_t st);
 
-// C[j] = LS[j] / pass_counts[j] where pass_counts[j] > 0.
+// C[j] = LS[j] / pass_counts[j] where pass_counts[j] > 0 (rescaled to norm
+// 1 when sph).
 hipError_t launch_finalize(int k, int d, const int32_t* pass_counts, const float* LS, float* C,
-                           hipStream_t st);
+                           bool sph, hipStream_t st);
 
 }  // namespace emk

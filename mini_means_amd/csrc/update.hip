@@ -70,9 +70,26 @@ __global__ __launch_bounds__(256) void cast_rows_kernel(const float* __restrict_
   }
 }
 
-// One wave per centroid: C[j] = X[pi(j)] converted to fp32.
+// Spherical e-means: rescale a row of length d to norm 1 in place, the norm
+// and the quotient in fp64 (stored fp32); a zero row stays zero. One wave.
+__device__ __forceinline__ void wave_normalize(float* c, int d, int lane) {
+  double s2 = 0.0;
+  for (int e = lane; e < d; e += 64) {
+    const double v = (double)c[e];
+    s2 += v * v;
+  }
+  s2 = wave_sum(s2);
+  if (s2 > 0.0) {
+    const double nr = sqrt(s2);
+    for (int e = lane; e < d; e += 64) c[e] = (float)((double)c[e] / nr);
+  }
+}
+
+// One wave per centroid: C[j] = X[pi(j)] converted to fp32 (rescaled to norm
+// 1 for spherical e-means).
 __global__ __launch_bounds__(256) void init_centroids_kernel(const unsigned char* X, int bf16,
-                                                             int d, PermKey pk, int k, float* C) {
+                                                             int d, PermKey pk, int k, float* C,
+                                                             int sph) {
   const int j = blockIdx.x * 4 + (threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
   if (j >= k) return;
@@ -87,11 +104,12 @@ __global__ __launch_bounds__(256) void init_centroids_kernel(const unsigned char
       v = reinterpret_cast<const float*>(X)[row * (uint64_t)d + e];
     C[(size_t)j * d + e] = v;
   }
+  if (sph) wave_normalize(C + (size_t)j * d, d, lane);
 }
 
 // One wave per centroid: bias = -|c|^2/2 in the search format, Chat = bf16(c).
 __global__ __launch_bounds__(256) void prep_kernel(const float* C, int k, int d, float* bias,
-                                                   uint16_t* Chat) {
+                                                   uint16_t* Chat, int sph) {
   const int j = blockIdx.x * 4 + (threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
   if (j >= k) return;
@@ -106,7 +124,7 @@ __global__ __launch_bounds__(256) void prep_kernel(const float* C, int k, int d,
     nrm += c * c;
   }
   nrm = wave_sum(nrm);
-  if (lane == 0) bias[j] = -0.5f * nrm;
+  if (lane == 0) bias[j] = sph ? 0.0f : -0.5f * nrm;  // spherical: score = x.c
 }
 
 // Single workgroup: exclusive scan of the counts (row offsets of the buckets)
@@ -434,7 +452,7 @@ __global__ __launch_bounds__(256) void ema_kernel(int k, int d, float a, float b
                                                   int32_t* counts, float* s_acc, float* N,
                                                   float* S, float* C, float* bias,
                                                   uint16_t* Chat, int32_t* pass_counts,
-                                                  float* LS) {
+                                                  float* LS, int sph) {
   const int j = blockIdx.x * 4 + (threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
   if (j >= k) return;
@@ -459,6 +477,7 @@ __global__ __launch_bounds__(256) void ema_kernel(int k, int d, float a, float b
       c = C[idx];
     }
     if (LS && n) LS[idx] += s;
+    if (sph) continue;  // rescaled (and rounded to Chat) below, once the norm is known
     if constexpr (BF16S) {
       const uint16_t h = f32_to_bf16_rne(c);
       Chat[idx] = h;
@@ -466,10 +485,18 @@ __global__ __launch_bounds__(256) void ema_kernel(int k, int d, float a, float b
     }
     nrm += c * c;
   }
-  nrm = wave_sum(nrm);
+  if (sph) {
+    // spherical e-means: the running average rescaled to norm 1 (a centroid
+    // without a count keeps its unit-norm value); the score is x.c, bias 0
+    if (Nn > 0.0f) wave_normalize(C + base, d, lane);
+    if constexpr (BF16S)
+      for (int e = lane; e < d; e += 64) Chat[base + e] = f32_to_bf16_rne(C[base + e]);
+  } else {
+    nrm = wave_sum(nrm);
+  }
   if (lane == 0) {
     N[j] = Nn;
-    bias[j] = -0.5f * nrm;
+    bias[j] = sph ? 0.0f : -0.5f * nrm;
     pass_counts[j] += n;
     counts[j] = 0;
   }
@@ -787,6 +814,21 @@ __global__ __launch_bounds__(256) void split_kernel(ReviveArgs A) {
       ni += ci * ci;
       nj += cj * cj;
     }
+    if (A.sph) {
+      // spherical e-means: both halves rescaled to norm 1, then rounded to Chat
+      wave_normalize(A.C + (size_t)i * d, d, lane);
+      wave_normalize(A.C + (size_t)j * d, d, lane);
+      if (A.Chat)
+        for (int e = lane; e < d; e += 64) {
+          A.Chat[(size_t)i * d + e] = f32_to_bf16_rne(A.C[(size_t)i * d + e]);
+          A.Chat[(size_t)j * d + e] = f32_to_bf16_rne(A.C[(size_t)j * d + e]);
+        }
+      if (lane == 0) {
+        A.bias[i] = 0.0f;
+        A.bias[j] = 0.0f;
+      }
+      continue;
+    }
     ni = wave_sum(ni);
     nj = wave_sum(nj);
     if (lane == 0) {
@@ -825,6 +867,21 @@ __global__ void finalize_kernel(int k, int d, const int32_t* pass_counts, const 
   }
 }
 
+// Spherical closing step: one wave per cluster, the exact mean of the last
+// pass rescaled to norm 1.
+__global__ __launch_bounds__(256) void finalize_sph_kernel(int k, int d,
+                                                           const int32_t* pass_counts,
+                                                           const float* LS, float* C) {
+  const int j = blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  if (j >= k) return;
+  const int n = pass_counts[j];
+  if (n <= 0) return;
+  const size_t base = (size_t)j * d;
+  for (int e = lane; e < d; e += 64) C[base + e] = __fdiv_rn(LS[base + e], (float)n);
+  wave_normalize(C + base, d, lane);
+}
+
 }  // namespace
 
 hipError_t launch_sample_rows(const PermKey& pk, uint64_t start, int count, uint32_t* rows,
@@ -859,15 +916,15 @@ hipError_t launch_sample_rows_i32(const PermKey& pk, uint64_t start, int count, 
 }
 
 hipError_t launch_init_centroids(bool bf16, const void* X, int d, const PermKey& pk, int k,
-                                 float* C, hipStream_t st) {
+                                 float* C, bool sph, hipStream_t st) {
   init_centroids_kernel<<<(k + 3) / 4, 256, 0, st>>>(static_cast<const unsigned char*>(X),
-                                                     bf16 ? 1 : 0, d, pk, k, C);
+                                                     bf16 ? 1 : 0, d, pk, k, C, sph ? 1 : 0);
   return hipGetLastError();
 }
 
-hipError_t launch_prep(const float* C, int k, int d, float* bias, uint16_t* Chat,
+hipError_t launch_prep(const float* C, int k, int d, float* bias, uint16_t* Chat, bool sph,
                        hipStream_t st) {
-  prep_kernel<<<(k + 3) / 4, 256, 0, st>>>(C, k, d, bias, Chat);
+  prep_kernel<<<(k + 3) / 4, 256, 0, st>>>(C, k, d, bias, Chat, sph ? 1 : 0);
   return hipGetLastError();
 }
 
@@ -928,14 +985,14 @@ hipError_t launch_group(bool bf16, const void* X, int d, const uint32_t* order,
 
 hipError_t launch_ema(int k, int d, float a, float b, int32_t* counts, float* s_acc, float* N,
                       float* S, float* C, float* bias, uint16_t* Chat, int32_t* pass_counts,
-                      float* LS, hipStream_t st) {
+                      float* LS, bool sph, hipStream_t st) {
   const dim3 grid((k + 3) / 4), block(256);
   if (Chat)
     ema_kernel<true><<<grid, block, 0, st>>>(k, d, a, b, counts, s_acc, N, S, C, bias, Chat,
-                                             pass_counts, LS);
+                                             pass_counts, LS, sph ? 1 : 0);
   else
     ema_kernel<false><<<grid, block, 0, st>>>(k, d, a, b, counts, s_acc, N, S, C, bias, Chat,
-                                              pass_counts, LS);
+                                              pass_counts, LS, sph ? 1 : 0);
   return hipGetLastError();
 }
 
@@ -966,7 +1023,11 @@ hipError_t launch_pass_stats(int32_t* pass_counts, int k, double* sums, int rese
 }
 
 hipError_t launch_finalize(int k, int d, const int32_t* pass_counts, const float* LS, float* C,
-                           hipStream_t st) {
+                           bool sph, hipStream_t st) {
+  if (sph) {
+    finalize_sph_kernel<<<(k + 3) / 4, 256, 0, st>>>(k, d, pass_counts, LS, C);
+    return hipGetLastError();
+  }
   const size_t total = (size_t)k * d;
   const size_t want = (total + 255) / 256;
   const unsigned blocks = (unsigned)(want < 65536 ? want : 65536);

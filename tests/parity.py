@@ -36,7 +36,7 @@ def scale_of(X, C, rows, labels):
     return np.einsum("ij,ij->i", Xf, Xf) + np.einsum("ij,ij->i", Cb, Cb)
 
 
-def bf16_flip_bound(X, rows, C32, labels, rel=1e-5):
+def bf16_flip_bound(X, rows, C32, labels, rel=1e-5, dot=False):
     """Bound on how much a label's squared distance can change when the bf16
     search centroid is rounded from running centroids that two exact
     implementations hold with different fp32 summation orders.
@@ -45,7 +45,8 @@ def bf16_flip_bound(X, rows, C32, labels, rel=1e-5):
     its magnitude and the centroid's RMS coordinate) of a bf16 rounding
     boundary may round either way; each such coordinate can move the distance
     by at most (2|x - c| + r) r, with r the possible change of the rounded
-    value. Coordinates away from a boundary round identically on both sides."""
+    value (with dot, the score -2 x.c of spherical e-means: by 2|x| r).
+    Coordinates away from a boundary round identically on both sides."""
     Xf = oracle.to_f32(X if rows is None else X[rows]).astype(np.float64)
     C = np.ascontiguousarray(C32[labels], dtype=np.float32)
     Cb = oracle.bf16_round(C).astype(np.float64)
@@ -58,16 +59,20 @@ def bf16_flip_bound(X, rows, C32, labels, rel=1e-5):
     ulp16 = ulp32 * 65536.0
     dist_to_boundary = np.abs(low - 0x8000) * ulp32
     r = np.where(dist_to_boundary <= delta, ulp16 + delta, 0.0)
+    if dot:
+        return np.sum(2.0 * np.abs(Xf) * r, axis=1)
     return np.sum((2.0 * np.abs(Xf - Cb) + r) * r, axis=1)
 
 
-def check_labels(X, Cs, rows, given, olab, d1, d2, given_dist=None, what="", C32=None):
+def check_labels(X, Cs, rows, given, olab, d1, d2, given_dist=None, what="", C32=None,
+                 dot=False):
     """Check labels `given` against the oracle's (olab, d1, d2) on the same rows.
 
     Every given label g must satisfy d(g) <= d1 + 1e-5 * (|x|^2 + |c_best|^2)
     (+ the bf16 rounding allowance when C32, the unrounded centroids behind a
     bf16 search, is passed). Where the oracle's runner-up gap exceeds that
-    band this forces g to be the oracle's label: decided labels are exact."""
+    band this forces g to be the oracle's label: decided labels are exact.
+    Spherical e-means (dot): d1, d2 and given_dist hold -2 x similarity."""
     given = np.asarray(given)
     assert np.all((given >= 0) & (given < Cs.shape[0]))
     if given_dist is None:
@@ -75,7 +80,8 @@ def check_labels(X, Cs, rows, given, olab, d1, d2, given_dist=None, what="", C32
     sc = scale_of(X, Cs, rows, olab)
     band = GAP_TOL * sc
     if C32 is not None:
-        band = band + bf16_flip_bound(X, rows, C32, olab) + bf16_flip_bound(X, rows, C32, given)
+        band = (band + bf16_flip_bound(X, rows, C32, olab, dot=dot)
+                + bf16_flip_bound(X, rows, C32, given, dot=dot))
     ok = given_dist <= d1 + band
     bad = ~ok
     assert not bad.any(), (
@@ -137,7 +143,8 @@ def lockstep(X: np.ndarray, out, k: int, T: float, seed: int, sample: int = 0,
         dec, und, diff = check_labels(Xs, chk["C"], chk["rows"], chk["given"], chk["oracle"],
                                       chk["d1"], chk["d2"], chk["given_dist"],
                                       what=f"step {chk['t']}",
-                                      C32=chk["C32"] if Xs.dtype == np.uint16 else None)
+                                      C32=chk["C32"] if Xs.dtype == np.uint16 else None,
+                                      dot=chk.get("spherical", False))
         summary["decided"] += dec
         summary["undecided"] += und
         summary["undecided_differ"] += diff

@@ -90,6 +90,39 @@ def test_assign_bf16_search(mm, gen, n, d, k):
     check_dists(Xs, Cs, None, lab, dist, what=f"bf16-search {gen} {n}x{d} k={k}")
 
 
+CASES_SPHERICAL = [("embedding", 1500, 768, 300, False), ("deep", 3000, 96, 1000, False),
+                   ("tiny", 700, 16, 40, False), ("large", 2000, 128, 300, True),
+                   ("large", 900, 64, 129, True), ("large", 600, 256, 70, True)]
+
+
+def _unit_rows(A):
+    A = A.astype(np.float64)
+    return (A / np.maximum(np.linalg.norm(A, axis=1, keepdims=True), 1e-30)).astype(np.float32)
+
+
+@pytest.mark.parametrize("gen,n,d,k,bf16", CASES_SPHERICAL)
+def test_assign_spherical(mm, gen, n, d, k, bf16):
+    """README "Spherical e-means": the centroid with the highest dot product and
+    that similarity (a zero centroid included, which scores 0)."""
+    import torch
+    X = datagen.make(gen, n, d, seed=19)
+    if not bf16:
+        X = _unit_rows(X)
+    C = _unit_rows(_centroids(X, k, 9))
+    C[k // 2] = 0.0
+    lab, sim = mm.assign(to_device(X), torch.from_numpy(C).cuda(), spherical=True)
+    lab, sim = lab.cpu().numpy(), sim.cpu().numpy()
+    Cs = oracle.bf16_round(C) if bf16 else C
+    olab, s1, s2 = oracle.assign_ip(X, Cs)
+    gd = -2.0 * oracle.dot_to(X, Cs, lab)
+    check_labels(X, Cs, None, lab, olab, -2.0 * s1, -2.0 * s2, given_dist=gd,
+                 what=f"spherical {gen} {n}x{d} k={k}")
+    ref = oracle.dot_to(X, Cs, lab)
+    Xf = oracle.to_f32(X).astype(np.float64)
+    scale = np.einsum("ij,ij->i", Xf, Xf) + np.sum(Cs[lab].astype(np.float64) ** 2, axis=1)
+    assert np.all(np.abs(sim - ref) <= 1e-5 * scale)
+
+
 @pytest.mark.parametrize("n,d,k", CASES_BF16)
 def test_assign_bf16(mm, n, d, k):
     X = datagen.large_host(n, d=d, m=64, seed=13)

@@ -51,6 +51,10 @@ LOCKSTEP = [
     ("emb-small-bf16s", "embedding", 12_000, 768, 256, 2.0, dict(bf16_search=True)),
     ("deep-small-bf16s", "deep", 30_000, 96, 1024, 3.0, dict(bf16_search=True)),
     ("ragged-bf16s", "tiny", 5_003, 37, 77, 1.5, dict(batch_size=700, bf16_search=True)),
+    # spherical e-means (README "Spherical e-means") on unit-norm data
+    ("emb-small-sph", "embedding", 12_000, 768, 256, 2.0, dict(spherical=True)),
+    ("deep-small-sph", "deep", 30_000, 96, 1024, 3.0, dict(spherical=True)),
+    ("large-small-sph", "large", 40_000, 128, 1024, 2.0, dict(spherical=True)),
 ]
 
 
@@ -78,6 +82,9 @@ def test_train_lockstep(mm, name, gen, n, d, k, T, o):
     m_ref = oracle.mse(X, res.centroids)
     assert abs(m_gpu - m_ref) <= 1e-3 * m_ref
     np.testing.assert_allclose(out.stats["obj"], res.obj, rtol=1e-4)
+    if o.get("spherical"):
+        nrm = np.linalg.norm(C.astype(np.float64), axis=1)
+        assert np.all((np.abs(nrm - 1.0) < 1e-6) | (nrm == 0.0))
 
 
 # Revival draws at larger k: 64 chunks of 64 V clusters, V = 2, 8 and the
