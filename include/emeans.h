@@ -166,6 +166,60 @@ int emeans_train(const void* X, int64_t n, int32_t d, int32_t k, double T, uint6
 int emeans_assign(const void* X, int64_t n, int32_t d, const float* C, int32_t k,
                   int32_t* labels, float* dists, const emeans_opts* opts);
 
+/* ---------------------------------------------------------------------------
+ * Streaming training (README "Data too big for memory"): the loop that
+ * emeans_train runs, fed batch by batch by the caller, for data that does not
+ * fit on the device while the centroids do:
+ *
+ *   emeans_begin(n, d, k, T, seed, start, &opts, &m);   // recipe from (n, d, k, T)
+ *   for each pass e (stats.rows_per_pass[e] rows, a fresh order):
+ *     for each batch (exactly stats.batch_size rows, the last of a pass: the rest):
+ *       emeans_accumulate(m, batch, rows, labels);    // once, or once per piece
+ *       emeans_update(m);
+ *     emeans_end_epoch(m);
+ *   emeans_finalize(m, centroids, &stats);  emeans_free(m);
+ *
+ * The model checks the counts (rows per batch and per pass), not which rows
+ * were sent. A batch too large for one call may be accumulated in pieces
+ * followed by one update. Revival runs every fifth update; the closing mean
+ * (each centroid the exact mean of the rows the last pass assigned to it) is
+ * taken when every pass has ended. All work is queued on opts->stream.
+ * ------------------------------------------------------------------------- */
+typedef struct emeans_model emeans_model;
+
+/* Start a run: the recipe of emeans_recipe(n, d, k, T, opts); start = device,
+ * k x d fp32 starting centroids (copied; rescaled to norm 1 when
+ * opts->spherical); seed drives the revival draws. opts->max_steps must be 0.
+ * Errors: EINVAL (as emeans_recipe, n >= 2^31, NULL start or model), EDTYPE,
+ * ENOTDEVICE, ENOMEM, EHIP. */
+int emeans_begin(int64_t n, int32_t d, int32_t k, double T, uint64_t seed, const float* start,
+                 const emeans_opts* opts, emeans_model** model);
+
+/* Add `rows` rows (device, rows x d, opts->dtype of emeans_begin, row-major)
+ * to the current batch: assignment with the current centroids, per-cluster
+ * counts and sums. labels: device, rows int32 output (each row's label) or
+ * NULL. Errors: EINVAL (NULL, rows < 1, more rows than the pass or the batch
+ * has left, all passes ended), ENOTDEVICE, EHIP. */
+int emeans_accumulate(emeans_model* m, const void* batch, int64_t rows, int32_t* labels);
+
+/* One update step with the batch accumulated since the last update. Errors:
+ * EINVAL (no rows, a batch other than the recipe's size that does not end
+ * the pass, all steps run), EHIP. */
+int emeans_update(emeans_model* m);
+
+/* End the current pass. Errors: EINVAL (the pass did not visit exactly its
+ * rows, rows accumulated without an update, all passes ended), EHIP. */
+int emeans_end_epoch(emeans_model* m);
+
+/* Centroids (device, k x d fp32 output): the closing mean when every pass has
+ * ended (unless opts->no_finalize), else the current centroids; stats as for
+ * emeans_train (host, or NULL). Synchronises the stream; the model stays
+ * valid. Errors: EINVAL, ENOTDEVICE, EHIP. */
+int emeans_finalize(emeans_model* m, float* centroids, emeans_stats* stats);
+
+/* Release the model and its device workspace (NULL is accepted). */
+void emeans_free(emeans_model* m);
+
 /* Rows visited by batch slots [start, start + count) of pass `pass` of a
  * training run with this seed (README "Data too big for memory": a fresh
  * order every pass, every vector once). rows_out: device, count int32.

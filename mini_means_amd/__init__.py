@@ -76,11 +76,20 @@ def lib() -> ctypes.CDLL:
         L.emeans_assign.argtypes = [c_vp, c_i64, c_i32, c_vp, c_i32, c_vp, c_vp,
                                     ctypes.POINTER(Opts)]
         L.emeans_batch_rows.argtypes = [c_i64, ctypes.c_uint64, c_i32, c_i64, c_i64, c_vp, c_vp]
+        L.emeans_begin.argtypes = [c_i64, c_i32, c_i32, c_dbl, ctypes.c_uint64, c_vp,
+                                   ctypes.POINTER(Opts), ctypes.POINTER(c_vp)]
+        L.emeans_accumulate.argtypes = [c_vp, c_vp, c_i64, c_vp]
+        L.emeans_update.argtypes = [c_vp]
+        L.emeans_end_epoch.argtypes = [c_vp]
+        L.emeans_finalize.argtypes = [c_vp, c_vp, ctypes.POINTER(Stats)]
+        L.emeans_free.argtypes = [c_vp]
+        L.emeans_free.restype = None
         L.emeans_last_error.restype = ctypes.c_char_p
         L.emeans_last_error.argtypes = []
         L.emeans_version.argtypes = []
         for f in ("emeans_recipe", "emeans_train", "emeans_assign", "emeans_batch_rows",
-                  "emeans_version"):
+                  "emeans_version", "emeans_begin", "emeans_accumulate", "emeans_update",
+                  "emeans_end_epoch", "emeans_finalize"):
             getattr(L, f).restype = ctypes.c_int
         _lib = L
     return _lib
@@ -90,7 +99,7 @@ def declared_functions() -> list:
     """Function names the C header declares."""
     with open(HEADER) as f:
         text = f.read()
-    return re.findall(r"^\s*(?:int|const char\*)\s+(emeans_\w+)\s*\(", text, flags=re.M)
+    return re.findall(r"^\s*(?:int|void|const char\*)\s+(emeans_\w+)\s*\(", text, flags=re.M)
 
 
 def _check(rc: int) -> None:
@@ -249,3 +258,199 @@ def batch_rows(n: int, seed: int, pass_: int, start: int, count: int, device="cu
                                            int(start), int(count), out.data_ptr(),
                                            ctypes.c_void_p(s.cuda_stream)))
     return out
+
+
+class Stream:
+    """README "Data too big for memory": the training loop of train(), fed
+    batch by batch by the caller (the model lives on the GPU; every batch is a
+    device tensor of the recipe's batch size, the last of each pass the rest).
+
+        em = mini_means_amd.begin(n, start, T)          # start: k x d fp32, on the GPU
+        B = em.recipe["batch_size"]
+        for rows in em.recipe["epoch_rows"]:
+            ...                                          # a fresh order of `rows` vectors
+            em.update(em.accumulate(batch))              # or accumulate pieces, then update
+            em.end_epoch()
+        centroids = em.finalize()
+    """
+
+    def __init__(self, n: int, start, T: float = 5.0, seed: int = 1234, *, dtype=None,
+                 batch_law="auto", batch_size: int = 0, alpha0: float = 0.0,
+                 unused_threshold=None, finalize: bool = True, bf16_search: bool = False,
+                 spherical: bool = False, profile: bool = False, counts: bool = False,
+                 split_log_cap: int = 0, stream=None):
+        import torch
+        if not (getattr(start, "is_cuda", False) and start.dtype == torch.float32
+                and start.is_contiguous() and start.dim() == 2):
+            raise EmeansError("EINVAL: start must be a contiguous k x d float32 tensor on the GPU")
+        self.k, self.d = start.shape
+        self.n = int(n)
+        self.device = start.device
+        code = F32 if dtype in (None, torch.float32) else BF16 if dtype == torch.bfloat16 else -1
+        if code < 0:
+            raise EmeansError(f"EDTYPE: {dtype} not supported (float32 or bfloat16)")
+        self.dtype = torch.float32 if code == F32 else torch.bfloat16
+        self._stream = stream if stream is not None else torch.cuda.current_stream(self.device)
+        with torch.cuda.device(self.device):
+            o = _opts(code, batch_law, batch_size, alpha0, unused_threshold, finalize, profile,
+                      ctypes.c_void_p(self._stream.cuda_stream))
+            o.bf16_search = 1 if bf16_search else 0
+            o.spherical = 1 if spherical else 0
+            self._counts = torch.empty((self.k,), dtype=torch.float32, device=self.device) \
+                if counts else None
+            self._log = (ctypes.c_int32 * (3 * split_log_cap))() if split_log_cap > 0 else None
+            if self._counts is not None:
+                o.out_counts = self._counts.data_ptr()
+            if self._log is not None:
+                o.split_log = ctypes.cast(self._log, c_vp)
+                o.split_log_cap = split_log_cap
+            self._opts = o
+            self.recipe = recipe(self.n, self.d, self.k, T, batch_law=batch_law,
+                                 batch_size=batch_size, alpha0=alpha0,
+                                 unused_threshold=unused_threshold)
+            h = c_vp()
+            _check(lib().emeans_begin(self.n, self.d, self.k, float(T), int(seed) & (2**64 - 1),
+                                      start.data_ptr(), ctypes.byref(o), ctypes.byref(h)))
+            self._h = h
+        self.stats = None
+
+    def _handle(self):
+        if self._h is None or not self._h.value:
+            raise EmeansError("EINVAL: the model was closed")
+        return self._h
+
+    def accumulate(self, batch, labels: bool = True):
+        """Add a batch (or a piece of one); returns its labels (int32) or None."""
+        import torch
+        _require_device(batch)
+        if batch.dtype != self.dtype or batch.dim() != 2 or batch.shape[1] != self.d:
+            raise EmeansError(f"EINVAL: batch must be rows x {self.d} {self.dtype}")
+        out = torch.empty((batch.shape[0],), dtype=torch.int32, device=self.device) \
+            if labels else None
+        _check(lib().emeans_accumulate(self._handle(), batch.data_ptr(), int(batch.shape[0]),
+                                       out.data_ptr() if out is not None else None))
+        return out
+
+    def update(self, _accumulated=None) -> None:
+        _check(lib().emeans_update(self._handle()))
+
+    def end_epoch(self) -> None:
+        _check(lib().emeans_end_epoch(self._handle()))
+
+    def finalize(self):
+        """Centroids (k x d float32): the closing mean once every pass ended."""
+        import torch
+        C = torch.empty((self.k, self.d), dtype=torch.float32, device=self.device)
+        s = Stats()
+        _check(lib().emeans_finalize(self._handle(), C.data_ptr(), ctypes.byref(s)))
+        self.stats = _stats_dict(s)
+        return C
+
+    @property
+    def counts(self):
+        return self._counts
+
+    @property
+    def split_log(self):
+        if self._log is None or self.stats is None:
+            return None
+        m = self.stats["n_splits"] if self.stats["n_splits"] < len(self._log) // 3 else len(self._log) // 3
+        return [tuple(self._log[3 * i:3 * i + 3]) for i in range(m)]
+
+    def close(self) -> None:
+        if getattr(self, "_h", None) is not None and self._h.value:
+            lib().emeans_free(self._h)
+        self._h = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+
+def begin(n: int, start, T: float = 5.0, seed: int = 1234, **kw) -> Stream:
+    return Stream(n, start, T, seed, **kw)
+
+
+@dataclass
+class HostTrainOutput:
+    centroids: object          # k x d float32 tensor
+    labels: object             # n int32 numpy array (last pass) or None
+    stream: "Stream"
+    trace: object = None       # every batch's labels in step order (int32 numpy) or None
+
+
+def train_from_host(Xh, k: int, T: float = 5.0, seed: int = 1234, *, start=None,
+                    labels: bool = True, trace: bool = False, order=None, device="cuda",
+                    order_seed: int = 0, **kw) -> HostTrainOutput:
+    """Train on a host array (numpy, any row-major n x d float32 array or
+    memory map) that need not fit on the device: every pass visits a fresh
+    order of the rows (order(e, rows) or a seeded random permutation); each
+    batch is gathered into one of two pinned host buffers and copied on a
+    second stream while the device works on the previous batch (default
+    stream priorities)."""
+    import numpy as np
+    import torch
+    Xh = np.asarray(Xh)
+    if Xh.dtype != np.float32 or Xh.ndim != 2:
+        raise EmeansError("EINVAL: Xh must be an n x d float32 array")
+    n, d = Xh.shape
+    dev = torch.device(device)
+    rng = np.random.default_rng(order_seed)
+    if start is None:
+        start = torch.from_numpy(np.ascontiguousarray(
+            Xh[np.sort(rng.choice(n, k, replace=False))])).to(dev)
+    em = Stream(n, start, T, seed, **kw)
+    B = em.recipe["batch_size"]
+    pinned = [torch.empty((B, d), dtype=torch.float32).pin_memory() for _ in range(2)]
+    dbuf = [torch.empty((B, d), dtype=torch.float32, device=dev) for _ in range(2)]
+    copy_stream = torch.cuda.Stream(device=dev)
+    ready = [torch.cuda.Event() for _ in range(2)]
+    used = [torch.cuda.Event() for _ in range(2)]
+    for e in used:
+        e.record(em._stream)
+    out_labels = np.full(n, -1, dtype=np.int32) if labels else None
+    jobs = []
+    for e, rows_e in enumerate(em.recipe["epoch_rows"]):
+        perm = np.asarray(order(e, rows_e)) if order is not None else rng.permutation(n)[:rows_e]
+        for i in range(0, rows_e, B):
+            jobs.append((e, perm[i:i + B]))
+    last_e = len(em.recipe["epoch_rows"]) - 1
+
+    def stage(j):
+        """Gather job j's rows into its pinned buffer and start the copy."""
+        slot = j % 2
+        rows = jobs[j][1]
+        used[slot].synchronize()          # the device is done with this slot's buffer
+        np.take(Xh, rows, axis=0, out=pinned[slot].numpy()[:len(rows)])
+        with torch.cuda.stream(copy_stream):
+            copy_stream.wait_event(used[slot])
+            dbuf[slot][:len(rows)].copy_(pinned[slot][:len(rows)], non_blocking=True)
+            ready[slot].record(copy_stream)
+
+    pending = []
+    if jobs:
+        stage(0)
+    for j, (e, rows) in enumerate(jobs):
+        slot = j % 2
+        if j + 1 < len(jobs):
+            stage(j + 1)                  # overlaps the copy with this batch's compute
+        em._stream.wait_event(ready[slot])
+        want = trace or (labels and e == last_e)
+        lab = em.accumulate(dbuf[slot][:len(rows)], labels=want)
+        used[slot].record(em._stream)
+        em.update(lab)
+        if lab is not None:
+            pending.append((e, rows, lab.to("cpu", non_blocking=True)))
+        if j + 1 == len(jobs) or jobs[j + 1][0] != e:
+            em.end_epoch()
+    C = em.finalize()
+    tr = []
+    for e, rows, lab in pending:
+        if labels and e == last_e:
+            out_labels[rows] = lab.numpy()
+        if trace:
+            tr.append(lab.numpy())
+    return HostTrainOutput(C, out_labels, em, np.concatenate(tr) if trace and tr else None)
+

@@ -6,6 +6,7 @@
 #include <string.h>
 
 #include <chrono>
+#include <new>
 #include <string>
 #include <vector>
 
@@ -171,6 +172,321 @@ struct Arena {
 
 }  // namespace
 
+// Checks of a training run that need no device: dtype, then the recipe's
+// arguments and limits.
+int check_run_args(int64_t n, int32_t d, int32_t k, double T, const emeans_opts* opts) {
+  const int32_t dtype = opts ? opts->dtype : EMEANS_F32;
+  if (dtype != EMEANS_F32 && dtype != EMEANS_BF16)
+    return fail(EMEANS_EDTYPE, "dtype %d not supported (fp32 = 0, bf16 = 1)", dtype);
+  Recipe r;
+  const int rc = make_recipe(n, d, k, T, opts, r);
+  if (rc) return rc;
+  if (n >= ((int64_t)1 << 31)) return fail(EMEANS_EINVAL, "n must be < 2^31");
+  if (r.B >= ((int64_t)1 << 24))
+    return fail(EMEANS_EINVAL, "batch size must be < 2^24 (counts are exact in fp32)");
+  return EMEANS_OK;
+}
+
+// ---------------------------------------------------------------------------
+// The training state of one e-means run: recipe, workspace (one stream-ordered
+// allocation) and the step loop's position. emeans_train drives it with the
+// on-device sampler; the streaming entry points (README "Data too big for
+// memory") let the caller feed the batches.
+// ---------------------------------------------------------------------------
+#define HIP_RET(expr)                                                                      \
+  do {                                                                                     \
+    hipError_t e_ = (expr);                                                                \
+    if (e_ != hipSuccess)                                                                  \
+      return fail(e_ == hipErrorOutOfMemory ? EMEANS_ENOMEM : EMEANS_EHIP, "%s: %s (%s:%d)", \
+                  #expr, hipGetErrorString(e_), __FILE__, __LINE__);                       \
+  } while (0)
+
+struct emeans_model {
+  enum { kAssign = 0, kBucket, kGroup, kUpdate, kRevive, kSample, kClasses };
+  struct Span {
+    int cls;
+    hipEvent_t a, b;
+  };
+
+  // configuration
+  int64_t n = 0;
+  int d = 0, k = 0;
+  uint64_t seed = 0;
+  Recipe r;
+  hipStream_t st = nullptr;
+  bool bf16 = false, bsearch = false, sbf = false, sph = false, profile = false;
+  bool no_finalize = false;
+  int32_t* trace = nullptr;
+  float* out_counts = nullptr;
+  int32_t* split_log = nullptr;
+  int64_t log_cap = 0;
+  std::chrono::steady_clock::time_point t_start;
+
+  // position in the schedule
+  int e = 0;              // current pass
+  int64_t t = 0;          // update steps done
+  int64_t rows_pass = 0;  // rows accumulated in the current pass
+  int64_t rows_step = 0;  // rows accumulated since the last update
+  int64_t trace_off = 0;
+  bool last_begun = false;
+
+  // workspace
+  void* base = nullptr;
+  float* C = nullptr;  // working centroids (the caller's output buffer in emeans_train)
+  uint32_t *rows = nullptr, *order = nullptr;
+  int32_t *blab = nullptr, *pcounts = nullptr, *counts = nullptr, *cursor = nullptr,
+          *off = nullptr, *ovf_n = nullptr, *pass_counts = nullptr, *flags = nullptr,
+          *dead = nullptr, *dlog = nullptr, *pair_i = nullptr, *rv_pos = nullptr,
+          *rv_head = nullptr, *rv_cbase = nullptr, *rv_clen = nullptr, *rv_heads = nullptr,
+          *rv_list = nullptr, *rv_nheads = nullptr;
+  double* rv_u = nullptr;
+  int2* ovf = nullptr;
+  float *s_acc = nullptr, *S = nullptr, *N = nullptr, *LS = nullptr, *bias = nullptr,
+        *n0 = nullptr, *pair_n = nullptr;
+  uint16_t *chat = nullptr, *xb = nullptr;
+  // per pass: [0, P) sum of distances, [P, 3P) sum n^2 and sum n, [3P, 4P) splits (int64)
+  double* dstat = nullptr;
+  int64_t* counters = nullptr;  // [0] splits, [1] logged, [2] dead count, [3] splits this pass
+  std::vector<Span> spans;
+
+  ~emeans_model() {
+    for (const Span& sp : spans) {
+      (void)hipEventDestroy(sp.a);
+      (void)hipEventDestroy(sp.b);
+    }
+    if (base) {
+      (void)hipFreeAsync(base, st);
+      (void)hipStreamSynchronize(st);
+    }
+  }
+
+  // Device time of a kernel class: events recorded on the launch stream around it.
+  template <typename F>
+  hipError_t timed(int cls, F&& launch) {
+    if (!profile) return launch();
+    Span sp{cls, nullptr, nullptr};
+    hipError_t er = hipEventCreate(&sp.a);
+    if (er == hipSuccess) er = hipEventCreate(&sp.b);
+    if (er != hipSuccess) return er;
+    spans.push_back(sp);
+    if ((er = hipEventRecord(sp.a, st)) != hipSuccess) return er;
+    if ((er = launch()) != hipSuccess) return er;
+    return hipEventRecord(sp.b, st);
+  }
+
+  ReviveArgs revive_args(bool count_only) {
+    return ReviveArgs{k, d, N, S, C, bias, chat, r.thr, seed, (uint64_t)t, flags, dead, n0, rv_u,
+                      pair_i, pair_n, rv_pos, rv_head, rv_cbase, rv_clen, rv_heads, rv_list,
+                      rv_nheads, counters, count_only ? nullptr : dlog,
+                      count_only ? 0 : log_cap, count_only ? 1 : 0, sph ? 1 : 0};
+  }
+
+  // Recipe, options and workspace; C = external (the caller's buffer) or own.
+  int init(int64_t n_, int32_t d_, int32_t k_, double T, uint64_t seed_, const emeans_opts* opts,
+           float* external_C) {
+    t_start = std::chrono::steady_clock::now();
+    n = n_;
+    d = d_;
+    k = k_;
+    seed = seed_;
+    const int32_t dtype = opts ? opts->dtype : EMEANS_F32;
+    if (dtype != EMEANS_F32 && dtype != EMEANS_BF16)
+      return fail(EMEANS_EDTYPE, "dtype %d not supported (fp32 = 0, bf16 = 1)", dtype);
+    int rc = make_recipe(n, d, k, T, opts, r);
+    if (rc) return rc;
+    if (n >= ((int64_t)1 << 31)) return fail(EMEANS_EINVAL, "n must be < 2^31");
+    if (r.B >= ((int64_t)1 << 24))
+      return fail(EMEANS_EINVAL, "batch size must be < 2^24 (counts are exact in fp32)");
+    if (opts && opts->trace_labels && (rc = check_device(opts->trace_labels, "trace_labels")))
+      return rc;
+    if (opts && opts->out_counts && (rc = check_device(opts->out_counts, "out_counts"))) return rc;
+    if (opts && opts->split_log && opts->split_log_cap < 0)
+      return fail(EMEANS_EINVAL, "split_log_cap must be >= 0");
+    st = static_cast<hipStream_t>(opts ? opts->stream : nullptr);
+    bf16 = dtype == EMEANS_BF16;
+    bsearch = !bf16 && opts && opts->bf16_search;  // fp32 rows searched in bf16 (into xb)
+    sbf = bf16 || bsearch;                         // the search runs in bf16 against chat
+    sph = opts && opts->spherical;
+    profile = opts && opts->profile;
+    no_finalize = opts && opts->no_finalize;
+    trace = opts ? opts->trace_labels : nullptr;
+    out_counts = opts ? opts->out_counts : nullptr;
+    split_log = (opts && opts->split_log) ? opts->split_log : nullptr;
+    log_cap = split_log ? opts->split_log_cap : 0;
+
+    const size_t kd = (size_t)k * d;
+    const int64_t B = r.B;
+    Arena ar;
+    if (!external_C) ar.want(&C, kd);
+    ar.want(&rows, (size_t)B);
+    ar.want(&order, (size_t)B);
+    ar.want(&blab, (size_t)B);
+    ar.want(&pcounts, (size_t)k);
+    ar.want(&counts, (size_t)k);
+    ar.want(&cursor, (size_t)k);
+    ar.want(&off, (size_t)k + 1);
+    ar.want(&ovf, (size_t)(B / kGroupRows) + 1);
+    ar.want(&ovf_n, 1);
+    ar.want(&pass_counts, (size_t)k);
+    ar.want(&flags, (size_t)k);
+    ar.want(&dead, (size_t)k);
+    ar.want(&n0, (size_t)k);
+    ar.want(&pair_i, (size_t)k);
+    ar.want(&pair_n, (size_t)k);
+    ar.want(&rv_u, (size_t)k);
+    ar.want(&rv_pos, (size_t)k);
+    ar.want(&rv_head, (size_t)k);
+    ar.want(&rv_cbase, (size_t)k);
+    ar.want(&rv_clen, (size_t)k);
+    ar.want(&rv_heads, (size_t)k);
+    ar.want(&rv_list, (size_t)k);
+    ar.want(&rv_nheads, 1);
+    ar.want(&s_acc, kd);
+    ar.want(&S, kd);
+    ar.want(&N, (size_t)k);
+    ar.want(&LS, kd);
+    ar.want(&bias, (size_t)k);
+    if (sbf) ar.want(&chat, kd);
+    if (bsearch) ar.want(&xb, (size_t)B * d);
+    ar.want(&dstat, (size_t)4 * EMEANS_MAX_PASSES);
+    ar.want(&counters, 4);
+    if (log_cap > 0) ar.want(&dlog, (size_t)3 * log_cap);
+    HIP_RET(ar.alloc(&base, st));
+    if (external_C) C = external_C;
+    // zero the statistics and every accumulator the step loop expects at zero
+    HIP_RET(hipMemsetAsync(pcounts, 0, sizeof(int32_t) * k, st));
+    HIP_RET(hipMemsetAsync(counts, 0, sizeof(int32_t) * k, st));
+    HIP_RET(hipMemsetAsync(pass_counts, 0, sizeof(int32_t) * k, st));
+    HIP_RET(hipMemsetAsync(s_acc, 0, sizeof(float) * kd, st));
+    HIP_RET(hipMemsetAsync(S, 0, sizeof(float) * kd, st));
+    HIP_RET(hipMemsetAsync(N, 0, sizeof(float) * k, st));
+    HIP_RET(hipMemsetAsync(LS, 0, sizeof(float) * kd, st));
+    HIP_RET(hipMemsetAsync(dstat, 0, sizeof(double) * 4 * EMEANS_MAX_PASSES, st));
+    HIP_RET(hipMemsetAsync(counters, 0, sizeof(int64_t) * 4, st));
+    return EMEANS_OK;
+  }
+
+  // One batch, or one piece of a batch, of nb rows (row = rows ? rows[r] : r
+  // of X): assignment, bucketing by label, per-cluster sums into s_acc and the
+  // counts of the update; out_labels[row] = label when non-null.
+  int accumulate(const void* X, const uint32_t* rws, int nb, int32_t* out_labels) {
+    if (nb <= 0) return EMEANS_OK;
+    const bool add = rows_step > 0;
+    if (bsearch)
+      HIP_RET(timed(kSample, [&] {
+        return launch_cast_rows(static_cast<const float*>(X), d, rws, nb, xb, st);
+      }));
+    HIP_RET(timed(kAssign, [&] {
+      if (bsearch)
+        return launch_assign(true, xb, d, nullptr, nb, chat, bias, k, blab, nullptr, pcounts,
+                             dstat + e, sph, st);
+      return launch_assign(bf16, X, d, rws, nb, bf16 ? (const void*)chat : (const void*)C, bias, k,
+                           blab, nullptr, pcounts, dstat + e, sph, st);
+    }));
+    if (trace) {
+      HIP_RET(hipMemcpyAsync(trace + trace_off, blab, sizeof(int32_t) * nb,
+                             hipMemcpyDeviceToDevice, st));
+      trace_off += nb;
+    }
+    HIP_RET(timed(kBucket, [&] {
+      hipError_t er = launch_scan(pcounts, k, kGroupRows, off, cursor, ovf, ovf_n, counts, st);
+      if (er != hipSuccess) return er;
+      return launch_scatter(blab, rws, nb, cursor, order, out_labels, st);
+    }));
+    HIP_RET(timed(kGroup, [&] {
+      return launch_group(bf16, X, d, order, off, ovf, ovf_n, k, kGroupRows, nb, s_acc, add, st);
+    }));
+    rows_step += nb;
+    rows_pass += nb;
+    return EMEANS_OK;
+  }
+
+  // EMA update with what was accumulated since the last one; revival every
+  // kReviveEvery updates.
+  int update() {
+    const float a = alpha_at(r.alpha0, t, r.S);
+    const float b = 1.0f - a;
+    const bool last = e == r.npass - 1;
+    HIP_RET(timed(kUpdate, [&] {
+      return launch_ema(k, d, a, b, counts, s_acc, N, S, C, bias, chat, pass_counts,
+                        last ? LS : nullptr, sph, st);
+    }));
+    if (r.thr > 0.0 && (t + 1) % kReviveEvery == 0) {
+      const ReviveArgs ra = revive_args(false);
+      HIP_RET(timed(kRevive, [&] { return launch_revive(ra, st); }));
+    }
+    ++t;
+    rows_step = 0;
+    return EMEANS_OK;
+  }
+
+  // Pass statistics (imbalance, splits) of the current pass; next pass.
+  int close_pass() {
+    const bool last = e == r.npass - 1;
+    HIP_RET(launch_pass_stats(pass_counts, k, dstat + EMEANS_MAX_PASSES + 2 * e, last ? 0 : 1, st));
+    // per-pass split count: snapshot counters[3] then reset it
+    HIP_RET(hipMemcpyAsync(dstat + 3 * EMEANS_MAX_PASSES + e, counters + 3, sizeof(int64_t),
+                           hipMemcpyDeviceToDevice, st));
+    HIP_RET(hipMemsetAsync(counters + 3, 0, sizeof(int64_t), st));
+    ++e;
+    rows_pass = 0;
+    return EMEANS_OK;
+  }
+
+  // Dead count at the end, optional outputs, the closing mean when `closing`,
+  // centroids into out_C (when it is not the working table), statistics.
+  int finish(float* out_C, emeans_stats* stats, bool closing) {
+    double host_stat[4 * EMEANS_MAX_PASSES];
+    int64_t host_counters[4] = {0, 0, 0, 0};
+    if (r.thr > 0.0) {
+      const ReviveArgs ra = revive_args(true);
+      HIP_RET(launch_revive(ra, st));
+    }
+    if (out_counts)
+      HIP_RET(hipMemcpyAsync(out_counts, N, sizeof(float) * k, hipMemcpyDeviceToDevice, st));
+    if (closing) HIP_RET(launch_finalize(k, d, pass_counts, LS, C, sph, st));
+    if (out_C && out_C != C)
+      HIP_RET(hipMemcpyAsync(out_C, C, sizeof(float) * (size_t)k * d, hipMemcpyDeviceToDevice, st));
+    HIP_RET(hipMemcpyAsync(host_stat, dstat, sizeof host_stat, hipMemcpyDeviceToHost, st));
+    HIP_RET(hipMemcpyAsync(host_counters, counters, sizeof host_counters, hipMemcpyDeviceToHost, st));
+    if (log_cap > 0)
+      HIP_RET(hipMemcpyAsync(split_log, dlog, sizeof(int32_t) * 3 * (size_t)log_cap,
+                             hipMemcpyDeviceToHost, st));
+    HIP_RET(hipStreamSynchronize(st));
+    if (!stats) return EMEANS_OK;
+    fill_stats(r, stats);
+    for (int q = 0; q < r.npass; ++q) {
+      stats->obj[q] = r.rows[q] ? host_stat[q] / (double)r.rows[q] : 0.0;
+      const double s2 = host_stat[EMEANS_MAX_PASSES + 2 * q];
+      const double s1 = host_stat[EMEANS_MAX_PASSES + 2 * q + 1];
+      stats->imbalance[q] = s1 > 0 ? (double)k * s2 / (s1 * s1) : 0.0;
+      int64_t sp;
+      memcpy(&sp, &host_stat[3 * EMEANS_MAX_PASSES + q], sizeof sp);
+      stats->splits[q] = sp;
+    }
+    stats->n_splits = host_counters[0];
+    stats->n_logged = host_counters[1] < log_cap ? host_counters[1] : log_cap;
+    stats->dead_at_end = r.thr > 0.0 ? host_counters[2] : 0;
+    if (profile) {
+      double cls_ms[kClasses] = {};
+      for (const Span& sp : spans) {
+        float ms = 0.0f;
+        if (hipEventElapsedTime(&ms, sp.a, sp.b) == hipSuccess) cls_ms[sp.cls] += ms;
+      }
+      stats->ms_assign = cls_ms[kAssign];
+      stats->ms_bucket = cls_ms[kBucket];
+      stats->ms_group = cls_ms[kGroup];
+      stats->ms_update = cls_ms[kUpdate];
+      stats->ms_revive = cls_ms[kRevive];
+      stats->ms_sample = cls_ms[kSample];
+    }
+    stats->steps_run = t;
+    stats->ms_total =
+        std::chrono::duration<double, std::milli>(std::chrono::steady_clock::now() - t_start).count();
+    return EMEANS_OK;
+  }
+};
+
 extern "C" {
 
 const char* emeans_last_error(void) { return g_err.c_str(); }
@@ -252,248 +568,132 @@ int emeans_train(const void* X, int64_t n, int32_t d, int32_t k, double T, uint6
                  float* centroids, int32_t* labels, const emeans_opts* opts,
                  emeans_stats* stats) {
   g_err.clear();
-  const auto t_start = std::chrono::steady_clock::now();
-  const int32_t dtype = opts ? opts->dtype : EMEANS_F32;
-  if (dtype != EMEANS_F32 && dtype != EMEANS_BF16)
-    return fail(EMEANS_EDTYPE, "dtype %d not supported (fp32 = 0, bf16 = 1)", dtype);
-  Recipe r;
-  int rc = make_recipe(n, d, k, T, opts, r);
-  if (rc) return rc;
-  if (n >= ((int64_t)1 << 31)) return fail(EMEANS_EINVAL, "n must be < 2^31");
-  if (r.B >= ((int64_t)1 << 24))
-    return fail(EMEANS_EINVAL, "batch size must be < 2^24 (counts are exact in fp32)");
+  int rc;
+  if ((rc = check_run_args(n, d, k, T, opts))) return rc;
   if (!X || !centroids) return fail(EMEANS_EINVAL, "X and centroids must not be NULL");
   if ((rc = check_device(X, "X")) || (rc = check_device(centroids, "centroids")) ||
       (labels && (rc = check_device(labels, "labels"))))
     return rc;
-  if (opts && opts->trace_labels && (rc = check_device(opts->trace_labels, "trace_labels")))
-    return rc;
-  if (opts && opts->out_counts && (rc = check_device(opts->out_counts, "out_counts"))) return rc;
-  if (opts && opts->split_log && opts->split_log_cap < 0)
-    return fail(EMEANS_EINVAL, "split_log_cap must be >= 0");
-
-  hipStream_t st = static_cast<hipStream_t>(opts ? opts->stream : nullptr);
-  const bool bf16 = dtype == EMEANS_BF16;
-  // fp32 rows searched in bf16: each batch is gathered and rounded into xb
-  const bool bsearch = !bf16 && opts && opts->bf16_search;
-  const bool sbf = bf16 || bsearch;  // the search runs in bf16 against chat
-  const bool sph = opts && opts->spherical;  // spherical e-means
-  const bool profile = opts && opts->profile;
-  const size_t kd = (size_t)k * d;
-  const int64_t B = r.B;
-  const int64_t log_cap = (opts && opts->split_log) ? opts->split_log_cap : 0;
-
-  void* base = nullptr;
-  uint32_t *rows = nullptr, *order = nullptr;
-  int32_t *blab = nullptr, *counts = nullptr, *cursor = nullptr, *off = nullptr,
-          *ovf_n = nullptr, *pass_counts = nullptr, *flags = nullptr, *dead = nullptr,
-          *dlog = nullptr, *pair_i = nullptr, *rv_pos = nullptr, *rv_head = nullptr,
-          *rv_cbase = nullptr, *rv_clen = nullptr, *rv_heads = nullptr, *rv_list = nullptr,
-          *rv_nheads = nullptr;
-  double* rv_u = nullptr;
-  int2* ovf = nullptr;
-  float *bdist = nullptr, *s_acc = nullptr, *S = nullptr, *N = nullptr, *LS = nullptr,
-        *bias = nullptr, *n0 = nullptr, *pair_n = nullptr;
-  uint16_t *chat = nullptr, *xb = nullptr;
-  // per pass: [0, P) sum of distances, [P, 3P) sum n^2 and sum n, [3P, 4P) splits (int64)
-  double* dstat = nullptr;
-  int64_t* counters = nullptr;
-  struct Span {
-    int cls;
-    hipEvent_t a, b;
-  };
-  std::vector<Span> spans;
-  double host_stat[4 * EMEANS_MAX_PASSES];
-  int64_t host_counters[4] = {0, 0, 0, 0};
-  int64_t trace_off = 0;
-  int64_t t = 0;
-
-  Arena ar;
-  ar.want(&rows, (size_t)B);
-  ar.want(&order, (size_t)B);
-  ar.want(&blab, (size_t)B);
-  ar.want(&bdist, (size_t)B);
-  ar.want(&counts, (size_t)k);
-  ar.want(&cursor, (size_t)k);
-  ar.want(&off, (size_t)k + 1);
-  ar.want(&ovf, (size_t)(B / kGroupRows) + 1);
-  ar.want(&ovf_n, 1);
-  ar.want(&pass_counts, (size_t)k);
-  ar.want(&flags, (size_t)k);
-  ar.want(&dead, (size_t)k);
-  ar.want(&n0, (size_t)k);
-  ar.want(&pair_i, (size_t)k);
-  ar.want(&pair_n, (size_t)k);
-  ar.want(&rv_u, (size_t)k);
-  ar.want(&rv_pos, (size_t)k);
-  ar.want(&rv_head, (size_t)k);
-  ar.want(&rv_cbase, (size_t)k);
-  ar.want(&rv_clen, (size_t)k);
-  ar.want(&rv_heads, (size_t)k);
-  ar.want(&rv_list, (size_t)k);
-  ar.want(&rv_nheads, 1);
-  ar.want(&s_acc, kd);
-  ar.want(&S, kd);
-  ar.want(&N, (size_t)k);
-  ar.want(&LS, kd);
-  ar.want(&bias, (size_t)k);
-  if (sbf) ar.want(&chat, kd);
-  if (bsearch) ar.want(&xb, (size_t)B * d);
-  ar.want(&dstat, (size_t)4 * EMEANS_MAX_PASSES);
-  ar.want(&counters, 4);
-  if (log_cap > 0) ar.want(&dlog, (size_t)3 * log_cap);
-
-  // Device time of a kernel class: events recorded on the launch stream around it.
-  enum { kAssign = 0, kBucket, kGroup, kUpdate, kRevive, kSample, kClasses };
-  auto timed = [&](int cls, auto&& launch) -> hipError_t {
-    if (!profile) return launch();
-    Span sp{cls, nullptr, nullptr};
-    hipError_t er = hipEventCreate(&sp.a);
-    if (er == hipSuccess) er = hipEventCreate(&sp.b);
-    if (er != hipSuccess) return er;
-    spans.push_back(sp);
-    if ((er = hipEventRecord(sp.a, st)) != hipSuccess) return er;
-    if ((er = launch()) != hipSuccess) return er;
-    return hipEventRecord(sp.b, st);
-  };
   const int64_t max_steps = opts ? opts->max_steps : 0;
   if (max_steps < 0) return fail(EMEANS_EINVAL, "max_steps must be >= 0");
-  const int64_t run_steps = (max_steps > 0 && max_steps < r.S) ? max_steps : r.S;
-  bool last_pass_begun = false;
 
-  HIP_TRY(ar.alloc(&base, st));
-  // zero the statistics and every accumulator the step loop expects at zero
-  HIP_TRY(hipMemsetAsync(counts, 0, sizeof(int32_t) * k, st));
-  HIP_TRY(hipMemsetAsync(pass_counts, 0, sizeof(int32_t) * k, st));
-  HIP_TRY(hipMemsetAsync(s_acc, 0, sizeof(float) * kd, st));
-  HIP_TRY(hipMemsetAsync(S, 0, sizeof(float) * kd, st));
-  HIP_TRY(hipMemsetAsync(N, 0, sizeof(float) * k, st));
-  HIP_TRY(hipMemsetAsync(LS, 0, sizeof(float) * kd, st));
-  HIP_TRY(hipMemsetAsync(dstat, 0, sizeof(double) * 4 * EMEANS_MAX_PASSES, st));
-  HIP_TRY(hipMemsetAsync(counters, 0, sizeof(int64_t) * 4, st));
-  if (labels) HIP_TRY(hipMemsetAsync(labels, 0xFF, sizeof(int32_t) * (size_t)n, st));
+  emeans_model m;
+  if ((rc = m.init(n, d, k, T, seed, opts, centroids))) return rc;
+  const Recipe& r = m.r;
+  const int64_t B = r.B;
+  const int64_t run_steps = (max_steps > 0 && max_steps < r.S) ? max_steps : r.S;
+  hipStream_t st = m.st;
+  if (labels) HIP_RET(hipMemsetAsync(labels, 0xFF, sizeof(int32_t) * (size_t)n, st));
 
   // starting centroids: k distinct rows (first k entries of the init permutation)
-  HIP_TRY(launch_init_centroids(bf16, X, d, make_perm_key((uint64_t)n, seed, kStreamInit, 0), k,
-                                centroids, sph, st));
-  HIP_TRY(launch_prep(centroids, k, d, bias, chat, sph, st));
+  HIP_RET(launch_init_centroids(m.bf16, X, d, make_perm_key((uint64_t)n, seed, kStreamInit, 0), k,
+                                m.C, m.sph, st));
+  HIP_RET(launch_prep(m.C, k, d, m.bias, m.chat, m.sph, st));
 
-  for (int e = 0; e < r.npass && t < run_steps; ++e) {
+  for (int e = 0; e < r.npass && m.t < run_steps; ++e) {
     const bool last = e == r.npass - 1;
-    last_pass_begun = last;
+    m.last_begun = last;
     const PermKey pk = make_perm_key((uint64_t)n, seed, kStreamPerm, (uint64_t)e);
-    for (int64_t s = 0; s < r.steps[e] && t < run_steps; ++s, ++t) {
+    for (int64_t s = 0; s < r.steps[e] && m.t < run_steps; ++s) {
       const int64_t rem = r.rows[e] - s * B;
       const int nb = (int)(rem < B ? rem : B);
-      const float a = alpha_at(r.alpha0, t, r.S);
-      const float b = 1.0f - a;
-      HIP_TRY(timed(kSample, [&] {
-        hipError_t er = launch_sample_rows(pk, (uint64_t)(s * B), nb, rows, st);
-        if (er != hipSuccess || !bsearch) return er;
-        return launch_cast_rows(static_cast<const float*>(X), d, rows, nb, xb, st);
+      HIP_RET(m.timed(emeans_model::kSample, [&] {
+        return launch_sample_rows(pk, (uint64_t)(s * B), nb, m.rows, st);
       }));
-      HIP_TRY(timed(kAssign, [&] {
-        if (bsearch)
-          return launch_assign(true, xb, d, nullptr, nb, chat, bias, k, blab, bdist, counts,
-                               dstat + e, sph, st);
-        return launch_assign(bf16, X, d, rows, nb, bf16 ? (const void*)chat : (const void*)centroids,
-                             bias, k, blab, bdist, counts, dstat + e, sph, st);
-      }));
-      if (opts && opts->trace_labels) {
-        HIP_TRY(hipMemcpyAsync(opts->trace_labels + trace_off, blab, sizeof(int32_t) * nb,
-                               hipMemcpyDeviceToDevice, st));
-        trace_off += nb;
-      }
-      HIP_TRY(timed(kBucket, [&] {
-        hipError_t er = launch_scan(counts, k, kGroupRows, off, cursor, ovf, ovf_n, st);
-        if (er != hipSuccess) return er;
-        return launch_scatter(blab, rows, nb, cursor, order, (last && labels) ? labels : nullptr, st);
-      }));
-      HIP_TRY(timed(kGroup, [&] {
-        return launch_group(bf16, X, d, order, off, ovf, ovf_n, k, kGroupRows, nb, s_acc, st);
-      }));
-      HIP_TRY(timed(kUpdate, [&] {
-        return launch_ema(k, d, a, b, counts, s_acc, N, S, centroids, bias, chat, pass_counts,
-                          last ? LS : nullptr, sph, st);
-      }));
-      if (r.thr > 0.0 && (t + 1) % kReviveEvery == 0) {
-        ReviveArgs ra{k, d, N, S, centroids, bias, chat, r.thr, seed, (uint64_t)t, flags, dead,
-                      n0, rv_u, pair_i, pair_n, rv_pos, rv_head, rv_cbase, rv_clen, rv_heads,
-                      rv_list, rv_nheads, counters, dlog, log_cap, 0, sph ? 1 : 0};
-        HIP_TRY(timed(kRevive, [&] { return launch_revive(ra, st); }));
-      }
+      if ((rc = m.accumulate(X, m.rows, nb, (last && labels) ? labels : nullptr))) return rc;
+      if ((rc = m.update())) return rc;
     }
-    HIP_TRY(launch_pass_stats(pass_counts, k, dstat + EMEANS_MAX_PASSES + 2 * e, last ? 0 : 1, st));
-    // per-pass split count: snapshot counters[3] then reset it
-    HIP_TRY(hipMemcpyAsync(dstat + 3 * EMEANS_MAX_PASSES + e, counters + 3, sizeof(int64_t),
-                           hipMemcpyDeviceToDevice, st));
-    HIP_TRY(hipMemsetAsync(counters + 3, 0, sizeof(int64_t), st));
+    if ((rc = m.close_pass())) return rc;
   }
-
-  if (r.thr > 0.0) {
-    ReviveArgs ra{k, d, N, S, centroids, bias, chat, r.thr, seed, (uint64_t)t, flags, dead,
-                  n0, rv_u, pair_i, pair_n, rv_pos, rv_head, rv_cbase, rv_clen, rv_heads,
-                  rv_list, rv_nheads, counters, nullptr, 0, 1, sph ? 1 : 0};
-    HIP_TRY(launch_revive(ra, st));
-  }
-  if (opts && opts->out_counts)
-    HIP_TRY(hipMemcpyAsync(opts->out_counts, N, sizeof(float) * k, hipMemcpyDeviceToDevice, st));
-  if (!(opts && opts->no_finalize) && last_pass_begun)
-    HIP_TRY(launch_finalize(k, d, pass_counts, LS, centroids, sph, st));
-
-  HIP_TRY(hipMemcpyAsync(host_stat, dstat, sizeof host_stat, hipMemcpyDeviceToHost, st));
-  HIP_TRY(hipMemcpyAsync(host_counters, counters, sizeof host_counters, hipMemcpyDeviceToHost, st));
-  if (log_cap > 0)
-    HIP_TRY(hipMemcpyAsync(opts->split_log, dlog, sizeof(int32_t) * 3 * (size_t)log_cap,
-                           hipMemcpyDeviceToHost, st));
-  HIP_TRY(hipStreamSynchronize(st));
-
-  if (stats) {
-    fill_stats(r, stats);
-    for (int e = 0; e < r.npass; ++e) {
-      stats->obj[e] = r.rows[e] ? host_stat[e] / (double)r.rows[e] : 0.0;
-      const double s2 = host_stat[EMEANS_MAX_PASSES + 2 * e], s1 = host_stat[EMEANS_MAX_PASSES + 2 * e + 1];
-      stats->imbalance[e] = s1 > 0 ? (double)k * s2 / (s1 * s1) : 0.0;
-      int64_t sp;
-      memcpy(&sp, &host_stat[3 * EMEANS_MAX_PASSES + e], sizeof sp);
-      stats->splits[e] = sp;
-    }
-    stats->n_splits = host_counters[0];
-    stats->n_logged = host_counters[1] < log_cap ? host_counters[1] : log_cap;
-    stats->dead_at_end = r.thr > 0.0 ? host_counters[2] : 0;
-    if (profile) {
-      double cls_ms[kClasses] = {};
-      for (const Span& sp : spans) {
-        float ms = 0.0f;
-        if (hipEventElapsedTime(&ms, sp.a, sp.b) == hipSuccess) cls_ms[sp.cls] += ms;
-      }
-      stats->ms_assign = cls_ms[kAssign];
-      stats->ms_bucket = cls_ms[kBucket];
-      stats->ms_group = cls_ms[kGroup];
-      stats->ms_update = cls_ms[kUpdate];
-      stats->ms_revive = cls_ms[kRevive];
-      stats->ms_sample = cls_ms[kSample];
-    }
-    stats->steps_run = t;
-    stats->ms_total =
-        std::chrono::duration<double, std::milli>(std::chrono::steady_clock::now() - t_start).count();
-  }
-
-done:
-  for (const Span& sp : spans) {
-    (void)hipEventDestroy(sp.a);
-    (void)hipEventDestroy(sp.b);
-  }
-  if (base) {
-    const hipError_t e = hipFreeAsync(base, st);
-    if (e != hipSuccess && rc == EMEANS_OK)
-      rc = fail(EMEANS_EHIP, "hipFreeAsync: %s", hipGetErrorString(e));
-    if (rc == EMEANS_OK) {
-      const hipError_t e2 = hipStreamSynchronize(st);
-      if (e2 != hipSuccess) rc = fail(EMEANS_EHIP, "hipStreamSynchronize: %s", hipGetErrorString(e2));
-    }
-  }
-  return rc;
+  return m.finish(centroids, stats, !m.no_finalize && m.last_begun);
 }
+
+int emeans_begin(int64_t n, int32_t d, int32_t k, double T, uint64_t seed, const float* start,
+                 const emeans_opts* opts, emeans_model** model) {
+  g_err.clear();
+  int rc;
+  if (!model) return fail(EMEANS_EINVAL, "model is NULL");
+  *model = nullptr;
+  if ((rc = check_run_args(n, d, k, T, opts))) return rc;
+  if (!start) return fail(EMEANS_EINVAL, "start must not be NULL");
+  if ((rc = check_device(start, "start"))) return rc;
+  if (opts && opts->max_steps) return fail(EMEANS_EINVAL, "max_steps is an emeans_train option");
+  emeans_model* m = new (std::nothrow) emeans_model;
+  if (!m) return fail(EMEANS_ENOMEM, "model allocation failed");
+  rc = m->init(n, d, k, T, seed, opts, nullptr);
+  if (rc == EMEANS_OK) {
+    const hipError_t e1 =
+        hipMemcpyAsync(m->C, start, sizeof(float) * (size_t)k * d, hipMemcpyDeviceToDevice, m->st);
+    if (e1 != hipSuccess) rc = fail(EMEANS_EHIP, "copy of the starting centroids: %s", hipGetErrorString(e1));
+  }
+  if (rc == EMEANS_OK && m->sph) {  // spherical: the starting centroids rescaled to norm 1 too
+    const hipError_t e3 = launch_normalize_rows(m->C, k, d, m->st);
+    if (e3 != hipSuccess) rc = fail(EMEANS_EHIP, "normalise: %s", hipGetErrorString(e3));
+  }
+  if (rc == EMEANS_OK) {
+    const hipError_t e2 = launch_prep(m->C, k, d, m->bias, m->chat, m->sph, m->st);
+    if (e2 != hipSuccess) rc = fail(EMEANS_EHIP, "centroid prep: %s", hipGetErrorString(e2));
+  }
+  if (rc != EMEANS_OK) {
+    delete m;
+    return rc;
+  }
+  *model = m;
+  return EMEANS_OK;
+}
+
+int emeans_accumulate(emeans_model* m, const void* batch, int64_t rows, int32_t* labels) {
+  g_err.clear();
+  int rc;
+  if (!m) return fail(EMEANS_EINVAL, "model is NULL");
+  if (!batch) return fail(EMEANS_EINVAL, "batch is NULL");
+  if (rows < 1) return fail(EMEANS_EINVAL, "rows must be >= 1 (got %lld)", (long long)rows);
+  if (m->e >= m->r.npass)
+    return fail(EMEANS_EINVAL, "all %d passes of the recipe have ended", m->r.npass);
+  if (m->rows_pass + rows > m->r.rows[m->e])
+    return fail(EMEANS_EINVAL, "pass %d visits %lld rows: %lld more would exceed it", m->e,
+                (long long)m->r.rows[m->e], (long long)rows);
+  if (m->rows_step + rows > m->r.B)
+    return fail(EMEANS_EINVAL, "a batch has at most %lld rows (the recipe's batch size)",
+                (long long)m->r.B);
+  if ((rc = check_device(batch, "batch")) || (labels && (rc = check_device(labels, "labels"))))
+    return rc;
+  if (m->e == m->r.npass - 1) m->last_begun = true;
+  return m->accumulate(batch, nullptr, (int)rows, labels);
+}
+
+int emeans_update(emeans_model* m) {
+  g_err.clear();
+  if (!m) return fail(EMEANS_EINVAL, "model is NULL");
+  if (m->rows_step < 1) return fail(EMEANS_EINVAL, "no rows accumulated since the last update");
+  if (m->rows_step != m->r.B && m->rows_pass != m->r.rows[m->e])
+    return fail(EMEANS_EINVAL,
+                "a batch must have exactly %lld rows except the last of a pass (got %lld)",
+                (long long)m->r.B, (long long)m->rows_step);
+  if (m->t >= m->r.S) return fail(EMEANS_EINVAL, "all %lld update steps have run", (long long)m->r.S);
+  return m->update();
+}
+
+int emeans_end_epoch(emeans_model* m) {
+  g_err.clear();
+  if (!m) return fail(EMEANS_EINVAL, "model is NULL");
+  if (m->e >= m->r.npass) return fail(EMEANS_EINVAL, "all %d passes have ended", m->r.npass);
+  if (m->rows_step) return fail(EMEANS_EINVAL, "rows accumulated without an update");
+  if (m->rows_pass != m->r.rows[m->e])
+    return fail(EMEANS_EINVAL, "pass %d must visit %lld rows (got %lld)", m->e,
+                (long long)m->r.rows[m->e], (long long)m->rows_pass);
+  return m->close_pass();
+}
+
+int emeans_finalize(emeans_model* m, float* centroids, emeans_stats* stats) {
+  g_err.clear();
+  int rc;
+  if (!m) return fail(EMEANS_EINVAL, "model is NULL");
+  if (!centroids) return fail(EMEANS_EINVAL, "centroids must not be NULL");
+  if ((rc = check_device(centroids, "centroids"))) return rc;
+  return m->finish(centroids, stats, !m->no_finalize && m->e == m->r.npass);
+}
+
+void emeans_free(emeans_model* m) { delete m; }
 
 }  // extern "C"

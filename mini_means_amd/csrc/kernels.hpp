@@ -48,19 +48,23 @@ hipError_t launch_cast_rows(const float* X, int d, const uint32_t* rows, int nro
 
 // off = exclusive scan of counts (k+1 entries), cursor = off[0..k); ovf lists
 // the grouping work items beyond the first R rows of each cluster as
-// (cluster, part) pairs, *ovf_n of them (room for rows / R pairs).
-hipError_t launch_scan(const int32_t* counts, int k, int R, int32_t* off, int32_t* cursor,
-                       int2* ovf, int32_t* ovf_n, hipStream_t st);
+// (cluster, part) pairs, *ovf_n of them (room for rows / R pairs). With acc:
+// acc += counts, then counts = 0 (the counts of one piece of a batch join the
+// update's totals).
+hipError_t launch_scan(int32_t* counts, int k, int R, int32_t* off, int32_t* cursor,
+                       int2* ovf, int32_t* ovf_n, int32_t* acc, hipStream_t st);
 
-// Bucket the batch by label: order[cursor[label]++] = rows[r]; when
-// out_labels is non-null also out_labels[rows[r]] = label.
+// Bucket the batch by label: order[cursor[label]++] = rows[r] (r when rows is
+// NULL); when out_labels is non-null also out_labels[rows[r]] = label.
 hipError_t launch_scatter(const int32_t* labels, const uint32_t* rows, int nb, int32_t* cursor,
                           uint32_t* order, int32_t* out_labels, hipStream_t st);
 
-// s_acc[j] += sum of X rows of cluster j (work items of at most R rows).
+// s_acc[j] += sum of X rows of cluster j (work items of at most R rows). A
+// cluster held by one work item is stored, assuming s_acc[j] = 0, unless
+// `add` (a later piece of the same update).
 hipError_t launch_group(bool bf16, const void* X, int d, const uint32_t* order,
                         const int32_t* off, const int2* ovf, const int32_t* ovf_n, int k, int R,
-                        int nb, float* s_acc, hipStream_t st);
+                        int nb, float* s_acc, bool add, hipStream_t st);
 
 // EMA update of every cluster; resets counts and s_acc for the next step;
 // pass_counts += counts; LS += s when LS is non-null; refreshes bias/Chat.
@@ -104,6 +108,9 @@ hipError_t launch_revive(const ReviveArgs& a, hipStream_t st);
 
 // sums[0] += sum n_j^2, sums[1] += sum n_j over pass_counts; zeroes them if `reset`.
 hipError_t launch_pass_stats(int32_t* pass_counts, int k, double* sums, int reset, hipStream_t st);
+
+// Rows of C rescaled to norm 1 (fp64 norm and quotient); zero rows stay zero.
+hipError_t launch_normalize_rows(float* C, int k, int d, hipStream_t st);
 
 // C[j] = LS[j] / pass_counts[j] where pass_counts[j] > 0 (rescaled to norm
 // 1 when sph).

@@ -136,11 +136,12 @@ __global__ __launch_bounds__(256) void prep_kernel(const float* C, int k, int d,
 // thread owns 16 consecutive clusters; one block scan of the packed pair (rows
 // in the high word, overflow items in the low word) serves both sums, and the
 // row offsets go back through LDS to be stored coalesced.
-__global__ __launch_bounds__(1024) void scan_kernel(const int32_t* __restrict__ counts, int k,
+__global__ __launch_bounds__(1024) void scan_kernel(int32_t* __restrict__ counts, int k,
                                                     int R, int32_t* __restrict__ off,
                                                     int32_t* __restrict__ cursor,
                                                     int2* __restrict__ ovf,
-                                                    int32_t* __restrict__ ovf_n) {
+                                                    int32_t* __restrict__ ovf_n,
+                                                    int32_t* __restrict__ acc) {
   constexpr int V = 16, kTile = 1024 * V;
   __shared__ int lds[kTile + kTile / 16];
   __shared__ uint64_t tmp[16];
@@ -165,6 +166,16 @@ __global__ __launch_bounds__(1024) void scan_kernel(const int32_t* __restrict__ 
     for (int v = 0; v < V; ++v) {
       const int j = t1 + v * 1024 + tid;
       nx[v] = j < k ? counts[j] : 0;
+    }
+    if (acc) {  // the piece's counts join the update's totals and are cleared
+#pragma unroll
+      for (int v = 0; v < V; ++v) {
+        const int j = t0 + v * 1024 + tid;
+        if (j < k) {
+          acc[j] += lds[at(v * 1024 + tid)];
+          counts[j] = 0;
+        }
+      }
     }
     uint64_t loc = 0;
 #pragma unroll
@@ -230,7 +241,7 @@ __global__ void scatter_kernel(const int32_t* labels, const uint32_t* rows, int 
   const int r = blockIdx.x * blockDim.x + threadIdx.x;
   if (r >= nb) return;
   const int j = labels[r];
-  const uint32_t row = rows[r];
+  const uint32_t row = rows ? rows[r] : (uint32_t)r;
   const int pos = atomicAdd(&cursor[j], 1);
   order[pos] = row;
   if (out_labels) out_labels[row] = j;
@@ -249,7 +260,7 @@ __global__ __launch_bounds__(256) void group_kernel(const unsigned char* __restr
                                                     const int32_t* __restrict__ off,
                                                     const int2* __restrict__ ovf,
                                                     const int32_t* __restrict__ ovf_n, int k,
-                                                    int R, float* __restrict__ s_acc) {
+                                                    int R, float* __restrict__ s_acc, int add) {
   constexpr int ES = BF16 ? 2 : 4;
   constexpr int EPV = VEC ? 16 / ES : 1;  // elements per column unit
   constexpr int U = 8;                    // rows in flight per thread
@@ -312,8 +323,10 @@ __global__ __launch_bounds__(256) void group_kernel(const unsigned char* __restr
   auto write_out = [&](int col, const float* acc) {
 #pragma unroll
     for (int e = 0; e < EPV; ++e) {
-      if (single)
+      if (single && !add)
         dst[col * EPV + e] = acc[e];
+      else if (single)
+        dst[col * EPV + e] += acc[e];  // later pieces of one update add to the sums
       else
         atomicAdd(&dst[col * EPV + e], acc[e]);
     }
@@ -362,7 +375,8 @@ __global__ __launch_bounds__(256) void group_wave_kernel(const unsigned char* __
                                                          const int32_t* __restrict__ off,
                                                          const int2* __restrict__ ovf,
                                                          const int32_t* __restrict__ ovf_n,
-                                                         int k, int R, float* __restrict__ s_acc) {
+                                                         int k, int R, float* __restrict__ s_acc,
+                                                         int add) {
   constexpr int ES = BF16 ? 2 : 4;
   constexpr int EPV = VEC ? 16 / ES : 1;  // elements per column unit
   constexpr int U = 8;                    // rows in flight per lane
@@ -437,8 +451,10 @@ __global__ __launch_bounds__(256) void group_wave_kernel(const unsigned char* __
     float* dst = s_acc + (size_t)j * d + (size_t)col * EPV;
 #pragma unroll
     for (int e = 0; e < EPV; ++e) {
-      if (single)
+      if (single && !add)
         dst[e] = acc[e];
+      else if (single)
+        dst[e] += acc[e];  // later pieces of one update add to the sums
       else
         atomicAdd(&dst[e], acc[e]);
     }
@@ -867,6 +883,12 @@ __global__ void finalize_kernel(int k, int d, const int32_t* pass_counts, const 
   }
 }
 
+// Spherical e-means: rows of C rescaled to norm 1 in place, one wave per row.
+__global__ __launch_bounds__(256) void normalize_rows_kernel(float* C, int k, int d) {
+  const int j = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (j < k) wave_normalize(C + (size_t)j * d, d, threadIdx.x & 63);
+}
+
 // Spherical closing step: one wave per cluster, the exact mean of the last
 // pass rescaled to norm 1.
 __global__ __launch_bounds__(256) void finalize_sph_kernel(int k, int d,
@@ -928,9 +950,9 @@ hipError_t launch_prep(const float* C, int k, int d, float* bias, uint16_t* Chat
   return hipGetLastError();
 }
 
-hipError_t launch_scan(const int32_t* counts, int k, int R, int32_t* off, int32_t* cursor,
-                       int2* ovf, int32_t* ovf_n, hipStream_t st) {
-  scan_kernel<<<1, 1024, 0, st>>>(counts, k, R, off, cursor, ovf, ovf_n);
+hipError_t launch_scan(int32_t* counts, int k, int R, int32_t* off, int32_t* cursor,
+                       int2* ovf, int32_t* ovf_n, int32_t* acc, hipStream_t st) {
+  scan_kernel<<<1, 1024, 0, st>>>(counts, k, R, off, cursor, ovf, ovf_n, acc);
   return hipGetLastError();
 }
 
@@ -943,7 +965,7 @@ hipError_t launch_scatter(const int32_t* labels, const uint32_t* rows, int nb, i
 
 hipError_t launch_group(bool bf16, const void* X, int d, const uint32_t* order,
                         const int32_t* off, const int2* ovf, const int32_t* ovf_n, int k, int R,
-                        int nb, float* s_acc, hipStream_t st) {
+                        int nb, float* s_acc, bool add, hipStream_t st) {
   if (nb <= 0) return hipSuccess;
   // work items: one per cluster plus at most nb / R overflow items
   const long long items = (long long)k + nb / R;
@@ -955,14 +977,14 @@ hipError_t launch_group(bool bf16, const void* X, int d, const uint32_t* order,
     const dim3 wgrid((unsigned)((items + 3) / 4)), wblock(256);
     if (bf16) {
       if (vec)
-        group_wave_kernel<true, true><<<wgrid, wblock, 0, st>>>(x, d, order, off, ovf, ovf_n, k, R, s_acc);
+        group_wave_kernel<true, true><<<wgrid, wblock, 0, st>>>(x, d, order, off, ovf, ovf_n, k, R, s_acc, add ? 1 : 0);
       else
-        group_wave_kernel<true, false><<<wgrid, wblock, 0, st>>>(x, d, order, off, ovf, ovf_n, k, R, s_acc);
+        group_wave_kernel<true, false><<<wgrid, wblock, 0, st>>>(x, d, order, off, ovf, ovf_n, k, R, s_acc, add ? 1 : 0);
     } else {
       if (vec)
-        group_wave_kernel<false, true><<<wgrid, wblock, 0, st>>>(x, d, order, off, ovf, ovf_n, k, R, s_acc);
+        group_wave_kernel<false, true><<<wgrid, wblock, 0, st>>>(x, d, order, off, ovf, ovf_n, k, R, s_acc, add ? 1 : 0);
       else
-        group_wave_kernel<false, false><<<wgrid, wblock, 0, st>>>(x, d, order, off, ovf, ovf_n, k, R, s_acc);
+        group_wave_kernel<false, false><<<wgrid, wblock, 0, st>>>(x, d, order, off, ovf, ovf_n, k, R, s_acc, add ? 1 : 0);
     }
     return hipGetLastError();
   }
@@ -971,14 +993,14 @@ hipError_t launch_group(bool bf16, const void* X, int d, const uint32_t* order,
   const dim3 grid((unsigned)items), block(nt);
   if (bf16) {
     if (vec)
-      group_kernel<true, true><<<grid, block, 0, st>>>(x, d, order, off, ovf, ovf_n, k, R, s_acc);
+      group_kernel<true, true><<<grid, block, 0, st>>>(x, d, order, off, ovf, ovf_n, k, R, s_acc, add ? 1 : 0);
     else
-      group_kernel<true, false><<<grid, block, 0, st>>>(x, d, order, off, ovf, ovf_n, k, R, s_acc);
+      group_kernel<true, false><<<grid, block, 0, st>>>(x, d, order, off, ovf, ovf_n, k, R, s_acc, add ? 1 : 0);
   } else {
     if (vec)
-      group_kernel<false, true><<<grid, block, 0, st>>>(x, d, order, off, ovf, ovf_n, k, R, s_acc);
+      group_kernel<false, true><<<grid, block, 0, st>>>(x, d, order, off, ovf, ovf_n, k, R, s_acc, add ? 1 : 0);
     else
-      group_kernel<false, false><<<grid, block, 0, st>>>(x, d, order, off, ovf, ovf_n, k, R, s_acc);
+      group_kernel<false, false><<<grid, block, 0, st>>>(x, d, order, off, ovf, ovf_n, k, R, s_acc, add ? 1 : 0);
   }
   return hipGetLastError();
 }
@@ -1019,6 +1041,11 @@ hipError_t launch_revive(const ReviveArgs& a, hipStream_t st) {
 hipError_t launch_pass_stats(int32_t* pass_counts, int k, double* sums, int reset,
                              hipStream_t st) {
   pass_stats_kernel<<<1, 1024, 0, st>>>(pass_counts, k, sums, reset);
+  return hipGetLastError();
+}
+
+hipError_t launch_normalize_rows(float* C, int k, int d, hipStream_t st) {
+  normalize_rows_kernel<<<(k + 3) / 4, 256, 0, st>>>(C, k, d);
   return hipGetLastError();
 }
 
