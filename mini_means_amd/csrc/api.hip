@@ -242,7 +242,7 @@ struct emeans_model {
   double* rv_u = nullptr;
   int2* ovf = nullptr;
   float *s_acc = nullptr, *S = nullptr, *N = nullptr, *LS = nullptr, *bias = nullptr,
-        *n0 = nullptr, *pair_n = nullptr;
+        *n0 = nullptr, *pair_n = nullptr, *wlive = nullptr;
   uint16_t *chat = nullptr, *xb = nullptr;
   // per pass: [0, P) sum of distances, [P, 3P) sum n^2 and sum n, [3P, 4P) splits (int64)
   double* dstat = nullptr;
@@ -278,7 +278,7 @@ struct emeans_model {
     return ReviveArgs{k, d, N, S, C, bias, chat, r.thr, seed, (uint64_t)t, flags, dead, n0, rv_u,
                       pair_i, pair_n, rv_pos, rv_head, rv_cbase, rv_clen, rv_heads, rv_list,
                       rv_nheads, counters, count_only ? nullptr : dlog,
-                      count_only ? 0 : log_cap, count_only ? 1 : 0, sph ? 1 : 0};
+                      count_only ? 0 : log_cap, count_only ? 1 : 0, sph ? 1 : 0, wlive};
   }
 
   // Recipe, options and workspace; C = external (the caller's buffer) or own.
@@ -341,6 +341,7 @@ struct emeans_model {
     ar.want(&rv_heads, (size_t)k);
     ar.want(&rv_list, (size_t)k);
     ar.want(&rv_nheads, 1);
+    if (k > 32768) ar.want(&wlive, (size_t)((k + 4095) / 4096) * 4096);
     ar.want(&s_acc, kd);
     ar.want(&S, kd);
     ar.want(&N, (size_t)k);

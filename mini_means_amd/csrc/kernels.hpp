@@ -101,6 +101,7 @@ struct ReviveArgs {
   int64_t log_cap;
   int count_only;
   int sph;            // spherical e-means: split centroids rescaled to norm 1, bias 0
+  float* wlive;       // live counts (0 for dead) when k > 32768; k rounded up to 4096
 };
 // Dead-cluster check and donor draws (one workgroup), then the splits of the
 // running sums, one wave per donor chain.

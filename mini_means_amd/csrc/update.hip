@@ -588,11 +588,17 @@ __global__ __launch_bounds__(1024) void revive_kernel(ReviveArgs A) {
     const int dd = ((double)nv < th) ? 1 : 0;
     A.flags[j] = dd;
     A.n0[j] = nv;
-    if constexpr (lds_n) wN[j] = dd ? 0.0f : nv;
+    if constexpr (lds_n)
+      wN[j] = dd ? 0.0f : nv;
+    else
+      A.wlive[j] = dd ? 0.0f : nv;  // live counts, read by the draws with wide loads
     cnt += dd;
   }
-  if constexpr (lds_n)  // zero counts past k up to the 64 chunks: no bounds test in a draw
+  // zero counts past k up to the 64 chunks: no bounds test in a draw
+  if constexpr (lds_n)
     for (int j = k + tid; j < 64 * CS; j += 1024) wN[j] = 0.0f;
+  else if constexpr (VT > 0)
+    for (int j = k + tid; j < 64 * CS; j += 1024) A.wlive[j] = 0.0f;
   const int incl = block_incl_scan<int, 1024>(cnt, itmp);
   if (tid == 1023) s_ndead = incl;
   if (tid == 0) s_last = -1;
@@ -636,7 +642,7 @@ __global__ __launch_bounds__(1024) void revive_kernel(ReviveArgs A) {
     auto live_count = [&](int idx) -> float {
       if constexpr (lds_n) return wN[idx];
       if (idx >= k) return 0.0f;
-      return A.flags[idx] ? 0.0f : A.N[idx];
+      return A.wlive[idx];
     };
     double lsum = csum[lane];
     double incA = wave_scan_f64(lsum);
@@ -684,8 +690,15 @@ __global__ __launch_bounds__(1024) void revive_kernel(ReviveArgs A) {
               }
             }
           } else {
+            // VT consecutive live counts (zero-padded to 64 chunks): independent wide loads
 #pragma unroll
-            for (int v = 0; v < VT; ++v) w[v] = live_count(i0 + v);
+            for (int v = 0; v < VT; v += 4) {
+              const float4 q4 = *reinterpret_cast<const float4*>(&A.wlive[i0 + v]);
+              w[v] = q4.x;
+              w[v + 1] = q4.y;
+              w[v + 2] = q4.z;
+              w[v + 3] = q4.w;
+            }
           }
 #pragma unroll
           for (int v = 0; v < VT; ++v) {
@@ -723,7 +736,7 @@ __global__ __launch_bounds__(1024) void revive_kernel(ReviveArgs A) {
         if constexpr (lds_n)
           nvd = wN[donor];
         else
-          nvd = A.N[donor];
+          nvd = A.wlive[donor];
       }
       const int i = donor;
       const float Nh = nvd * 0.5f;
@@ -732,7 +745,10 @@ __global__ __launch_bounds__(1024) void revive_kernel(ReviveArgs A) {
         A.N[j] = Nh;
         A.pair_i[q] = i;
         A.pair_n[q] = Nh;
-        if constexpr (lds_n) wN[i] = Nh;
+        if constexpr (lds_n)
+          wN[i] = Nh;
+        else
+          A.wlive[i] = Nh;
         if (A.log && logc < A.log_cap) {
           A.log[3 * logc] = (int32_t)A.step;
           A.log[3 * logc + 1] = j;

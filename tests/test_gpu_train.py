@@ -87,11 +87,13 @@ def test_train_lockstep(mm, name, gen, n, d, k, T, o):
         assert np.all((np.abs(nrm - 1.0) < 1e-6) | (nrm == 0.0))
 
 
-# Revival draws at larger k: 64 chunks of 64 V clusters, V = 2, 8 and the
-# register-free path (k > 65536), each with thousands of revivals.
+# Revival draws at larger k: 64 chunks of 64 V clusters, V = 2, 8, 16 (live
+# counts in global memory) and the generic path (k > 65536), each with
+# thousands of revivals.
 REVIVAL_K = [
     ("k6000", 24_000, 8, 6_000, 4_096),
     ("k20000", 60_000, 8, 20_000, 8_192),
+    ("k40000", 100_000, 4, 40_000, 16_384),
     ("k66000", 140_000, 4, 66_000, 16_384),
 ]
 
