@@ -216,12 +216,16 @@ def _dtype_code(X: np.ndarray) -> int:
         return 0
     if X.dtype == np.uint16:      # bf16 bit patterns
         return 1
+    if X.dtype == np.int8:        # int8 codes
+        return 2
     raise TypeError(f"unsupported data type {X.dtype}")
 
 
 def to_f32(X: np.ndarray) -> np.ndarray:
     if X.dtype == np.uint16:
         return (X.astype(np.uint32) << 16).view(np.float32)
+    if X.dtype == np.int8:
+        return X.astype(np.float32)
     return X
 
 
@@ -246,9 +250,54 @@ def search_data(X: np.ndarray, bf16_search: bool) -> np.ndarray:
     return X
 
 
+def int8_round(C: np.ndarray) -> np.ndarray:
+    """Centroids (code space) -> nearest int8 code (ties to even), clamped to
+    [-127, 127], returned as fp32 values."""
+    return np.clip(np.rint(np.asarray(C, dtype=np.float32)), -127, 127).astype(np.float32)
+
+
+def int8_calibrate(sample: np.ndarray):
+    """README "Data precision", INT8: a shift per dimension and one power-of-two
+    scale from a sample. Readings: the shift is the sample's midrange per
+    dimension (fp64, stored fp32); the scale is the largest power of two that
+    maps every sample value within [-127, 127] (1 for a constant sample)."""
+    x = np.asarray(sample, dtype=np.float32)
+    mn = x.min(axis=0).astype(np.float64)
+    mx = x.max(axis=0).astype(np.float64)
+    shift = ((mn + mx) / 2.0).astype(np.float32)
+    s64 = shift.astype(np.float64)
+    r = float(np.max(np.maximum(mx - s64, s64 - mn))) if x.size else 0.0
+    scale = 1.0 if r <= 0.0 else 2.0 ** math.floor(math.log2(127.0 / r))
+    while scale * r > 127.0:    # guard the floor of a rounded logarithm
+        scale /= 2.0
+    while scale * 2.0 * r <= 127.0:
+        scale *= 2.0
+    return shift, scale
+
+
+def int8_encode(X: np.ndarray, shift: np.ndarray, scale: float) -> np.ndarray:
+    """Codes: (x - shift) * scale in fp32 (the scale is a power of two, so the
+    product is exact), rounded to nearest (ties to even) and clamped to
+    [-127, 127] (values beyond the calibrated range go to the edge)."""
+    y = (np.asarray(X, dtype=np.float32) - np.asarray(shift, dtype=np.float32)) * np.float32(scale)
+    return np.clip(np.rint(y), -127, 127).astype(np.int8)
+
+
+def int8_decode(C: np.ndarray, shift: np.ndarray, scale: float) -> np.ndarray:
+    """Code-space vectors (centroids) back to data space: c / scale + shift."""
+    return (np.asarray(C, dtype=np.float64) / scale
+            + np.asarray(shift, dtype=np.float64)).astype(np.float32)
+
+
 def search_centroids(C: np.ndarray, X: np.ndarray) -> np.ndarray:
-    """Centroids in the search format: bf16 for bf16 data, fp32 otherwise."""
-    return bf16_round(C) if X.dtype == np.uint16 else np.ascontiguousarray(C, dtype=np.float32)
+    """Centroids in the search format: bf16 for bf16 data, int8 codes for int8
+    data (README "Data precision": only the search uses the smaller format),
+    fp32 otherwise."""
+    if X.dtype == np.uint16:
+        return bf16_round(C)
+    if X.dtype == np.int8:
+        return int8_round(C)
+    return np.ascontiguousarray(C, dtype=np.float32)
 
 
 def assign(X: np.ndarray, C: np.ndarray, rows: Optional[np.ndarray] = None, nthreads: int = 0):

@@ -105,10 +105,11 @@ void ref_perm_range(uint64_t n, uint64_t seed, uint64_t stream, uint64_t pass, u
 
 /* ------------------------------------------------------------------------ */
 /* Element access: dtype 0 = fp32, 1 = bf16 (stored as the high 16 bits of  */
-/* an fp32).                                                                 */
+/* an fp32), 2 = int8 codes.                                                 */
 /* ------------------------------------------------------------------------ */
 static inline double ref_elem(const void* X, int dtype, int64_t row, int32_t d, int32_t t) {
   if (dtype == 0) return (double)((const float*)X)[row * (int64_t)d + t];
+  if (dtype == 2) return (double)((const int8_t*)X)[row * (int64_t)d + t];  /* int8 codes */
   uint32_t bits = (uint32_t)((const uint16_t*)X)[row * (int64_t)d + t] << 16;
   float f;
   memcpy(&f, &bits, 4);

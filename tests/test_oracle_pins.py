@@ -491,6 +491,72 @@ def test_spherical_closing_step_is_normalised_mean():
     np.testing.assert_allclose(en[en > 0], 1.0, atol=1e-6)
 
 
+# ---------------------------------------------------------------------------
+# int8 codes (README "Data precision", INT8)
+# ---------------------------------------------------------------------------
+
+def test_assign_int8_is_exact_integer_argmin():
+    """int8 rows against int8-valued centroids: distances are integers, so the
+    oracle's fp64 argmin equals numpy's int64 argmin exactly (lowest index on
+    ties, which duplicated centroids force)."""
+    rng = np.random.default_rng(41)
+    X = rng.integers(-127, 128, size=(900, 48)).astype(np.int8)
+    C = rng.integers(-127, 128, size=(70, 48)).astype(np.float32)
+    C[9] = C[2]
+    X[:40] = C[2].astype(np.int8)                    # exact hits on the tied pair
+    D = ((X.astype(np.int64)[:, None, :] - C.astype(np.int64)[None, :, :]) ** 2).sum(-1)
+    lab, d1, d2 = oracle.assign(X, C)
+    assert np.array_equal(lab, np.argmin(D, axis=1))
+    assert np.array_equal(d1, D.min(axis=1).astype(np.float64))
+    assert np.all(lab[:40] == 2) and not np.any(lab == 9)
+
+
+def test_int8_calibration_and_codes():
+    rng = np.random.default_rng(42)
+    S = (rng.standard_normal((5000, 24)) * rng.uniform(0.1, 9.0, 24) + rng.uniform(-5, 5, 24))
+    S = S.astype(np.float32)
+    shift, scale = oracle.int8_calibrate(S)
+    mn, mx = S.min(0).astype(np.float64), S.max(0).astype(np.float64)
+    np.testing.assert_allclose(shift, (mn + mx) / 2, rtol=1e-6, atol=1e-6)
+    r = np.max(np.maximum(mx - shift, shift - mn))
+    assert math.log2(scale) == int(math.log2(scale))          # a power of two
+    assert scale * r <= 127.0 < 2.0 * scale * r               # the largest one that fits
+    codes = oracle.int8_encode(S, shift, scale)
+    assert codes.dtype == np.int8 and codes.min() >= -127 and codes.max() <= 127
+    back = oracle.int8_decode(codes, shift, scale)
+    assert np.max(np.abs(back.astype(np.float64) - S)) <= 0.5 / scale * (1 + 1e-6)
+    # beyond the calibrated range: clamped to the edge
+    far = np.full((1, 24), 1e6, np.float32)
+    assert np.all(oracle.int8_encode(far, shift, scale) == 127)
+    assert np.all(oracle.int8_encode(-far, shift, scale) == -127)
+    # the search rounds centroids to the nearest code, ties to even, clamped
+    C = np.array([[2.5, -0.5, 127.6, -200.0, 3.49, -2.5]], np.float32)
+    assert oracle.int8_round(C).tolist() == [[2.0, -0.0, 127.0, -127.0, 3.0, -2.0]]
+
+
+def test_int8_training_closing_mean_is_exact_mean_of_codes():
+    """Training on int8 codes: the centroids live in code space (fp32), the
+    search uses their int8 rounding, and the closing mean is the exact mean of
+    the codes the last pass assigned."""
+    S = datagen.tiny(n=6000, d=16, seed=9)
+    shift, scale = oracle.int8_calibrate(S)
+    X = oracle.int8_encode(S, shift, scale)
+    res = oracle.train(X, 48, 2.0, seed=5)
+    lab = res.labels
+    assert np.all(lab >= 0)
+    for j in range(48):
+        m = lab == j
+        if m.any():
+            np.testing.assert_allclose(res.centroids[j], X[m].astype(np.float64).mean(axis=0),
+                                       rtol=0, atol=1e-4)
+    # the search of int8 data uses the rounded centroids: x = 1 against 0.3 and
+    # 1.6 is nearer 1.6, but against their codes 0 and 2 it is a tie, won by 0
+    x1 = np.array([[1]], np.int8)
+    c2 = np.array([[0.3], [1.6]], np.float32)
+    assert oracle.assign(x1, oracle.search_centroids(c2, x1))[0].tolist() == [0]
+    assert oracle.assign(x1, c2)[0].tolist() == [1]
+
+
 def test_fractional_last_pass_labels():
     X = datagen.tiny(n=2000, d=16, seed=3)
     res = oracle.train(X, 16, 1.5, seed=5, batch_size=256)
