@@ -21,8 +21,9 @@
  *   - X, centroids, labels and dists are DEVICE pointers (HIP device memory on
  *     the current device), row-major and contiguous, owned by the caller. The
  *     library never copies data between host and device for the caller.
- *   - X is n x d, either fp32 or bf16 (opts->dtype). Centroids are always
- *     k x d fp32. Labels are int32 in [0, k). Distances are fp32 squared L2.
+ *   - X is n x d, fp32, bf16 or int8 codes (opts->dtype). Centroids are
+ *     always k x d fp32 (for int8 X: in code space). Labels are int32 in
+ *     [0, k). Distances are fp32 squared L2.
  *   - Work is queued on opts->stream (a hipStream_t; NULL = the null stream).
  *     emeans_train synchronises that stream before it returns (its statistics
  *     are host values); emeans_assign and emeans_batch_rows are asynchronous.
@@ -46,7 +47,16 @@ extern "C" {
 
 #define EMEANS_MAX_PASSES 64
 
-enum emeans_dtype { EMEANS_F32 = 0, EMEANS_BF16 = 1 };
+/* EMEANS_I8: X holds int8 codes of the data (README "Data precision", INT8:
+ * the caller encodes each dimension with a shift and a power-of-two scale,
+ * code = clamp(rint((x - shift) * scale), -127, 127), and decodes the
+ * centroids as c / scale + shift). Training runs in code space: running sums
+ * and centroids are fp32 averages of the codes, and the nearest-centroid
+ * search compares each row with the centroids rounded to int8 codes (nearest,
+ * ties to even, clamped to [-127, 127]) exactly, in integers; the distances
+ * are those of the codes. Requires d <= 43919 (the integer score then fits
+ * int32) and no spherical mode. */
+enum emeans_dtype { EMEANS_F32 = 0, EMEANS_BF16 = 1, EMEANS_I8 = 2 };
 
 enum emeans_status {
   EMEANS_OK = 0,
@@ -89,7 +99,7 @@ typedef struct emeans_opts {
                                  nearest-centroid search only, and the distances are
                                  those of the rounded vectors; grouping, running sums
                                  and centroids use the fp32 rows. 0: fp32 X is searched
-                                 in fp32 (exact). Ignored for bf16 X. */
+                                 in fp32 (exact). Ignored for bf16 and int8 X. */
   int32_t spherical;          /* 1: spherical e-means (README "Spherical e-means"):
                                  every centroid is its running average rescaled to
                                  norm 1 before use (a zero centroid stays zero), each
@@ -99,7 +109,8 @@ typedef struct emeans_opts {
                                  2 - 2 x similarity. Vectors are not normalised (nor
                                  checked): pass unit-norm rows for cosine semantics.
                                  emeans_assign: labels by the highest dot product with
-                                 C as given, dists[i] = that similarity. */
+                                 C as given, dists[i] = that similarity. fp32 or
+                                 bf16 X only (EINVAL with int8 X). */
 } emeans_opts;
 
 /* Recipe and statistics of a run (README "Settings and results": recipe, obj,
@@ -158,7 +169,9 @@ int emeans_train(const void* X, int64_t n, int32_t d, int32_t k, double T, uint6
  * dists[i] = that squared distance (fp32, >= 0). For bf16 X the centroids
  * are searched in bf16 (README "Data precision"); so are fp32 X and the
  * centroids with opts->bf16_search (rows and centroids rounded to bf16, the
- * distances those of the rounded vectors; workspace n x d bf16).
+ * distances those of the rounded vectors; workspace n x d bf16). For int8 X
+ * the centroids (code space) are rounded to int8 codes and the labels and
+ * distances are exact for the codes (see EMEANS_I8).
  *   X        device, n x d, opts->dtype      C       device, k x d fp32
  *   labels   device, n int32 output          dists   device, n fp32 output or NULL
  * Errors: EINVAL (n < 0, d < 1, k < 1, n >= 2^31, NULL pointers), EDTYPE,

@@ -23,7 +23,7 @@ LIB_PATH = os.path.join(_PKG, "_lib", "libemeans.so")
 HEADER = os.path.join(os.path.dirname(_PKG), "include", "emeans.h")
 
 MAX_PASSES = 64
-F32, BF16 = 0, 1
+F32, BF16, I8 = 0, 1, 2
 LAWS = {"auto": 0, "throughput": 1, "quality": 2}
 STATUS = {0: "OK", -1: "EINVAL", -2: "EDTYPE", -3: "ENOMEM", -4: "EHIP", -5: "ENOTDEVICE"}
 
@@ -154,7 +154,9 @@ def _dtype_of(X) -> int:
         return F32
     if X.dtype == torch.bfloat16:
         return BF16
-    raise EmeansError(f"EDTYPE: {X.dtype} not supported (float32 or bfloat16)")
+    if X.dtype == torch.int8:
+        return I8
+    raise EmeansError(f"EDTYPE: {X.dtype} not supported (float32, bfloat16 or int8)")
 
 
 def _stream_ptr(X, stream):
@@ -286,10 +288,11 @@ class Stream:
         self.k, self.d = start.shape
         self.n = int(n)
         self.device = start.device
-        code = F32 if dtype in (None, torch.float32) else BF16 if dtype == torch.bfloat16 else -1
+        codes = {None: F32, torch.float32: F32, torch.bfloat16: BF16, torch.int8: I8}
+        code = codes.get(dtype, -1)
         if code < 0:
-            raise EmeansError(f"EDTYPE: {dtype} not supported (float32 or bfloat16)")
-        self.dtype = torch.float32 if code == F32 else torch.bfloat16
+            raise EmeansError(f"EDTYPE: {dtype} not supported (float32, bfloat16 or int8)")
+        self.dtype = {F32: torch.float32, BF16: torch.bfloat16, I8: torch.int8}[code]
         self._stream = stream if stream is not None else torch.cuda.current_stream(self.device)
         with torch.cuda.device(self.device):
             o = _opts(code, batch_law, batch_size, alpha0, unused_threshold, finalize, profile,

@@ -174,10 +174,23 @@ struct Arena {
 
 // Checks of a training run that need no device: dtype, then the recipe's
 // arguments and limits.
-int check_run_args(int64_t n, int32_t d, int32_t k, double T, const emeans_opts* opts) {
+constexpr int32_t kMaxDimI8 = 43919;  // int8 search: |2 x.q| + |q|^2 < 2^31
+
+// dtype supported; int8 codes: dimension limit and no spherical mode.
+int check_dtype(int32_t d, const emeans_opts* opts) {
   const int32_t dtype = opts ? opts->dtype : EMEANS_F32;
-  if (dtype != EMEANS_F32 && dtype != EMEANS_BF16)
-    return fail(EMEANS_EDTYPE, "dtype %d not supported (fp32 = 0, bf16 = 1)", dtype);
+  if (dtype != EMEANS_F32 && dtype != EMEANS_BF16 && dtype != EMEANS_I8)
+    return fail(EMEANS_EDTYPE, "dtype %d not supported (fp32 = 0, bf16 = 1, int8 = 2)", dtype);
+  if (dtype == EMEANS_I8 && d > kMaxDimI8)
+    return fail(EMEANS_EINVAL, "int8 data needs d <= %d (got %d)", kMaxDimI8, d);
+  if (dtype == EMEANS_I8 && opts->spherical)
+    return fail(EMEANS_EINVAL, "spherical e-means takes fp32 or bf16 data");
+  return EMEANS_OK;
+}
+
+int check_run_args(int64_t n, int32_t d, int32_t k, double T, const emeans_opts* opts) {
+  int rc0 = check_dtype(d, opts);
+  if (rc0) return rc0;
   Recipe r;
   const int rc = make_recipe(n, d, k, T, opts, r);
   if (rc) return rc;
@@ -214,7 +227,8 @@ struct emeans_model {
   uint64_t seed = 0;
   Recipe r;
   hipStream_t st = nullptr;
-  bool bf16 = false, bsearch = false, sbf = false, sph = false, profile = false;
+  int dt = EMEANS_F32;  // emeans_dtype of X
+  bool bf16 = false, bsearch = false, sbf = false, i8 = false, sph = false, profile = false;
   bool no_finalize = false;
   int32_t* trace = nullptr;
   float* out_counts = nullptr;
@@ -244,6 +258,7 @@ struct emeans_model {
   float *s_acc = nullptr, *S = nullptr, *N = nullptr, *LS = nullptr, *bias = nullptr,
         *n0 = nullptr, *pair_n = nullptr, *wlive = nullptr;
   uint16_t *chat = nullptr, *xb = nullptr;
+  int8_t* cq = nullptr;  // int8 codes of C (int8 data)
   // per pass: [0, P) sum of distances, [P, 3P) sum n^2 and sum n, [3P, 4P) splits (int64)
   double* dstat = nullptr;
   int64_t* counters = nullptr;  // [0] splits, [1] logged, [2] dead count, [3] splits this pass
@@ -274,8 +289,13 @@ struct emeans_model {
     return hipEventRecord(sp.b, st);
   }
 
+  // Centroid table the search reads for rows of type dt.
+  const void* search_table() const {
+    return i8 ? (const void*)cq : bf16 ? (const void*)chat : (const void*)C;
+  }
+
   ReviveArgs revive_args(bool count_only) {
-    return ReviveArgs{k, d, N, S, C, bias, chat, r.thr, seed, (uint64_t)t, flags, dead, n0, rv_u,
+    return ReviveArgs{k, d, N, S, C, bias, chat, cq, r.thr, seed, (uint64_t)t, flags, dead, n0, rv_u,
                       pair_i, pair_n, rv_pos, rv_head, rv_cbase, rv_clen, rv_heads, rv_list,
                       rv_nheads, counters, count_only ? nullptr : dlog,
                       count_only ? 0 : log_cap, count_only ? 1 : 0, sph ? 1 : 0, wlive};
@@ -290,9 +310,9 @@ struct emeans_model {
     k = k_;
     seed = seed_;
     const int32_t dtype = opts ? opts->dtype : EMEANS_F32;
-    if (dtype != EMEANS_F32 && dtype != EMEANS_BF16)
-      return fail(EMEANS_EDTYPE, "dtype %d not supported (fp32 = 0, bf16 = 1)", dtype);
-    int rc = make_recipe(n, d, k, T, opts, r);
+    int rc = check_dtype(d, opts);
+    if (rc) return rc;
+    rc = make_recipe(n, d, k, T, opts, r);
     if (rc) return rc;
     if (n >= ((int64_t)1 << 31)) return fail(EMEANS_EINVAL, "n must be < 2^31");
     if (r.B >= ((int64_t)1 << 24))
@@ -303,9 +323,11 @@ struct emeans_model {
     if (opts && opts->split_log && opts->split_log_cap < 0)
       return fail(EMEANS_EINVAL, "split_log_cap must be >= 0");
     st = static_cast<hipStream_t>(opts ? opts->stream : nullptr);
+    dt = dtype;
     bf16 = dtype == EMEANS_BF16;
-    bsearch = !bf16 && opts && opts->bf16_search;  // fp32 rows searched in bf16 (into xb)
-    sbf = bf16 || bsearch;                         // the search runs in bf16 against chat
+    bsearch = dtype == EMEANS_F32 && opts && opts->bf16_search;  // fp32 rows searched in bf16 (xb)
+    sbf = bf16 || bsearch;  // the search runs in bf16 against chat
+    i8 = dtype == EMEANS_I8;  // the search runs in int8 against cq
     sph = opts && opts->spherical;
     profile = opts && opts->profile;
     no_finalize = opts && opts->no_finalize;
@@ -348,6 +370,7 @@ struct emeans_model {
     ar.want(&LS, kd);
     ar.want(&bias, (size_t)k);
     if (sbf) ar.want(&chat, kd);
+    if (i8) ar.want(&cq, kd);
     if (bsearch) ar.want(&xb, (size_t)B * d);
     ar.want(&dstat, (size_t)4 * EMEANS_MAX_PASSES);
     ar.want(&counters, 4);
@@ -379,10 +402,10 @@ struct emeans_model {
       }));
     HIP_RET(timed(kAssign, [&] {
       if (bsearch)
-        return launch_assign(true, xb, d, nullptr, nb, chat, bias, k, blab, nullptr, pcounts,
-                             dstat + e, sph, st);
-      return launch_assign(bf16, X, d, rws, nb, bf16 ? (const void*)chat : (const void*)C, bias, k,
-                           blab, nullptr, pcounts, dstat + e, sph, st);
+        return launch_assign(EMEANS_BF16, xb, d, nullptr, nb, chat, bias, k, blab, nullptr,
+                             pcounts, dstat + e, sph, st);
+      return launch_assign(dt, X, d, rws, nb, search_table(), bias, k, blab, nullptr, pcounts,
+                           dstat + e, sph, st);
     }));
     if (trace) {
       HIP_RET(hipMemcpyAsync(trace + trace_off, blab, sizeof(int32_t) * nb,
@@ -395,7 +418,7 @@ struct emeans_model {
       return launch_scatter(blab, rws, nb, cursor, order, out_labels, st);
     }));
     HIP_RET(timed(kGroup, [&] {
-      return launch_group(bf16, X, d, order, off, ovf, ovf_n, k, kGroupRows, nb, s_acc, add, st);
+      return launch_group(dt, X, d, order, off, ovf, ovf_n, k, kGroupRows, nb, s_acc, add, st);
     }));
     rows_step += nb;
     rows_pass += nb;
@@ -409,7 +432,7 @@ struct emeans_model {
     const float b = 1.0f - a;
     const bool last = e == r.npass - 1;
     HIP_RET(timed(kUpdate, [&] {
-      return launch_ema(k, d, a, b, counts, s_acc, N, S, C, bias, chat, pass_counts,
+      return launch_ema(k, d, a, b, counts, s_acc, N, S, C, bias, chat, cq, pass_counts,
                         last ? LS : nullptr, sph, st);
     }));
     if (r.thr > 0.0 && (t + 1) % kReviveEvery == 0) {
@@ -526,36 +549,43 @@ int emeans_assign(const void* X, int64_t n, int32_t d, const float* C, int32_t k
                   int32_t* labels, float* dists, const emeans_opts* opts) {
   g_err.clear();
   const int32_t dtype = opts ? opts->dtype : EMEANS_F32;
-  if (dtype != EMEANS_F32 && dtype != EMEANS_BF16)
-    return fail(EMEANS_EDTYPE, "dtype %d not supported (fp32 = 0, bf16 = 1)", dtype);
+  if (dtype != EMEANS_F32 && dtype != EMEANS_BF16 && dtype != EMEANS_I8)
+    return fail(EMEANS_EDTYPE, "dtype %d not supported (fp32 = 0, bf16 = 1, int8 = 2)", dtype);
   if (n < 0 || n >= ((int64_t)1 << 31)) return fail(EMEANS_EINVAL, "n out of range (%lld)", (long long)n);
   if (d < 1) return fail(EMEANS_EINVAL, "d must be >= 1");
   if (k < 1) return fail(EMEANS_EINVAL, "k must be >= 1");
   if (!X || !C || !labels) return fail(EMEANS_EINVAL, "X, C and labels must not be NULL");
-  if (n == 0) return EMEANS_OK;
   int rc;
+  if ((rc = check_dtype(d, opts))) return rc;
+  if (n == 0) return EMEANS_OK;
   if ((rc = check_device(X, "X")) || (rc = check_device(C, "C")) ||
       (rc = check_device(labels, "labels")) || (dists && (rc = check_device(dists, "dists"))))
     return rc;
   hipStream_t st = static_cast<hipStream_t>(opts ? opts->stream : nullptr);
   const bool bf16 = dtype == EMEANS_BF16;
-  const bool bsearch = !bf16 && opts && opts->bf16_search;  // fp32 rows searched in bf16
+  const bool i8 = dtype == EMEANS_I8;
+  const bool bsearch = dtype == EMEANS_F32 && opts && opts->bf16_search;  // fp32 rows in bf16
   const bool sph = opts && opts->spherical;  // highest dot product, similarity out
   void* base = nullptr;
   float* bias = nullptr;
   uint16_t* chat = nullptr;
   uint16_t* xb = nullptr;
+  int8_t* cq = nullptr;
   Arena ar;
   ar.want(&bias, (size_t)k);
   if (bf16 || bsearch) ar.want(&chat, (size_t)k * d);
+  if (i8) ar.want(&cq, (size_t)k * d);
   if (bsearch) ar.want(&xb, (size_t)n * d);
   rc = EMEANS_OK;
   HIP_TRY(ar.alloc(&base, st));
-  HIP_TRY(launch_prep(C, k, d, bias, chat, sph, st));
+  HIP_TRY(launch_prep(C, k, d, bias, chat, cq, sph, st));
   if (bsearch) HIP_TRY(launch_cast_rows(static_cast<const float*>(X), d, nullptr, (int)n, xb, st));
-  HIP_TRY(launch_assign(bf16 || bsearch, bsearch ? (const void*)xb : X, d, nullptr, (int)n,
-                        (bf16 || bsearch) ? (const void*)chat : (const void*)C, bias, k, labels,
-                        dists, nullptr, nullptr, sph, st));
+  {
+    const int sdt = bsearch ? EMEANS_BF16 : dtype;
+    const void* cs = i8 ? (const void*)cq : (bf16 || bsearch) ? (const void*)chat : (const void*)C;
+    HIP_TRY(launch_assign(sdt, bsearch ? (const void*)xb : X, d, nullptr, (int)n, cs, bias, k,
+                          labels, dists, nullptr, nullptr, sph, st));
+  }
 done:
   if (base) {
     const hipError_t e = hipFreeAsync(base, st);
@@ -587,9 +617,9 @@ int emeans_train(const void* X, int64_t n, int32_t d, int32_t k, double T, uint6
   if (labels) HIP_RET(hipMemsetAsync(labels, 0xFF, sizeof(int32_t) * (size_t)n, st));
 
   // starting centroids: k distinct rows (first k entries of the init permutation)
-  HIP_RET(launch_init_centroids(m.bf16, X, d, make_perm_key((uint64_t)n, seed, kStreamInit, 0), k,
+  HIP_RET(launch_init_centroids(m.dt, X, d, make_perm_key((uint64_t)n, seed, kStreamInit, 0), k,
                                 m.C, m.sph, st));
-  HIP_RET(launch_prep(m.C, k, d, m.bias, m.chat, m.sph, st));
+  HIP_RET(launch_prep(m.C, k, d, m.bias, m.chat, m.cq, m.sph, st));
 
   for (int e = 0; e < r.npass && m.t < run_steps; ++e) {
     const bool last = e == r.npass - 1;
@@ -632,7 +662,7 @@ int emeans_begin(int64_t n, int32_t d, int32_t k, double T, uint64_t seed, const
     if (e3 != hipSuccess) rc = fail(EMEANS_EHIP, "normalise: %s", hipGetErrorString(e3));
   }
   if (rc == EMEANS_OK) {
-    const hipError_t e2 = launch_prep(m->C, k, d, m->bias, m->chat, m->sph, m->st);
+    const hipError_t e2 = launch_prep(m->C, k, d, m->bias, m->chat, m->cq, m->sph, m->st);
     if (e2 != hipSuccess) rc = fail(EMEANS_EHIP, "centroid prep: %s", hipGetErrorString(e2));
   }
   if (rc != EMEANS_OK) {

@@ -4,7 +4,8 @@
 // in panels of 256. For each (panel, d-chunk) the point rows and centroid
 // rows are staged through LDS (double buffered, one 128-byte slab per row);
 // each wave computes a 64 x 64 block of scores with 16x16 MFMA tiles:
-//   fp32 X: v_mfma_f32_16x16x4_f32     bf16 X: v_mfma_f32_16x16x32_bf16.
+//   fp32 X: v_mfma_f32_16x16x4_f32     bf16 X: v_mfma_f32_16x16x32_bf16
+//   int8 X: v_mfma_i32_16x16x64_i8.
 // Centroids sit on the MFMA M dimension and points on N, so after a tile each
 // lane holds four centroid scores of a single point; the running best score
 // and its index stay in registers across all panels and are merged across the
@@ -18,6 +19,12 @@
 // Ties: each lane visits its centroids in increasing index order and keeps
 // the first strict maximum; merges prefer the lower index on equal scores, so
 // the lowest index wins overall, matching argmin over the squared distance.
+//
+// int8 codes against int8 centroid codes q: the products accumulate exactly
+// in int32 from zero and the score is the integer 2 x.q - |q|^2 (the bias
+// array then holds -|q|^2 as int32), so labels and distances are exact.
+// With d <= 43919 no intermediate leaves the int32 range:
+// |2 x.q| + |q|^2 <= d (2 * 128 * 127 + 127^2) < 2^31.
 #include "kernels.hpp"
 
 namespace emk {
@@ -27,6 +34,28 @@ namespace {
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef int32_t i32x4 __attribute__((ext_vector_type(4)));
+
+// Per data type (0 fp32, 1 bf16, 2 int8): element bytes, the accumulator
+// tile and the score type.
+template <int DT>
+struct Fmt {
+  static constexpr int ES = 4;
+  using Acc = f32x4;
+  using Sc = float;
+};
+template <>
+struct Fmt<1> {
+  static constexpr int ES = 2;
+  using Acc = f32x4;
+  using Sc = float;
+};
+template <>
+struct Fmt<2> {
+  static constexpr int ES = 1;
+  using Acc = i32x4;
+  using Sc = int;
+};
 
 constexpr int kWM = 4;               // waves along the centroid (M) dimension
 constexpr int kWN = 2;               // waves along the point (N) dimension
@@ -40,44 +69,50 @@ constexpr int kRowsPerPass = kThreads / kChunks;
 constexpr int kXL = kTP / kRowsPerPass;     // point-row slabs per thread
 constexpr int kCL = kTC / kRowsPerPass;     // centroid-row slabs per thread
 
-template <bool BF16, bool VEC>
+template <int DT, bool VEC>
 __device__ __forceinline__ u32x4 load_slab16(const unsigned char* row, int col, int d) {
   // 16 bytes of a row starting at element `col`. With whole 16-byte chunks
   // per row (VEC) the address is clamped into the row and the caller zeroes
   // chunks past the end when it stores them, so the load stays in flight
   // across the MFMA work; otherwise elements past the end read as zero.
-  constexpr int ES = BF16 ? 2 : 4;
+  constexpr int ES = Fmt<DT>::ES;
   constexpr int EPV = 16 / ES;
   if constexpr (VEC) {
     return *reinterpret_cast<const u32x4*>(row + (size_t)(col < d ? col : d - EPV) * ES);
   } else {
-    if constexpr (BF16) {
-      const uint16_t* p = reinterpret_cast<const uint16_t*>(row);
-      uint32_t w[4] = {0u, 0u, 0u, 0u};
+    uint32_t w[4] = {0u, 0u, 0u, 0u};
 #pragma unroll
-      for (int e = 0; e < EPV; ++e) {
-        const int c = col + e;
-        const uint32_t h = c < d ? (uint32_t)p[c] : 0u;
-        w[e >> 1] |= h << (16 * (e & 1));
+    for (int e = 0; e < EPV; ++e) {
+      const int c = col + e;
+      uint32_t v = 0u;
+      if (c < d) {
+        if constexpr (DT == 2)
+          v = (uint32_t)row[c];
+        else if constexpr (DT == 1)
+          v = (uint32_t)reinterpret_cast<const uint16_t*>(row)[c];
+        else
+          v = reinterpret_cast<const uint32_t*>(row)[c];
       }
-      return u32x4{w[0], w[1], w[2], w[3]};
-    } else {
-      const float* p = reinterpret_cast<const float*>(row);
-      float f[4];
-#pragma unroll
-      for (int e = 0; e < 4; ++e) f[e] = (col + e) < d ? p[col + e] : 0.0f;
-      return u32x4{__float_as_uint(f[0]), __float_as_uint(f[1]), __float_as_uint(f[2]),
-                   __float_as_uint(f[3])};
+      constexpr int PW = 4 / ES;  // elements per 32-bit word
+      w[e / PW] |= v << (8 * ES * (e % PW));
     }
+    return u32x4{w[0], w[1], w[2], w[3]};
   }
 }
 
-template <bool BF16>
-__device__ __forceinline__ float sumsq16(u32x4 w) {
-  float s = 0.0f;
+// Sum of squares of the elements in a 16-byte chunk (exact integer for int8).
+template <int DT>
+__device__ __forceinline__ typename Fmt<DT>::Sc sumsq16(u32x4 w) {
+  typename Fmt<DT>::Sc s = 0;
 #pragma unroll
   for (int e = 0; e < 4; ++e) {
-    if constexpr (BF16) {
+    if constexpr (DT == 2) {
+#pragma unroll
+      for (int b = 0; b < 4; ++b) {
+        const int v = (int)(int8_t)(w[e] >> (8 * b));
+        s += v * v;
+      }
+    } else if constexpr (DT == 1) {
       const float lo = __uint_as_float(w[e] << 16);
       const float hi = __uint_as_float(w[e] & 0xFFFF0000u);
       s += lo * lo + hi * hi;
@@ -89,20 +124,186 @@ __device__ __forceinline__ float sumsq16(u32x4 w) {
   return s;
 }
 
-template <bool BF16, bool VEC>
+// One 64-byte slice of K for a 64 x 64 score block: a[mb] holds 16 centroid
+// rows, b[nb] 16 point rows, 16 bytes per lane (lane / 16 selects the 16-byte
+// piece of the slice).
+template <int DT>
+__device__ __forceinline__ void mfma_slice(typename Fmt<DT>::Acc (&acc)[4][4], const u32x4 (&a)[4],
+                                           const u32x4 (&b)[4]) {
+  if constexpr (DT == 2) {
+#pragma unroll
+    for (int mb = 0; mb < 4; ++mb)
+#pragma unroll
+      for (int nb = 0; nb < 4; ++nb)
+        acc[mb][nb] = __builtin_amdgcn_mfma_i32_16x16x64_i8(__builtin_bit_cast(i32x4, a[mb]),
+                                                            __builtin_bit_cast(i32x4, b[nb]),
+                                                            acc[mb][nb], 0, 0, 0);
+  } else if constexpr (DT == 1) {
+#pragma unroll
+    for (int mb = 0; mb < 4; ++mb)
+#pragma unroll
+      for (int nb = 0; nb < 4; ++nb)
+        acc[mb][nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+            __builtin_bit_cast(bf16x8, a[mb]), __builtin_bit_cast(bf16x8, b[nb]), acc[mb][nb], 0,
+            0, 0);
+  } else {
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+#pragma unroll
+      for (int mb = 0; mb < 4; ++mb)
+#pragma unroll
+        for (int nb = 0; nb < 4; ++nb)
+          acc[mb][nb] = __builtin_amdgcn_mfma_f32_16x16x4f32(
+              __uint_as_float(a[mb][q]), __uint_as_float(b[nb][q]), acc[mb][nb], 0, 0, 0);
+  }
+}
+
+// Bias tile of a panel: lane-group g holds centroids 4 g .. 4 g + 3 of each
+// 16-row block. fp32 / bf16: -|c|^2/2, -inf past k (the accumulator's initial
+// value). int8: -|q|^2 (added at the fold; centroids past k are skipped).
+template <int DT>
+__device__ __forceinline__ void panel_bias(const float* bias, int k, int j0, int lane,
+                                           typename Fmt<DT>::Acc (&bt)[4]) {
+#pragma unroll
+  for (int mb = 0; mb < 4; ++mb)
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+      const int j = j0 + mb * 16 + 4 * (lane >> 4) + v;
+      if constexpr (DT == 2)
+        bt[mb][v] = j < k ? reinterpret_cast<const int32_t*>(bias)[j] : 0;
+      else
+        bt[mb][v] = j < k ? bias[j] : -__builtin_inff();
+    }
+}
+
+// Folds a finished panel into the running best of each point column
+// (centroids in increasing order; the first strict maximum is kept).
+template <int DT>
+__device__ __forceinline__ void fold_panel(const typename Fmt<DT>::Acc (&acc)[4][4],
+                                           const typename Fmt<DT>::Acc (&bt)[4], int j0, int k,
+                                           int lane, typename Fmt<DT>::Sc (&best)[4],
+                                           int (&bidx)[4]) {
+#pragma unroll
+  for (int nb = 0; nb < 4; ++nb)
+#pragma unroll
+    for (int mb = 0; mb < 4; ++mb)
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        const int j = j0 + mb * 16 + 4 * (lane >> 4) + v;
+        if constexpr (DT == 2) {
+          const int sc = 2 * acc[mb][nb][v] + bt[mb][v];
+          if (j < k && sc > best[nb]) {
+            best[nb] = sc;
+            bidx[nb] = j;
+          }
+        } else {
+          const float sc = acc[mb][nb][v];
+          if (sc > best[nb]) {
+            best[nb] = sc;
+            bidx[nb] = j;
+          }
+        }
+      }
+}
+
+template <int DT>
+__device__ __forceinline__ void init_tile(typename Fmt<DT>::Acc (&acc)[4][4],
+                                          const typename Fmt<DT>::Acc (&bt)[4]) {
+#pragma unroll
+  for (int mb = 0; mb < 4; ++mb)
+#pragma unroll
+    for (int nb = 0; nb < 4; ++nb) {
+      if constexpr (DT == 2)
+        acc[mb][nb] = i32x4{0, 0, 0, 0};
+      else
+        acc[mb][nb] = bt[mb];
+    }
+}
+
+// Cross-wave merge and the per-point outputs, shared by both kernels: the
+// four lane groups of a point, then the kWM centroid waves through LDS.
+// xn = |x|^2; dist = |x|^2 - score (int8: the exact integer |x - q|^2), or
+// for fp32 / bf16 |x|^2 - 2 score, clamped at 0; with sim the score is the
+// similarity, reported as is, and the error adds 2 - 2 x similarity.
+template <int DT>
+__device__ __forceinline__ double finish_points(typename Fmt<DT>::Sc (&best)[4], int (&bidx)[4],
+                                                typename Fmt<DT>::Sc (*m_s)[kTP],
+                                                int (*m_j)[kTP],
+                                                const typename Fmt<DT>::Sc* xn_s, int tile0,
+                                                int nrows, int k, int32_t* labels, float* dists,
+                                                int32_t* counts, int sim) {
+  using Sc = typename Fmt<DT>::Sc;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wm = wave >> 1, wn = wave & 1;
+#pragma unroll
+  for (int nb = 0; nb < 4; ++nb) {
+    Sc sc = best[nb];
+    int j = bidx[nb];
+#pragma unroll
+    for (int off = 16; off <= 32; off <<= 1) {
+      const Sc os = __shfl_xor(sc, off, 64);
+      const int oj = __shfl_xor(j, off, 64);
+      if (os > sc || (os == sc && (unsigned)oj < (unsigned)j)) {
+        sc = os;
+        j = oj;
+      }
+    }
+    if ((lane >> 4) == 0) {
+      m_s[wm][wn * 64 + nb * 16 + lane] = sc;
+      m_j[wm][wn * 64 + nb * 16 + lane] = j;
+    }
+  }
+  __syncthreads();
+
+  double dsum = 0.0;
+  if (tid < kTP) {
+    const int p = tid;
+    Sc sc = m_s[0][p];
+    int j = m_j[0][p];
+#pragma unroll
+    for (int w = 1; w < kWM; ++w) {
+      const Sc s1 = m_s[w][p];
+      const int j1 = m_j[w][p];
+      if (s1 > sc || (s1 == sc && (unsigned)j1 < (unsigned)j)) {
+        sc = s1;
+        j = j1;
+      }
+    }
+    if (j < 0 || j >= k) j = 0;  // only reachable with non-finite data
+    const int slot = tile0 + p;
+    if (slot < nrows) {
+      labels[slot] = j;
+      if (counts) atomicAdd(&counts[j], 1);
+      if constexpr (DT == 2) {
+        const long long dist = (long long)xn_s[p] - (long long)sc;
+        if (dists) dists[slot] = (float)dist;
+        dsum = (double)dist;
+      } else {
+        const float dist = fmaxf(xn_s[p] - 2.0f * sc, 0.0f);
+        if (dists) dists[slot] = sim ? sc : dist;
+        dsum = sim ? 2.0 - 2.0 * (double)sc : (double)dist;
+      }
+    }
+  }
+  return dsum;
+}
+
+template <int DT>
 __global__ __launch_bounds__(kThreads, 1) void assign_kernel(
     const unsigned char* __restrict__ X, int d, const uint32_t* __restrict__ rows, int nrows,
     const unsigned char* __restrict__ Cs, const float* __restrict__ bias, int k,
     int32_t* __restrict__ labels, float* __restrict__ dists, int32_t* __restrict__ counts,
     double* __restrict__ obj, int sim) {
-  constexpr int ES = BF16 ? 2 : 4;
+  using Acc = typename Fmt<DT>::Acc;
+  using Sc = typename Fmt<DT>::Sc;
+  constexpr int ES = Fmt<DT>::ES;
   constexpr int EPV = 16 / ES;          // elements per 16-byte chunk
   constexpr int EPS = kSlab / ES;       // elements per stage
   __shared__ __attribute__((aligned(16))) unsigned char lx[2][kTP * kStride];
   __shared__ __attribute__((aligned(16))) unsigned char lc[2][kTC * kStride];
-  __shared__ float m_s[kWM][kTP];
+  __shared__ Sc m_s[kWM][kTP];
   __shared__ int m_j[kWM][kTP];
-  __shared__ float xn_s[kTP];
+  __shared__ Sc xn_s[kTP];
   __shared__ double red[kThreads / 64];
 
   const int tid = threadIdx.x;
@@ -134,11 +335,11 @@ __global__ __launch_bounds__(kThreads, 1) void assign_kernel(
     const int col = s * EPS + ch * EPV;
     colin = col < d;
 #pragma unroll
-    for (int i = 0; i < kXL; ++i) rx[i] = load_slab16<BF16, VEC>(xrow[i], col, d);
+    for (int i = 0; i < kXL; ++i) rx[i] = load_slab16<DT, false>(xrow[i], col, d);
 #pragma unroll
     for (int i = 0; i < kCL; ++i) {
       const int j = min(panel * kTC + rb + kRowsPerPass * i, k - 1);
-      rc[i] = load_slab16<BF16, VEC>(Cs + (size_t)j * rowbytes, col, d);
+      rc[i] = load_slab16<DT, false>(Cs + (size_t)j * rowbytes, col, d);
     }
   };
   auto sstore = [&](int buf) {
@@ -153,40 +354,28 @@ __global__ __launch_bounds__(kThreads, 1) void assign_kernel(
           colin ? rc[i] : z;
   };
 
-  f32x4 acc[4][4];
-  auto init_acc = [&](int panel) {
-#pragma unroll
-    for (int mb = 0; mb < 4; ++mb) {
-      f32x4 b;
-#pragma unroll
-      for (int v = 0; v < 4; ++v) {
-        const int j = panel * kTC + wm * 64 + mb * 16 + 4 * (lane >> 4) + v;
-        b[v] = j < k ? bias[j] : -__builtin_inff();
-      }
-#pragma unroll
-      for (int nb = 0; nb < 4; ++nb) acc[mb][nb] = b;
-    }
-  };
-
-  float best[4];
+  Acc acc[4][4];
+  Acc bt[4];
+  Sc best[4];
   int bidx[4];
 #pragma unroll
   for (int nb = 0; nb < 4; ++nb) {
-    best[nb] = -__builtin_inff();
+    best[nb] = DT == 2 ? (Sc)INT32_MIN : (Sc)-__builtin_inff();
     bidx[nb] = -1;
   }
-  float xpart[kXL];  // |x|^2 partials of this thread's point-row slabs
+  Sc xpart[kXL];  // |x|^2 partials of this thread's point-row slabs
 #pragma unroll
-  for (int i = 0; i < kXL; ++i) xpart[i] = 0.0f;
+  for (int i = 0; i < kXL; ++i) xpart[i] = 0;
 
   // Two LDS stages: the global loads of the next stage are in flight while
   // the MFMAs consume the current one.
   gload(0, 0);
 #pragma unroll
-  for (int i = 0; i < kXL; ++i) xpart[i] += colin ? sumsq16<BF16>(rx[i]) : 0.0f;
+  for (int i = 0; i < kXL; ++i) xpart[i] += colin ? sumsq16<DT>(rx[i]) : (Sc)0;
   sstore(0);
   __syncthreads();
-  init_acc(0);
+  panel_bias<DT>(bias, k, wm * 64, lane, bt);
+  init_tile<DT>(acc, bt);
 
   int panel = 0, s = 0, buf = 0;
   while (true) {
@@ -209,46 +398,21 @@ __global__ __launch_bounds__(kThreads, 1) void assign_kernel(
       for (int nb = 0; nb < 4; ++nb)
         b[nb] = *reinterpret_cast<const u32x4*>(
             &lx[buf][(wn * 64 + nb * 16 + (lane & 15)) * kStride + kk * 64 + (lane >> 4) * 16]);
-      if constexpr (BF16) {
-#pragma unroll
-        for (int mb = 0; mb < 4; ++mb)
-#pragma unroll
-          for (int nb = 0; nb < 4; ++nb)
-            acc[mb][nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-                __builtin_bit_cast(bf16x8, a[mb]), __builtin_bit_cast(bf16x8, b[nb]),
-                acc[mb][nb], 0, 0, 0);
-      } else {
-#pragma unroll
-        for (int q = 0; q < 4; ++q)
-#pragma unroll
-          for (int mb = 0; mb < 4; ++mb)
-#pragma unroll
-            for (int nb = 0; nb < 4; ++nb)
-              acc[mb][nb] = __builtin_amdgcn_mfma_f32_16x16x4f32(
-                  __uint_as_float(a[mb][q]), __uint_as_float(b[nb][q]), acc[mb][nb], 0, 0, 0);
-      }
+      mfma_slice<DT>(acc, a, b);
     }
 
     if (ns == 0) {
-      // panel complete: fold it into the running best (centroids in increasing order)
-#pragma unroll
-      for (int nb = 0; nb < 4; ++nb)
-#pragma unroll
-        for (int mb = 0; mb < 4; ++mb)
-#pragma unroll
-          for (int v = 0; v < 4; ++v) {
-            const float sc = acc[mb][nb][v];
-            if (sc > best[nb]) {
-              best[nb] = sc;
-              bidx[nb] = panel * kTC + wm * 64 + mb * 16 + 4 * (lane >> 4) + v;
-            }
-          }
-      if (more) init_acc(np);
+      // panel complete: fold it into the running best
+      fold_panel<DT>(acc, bt, panel * kTC + wm * 64, k, lane, best, bidx);
+      if (more) {
+        panel_bias<DT>(bias, k, np * kTC + wm * 64, lane, bt);
+        init_tile<DT>(acc, bt);
+      }
     }
     if (!more) break;
     if (np == 0) {
 #pragma unroll
-      for (int i = 0; i < kXL; ++i) xpart[i] += colin ? sumsq16<BF16>(rx[i]) : 0.0f;
+      for (int i = 0; i < kXL; ++i) xpart[i] += colin ? sumsq16<DT>(rx[i]) : (Sc)0;
     }
     sstore(buf ^ 1);
     __syncthreads();
@@ -260,58 +424,13 @@ __global__ __launch_bounds__(kThreads, 1) void assign_kernel(
   // |x|^2: fold the column-chunk threads of each point row (adjacent lanes)
 #pragma unroll
   for (int i = 0; i < kXL; ++i) {
-    float v = xpart[i];
+    Sc v = xpart[i];
 #pragma unroll
     for (int o = 1; o < kChunks; o <<= 1) v += __shfl_xor(v, o, 64);
     if (ch == 0) xn_s[rb + kRowsPerPass * i] = v;
   }
-  // merge the four lane groups that share a point
-#pragma unroll
-  for (int nb = 0; nb < 4; ++nb) {
-    float sc = best[nb];
-    int j = bidx[nb];
-#pragma unroll
-    for (int off = 16; off <= 32; off <<= 1) {
-      const float os = __shfl_xor(sc, off, 64);
-      const int oj = __shfl_xor(j, off, 64);
-      if (os > sc || (os == sc && (unsigned)oj < (unsigned)j)) {
-        sc = os;
-        j = oj;
-      }
-    }
-    if ((lane >> 4) == 0) {
-      m_s[wm][wn * 64 + nb * 16 + lane] = sc;
-      m_j[wm][wn * 64 + nb * 16 + lane] = j;
-    }
-  }
-  __syncthreads();
-
-  double dsum = 0.0;
-  if (tid < kTP) {
-    const int p = tid;
-    float sc = m_s[0][p];
-    int j = m_j[0][p];
-#pragma unroll
-    for (int w = 1; w < kWM; ++w) {
-      const float s1 = m_s[w][p];
-      const int j1 = m_j[w][p];
-      if (s1 > sc || (s1 == sc && (unsigned)j1 < (unsigned)j)) {
-        sc = s1;
-        j = j1;
-      }
-    }
-    if (j < 0 || j >= k) j = 0;  // only reachable with non-finite data
-    const int slot = tile0 + p;
-    if (slot < nrows) {
-      // sim (spherical e-means): the score is the similarity x.c (zero bias);
-      // the error adds 2 - 2 x similarity
-      const float dist = fmaxf(xn_s[p] - 2.0f * sc, 0.0f);
-      labels[slot] = j;
-      if (dists) dists[slot] = sim ? sc : dist;
-      if (counts) atomicAdd(&counts[j], 1);
-      dsum = sim ? 2.0 - 2.0 * (double)sc : (double)dist;
-    }
-  }
+  double dsum = finish_points<DT>(best, bidx, m_s, m_j, xn_s, tile0, nrows, k, labels, dists,
+                                  counts, sim);
   if (obj) {
     dsum = wave_sum(dsum);
     if (lane == 0) red[wave] = dsum;
@@ -381,19 +500,21 @@ __device__ __forceinline__ void lds_barrier() {
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
 }
 
-template <bool BF16>
+template <int DT>
 __global__ __launch_bounds__(kThreads, 1) void assign_ring_kernel(
     const unsigned char* __restrict__ X, int d, const uint32_t* __restrict__ rows, int nrows,
     const unsigned char* __restrict__ Cs, const float* __restrict__ bias, int k,
     int32_t* __restrict__ labels, float* __restrict__ dists, int32_t* __restrict__ counts,
     double* __restrict__ obj, int sim) {
-  constexpr int ES = BF16 ? 2 : 4;
+  using Acc = typename Fmt<DT>::Acc;
+  using Sc = typename Fmt<DT>::Sc;
+  constexpr int ES = Fmt<DT>::ES;
   constexpr int EPV = 16 / ES;
   constexpr int EPS = kSlab / ES;
   __shared__ __attribute__((aligned(1024))) unsigned char ring[kRing * kStageBytes];
-  __shared__ float m_s[kWM][kTP];
+  __shared__ Sc m_s[kWM][kTP];
   __shared__ int m_j[kWM][kTP];
-  __shared__ float xn_s[kTP];
+  __shared__ Sc xn_s[kTP];
   __shared__ double red[kThreads / 64];
 
   const int tid = threadIdx.x;
@@ -458,40 +579,28 @@ __global__ __launch_bounds__(kThreads, 1) void assign_ring_kernel(
     }
   };
 
-  f32x4 acc[4][4];
-  f32x4 bnext[4];
-  auto load_bias = [&](int panel) {
-#pragma unroll
-    for (int mb = 0; mb < 4; ++mb)
-#pragma unroll
-      for (int v = 0; v < 4; ++v) {
-        const int j = panel * kTC + wm * 64 + mb * 16 + 4 * (lane >> 4) + v;
-        bnext[mb][v] = j < k ? bias[j] : -__builtin_inff();
-      }
-  };
-  auto init_acc = [&]() {
-#pragma unroll
-    for (int mb = 0; mb < 4; ++mb)
-#pragma unroll
-      for (int nb = 0; nb < 4; ++nb) acc[mb][nb] = bnext[mb];
-  };
+  Acc acc[4][4];
+  Acc bcur[4], bnext[4];  // bias tiles of the current and the next panel
+  auto load_bias = [&](int panel) { panel_bias<DT>(bias, k, panel * kTC + wm * 64, lane, bnext); };
 
-  float best[4];
+  Sc best[4];
   int bidx[4];
 #pragma unroll
   for (int nb = 0; nb < 4; ++nb) {
-    best[nb] = -__builtin_inff();
+    best[nb] = DT == 2 ? (Sc)INT32_MIN : (Sc)-__builtin_inff();
     bidx[nb] = -1;
   }
   // |x|^2 partials: thread (rb, ch) covers chunk ch of point rows rb + kRowsPerPass i
   const int ch = tid & 7, rb = tid >> 3;
   constexpr int kXR = kTP / kRowsPerPass;
-  float xpart[kXR];
+  Sc xpart[kXR];
 #pragma unroll
-  for (int i = 0; i < kXR; ++i) xpart[i] = 0.0f;
+  for (int i = 0; i < kXR; ++i) xpart[i] = 0;
 
   load_bias(0);
-  init_acc();
+#pragma unroll
+  for (int mb = 0; mb < 4; ++mb) bcur[mb] = bnext[mb];
+  init_tile<DT>(acc, bcur);
   // Exactly kLoadsPerWave ring loads are issued per stage (the last stages
   // reload the final stage into a buffer that is no longer read), so "the
   // previous stage's loads are done" is always vmcnt <= kLoadsPerWave.
@@ -520,7 +629,7 @@ __global__ __launch_bounds__(kThreads, 1) void assign_ring_kernel(
 #pragma unroll
       for (int i = 0; i < kXR; ++i)
         if (in)
-          xpart[i] += sumsq16<BF16>(
+          xpart[i] += sumsq16<DT>(
               *reinterpret_cast<const u32x4*>(cur + swz(rb + kRowsPerPass * i, ch)));
     }
 #pragma unroll
@@ -534,43 +643,19 @@ __global__ __launch_bounds__(kThreads, 1) void assign_ring_kernel(
 #pragma unroll
       for (int nb = 0; nb < 4; ++nb)
         b[nb] = *reinterpret_cast<const u32x4*>(cur + (wn * 64 + nb * 16 + (lane & 15)) * kSlab + pc);
-      if constexpr (BF16) {
-#pragma unroll
-        for (int mb = 0; mb < 4; ++mb)
-#pragma unroll
-          for (int nb = 0; nb < 4; ++nb)
-            acc[mb][nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-                __builtin_bit_cast(bf16x8, a[mb]), __builtin_bit_cast(bf16x8, b[nb]),
-                acc[mb][nb], 0, 0, 0);
-      } else {
-#pragma unroll
-        for (int q = 0; q < 4; ++q)
-#pragma unroll
-          for (int mb = 0; mb < 4; ++mb)
-#pragma unroll
-            for (int nb = 0; nb < 4; ++nb)
-              acc[mb][nb] = __builtin_amdgcn_mfma_f32_16x16x4f32(
-                  __uint_as_float(a[mb][q]), __uint_as_float(b[nb][q]), acc[mb][nb], 0, 0, 0);
-      }
+      mfma_slice<DT>(acc, a, b);
       // the loads of stage t + 2, issued while the matrix core works on this
       // stage's first half
       if (kk == 0) issue_next();
     }
     if (last_s) {
       // panel complete: fold it into the running best (centroids in increasing order)
+      fold_panel<DT>(acc, bcur, panel * kTC + wm * 64, k, lane, best, bidx);
+      if (more_p) {
 #pragma unroll
-      for (int nb = 0; nb < 4; ++nb)
-#pragma unroll
-        for (int mb = 0; mb < 4; ++mb)
-#pragma unroll
-          for (int v = 0; v < 4; ++v) {
-            const float sc = acc[mb][nb][v];
-            if (sc > best[nb]) {
-              best[nb] = sc;
-              bidx[nb] = panel * kTC + wm * 64 + mb * 16 + 4 * (lane >> 4) + v;
-            }
-          }
-      if (more_p) init_acc();
+        for (int mb = 0; mb < 4; ++mb) bcur[mb] = bnext[mb];
+        init_tile<DT>(acc, bcur);
+      }
     }
     // the next stage's loads have landed in LDS for this wave, then for all
     EMK_WAIT_VMCNT(kLoadsPerWave);
@@ -589,58 +674,13 @@ __global__ __launch_bounds__(kThreads, 1) void assign_ring_kernel(
   // |x|^2: fold the eight chunk threads of each point row (adjacent lanes)
 #pragma unroll
   for (int i = 0; i < kXR; ++i) {
-    float v = xpart[i];
+    Sc v = xpart[i];
 #pragma unroll
     for (int o = 1; o < 8; o <<= 1) v += __shfl_xor(v, o, 64);
     if (ch == 0) xn_s[rb + kRowsPerPass * i] = v;
   }
-  // merge the four lane groups that share a point
-#pragma unroll
-  for (int nb = 0; nb < 4; ++nb) {
-    float sc = best[nb];
-    int j = bidx[nb];
-#pragma unroll
-    for (int off = 16; off <= 32; off <<= 1) {
-      const float os = __shfl_xor(sc, off, 64);
-      const int oj = __shfl_xor(j, off, 64);
-      if (os > sc || (os == sc && (unsigned)oj < (unsigned)j)) {
-        sc = os;
-        j = oj;
-      }
-    }
-    if ((lane >> 4) == 0) {
-      m_s[wm][wn * 64 + nb * 16 + lane] = sc;
-      m_j[wm][wn * 64 + nb * 16 + lane] = j;
-    }
-  }
-  __syncthreads();
-
-  double dsum = 0.0;
-  if (tid < kTP) {
-    const int p = tid;
-    float sc = m_s[0][p];
-    int j = m_j[0][p];
-#pragma unroll
-    for (int w = 1; w < kWM; ++w) {
-      const float s1 = m_s[w][p];
-      const int j1 = m_j[w][p];
-      if (s1 > sc || (s1 == sc && (unsigned)j1 < (unsigned)j)) {
-        sc = s1;
-        j = j1;
-      }
-    }
-    if (j < 0 || j >= k) j = 0;  // only reachable with non-finite data
-    const int slot = tile0 + p;
-    if (slot < nrows) {
-      // sim (spherical e-means): the score is the similarity x.c (zero bias);
-      // the error adds 2 - 2 x similarity
-      const float dist = fmaxf(xn_s[p] - 2.0f * sc, 0.0f);
-      labels[slot] = j;
-      if (dists) dists[slot] = sim ? sc : dist;
-      if (counts) atomicAdd(&counts[j], 1);
-      dsum = sim ? 2.0 - 2.0 * (double)sc : (double)dist;
-    }
-  }
+  double dsum = finish_points<DT>(best, bidx, m_s, m_j, xn_s, tile0, nrows, k, labels, dists,
+                                  counts, sim);
   if (obj) {
     dsum = wave_sum(dsum);
     if (lane == 0) red[wave] = dsum;
@@ -655,32 +695,39 @@ __global__ __launch_bounds__(kThreads, 1) void assign_ring_kernel(
 
 }  // namespace
 
-hipError_t launch_assign(bool bf16, const void* X, int d, const uint32_t* rows, int nrows,
+hipError_t launch_assign(int dt, const void* X, int d, const uint32_t* rows, int nrows,
                          const void* Cs, const float* bias, int k, int32_t* labels, float* dists,
                          int32_t* counts, double* obj, bool sim, hipStream_t st) {
   if (nrows <= 0) return hipSuccess;
-  if (bf16 && assign_bf16_resident_ok(d, X, Cs))
+  if (dt == 1 && assign_bf16_resident_ok(d, X, Cs))
     return launch_assign_bf16_resident(X, d, rows, nrows, Cs, bias, k, labels, dists, counts, obj,
                                        sim, st);
   const dim3 grid((nrows + kTP - 1) / kTP), block(kThreads);
   const auto* x = static_cast<const unsigned char*>(X);
   const auto* c = static_cast<const unsigned char*>(Cs);
   const bool aligned = ((uintptr_t)X % 16 == 0) && ((uintptr_t)Cs % 16 == 0);
-  if (bf16) {
-    if (aligned && d % 8 == 0)
-      assign_ring_kernel<true><<<grid, block, 0, st>>>(x, d, rows, nrows, c, bias, k, labels,
-                                                       dists, counts, obj, sim ? 1 : 0);
+  const int epv = dt == 2 ? 16 : dt == 1 ? 8 : 4;  // elements per 16 bytes
+  const bool ring = aligned && d % epv == 0;
+  const int sm = sim ? 1 : 0;
+#define EMK_ASSIGN(KERNEL) \
+  KERNEL<<<grid, block, 0, st>>>(x, d, rows, nrows, c, bias, k, labels, dists, counts, obj, sm)
+  if (dt == 2) {
+    if (ring)
+      EMK_ASSIGN(assign_ring_kernel<2>);
     else
-      assign_kernel<true, false><<<grid, block, 0, st>>>(x, d, rows, nrows, c, bias, k, labels,
-                                                         dists, counts, obj, sim ? 1 : 0);
+      EMK_ASSIGN(assign_kernel<2>);
+  } else if (dt == 1) {
+    if (ring)
+      EMK_ASSIGN(assign_ring_kernel<1>);
+    else
+      EMK_ASSIGN(assign_kernel<1>);
   } else {
-    if (aligned && d % 4 == 0)
-      assign_ring_kernel<false><<<grid, block, 0, st>>>(x, d, rows, nrows, c, bias, k, labels,
-                                                        dists, counts, obj, sim ? 1 : 0);
+    if (ring)
+      EMK_ASSIGN(assign_ring_kernel<0>);
     else
-      assign_kernel<false, false><<<grid, block, 0, st>>>(x, d, rows, nrows, c, bias, k, labels,
-                                                          dists, counts, obj, sim ? 1 : 0);
+      EMK_ASSIGN(assign_kernel<0>);
   }
+#undef EMK_ASSIGN
   return hipGetLastError();
 }
 

@@ -10,12 +10,14 @@ namespace emk {
 
 // Assign: for batch slot r (row = rows ? rows[r] : r) of X, the nearest
 // centroid by maximal score x.c - |c|^2/2 (equivalent to minimal squared
-// distance). `Cs` is the search-format centroid table (fp32 C, or bf16 C-hat
-// for bf16 X) and `bias` = -|c|^2/2 computed from it. Writes labels[r],
-// dists[r] (optional), counts[label] += 1 (optional) and obj[0] += sum of
-// distances (optional). With `sim` (spherical e-means, bias = 0) dists[r] is
-// the similarity x.c and obj adds 2 - 2 x similarity.
-hipError_t launch_assign(bool bf16, const void* X, int d, const uint32_t* rows, int nrows,
+// distance). dt is the search type of X and `Cs`: 0 fp32 (Cs = C), 1 bf16
+// (Cs = bf16 C-hat), 2 int8 (Cs = int8 codes q). `bias` = -|c|^2/2 computed
+// from Cs as fp32, except for int8, where it holds -|q|^2 as int32 and the
+// score is the exact integer 2 x.q - |q|^2. Writes labels[r], dists[r]
+// (optional), counts[label] += 1 (optional) and obj[0] += sum of distances
+// (optional). With `sim` (spherical e-means, bias = 0; fp32 or bf16 only)
+// dists[r] is the similarity x.c and obj adds 2 - 2 x similarity.
+hipError_t launch_assign(int dt, const void* X, int d, const uint32_t* rows, int nrows,
                          const void* Cs, const float* bias, int k, int32_t* labels, float* dists,
                          int32_t* counts, double* obj, bool sim, hipStream_t st);
 
@@ -33,14 +35,16 @@ hipError_t launch_sample_rows(const PermKey& pk, uint64_t start, int count, uint
 hipError_t launch_sample_rows_i32(const PermKey& pk, uint64_t start, int count, int32_t* rows,
                                   hipStream_t st);
 
-// C[j] = X[pi(j)] as fp32, j < k (rescaled to norm 1 when sph).
-hipError_t launch_init_centroids(bool bf16, const void* X, int d, const PermKey& pk, int k,
+// C[j] = X[pi(j)] as fp32, j < k (rescaled to norm 1 when sph); dt is the
+// data type of X: 0 fp32, 1 bf16, 2 int8.
+hipError_t launch_init_centroids(int dt, const void* X, int d, const PermKey& pk, int k,
                                  float* C, bool sph, hipStream_t st);
 
 // bias[j] = -|c_j|^2 / 2 in the search format (0 when sph); Chat = bf16(C)
-// when non-null.
-hipError_t launch_prep(const float* C, int k, int d, float* bias, uint16_t* Chat, bool sph,
-                       hipStream_t st);
+// when non-null, else Cq = int8 codes q of C (nearest, clamped to +-127) when
+// non-null, and then bias[j] holds the int32 -|q_j|^2 (the assign contract).
+hipError_t launch_prep(const float* C, int k, int d, float* bias, uint16_t* Chat, int8_t* Cq,
+                       bool sph, hipStream_t st);
 
 // out[r] = bf16(X[rows[r]]) for r < nrows (rows NULL: row r), row-major.
 hipError_t launch_cast_rows(const float* X, int d, const uint32_t* rows, int nrows,
@@ -62,16 +66,17 @@ hipError_t launch_scatter(const int32_t* labels, const uint32_t* rows, int nb, i
 // s_acc[j] += sum of X rows of cluster j (work items of at most R rows). A
 // cluster held by one work item is stored, assuming s_acc[j] = 0, unless
 // `add` (a later piece of the same update).
-hipError_t launch_group(bool bf16, const void* X, int d, const uint32_t* order,
+hipError_t launch_group(int dt, const void* X, int d, const uint32_t* order,
                         const int32_t* off, const int2* ovf, const int32_t* ovf_n, int k, int R,
                         int nb, float* s_acc, bool add, hipStream_t st);
 
 // EMA update of every cluster; resets counts and s_acc for the next step;
-// pass_counts += counts; LS += s when LS is non-null; refreshes bias/Chat.
+// pass_counts += counts; LS += s when LS is non-null; refreshes bias and the
+// search format (Chat or Cq, at most one non-null).
 // sph: the centroids are rescaled to norm 1 and the bias is 0.
 hipError_t launch_ema(int k, int d, float a, float b, int32_t* counts, float* s_acc, float* N,
-                      float* S, float* C, float* bias, uint16_t* Chat, int32_t* pass_counts,
-                      float* LS, bool sph, hipStream_t st);
+                      float* S, float* C, float* bias, uint16_t* Chat, int8_t* Cq,
+                      int32_t* pass_counts, float* LS, bool sph, hipStream_t st);
 
 struct ReviveArgs {
   int k, d;
@@ -79,7 +84,8 @@ struct ReviveArgs {
   float* S;
   float* C;
   float* bias;
-  uint16_t* Chat;
+  uint16_t* Chat;     // bf16 search copy of C, or NULL
+  int8_t* Cq;         // int8 search codes of C, or NULL
   double thr;
   uint64_t seed, step;
   // k-sized scratch

@@ -85,6 +85,12 @@ __device__ __forceinline__ void wave_normalize(float* c, int d, int lane) {
   }
 }
 
+// int8 search code of a code-space centroid value: nearest (ties to even),
+// clamped to [-127, 127].
+__device__ __forceinline__ int8_t to_code_i8(float c) {
+  return (int8_t)fminf(fmaxf(__builtin_rintf(c), -127.0f), 127.0f);
+}
+
 // One wave per centroid: C[j] = X[pi(j)] converted to fp32 (rescaled to norm
 // 1 for spherical e-means).
 __global__ __launch_bounds__(256) void init_centroids_kernel(const unsigned char* X, int bf16,
@@ -98,8 +104,10 @@ __global__ __launch_bounds__(256) void init_centroids_kernel(const unsigned char
   row = __shfl(row, 0, 64);
   for (int e = lane; e < d; e += 64) {
     float v;
-    if (bf16)
+    if (bf16 == 1)
       v = bf16_to_f32(reinterpret_cast<const uint16_t*>(X)[row * (uint64_t)d + e]);
+    else if (bf16 == 2)
+      v = (float)reinterpret_cast<const int8_t*>(X)[row * (uint64_t)d + e];
     else
       v = reinterpret_cast<const float*>(X)[row * (uint64_t)d + e];
     C[(size_t)j * d + e] = v;
@@ -107,21 +115,33 @@ __global__ __launch_bounds__(256) void init_centroids_kernel(const unsigned char
   if (sph) wave_normalize(C + (size_t)j * d, d, lane);
 }
 
-// One wave per centroid: bias = -|c|^2/2 in the search format, Chat = bf16(c).
+// One wave per centroid: bias = -|c|^2/2 in the search format, Chat = bf16(c)
+// (bf16 search) or Cq = int8 codes of c (int8 data).
 __global__ __launch_bounds__(256) void prep_kernel(const float* C, int k, int d, float* bias,
-                                                   uint16_t* Chat, int sph) {
+                                                   uint16_t* Chat, int8_t* Cq, int sph) {
   const int j = blockIdx.x * 4 + (threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
   if (j >= k) return;
   float nrm = 0.0f;
+  int nq = 0;  // |q|^2 of the int8 codes, exact
   for (int e = lane; e < d; e += 64) {
     float c = C[(size_t)j * d + e];
     if (Chat) {
       const uint16_t h = f32_to_bf16_rne(c);
       Chat[(size_t)j * d + e] = h;
       c = bf16_to_f32(h);
+    } else if (Cq) {
+      const int8_t q = to_code_i8(c);
+      Cq[(size_t)j * d + e] = q;
+      nq += (int)q * (int)q;
+      continue;
     }
     nrm += c * c;
+  }
+  if (Cq) {
+    nq = wave_sum(nq);
+    if (lane == 0) reinterpret_cast<int32_t*>(bias)[j] = -nq;
+    return;
   }
   nrm = wave_sum(nrm);
   if (lane == 0) bias[j] = sph ? 0.0f : -0.5f * nrm;  // spherical: score = x.c
@@ -247,6 +267,37 @@ __global__ void scatter_kernel(const int32_t* labels, const uint32_t* rows, int 
   if (out_labels) out_labels[row] = j;
 }
 
+// Column unit `col` of a row as fp32 values: 16 bytes of fp32 / bf16 (VEC),
+// 4 bytes of int8 (VEC), or one element.
+template <int DT, bool VEC>
+__device__ __forceinline__ void load_unit_dt(const unsigned char* base, int col, float* v) {
+  if constexpr (VEC && DT == 2) {
+    const uint32_t q = *reinterpret_cast<const uint32_t*>(base + (size_t)col * 4);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) v[e] = (float)(int8_t)(q >> (8 * e));
+  } else if constexpr (VEC) {
+    typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+    const u32x4 q = *reinterpret_cast<const u32x4*>(base + (size_t)col * 16);
+    if constexpr (DT == 1) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        v[2 * e] = __uint_as_float(q[e] << 16);
+        v[2 * e + 1] = __uint_as_float(q[e] & 0xFFFF0000u);
+      }
+    } else {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) v[e] = __uint_as_float(q[e]);
+    }
+  } else {
+    if constexpr (DT == 1)
+      v[0] = bf16_to_f32(reinterpret_cast<const uint16_t*>(base)[col]);
+    else if constexpr (DT == 2)
+      v[0] = (float)reinterpret_cast<const int8_t*>(base)[col];
+    else
+      v[0] = reinterpret_cast<const float*>(base)[col];
+  }
+}
+
 // One workgroup per work item: up to R rows of one cluster (rows taken from
 // the bucketed order). Columns are 16-byte chunks when the rows allow it.
 // Threads are arranged as rpar row groups x ncol columns (blockDim.x =
@@ -254,15 +305,18 @@ __global__ void scatter_kernel(const int32_t* labels, const uint32_t* rows, int 
 // through LDS; a cluster held by a single item is stored, otherwise its
 // partial sums are added atomically. Eight row loads are kept in flight per
 // thread.
-template <bool BF16, bool VEC>
+template <int DT, bool VEC>
 __global__ __launch_bounds__(256) void group_kernel(const unsigned char* __restrict__ X, int d,
                                                     const uint32_t* __restrict__ order,
                                                     const int32_t* __restrict__ off,
                                                     const int2* __restrict__ ovf,
                                                     const int32_t* __restrict__ ovf_n, int k,
                                                     int R, float* __restrict__ s_acc, int add) {
-  constexpr int ES = BF16 ? 2 : 4;
-  constexpr int EPV = VEC ? 16 / ES : 1;  // elements per column unit
+  // element bytes: fp32 4, bf16 2, int8 1; a column unit is 16 bytes (4 for
+  // int8, which keeps the rows in flight within the register budget)
+  constexpr int ES = DT == 0 ? 4 : DT == 1 ? 2 : 1;
+  constexpr int UB = DT == 2 ? 4 : 16;
+  constexpr int EPV = VEC ? UB / ES : 1;  // elements per column unit
   constexpr int U = 8;                    // rows in flight per thread
   __shared__ float red[256 * EPV];
   int j, beg, end;
@@ -276,26 +330,9 @@ __global__ __launch_bounds__(256) void group_kernel(const unsigned char* __restr
 
   auto load_unit = [&](uint32_t row, int col, float* v) {
     const unsigned char* base = X + (size_t)row * rowbytes;
-    if constexpr (VEC) {
-      typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-      const u32x4 q = *reinterpret_cast<const u32x4*>(base + (size_t)col * 16);
-      if constexpr (BF16) {
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          v[2 * e] = __uint_as_float(q[e] << 16);
-          v[2 * e + 1] = __uint_as_float(q[e] & 0xFFFF0000u);
-        }
-      } else {
-#pragma unroll
-        for (int e = 0; e < 4; ++e) v[e] = __uint_as_float(q[e]);
-      }
-    } else {
-      if constexpr (BF16)
-        v[0] = bf16_to_f32(reinterpret_cast<const uint16_t*>(base)[col]);
-      else
-        v[0] = reinterpret_cast<const float*>(base)[col];
-    }
+    load_unit_dt<DT, VEC>(base, col, v);
   };
+
 
   // sum rows beg+first, beg+first+stride, ... < end of column col into acc
   auto sum_rows = [&](int first, int stride, int col, float* acc) {
@@ -369,7 +406,7 @@ __global__ __launch_bounds__(256) void group_kernel(const unsigned char* __restr
 // d <= 512 bf16): one wave per work item, four items per workgroup. The 64
 // lanes form 64 / ncol row groups; row groups are folded with cross-lane
 // shuffles, so a wave needs no LDS and no barrier.
-template <bool BF16, bool VEC>
+template <int DT, bool VEC>
 __global__ __launch_bounds__(256) void group_wave_kernel(const unsigned char* __restrict__ X,
                                                          int d, const uint32_t* __restrict__ order,
                                                          const int32_t* __restrict__ off,
@@ -377,8 +414,11 @@ __global__ __launch_bounds__(256) void group_wave_kernel(const unsigned char* __
                                                          const int32_t* __restrict__ ovf_n,
                                                          int k, int R, float* __restrict__ s_acc,
                                                          int add) {
-  constexpr int ES = BF16 ? 2 : 4;
-  constexpr int EPV = VEC ? 16 / ES : 1;  // elements per column unit
+  // element bytes: fp32 4, bf16 2, int8 1; a column unit is 16 bytes (4 for
+  // int8, which keeps the rows in flight within the register budget)
+  constexpr int ES = DT == 0 ? 4 : DT == 1 ? 2 : 1;
+  constexpr int UB = DT == 2 ? 4 : 16;
+  constexpr int EPV = VEC ? UB / ES : 1;  // elements per column unit
   constexpr int U = 8;                    // rows in flight per lane
   const int lane = threadIdx.x & 63;
   int j, beg, end;
@@ -393,25 +433,7 @@ __global__ __launch_bounds__(256) void group_wave_kernel(const unsigned char* __
 
   auto load_unit = [&](uint32_t row, float* v) {
     const unsigned char* base = X + (size_t)row * rowbytes;
-    if constexpr (VEC) {
-      typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-      const u32x4 q = *reinterpret_cast<const u32x4*>(base + (size_t)col * 16);
-      if constexpr (BF16) {
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          v[2 * e] = __uint_as_float(q[e] << 16);
-          v[2 * e + 1] = __uint_as_float(q[e] & 0xFFFF0000u);
-        }
-      } else {
-#pragma unroll
-        for (int e = 0; e < 4; ++e) v[e] = __uint_as_float(q[e]);
-      }
-    } else {
-      if constexpr (BF16)
-        v[0] = bf16_to_f32(reinterpret_cast<const uint16_t*>(base)[col]);
-      else
-        v[0] = reinterpret_cast<const float*>(base)[col];
-    }
+    load_unit_dt<DT, VEC>(base, col, v);
   };
 
   float acc[EPV];
@@ -463,18 +485,19 @@ __global__ __launch_bounds__(256) void group_wave_kernel(const unsigned char* __
 
 // One wave per cluster: EMA of the running count and sum, centroid S/N,
 // search-format refresh, last-pass accumulation; resets counts and s_acc.
-template <bool BF16S>
+template <int SF>  // search format kept beside C: 0 none, 1 bf16 (Chat), 2 int8 (Cq)
 __global__ __launch_bounds__(256) void ema_kernel(int k, int d, float a, float b,
                                                   int32_t* counts, float* s_acc, float* N,
                                                   float* S, float* C, float* bias,
-                                                  uint16_t* Chat, int32_t* pass_counts,
-                                                  float* LS, int sph) {
+                                                  uint16_t* Chat, int8_t* Cq,
+                                                  int32_t* pass_counts, float* LS, int sph) {
   const int j = blockIdx.x * 4 + (threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
   if (j >= k) return;
   const int n = counts[j];
   const float Nn = __fadd_rn(__fmul_rn(b, N[j]), __fmul_rn(a, (float)n));
   float nrm = 0.0f;
+  int nq = 0;  // |q|^2 of the int8 codes, exact
   const size_t base = (size_t)j * d;
   for (int e = lane; e < d; e += 64) {
     const size_t idx = base + e;
@@ -494,25 +517,34 @@ __global__ __launch_bounds__(256) void ema_kernel(int k, int d, float a, float b
     }
     if (LS && n) LS[idx] += s;
     if (sph) continue;  // rescaled (and rounded to Chat) below, once the norm is known
-    if constexpr (BF16S) {
+    if constexpr (SF == 1) {
       const uint16_t h = f32_to_bf16_rne(c);
       Chat[idx] = h;
       c = bf16_to_f32(h);
+    } else if constexpr (SF == 2) {
+      const int8_t q = to_code_i8(c);
+      Cq[idx] = q;
+      nq += (int)q * (int)q;
+      continue;
     }
     nrm += c * c;
   }
+  if constexpr (SF == 2) nq = wave_sum(nq);
   if (sph) {
     // spherical e-means: the running average rescaled to norm 1 (a centroid
     // without a count keeps its unit-norm value); the score is x.c, bias 0
     if (Nn > 0.0f) wave_normalize(C + base, d, lane);
-    if constexpr (BF16S)
+    if constexpr (SF == 1)
       for (int e = lane; e < d; e += 64) Chat[base + e] = f32_to_bf16_rne(C[base + e]);
   } else {
     nrm = wave_sum(nrm);
   }
   if (lane == 0) {
     N[j] = Nn;
-    bias[j] = sph ? 0.0f : -0.5f * nrm;
+    if constexpr (SF == 2)
+      reinterpret_cast<int32_t*>(bias)[j] = -nq;
+    else
+      bias[j] = sph ? 0.0f : -0.5f * nrm;
     pass_counts[j] += n;
     counts[j] = 0;
   }
@@ -821,6 +853,7 @@ __global__ __launch_bounds__(256) void split_kernel(ReviveArgs A) {
     const int j = A.dead[q];
     const float Nh = A.pair_n[q];
     float ni = 0.0f, nj = 0.0f;
+    int qni = 0, qnj = 0;  // |q|^2 of the int8 codes, exact
     U64x4 wd = {0, 0, 0, 0};
     for (int e = lane, it = 0; e < d; e += 64, ++it) {
       if ((it & 3) == 0)
@@ -842,6 +875,13 @@ __global__ __launch_bounds__(256) void split_kernel(ReviveArgs A) {
         A.Chat[ii] = hi;
         cj = bf16_to_f32(hj);
         ci = bf16_to_f32(hi);
+      } else if (A.Cq) {
+        const int8_t qj = to_code_i8(cj), qi = to_code_i8(ci);
+        A.Cq[jj] = qj;
+        A.Cq[ii] = qi;
+        qni += (int)qi * (int)qi;
+        qnj += (int)qj * (int)qj;
+        continue;
       }
       ni += ci * ci;
       nj += cj * cj;
@@ -858,6 +898,15 @@ __global__ __launch_bounds__(256) void split_kernel(ReviveArgs A) {
       if (lane == 0) {
         A.bias[i] = 0.0f;
         A.bias[j] = 0.0f;
+      }
+      continue;
+    }
+    if (A.Cq) {
+      qni = wave_sum(qni);
+      qnj = wave_sum(qnj);
+      if (lane == 0) {
+        reinterpret_cast<int32_t*>(A.bias)[i] = -qni;
+        reinterpret_cast<int32_t*>(A.bias)[j] = -qnj;
       }
       continue;
     }
@@ -953,16 +1002,16 @@ hipError_t launch_sample_rows_i32(const PermKey& pk, uint64_t start, int count, 
   return hipGetLastError();
 }
 
-hipError_t launch_init_centroids(bool bf16, const void* X, int d, const PermKey& pk, int k,
+hipError_t launch_init_centroids(int dt, const void* X, int d, const PermKey& pk, int k,
                                  float* C, bool sph, hipStream_t st) {
-  init_centroids_kernel<<<(k + 3) / 4, 256, 0, st>>>(static_cast<const unsigned char*>(X),
-                                                     bf16 ? 1 : 0, d, pk, k, C, sph ? 1 : 0);
+  init_centroids_kernel<<<(k + 3) / 4, 256, 0, st>>>(static_cast<const unsigned char*>(X), dt, d,
+                                                     pk, k, C, sph ? 1 : 0);
   return hipGetLastError();
 }
 
-hipError_t launch_prep(const float* C, int k, int d, float* bias, uint16_t* Chat, bool sph,
-                       hipStream_t st) {
-  prep_kernel<<<(k + 3) / 4, 256, 0, st>>>(C, k, d, bias, Chat, sph ? 1 : 0);
+hipError_t launch_prep(const float* C, int k, int d, float* bias, uint16_t* Chat, int8_t* Cq,
+                       bool sph, hipStream_t st) {
+  prep_kernel<<<(k + 3) / 4, 256, 0, st>>>(C, k, d, bias, Chat, Cq, sph ? 1 : 0);
   return hipGetLastError();
 }
 
@@ -979,58 +1028,65 @@ hipError_t launch_scatter(const int32_t* labels, const uint32_t* rows, int nb, i
   return hipGetLastError();
 }
 
-hipError_t launch_group(bool bf16, const void* X, int d, const uint32_t* order,
+template <int DT>
+static hipError_t launch_group_dt(const unsigned char* x, int d, bool vec, int ncol,
+                                  const uint32_t* order, const int32_t* off, const int2* ovf,
+                                  const int32_t* ovf_n, int k, int R, long long items,
+                                  float* s_acc, int add, hipStream_t st) {
+  if (ncol <= 64) {
+    const dim3 wgrid((unsigned)((items + 3) / 4)), wblock(256);
+    if (vec)
+      group_wave_kernel<DT, true>
+          <<<wgrid, wblock, 0, st>>>(x, d, order, off, ovf, ovf_n, k, R, s_acc, add);
+    else
+      group_wave_kernel<DT, false>
+          <<<wgrid, wblock, 0, st>>>(x, d, order, off, ovf, ovf_n, k, R, s_acc, add);
+    return hipGetLastError();
+  }
+  int nt = 256;
+  if (ncol < 256) nt = (((256 / ncol) * ncol + 63) / 64) * 64;
+  const dim3 grid((unsigned)items), block(nt);
+  if (vec)
+    group_kernel<DT, true><<<grid, block, 0, st>>>(x, d, order, off, ovf, ovf_n, k, R, s_acc, add);
+  else
+    group_kernel<DT, false><<<grid, block, 0, st>>>(x, d, order, off, ovf, ovf_n, k, R, s_acc, add);
+  return hipGetLastError();
+}
+
+hipError_t launch_group(int dt, const void* X, int d, const uint32_t* order,
                         const int32_t* off, const int2* ovf, const int32_t* ovf_n, int k, int R,
                         int nb, float* s_acc, bool add, hipStream_t st) {
   if (nb <= 0) return hipSuccess;
   // work items: one per cluster plus at most nb / R overflow items
   const long long items = (long long)k + nb / R;
   const auto* x = static_cast<const unsigned char*>(X);
-  const bool aligned = (uintptr_t)X % 16 == 0;
-  const bool vec = aligned && d % (bf16 ? 8 : 4) == 0;
-  const int ncol = vec ? d / (bf16 ? 8 : 4) : d;
-  if (ncol <= 64) {
-    const dim3 wgrid((unsigned)((items + 3) / 4)), wblock(256);
-    if (bf16) {
-      if (vec)
-        group_wave_kernel<true, true><<<wgrid, wblock, 0, st>>>(x, d, order, off, ovf, ovf_n, k, R, s_acc, add ? 1 : 0);
-      else
-        group_wave_kernel<true, false><<<wgrid, wblock, 0, st>>>(x, d, order, off, ovf, ovf_n, k, R, s_acc, add ? 1 : 0);
-    } else {
-      if (vec)
-        group_wave_kernel<false, true><<<wgrid, wblock, 0, st>>>(x, d, order, off, ovf, ovf_n, k, R, s_acc, add ? 1 : 0);
-      else
-        group_wave_kernel<false, false><<<wgrid, wblock, 0, st>>>(x, d, order, off, ovf, ovf_n, k, R, s_acc, add ? 1 : 0);
-    }
-    return hipGetLastError();
-  }
-  int nt = 256;
-  if (ncol < 256) nt = (((256 / ncol) * ncol + 63) / 64) * 64;
-  const dim3 grid((unsigned)items), block(nt);
-  if (bf16) {
-    if (vec)
-      group_kernel<true, true><<<grid, block, 0, st>>>(x, d, order, off, ovf, ovf_n, k, R, s_acc, add ? 1 : 0);
-    else
-      group_kernel<true, false><<<grid, block, 0, st>>>(x, d, order, off, ovf, ovf_n, k, R, s_acc, add ? 1 : 0);
-  } else {
-    if (vec)
-      group_kernel<false, true><<<grid, block, 0, st>>>(x, d, order, off, ovf, ovf_n, k, R, s_acc, add ? 1 : 0);
-    else
-      group_kernel<false, false><<<grid, block, 0, st>>>(x, d, order, off, ovf, ovf_n, k, R, s_acc, add ? 1 : 0);
-  }
-  return hipGetLastError();
+  // a vector unit is 16 B (4 fp32, 8 bf16) or, for int8, 4 B (4 codes)
+  const int per = dt == 1 ? 8 : 4;
+  const bool aligned = (uintptr_t)X % (dt == 2 ? 4 : 16) == 0;
+  const bool vec = aligned && d % per == 0;
+  const int ncol = vec ? d / per : d;
+  const int a = add ? 1 : 0;
+  if (dt == 1)
+    return launch_group_dt<1>(x, d, vec, ncol, order, off, ovf, ovf_n, k, R, items, s_acc, a, st);
+  if (dt == 2)
+    return launch_group_dt<2>(x, d, vec, ncol, order, off, ovf, ovf_n, k, R, items, s_acc, a, st);
+  return launch_group_dt<0>(x, d, vec, ncol, order, off, ovf, ovf_n, k, R, items, s_acc, a, st);
 }
 
 hipError_t launch_ema(int k, int d, float a, float b, int32_t* counts, float* s_acc, float* N,
-                      float* S, float* C, float* bias, uint16_t* Chat, int32_t* pass_counts,
-                      float* LS, bool sph, hipStream_t st) {
+                      float* S, float* C, float* bias, uint16_t* Chat, int8_t* Cq,
+                      int32_t* pass_counts, float* LS, bool sph, hipStream_t st) {
   const dim3 grid((k + 3) / 4), block(256);
+  const int sp = sph ? 1 : 0;
   if (Chat)
-    ema_kernel<true><<<grid, block, 0, st>>>(k, d, a, b, counts, s_acc, N, S, C, bias, Chat,
-                                             pass_counts, LS, sph ? 1 : 0);
+    ema_kernel<1><<<grid, block, 0, st>>>(k, d, a, b, counts, s_acc, N, S, C, bias, Chat, Cq,
+                                          pass_counts, LS, sp);
+  else if (Cq)
+    ema_kernel<2><<<grid, block, 0, st>>>(k, d, a, b, counts, s_acc, N, S, C, bias, Chat, Cq,
+                                          pass_counts, LS, sp);
   else
-    ema_kernel<false><<<grid, block, 0, st>>>(k, d, a, b, counts, s_acc, N, S, C, bias, Chat,
-                                              pass_counts, LS, sph ? 1 : 0);
+    ema_kernel<0><<<grid, block, 0, st>>>(k, d, a, b, counts, s_acc, N, S, C, bias, Chat, Cq,
+                                          pass_counts, LS, sp);
   return hipGetLastError();
 }
 

@@ -202,8 +202,30 @@ WORKLOADS = {
 }
 
 
+def codes_i8(n: int = 1_000_000, d: int = 768, m: int = 4096, spread: float = 80.0,
+             sigma: float = 12.0, seed: int = 107, split: int = 0) -> np.ndarray:
+    """int8 codes of clustered data (README "Data precision", INT8 input):
+    m centres uniform in [-spread, spread]^d, Zipf(1.1) weights, Gaussian
+    noise of s.d. sigma, rounded to the nearest integer and clamped to
+    [-127, 127] (a few values saturate, as real calibrated codes do)."""
+    r0 = _rng(seed, 0)
+    means = r0.uniform(-spread, spread, size=(m, d)).astype(np.float32)
+    w = zipf_weights(m, 1.1)
+
+    def fill(c, lo, hi, out):
+        r = _rng(seed, 1 + split, c)
+        comp = r.choice(m, size=hi - lo, p=w)
+        g = r.standard_normal((hi - lo, d), dtype=np.float32)
+        out[:] = np.clip(np.rint(means[comp] + np.float32(sigma) * g), -127, 127).astype(np.int8)
+
+    return _chunked(n, d, np.int8, fill)
+
+
 def make(gen: str, n: int, d: int, split: int = 0, **kw) -> np.ndarray:
-    """Host data for a generator name at any (n, d) (fp32, or bf16 bits for 'large')."""
+    """Host data for a generator name at any (n, d) (fp32, bf16 bits for
+    'large', int8 for 'codes')."""
+    if gen == "codes":
+        return codes_i8(n=n, d=d, split=split, **kw)
     if gen == "tiny":
         return tiny(n=n, d=d, split=split, **kw)
     if gen == "embedding":

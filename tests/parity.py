@@ -64,6 +64,21 @@ def bf16_flip_bound(X, rows, C32, labels, rel=1e-5, dot=False):
     return np.sum((2.0 * np.abs(Xf - Cb) + r) * r, axis=1)
 
 
+def int8_flip_bound(X, rows, C32, labels, rel=1e-5):
+    """The int8 analogue of bf16_flip_bound: a running-centroid coordinate
+    within `rel` (relative to the larger of its magnitude and the centroid's
+    RMS coordinate) of a rounding boundary k + 1/2 inside the code range may
+    round to either neighbouring code; each such coordinate can move the
+    distance by at most 2|x - q| + 1."""
+    Xf = oracle.to_f32(X if rows is None else X[rows]).astype(np.float64)
+    c64 = np.ascontiguousarray(C32[labels], dtype=np.float32).astype(np.float64)
+    q = oracle.int8_round(c64).astype(np.float64)
+    rms = np.sqrt(np.mean(c64 * c64, axis=1, keepdims=True))
+    delta = rel * np.maximum(np.abs(c64), rms)
+    near = (np.abs(c64 - (np.floor(c64) + 0.5)) <= delta) & (np.abs(c64) < 127.5 + delta)
+    return np.sum(np.where(near, 2.0 * np.abs(Xf - q) + 1.0, 0.0), axis=1)
+
+
 def check_labels(X, Cs, rows, given, olab, d1, d2, given_dist=None, what="", C32=None,
                  dot=False):
     """Check labels `given` against the oracle's (olab, d1, d2) on the same rows.
@@ -79,7 +94,9 @@ def check_labels(X, Cs, rows, given, olab, d1, d2, given_dist=None, what="", C32
         given_dist = oracle.dist_to(X, Cs, given, rows)
     sc = scale_of(X, Cs, rows, olab)
     band = GAP_TOL * sc
-    if C32 is not None:
+    if C32 is not None and X.dtype == np.int8:
+        band = (band + int8_flip_bound(X, rows, C32, olab) + int8_flip_bound(X, rows, C32, given))
+    elif C32 is not None:
         band = (band + bf16_flip_bound(X, rows, C32, olab, dot=dot)
                 + bf16_flip_bound(X, rows, C32, given, dot=dot))
     ok = given_dist <= d1 + band
@@ -143,7 +160,8 @@ def lockstep(X: np.ndarray, out, k: int, T: float, seed: int, sample: int = 0,
         dec, und, diff = check_labels(Xs, chk["C"], chk["rows"], chk["given"], chk["oracle"],
                                       chk["d1"], chk["d2"], chk["given_dist"],
                                       what=f"step {chk['t']}",
-                                      C32=chk["C32"] if Xs.dtype == np.uint16 else None,
+                                      C32=chk["C32"] if Xs.dtype in (np.uint16, np.int8)
+                                      else None,
                                       dot=chk.get("spherical", False))
         summary["decided"] += dec
         summary["undecided"] += und

@@ -123,6 +123,60 @@ def test_assign_spherical(mm, gen, n, d, k, bf16):
     assert np.all(np.abs(sim - ref) <= 1e-5 * scale)
 
 
+CASES_I8 = [(2000, 768, 300), (1000, 64, 129), (777, 48, 50), (500, 37, 20), (300, 256, 1),
+            (900, 520, 300), (600, 1040, 257), (3000, 128, 1000)]
+
+
+def _int8_centroids(X, k, seed):
+    """Code-space centroids near data rows, a few coordinates outside the code
+    range (clamped to +-127) and at exact half-integers (ties to even)."""
+    C = _centroids(X, k, seed)
+    d = C.shape[1]
+    C[0, : min(d, 4)] = np.array([200.0, -300.0, 126.5, -0.5], np.float32)[: min(d, 4)]
+    if k > 1:
+        C[1, : min(d, 2)] = np.array([2.5, -127.5], np.float32)[: min(d, 2)]
+    return C
+
+
+@pytest.mark.parametrize("n,d,k", CASES_I8)
+def test_assign_int8(mm, n, d, k):
+    """int8 codes: the search is exact in integers, so labels (lowest index on
+    ties) and distances equal the oracle's exactly."""
+    X = datagen.codes_i8(n, d, m=64, seed=23)
+    C = _int8_centroids(X, k, 10)
+    lab, dist = _run(mm, X, C)
+    Cs = oracle.int8_round(C)
+    olab, d1, _ = oracle.assign(X, Cs)
+    assert np.array_equal(lab, olab), f"{int(np.sum(lab != olab))} labels differ"
+    assert np.array_equal(dist, d1.astype(np.float32))
+
+
+def test_assign_int8_misaligned(mm):
+    """Rows that do not start on a 16-byte boundary take the register-staged
+    kernel; the result is the same exact assignment."""
+    import torch
+    n, d, k = 700, 64, 90
+    X = datagen.codes_i8(n, d, m=32, seed=29)
+    C = _int8_centroids(X, k, 12)
+    buf = torch.empty(n * d + 1, dtype=torch.int8, device="cuda")
+    Xd = buf[1:].view(n, d)
+    Xd.copy_(torch.from_numpy(X).cuda())
+    lab, dist = mm.assign(Xd, torch.from_numpy(C).cuda())
+    olab, d1, _ = oracle.assign(X, oracle.int8_round(C))
+    assert np.array_equal(lab.cpu().numpy(), olab)
+    assert np.array_equal(dist.cpu().numpy(), d1.astype(np.float32))
+
+
+def test_assign_int8_rules(mm):
+    import torch
+    X = torch.zeros((10, 43920), dtype=torch.int8, device="cuda")
+    C = torch.zeros((2, 43920), dtype=torch.float32, device="cuda")
+    with pytest.raises(mm.EmeansError, match="EINVAL"):
+        mm.assign(X, C)
+    with pytest.raises(mm.EmeansError, match="EINVAL"):
+        mm.assign(X[:, :16].contiguous(), C[:, :16].contiguous(), spherical=True)
+
+
 @pytest.mark.parametrize("n,d,k", CASES_BF16)
 def test_assign_bf16(mm, n, d, k):
     X = datagen.large_host(n, d=d, m=64, seed=13)

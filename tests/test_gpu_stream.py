@@ -74,6 +74,7 @@ STREAM = [
     ("large-bf16", "large", 40_000, 128, 1024, 2.0, 2, {}),
     ("emb-small-sph", "embedding", 12_000, 768, 256, 2.0, 1, dict(spherical=True)),
     ("ragged-bf16s", "tiny", 5_003, 37, 77, 1.5, 2, dict(batch_size=700, bf16_search=True)),
+    ("codes-pieces", "codes", 12_000, 64, 256, 2.0, 2, {}),
 ]
 
 

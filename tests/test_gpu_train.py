@@ -55,6 +55,10 @@ LOCKSTEP = [
     ("emb-small-sph", "embedding", 12_000, 768, 256, 2.0, dict(spherical=True)),
     ("deep-small-sph", "deep", 30_000, 96, 1024, 3.0, dict(spherical=True)),
     ("large-small-sph", "large", 40_000, 128, 1024, 2.0, dict(spherical=True)),
+    # int8 codes (README "Data precision", INT8): exact integer search
+    ("codes-small", "codes", 12_000, 768, 256, 2.0, {}),
+    ("codes-ragged", "codes", 5_003, 37, 77, 1.5, dict(batch_size=700)),
+    ("codes-deep", "codes", 30_000, 96, 1024, 3.0, {}),
 ]
 
 
