@@ -267,7 +267,9 @@ def int8_calibrate(sample: np.ndarray):
     shift = ((mn + mx) / 2.0).astype(np.float32)
     s64 = shift.astype(np.float64)
     r = float(np.max(np.maximum(mx - s64, s64 - mn))) if x.size else 0.0
-    scale = 1.0 if r <= 0.0 else 2.0 ** math.floor(math.log2(127.0 / r))
+    if r <= 0.0:
+        return shift, 1.0
+    scale = 2.0 ** math.floor(math.log2(127.0 / r))
     while scale * r > 127.0:    # guard the floor of a rounded logarithm
         scale /= 2.0
     while scale * 2.0 * r <= 127.0:

@@ -529,6 +529,16 @@ def test_int8_calibration_and_codes():
     far = np.full((1, 24), 1e6, np.float32)
     assert np.all(oracle.int8_encode(far, shift, scale) == 127)
     assert np.all(oracle.int8_encode(-far, shift, scale) == -127)
+    # a constant sample (radius 0): scale 1, the shift is the value, codes 0
+    const = np.full((7, 3), -2.75, np.float32)
+    cs, cscale = oracle.int8_calibrate(const)
+    assert cscale == 1.0 and np.all(cs == np.float32(-2.75))
+    assert np.all(oracle.int8_encode(const, cs, cscale) == 0)
+    # a radius of exactly 127 / 2^e gives scale 2^e; one ulp more halves it
+    edge = np.array([[-127.0 / 64], [127.0 / 64]], np.float32)
+    assert oracle.int8_calibrate(edge)[1] == 64.0
+    edge[1, 0] = np.nextafter(edge[1, 0], np.float32(1e9))
+    assert oracle.int8_calibrate(edge)[1] == 32.0
     # the search rounds centroids to the nearest code, ties to even, clamped
     C = np.array([[2.5, -0.5, 127.6, -200.0, 3.49, -2.5]], np.float32)
     assert oracle.int8_round(C).tolist() == [[2.0, -0.0, 127.0, -127.0, 3.0, -2.0]]
