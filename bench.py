@@ -23,7 +23,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, HERE)
 
 METRIC = "assign TFLOP/s (% MFMA peak) + s to Lloyd-25 MSE, 1M×768 k=4096"
-MFMA_PEAK_TFLOPS = {"f32": 157.3, "bf16": 2516.6}   # MI355X dense MFMA
+MFMA_PEAK_TFLOPS = {"f32": 157.3, "bf16": 2516.6, "i8": 5033.2}   # MI355X dense MFMA (i8: TOP/s)
 HBM_PEAK_GBS = 8000.0
 
 DESCR = {
@@ -42,7 +42,7 @@ def kernel_source_sha() -> str:
     """Hash of the assign kernels' sources: counter readings are only reused
     while it is unchanged."""
     h = hashlib.sha256()
-    for f in ("assign.hip", "assign_bf16.hip", "common.hpp", "kernels.hpp"):
+    for f in ("assign.hip", "assign_bf16.hip", "common.hpp", "kernels.hpp"):  # assign kernels
         with open(os.path.join(HERE, "mini_means_amd", "csrc", f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()
@@ -53,7 +53,7 @@ def assign_kernel_name(dtype: str, d: int) -> str:
     dtype and width (the dispatch rule of launch_assign in assign.hip)."""
     if dtype == "bf16" and d in (32, 64, 96, 128):
         return "assign_bf16_kernel (points resident in registers, 32x32x16 bf16 MFMA)"
-    if d % (8 if dtype == "bf16" else 4) == 0:
+    if d % {"bf16": 8, "i8": 16}.get(dtype, 4) == 0:
         return "assign_ring_kernel (direct-to-LDS stage ring, 16x16 MFMA)"
     return "assign_kernel (register-staged stages, 16x16 MFMA)"
 
@@ -87,9 +87,27 @@ def batch_sizes(rc: dict) -> list:
     return out
 
 
-def make_data(name: str, W: dict, torch):
+def make_data(name: str, W: dict, torch, int8: bool = False, mm=None):
+    """Training data, held-out data (fp32 or bf16, on the GPU) and the host
+    copy of the training data (None when it is made on the GPU). int8: the
+    training rows as int8 codes, calibrated on the first 65536 rows (the data
+    is an iid draw) and encoded on the GPU; returns the codes, the held-out
+    data, the host codes and (shift, scale, encode seconds)."""
     from mini_means_amd import datagen
     t0 = time.time()
+    if int8:
+        Xf = torch.from_numpy(datagen.make(W["gen"], W["n"], W["d"])).cuda()
+        Xh = torch.from_numpy(datagen.make(W["gen"], W["heldout"], W["d"], split=1)).cuda()
+        torch.cuda.synchronize()
+        t1 = time.perf_counter()
+        shift, scale = mm.int8_calibrate(Xf[:65536])
+        X = mm.int8_encode(Xf, shift, scale)
+        torch.cuda.synchronize()
+        enc_s = time.perf_counter() - t1
+        del Xf
+        log(f"int8 codes {tuple(X.shape)} (scale {scale}) calibrated + encoded in {enc_s:.4f}s; "
+            f"data in {time.time() - t0:.1f}s")
+        return X, Xh, X.cpu().numpy(), (shift, scale, enc_s)
     if W["dtype"] == "bf16":
         X = datagen.large_device(n=W["n"], d=W["d"])
         Xh = datagen.large_device(n=W["heldout"], d=W["d"], split=1)
@@ -100,7 +118,7 @@ def make_data(name: str, W: dict, torch):
         Xh = torch.from_numpy(datagen.make(W["gen"], W["heldout"], W["d"], split=1)).cuda()
     torch.cuda.synchronize()
     log(f"data {tuple(X.shape)} {X.dtype} + held-out {tuple(Xh.shape)} in {time.time() - t0:.1f}s")
-    return X, Xh, Xhost
+    return X, Xh, Xhost, None
 
 
 def heldout_mse(mm, Xh, C, torch) -> float:
@@ -108,9 +126,11 @@ def heldout_mse(mm, Xh, C, torch) -> float:
     return float(dist.double().mean().item())
 
 
-def time_to_target(mm, X, Xh, k, target, seeds, Ts, torch, bf16_search=False) -> dict:
+def time_to_target(mm, X, Xh, k, target, seeds, Ts, torch, bf16_search=False,
+                   decode=None) -> dict:
     """Smallest median wall-clock among pass counts whose finalised held-out MSE
-    reaches the Lloyd-25 held-out MSE (median over training seeds)."""
+    reaches the Lloyd-25 held-out MSE (median over training seeds). decode:
+    code-space centroids to data space (int8 codes), outside the clock."""
     import statistics
     rows = []
     best = None
@@ -122,7 +142,8 @@ def time_to_target(mm, X, Xh, k, target, seeds, Ts, torch, bf16_search=False) ->
             out = mm.train(X, k, T, s, capture_labels=True, bf16_search=bf16_search)
             torch.cuda.synchronize()
             walls.append(time.perf_counter() - t0)
-            mses.append(heldout_mse(mm, Xh, out.centroids, torch))
+            C = out.centroids if decode is None else decode(out.centroids)
+            mses.append(heldout_mse(mm, Xh, C, torch))
         w, m = statistics.median(walls), statistics.median(mses)
         rows.append(dict(T=T, seconds=round(w, 4), heldout_mse=m))
         log(f"T={T}: {w:.3f}s held-out MSE {m:.6f} (target {target:.6f})")
@@ -135,9 +156,11 @@ def time_to_target(mm, X, Xh, k, target, seeds, Ts, torch, bf16_search=False) ->
 
 def cpu_baseline(Xhost, C, k, d, budget_s: float) -> dict:
     """The CPU oracle's assignment (fp64 brute force, OpenMP over rows) on a
-    bounded sample of the workload's rows, in the metric's unit."""
+    bounded sample of the workload's rows, in the metric's unit (int8 codes:
+    against the centroids' codes)."""
     import numpy as np
     import oracle
+    C = oracle.search_centroids(C, Xhost)
     rng = np.random.default_rng(0)
     cores = int(os.environ.get("OMP_NUM_THREADS", "0")) or len(os.sched_getaffinity(0))
     npr = 2048
@@ -174,6 +197,10 @@ def main() -> int:
                          "default); the held-out MSE is still evaluated in fp32")
     ap.add_argument("--spherical", action="store_true",
                     help="spherical e-means (README \"Spherical e-means\"); no time-to-target")
+    ap.add_argument("--int8", action="store_true",
+                    help="README \"Data precision\", INT8: calibrate on the first 65536 rows, "
+                         "encode on the GPU, train on the codes (exact integer search); "
+                         "held-out MSE of the decoded centroids in fp32")
     ap.add_argument("--print-source-sha", action="store_true")
     args = ap.parse_args()
     if args.print_source_sha:
@@ -203,16 +230,18 @@ def main() -> int:
     K = min(K, S)
     Wm = min(args.warmup, S)
     sizes = batch_sizes(rc)[:K]
-    es = 2 if W["dtype"] == "bf16" else 4
+    i8 = bool(args.int8) and W["dtype"] == "f32"
+    es = 2 if W["dtype"] == "bf16" else (1 if i8 else 4)
     flops = float(sum(2.0 * b * k * d for b in sizes))
-    bsearch = bool(args.bf16_search) and W["dtype"] == "f32"
-    sdtype = "bf16" if bsearch else W["dtype"]   # arithmetic type of the search
-    sph = bool(args.spherical)
-    tag = args.workload + ("_bf16search" if bsearch else "") + ("_spherical" if sph else "")
+    bsearch = bool(args.bf16_search) and W["dtype"] == "f32" and not i8
+    sdtype = "bf16" if bsearch else ("i8" if i8 else W["dtype"])   # arithmetic type of the search
+    sph = bool(args.spherical) and not i8
+    tag = (args.workload + ("_bf16search" if bsearch else "") + ("_spherical" if sph else "")
+           + ("_int8" if i8 else ""))
     if sph:
         args.no_ttt = True   # the Lloyd-25 target is Euclidean
 
-    X, Xh, Xhost = make_data(args.workload, W, torch)
+    X, Xh, Xhost, codes = make_data(args.workload, W, torch, i8, mm)
 
     # warm-up (untimed)
     if Wm > 0:
@@ -245,6 +274,7 @@ def main() -> int:
     a_ms = prof["ms_assign"]
     assign_tflops = flops / (a_ms / 1e3) / 1e12 if a_ms > 0 else None
     peak = MFMA_PEAK_TFLOPS[sdtype]
+    unit = "TOP/s" if i8 else "TFLOP/s"
     group_bytes = float(sum(b * d * es + 4 * b + 4 * k * d for b in sizes))
     update_bytes = float(K * (4 * 4 * k * d))   # read s, S, C; write S, C (+ counts, small)
     g_ms = prof["ms_group"]
@@ -258,7 +288,7 @@ def main() -> int:
     line = {
         "metric": METRIC,
         "value": round(value, 3),
-        "unit": "TFLOP/s",
+        "unit": unit,
         "n_gpus": 1,
         "steps": K,
         "warmup": Wm,
@@ -272,6 +302,7 @@ def main() -> int:
                    "batch": rc["batch_size"], "alpha0": round(rc["alpha0"], 6),
                    "steps_per_run": S,
                    "search": "bf16 (fp32 rows rounded for the search; sums in fp32)" if bsearch
+                   else "int8 codes (exact integer search; sums in fp32)" if i8
                    else ("bf16" if W["dtype"] == "bf16" else "fp32 (exact)"),
                    "mode": "spherical" if sph else "euclidean"},
         "mfma_peak_frac": round(value / peak, 4),
@@ -280,7 +311,7 @@ def main() -> int:
             "bound": "mfma",
             "achieved": round(assign_tflops, 3) if assign_tflops else None,
             "peak": peak,
-            "unit": "TFLOP/s",
+            "unit": unit,
             "frac": round(assign_tflops / peak, 4) if assign_tflops else None,
             "traffic": traffic,
             "launches": K,
@@ -297,14 +328,22 @@ def main() -> int:
                       ("assign", "bucket", "group", "update", "revive", "sample")},
     }
 
+    if codes is not None:
+        line["config"]["int8"] = {"calibration_rows": 65536, "scale": codes[1],
+                                  "calibrate_encode_s": round(codes[2], 4)}
+
     if not args.no_ttt and args.workload == "embedding":
         path = os.path.join(HERE, "tests", "golden", f"lloyd25_{args.workload}.json")
         if os.path.exists(path):
             with open(path) as f:
                 target = json.load(f)["heldout_mse"]
             seeds = [args.seed + i for i in range(args.ttt_seeds)]
-            ttt = time_to_target(mm, X, Xh, k, target, seeds, [1.0, 1.5, 2.0, 2.5, 3.0, 5.0],
-                                 torch, bsearch)
+            dec = None
+            if codes is not None:
+                shift, scale = codes[0], codes[1]
+                dec = lambda C: mm.int8_decode(C, shift, scale)  # noqa: E731
+            ttt = time_to_target(mm, X, Xh, k, target, seeds, [1.0, 1.25, 1.5, 2.0, 2.5, 3.0, 5.0],
+                                 torch, bsearch, dec)
             line["s_to_lloyd25"] = ttt["seconds"]
             line["time_to_target"] = ttt
         else:

@@ -241,6 +241,43 @@ void emeans_free(emeans_model* m);
 int emeans_batch_rows(int64_t n, uint64_t seed, int32_t pass, int64_t start, int64_t count,
                       int32_t* rows_out, void* stream);
 
+/* ---------------------------------------------------------------------------
+ * int8 codes (README "Data precision", INT8: a shift per dimension and one
+ * power-of-two scale, calibrated from a sample, map fp32 data to int8 codes
+ * that training and assignment take with opts->dtype = EMEANS_I8).
+ * ------------------------------------------------------------------------- */
+
+/* Calibrate from n sample rows (the caller picks the sample):
+ * shift[j] = (min_j + max_j) / 2 over the sample's column j (fp64, stored
+ * fp32); r = the largest |x - shift| over the sample (fp64); *scale = the
+ * largest power of two s with s r <= 127 (1 when r = 0).
+ *   X      device, n x d fp32     shift  device, d fp32 output
+ *   scale  host, one double output
+ * Errors: EINVAL (n < 1, n >= 2^31, d < 1, NULL), ENOTDEVICE, ENOMEM, EHIP.
+ * Synchronises `stream`. */
+int emeans_int8_calibrate(const float* X, int64_t n, int32_t d, float* shift, double* scale,
+                          void* stream);
+
+/* codes = clamp(rint((X - shift) * scale), -127, 127): the difference and the
+ * product in fp32, rounding to nearest with ties to even; values beyond the
+ * calibrated range go to the edge codes.
+ *   X      device, n x d fp32     shift  device, d fp32
+ *   scale  a power of two in [2^-126, 2^126]
+ *   codes  device, n x d int8 output
+ * Errors: EINVAL (n < 0, n >= 2^31, d < 1, scale not such a power of two,
+ * NULL), ENOTDEVICE, EHIP. Asynchronous on `stream`. */
+int emeans_int8_encode(const float* X, int64_t n, int32_t d, const float* shift, double scale,
+                       int8_t* codes, void* stream);
+
+/* Code-space vectors (centroids trained on codes) back to data space:
+ * out = C / scale + shift in fp64, stored fp32.
+ *   C      device, k x d fp32     shift  device, d fp32
+ *   out    device, k x d fp32 output (may equal C)
+ * Errors: EINVAL (k < 0, d < 1, scale as for emeans_int8_encode, NULL),
+ * ENOTDEVICE, EHIP. Asynchronous on `stream`. */
+int emeans_int8_decode(const float* C, int64_t k, int32_t d, const float* shift, double scale,
+                       float* out, void* stream);
+
 /* Message for the last non-zero return on this thread ("" if none). */
 const char* emeans_last_error(void);
 

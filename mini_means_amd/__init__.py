@@ -84,12 +84,16 @@ def lib() -> ctypes.CDLL:
         L.emeans_finalize.argtypes = [c_vp, c_vp, ctypes.POINTER(Stats)]
         L.emeans_free.argtypes = [c_vp]
         L.emeans_free.restype = None
+        L.emeans_int8_calibrate.argtypes = [c_vp, c_i64, c_i32, c_vp, ctypes.POINTER(c_dbl), c_vp]
+        L.emeans_int8_encode.argtypes = [c_vp, c_i64, c_i32, c_vp, c_dbl, c_vp, c_vp]
+        L.emeans_int8_decode.argtypes = [c_vp, c_i64, c_i32, c_vp, c_dbl, c_vp, c_vp]
         L.emeans_last_error.restype = ctypes.c_char_p
         L.emeans_last_error.argtypes = []
         L.emeans_version.argtypes = []
         for f in ("emeans_recipe", "emeans_train", "emeans_assign", "emeans_batch_rows",
                   "emeans_version", "emeans_begin", "emeans_accumulate", "emeans_update",
-                  "emeans_end_epoch", "emeans_finalize"):
+                  "emeans_end_epoch", "emeans_finalize", "emeans_int8_calibrate",
+                  "emeans_int8_encode", "emeans_int8_decode"):
             getattr(L, f).restype = ctypes.c_int
         _lib = L
     return _lib
@@ -247,6 +251,59 @@ def assign(X, C, *, with_dists: bool = True, bf16_search: bool = False, spherica
                                        dists.data_ptr() if dists is not None else None,
                                        ctypes.byref(o)))
     return labels, dists
+
+
+def _f32_device(A, what: str):
+    import torch
+    if not (getattr(A, "is_cuda", False) and A.dtype == torch.float32 and A.is_contiguous()):
+        raise EmeansError(f"EINVAL: {what} must be a contiguous float32 tensor on the GPU")
+
+
+def int8_calibrate(sample, stream=None):
+    """README "Data precision", INT8: per-dimension shift (d float32 tensor)
+    and power-of-two scale (float) from sample rows (n x d float32 tensor)."""
+    import torch
+    _require_device(sample)
+    _f32_device(sample, "sample")
+    n, d = sample.shape
+    shift = torch.empty((d,), dtype=torch.float32, device=sample.device)
+    scale = c_dbl(0.0)
+    with torch.cuda.device(sample.device):
+        s = _stream_ptr(sample, stream)
+        _check(lib().emeans_int8_calibrate(sample.data_ptr(), n, d, shift.data_ptr(),
+                                           ctypes.byref(scale), s))
+    return shift, scale.value
+
+
+def int8_encode(X, shift, scale: float, stream=None):
+    """int8 codes of X (n x d float32 tensor): clamp(rint((X - shift) * scale), +-127)."""
+    import torch
+    _require_device(X)
+    _f32_device(X, "X")
+    _f32_device(shift, "shift")
+    n, d = X.shape
+    if shift.numel() != d:
+        raise EmeansError("EINVAL: shift must have d entries")
+    codes = torch.empty((n, d), dtype=torch.int8, device=X.device)
+    with torch.cuda.device(X.device):
+        _check(lib().emeans_int8_encode(X.data_ptr(), n, d, shift.data_ptr(), float(scale),
+                                        codes.data_ptr(), _stream_ptr(X, stream)))
+    return codes
+
+
+def int8_decode(C, shift, scale: float, stream=None):
+    """Code-space centroids (k x d float32 tensor) back to data space: C / scale + shift."""
+    import torch
+    _f32_device(C, "C")
+    _f32_device(shift, "shift")
+    k, d = C.shape
+    if shift.numel() != d:
+        raise EmeansError("EINVAL: shift must have d entries")
+    out = torch.empty_like(C)
+    with torch.cuda.device(C.device):
+        _check(lib().emeans_int8_decode(C.data_ptr(), k, d, shift.data_ptr(), float(scale),
+                                        out.data_ptr(), _stream_ptr(C, stream)))
+    return out
 
 
 def batch_rows(n: int, seed: int, pass_: int, start: int, count: int, device="cuda", stream=None):

@@ -727,4 +727,76 @@ int emeans_finalize(emeans_model* m, float* centroids, emeans_stats* stats) {
 
 void emeans_free(emeans_model* m) { delete m; }
 
+// README "Data precision", INT8: calibration, encoding and decoding of codes.
+namespace {
+bool pow2_scale(double s) {
+  if (!(s >= 0x1p-126 && s <= 0x1p126)) return false;
+  int e;
+  return frexp(s, &e) == 0.5;
+}
+}  // namespace
+
+int emeans_int8_calibrate(const float* X, int64_t n, int32_t d, float* shift, double* scale,
+                          void* stream) {
+  g_err.clear();
+  if (n < 1 || n >= ((int64_t)1 << 31)) return fail(EMEANS_EINVAL, "n out of range (%lld)", (long long)n);
+  if (d < 1) return fail(EMEANS_EINVAL, "d must be >= 1");
+  if (!X || !shift || !scale) return fail(EMEANS_EINVAL, "X, shift and scale must not be NULL");
+  int rc;
+  if ((rc = check_device(X, "X")) || (rc = check_device(shift, "shift"))) return rc;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  void* base = nullptr;
+  float* work = nullptr;
+  double* dscale = nullptr;
+  Arena ar;
+  ar.want(&dscale, 1);
+  ar.want(&work, calib_workspace_floats(n, d));
+  rc = EMEANS_OK;
+  HIP_TRY(ar.alloc(&base, st));
+  HIP_TRY(launch_calibrate(X, n, d, shift, work, dscale, st));
+  HIP_TRY(hipMemcpyAsync(scale, dscale, sizeof(double), hipMemcpyDeviceToHost, st));
+  HIP_TRY(hipStreamSynchronize(st));
+done:
+  if (base) {
+    const hipError_t e = hipFreeAsync(base, st);
+    if (e != hipSuccess && rc == EMEANS_OK)
+      rc = fail(EMEANS_EHIP, "hipFreeAsync: %s", hipGetErrorString(e));
+  }
+  return rc;
+}
+
+int emeans_int8_encode(const float* X, int64_t n, int32_t d, const float* shift, double scale,
+                       int8_t* codes, void* stream) {
+  g_err.clear();
+  if (n < 0 || n >= ((int64_t)1 << 31)) return fail(EMEANS_EINVAL, "n out of range (%lld)", (long long)n);
+  if (d < 1) return fail(EMEANS_EINVAL, "d must be >= 1");
+  if (!pow2_scale(scale)) return fail(EMEANS_EINVAL, "scale must be a power of two in [2^-126, 2^126] (got %g)", scale);
+  if (!X || !shift || !codes) return fail(EMEANS_EINVAL, "X, shift and codes must not be NULL");
+  if (n == 0) return EMEANS_OK;
+  int rc;
+  if ((rc = check_device(X, "X")) || (rc = check_device(shift, "shift")) ||
+      (rc = check_device(codes, "codes")))
+    return rc;
+  const hipError_t e = launch_encode(X, n, d, shift, (float)scale, codes, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return fail(EMEANS_EHIP, "encode launch: %s", hipGetErrorString(e));
+  return EMEANS_OK;
+}
+
+int emeans_int8_decode(const float* C, int64_t k, int32_t d, const float* shift, double scale,
+                       float* out, void* stream) {
+  g_err.clear();
+  if (k < 0 || k >= ((int64_t)1 << 31)) return fail(EMEANS_EINVAL, "k out of range (%lld)", (long long)k);
+  if (d < 1) return fail(EMEANS_EINVAL, "d must be >= 1");
+  if (!pow2_scale(scale)) return fail(EMEANS_EINVAL, "scale must be a power of two in [2^-126, 2^126] (got %g)", scale);
+  if (!C || !shift || !out) return fail(EMEANS_EINVAL, "C, shift and out must not be NULL");
+  if (k == 0) return EMEANS_OK;
+  int rc;
+  if ((rc = check_device(C, "C")) || (rc = check_device(shift, "shift")) ||
+      (rc = check_device(out, "out")))
+    return rc;
+  const hipError_t e = launch_decode(C, k, d, shift, scale, out, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return fail(EMEANS_EHIP, "decode launch: %s", hipGetErrorString(e));
+  return EMEANS_OK;
+}
+
 }  // extern "C"

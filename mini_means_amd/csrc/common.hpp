@@ -125,6 +125,16 @@ __device__ __forceinline__ T wave_sum(T v) {
   return v;
 }
 
+template <typename T>
+__device__ __forceinline__ T wave_max(T v) {
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) {
+    const T o = __shfl_xor(v, off, kWave);
+    v = o > v ? o : v;
+  }
+  return v;
+}
+
 // Inclusive scan across the 64 lanes of a wave.
 template <typename T>
 __device__ __forceinline__ T wave_incl_scan(T v) {

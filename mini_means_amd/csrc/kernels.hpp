@@ -124,4 +124,17 @@ hipError_t launch_normalize_rows(float* C, int k, int d, hipStream_t st);
 hipError_t launch_finalize(int k, int d, const int32_t* pass_counts, const float* LS, float* C,
                            bool sph, hipStream_t st);
 
+// int8 codes (codes.hip). Calibration of shift (d fp32, device) and scale
+// (one fp64, device) from n sample rows; `work` holds
+// calib_workspace_floats(n, d) floats (8-byte aligned).
+size_t calib_workspace_floats(int64_t n, int d);
+hipError_t launch_calibrate(const float* X, int64_t n, int d, float* shift, float* work,
+                            double* scale, hipStream_t st);
+// codes = clamp(rint((X - shift) * scale), -127, 127), n x d.
+hipError_t launch_encode(const float* X, int64_t n, int d, const float* shift, float scale,
+                         int8_t* codes, hipStream_t st);
+// out = C / scale + shift (fp64, stored fp32), k x d.
+hipError_t launch_decode(const float* C, int64_t k, int d, const float* shift, double scale,
+                         float* out, hipStream_t st);
+
 }  // namespace emk
