@@ -111,6 +111,18 @@ typedef struct emeans_opts {
                                  emeans_assign: labels by the highest dot product with
                                  C as given, dists[i] = that similarity. fp32 or
                                  bf16 X only (EINVAL with int8 X). */
+  int32_t lloyd;              /* 1: plain Lloyd iterations instead of e-means (the
+                                 baseline of the blog's Lloyd section, the loss
+                                 e-means is timed against): each of the T passes
+                                 (T a whole number) is one step over all n rows in
+                                 row order with alpha = 1, so every centroid becomes
+                                 the exact mean of its rows and a centroid with no
+                                 row stays where it is; no revival. batch_size,
+                                 alpha0 and unused_threshold are ignored; stats->obj
+                                 holds the mean squared distance of every iteration's
+                                 assignment. n < 2^31 (the 2^24 batch limit does not
+                                 apply; a cluster of more than 2^24 rows divides by
+                                 its fp32-rounded count). Not with emeans_begin. */
 } emeans_opts;
 
 /* Recipe and statistics of a run (README "Settings and results": recipe, obj,

@@ -36,7 +36,7 @@ class Opts(ctypes.Structure):
         ("unused_threshold", c_dbl), ("no_finalize", c_i32), ("profile", c_i32),
         ("stream", c_vp), ("trace_labels", c_vp), ("out_counts", c_vp), ("split_log", c_vp),
         ("split_log_cap", c_i64), ("max_steps", c_i64), ("bf16_search", c_i32),
-        ("spherical", c_i32),
+        ("spherical", c_i32), ("lloyd", c_i32),
     ]
 
 
@@ -113,8 +113,9 @@ def _check(rc: int) -> None:
 
 
 def _opts(dtype=F32, batch_law="auto", batch_size=0, alpha0=0.0, unused_threshold=None,
-          finalize=True, profile=False, stream=None) -> Opts:
+          finalize=True, profile=False, stream=None, lloyd=False) -> Opts:
     o = Opts()
+    o.lloyd = 1 if lloyd else 0
     o.dtype = dtype
     o.batch_law = LAWS[batch_law] if isinstance(batch_law, str) else int(batch_law)
     o.batch_size = int(batch_size or 0)
@@ -190,16 +191,19 @@ def train(X, k: int, T: float = 5.0, seed: int = 1234, *, batch_law="auto", batc
           alpha0: float = 0.0, unused_threshold=None, finalize: bool = True,
           capture_labels: bool = True, trace: bool = False, counts: bool = False,
           split_log_cap: int = 0, profile: bool = False, max_steps: int = 0,
-          bf16_search: bool = False, spherical: bool = False, stream=None) -> TrainOutput:
+          bf16_search: bool = False, spherical: bool = False, lloyd: bool = False,
+          stream=None) -> TrainOutput:
+    """e-means training of X (n x d tensor on the GPU). lloyd: plain Lloyd
+    iterations instead (T of them, every row each time, alpha = 1)."""
     import torch
     _require_device(X)
     n, d = X.shape
     dev = X.device
     with torch.cuda.device(dev):
         o = _opts(_dtype_of(X), batch_law, batch_size, alpha0, unused_threshold, finalize,
-                  profile, _stream_ptr(X, stream))
+                  profile, _stream_ptr(X, stream), lloyd)
         rc = recipe(n, d, k, T, batch_law=batch_law, batch_size=batch_size, alpha0=alpha0,
-                    unused_threshold=unused_threshold)
+                    unused_threshold=unused_threshold, lloyd=lloyd)
         C = torch.empty((k, d), dtype=torch.float32, device=dev)
         labels = torch.empty((n,), dtype=torch.int32, device=dev) if capture_labels else None
         tr = torch.empty((sum(rc["epoch_rows"]),), dtype=torch.int32, device=dev) if trace else None

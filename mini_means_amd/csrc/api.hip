@@ -44,6 +44,7 @@ constexpr int kReviveEvery = 5;  // blog: dead clusters are checked every five b
 
 struct Recipe {
   int law = 0;
+  bool lloyd = false;  // plain Lloyd iterations: B = n, alpha = 1, no revival
   int64_t B = 0;
   double alpha0 = 0;
   double thr = 0;
@@ -61,6 +62,26 @@ int make_recipe(int64_t n, int32_t d, int32_t k, double T, const emeans_opts* o,
   if (k < 1) return fail(EMEANS_EINVAL, "k must be >= 1 (got %d)", k);
   if ((int64_t)k > n) return fail(EMEANS_EINVAL, "k (%d) must not exceed n (%lld)", k, (long long)n);
   if (!(T > 0.0) || !isfinite(T)) return fail(EMEANS_EINVAL, "T must be > 0 (got %g)", T);
+  if (o && o->lloyd) {
+    // blog, Lloyd section: assign every vector, then move each centroid to the
+    // exact mean of its vectors; T whole iterations
+    if (T != floor(T) || T > EMEANS_MAX_PASSES)
+      return fail(EMEANS_EINVAL, "lloyd mode needs a whole number of iterations 1..%d (got %g)",
+                  EMEANS_MAX_PASSES, T);
+    r.lloyd = true;
+    r.law = o->batch_law ? o->batch_law : (d <= 16 ? EMEANS_LAW_QUALITY : EMEANS_LAW_THROUGHPUT);
+    r.B = n;
+    r.alpha0 = 1.0;
+    r.thr = 0.0;
+    r.npass = (int)T;
+    r.S = 0;
+    for (int e = 0; e < r.npass; ++e) {
+      r.rows[e] = n;
+      r.steps[e] = 1;
+      r.S += 1;
+    }
+    return EMEANS_OK;
+  }
   const int32_t law_opt = o ? o->batch_law : 0;
   if (law_opt < 0 || law_opt > 2) return fail(EMEANS_EINVAL, "batch_law must be 0, 1 or 2");
   r.law = law_opt ? law_opt : (d <= 16 ? EMEANS_LAW_QUALITY : EMEANS_LAW_THROUGHPUT);
@@ -195,7 +216,7 @@ int check_run_args(int64_t n, int32_t d, int32_t k, double T, const emeans_opts*
   const int rc = make_recipe(n, d, k, T, opts, r);
   if (rc) return rc;
   if (n >= ((int64_t)1 << 31)) return fail(EMEANS_EINVAL, "n must be < 2^31");
-  if (r.B >= ((int64_t)1 << 24))
+  if (!r.lloyd && r.B >= ((int64_t)1 << 24))
     return fail(EMEANS_EINVAL, "batch size must be < 2^24 (counts are exact in fp32)");
   return EMEANS_OK;
 }
@@ -315,7 +336,7 @@ struct emeans_model {
     rc = make_recipe(n, d, k, T, opts, r);
     if (rc) return rc;
     if (n >= ((int64_t)1 << 31)) return fail(EMEANS_EINVAL, "n must be < 2^31");
-    if (r.B >= ((int64_t)1 << 24))
+    if (!r.lloyd && r.B >= ((int64_t)1 << 24))
       return fail(EMEANS_EINVAL, "batch size must be < 2^24 (counts are exact in fp32)");
     if (opts && opts->trace_labels && (rc = check_device(opts->trace_labels, "trace_labels")))
       return rc;
@@ -340,7 +361,7 @@ struct emeans_model {
     const int64_t B = r.B;
     Arena ar;
     if (!external_C) ar.want(&C, kd);
-    ar.want(&rows, (size_t)B);
+    ar.want(&rows, r.lloyd ? (size_t)1 : (size_t)B);
     ar.want(&order, (size_t)B);
     ar.want(&blab, (size_t)B);
     ar.want(&pcounts, (size_t)k);
@@ -428,7 +449,7 @@ struct emeans_model {
   // EMA update with what was accumulated since the last one; revival every
   // kReviveEvery updates.
   int update() {
-    const float a = alpha_at(r.alpha0, t, r.S);
+    const float a = r.lloyd ? 1.0f : alpha_at(r.alpha0, t, r.S);
     const float b = 1.0f - a;
     const bool last = e == r.npass - 1;
     HIP_RET(timed(kUpdate, [&] {
@@ -628,10 +649,13 @@ int emeans_train(const void* X, int64_t n, int32_t d, int32_t k, double T, uint6
     for (int64_t s = 0; s < r.steps[e] && m.t < run_steps; ++s) {
       const int64_t rem = r.rows[e] - s * B;
       const int nb = (int)(rem < B ? rem : B);
-      HIP_RET(m.timed(emeans_model::kSample, [&] {
-        return launch_sample_rows(pk, (uint64_t)(s * B), nb, m.rows, st);
-      }));
-      if ((rc = m.accumulate(X, m.rows, nb, (last && labels) ? labels : nullptr))) return rc;
+      // Lloyd iterations visit the rows in their own order (rows = NULL)
+      if (!r.lloyd)
+        HIP_RET(m.timed(emeans_model::kSample, [&] {
+          return launch_sample_rows(pk, (uint64_t)(s * B), nb, m.rows, st);
+        }));
+      if ((rc = m.accumulate(X, r.lloyd ? nullptr : m.rows, nb, (last && labels) ? labels : nullptr)))
+        return rc;
       if ((rc = m.update())) return rc;
     }
     if ((rc = m.close_pass())) return rc;
@@ -646,6 +670,7 @@ int emeans_begin(int64_t n, int32_t d, int32_t k, double T, uint64_t seed, const
   if (!model) return fail(EMEANS_EINVAL, "model is NULL");
   *model = nullptr;
   if ((rc = check_run_args(n, d, k, T, opts))) return rc;
+  if (opts && opts->lloyd) return fail(EMEANS_EINVAL, "lloyd is an emeans_train option");
   if (!start) return fail(EMEANS_EINVAL, "start must not be NULL");
   if ((rc = check_device(start, "start"))) return rc;
   if (opts && opts->max_steps) return fail(EMEANS_EINVAL, "max_steps is an emeans_train option");

@@ -563,15 +563,30 @@ def train(X: np.ndarray, k: int, T: float, seed: int = 1234, *, batch_law: int =
 
 
 def lloyd(X: np.ndarray, k: int, iters: int, seed: int = 1234, nthreads: int = 0,
-          progress: Optional[Callable[[int, float], None]] = None):
+          progress: Optional[Callable[[int, float], None]] = None,
+          labels_for_step: Optional[Callable[[int, np.ndarray], np.ndarray]] = None,
+          check_hook: Optional[Callable[[dict], None]] = None):
     """Plain Lloyd from the same k starting rows: assign all rows, move each
     centroid to the exact mean of its rows (a centroid with no row stays).
-    Returns the centroids after `iters` updates and the MSE seen at each assign."""
+    Returns the centroids after `iters` updates and the MSE seen at each assign.
+
+    labels_for_step(i, None) may supply the labels of iteration i from
+    elsewhere (lockstep replay, as in train): they are handed to check_hook
+    with the oracle's own assignment and then adopted; the MSE is that of the
+    adopted labels."""
     n, d = X.shape
     C = np.ascontiguousarray(to_f32(X[init_rows(n, k, seed)]), dtype=np.float32)
     hist = []
-    for _ in range(iters):
-        lab, d1, _ = assign(X, search_centroids(C, X), nthreads=nthreads)
+    for i in range(iters):
+        Cs = search_centroids(C, X)
+        lab, d1, d2 = assign(X, Cs, nthreads=nthreads)
+        if labels_for_step is not None:
+            given = np.asarray(labels_for_step(i, None), dtype=np.int32)
+            gd = dist_to(X, Cs, given)
+            if check_hook is not None:
+                check_hook(dict(t=i, rows=None, C=Cs, C32=C.copy(), given=given, oracle=lab,
+                                d1=d1, d2=d2, given_dist=gd))
+            lab, d1 = given, gd
         hist.append(float(d1.mean()))
         if progress is not None:
             progress(len(hist), hist[-1])

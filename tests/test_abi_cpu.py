@@ -111,6 +111,25 @@ def test_recipe_rejects(L, args, code):
     assert L.emeans_last_error()
 
 
+def test_lloyd_recipe(L):
+    """Lloyd mode (blog, Lloyd section): T whole iterations over all n rows,
+    alpha = 1, no revival; the 2^24 batch limit does not apply."""
+    r = mm.recipe(1000, 16, 10, 7, lloyd=True)
+    assert (r["batch_size"], r["alpha0"], r["total_steps"], r["unused_threshold"]) == (1000, 1.0, 7, 0.0)
+    assert r["epoch_rows"] == [1000] * 7 and r["steps_per_pass"] == [1] * 7
+    assert mm.recipe(20_000_000, 128, 100, 3, lloyd=True)["batch_size"] == 20_000_000
+    for T in (2.5, 65.0):
+        with pytest.raises(mm.EmeansError, match="EINVAL"):
+            mm.recipe(1000, 16, 10, T, lloyd=True)
+    o = mm.Opts()
+    o.lloyd = 1
+    s = mm.Stats()
+    # streaming training takes no Lloyd mode; the check precedes device work
+    m = ctypes.c_void_p()
+    assert L.emeans_begin(100, 4, 3, 2.0, 1, None, ctypes.byref(o), ctypes.byref(m)) == -1
+    assert b"lloyd" in L.emeans_last_error()
+
+
 def test_train_rejects_before_device_work(L):
     o = mm.Opts()
     s = mm.Stats()

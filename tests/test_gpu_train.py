@@ -91,6 +91,39 @@ def test_train_lockstep(mm, name, gen, n, d, k, T, o):
         assert np.all((np.abs(nrm - 1.0) < 1e-6) | (nrm == 0.0))
 
 
+LLOYD = [("tiny", "tiny", 10_000, 16, 64, 8), ("emb-small", "embedding", 12_000, 768, 256, 4),
+         ("large-small", "large", 40_000, 128, 1024, 3), ("codes", "codes", 12_000, 96, 200, 4),
+         ("ragged", "tiny", 5_003, 37, 77, 5)]
+
+
+@pytest.mark.parametrize("name,gen,n,d,k,iters", LLOYD, ids=[c[0] for c in LLOYD])
+def test_lloyd_mode_lockstep(mm, name, gen, n, d, k, iters):
+    """GPU Lloyd mode against the oracle's Lloyd, adopting the band-checked
+    GPU labels every iteration: per-iteration MSE, final counts and centroids."""
+    from parity import check_labels
+    X = datagen.make(gen, n, d, seed=23)
+    out = _gpu_train(mm, X, k, float(iters), 1234, lloyd=True)
+    trace = out.trace.cpu().numpy().reshape(iters, n)
+    last = {}
+
+    def hook(chk):
+        C32 = chk["C32"] if X.dtype in (np.uint16, np.int8) else None
+        check_labels(X, chk["C"], None, chk["given"], chk["oracle"], chk["d1"], chk["d2"],
+                     chk["given_dist"], what=f"lloyd {name} iteration {chk['t']}", C32=C32)
+        last["labels"] = chk["given"]
+
+    C, hist = oracle.lloyd(X, k, iters, 1234, labels_for_step=lambda i, _: trace[i],
+                           check_hook=hook)
+    np.testing.assert_allclose(out.stats["obj"], hist, rtol=1e-4)
+    counts = np.bincount(last["labels"], minlength=k).astype(np.float32)
+    assert np.array_equal(out.counts.cpu().numpy(), counts)
+    assert np.array_equal(out.labels.cpu().numpy(), last["labels"])
+    tol = 1e-2 if X.dtype == np.uint16 else 1e-4
+    err = rel_l2(out.centroids.cpu().numpy(), C)
+    assert err <= tol, f"centroids rel L2 {err:.3e}"
+    assert out.stats["n_splits"] == 0
+
+
 # Revival draws at larger k: 64 chunks of 64 V clusters, V = 2, 8, 16 (live
 # counts in global memory) and the generic path (k > 65536), each with
 # thousands of revivals.
