@@ -42,7 +42,13 @@ Do."):
                     smaller format: for bf16 data, and for fp32 data when
                     bf16_search asks for the pages' GPU default (rows and
                     centroids rounded to bf16 for the search, fp32 rows
-                    grouped).
+                    grouped). INT8 and FP8 (E4M3) codes: a shift per
+                    dimension and one power-of-two scale calibrated on a
+                    sample, values beyond its range clamped to the edge
+                    (127 / 448); training runs on the codes and the search
+                    compares them with the centroids rounded to codes.
+* Lloyd             blog, Lloyd section: assign all, move each centroid to
+                    the exact mean of its points (the Lloyd-25 target).
 
 Readings where the pages are silent (each listed in the design notes):
 power-of-two rounding in log2 space; cap = largest power of two <= n/2;
@@ -218,6 +224,8 @@ def _dtype_code(X: np.ndarray) -> int:
         return 1
     if X.dtype == np.int8:        # int8 codes
         return 2
+    if X.dtype == np.uint8:       # FP8 E4M3 codes (bit patterns)
+        return 3
     raise TypeError(f"unsupported data type {X.dtype}")
 
 
@@ -226,6 +234,8 @@ def to_f32(X: np.ndarray) -> np.ndarray:
         return (X.astype(np.uint32) << 16).view(np.float32)
     if X.dtype == np.int8:
         return X.astype(np.float32)
+    if X.dtype == np.uint8:
+        return E4M3_VALUES[X]
     return X
 
 
@@ -261,6 +271,13 @@ def int8_calibrate(sample: np.ndarray):
     scale from a sample. Readings: the shift is the sample's midrange per
     dimension (fp64, stored fp32); the scale is the largest power of two that
     maps every sample value within [-127, 127] (1 for a constant sample)."""
+    return _calibrate(sample, 127.0)
+
+
+def _calibrate(sample: np.ndarray, bound: float):
+    """Midrange shift per dimension and the largest power-of-two scale s with
+    s * r <= bound, r the sample's largest distance from its shift (1 when
+    r = 0)."""
     x = np.asarray(sample, dtype=np.float32)
     mn = x.min(axis=0).astype(np.float64)
     mx = x.max(axis=0).astype(np.float64)
@@ -269,10 +286,10 @@ def int8_calibrate(sample: np.ndarray):
     r = float(np.max(np.maximum(mx - s64, s64 - mn))) if x.size else 0.0
     if r <= 0.0:
         return shift, 1.0
-    scale = 2.0 ** math.floor(math.log2(127.0 / r))
-    while scale * r > 127.0:    # guard the floor of a rounded logarithm
+    scale = 2.0 ** math.floor(math.log2(bound / r))
+    while scale * r > bound:    # guard the floor of a rounded logarithm
         scale /= 2.0
-    while scale * 2.0 * r <= 127.0:
+    while scale * 2.0 * r <= bound:
         scale *= 2.0
     return shift, scale
 
@@ -291,14 +308,84 @@ def int8_decode(C: np.ndarray, shift: np.ndarray, scale: float) -> np.ndarray:
             + np.asarray(shift, dtype=np.float64)).astype(np.float32)
 
 
+# ----------------------------------------------------------------------------
+# FP8 E4M3 (OCP 8-bit floating point, the "FP8 (E4M3)" of README "Data
+# precision"): sign bit, 4 exponent bits with bias 7, 3 mantissa bits;
+# exponent 0 holds the subnormals m * 2^-9; exponent 15 with mantissa 7 is NaN;
+# no infinities; the largest finite value is 448.
+# ----------------------------------------------------------------------------
+
+def _e4m3_table() -> np.ndarray:
+    vals = np.empty(256, dtype=np.float32)
+    for c in range(256):
+        e, m = (c >> 3) & 15, c & 7
+        if e == 15 and m == 7:
+            v = float("nan")
+        elif e == 0:
+            v = m * 2.0 ** -9
+        else:
+            v = (1.0 + m / 8.0) * 2.0 ** (e - 7)
+        vals[c] = -v if c & 0x80 else v
+    return vals
+
+
+E4M3_VALUES = _e4m3_table()
+E4M3_MAX = 448.0
+
+
+def e4m3_round(C: np.ndarray) -> np.ndarray:
+    """fp32 -> nearest E4M3 value (ties to the even mantissa), saturating at
+    +-448 (README "Data precision": values beyond the range go to the edge),
+    returned as fp32 values. The spacing of E4M3 values is 2^-9 below 2^-6
+    and 2^(E-4) in the binade [2^(E-1), 2^E)."""
+    x = np.asarray(C, dtype=np.float32).astype(np.float64)
+    a = np.minimum(np.abs(x), E4M3_MAX)
+    _, E = np.frexp(a)
+    spacing = np.where(a < 2.0 ** -6, 2.0 ** -9, np.ldexp(1.0, E - 4))
+    q = np.rint(a / spacing) * spacing
+    return np.copysign(q, x).astype(np.float32)
+
+
+def e4m3_bits(V: np.ndarray) -> np.ndarray:
+    """E4M3 values (as e4m3_round returns them) -> their bit patterns (uint8)."""
+    v = np.asarray(V, dtype=np.float32).astype(np.float64)
+    a = np.abs(v)
+    m, E = np.frexp(a)
+    normal = a >= 2.0 ** -6
+    code = np.where(normal, ((E - 1 + 7) << 3) | np.rint((2.0 * m - 1.0) * 8.0).astype(np.int64),
+                    np.rint(a * 512.0).astype(np.int64))
+    return (code | np.where(np.signbit(v), 0x80, 0)).astype(np.uint8)
+
+
+def fp8_calibrate(sample: np.ndarray):
+    """README "Data precision", FP8: as int8_calibrate, with the largest
+    power-of-two scale that maps the sample within [-448, 448]."""
+    return _calibrate(sample, E4M3_MAX)
+
+
+def fp8_encode(X: np.ndarray, shift: np.ndarray, scale: float) -> np.ndarray:
+    """FP8 codes: (x - shift) * scale in fp32 (the product by a power of two is
+    exact), rounded to the nearest E4M3 value (ties to even), saturating at
+    +-448; returned as bit patterns (uint8)."""
+    y = (np.asarray(X, dtype=np.float32) - np.asarray(shift, dtype=np.float32)) * np.float32(scale)
+    return e4m3_bits(e4m3_round(y))
+
+
+def fp8_decode(C: np.ndarray, shift: np.ndarray, scale: float) -> np.ndarray:
+    """Code-space vectors (centroids) back to data space: c / scale + shift."""
+    return int8_decode(C, shift, scale)
+
+
 def search_centroids(C: np.ndarray, X: np.ndarray) -> np.ndarray:
     """Centroids in the search format: bf16 for bf16 data, int8 codes for int8
-    data (README "Data precision": only the search uses the smaller format),
-    fp32 otherwise."""
+    data, E4M3 values for FP8 data (README "Data precision": only the search
+    uses the smaller format), fp32 otherwise."""
     if X.dtype == np.uint16:
         return bf16_round(C)
     if X.dtype == np.int8:
         return int8_round(C)
+    if X.dtype == np.uint8:
+        return e4m3_round(C)
     return np.ascontiguousarray(C, dtype=np.float32)
 
 

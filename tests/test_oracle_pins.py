@@ -544,6 +544,81 @@ def test_int8_calibration_and_codes():
     assert oracle.int8_round(C).tolist() == [[2.0, -0.0, 127.0, -127.0, 3.0, -2.0]]
 
 
+# FP8 E4M3 (README "Data precision", FP8)
+
+def test_e4m3_table_and_rounding_against_brute_force():
+    V = oracle.E4M3_VALUES
+    # code points fixed by the OCP E4M3 definition (bias 7, subnormals m * 2^-9)
+    assert V[0x00] == 0.0 and V[0x01] == 2.0 ** -9 and V[0x07] == 7 * 2.0 ** -9
+    assert V[0x08] == 2.0 ** -6 and V[0x38] == 1.0 and V[0x3F] == 1.875 and V[0x40] == 2.0
+    assert V[0x7E] == 448.0 and V[0xB8] == -1.0 and V[0xFE] == -448.0
+    assert np.isnan(V[0x7F]) and np.isnan(V[0xFF])
+    assert np.all(np.diff(V[:0x7F].astype(np.float64)) > 0)   # codes 0..126 increase
+    codes = np.array([c for c in range(256) if (c & 0x7F) != 0x7F])
+    finite = V[codes].astype(np.float64)
+    rng = np.random.default_rng(7)
+    pos = np.sort(V[:0x7F].astype(np.float64))
+    mids = (pos[1:] + pos[:-1]) / 2.0                  # exact ties between neighbours
+    x = np.concatenate([rng.uniform(-500, 500, 4000),
+                        np.exp(rng.uniform(-12, 6, 3000)) * rng.choice([-1, 1], 3000),
+                        mids, -mids, [448.0, 455.9, 464.0, 1e6, -1e6, 0.0]]).astype(np.float32)
+    got = oracle.e4m3_round(x).astype(np.float64)
+    dist = np.abs(x.astype(np.float64)[:, None] - finite[None, :])
+    best = dist.min(axis=1, keepdims=True)
+    tied = dist == best
+    even = tied & ((codes[None, :] & 1) == 0)     # ties go to the even mantissa
+    pick = np.where(even.any(axis=1), np.argmax(even, axis=1), np.argmax(tied, axis=1))
+    assert np.array_equal(got, finite[pick])
+    # bit patterns round-trip (all finite codes but -0)
+    nz = codes[codes != 0x80]
+    assert np.array_equal(oracle.e4m3_bits(V[nz]), nz.astype(np.uint8))
+
+
+def test_fp8_calibration_and_codes():
+    rng = np.random.default_rng(43)
+    S = (rng.standard_normal((4000, 20)) * rng.uniform(0.1, 9.0, 20) + rng.uniform(-5, 5, 20))
+    S = S.astype(np.float32)
+    shift, scale = oracle.fp8_calibrate(S)
+    mn, mx = S.min(0).astype(np.float64), S.max(0).astype(np.float64)
+    r = np.max(np.maximum(mx - shift, shift - mn))
+    assert math.log2(scale) == int(math.log2(scale))
+    assert scale * r <= 448.0 < 2.0 * scale * r
+    codes = oracle.fp8_encode(S, shift, scale)
+    assert codes.dtype == np.uint8 and not np.any((codes & 0x7F) == 0x7F)
+    y = (S - shift) * np.float32(scale)
+    back = oracle.to_f32(codes).astype(np.float64)
+    # E4M3 keeps 3 mantissa bits: relative error at most 2^-4 (or 2^-10 absolute)
+    assert np.all(np.abs(back - y) <= np.maximum(np.abs(y) * 2.0 ** -4, 2.0 ** -10) + 1e-12)
+    dec = oracle.fp8_decode(back.astype(np.float32), shift, scale).astype(np.float64)
+    bound = np.maximum(np.abs(y) * 2.0 ** -4, 2.0 ** -10) / scale
+    assert np.all(np.abs(dec - S) <= bound + 1e-6 * (np.abs(S) + np.abs(shift)))
+    edge = np.array([[-448.0 / 64], [448.0 / 64]], np.float32)
+    assert oracle.fp8_calibrate(edge)[1] == 64.0
+    assert oracle.fp8_calibrate(np.full((3, 2), 5.0, np.float32))[1] == 1.0
+    far = np.full((1, 20), 1e9, np.float32)
+    assert np.all(oracle.fp8_encode(far, shift, scale) == 0x7E)
+    assert np.all(oracle.fp8_encode(-far, shift, scale) == 0xFE)
+
+
+def test_fp8_training_closing_mean_is_exact_mean_of_codes():
+    S = datagen.tiny(n=5000, d=16, seed=9)
+    shift, scale = oracle.fp8_calibrate(S)
+    X = oracle.fp8_encode(S, shift, scale)
+    res = oracle.train(X, 40, 2.0, seed=5)
+    Xv = oracle.to_f32(X).astype(np.float64)
+    for j in range(40):
+        m = res.labels == j
+        if m.any():
+            np.testing.assert_allclose(res.centroids[j], Xv[m].mean(axis=0), rtol=1e-6, atol=1e-6)
+    # the search uses the centroids rounded to E4M3: x = 1 against 0.95 and
+    # 1.06: as values 0.95 is nearer, but they round to 0.9375 and 1.0
+    x1 = oracle.e4m3_bits(np.array([[1.0]], np.float32))
+    c2 = np.array([[0.95], [1.06]], np.float32)
+    assert oracle.e4m3_round(c2).ravel().tolist() == [0.9375, 1.0]
+    assert oracle.assign(x1, oracle.search_centroids(c2, x1))[0].tolist() == [1]
+    assert oracle.assign(x1, c2)[0].tolist() == [0]
+
+
 def test_int8_training_closing_mean_is_exact_mean_of_codes():
     """Training on int8 codes: the centroids live in code space (fp32), the
     search uses their int8 rounding, and the closing mean is the exact mean of
