@@ -23,7 +23,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, HERE)
 
 METRIC = "assign TFLOP/s (% MFMA peak) + s to Lloyd-25 MSE, 1M×768 k=4096"
-MFMA_PEAK_TFLOPS = {"f32": 157.3, "bf16": 2516.6, "i8": 5033.2}   # MI355X dense MFMA (i8: TOP/s)
+MFMA_PEAK_TFLOPS = {"f32": 157.3, "bf16": 2516.6, "i8": 5033.2, "f8": 5033.2}  # MI355X dense (i8: TOP/s)
 HBM_PEAK_GBS = 8000.0
 
 DESCR = {
@@ -53,7 +53,7 @@ def assign_kernel_name(dtype: str, d: int) -> str:
     dtype and width (the dispatch rule of launch_assign in assign.hip)."""
     if dtype == "bf16" and d in (32, 64, 96, 128):
         return "assign_bf16_kernel (points resident in registers, 32x32x16 bf16 MFMA)"
-    if d % {"bf16": 8, "i8": 16}.get(dtype, 4) == 0:
+    if d % {"bf16": 8, "i8": 16, "f8": 16}.get(dtype, 4) == 0:
         return "assign_ring_kernel (direct-to-LDS stage ring, 16x16 MFMA)"
     return "assign_kernel (register-staged stages, 16x16 MFMA)"
 
@@ -87,27 +87,31 @@ def batch_sizes(rc: dict) -> list:
     return out
 
 
-def make_data(name: str, W: dict, torch, int8: bool = False, mm=None):
+def make_data(name: str, W: dict, torch, codes: str = "", mm=None):
     """Training data, held-out data (fp32 or bf16, on the GPU) and the host
-    copy of the training data (None when it is made on the GPU). int8: the
-    training rows as int8 codes, calibrated on the first 65536 rows (the data
-    is an iid draw) and encoded on the GPU; returns the codes, the held-out
-    data, the host codes and (shift, scale, encode seconds)."""
+    copy of the training data (None when it is made on the GPU). codes
+    ("int8" or "fp8"): the training rows as codes, calibrated on the first
+    65536 rows (the data is an iid draw) and encoded on the GPU; returns the
+    codes, the held-out data, the host codes (int8, or E4M3 bit patterns) and
+    (shift, scale, encode seconds, decode function)."""
     from mini_means_amd import datagen
     t0 = time.time()
-    if int8:
+    if codes:
+        cal, enc, dec = ((mm.int8_calibrate, mm.int8_encode, mm.int8_decode) if codes == "int8"
+                         else (mm.fp8_calibrate, mm.fp8_encode, mm.fp8_decode))
         Xf = torch.from_numpy(datagen.make(W["gen"], W["n"], W["d"])).cuda()
         Xh = torch.from_numpy(datagen.make(W["gen"], W["heldout"], W["d"], split=1)).cuda()
         torch.cuda.synchronize()
         t1 = time.perf_counter()
-        shift, scale = mm.int8_calibrate(Xf[:65536])
-        X = mm.int8_encode(Xf, shift, scale)
+        shift, scale = cal(Xf[:65536])
+        X = enc(Xf, shift, scale)
         torch.cuda.synchronize()
         enc_s = time.perf_counter() - t1
         del Xf
-        log(f"int8 codes {tuple(X.shape)} (scale {scale}) calibrated + encoded in {enc_s:.4f}s; "
-            f"data in {time.time() - t0:.1f}s")
-        return X, Xh, X.cpu().numpy(), (shift, scale, enc_s)
+        log(f"{codes} codes {tuple(X.shape)} (scale {scale}) calibrated + encoded in "
+            f"{enc_s:.4f}s; data in {time.time() - t0:.1f}s")
+        host = X.cpu().numpy() if codes == "int8" else X.view(torch.uint8).cpu().numpy()
+        return X, Xh, host, (shift, scale, enc_s, lambda C: dec(C, shift, scale))
     if W["dtype"] == "bf16":
         X = datagen.large_device(n=W["n"], d=W["d"])
         Xh = datagen.large_device(n=W["heldout"], d=W["d"], split=1)
@@ -224,6 +228,9 @@ def main() -> int:
                     help="README \"Data precision\", INT8: calibrate on the first 65536 rows, "
                          "encode on the GPU, train on the codes (exact integer search); "
                          "held-out MSE of the decoded centroids in fp32")
+    ap.add_argument("--fp8", action="store_true",
+                    help="README \"Data precision\", FP8: as --int8 with E4M3 codes (products "
+                         "in FP8, sums in fp32)")
     ap.add_argument("--print-source-sha", action="store_true")
     args = ap.parse_args()
     if args.print_source_sha:
@@ -253,18 +260,20 @@ def main() -> int:
     K = min(K, S)
     Wm = min(args.warmup, S)
     sizes = batch_sizes(rc)[:K]
-    i8 = bool(args.int8) and W["dtype"] == "f32"
-    es = 2 if W["dtype"] == "bf16" else (1 if i8 else 4)
+    codes_fmt = ("int8" if args.int8 else "fp8" if args.fp8 else "") if W["dtype"] == "f32" else ""
+    i8 = codes_fmt == "int8"
+    es = 2 if W["dtype"] == "bf16" else (1 if codes_fmt else 4)
     flops = float(sum(2.0 * b * k * d for b in sizes))
-    bsearch = bool(args.bf16_search) and W["dtype"] == "f32" and not i8
-    sdtype = "bf16" if bsearch else ("i8" if i8 else W["dtype"])   # arithmetic type of the search
-    sph = bool(args.spherical) and not i8
+    bsearch = bool(args.bf16_search) and W["dtype"] == "f32" and not codes_fmt
+    # arithmetic type of the search
+    sdtype = "bf16" if bsearch else {"int8": "i8", "fp8": "f8"}.get(codes_fmt, W["dtype"])
+    sph = bool(args.spherical) and not codes_fmt
     tag = (args.workload + ("_bf16search" if bsearch else "") + ("_spherical" if sph else "")
-           + ("_int8" if i8 else ""))
+           + (f"_{codes_fmt}" if codes_fmt else ""))
     if sph:
         args.no_ttt = True   # the Lloyd-25 target is Euclidean
 
-    X, Xh, Xhost, codes = make_data(args.workload, W, torch, i8, mm)
+    X, Xh, Xhost, codes = make_data(args.workload, W, torch, codes_fmt, mm)
 
     # warm-up (untimed)
     if Wm > 0:
@@ -326,6 +335,7 @@ def main() -> int:
                    "steps_per_run": S,
                    "search": "bf16 (fp32 rows rounded for the search; sums in fp32)" if bsearch
                    else "int8 codes (exact integer search; sums in fp32)" if i8
+                   else "FP8 E4M3 codes (FP8 products, fp32 sums)" if codes_fmt == "fp8"
                    else ("bf16" if W["dtype"] == "bf16" else "fp32 (exact)"),
                    "mode": "spherical" if sph else "euclidean"},
         "mfma_peak_frac": round(value / peak, 4),
@@ -352,14 +362,11 @@ def main() -> int:
     }
 
     if codes is not None:
-        line["config"]["int8"] = {"calibration_rows": 65536, "scale": codes[1],
-                                  "calibrate_encode_s": round(codes[2], 4)}
+        line["config"][codes_fmt] = {"calibration_rows": 65536, "scale": codes[1],
+                                     "calibrate_encode_s": round(codes[2], 4)}
 
     if not args.no_ttt:
-        dec = None
-        if codes is not None:
-            shift, scale = codes[0], codes[1]
-            dec = lambda C: mm.int8_decode(C, shift, scale)  # noqa: E731
+        dec = codes[3] if codes is not None else None
         # GPU Lloyd-25 on the same resident data, from the same starting rows:
         # the baseline e-means is timed against (and, where the oracle has no
         # stored target, the target itself)

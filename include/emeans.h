@@ -21,9 +21,9 @@
  *   - X, centroids, labels and dists are DEVICE pointers (HIP device memory on
  *     the current device), row-major and contiguous, owned by the caller. The
  *     library never copies data between host and device for the caller.
- *   - X is n x d, fp32, bf16 or int8 codes (opts->dtype). Centroids are
- *     always k x d fp32 (for int8 X: in code space). Labels are int32 in
- *     [0, k). Distances are fp32 squared L2.
+ *   - X is n x d, fp32, bf16, int8 codes or FP8 E4M3 codes (opts->dtype).
+ *     Centroids are always k x d fp32 (for code data: in code space). Labels
+ *     are int32 in [0, k). Distances are fp32 squared L2.
  *   - Work is queued on opts->stream (a hipStream_t; NULL = the null stream).
  *     emeans_train synchronises that stream before it returns (its statistics
  *     are host values); emeans_assign and emeans_batch_rows are asynchronous.
@@ -56,7 +56,15 @@ extern "C" {
  * ties to even, clamped to [-127, 127]) exactly, in integers; the distances
  * are those of the codes. Requires d <= 43919 (the integer score then fits
  * int32) and no spherical mode. */
-enum emeans_dtype { EMEANS_F32 = 0, EMEANS_BF16 = 1, EMEANS_I8 = 2 };
+/* EMEANS_F8: X holds FP8 E4M3 codes (OCP E4M3: bias 7, subnormals, no
+ * infinities, largest 448; README "Data precision", FP8) made up front by a
+ * converter (emeans_fp8_encode: the nearest E4M3 value of (x - shift) *
+ * scale, saturating at +-448). Training runs in code space as for int8; the
+ * search compares each row with the centroids rounded to the nearest E4M3
+ * value (ties to even, saturating), multiplying in FP8 and accumulating in
+ * fp32, so labels are exact only up to fp32 rounding, as for fp32 data. No
+ * spherical mode. */
+enum emeans_dtype { EMEANS_F32 = 0, EMEANS_BF16 = 1, EMEANS_I8 = 2, EMEANS_F8 = 3 };
 
 enum emeans_status {
   EMEANS_OK = 0,
@@ -110,7 +118,7 @@ typedef struct emeans_opts {
                                  checked): pass unit-norm rows for cosine semantics.
                                  emeans_assign: labels by the highest dot product with
                                  C as given, dists[i] = that similarity. fp32 or
-                                 bf16 X only (EINVAL with int8 X). */
+                                 bf16 X only (EINVAL with int8 or FP8 X). */
   int32_t lloyd;              /* 1: plain Lloyd iterations instead of e-means (the
                                  baseline of the blog's Lloyd section, the loss
                                  e-means is timed against): each of the T passes
@@ -289,6 +297,19 @@ int emeans_int8_encode(const float* X, int64_t n, int32_t d, const float* shift,
  * ENOTDEVICE, EHIP. Asynchronous on `stream`. */
 int emeans_int8_decode(const float* C, int64_t k, int32_t d, const float* shift, double scale,
                        float* out, void* stream);
+
+/* FP8 E4M3 codes: the same converter with the FP8 range. Calibration picks
+ * the largest power of two s with s r <= 448; codes are the nearest E4M3
+ * value of (x - shift) * s (difference and product in fp32), ties to the
+ * even mantissa, saturating at +-448, as E4M3 bit patterns; decoding is as
+ * for int8 (c / scale + shift in fp64). Arguments and errors as for the
+ * int8 functions. */
+int emeans_fp8_calibrate(const float* X, int64_t n, int32_t d, float* shift, double* scale,
+                         void* stream);
+int emeans_fp8_encode(const float* X, int64_t n, int32_t d, const float* shift, double scale,
+                      uint8_t* codes, void* stream);
+int emeans_fp8_decode(const float* C, int64_t k, int32_t d, const float* shift, double scale,
+                      float* out, void* stream);
 
 /* Message for the last non-zero return on this thread ("" if none). */
 const char* emeans_last_error(void);

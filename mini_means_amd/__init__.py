@@ -23,7 +23,7 @@ LIB_PATH = os.path.join(_PKG, "_lib", "libemeans.so")
 HEADER = os.path.join(os.path.dirname(_PKG), "include", "emeans.h")
 
 MAX_PASSES = 64
-F32, BF16, I8 = 0, 1, 2
+F32, BF16, I8, F8 = 0, 1, 2, 3
 LAWS = {"auto": 0, "throughput": 1, "quality": 2}
 STATUS = {0: "OK", -1: "EINVAL", -2: "EDTYPE", -3: "ENOMEM", -4: "EHIP", -5: "ENOTDEVICE"}
 
@@ -87,6 +87,9 @@ def lib() -> ctypes.CDLL:
         L.emeans_int8_calibrate.argtypes = [c_vp, c_i64, c_i32, c_vp, ctypes.POINTER(c_dbl), c_vp]
         L.emeans_int8_encode.argtypes = [c_vp, c_i64, c_i32, c_vp, c_dbl, c_vp, c_vp]
         L.emeans_int8_decode.argtypes = [c_vp, c_i64, c_i32, c_vp, c_dbl, c_vp, c_vp]
+        for f in ("emeans_fp8_calibrate", "emeans_fp8_encode", "emeans_fp8_decode"):
+            getattr(L, f).argtypes = getattr(L, f.replace("fp8", "int8")).argtypes
+            getattr(L, f).restype = ctypes.c_int
         L.emeans_last_error.restype = ctypes.c_char_p
         L.emeans_last_error.argtypes = []
         L.emeans_version.argtypes = []
@@ -161,7 +164,10 @@ def _dtype_of(X) -> int:
         return BF16
     if X.dtype == torch.int8:
         return I8
-    raise EmeansError(f"EDTYPE: {X.dtype} not supported (float32, bfloat16 or int8)")
+    if X.dtype == torch.float8_e4m3fn:
+        return F8
+    raise EmeansError(f"EDTYPE: {X.dtype} not supported (float32, bfloat16, int8 or "
+                      f"float8_e4m3fn)")
 
 
 def _stream_ptr(X, stream):
@@ -263,9 +269,7 @@ def _f32_device(A, what: str):
         raise EmeansError(f"EINVAL: {what} must be a contiguous float32 tensor on the GPU")
 
 
-def int8_calibrate(sample, stream=None):
-    """README "Data precision", INT8: per-dimension shift (d float32 tensor)
-    and power-of-two scale (float) from sample rows (n x d float32 tensor)."""
+def _calibrate(sample, stream, fn):
     import torch
     _require_device(sample)
     _f32_device(sample, "sample")
@@ -273,14 +277,12 @@ def int8_calibrate(sample, stream=None):
     shift = torch.empty((d,), dtype=torch.float32, device=sample.device)
     scale = c_dbl(0.0)
     with torch.cuda.device(sample.device):
-        s = _stream_ptr(sample, stream)
-        _check(lib().emeans_int8_calibrate(sample.data_ptr(), n, d, shift.data_ptr(),
-                                           ctypes.byref(scale), s))
+        _check(getattr(lib(), fn)(sample.data_ptr(), n, d, shift.data_ptr(), ctypes.byref(scale),
+                                  _stream_ptr(sample, stream)))
     return shift, scale.value
 
 
-def int8_encode(X, shift, scale: float, stream=None):
-    """int8 codes of X (n x d float32 tensor): clamp(rint((X - shift) * scale), +-127)."""
+def _encode(X, shift, scale, stream, fn, dtype):
     import torch
     _require_device(X)
     _f32_device(X, "X")
@@ -288,15 +290,14 @@ def int8_encode(X, shift, scale: float, stream=None):
     n, d = X.shape
     if shift.numel() != d:
         raise EmeansError("EINVAL: shift must have d entries")
-    codes = torch.empty((n, d), dtype=torch.int8, device=X.device)
+    codes = torch.empty((n, d), dtype=dtype, device=X.device)
     with torch.cuda.device(X.device):
-        _check(lib().emeans_int8_encode(X.data_ptr(), n, d, shift.data_ptr(), float(scale),
-                                        codes.data_ptr(), _stream_ptr(X, stream)))
+        _check(getattr(lib(), fn)(X.data_ptr(), n, d, shift.data_ptr(), float(scale),
+                                  codes.data_ptr(), _stream_ptr(X, stream)))
     return codes
 
 
-def int8_decode(C, shift, scale: float, stream=None):
-    """Code-space centroids (k x d float32 tensor) back to data space: C / scale + shift."""
+def _decode(C, shift, scale, stream, fn):
     import torch
     _f32_device(C, "C")
     _f32_device(shift, "shift")
@@ -305,9 +306,43 @@ def int8_decode(C, shift, scale: float, stream=None):
         raise EmeansError("EINVAL: shift must have d entries")
     out = torch.empty_like(C)
     with torch.cuda.device(C.device):
-        _check(lib().emeans_int8_decode(C.data_ptr(), k, d, shift.data_ptr(), float(scale),
-                                        out.data_ptr(), _stream_ptr(C, stream)))
+        _check(getattr(lib(), fn)(C.data_ptr(), k, d, shift.data_ptr(), float(scale),
+                                  out.data_ptr(), _stream_ptr(C, stream)))
     return out
+
+
+def int8_calibrate(sample, stream=None):
+    """README "Data precision", INT8: per-dimension shift (d float32 tensor)
+    and power-of-two scale (float) from sample rows (n x d float32 tensor)."""
+    return _calibrate(sample, stream, "emeans_int8_calibrate")
+
+
+def int8_encode(X, shift, scale: float, stream=None):
+    """int8 codes of X (n x d float32 tensor): clamp(rint((X - shift) * scale), +-127)."""
+    import torch
+    return _encode(X, shift, scale, stream, "emeans_int8_encode", torch.int8)
+
+
+def int8_decode(C, shift, scale: float, stream=None):
+    """Code-space centroids (k x d float32 tensor) back to data space: C / scale + shift."""
+    return _decode(C, shift, scale, stream, "emeans_int8_decode")
+
+
+def fp8_calibrate(sample, stream=None):
+    """README "Data precision", FP8: as int8_calibrate, for the +-448 range of E4M3."""
+    return _calibrate(sample, stream, "emeans_fp8_calibrate")
+
+
+def fp8_encode(X, shift, scale: float, stream=None):
+    """FP8 E4M3 codes of X (a float8_e4m3fn tensor): the nearest E4M3 value of
+    (X - shift) * scale, saturating at +-448."""
+    import torch
+    return _encode(X, shift, scale, stream, "emeans_fp8_encode", torch.float8_e4m3fn)
+
+
+def fp8_decode(C, shift, scale: float, stream=None):
+    """Code-space centroids back to data space: C / scale + shift."""
+    return _decode(C, shift, scale, stream, "emeans_fp8_decode")
 
 
 def batch_rows(n: int, seed: int, pass_: int, start: int, count: int, device="cuda", stream=None):
@@ -349,11 +384,14 @@ class Stream:
         self.k, self.d = start.shape
         self.n = int(n)
         self.device = start.device
-        codes = {None: F32, torch.float32: F32, torch.bfloat16: BF16, torch.int8: I8}
+        codes = {None: F32, torch.float32: F32, torch.bfloat16: BF16, torch.int8: I8,
+                 torch.float8_e4m3fn: F8}
         code = codes.get(dtype, -1)
         if code < 0:
-            raise EmeansError(f"EDTYPE: {dtype} not supported (float32, bfloat16 or int8)")
-        self.dtype = {F32: torch.float32, BF16: torch.bfloat16, I8: torch.int8}[code]
+            raise EmeansError(f"EDTYPE: {dtype} not supported (float32, bfloat16, int8 or "
+                              f"float8_e4m3fn)")
+        self.dtype = {F32: torch.float32, BF16: torch.bfloat16, I8: torch.int8,
+                      F8: torch.float8_e4m3fn}[code]
         self._stream = stream if stream is not None else torch.cuda.current_stream(self.device)
         with torch.cuda.device(self.device):
             o = _opts(code, batch_law, batch_size, alpha0, unused_threshold, finalize, profile,

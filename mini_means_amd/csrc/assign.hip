@@ -5,7 +5,7 @@
 // rows are staged through LDS (double buffered, one 128-byte slab per row);
 // each wave computes a 64 x 64 block of scores with 16x16 MFMA tiles:
 //   fp32 X: v_mfma_f32_16x16x4_f32     bf16 X: v_mfma_f32_16x16x32_bf16
-//   int8 X: v_mfma_i32_16x16x64_i8.
+//   int8 X: v_mfma_i32_16x16x64_i8     FP8 E4M3 X: v_mfma_f32_16x16x32_fp8_fp8.
 // Centroids sit on the MFMA M dimension and points on N, so after a tile each
 // lane holds four centroid scores of a single point; the running best score
 // and its index stay in registers across all panels and are merged across the
@@ -56,6 +56,12 @@ struct Fmt<2> {
   using Acc = i32x4;
   using Sc = int;
 };
+template <>
+struct Fmt<3> {
+  static constexpr int ES = 1;
+  using Acc = f32x4;
+  using Sc = float;
+};
 
 constexpr int kWM = 4;               // waves along the centroid (M) dimension
 constexpr int kWN = 2;               // waves along the point (N) dimension
@@ -86,7 +92,7 @@ __device__ __forceinline__ u32x4 load_slab16(const unsigned char* row, int col, 
       const int c = col + e;
       uint32_t v = 0u;
       if (c < d) {
-        if constexpr (DT == 2)
+        if constexpr (DT >= 2)
           v = (uint32_t)row[c];
         else if constexpr (DT == 1)
           v = (uint32_t)reinterpret_cast<const uint16_t*>(row)[c];
@@ -110,6 +116,12 @@ __device__ __forceinline__ typename Fmt<DT>::Sc sumsq16(u32x4 w) {
 #pragma unroll
       for (int b = 0; b < 4; ++b) {
         const int v = (int)(int8_t)(w[e] >> (8 * b));
+        s += v * v;
+      }
+    } else if constexpr (DT == 3) {
+#pragma unroll
+      for (int b = 0; b < 4; ++b) {
+        const float v = e4m3_to_f32((w[e] >> (8 * b)) & 0xFFu);
         s += v * v;
       }
     } else if constexpr (DT == 1) {
@@ -138,6 +150,18 @@ __device__ __forceinline__ void mfma_slice(typename Fmt<DT>::Acc (&acc)[4][4], c
         acc[mb][nb] = __builtin_amdgcn_mfma_i32_16x16x64_i8(__builtin_bit_cast(i32x4, a[mb]),
                                                             __builtin_bit_cast(i32x4, b[nb]),
                                                             acc[mb][nb], 0, 0, 0);
+  } else if constexpr (DT == 3) {
+    // two K = 32 steps: the low and the high 8 bytes of each lane's chunk
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+#pragma unroll
+      for (int mb = 0; mb < 4; ++mb)
+#pragma unroll
+        for (int nb = 0; nb < 4; ++nb) {
+          const long av = (long)(((uint64_t)a[mb][2 * h + 1] << 32) | a[mb][2 * h]);
+          const long bv = (long)(((uint64_t)b[nb][2 * h + 1] << 32) | b[nb][2 * h]);
+          acc[mb][nb] = __builtin_amdgcn_mfma_f32_16x16x32_fp8_fp8(av, bv, acc[mb][nb], 0, 0, 0);
+        }
   } else if constexpr (DT == 1) {
 #pragma unroll
     for (int mb = 0; mb < 4; ++mb)
@@ -706,12 +730,17 @@ hipError_t launch_assign(int dt, const void* X, int d, const uint32_t* rows, int
   const auto* x = static_cast<const unsigned char*>(X);
   const auto* c = static_cast<const unsigned char*>(Cs);
   const bool aligned = ((uintptr_t)X % 16 == 0) && ((uintptr_t)Cs % 16 == 0);
-  const int epv = dt == 2 ? 16 : dt == 1 ? 8 : 4;  // elements per 16 bytes
+  const int epv = dt >= 2 ? 16 : dt == 1 ? 8 : 4;  // elements per 16 bytes
   const bool ring = aligned && d % epv == 0;
   const int sm = sim ? 1 : 0;
 #define EMK_ASSIGN(KERNEL) \
   KERNEL<<<grid, block, 0, st>>>(x, d, rows, nrows, c, bias, k, labels, dists, counts, obj, sm)
-  if (dt == 2) {
+  if (dt == 3) {
+    if (ring)
+      EMK_ASSIGN(assign_ring_kernel<3>);
+    else
+      EMK_ASSIGN(assign_kernel<3>);
+  } else if (dt == 2) {
     if (ring)
       EMK_ASSIGN(assign_ring_kernel<2>);
     else

@@ -1,15 +1,16 @@
-// int8 codes of fp32 data (README "Data precision", INT8): calibration of a
-// per-dimension shift and one power-of-two scale from sample rows, encoding
-// of rows into codes, decoding of code-space centroids. All three are
-// HBM-bound elementwise or column-reduction kernels.
+// INT8 and FP8 (E4M3) codes of fp32 data (README "Data precision"):
+// calibration of a per-dimension shift and one power-of-two scale from sample
+// rows, encoding of rows into codes, decoding of code-space centroids. All
+// three are HBM-bound elementwise or column-reduction kernels.
 //
 // Calibration: the shift of dimension j is the midrange (min + max) / 2 of
 // the sample's column j (fp64, stored as fp32); r is the largest distance of
 // a sample value from its shift (fp64); the scale is the largest power of two
-// s with s r <= 127 (1 when r = 0). Encoding: code = clamp(rint((x - shift)
-// * s), -127, 127) with the subtraction and the product in fp32 (the product
-// by a power of two is exact), ties to even. Decoding: c / s + shift in fp64,
-// stored as fp32.
+// s with s r <= L (L = 127 for int8, 448 for FP8; s = 1 when r = 0).
+// Encoding: y = (x - shift) * s with the subtraction and the product in fp32
+// (the product by a power of two is exact); int8: clamp(rint(y), -127, 127);
+// FP8: the nearest E4M3 value, saturating at +-448; ties to even in both.
+// Decoding: c / s + shift in fp64, stored as fp32.
 #include "kernels.hpp"
 
 namespace emk {
@@ -79,11 +80,12 @@ __global__ __launch_bounds__(256) void calib_finish_kernel(const float* __restri
 }
 
 // r = the largest of the nparts block radii; the largest power of two s with
-// s r <= 127. With r = m 2^E, m in [0.5, 1): s = 2^e maps r to m 2^(E + e),
-// which is <= 127 = (127/128) 2^7 for E + e = 7 exactly when m <= 127/128,
-// and always for E + e = 6.
+// s r <= L. With r = m 2^E and L = mL 2^EL (m, mL in [0.5, 1)), s = 2^e maps
+// r to m 2^(E + e), which is <= L for E + e = EL exactly when m <= mL, and
+// always for E + e = EL - 1.
 __global__ __launch_bounds__(256) void calib_scale_kernel(const double* __restrict__ rpart,
-                                                          int nparts, double* scale) {
+                                                          int nparts, double bound,
+                                                          double* scale) {
   __shared__ double red[4];
   double r = 0.0;
   for (int i = threadIdx.x; i < nparts; i += 256) r = fmax(r, rpart[i]);
@@ -96,24 +98,28 @@ __global__ __launch_bounds__(256) void calib_scale_kernel(const double* __restri
     *scale = 1.0;
     return;
   }
-  int E;
+  int E, EL;
   const double m = frexp(r, &E);
-  const int e = (m <= 127.0 / 128.0 ? 7 : 6) - E;
+  const double mL = frexp(bound, &EL);
+  const int e = (m <= mL ? EL : EL - 1) - E;
   *scale = ldexp(1.0, e);
 }
 
-__device__ __forceinline__ int8_t encode_one(float x, float sh, float sc) {
+// One code (as its byte): FMT 0 int8, 1 FP8 E4M3.
+template <int FMT>
+__device__ __forceinline__ uint32_t encode_one(float x, float sh, float sc) {
   const float y = __fmul_rn(__fsub_rn(x, sh), sc);
-  return (int8_t)fminf(fmaxf(__builtin_rintf(y), -127.0f), 127.0f);
+  if constexpr (FMT == 1) return f32_to_e4m3(y);
+  return (uint32_t)(uint8_t)(int8_t)fminf(fmaxf(__builtin_rintf(y), -127.0f), 127.0f);
 }
 
 // Thread i encodes the 16 consecutive elements [16 i, 16 i + 16) of the flat
 // n x d array (VEC: four 16-byte loads, one 16-byte store); the thread past
 // the last whole group takes the remaining tail.
-template <bool VEC>
+template <bool VEC, int FMT>
 __global__ __launch_bounds__(256) void encode_kernel(const float* __restrict__ X, int64_t total,
                                                      int d, const float* __restrict__ shift,
-                                                     float sc, int8_t* __restrict__ out) {
+                                                     float sc, uint8_t* __restrict__ out) {
   const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
   const int64_t e0 = i * 16;
   if (e0 >= total) return;
@@ -129,8 +135,7 @@ __global__ __launch_bounds__(256) void encode_kernel(const float* __restrict__ X
     for (int q = 0; q < 4; ++q)
 #pragma unroll
       for (int u = 0; u < 4; ++u) {
-        const int8_t c = encode_one(v[q][u], shift[col], sc);
-        w[q] |= (uint32_t)(uint8_t)c << (8 * u);
+        w[q] |= encode_one<FMT>(v[q][u], shift[col], sc) << (8 * u);
         if (++col == d) col = 0;
       }
     *reinterpret_cast<u32x4*>(out + e0) = u32x4{w[0], w[1], w[2], w[3]};
@@ -138,7 +143,7 @@ __global__ __launch_bounds__(256) void encode_kernel(const float* __restrict__ X
   }
   const int64_t e1 = e0 + 16 < total ? e0 + 16 : total;
   for (int64_t e = e0; e < e1; ++e) {
-    out[e] = encode_one(X[e], shift[col], sc);
+    out[e] = (uint8_t)encode_one<FMT>(X[e], shift[col], sc);
     if (++col == d) col = 0;
   }
 }
@@ -159,7 +164,7 @@ size_t calib_workspace_floats(int64_t n, int d) {
 }
 
 hipError_t launch_calibrate(const float* X, int64_t n, int d, float* shift, float* work,
-                            double* scale, hipStream_t st) {
+                            double bound, double* scale, hipStream_t st) {
   const int chunks = (int)((n + kCalRows - 1) / kCalRows);
   const int nparts = (d + 255) / 256;
   float* pmin = work;
@@ -168,20 +173,28 @@ hipError_t launch_calibrate(const float* X, int64_t n, int d, float* shift, floa
   minmax_partial_kernel<<<dim3(chunks, (d + kCalCols - 1) / kCalCols), kCalCols, 0, st>>>(
       X, n, d, pmin, pmax);
   calib_finish_kernel<<<nparts, 256, 0, st>>>(pmin, pmax, chunks, d, shift, rpart);
-  calib_scale_kernel<<<1, 256, 0, st>>>(rpart, nparts, scale);
+  calib_scale_kernel<<<1, 256, 0, st>>>(rpart, nparts, bound, scale);
   return hipGetLastError();
 }
 
 hipError_t launch_encode(const float* X, int64_t n, int d, const float* shift, float scale,
-                         int8_t* codes, hipStream_t st) {
+                         int fmt, uint8_t* codes, hipStream_t st) {
   const int64_t total = n * (int64_t)d;
   if (total <= 0) return hipSuccess;
   const int64_t threads = (total + 15) / 16;
   const dim3 grid((unsigned)((threads + 255) / 256)), block(256);
-  if ((uintptr_t)X % 16 == 0 && (uintptr_t)codes % 16 == 0)
-    encode_kernel<true><<<grid, block, 0, st>>>(X, total, d, shift, scale, codes);
-  else
-    encode_kernel<false><<<grid, block, 0, st>>>(X, total, d, shift, scale, codes);
+  const bool vec = (uintptr_t)X % 16 == 0 && (uintptr_t)codes % 16 == 0;
+  if (fmt == 1) {
+    if (vec)
+      encode_kernel<true, 1><<<grid, block, 0, st>>>(X, total, d, shift, scale, codes);
+    else
+      encode_kernel<false, 1><<<grid, block, 0, st>>>(X, total, d, shift, scale, codes);
+  } else {
+    if (vec)
+      encode_kernel<true, 0><<<grid, block, 0, st>>>(X, total, d, shift, scale, codes);
+    else
+      encode_kernel<false, 0><<<grid, block, 0, st>>>(X, total, d, shift, scale, codes);
+  }
   return hipGetLastError();
 }
 

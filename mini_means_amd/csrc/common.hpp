@@ -115,6 +115,29 @@ __device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
 
 __device__ __forceinline__ float bf16_to_f32(uint16_t h) { return __uint_as_float((uint32_t)h << 16); }
 
+// FP8 E4M3 (OCP): sign bit, 4 exponent bits with bias 7, 3 mantissa bits;
+// exponent 0 holds the subnormals m * 2^-9; 0x7F / 0xFF are NaN; no
+// infinities; the largest finite value is 448.
+//
+// Decoding: the 7 low bits placed at fp32 bit 20 read as 2^(e-127) (1 + m/8)
+// for e >= 1 and as the fp32 subnormal m 2^-129 for e = 0; one exact product
+// by 2^120 gives 2^(e-7) (1 + m/8) and m 2^-9 (fp32 denormals are kept). The
+// NaN codes, which no encoder here produces, decode to +-480.
+__device__ __forceinline__ float e4m3_to_f32(uint32_t c) {
+  return __uint_as_float(((c & 0x80u) << 24) | ((c & 0x7Fu) << 20)) * 0x1p120f;
+}
+
+// Nearest E4M3 value (ties to the even mantissa), saturating at +-448; the
+// sign of a zero result follows x. Non-finite input is not supported.
+__device__ __forceinline__ uint32_t f32_to_e4m3(float x) {
+  const uint32_t sign = (__float_as_uint(x) >> 24) & 0x80u;
+  const float a = fminf(fabsf(x), 448.0f);
+  if (a < 0x1p-6f) return sign | (uint32_t)__builtin_rintf(a * 512.0f);  // 8 = 2^-6, the first normal
+  uint32_t b = __float_as_uint(a);
+  b += 0x7FFFFu + ((b >> 20) & 1u);  // round the fp32 mantissa to 3 bits, ties to even
+  return sign | (((b >> 23) - 120u) << 3) | ((b >> 20) & 7u);
+}
+
 // ---------------------------------------------------------------------------
 // reductions
 // ---------------------------------------------------------------------------

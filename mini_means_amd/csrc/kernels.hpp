@@ -11,7 +11,8 @@ namespace emk {
 // Assign: for batch slot r (row = rows ? rows[r] : r) of X, the nearest
 // centroid by maximal score x.c - |c|^2/2 (equivalent to minimal squared
 // distance). dt is the search type of X and `Cs`: 0 fp32 (Cs = C), 1 bf16
-// (Cs = bf16 C-hat), 2 int8 (Cs = int8 codes q). `bias` = -|c|^2/2 computed
+// (Cs = bf16 C-hat), 2 int8 (Cs = int8 codes q), 3 FP8 E4M3 (Cs = E4M3
+// codes of C, products accumulated in fp32). `bias` = -|c|^2/2 computed
 // from Cs as fp32, except for int8, where it holds -|q|^2 as int32 and the
 // score is the exact integer 2 x.q - |q|^2. Writes labels[r], dists[r]
 // (optional), counts[label] += 1 (optional) and obj[0] += sum of distances
@@ -36,15 +37,16 @@ hipError_t launch_sample_rows_i32(const PermKey& pk, uint64_t start, int count, 
                                   hipStream_t st);
 
 // C[j] = X[pi(j)] as fp32, j < k (rescaled to norm 1 when sph); dt is the
-// data type of X: 0 fp32, 1 bf16, 2 int8.
+// data type of X: 0 fp32, 1 bf16, 2 int8, 3 FP8 E4M3.
 hipError_t launch_init_centroids(int dt, const void* X, int d, const PermKey& pk, int k,
                                  float* C, bool sph, hipStream_t st);
 
-// bias[j] = -|c_j|^2 / 2 in the search format (0 when sph); Chat = bf16(C)
-// when non-null, else Cq = int8 codes q of C (nearest, clamped to +-127) when
-// non-null, and then bias[j] holds the int32 -|q_j|^2 (the assign contract).
+// bias[j] = -|c_j|^2 / 2 in the search format (0 when sph). At most one
+// search copy is non-null: Chat = bf16(C); Cq = int8 codes q of C (nearest,
+// clamped to +-127), and then bias[j] holds the int32 -|q_j|^2 (the assign
+// contract); Cf = E4M3 codes of C (nearest, saturating at +-448).
 hipError_t launch_prep(const float* C, int k, int d, float* bias, uint16_t* Chat, int8_t* Cq,
-                       bool sph, hipStream_t st);
+                       uint8_t* Cf, bool sph, hipStream_t st);
 
 // out[r] = bf16(X[rows[r]]) for r < nrows (rows NULL: row r), row-major.
 hipError_t launch_cast_rows(const float* X, int d, const uint32_t* rows, int nrows,
@@ -72,10 +74,10 @@ hipError_t launch_group(int dt, const void* X, int d, const uint32_t* order,
 
 // EMA update of every cluster; resets counts and s_acc for the next step;
 // pass_counts += counts; LS += s when LS is non-null; refreshes bias and the
-// search format (Chat or Cq, at most one non-null).
+// search format (Chat, Cq or Cf, at most one non-null).
 // sph: the centroids are rescaled to norm 1 and the bias is 0.
 hipError_t launch_ema(int k, int d, float a, float b, int32_t* counts, float* s_acc, float* N,
-                      float* S, float* C, float* bias, uint16_t* Chat, int8_t* Cq,
+                      float* S, float* C, float* bias, uint16_t* Chat, int8_t* Cq, uint8_t* Cf,
                       int32_t* pass_counts, float* LS, bool sph, hipStream_t st);
 
 struct ReviveArgs {
@@ -86,6 +88,7 @@ struct ReviveArgs {
   float* bias;
   uint16_t* Chat;     // bf16 search copy of C, or NULL
   int8_t* Cq;         // int8 search codes of C, or NULL
+  uint8_t* Cf;        // E4M3 search codes of C, or NULL
   double thr;
   uint64_t seed, step;
   // k-sized scratch
@@ -124,15 +127,17 @@ hipError_t launch_normalize_rows(float* C, int k, int d, hipStream_t st);
 hipError_t launch_finalize(int k, int d, const int32_t* pass_counts, const float* LS, float* C,
                            bool sph, hipStream_t st);
 
-// int8 codes (codes.hip). Calibration of shift (d fp32, device) and scale
-// (one fp64, device) from n sample rows; `work` holds
-// calib_workspace_floats(n, d) floats (8-byte aligned).
+// INT8 / FP8 codes (codes.hip). Calibration of shift (d fp32, device) and
+// scale (one fp64, device: the largest power of two s with s r <= bound)
+// from n sample rows; `work` holds calib_workspace_floats(n, d) floats
+// (8-byte aligned).
 size_t calib_workspace_floats(int64_t n, int d);
 hipError_t launch_calibrate(const float* X, int64_t n, int d, float* shift, float* work,
-                            double* scale, hipStream_t st);
-// codes = clamp(rint((X - shift) * scale), -127, 127), n x d.
+                            double bound, double* scale, hipStream_t st);
+// codes of (X - shift) * scale, n x d bytes: fmt 0 int8 (clamp(rint(.),
+// -127, 127)), fmt 1 FP8 E4M3 (nearest, saturating at +-448).
 hipError_t launch_encode(const float* X, int64_t n, int d, const float* shift, float scale,
-                         int8_t* codes, hipStream_t st);
+                         int fmt, uint8_t* codes, hipStream_t st);
 // out = C / scale + shift (fp64, stored fp32), k x d.
 hipError_t launch_decode(const float* C, int64_t k, int d, const float* shift, double scale,
                          float* out, hipStream_t st);

@@ -108,6 +108,8 @@ __global__ __launch_bounds__(256) void init_centroids_kernel(const unsigned char
       v = bf16_to_f32(reinterpret_cast<const uint16_t*>(X)[row * (uint64_t)d + e]);
     else if (bf16 == 2)
       v = (float)reinterpret_cast<const int8_t*>(X)[row * (uint64_t)d + e];
+    else if (bf16 == 3)
+      v = e4m3_to_f32(reinterpret_cast<const uint8_t*>(X)[row * (uint64_t)d + e]);
     else
       v = reinterpret_cast<const float*>(X)[row * (uint64_t)d + e];
     C[(size_t)j * d + e] = v;
@@ -116,9 +118,11 @@ __global__ __launch_bounds__(256) void init_centroids_kernel(const unsigned char
 }
 
 // One wave per centroid: bias = -|c|^2/2 in the search format, Chat = bf16(c)
-// (bf16 search) or Cq = int8 codes of c (int8 data).
+// (bf16 search), Cq = int8 codes of c (int8 data) or Cf = E4M3 codes of c
+// (FP8 data).
 __global__ __launch_bounds__(256) void prep_kernel(const float* C, int k, int d, float* bias,
-                                                   uint16_t* Chat, int8_t* Cq, int sph) {
+                                                   uint16_t* Chat, int8_t* Cq, uint8_t* Cf,
+                                                   int sph) {
   const int j = blockIdx.x * 4 + (threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
   if (j >= k) return;
@@ -135,6 +139,10 @@ __global__ __launch_bounds__(256) void prep_kernel(const float* C, int k, int d,
       Cq[(size_t)j * d + e] = q;
       nq += (int)q * (int)q;
       continue;
+    } else if (Cf) {
+      const uint32_t q = f32_to_e4m3(c);
+      Cf[(size_t)j * d + e] = (uint8_t)q;
+      c = e4m3_to_f32(q);
     }
     nrm += c * c;
   }
@@ -268,13 +276,18 @@ __global__ void scatter_kernel(const int32_t* labels, const uint32_t* rows, int 
 }
 
 // Column unit `col` of a row as fp32 values: 16 bytes of fp32 / bf16 (VEC),
-// 4 bytes of int8 (VEC), or one element.
+// 4 bytes of int8 or E4M3 codes (VEC), or one element.
 template <int DT, bool VEC>
 __device__ __forceinline__ void load_unit_dt(const unsigned char* base, int col, float* v) {
-  if constexpr (VEC && DT == 2) {
+  if constexpr (VEC && DT >= 2) {
     const uint32_t q = *reinterpret_cast<const uint32_t*>(base + (size_t)col * 4);
 #pragma unroll
-    for (int e = 0; e < 4; ++e) v[e] = (float)(int8_t)(q >> (8 * e));
+    for (int e = 0; e < 4; ++e) {
+      if constexpr (DT == 3)
+        v[e] = e4m3_to_f32((q >> (8 * e)) & 0xFFu);
+      else
+        v[e] = (float)(int8_t)(q >> (8 * e));
+    }
   } else if constexpr (VEC) {
     typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
     const u32x4 q = *reinterpret_cast<const u32x4*>(base + (size_t)col * 16);
@@ -293,6 +306,8 @@ __device__ __forceinline__ void load_unit_dt(const unsigned char* base, int col,
       v[0] = bf16_to_f32(reinterpret_cast<const uint16_t*>(base)[col]);
     else if constexpr (DT == 2)
       v[0] = (float)reinterpret_cast<const int8_t*>(base)[col];
+    else if constexpr (DT == 3)
+      v[0] = e4m3_to_f32(base[col]);
     else
       v[0] = reinterpret_cast<const float*>(base)[col];
   }
@@ -315,7 +330,7 @@ __global__ __launch_bounds__(256) void group_kernel(const unsigned char* __restr
   // element bytes: fp32 4, bf16 2, int8 1; a column unit is 16 bytes (4 for
   // int8, which keeps the rows in flight within the register budget)
   constexpr int ES = DT == 0 ? 4 : DT == 1 ? 2 : 1;
-  constexpr int UB = DT == 2 ? 4 : 16;
+  constexpr int UB = DT >= 2 ? 4 : 16;
   constexpr int EPV = VEC ? UB / ES : 1;  // elements per column unit
   constexpr int U = 8;                    // rows in flight per thread
   __shared__ float red[256 * EPV];
@@ -417,7 +432,7 @@ __global__ __launch_bounds__(256) void group_wave_kernel(const unsigned char* __
   // element bytes: fp32 4, bf16 2, int8 1; a column unit is 16 bytes (4 for
   // int8, which keeps the rows in flight within the register budget)
   constexpr int ES = DT == 0 ? 4 : DT == 1 ? 2 : 1;
-  constexpr int UB = DT == 2 ? 4 : 16;
+  constexpr int UB = DT >= 2 ? 4 : 16;
   constexpr int EPV = VEC ? UB / ES : 1;  // elements per column unit
   constexpr int U = 8;                    // rows in flight per lane
   const int lane = threadIdx.x & 63;
@@ -485,11 +500,12 @@ __global__ __launch_bounds__(256) void group_wave_kernel(const unsigned char* __
 
 // One wave per cluster: EMA of the running count and sum, centroid S/N,
 // search-format refresh, last-pass accumulation; resets counts and s_acc.
-template <int SF>  // search format kept beside C: 0 none, 1 bf16 (Chat), 2 int8 (Cq)
+// search format kept beside C: 0 none, 1 bf16 (Chat), 2 int8 (Cq), 3 E4M3 (Cf)
+template <int SF>
 __global__ __launch_bounds__(256) void ema_kernel(int k, int d, float a, float b,
                                                   int32_t* counts, float* s_acc, float* N,
                                                   float* S, float* C, float* bias,
-                                                  uint16_t* Chat, int8_t* Cq,
+                                                  uint16_t* Chat, int8_t* Cq, uint8_t* Cf,
                                                   int32_t* pass_counts, float* LS, int sph) {
   const int j = blockIdx.x * 4 + (threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
@@ -526,6 +542,10 @@ __global__ __launch_bounds__(256) void ema_kernel(int k, int d, float a, float b
       Cq[idx] = q;
       nq += (int)q * (int)q;
       continue;
+    } else if constexpr (SF == 3) {
+      const uint32_t q = f32_to_e4m3(c);
+      Cf[idx] = (uint8_t)q;
+      c = e4m3_to_f32(q);
     }
     nrm += c * c;
   }
@@ -875,6 +895,12 @@ __global__ __launch_bounds__(256) void split_kernel(ReviveArgs A) {
         A.Chat[ii] = hi;
         cj = bf16_to_f32(hj);
         ci = bf16_to_f32(hi);
+      } else if (A.Cf) {
+        const uint32_t fj = f32_to_e4m3(cj), fi = f32_to_e4m3(ci);
+        A.Cf[jj] = (uint8_t)fj;
+        A.Cf[ii] = (uint8_t)fi;
+        cj = e4m3_to_f32(fj);
+        ci = e4m3_to_f32(fi);
       } else if (A.Cq) {
         const int8_t qj = to_code_i8(cj), qi = to_code_i8(ci);
         A.Cq[jj] = qj;
@@ -1010,8 +1036,8 @@ hipError_t launch_init_centroids(int dt, const void* X, int d, const PermKey& pk
 }
 
 hipError_t launch_prep(const float* C, int k, int d, float* bias, uint16_t* Chat, int8_t* Cq,
-                       bool sph, hipStream_t st) {
-  prep_kernel<<<(k + 3) / 4, 256, 0, st>>>(C, k, d, bias, Chat, Cq, sph ? 1 : 0);
+                       uint8_t* Cf, bool sph, hipStream_t st) {
+  prep_kernel<<<(k + 3) / 4, 256, 0, st>>>(C, k, d, bias, Chat, Cq, Cf, sph ? 1 : 0);
   return hipGetLastError();
 }
 
@@ -1060,9 +1086,9 @@ hipError_t launch_group(int dt, const void* X, int d, const uint32_t* order,
   // work items: one per cluster plus at most nb / R overflow items
   const long long items = (long long)k + nb / R;
   const auto* x = static_cast<const unsigned char*>(X);
-  // a vector unit is 16 B (4 fp32, 8 bf16) or, for int8, 4 B (4 codes)
+  // a vector unit is 16 B (4 fp32, 8 bf16) or, for int8 / E4M3 codes, 4 B
   const int per = dt == 1 ? 8 : 4;
-  const bool aligned = (uintptr_t)X % (dt == 2 ? 4 : 16) == 0;
+  const bool aligned = (uintptr_t)X % (dt >= 2 ? 4 : 16) == 0;
   const bool vec = aligned && d % per == 0;
   const int ncol = vec ? d / per : d;
   const int a = add ? 1 : 0;
@@ -1070,23 +1096,28 @@ hipError_t launch_group(int dt, const void* X, int d, const uint32_t* order,
     return launch_group_dt<1>(x, d, vec, ncol, order, off, ovf, ovf_n, k, R, items, s_acc, a, st);
   if (dt == 2)
     return launch_group_dt<2>(x, d, vec, ncol, order, off, ovf, ovf_n, k, R, items, s_acc, a, st);
+  if (dt == 3)
+    return launch_group_dt<3>(x, d, vec, ncol, order, off, ovf, ovf_n, k, R, items, s_acc, a, st);
   return launch_group_dt<0>(x, d, vec, ncol, order, off, ovf, ovf_n, k, R, items, s_acc, a, st);
 }
 
 hipError_t launch_ema(int k, int d, float a, float b, int32_t* counts, float* s_acc, float* N,
-                      float* S, float* C, float* bias, uint16_t* Chat, int8_t* Cq,
+                      float* S, float* C, float* bias, uint16_t* Chat, int8_t* Cq, uint8_t* Cf,
                       int32_t* pass_counts, float* LS, bool sph, hipStream_t st) {
   const dim3 grid((k + 3) / 4), block(256);
   const int sp = sph ? 1 : 0;
+#define EMK_EMA(SF)                                                                        \
+  ema_kernel<SF><<<grid, block, 0, st>>>(k, d, a, b, counts, s_acc, N, S, C, bias, Chat, Cq, \
+                                         Cf, pass_counts, LS, sp)
   if (Chat)
-    ema_kernel<1><<<grid, block, 0, st>>>(k, d, a, b, counts, s_acc, N, S, C, bias, Chat, Cq,
-                                          pass_counts, LS, sp);
+    EMK_EMA(1);
   else if (Cq)
-    ema_kernel<2><<<grid, block, 0, st>>>(k, d, a, b, counts, s_acc, N, S, C, bias, Chat, Cq,
-                                          pass_counts, LS, sp);
+    EMK_EMA(2);
+  else if (Cf)
+    EMK_EMA(3);
   else
-    ema_kernel<0><<<grid, block, 0, st>>>(k, d, a, b, counts, s_acc, N, S, C, bias, Chat, Cq,
-                                          pass_counts, LS, sp);
+    EMK_EMA(0);
+#undef EMK_EMA
   return hipGetLastError();
 }
 

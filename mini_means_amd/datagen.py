@@ -221,11 +221,36 @@ def codes_i8(n: int = 1_000_000, d: int = 768, m: int = 4096, spread: float = 80
     return _chunked(n, d, np.int8, fill)
 
 
+def codes_e4m3(n: int = 1_000_000, d: int = 768, m: int = 1024, sigma: float = 2.0,
+               seed: int = 109, split: int = 0) -> np.ndarray:
+    """FP8 E4M3 codes of clustered data (README "Data precision", FP8 input),
+    drawn directly as bit patterns: each of m centres has, per dimension, a
+    sign bit and a magnitude code in [24, 112] (E4M3 codes grow with the
+    value, so nearby codes are nearby values); a row of a centre keeps its
+    signs and moves each magnitude code by a rounded Gaussian of s.d. sigma,
+    clamped to [0, 126] (126 = 0x7E, the largest finite code). Zipf(1.1)
+    weights."""
+    r0 = _rng(seed, 0)
+    mag = r0.integers(24, 113, size=(m, d))
+    sgn = r0.integers(0, 2, size=(m, d)) * 0x80
+    w = zipf_weights(m, 1.1)
+
+    def fill(c, lo, hi, out):
+        r = _rng(seed, 1 + split, c)
+        comp = r.choice(m, size=hi - lo, p=w)
+        noise = np.rint(r.standard_normal((hi - lo, d)) * sigma).astype(np.int64)
+        out[:] = (sgn[comp] | np.clip(mag[comp] + noise, 0, 126)).astype(np.uint8)
+
+    return _chunked(n, d, np.uint8, fill)
+
+
 def make(gen: str, n: int, d: int, split: int = 0, **kw) -> np.ndarray:
     """Host data for a generator name at any (n, d) (fp32, bf16 bits for
-    'large', int8 for 'codes')."""
+    'large', int8 for 'codes', E4M3 bits for 'codes8')."""
     if gen == "codes":
         return codes_i8(n=n, d=d, split=split, **kw)
+    if gen == "codes8":
+        return codes_e4m3(n=n, d=d, split=split, **kw)
     if gen == "tiny":
         return tiny(n=n, d=d, split=split, **kw)
     if gen == "embedding":

@@ -21,12 +21,33 @@ import oracle
 
 GAP_TOL = 1e-5
 DIST_TOL = 1e-5
+# FP8 E4M3 data: single products are exact, but the matrix unit sums them
+# with about 13 bits (measured: at most 1.6e-4 of sum |x_i q_i| for d = 32 to
+# 2048). A distance then errs by at most 2 e sum |x_i q_i| <= e (|x|^2 + |q|^2);
+# the band and the distance tolerance take 5e-4, three times the measured e.
+F8_TOL = 5e-4
+
+
+def _tol(X, base):
+    return F8_TOL if X.dtype == np.uint8 else base
+
+
+def obj_atol(X) -> float:
+    """Absolute tolerance of a mean distance (stats obj): 0 except for FP8
+    data, where each distance may err by F8_TOL (|x|^2 + |q|^2); with |q|^2
+    at most twice |x|^2 on average that is F8_TOL * 3 * mean |x|^2."""
+    if X.dtype != np.uint8:
+        return 0.0
+    Xf = oracle.to_f32(X).astype(np.float64)
+    return F8_TOL * 3.0 * float(np.mean(np.einsum("ij,ij->i", Xf, Xf)))
 
 
 def to_device(X: np.ndarray, device="cuda"):
     import torch
     if X.dtype == np.uint16:
         return torch.from_numpy(X.view(np.int16)).to(device).view(torch.bfloat16)
+    if X.dtype == np.uint8:        # FP8 E4M3 bit patterns
+        return torch.from_numpy(X).to(device).view(torch.float8_e4m3fn)
     return torch.from_numpy(X).to(device)
 
 
@@ -79,6 +100,23 @@ def int8_flip_bound(X, rows, C32, labels, rel=1e-5):
     return np.sum(np.where(near, 2.0 * np.abs(Xf - q) + 1.0, 0.0), axis=1)
 
 
+def e4m3_flip_bound(X, rows, C32, labels, rel=1e-5):
+    """The E4M3 analogue of bf16_flip_bound: a running-centroid coordinate
+    that rounds differently at c - delta and c + delta (delta = rel x
+    max(|c|, RMS coordinate)) lies near a rounding boundary and may round to
+    either neighbour; each such coordinate can move the distance by at most
+    (2|x - q| + r) r, with r the gap between the two candidates."""
+    Xf = oracle.to_f32(X if rows is None else X[rows]).astype(np.float64)
+    c64 = np.ascontiguousarray(C32[labels], dtype=np.float32).astype(np.float64)
+    q = oracle.e4m3_round(c64).astype(np.float64)
+    rms = np.sqrt(np.mean(c64 * c64, axis=1, keepdims=True))
+    delta = rel * np.maximum(np.abs(c64), rms)
+    lo = oracle.e4m3_round(c64 - delta).astype(np.float64)
+    hi = oracle.e4m3_round(c64 + delta).astype(np.float64)
+    r = np.abs(hi - lo)
+    return np.sum((2.0 * np.abs(Xf - q) + r) * r, axis=1)
+
+
 def check_labels(X, Cs, rows, given, olab, d1, d2, given_dist=None, what="", C32=None,
                  dot=False):
     """Check labels `given` against the oracle's (olab, d1, d2) on the same rows.
@@ -93,9 +131,11 @@ def check_labels(X, Cs, rows, given, olab, d1, d2, given_dist=None, what="", C32
     if given_dist is None:
         given_dist = oracle.dist_to(X, Cs, given, rows)
     sc = scale_of(X, Cs, rows, olab)
-    band = GAP_TOL * sc
+    band = _tol(X, GAP_TOL) * sc
     if C32 is not None and X.dtype == np.int8:
         band = (band + int8_flip_bound(X, rows, C32, olab) + int8_flip_bound(X, rows, C32, given))
+    elif C32 is not None and X.dtype == np.uint8:
+        band = (band + e4m3_flip_bound(X, rows, C32, olab) + e4m3_flip_bound(X, rows, C32, given))
     elif C32 is not None:
         band = (band + bf16_flip_bound(X, rows, C32, olab, dot=dot)
                 + bf16_flip_bound(X, rows, C32, given, dot=dot))
@@ -113,7 +153,7 @@ def check_dists(X, Cs, rows, labels, dists, what=""):
     ref = oracle.dist_to(X, Cs, labels, rows)
     sc = scale_of(X, Cs, rows, labels)
     err = np.abs(dists.astype(np.float64) - ref)
-    assert np.all(err <= DIST_TOL * sc + 1e-30), (
+    assert np.all(err <= _tol(X, DIST_TOL) * sc + 1e-30), (
         f"{what}: distance error {err.max():.3e} (scale {sc[np.argmax(err)]:.3e})")
     assert np.all(dists >= 0)
 
@@ -160,7 +200,8 @@ def lockstep(X: np.ndarray, out, k: int, T: float, seed: int, sample: int = 0,
         dec, und, diff = check_labels(Xs, chk["C"], chk["rows"], chk["given"], chk["oracle"],
                                       chk["d1"], chk["d2"], chk["given_dist"],
                                       what=f"step {chk['t']}",
-                                      C32=chk["C32"] if Xs.dtype in (np.uint16, np.int8)
+                                      C32=chk["C32"] if Xs.dtype in (np.uint16, np.int8,
+                                                                     np.uint8)
                                       else None,
                                       dot=chk.get("spherical", False))
         summary["decided"] += dec

@@ -177,6 +177,40 @@ def test_assign_int8_rules(mm):
         mm.assign(X[:, :16].contiguous(), C[:, :16].contiguous(), spherical=True)
 
 
+CASES_F8 = [(2000, 768, 300), (1000, 64, 129), (777, 48, 50), (500, 37, 20), (300, 256, 1),
+            (600, 1040, 257), (3000, 128, 1000)]
+
+
+@pytest.mark.parametrize("n,d,k", CASES_F8)
+def test_assign_fp8(mm, n, d, k):
+    """FP8 E4M3 codes: the search uses the centroids rounded to E4M3 (ties to
+    even, saturating; a few coordinates set past the range and on ties)."""
+    X = datagen.codes_e4m3(n, d, m=64, seed=25)
+    C = _centroids(X, k, 11)
+    C[0, : min(d, 4)] = np.array([500.0, -1e4, 1.0625, -1.1875], np.float32)[: min(d, 4)]
+    lab, dist = _run(mm, X, C)
+    Cs = oracle.e4m3_round(C)
+    olab, d1, d2 = oracle.assign(X, Cs)
+    check_labels(X, Cs, None, lab, olab, d1, d2, what=f"fp8 {n}x{d} k={k}")
+    check_dists(X, Cs, None, lab, dist, what=f"fp8 {n}x{d} k={k}")
+
+
+def test_assign_fp8_misaligned_and_rules(mm):
+    import torch
+    n, d, k = 700, 64, 90
+    X = datagen.codes_e4m3(n, d, m=32, seed=29)
+    C = _centroids(X, k, 12)
+    buf = torch.empty(n * d + 1, dtype=torch.uint8, device="cuda")
+    Xd = buf[1:].view(n, d)
+    Xd.copy_(torch.from_numpy(X).cuda())
+    lab, dist = mm.assign(Xd.view(torch.float8_e4m3fn), torch.from_numpy(C).cuda())
+    Cs = oracle.e4m3_round(C)
+    olab, d1, d2 = oracle.assign(X, Cs)
+    check_labels(X, Cs, None, lab.cpu().numpy(), olab, d1, d2, what="fp8 misaligned")
+    with pytest.raises(mm.EmeansError, match="EINVAL"):
+        mm.assign(to_device(X), torch.from_numpy(C).cuda(), spherical=True)
+
+
 @pytest.mark.parametrize("n,d,k", CASES_BF16)
 def test_assign_bf16(mm, n, d, k):
     X = datagen.large_host(n, d=d, m=64, seed=13)

@@ -1,6 +1,7 @@
-"""int8 codes (README "Data precision", INT8) on the GPU against the oracle:
-calibration, encoding and decoding are exact (the same fp32 / fp64
-operations, elementwise), so every output must equal the oracle's."""
+"""INT8 and FP8 E4M3 codes (README "Data precision") on the GPU against the
+oracle: calibration, encoding and decoding are exact (the same fp32 / fp64
+operations and the same rounding, elementwise), so every output must equal
+the oracle's."""
 import numpy as np
 import pytest
 
@@ -111,3 +112,54 @@ def test_train_on_codes_end_to_end(mm):
     mse_codes = oracle.mse(X, C)
     res32 = oracle.train(X, k, T, seed)
     assert mse_codes <= 1.05 * oracle.mse(X, res32.centroids)
+
+
+FP8_CAL = [("embedding", 4000, 768), ("sift", 1500, 128), ("tiny", 513, 16), ("deep", 1025, 96),
+           ("tiny", 1, 7), ("embedding", 333, 37)]
+
+
+@pytest.mark.parametrize("gen,n,d", FP8_CAL)
+def test_fp8_calibrate_encode_decode(mm, gen, n, d):
+    import torch
+    X = datagen.make(gen, n, d, seed=33)
+    shift, scale = mm.fp8_calibrate(_dev(X))
+    oshift, oscale = oracle.fp8_calibrate(X)
+    assert np.array_equal(shift.cpu().numpy(), oshift)
+    assert scale == oscale
+    Y = datagen.make(gen, 3 * n + 5, d, seed=33, split=1)   # values may leave the range
+    codes = mm.fp8_encode(_dev(Y), shift, scale)
+    assert codes.dtype == torch.float8_e4m3fn
+    assert np.array_equal(codes.view(torch.uint8).cpu().numpy(), oracle.fp8_encode(Y, oshift, oscale))
+    C = np.ascontiguousarray(Y[: min(len(Y), 50)] * np.float32(scale) * np.float32(0.9))
+    dec = mm.fp8_decode(_dev(C), shift, scale)
+    assert np.array_equal(dec.cpu().numpy(), oracle.fp8_decode(C, oshift, oscale))
+
+
+def test_fp8_encode_ties_and_saturation(mm):
+    import torch
+    # ties to the even mantissa in the normal and the subnormal range, and
+    # saturation at +-448 (README "Data precision": clamped to the edge)
+    Z = np.array([[1.0625, 1.1875, -1.0625, 2.0 ** -10, 3 * 2.0 ** -10, 447.0, 460.0, 1e6,
+                   -1e6, 0.0, -1e-30, 2.0 ** -6, 240.0, 248.0, 0.1, -0.3]], np.float32)
+    codes = mm.fp8_encode(_dev(Z), torch.zeros(Z.shape[1], device="cuda"), 1.0)
+    got = codes.view(torch.uint8).cpu().numpy()
+    assert np.array_equal(got, oracle.fp8_encode(Z, np.zeros(Z.shape[1], np.float32), 1.0))
+
+
+def test_train_on_fp8_codes_end_to_end(mm):
+    from parity import lockstep, rel_l2
+    import torch
+    n, d, k, T, seed = 12_000, 64, 128, 2.0, 77
+    X = datagen.make("embedding", n, d, seed=41)
+    shift, scale = mm.fp8_calibrate(_dev(X[:4096]))
+    codes = mm.fp8_encode(_dev(X), shift, scale)
+    out = mm.train(codes, k, T, seed, trace=True, counts=True, capture_labels=True,
+                   split_log_cap=1 << 16)
+    Xc = codes.view(torch.uint8).cpu().numpy()
+    res, _ = lockstep(Xc, out, k, T, seed)
+    assert np.array_equal(out.counts.cpu().numpy(), res.N)
+    C = mm.fp8_decode(out.centroids, shift, scale).cpu().numpy()
+    oshift, oscale = oracle.fp8_calibrate(X[:4096])
+    assert rel_l2(C, oracle.fp8_decode(res.centroids, oshift, oscale)) <= 1e-4
+    res32 = oracle.train(X, k, T, seed)
+    assert oracle.mse(X, C) <= 1.05 * oracle.mse(X, res32.centroids)

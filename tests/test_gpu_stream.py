@@ -10,7 +10,7 @@ import pytest
 import oracle
 from mini_means_amd import datagen
 
-from parity import lockstep, rel_l2, to_device
+from parity import lockstep, obj_atol, rel_l2, to_device
 
 pytestmark = pytest.mark.gpu
 
@@ -75,6 +75,7 @@ STREAM = [
     ("emb-small-sph", "embedding", 12_000, 768, 256, 2.0, 1, dict(spherical=True)),
     ("ragged-bf16s", "tiny", 5_003, 37, 77, 1.5, 2, dict(batch_size=700, bf16_search=True)),
     ("codes-pieces", "codes", 12_000, 64, 256, 2.0, 2, {}),
+    ("f8-pieces", "codes8", 12_000, 64, 256, 2.0, 2, {}),
 ]
 
 
@@ -90,7 +91,7 @@ def test_stream_lockstep(mm, name, gen, n, d, k, T, pieces, o):
     assert np.array_equal(out.labels.cpu().numpy(), res.labels)
     tol = 1e-2 if X.dtype == np.uint16 else 1e-4
     assert rel_l2(out.centroids.cpu().numpy(), res.centroids) <= tol
-    np.testing.assert_allclose(out.stats["obj"], res.obj, rtol=1e-4)
+    np.testing.assert_allclose(out.stats["obj"], res.obj, rtol=1e-4, atol=obj_atol(X))
 
 
 def test_stream_rejects_rule_breaks(mm):

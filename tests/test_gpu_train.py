@@ -12,7 +12,7 @@ import pytest
 import oracle
 from mini_means_amd import datagen
 
-from parity import lockstep, rel_l2, to_device
+from parity import lockstep, obj_atol, rel_l2, to_device
 
 pytestmark = pytest.mark.gpu
 
@@ -59,6 +59,10 @@ LOCKSTEP = [
     ("codes-small", "codes", 12_000, 768, 256, 2.0, {}),
     ("codes-ragged", "codes", 5_003, 37, 77, 1.5, dict(batch_size=700)),
     ("codes-deep", "codes", 30_000, 96, 1024, 3.0, {}),
+    # FP8 E4M3 codes (README "Data precision", FP8)
+    ("f8-small", "codes8", 12_000, 768, 256, 2.0, {}),
+    ("f8-ragged", "codes8", 5_003, 37, 77, 1.5, dict(batch_size=700)),
+    ("f8-deep", "codes8", 30_000, 96, 1024, 3.0, {}),
 ]
 
 
@@ -85,7 +89,7 @@ def test_train_lockstep(mm, name, gen, n, d, k, T, o):
     m_gpu = oracle.mse(X, C)
     m_ref = oracle.mse(X, res.centroids)
     assert abs(m_gpu - m_ref) <= 1e-3 * m_ref
-    np.testing.assert_allclose(out.stats["obj"], res.obj, rtol=1e-4)
+    np.testing.assert_allclose(out.stats["obj"], res.obj, rtol=1e-4, atol=obj_atol(X))
     if o.get("spherical"):
         nrm = np.linalg.norm(C.astype(np.float64), axis=1)
         assert np.all((np.abs(nrm - 1.0) < 1e-6) | (nrm == 0.0))
@@ -93,7 +97,7 @@ def test_train_lockstep(mm, name, gen, n, d, k, T, o):
 
 LLOYD = [("tiny", "tiny", 10_000, 16, 64, 8), ("emb-small", "embedding", 12_000, 768, 256, 4),
          ("large-small", "large", 40_000, 128, 1024, 3), ("codes", "codes", 12_000, 96, 200, 4),
-         ("ragged", "tiny", 5_003, 37, 77, 5)]
+         ("ragged", "tiny", 5_003, 37, 77, 5), ("f8", "codes8", 12_000, 128, 200, 4)]
 
 
 @pytest.mark.parametrize("name,gen,n,d,k,iters", LLOYD, ids=[c[0] for c in LLOYD])
@@ -107,14 +111,14 @@ def test_lloyd_mode_lockstep(mm, name, gen, n, d, k, iters):
     last = {}
 
     def hook(chk):
-        C32 = chk["C32"] if X.dtype in (np.uint16, np.int8) else None
+        C32 = chk["C32"] if X.dtype in (np.uint16, np.int8, np.uint8) else None
         check_labels(X, chk["C"], None, chk["given"], chk["oracle"], chk["d1"], chk["d2"],
                      chk["given_dist"], what=f"lloyd {name} iteration {chk['t']}", C32=C32)
         last["labels"] = chk["given"]
 
     C, hist = oracle.lloyd(X, k, iters, 1234, labels_for_step=lambda i, _: trace[i],
                            check_hook=hook)
-    np.testing.assert_allclose(out.stats["obj"], hist, rtol=1e-4)
+    np.testing.assert_allclose(out.stats["obj"], hist, rtol=1e-4, atol=obj_atol(X))
     counts = np.bincount(last["labels"], minlength=k).astype(np.float32)
     assert np.array_equal(out.counts.cpu().numpy(), counts)
     assert np.array_equal(out.labels.cpu().numpy(), last["labels"])
