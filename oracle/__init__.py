@@ -226,6 +226,8 @@ def _dtype_code(X: np.ndarray) -> int:
         return 2
     if X.dtype == np.uint8:       # FP8 E4M3 codes (bit patterns)
         return 3
+    if X.dtype == np.float16:     # IEEE binary16
+        return 4
     raise TypeError(f"unsupported data type {X.dtype}")
 
 
@@ -236,6 +238,8 @@ def to_f32(X: np.ndarray) -> np.ndarray:
         return X.astype(np.float32)
     if X.dtype == np.uint8:
         return E4M3_VALUES[X]
+    if X.dtype == np.float16:
+        return X.astype(np.float32)
     return X
 
 
@@ -376,16 +380,26 @@ def fp8_decode(C: np.ndarray, shift: np.ndarray, scale: float) -> np.ndarray:
     return int8_decode(C, shift, scale)
 
 
+def f16_round(C: np.ndarray) -> np.ndarray:
+    """fp32 -> nearest IEEE binary16 (ties to even; 65520 and beyond become
+    infinity, as README "Data precision" says of FP16), returned as fp32
+    values (numpy's conversion)."""
+    with np.errstate(over="ignore"):
+        return np.asarray(C, dtype=np.float32).astype(np.float16).astype(np.float32)
+
+
 def search_centroids(C: np.ndarray, X: np.ndarray) -> np.ndarray:
-    """Centroids in the search format: bf16 for bf16 data, int8 codes for int8
-    data, E4M3 values for FP8 data (README "Data precision": only the search
-    uses the smaller format), fp32 otherwise."""
+    """Centroids in the search format: bf16 for bf16 data, fp16 for fp16 data,
+    int8 codes for int8 data, E4M3 values for FP8 data (README "Data
+    precision": only the search uses the smaller format), fp32 otherwise."""
     if X.dtype == np.uint16:
         return bf16_round(C)
     if X.dtype == np.int8:
         return int8_round(C)
     if X.dtype == np.uint8:
         return e4m3_round(C)
+    if X.dtype == np.float16:
+        return f16_round(C)
     return np.ascontiguousarray(C, dtype=np.float32)
 
 

@@ -105,7 +105,7 @@ void ref_perm_range(uint64_t n, uint64_t seed, uint64_t stream, uint64_t pass, u
 
 /* ------------------------------------------------------------------------ */
 /* Element access: dtype 0 = fp32, 1 = bf16 (stored as the high 16 bits of  */
-/* an fp32), 2 = int8 codes, 3 = FP8 E4M3 codes (OCP: sign, 4 exponent bits  */
+/* an fp32), 2 = int8 codes, 4 = IEEE fp16, 3 = FP8 E4M3 codes (OCP: sign, 4 exponent bits  */
 /* with bias 7, 3 mantissa bits; exponent 0 is subnormal, m * 2^-9; the     */
 /* pattern with all exponent and mantissa bits set is NaN, there is no inf). */
 /* ------------------------------------------------------------------------ */
@@ -116,10 +116,22 @@ static inline double e4m3_value(uint8_t c) {
   return (c & 0x80) ? -v : v;
 }
 
+/* IEEE binary16: sign, 5 exponent bits with bias 15, 10 mantissa bits;     */
+/* exponent 0 holds the subnormals m * 2^-24; exponent 31 is inf / NaN.     */
+static inline double f16_value(uint16_t h) {
+  const int e = (h >> 10) & 31, m = h & 1023;
+  double v;
+  if (e == 31) v = m ? NAN : INFINITY;
+  else if (e == 0) v = ldexp((double)m, -24);
+  else v = ldexp(1.0 + m / 1024.0, e - 15);
+  return (h & 0x8000) ? -v : v;
+}
+
 static inline double ref_elem(const void* X, int dtype, int64_t row, int32_t d, int32_t t) {
   if (dtype == 0) return (double)((const float*)X)[row * (int64_t)d + t];
   if (dtype == 2) return (double)((const int8_t*)X)[row * (int64_t)d + t];  /* int8 codes */
   if (dtype == 3) return e4m3_value(((const uint8_t*)X)[row * (int64_t)d + t]);
+  if (dtype == 4) return f16_value(((const uint16_t*)X)[row * (int64_t)d + t]);
   uint32_t bits = (uint32_t)((const uint16_t*)X)[row * (int64_t)d + t] << 16;
   float f;
   memcpy(&f, &bits, 4);

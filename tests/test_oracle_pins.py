@@ -544,6 +544,43 @@ def test_int8_calibration_and_codes():
     assert oracle.int8_round(C).tolist() == [[2.0, -0.0, 127.0, -127.0, 3.0, -2.0]]
 
 
+# FP16 (README "Data precision", FP16)
+
+def test_f16_rounding_and_decode():
+    r = oracle.f16_round(np.array([65504.0, 65519.99, 65520.0, -70000.0, 1.0 + 2.0 ** -11,
+                                   1.0 + 3 * 2.0 ** -11, 2.0 ** -24, 2.0 ** -25, 3 * 2.0 ** -25],
+                                  np.float32))
+    # the pages: values of 65,520 and above become infinity, silently
+    assert r[0] == 65504.0 and r[1] == 65504.0 and np.isinf(r[2]) and r[3] == -np.inf
+    # ties to even: 1 + 2^-11 -> 1; 1 + 3 2^-11 -> 1 + 2^-9; 2^-25 -> 0; 3 2^-25 -> 2^-23
+    assert r[4] == 1.0 and r[5] == 1.0 + 2.0 ** -9
+    assert r[6] == 2.0 ** -24 and r[7] == 0.0 and r[8] == 2.0 ** -23
+    # the C side decodes every finite binary16 pattern to its value (distance to 0)
+    bits = np.arange(1 << 16, dtype=np.uint32).astype(np.uint16)
+    X = bits.view(np.float16)
+    X = X[np.isfinite(X)].reshape(-1, 1)
+    _, d1, _ = oracle.assign(X, np.zeros((1, 1), np.float32))
+    assert np.array_equal(d1, X.astype(np.float64).ravel() ** 2)
+
+
+def test_f16_training_closing_mean_and_search():
+    S = datagen.tiny(n=5000, d=16, seed=9).astype(np.float16)
+    res = oracle.train(S, 40, 2.0, seed=5)
+    Xv = S.astype(np.float64)
+    for j in range(40):
+        m = res.labels == j
+        if m.any():
+            np.testing.assert_allclose(res.centroids[j], Xv[m].mean(axis=0), rtol=1e-6, atol=1e-6)
+    # the search uses the centroids rounded to fp16: x = 1 against
+    # 1 - 1.1 2^-12 and 1 + 1.2 2^-12: as values the first is nearer, but they
+    # round to 1 - 2^-11 and to 1 (an exact hit)
+    x1 = np.array([[1.0]], np.float16)
+    c2 = np.array([[1.0 - 1.1 * 2.0 ** -12], [1.0 + 1.2 * 2.0 ** -12]], np.float32)
+    assert oracle.assign(x1, c2)[0].tolist() == [0]
+    assert oracle.f16_round(c2).ravel().tolist() == [1.0 - 2.0 ** -11, 1.0]
+    assert oracle.assign(x1, oracle.search_centroids(c2, x1))[0].tolist() == [1]
+
+
 # FP8 E4M3 (README "Data precision", FP8)
 
 def test_e4m3_table_and_rounding_against_brute_force():
