@@ -23,7 +23,8 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, HERE)
 
 METRIC = "assign TFLOP/s (% MFMA peak) + s to Lloyd-25 MSE, 1M×768 k=4096"
-MFMA_PEAK_TFLOPS = {"f32": 157.3, "bf16": 2516.6, "i8": 5033.2, "f8": 5033.2}  # MI355X dense (i8: TOP/s)
+# MI355X dense (i8: TOP/s)
+MFMA_PEAK_TFLOPS = {"f32": 157.3, "bf16": 2516.6, "f16": 2516.6, "i8": 5033.2, "f8": 5033.2}
 HBM_PEAK_GBS = 8000.0
 
 DESCR = {
@@ -51,9 +52,9 @@ def kernel_source_sha() -> str:
 def assign_kernel_name(dtype: str, d: int) -> str:
     """The assign kernel the library launches for 16-byte aligned rows of this
     dtype and width (the dispatch rule of launch_assign in assign.hip)."""
-    if dtype == "bf16" and d in (32, 64, 96, 128):
-        return "assign_bf16_kernel (points resident in registers, 32x32x16 bf16 MFMA)"
-    if d % {"bf16": 8, "i8": 16, "f8": 16}.get(dtype, 4) == 0:
+    if dtype in ("bf16", "f16") and d in (32, 64, 96, 128):
+        return f"assign_bf16_kernel (points resident in registers, 32x32x16 {dtype} MFMA)"
+    if d % {"bf16": 8, "f16": 8, "i8": 16, "f8": 16}.get(dtype, 4) == 0:
         return "assign_ring_kernel (direct-to-LDS stage ring, 16x16 MFMA)"
     return "assign_kernel (register-staged stages, 16x16 MFMA)"
 
@@ -87,15 +88,28 @@ def batch_sizes(rc: dict) -> list:
     return out
 
 
-def make_data(name: str, W: dict, torch, codes: str = "", mm=None):
+def make_data(name: str, W: dict, torch, codes: str = "", mm=None, fp16: bool = False):
     """Training data, held-out data (fp32 or bf16, on the GPU) and the host
     copy of the training data (None when it is made on the GPU). codes
     ("int8" or "fp8"): the training rows as codes, calibrated on the first
     65536 rows (the data is an iid draw) and encoded on the GPU; returns the
     codes, the held-out data, the host codes (int8, or E4M3 bit patterns) and
-    (shift, scale, encode seconds, decode function)."""
+    (shift, scale, encode seconds, decode function). fp16: the training rows
+    converted once to fp16 on the GPU (held-out rows stay fp32)."""
     from mini_means_amd import datagen
     t0 = time.time()
+    if fp16:
+        Xf = torch.from_numpy(datagen.make(W["gen"], W["n"], W["d"])).cuda()
+        Xh = torch.from_numpy(datagen.make(W["gen"], W["heldout"], W["d"], split=1)).cuda()
+        torch.cuda.synchronize()
+        t1 = time.perf_counter()
+        X = Xf.half()
+        torch.cuda.synchronize()
+        conv_s = time.perf_counter() - t1
+        del Xf
+        log(f"fp16 data {tuple(X.shape)} converted in {conv_s:.4f}s; data in "
+            f"{time.time() - t0:.1f}s")
+        return X, Xh, X.cpu().numpy(), None
     if codes:
         cal, enc, dec = ((mm.int8_calibrate, mm.int8_encode, mm.int8_decode) if codes == "int8"
                          else (mm.fp8_calibrate, mm.fp8_encode, mm.fp8_decode))
@@ -231,6 +245,9 @@ def main() -> int:
     ap.add_argument("--fp8", action="store_true",
                     help="README \"Data precision\", FP8: as --int8 with E4M3 codes (products "
                          "in FP8, sums in fp32)")
+    ap.add_argument("--fp16", action="store_true",
+                    help="README \"Data precision\", FP16: the rows converted once to fp16 on "
+                         "the GPU (fp16 search, fp32 sums); held-out MSE in fp32")
     ap.add_argument("--print-source-sha", action="store_true")
     args = ap.parse_args()
     if args.print_source_sha:
@@ -262,18 +279,20 @@ def main() -> int:
     sizes = batch_sizes(rc)[:K]
     codes_fmt = ("int8" if args.int8 else "fp8" if args.fp8 else "") if W["dtype"] == "f32" else ""
     i8 = codes_fmt == "int8"
-    es = 2 if W["dtype"] == "bf16" else (1 if codes_fmt else 4)
+    f16 = bool(args.fp16) and W["dtype"] == "f32" and not codes_fmt
+    es = 2 if (W["dtype"] == "bf16" or f16) else (1 if codes_fmt else 4)
     flops = float(sum(2.0 * b * k * d for b in sizes))
-    bsearch = bool(args.bf16_search) and W["dtype"] == "f32" and not codes_fmt
+    bsearch = bool(args.bf16_search) and W["dtype"] == "f32" and not codes_fmt and not f16
     # arithmetic type of the search
-    sdtype = "bf16" if bsearch else {"int8": "i8", "fp8": "f8"}.get(codes_fmt, W["dtype"])
+    sdtype = ("bf16" if bsearch else "f16" if f16
+              else {"int8": "i8", "fp8": "f8"}.get(codes_fmt, W["dtype"]))
     sph = bool(args.spherical) and not codes_fmt
     tag = (args.workload + ("_bf16search" if bsearch else "") + ("_spherical" if sph else "")
-           + (f"_{codes_fmt}" if codes_fmt else ""))
+           + (f"_{codes_fmt}" if codes_fmt else "") + ("_fp16" if f16 else ""))
     if sph:
         args.no_ttt = True   # the Lloyd-25 target is Euclidean
 
-    X, Xh, Xhost, codes = make_data(args.workload, W, torch, codes_fmt, mm)
+    X, Xh, Xhost, codes = make_data(args.workload, W, torch, codes_fmt, mm, f16)
 
     # warm-up (untimed)
     if Wm > 0:
@@ -336,6 +355,7 @@ def main() -> int:
                    "search": "bf16 (fp32 rows rounded for the search; sums in fp32)" if bsearch
                    else "int8 codes (exact integer search; sums in fp32)" if i8
                    else "FP8 E4M3 codes (FP8 products, fp32 sums)" if codes_fmt == "fp8"
+                   else "fp16 data (fp16 products, fp32 sums)" if f16
                    else ("bf16" if W["dtype"] == "bf16" else "fp32 (exact)"),
                    "mode": "spherical" if sph else "euclidean"},
         "mfma_peak_frac": round(value / peak, 4),

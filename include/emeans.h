@@ -21,7 +21,7 @@
  *   - X, centroids, labels and dists are DEVICE pointers (HIP device memory on
  *     the current device), row-major and contiguous, owned by the caller. The
  *     library never copies data between host and device for the caller.
- *   - X is n x d, fp32, bf16, int8 codes or FP8 E4M3 codes (opts->dtype).
+ *   - X is n x d, fp32, bf16, fp16, int8 codes or FP8 E4M3 codes (opts->dtype).
  *     Centroids are always k x d fp32 (for code data: in code space). Labels
  *     are int32 in [0, k). Distances are fp32 squared L2.
  *   - Work is queued on opts->stream (a hipStream_t; NULL = the null stream).
@@ -64,7 +64,19 @@ extern "C" {
  * value (ties to even, saturating), multiplying in FP8 and accumulating in
  * fp32, so labels are exact only up to fp32 rounding, as for fp32 data. No
  * spherical mode. */
-enum emeans_dtype { EMEANS_F32 = 0, EMEANS_BF16 = 1, EMEANS_I8 = 2, EMEANS_F8 = 3 };
+/* EMEANS_F16: X holds IEEE binary16 values (README "Data precision", FP16:
+ * data converted once by the caller). As for bf16 data, only the search is in
+ * the 16-bit format: it compares each row with the centroids rounded to fp16
+ * (nearest, ties to even, subnormals kept; magnitudes from 65520 up become
+ * infinity, as the README's table of out-of-range values states), multiplying
+ * in fp16 and accumulating in fp32. Running sums and centroids are fp32. */
+enum emeans_dtype {
+  EMEANS_F32 = 0,
+  EMEANS_BF16 = 1,
+  EMEANS_I8 = 2,
+  EMEANS_F8 = 3,
+  EMEANS_F16 = 4
+};
 
 enum emeans_status {
   EMEANS_OK = 0,

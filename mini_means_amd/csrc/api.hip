@@ -199,18 +199,19 @@ constexpr int32_t kMaxDimI8 = 43919;  // int8 search: |2 x.q| + |q|^2 < 2^31
 
 // dtype supported; int8 codes: dimension limit and no spherical mode.
 bool dtype_known(int32_t dtype) {
-  return dtype == EMEANS_F32 || dtype == EMEANS_BF16 || dtype == EMEANS_I8 || dtype == EMEANS_F8;
+  return dtype == EMEANS_F32 || dtype == EMEANS_BF16 || dtype == EMEANS_I8 ||
+         dtype == EMEANS_F8 || dtype == EMEANS_F16;
 }
 
 int check_dtype(int32_t d, const emeans_opts* opts) {
   const int32_t dtype = opts ? opts->dtype : EMEANS_F32;
   if (!dtype_known(dtype))
-    return fail(EMEANS_EDTYPE, "dtype %d not supported (fp32 = 0, bf16 = 1, int8 = 2, fp8 = 3)",
-                dtype);
+    return fail(EMEANS_EDTYPE,
+                "dtype %d not supported (fp32 = 0, bf16 = 1, int8 = 2, fp8 = 3, fp16 = 4)", dtype);
   if (dtype == EMEANS_I8 && d > kMaxDimI8)
     return fail(EMEANS_EINVAL, "int8 data needs d <= %d (got %d)", kMaxDimI8, d);
   if ((dtype == EMEANS_I8 || dtype == EMEANS_F8) && opts->spherical)
-    return fail(EMEANS_EINVAL, "spherical e-means takes fp32 or bf16 data");
+    return fail(EMEANS_EINVAL, "spherical e-means takes fp32, bf16 or fp16 data");
   return EMEANS_OK;
 }
 
@@ -254,8 +255,8 @@ struct emeans_model {
   Recipe r;
   hipStream_t st = nullptr;
   int dt = EMEANS_F32;  // emeans_dtype of X
-  bool bf16 = false, bsearch = false, sbf = false, i8 = false, f8 = false, sph = false,
-       profile = false;
+  bool bf16 = false, bsearch = false, sbf = false, i8 = false, f8 = false, f16 = false,
+       sph = false, profile = false;
   bool no_finalize = false;
   int32_t* trace = nullptr;
   float* out_counts = nullptr;
@@ -284,7 +285,7 @@ struct emeans_model {
   int2* ovf = nullptr;
   float *s_acc = nullptr, *S = nullptr, *N = nullptr, *LS = nullptr, *bias = nullptr,
         *n0 = nullptr, *pair_n = nullptr, *wlive = nullptr;
-  uint16_t *chat = nullptr, *xb = nullptr;
+  uint16_t *chat = nullptr, *xb = nullptr;  // chat: bf16 or (fp16 data) fp16 copy of C
   int8_t* cq = nullptr;   // int8 codes of C (int8 data)
   uint8_t* cf = nullptr;  // E4M3 codes of C (FP8 data)
   // per pass: [0, P) sum of distances, [P, 3P) sum n^2 and sum n, [3P, 4P) splits (int64)
@@ -319,14 +320,17 @@ struct emeans_model {
 
   // Centroid table the search reads for rows of type dt.
   const void* search_table() const {
-    return i8 ? (const void*)cq : f8 ? (const void*)cf : bf16 ? (const void*)chat : (const void*)C;
+    return i8 ? (const void*)cq
+           : f8 ? (const void*)cf
+           : (bf16 || f16) ? (const void*)chat : (const void*)C;
   }
 
   ReviveArgs revive_args(bool count_only) {
     return ReviveArgs{k, d, N, S, C, bias, chat, cq, cf, r.thr, seed, (uint64_t)t, flags, dead, n0, rv_u,
                       pair_i, pair_n, rv_pos, rv_head, rv_cbase, rv_clen, rv_heads, rv_list,
                       rv_nheads, counters, count_only ? nullptr : dlog,
-                      count_only ? 0 : log_cap, count_only ? 1 : 0, sph ? 1 : 0, wlive};
+                      count_only ? 0 : log_cap, count_only ? 1 : 0, sph ? 1 : 0, wlive,
+                      f16 ? 1 : 0};
   }
 
   // Recipe, options and workspace; C = external (the caller's buffer) or own.
@@ -357,6 +361,7 @@ struct emeans_model {
     sbf = bf16 || bsearch;  // the search runs in bf16 against chat
     i8 = dtype == EMEANS_I8;  // the search runs in int8 against cq
     f8 = dtype == EMEANS_F8;  // the search runs in FP8 against cf
+    f16 = dtype == EMEANS_F16;  // the search runs in fp16 against chat
     sph = opts && opts->spherical;
     profile = opts && opts->profile;
     no_finalize = opts && opts->no_finalize;
@@ -398,7 +403,7 @@ struct emeans_model {
     ar.want(&N, (size_t)k);
     ar.want(&LS, kd);
     ar.want(&bias, (size_t)k);
-    if (sbf) ar.want(&chat, kd);
+    if (sbf || f16) ar.want(&chat, kd);
     if (i8) ar.want(&cq, kd);
     if (f8) ar.want(&cf, kd);
     if (bsearch) ar.want(&xb, (size_t)B * d);
@@ -462,7 +467,7 @@ struct emeans_model {
     const float b = 1.0f - a;
     const bool last = e == r.npass - 1;
     HIP_RET(timed(kUpdate, [&] {
-      return launch_ema(k, d, a, b, counts, s_acc, N, S, C, bias, chat, cq, cf, pass_counts,
+      return launch_ema(k, d, a, b, counts, s_acc, N, S, C, bias, chat, f16, cq, cf, pass_counts,
                         last ? LS : nullptr, sph, st);
     }));
     if (r.thr > 0.0 && (t + 1) % kReviveEvery == 0) {
@@ -580,8 +585,8 @@ int emeans_assign(const void* X, int64_t n, int32_t d, const float* C, int32_t k
   g_err.clear();
   const int32_t dtype = opts ? opts->dtype : EMEANS_F32;
   if (!dtype_known(dtype))
-    return fail(EMEANS_EDTYPE, "dtype %d not supported (fp32 = 0, bf16 = 1, int8 = 2, fp8 = 3)",
-                dtype);
+    return fail(EMEANS_EDTYPE,
+                "dtype %d not supported (fp32 = 0, bf16 = 1, int8 = 2, fp8 = 3, fp16 = 4)", dtype);
   if (n < 0 || n >= ((int64_t)1 << 31)) return fail(EMEANS_EINVAL, "n out of range (%lld)", (long long)n);
   if (d < 1) return fail(EMEANS_EINVAL, "d must be >= 1");
   if (k < 1) return fail(EMEANS_EINVAL, "k must be >= 1");
@@ -596,6 +601,7 @@ int emeans_assign(const void* X, int64_t n, int32_t d, const float* C, int32_t k
   const bool bf16 = dtype == EMEANS_BF16;
   const bool i8 = dtype == EMEANS_I8;
   const bool f8 = dtype == EMEANS_F8;
+  const bool f16 = dtype == EMEANS_F16;
   const bool bsearch = dtype == EMEANS_F32 && opts && opts->bf16_search;  // fp32 rows in bf16
   const bool sph = opts && opts->spherical;  // highest dot product, similarity out
   void* base = nullptr;
@@ -606,19 +612,19 @@ int emeans_assign(const void* X, int64_t n, int32_t d, const float* C, int32_t k
   uint8_t* cf = nullptr;
   Arena ar;
   ar.want(&bias, (size_t)k);
-  if (bf16 || bsearch) ar.want(&chat, (size_t)k * d);
+  if (bf16 || bsearch || f16) ar.want(&chat, (size_t)k * d);
   if (i8) ar.want(&cq, (size_t)k * d);
   if (f8) ar.want(&cf, (size_t)k * d);
   if (bsearch) ar.want(&xb, (size_t)n * d);
   rc = EMEANS_OK;
   HIP_TRY(ar.alloc(&base, st));
-  HIP_TRY(launch_prep(C, k, d, bias, chat, cq, cf, sph, st));
+  HIP_TRY(launch_prep(C, k, d, bias, chat, f16, cq, cf, sph, st));
   if (bsearch) HIP_TRY(launch_cast_rows(static_cast<const float*>(X), d, nullptr, (int)n, xb, st));
   {
     const int sdt = bsearch ? EMEANS_BF16 : dtype;
     const void* cs = i8 ? (const void*)cq
                      : f8 ? (const void*)cf
-                     : (bf16 || bsearch) ? (const void*)chat : (const void*)C;
+                     : (bf16 || bsearch || f16) ? (const void*)chat : (const void*)C;
     HIP_TRY(launch_assign(sdt, bsearch ? (const void*)xb : X, d, nullptr, (int)n, cs, bias, k,
                           labels, dists, nullptr, nullptr, sph, st));
   }
@@ -655,7 +661,7 @@ int emeans_train(const void* X, int64_t n, int32_t d, int32_t k, double T, uint6
   // starting centroids: k distinct rows (first k entries of the init permutation)
   HIP_RET(launch_init_centroids(m.dt, X, d, make_perm_key((uint64_t)n, seed, kStreamInit, 0), k,
                                 m.C, m.sph, st));
-  HIP_RET(launch_prep(m.C, k, d, m.bias, m.chat, m.cq, m.cf, m.sph, st));
+  HIP_RET(launch_prep(m.C, k, d, m.bias, m.chat, m.f16, m.cq, m.cf, m.sph, st));
 
   for (int e = 0; e < r.npass && m.t < run_steps; ++e) {
     const bool last = e == r.npass - 1;
@@ -702,7 +708,8 @@ int emeans_begin(int64_t n, int32_t d, int32_t k, double T, uint64_t seed, const
     if (e3 != hipSuccess) rc = fail(EMEANS_EHIP, "normalise: %s", hipGetErrorString(e3));
   }
   if (rc == EMEANS_OK) {
-    const hipError_t e2 = launch_prep(m->C, k, d, m->bias, m->chat, m->cq, m->cf, m->sph, m->st);
+    const hipError_t e2 =
+        launch_prep(m->C, k, d, m->bias, m->chat, m->f16, m->cq, m->cf, m->sph, m->st);
     if (e2 != hipSuccess) rc = fail(EMEANS_EHIP, "centroid prep: %s", hipGetErrorString(e2));
   }
   if (rc != EMEANS_OK) {

@@ -5,7 +5,8 @@
 // rows are staged through LDS (double buffered, one 128-byte slab per row);
 // each wave computes a 64 x 64 block of scores with 16x16 MFMA tiles:
 //   fp32 X: v_mfma_f32_16x16x4_f32     bf16 X: v_mfma_f32_16x16x32_bf16
-//   int8 X: v_mfma_i32_16x16x64_i8     FP8 E4M3 X: v_mfma_f32_16x16x32_fp8_fp8.
+//   int8 X: v_mfma_i32_16x16x64_i8     FP8 E4M3 X: v_mfma_f32_16x16x32_fp8_fp8
+//   fp16 X: v_mfma_f32_16x16x32_f16.
 // Centroids sit on the MFMA M dimension and points on N, so after a tile each
 // lane holds four centroid scores of a single point; the running best score
 // and its index stay in registers across all panels and are merged across the
@@ -34,10 +35,11 @@ namespace {
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 typedef int32_t i32x4 __attribute__((ext_vector_type(4)));
 
-// Per data type (0 fp32, 1 bf16, 2 int8): element bytes, the accumulator
-// tile and the score type.
+// Per data type (0 fp32, 1 bf16, 2 int8, 3 FP8 E4M3, 4 fp16): element bytes,
+// the accumulator tile and the score type.
 template <int DT>
 struct Fmt {
   static constexpr int ES = 4;
@@ -59,6 +61,12 @@ struct Fmt<2> {
 template <>
 struct Fmt<3> {
   static constexpr int ES = 1;
+  using Acc = f32x4;
+  using Sc = float;
+};
+template <>
+struct Fmt<4> {
+  static constexpr int ES = 2;
   using Acc = f32x4;
   using Sc = float;
 };
@@ -92,9 +100,9 @@ __device__ __forceinline__ u32x4 load_slab16(const unsigned char* row, int col, 
       const int c = col + e;
       uint32_t v = 0u;
       if (c < d) {
-        if constexpr (DT >= 2)
+        if constexpr (ES == 1)
           v = (uint32_t)row[c];
-        else if constexpr (DT == 1)
+        else if constexpr (ES == 2)
           v = (uint32_t)reinterpret_cast<const uint16_t*>(row)[c];
         else
           v = reinterpret_cast<const uint32_t*>(row)[c];
@@ -127,6 +135,10 @@ __device__ __forceinline__ typename Fmt<DT>::Sc sumsq16(u32x4 w) {
     } else if constexpr (DT == 1) {
       const float lo = __uint_as_float(w[e] << 16);
       const float hi = __uint_as_float(w[e] & 0xFFFF0000u);
+      s += lo * lo + hi * hi;
+    } else if constexpr (DT == 4) {
+      const float lo = f16_to_f32((uint16_t)(w[e] & 0xFFFFu));
+      const float hi = f16_to_f32((uint16_t)(w[e] >> 16));
       s += lo * lo + hi * hi;
     } else {
       const float f = __uint_as_float(w[e]);
@@ -170,6 +182,14 @@ __device__ __forceinline__ void mfma_slice(typename Fmt<DT>::Acc (&acc)[4][4], c
         acc[mb][nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
             __builtin_bit_cast(bf16x8, a[mb]), __builtin_bit_cast(bf16x8, b[nb]), acc[mb][nb], 0,
             0, 0);
+  } else if constexpr (DT == 4) {
+#pragma unroll
+    for (int mb = 0; mb < 4; ++mb)
+#pragma unroll
+      for (int nb = 0; nb < 4; ++nb)
+        acc[mb][nb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, a[mb]),
+                                                             __builtin_bit_cast(f16x8, b[nb]),
+                                                             acc[mb][nb], 0, 0, 0);
   } else {
 #pragma unroll
     for (int q = 0; q < 4; ++q)
@@ -723,19 +743,24 @@ hipError_t launch_assign(int dt, const void* X, int d, const uint32_t* rows, int
                          const void* Cs, const float* bias, int k, int32_t* labels, float* dists,
                          int32_t* counts, double* obj, bool sim, hipStream_t st) {
   if (nrows <= 0) return hipSuccess;
-  if (dt == 1 && assign_bf16_resident_ok(d, X, Cs))
+  if ((dt == 1 || dt == 4) && assign_bf16_resident_ok(d, X, Cs))
     return launch_assign_bf16_resident(X, d, rows, nrows, Cs, bias, k, labels, dists, counts, obj,
-                                       sim, st);
+                                       sim, dt == 4, st);
   const dim3 grid((nrows + kTP - 1) / kTP), block(kThreads);
   const auto* x = static_cast<const unsigned char*>(X);
   const auto* c = static_cast<const unsigned char*>(Cs);
   const bool aligned = ((uintptr_t)X % 16 == 0) && ((uintptr_t)Cs % 16 == 0);
-  const int epv = dt >= 2 ? 16 : dt == 1 ? 8 : 4;  // elements per 16 bytes
+  const int epv = (dt == 2 || dt == 3) ? 16 : (dt == 1 || dt == 4) ? 8 : 4;  // per 16 bytes
   const bool ring = aligned && d % epv == 0;
   const int sm = sim ? 1 : 0;
 #define EMK_ASSIGN(KERNEL) \
   KERNEL<<<grid, block, 0, st>>>(x, d, rows, nrows, c, bias, k, labels, dists, counts, obj, sm)
-  if (dt == 3) {
+  if (dt == 4) {
+    if (ring)
+      EMK_ASSIGN(assign_ring_kernel<4>);
+    else
+      EMK_ASSIGN(assign_kernel<4>);
+  } else if (dt == 3) {
     if (ring)
       EMK_ASSIGN(assign_ring_kernel<3>);
     else

@@ -1,5 +1,7 @@
-// Nearest-centroid assignment for bf16 data of small dimension (d = 16 * KS,
-// d <= 128) on gfx950: points resident in registers, centroids streamed.
+// Nearest-centroid assignment for bf16 or fp16 data of small dimension
+// (d = 16 * KS, d <= 128) on gfx950: points resident in registers, centroids
+// streamed. The two 16-bit formats differ only in the decode of |x|^2 and in
+// the MFMA (v_mfma_f32_32x32x16_bf16 or _f16, same operand layout).
 //
 // At d = 128 a bf16 point row is 256 bytes, so a wave can keep 64 points as
 // MFMA B operands in registers (64 VGPRs) for the whole sweep over the
@@ -22,6 +24,7 @@ namespace {
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 
 constexpr int kPB = 2;                  // 32-point blocks per wave
 constexpr int kWaves = 8;               // two waves per SIMD: one folds while the other multiplies
@@ -34,7 +37,7 @@ constexpr int kStride = kRowB + 16;     // 16 consecutive rows hit 16 disjoint 4
 
 __device__ __forceinline__ float max3f(float a, float b, float c) { return fmaxf(fmaxf(a, b), c); }
 
-template <int KS>
+template <int KS, bool F16>
 __global__ __launch_bounds__(kThreads, 1) void assign_bf16_kernel(
     const uint16_t* __restrict__ X, const uint32_t* __restrict__ rows, int nrows,
     const uint16_t* __restrict__ Chat, const float* __restrict__ bias, int k,
@@ -69,8 +72,9 @@ __global__ __launch_bounds__(kThreads, 1) void assign_bf16_kernel(
       pB[pb][ks] = *reinterpret_cast<const u32x4*>(row + 32 * ks + 16 * half);
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        const float lo = __uint_as_float(pB[pb][ks][e] << 16);
-        const float hi = __uint_as_float(pB[pb][ks][e] & 0xFFFF0000u);
+        const uint32_t w = pB[pb][ks][e];
+        const float lo = half_to_f32((uint16_t)(w & 0xFFFFu), F16);
+        const float hi = half_to_f32((uint16_t)(w >> 16), F16);
         s += lo * lo + hi * hi;
       }
     }
@@ -140,10 +144,16 @@ __global__ __launch_bounds__(kThreads, 1) void assign_bf16_kernel(
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks)
 #pragma unroll
-      for (int pb = 0; pb < kPB; ++pb)
-        acc[pb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, o.a[ks]),
-                                                          __builtin_bit_cast(bf16x8, pB[pb][ks]),
-                                                          acc[pb], 0, 0, 0);
+      for (int pb = 0; pb < kPB; ++pb) {
+        if constexpr (F16)
+          acc[pb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, o.a[ks]),
+                                                           __builtin_bit_cast(f16x8, pB[pb][ks]),
+                                                           acc[pb], 0, 0, 0);
+        else
+          acc[pb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, o.a[ks]),
+                                                            __builtin_bit_cast(bf16x8, pB[pb][ks]),
+                                                            acc[pb], 0, 0, 0);
+      }
   };
   // Fold a finished block into the running best: the max m of the 16 scores
   // per point; only when some lane of the wave improves on its best does the
@@ -250,29 +260,36 @@ bool assign_bf16_resident_ok(int d, const void* X, const void* Chat) {
 hipError_t launch_assign_bf16_resident(const void* X, int d, const uint32_t* rows, int nrows,
                                        const void* Chat, const float* bias, int k,
                                        int32_t* labels, float* dists, int32_t* counts,
-                                       double* obj, bool sim, hipStream_t st) {
+                                       double* obj, bool sim, bool f16, hipStream_t st) {
   if (nrows <= 0) return hipSuccess;
   const dim3 grid((nrows + kTP - 1) / kTP), block(kThreads);
   const auto* x = static_cast<const uint16_t*>(X);
   const auto* c = static_cast<const uint16_t*>(Chat);
+  const int sm = sim ? 1 : 0;
+#define EMK_RES(KS)                                                                           \
+  do {                                                                                        \
+    if (f16)                                                                                  \
+      assign_bf16_kernel<KS, true>                                                            \
+          <<<grid, block, 0, st>>>(x, rows, nrows, c, bias, k, labels, dists, counts, obj, sm); \
+    else                                                                                      \
+      assign_bf16_kernel<KS, false>                                                           \
+          <<<grid, block, 0, st>>>(x, rows, nrows, c, bias, k, labels, dists, counts, obj, sm); \
+  } while (0)
   switch (d) {
     case 32:
-      assign_bf16_kernel<2><<<grid, block, 0, st>>>(x, rows, nrows, c, bias, k, labels, dists, counts, obj,
-                                                     sim ? 1 : 0);
+      EMK_RES(2);
       break;
     case 64:
-      assign_bf16_kernel<4><<<grid, block, 0, st>>>(x, rows, nrows, c, bias, k, labels, dists, counts, obj,
-                                                     sim ? 1 : 0);
+      EMK_RES(4);
       break;
     case 96:
-      assign_bf16_kernel<6><<<grid, block, 0, st>>>(x, rows, nrows, c, bias, k, labels, dists, counts, obj,
-                                                     sim ? 1 : 0);
+      EMK_RES(6);
       break;
     default:
-      assign_bf16_kernel<8><<<grid, block, 0, st>>>(x, rows, nrows, c, bias, k, labels, dists, counts, obj,
-                                                     sim ? 1 : 0);
+      EMK_RES(8);
       break;
   }
+#undef EMK_RES
   return hipGetLastError();
 }
 

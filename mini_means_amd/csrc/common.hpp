@@ -115,6 +115,25 @@ __device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
 
 __device__ __forceinline__ float bf16_to_f32(uint16_t h) { return __uint_as_float((uint32_t)h << 16); }
 
+// IEEE binary16 storage: the hardware conversion rounds to nearest, ties to
+// even, keeps subnormals and overflows to infinity (finite range +-65504).
+__device__ __forceinline__ uint16_t f32_to_f16_rne(float f) {
+  return __builtin_bit_cast(uint16_t, (_Float16)f);
+}
+
+__device__ __forceinline__ float f16_to_f32(uint16_t h) {
+  return (float)__builtin_bit_cast(_Float16, h);
+}
+
+// Search copy of a centroid coordinate in bf16 (f16 false) or fp16 bits.
+__device__ __forceinline__ uint16_t to_half_rne(float f, bool f16) {
+  return f16 ? f32_to_f16_rne(f) : f32_to_bf16_rne(f);
+}
+
+__device__ __forceinline__ float half_to_f32(uint16_t h, bool f16) {
+  return f16 ? f16_to_f32(h) : bf16_to_f32(h);
+}
+
 // FP8 E4M3 (OCP): sign bit, 4 exponent bits with bias 7, 3 mantissa bits;
 // exponent 0 holds the subnormals m * 2^-9; 0x7F / 0xFF are NaN; no
 // infinities; the largest finite value is 448.

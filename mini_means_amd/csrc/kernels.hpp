@@ -12,23 +12,23 @@ namespace emk {
 // centroid by maximal score x.c - |c|^2/2 (equivalent to minimal squared
 // distance). dt is the search type of X and `Cs`: 0 fp32 (Cs = C), 1 bf16
 // (Cs = bf16 C-hat), 2 int8 (Cs = int8 codes q), 3 FP8 E4M3 (Cs = E4M3
-// codes of C, products accumulated in fp32). `bias` = -|c|^2/2 computed
+// codes of C, products accumulated in fp32), 4 fp16 (Cs = fp16 C-hat). `bias` = -|c|^2/2 computed
 // from Cs as fp32, except for int8, where it holds -|q|^2 as int32 and the
 // score is the exact integer 2 x.q - |q|^2. Writes labels[r], dists[r]
 // (optional), counts[label] += 1 (optional) and obj[0] += sum of distances
-// (optional). With `sim` (spherical e-means, bias = 0; fp32 or bf16 only)
+// (optional). With `sim` (spherical e-means, bias = 0; fp32, bf16 or fp16)
 // dists[r] is the similarity x.c and obj adds 2 - 2 x similarity.
 hipError_t launch_assign(int dt, const void* X, int d, const uint32_t* rows, int nrows,
                          const void* Cs, const float* bias, int k, int32_t* labels, float* dists,
                          int32_t* counts, double* obj, bool sim, hipStream_t st);
 
-// bf16 data of dimension 32, 64, 96 or 128: points resident in registers,
-// 32x32x16 bf16 MFMA tiles (same contract as launch_assign).
+// bf16 (f16 false) or fp16 data of dimension 32, 64, 96 or 128: points
+// resident in registers, 32x32x16 MFMA tiles (same contract as launch_assign).
 bool assign_bf16_resident_ok(int d, const void* X, const void* Chat);
 hipError_t launch_assign_bf16_resident(const void* X, int d, const uint32_t* rows, int nrows,
                                        const void* Chat, const float* bias, int k,
                                        int32_t* labels, float* dists, int32_t* counts,
-                                       double* obj, bool sim, hipStream_t st);
+                                       double* obj, bool sim, bool f16, hipStream_t st);
 
 // rows[r] = pi(start + r) for the keyed permutation pk.
 hipError_t launch_sample_rows(const PermKey& pk, uint64_t start, int count, uint32_t* rows,
@@ -37,16 +37,17 @@ hipError_t launch_sample_rows_i32(const PermKey& pk, uint64_t start, int count, 
                                   hipStream_t st);
 
 // C[j] = X[pi(j)] as fp32, j < k (rescaled to norm 1 when sph); dt is the
-// data type of X: 0 fp32, 1 bf16, 2 int8, 3 FP8 E4M3.
+// data type of X: 0 fp32, 1 bf16, 2 int8, 3 FP8 E4M3, 4 fp16.
 hipError_t launch_init_centroids(int dt, const void* X, int d, const PermKey& pk, int k,
                                  float* C, bool sph, hipStream_t st);
 
 // bias[j] = -|c_j|^2 / 2 in the search format (0 when sph). At most one
-// search copy is non-null: Chat = bf16(C); Cq = int8 codes q of C (nearest,
-// clamped to +-127), and then bias[j] holds the int32 -|q_j|^2 (the assign
-// contract); Cf = E4M3 codes of C (nearest, saturating at +-448).
-hipError_t launch_prep(const float* C, int k, int d, float* bias, uint16_t* Chat, int8_t* Cq,
-                       uint8_t* Cf, bool sph, hipStream_t st);
+// search copy is non-null: Chat = bf16(C), or fp16(C) with chat_f16; Cq =
+// int8 codes q of C (nearest, clamped to +-127), and then bias[j] holds the
+// int32 -|q_j|^2 (the assign contract); Cf = E4M3 codes of C (nearest,
+// saturating at +-448).
+hipError_t launch_prep(const float* C, int k, int d, float* bias, uint16_t* Chat, bool chat_f16,
+                       int8_t* Cq, uint8_t* Cf, bool sph, hipStream_t st);
 
 // out[r] = bf16(X[rows[r]]) for r < nrows (rows NULL: row r), row-major.
 hipError_t launch_cast_rows(const float* X, int d, const uint32_t* rows, int nrows,
@@ -77,8 +78,8 @@ hipError_t launch_group(int dt, const void* X, int d, const uint32_t* order,
 // search format (Chat, Cq or Cf, at most one non-null).
 // sph: the centroids are rescaled to norm 1 and the bias is 0.
 hipError_t launch_ema(int k, int d, float a, float b, int32_t* counts, float* s_acc, float* N,
-                      float* S, float* C, float* bias, uint16_t* Chat, int8_t* Cq, uint8_t* Cf,
-                      int32_t* pass_counts, float* LS, bool sph, hipStream_t st);
+                      float* S, float* C, float* bias, uint16_t* Chat, bool chat_f16, int8_t* Cq,
+                      uint8_t* Cf, int32_t* pass_counts, float* LS, bool sph, hipStream_t st);
 
 struct ReviveArgs {
   int k, d;
@@ -86,7 +87,7 @@ struct ReviveArgs {
   float* S;
   float* C;
   float* bias;
-  uint16_t* Chat;     // bf16 search copy of C, or NULL
+  uint16_t* Chat;     // bf16 (fp16 with chat_f16) search copy of C, or NULL
   int8_t* Cq;         // int8 search codes of C, or NULL
   uint8_t* Cf;        // E4M3 search codes of C, or NULL
   double thr;
@@ -111,6 +112,7 @@ struct ReviveArgs {
   int count_only;
   int sph;            // spherical e-means: split centroids rescaled to norm 1, bias 0
   float* wlive;       // live counts (0 for dead) when k > 32768; k rounded up to 4096
+  int chat_f16;       // Chat holds fp16 rather than bf16
 };
 // Dead-cluster check and donor draws (one workgroup), then the splits of the
 // running sums, one wave per donor chain.

@@ -93,7 +93,7 @@ __device__ __forceinline__ int8_t to_code_i8(float c) {
 
 // One wave per centroid: C[j] = X[pi(j)] converted to fp32 (rescaled to norm
 // 1 for spherical e-means).
-__global__ __launch_bounds__(256) void init_centroids_kernel(const unsigned char* X, int bf16,
+__global__ __launch_bounds__(256) void init_centroids_kernel(const unsigned char* X, int dt,
                                                              int d, PermKey pk, int k, float* C,
                                                              int sph) {
   const int j = blockIdx.x * 4 + (threadIdx.x >> 6);
@@ -104,12 +104,14 @@ __global__ __launch_bounds__(256) void init_centroids_kernel(const unsigned char
   row = __shfl(row, 0, 64);
   for (int e = lane; e < d; e += 64) {
     float v;
-    if (bf16 == 1)
+    if (dt == 1)
       v = bf16_to_f32(reinterpret_cast<const uint16_t*>(X)[row * (uint64_t)d + e]);
-    else if (bf16 == 2)
+    else if (dt == 2)
       v = (float)reinterpret_cast<const int8_t*>(X)[row * (uint64_t)d + e];
-    else if (bf16 == 3)
+    else if (dt == 3)
       v = e4m3_to_f32(reinterpret_cast<const uint8_t*>(X)[row * (uint64_t)d + e]);
+    else if (dt == 4)
+      v = f16_to_f32(reinterpret_cast<const uint16_t*>(X)[row * (uint64_t)d + e]);
     else
       v = reinterpret_cast<const float*>(X)[row * (uint64_t)d + e];
     C[(size_t)j * d + e] = v;
@@ -118,10 +120,10 @@ __global__ __launch_bounds__(256) void init_centroids_kernel(const unsigned char
 }
 
 // One wave per centroid: bias = -|c|^2/2 in the search format, Chat = bf16(c)
-// (bf16 search), Cq = int8 codes of c (int8 data) or Cf = E4M3 codes of c
-// (FP8 data).
+// (bf16 search) or fp16(c) (fp16 data, hf), Cq = int8 codes of c (int8 data)
+// or Cf = E4M3 codes of c (FP8 data).
 __global__ __launch_bounds__(256) void prep_kernel(const float* C, int k, int d, float* bias,
-                                                   uint16_t* Chat, int8_t* Cq, uint8_t* Cf,
+                                                   uint16_t* Chat, int hf, int8_t* Cq, uint8_t* Cf,
                                                    int sph) {
   const int j = blockIdx.x * 4 + (threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
@@ -131,9 +133,9 @@ __global__ __launch_bounds__(256) void prep_kernel(const float* C, int k, int d,
   for (int e = lane; e < d; e += 64) {
     float c = C[(size_t)j * d + e];
     if (Chat) {
-      const uint16_t h = f32_to_bf16_rne(c);
+      const uint16_t h = to_half_rne(c, hf);
       Chat[(size_t)j * d + e] = h;
-      c = bf16_to_f32(h);
+      c = half_to_f32(h, hf);
     } else if (Cq) {
       const int8_t q = to_code_i8(c);
       Cq[(size_t)j * d + e] = q;
@@ -275,11 +277,11 @@ __global__ void scatter_kernel(const int32_t* labels, const uint32_t* rows, int 
   if (out_labels) out_labels[row] = j;
 }
 
-// Column unit `col` of a row as fp32 values: 16 bytes of fp32 / bf16 (VEC),
-// 4 bytes of int8 or E4M3 codes (VEC), or one element.
+// Column unit `col` of a row as fp32 values: 16 bytes of fp32 / bf16 / fp16
+// (VEC), 4 bytes of int8 or E4M3 codes (VEC), or one element.
 template <int DT, bool VEC>
 __device__ __forceinline__ void load_unit_dt(const unsigned char* base, int col, float* v) {
-  if constexpr (VEC && DT >= 2) {
+  if constexpr (VEC && (DT == 2 || DT == 3)) {
     const uint32_t q = *reinterpret_cast<const uint32_t*>(base + (size_t)col * 4);
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
@@ -297,6 +299,12 @@ __device__ __forceinline__ void load_unit_dt(const unsigned char* base, int col,
         v[2 * e] = __uint_as_float(q[e] << 16);
         v[2 * e + 1] = __uint_as_float(q[e] & 0xFFFF0000u);
       }
+    } else if constexpr (DT == 4) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        v[2 * e] = f16_to_f32((uint16_t)(q[e] & 0xFFFFu));
+        v[2 * e + 1] = f16_to_f32((uint16_t)(q[e] >> 16));
+      }
     } else {
 #pragma unroll
       for (int e = 0; e < 4; ++e) v[e] = __uint_as_float(q[e]);
@@ -308,6 +316,8 @@ __device__ __forceinline__ void load_unit_dt(const unsigned char* base, int col,
       v[0] = (float)reinterpret_cast<const int8_t*>(base)[col];
     else if constexpr (DT == 3)
       v[0] = e4m3_to_f32(base[col]);
+    else if constexpr (DT == 4)
+      v[0] = f16_to_f32(reinterpret_cast<const uint16_t*>(base)[col]);
     else
       v[0] = reinterpret_cast<const float*>(base)[col];
   }
@@ -327,10 +337,11 @@ __global__ __launch_bounds__(256) void group_kernel(const unsigned char* __restr
                                                     const int2* __restrict__ ovf,
                                                     const int32_t* __restrict__ ovf_n, int k,
                                                     int R, float* __restrict__ s_acc, int add) {
-  // element bytes: fp32 4, bf16 2, int8 1; a column unit is 16 bytes (4 for
-  // int8, which keeps the rows in flight within the register budget)
-  constexpr int ES = DT == 0 ? 4 : DT == 1 ? 2 : 1;
-  constexpr int UB = DT >= 2 ? 4 : 16;
+  // element bytes: fp32 4, bf16 / fp16 2, int8 / E4M3 1; a column unit is 16
+  // bytes (4 for the 1-byte codes, which keeps the rows in flight within the
+  // register budget)
+  constexpr int ES = DT == 0 ? 4 : (DT == 1 || DT == 4) ? 2 : 1;
+  constexpr int UB = ES == 1 ? 4 : 16;
   constexpr int EPV = VEC ? UB / ES : 1;  // elements per column unit
   constexpr int U = 8;                    // rows in flight per thread
   __shared__ float red[256 * EPV];
@@ -429,10 +440,11 @@ __global__ __launch_bounds__(256) void group_wave_kernel(const unsigned char* __
                                                          const int32_t* __restrict__ ovf_n,
                                                          int k, int R, float* __restrict__ s_acc,
                                                          int add) {
-  // element bytes: fp32 4, bf16 2, int8 1; a column unit is 16 bytes (4 for
-  // int8, which keeps the rows in flight within the register budget)
-  constexpr int ES = DT == 0 ? 4 : DT == 1 ? 2 : 1;
-  constexpr int UB = DT >= 2 ? 4 : 16;
+  // element bytes: fp32 4, bf16 / fp16 2, int8 / E4M3 1; a column unit is 16
+  // bytes (4 for the 1-byte codes, which keeps the rows in flight within the
+  // register budget)
+  constexpr int ES = DT == 0 ? 4 : (DT == 1 || DT == 4) ? 2 : 1;
+  constexpr int UB = ES == 1 ? 4 : 16;
   constexpr int EPV = VEC ? UB / ES : 1;  // elements per column unit
   constexpr int U = 8;                    // rows in flight per lane
   const int lane = threadIdx.x & 63;
@@ -500,7 +512,8 @@ __global__ __launch_bounds__(256) void group_wave_kernel(const unsigned char* __
 
 // One wave per cluster: EMA of the running count and sum, centroid S/N,
 // search-format refresh, last-pass accumulation; resets counts and s_acc.
-// search format kept beside C: 0 none, 1 bf16 (Chat), 2 int8 (Cq), 3 E4M3 (Cf)
+// search format kept beside C: 0 none, 1 bf16 (Chat), 2 int8 (Cq), 3 E4M3 (Cf),
+// 4 fp16 (Chat)
 template <int SF>
 __global__ __launch_bounds__(256) void ema_kernel(int k, int d, float a, float b,
                                                   int32_t* counts, float* s_acc, float* N,
@@ -533,10 +546,10 @@ __global__ __launch_bounds__(256) void ema_kernel(int k, int d, float a, float b
     }
     if (LS && n) LS[idx] += s;
     if (sph) continue;  // rescaled (and rounded to Chat) below, once the norm is known
-    if constexpr (SF == 1) {
-      const uint16_t h = f32_to_bf16_rne(c);
+    if constexpr (SF == 1 || SF == 4) {
+      const uint16_t h = to_half_rne(c, SF == 4);
       Chat[idx] = h;
-      c = bf16_to_f32(h);
+      c = half_to_f32(h, SF == 4);
     } else if constexpr (SF == 2) {
       const int8_t q = to_code_i8(c);
       Cq[idx] = q;
@@ -554,8 +567,8 @@ __global__ __launch_bounds__(256) void ema_kernel(int k, int d, float a, float b
     // spherical e-means: the running average rescaled to norm 1 (a centroid
     // without a count keeps its unit-norm value); the score is x.c, bias 0
     if (Nn > 0.0f) wave_normalize(C + base, d, lane);
-    if constexpr (SF == 1)
-      for (int e = lane; e < d; e += 64) Chat[base + e] = f32_to_bf16_rne(C[base + e]);
+    if constexpr (SF == 1 || SF == 4)
+      for (int e = lane; e < d; e += 64) Chat[base + e] = to_half_rne(C[base + e], SF == 4);
   } else {
     nrm = wave_sum(nrm);
   }
@@ -890,11 +903,12 @@ __global__ __launch_bounds__(256) void split_kernel(ReviveArgs A) {
       A.C[jj] = cj;
       A.C[ii] = ci;
       if (A.Chat) {
-        const uint16_t hj = f32_to_bf16_rne(cj), hi = f32_to_bf16_rne(ci);
+        const bool hf = A.chat_f16;
+        const uint16_t hj = to_half_rne(cj, hf), hi = to_half_rne(ci, hf);
         A.Chat[jj] = hj;
         A.Chat[ii] = hi;
-        cj = bf16_to_f32(hj);
-        ci = bf16_to_f32(hi);
+        cj = half_to_f32(hj, hf);
+        ci = half_to_f32(hi, hf);
       } else if (A.Cf) {
         const uint32_t fj = f32_to_e4m3(cj), fi = f32_to_e4m3(ci);
         A.Cf[jj] = (uint8_t)fj;
@@ -918,8 +932,8 @@ __global__ __launch_bounds__(256) void split_kernel(ReviveArgs A) {
       wave_normalize(A.C + (size_t)j * d, d, lane);
       if (A.Chat)
         for (int e = lane; e < d; e += 64) {
-          A.Chat[(size_t)i * d + e] = f32_to_bf16_rne(A.C[(size_t)i * d + e]);
-          A.Chat[(size_t)j * d + e] = f32_to_bf16_rne(A.C[(size_t)j * d + e]);
+          A.Chat[(size_t)i * d + e] = to_half_rne(A.C[(size_t)i * d + e], A.chat_f16);
+          A.Chat[(size_t)j * d + e] = to_half_rne(A.C[(size_t)j * d + e], A.chat_f16);
         }
       if (lane == 0) {
         A.bias[i] = 0.0f;
@@ -1035,9 +1049,10 @@ hipError_t launch_init_centroids(int dt, const void* X, int d, const PermKey& pk
   return hipGetLastError();
 }
 
-hipError_t launch_prep(const float* C, int k, int d, float* bias, uint16_t* Chat, int8_t* Cq,
-                       uint8_t* Cf, bool sph, hipStream_t st) {
-  prep_kernel<<<(k + 3) / 4, 256, 0, st>>>(C, k, d, bias, Chat, Cq, Cf, sph ? 1 : 0);
+hipError_t launch_prep(const float* C, int k, int d, float* bias, uint16_t* Chat, bool chat_f16,
+                       int8_t* Cq, uint8_t* Cf, bool sph, hipStream_t st) {
+  prep_kernel<<<(k + 3) / 4, 256, 0, st>>>(C, k, d, bias, Chat, chat_f16 ? 1 : 0, Cq, Cf,
+                                           sph ? 1 : 0);
   return hipGetLastError();
 }
 
@@ -1086,9 +1101,10 @@ hipError_t launch_group(int dt, const void* X, int d, const uint32_t* order,
   // work items: one per cluster plus at most nb / R overflow items
   const long long items = (long long)k + nb / R;
   const auto* x = static_cast<const unsigned char*>(X);
-  // a vector unit is 16 B (4 fp32, 8 bf16) or, for int8 / E4M3 codes, 4 B
-  const int per = dt == 1 ? 8 : 4;
-  const bool aligned = (uintptr_t)X % (dt >= 2 ? 4 : 16) == 0;
+  // a vector unit is 16 B (4 fp32, 8 bf16 / fp16) or, for int8 / E4M3 codes, 4 B
+  const bool codes = dt == 2 || dt == 3;
+  const int per = (dt == 1 || dt == 4) ? 8 : 4;
+  const bool aligned = (uintptr_t)X % (codes ? 4 : 16) == 0;
   const bool vec = aligned && d % per == 0;
   const int ncol = vec ? d / per : d;
   const int a = add ? 1 : 0;
@@ -1098,18 +1114,22 @@ hipError_t launch_group(int dt, const void* X, int d, const uint32_t* order,
     return launch_group_dt<2>(x, d, vec, ncol, order, off, ovf, ovf_n, k, R, items, s_acc, a, st);
   if (dt == 3)
     return launch_group_dt<3>(x, d, vec, ncol, order, off, ovf, ovf_n, k, R, items, s_acc, a, st);
+  if (dt == 4)
+    return launch_group_dt<4>(x, d, vec, ncol, order, off, ovf, ovf_n, k, R, items, s_acc, a, st);
   return launch_group_dt<0>(x, d, vec, ncol, order, off, ovf, ovf_n, k, R, items, s_acc, a, st);
 }
 
 hipError_t launch_ema(int k, int d, float a, float b, int32_t* counts, float* s_acc, float* N,
-                      float* S, float* C, float* bias, uint16_t* Chat, int8_t* Cq, uint8_t* Cf,
-                      int32_t* pass_counts, float* LS, bool sph, hipStream_t st) {
+                      float* S, float* C, float* bias, uint16_t* Chat, bool chat_f16, int8_t* Cq,
+                      uint8_t* Cf, int32_t* pass_counts, float* LS, bool sph, hipStream_t st) {
   const dim3 grid((k + 3) / 4), block(256);
   const int sp = sph ? 1 : 0;
 #define EMK_EMA(SF)                                                                        \
   ema_kernel<SF><<<grid, block, 0, st>>>(k, d, a, b, counts, s_acc, N, S, C, bias, Chat, Cq, \
                                          Cf, pass_counts, LS, sp)
-  if (Chat)
+  if (Chat && chat_f16)
+    EMK_EMA(4);
+  else if (Chat)
     EMK_EMA(1);
   else if (Cq)
     EMK_EMA(2);

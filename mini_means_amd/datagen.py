@@ -246,7 +246,14 @@ def codes_e4m3(n: int = 1_000_000, d: int = 768, m: int = 1024, sigma: float = 2
 
 def make(gen: str, n: int, d: int, split: int = 0, **kw) -> np.ndarray:
     """Host data for a generator name at any (n, d) (fp32, bf16 bits for
-    'large', int8 for 'codes', E4M3 bits for 'codes8')."""
+    'large', int8 for 'codes', E4M3 bits for 'codes8'). A name ending in
+    '-f16' stores that generator's rows as IEEE fp16 (numpy float16: nearest,
+    ties to even), the one-off conversion a caller makes for FP16 data."""
+    if gen.endswith("-f16"):
+        X = make(gen[:-4], n, d, split=split, **kw)
+        if X.dtype == np.uint16:
+            X = bf16_bits_to_f32(X)
+        return X.astype(np.float16)
     if gen == "codes":
         return codes_i8(n=n, d=d, split=split, **kw)
     if gen == "codes8":

@@ -5,8 +5,9 @@ Tolerances (the parity bar):
     (d2 - d1) exceeds 1e-5 relative to |x|^2 + |c_best|^2, the size of the
     quantities a distance is computed from; elsewhere the label must be one
     of the near-tied centroids (its distance within that band of the best).
-    During bf16 training the band also covers coordinates of the running
-    centroids that sit on a bf16 rounding boundary (bf16_flip_bound);
+    During low-precision training the band also covers coordinates of the
+    running centroids that sit on a rounding boundary of the search format
+    (bf16_flip_bound and its int8, E4M3 and fp16 analogues);
   * distances: within 1e-5 * (|x|^2 + |c|^2) of the oracle's fp64 distance
     to the same centroid;
   * centroids: relative L2 error 1e-4 (fp32 data) or 1e-2 (bf16 data);
@@ -26,6 +27,12 @@ DIST_TOL = 1e-5
 # 2048). A distance then errs by at most 2 e sum |x_i q_i| <= e (|x|^2 + |q|^2);
 # the band and the distance tolerance take 5e-4, three times the measured e.
 F8_TOL = 5e-4
+
+
+# search formats whose centroids are the running centroids rounded (the
+# band then covers coordinates on a rounding boundary): bf16 bits, int8
+# codes, E4M3 bits, fp16
+LOW_PRECISION = (np.uint16, np.int8, np.uint8, np.float16)
 
 
 def _tol(X, base):
@@ -100,21 +107,33 @@ def int8_flip_bound(X, rows, C32, labels, rel=1e-5):
     return np.sum(np.where(near, 2.0 * np.abs(Xf - q) + 1.0, 0.0), axis=1)
 
 
-def e4m3_flip_bound(X, rows, C32, labels, rel=1e-5):
-    """The E4M3 analogue of bf16_flip_bound: a running-centroid coordinate
-    that rounds differently at c - delta and c + delta (delta = rel x
-    max(|c|, RMS coordinate)) lies near a rounding boundary and may round to
-    either neighbour; each such coordinate can move the distance by at most
-    (2|x - q| + r) r, with r the gap between the two candidates."""
+def _round_flip_bound(X, rows, C32, labels, rnd, rel=1e-5, dot=False):
+    """A running-centroid coordinate that the search format's rounding `rnd`
+    maps differently at c - delta and c + delta (delta = rel x max(|c|, RMS
+    coordinate)) lies near a rounding boundary and may round to either
+    neighbour; each such coordinate can move the distance by at most
+    (2|x - q| + r) r, with r the gap between the two candidates (with dot,
+    the score -2 x.c of spherical e-means: by 2|x| r)."""
     Xf = oracle.to_f32(X if rows is None else X[rows]).astype(np.float64)
     c64 = np.ascontiguousarray(C32[labels], dtype=np.float32).astype(np.float64)
-    q = oracle.e4m3_round(c64).astype(np.float64)
+    q = rnd(c64).astype(np.float64)
     rms = np.sqrt(np.mean(c64 * c64, axis=1, keepdims=True))
     delta = rel * np.maximum(np.abs(c64), rms)
-    lo = oracle.e4m3_round(c64 - delta).astype(np.float64)
-    hi = oracle.e4m3_round(c64 + delta).astype(np.float64)
-    r = np.abs(hi - lo)
+    r = np.abs(rnd(c64 + delta).astype(np.float64) - rnd(c64 - delta).astype(np.float64))
+    if dot:
+        return np.sum(2.0 * np.abs(Xf) * r, axis=1)
     return np.sum((2.0 * np.abs(Xf - q) + r) * r, axis=1)
+
+
+def e4m3_flip_bound(X, rows, C32, labels, rel=1e-5):
+    """The E4M3 analogue of bf16_flip_bound."""
+    return _round_flip_bound(X, rows, C32, labels, oracle.e4m3_round, rel)
+
+
+def f16_flip_bound(X, rows, C32, labels, rel=1e-5, dot=False):
+    """The fp16 analogue of bf16_flip_bound (fp16 data: the search centroids
+    are the running centroids rounded to fp16)."""
+    return _round_flip_bound(X, rows, C32, labels, oracle.f16_round, rel, dot)
 
 
 def check_labels(X, Cs, rows, given, olab, d1, d2, given_dist=None, what="", C32=None,
@@ -136,6 +155,9 @@ def check_labels(X, Cs, rows, given, olab, d1, d2, given_dist=None, what="", C32
         band = (band + int8_flip_bound(X, rows, C32, olab) + int8_flip_bound(X, rows, C32, given))
     elif C32 is not None and X.dtype == np.uint8:
         band = (band + e4m3_flip_bound(X, rows, C32, olab) + e4m3_flip_bound(X, rows, C32, given))
+    elif C32 is not None and X.dtype == np.float16:
+        band = (band + f16_flip_bound(X, rows, C32, olab, dot=dot)
+                + f16_flip_bound(X, rows, C32, given, dot=dot))
     elif C32 is not None:
         band = (band + bf16_flip_bound(X, rows, C32, olab, dot=dot)
                 + bf16_flip_bound(X, rows, C32, given, dot=dot))
@@ -200,9 +222,7 @@ def lockstep(X: np.ndarray, out, k: int, T: float, seed: int, sample: int = 0,
         dec, und, diff = check_labels(Xs, chk["C"], chk["rows"], chk["given"], chk["oracle"],
                                       chk["d1"], chk["d2"], chk["given_dist"],
                                       what=f"step {chk['t']}",
-                                      C32=chk["C32"] if Xs.dtype in (np.uint16, np.int8,
-                                                                     np.uint8)
-                                      else None,
+                                      C32=chk["C32"] if Xs.dtype in LOW_PRECISION else None,
                                       dot=chk.get("spherical", False))
         summary["decided"] += dec
         summary["undecided"] += und

@@ -222,6 +222,71 @@ def test_assign_bf16(mm, n, d, k):
     check_dists(X, Cs, None, lab, dist, what=f"bf16 {n}x{d} k={k}")
 
 
+CASES_F16 = [("embedding", 2000, 768, 300), ("deep", 1000, 96, 129), ("sift", 1500, 128, 257),
+             ("tiny", 777, 40, 50), ("tiny", 500, 37, 20), ("embedding", 300, 256, 1),
+             ("deep", 600, 32, 70), ("sift", 900, 64, 1000), ("embedding", 513, 1040, 257)]
+
+
+@pytest.mark.parametrize("gen,n,d,k", CASES_F16)
+def test_assign_fp16(mm, gen, n, d, k):
+    """fp16 data (README "Data precision", FP16) is searched with the
+    centroids rounded to fp16; d = 32, 64, 96 and 128 take the kernel that
+    keeps the points in registers, d = 37 the unaligned path."""
+    X = datagen.make(gen + "-f16", n, d, seed=27)
+    C = _centroids(X, k, 13)
+    lab, dist = _run(mm, X, C)
+    Cs = oracle.f16_round(C)
+    olab, d1, d2 = oracle.assign(X, Cs)
+    check_labels(X, Cs, None, lab, olab, d1, d2, what=f"fp16 {gen} {n}x{d} k={k}")
+    check_dists(X, Cs, None, lab, dist, what=f"fp16 {gen} {n}x{d} k={k}")
+
+
+def test_assign_fp16_rounding_and_misaligned(mm):
+    """The search centroid is the nearest fp16 value (ties to even, subnormals
+    kept, 65519 down to 65504): from a zero row the distance is exactly the
+    square of the rounded coordinate. Then a view at an odd element offset."""
+    import torch
+    vals = [1 + 2.0 ** -11, 1 + 3 * 2.0 ** -11, -(1 + 2.0 ** -11), 65519.0, 1.5 * 2.0 ** -24,
+            3 * 2.0 ** -20, 0.1, -2049.0, 2051.0]
+    for d in (1, 8):
+        for v in vals:
+            C = np.zeros((1, d), np.float32)
+            C[0, 0] = v
+            lab, dist = _run(mm, np.zeros((3, d), np.float16), C)
+            want = np.float32(oracle.f16_round(np.float32(v))) ** 2
+            assert lab.tolist() == [0, 0, 0] and np.all(dist == want), (d, v, dist, want)
+    n, d, k = 700, 64, 90
+    X = datagen.make("embedding-f16", n, d, seed=29)
+    C = _centroids(X, k, 12)
+    buf = torch.empty(n * d + 1, dtype=torch.float16, device="cuda")
+    Xd = buf[1:].view(n, d)
+    Xd.copy_(torch.from_numpy(X).cuda())
+    lab, dist = mm.assign(Xd, torch.from_numpy(C).cuda())
+    Cs = oracle.f16_round(C)
+    olab, d1, d2 = oracle.assign(X, Cs)
+    check_labels(X, Cs, None, lab.cpu().numpy(), olab, d1, d2, what="fp16 misaligned")
+    check_dists(X, Cs, None, lab.cpu().numpy(), dist.cpu().numpy(), what="fp16 misaligned")
+
+
+@pytest.mark.parametrize("n,d,k", [(1500, 768, 300), (3000, 96, 1000), (900, 128, 257)])
+def test_assign_fp16_spherical(mm, n, d, k):
+    """Spherical e-means on fp16 data: highest dot product with the unit
+    centroids rounded to fp16, and that similarity."""
+    import torch
+    X = _unit_rows(datagen.make("embedding", n, d, seed=31)).astype(np.float16)
+    C = _unit_rows(_centroids(X, k, 14))
+    lab, sim = mm.assign(to_device(X), torch.from_numpy(C).cuda(), spherical=True)
+    lab, sim = lab.cpu().numpy(), sim.cpu().numpy()
+    Cs = oracle.f16_round(C)
+    olab, s1, s2 = oracle.assign_ip(X, Cs)
+    gd = -2.0 * oracle.dot_to(X, Cs, lab)
+    check_labels(X, Cs, None, lab, olab, -2.0 * s1, -2.0 * s2, given_dist=gd,
+                 what=f"spherical fp16 {n}x{d} k={k}")
+    Xf = oracle.to_f32(X).astype(np.float64)
+    scale = np.einsum("ij,ij->i", Xf, Xf) + np.sum(Cs[lab].astype(np.float64) ** 2, axis=1)
+    assert np.all(np.abs(sim - oracle.dot_to(X, Cs, lab)) <= 1e-5 * scale)
+
+
 def test_assign_ties_lowest_index(mm):
     rng = np.random.default_rng(3)
     X = rng.standard_normal((500, 24)).astype(np.float32)

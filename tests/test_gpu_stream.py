@@ -76,6 +76,7 @@ STREAM = [
     ("ragged-bf16s", "tiny", 5_003, 37, 77, 1.5, 2, dict(batch_size=700, bf16_search=True)),
     ("codes-pieces", "codes", 12_000, 64, 256, 2.0, 2, {}),
     ("f8-pieces", "codes8", 12_000, 64, 256, 2.0, 2, {}),
+    ("f16-pieces", "deep-f16", 12_000, 96, 256, 2.0, 2, {}),
 ]
 
 

@@ -12,7 +12,7 @@ import pytest
 import oracle
 from mini_means_amd import datagen
 
-from parity import lockstep, obj_atol, rel_l2, to_device
+from parity import LOW_PRECISION, lockstep, obj_atol, rel_l2, to_device
 
 pytestmark = pytest.mark.gpu
 
@@ -63,6 +63,11 @@ LOCKSTEP = [
     ("f8-small", "codes8", 12_000, 768, 256, 2.0, {}),
     ("f8-ragged", "codes8", 5_003, 37, 77, 1.5, dict(batch_size=700)),
     ("f8-deep", "codes8", 30_000, 96, 1024, 3.0, {}),
+    # fp16 data (README "Data precision", FP16): fp16 search, fp32 sums
+    ("f16-small", "embedding-f16", 12_000, 768, 256, 2.0, {}),
+    ("f16-deep", "deep-f16", 30_000, 96, 1024, 3.0, {}),
+    ("f16-ragged", "tiny-f16", 5_003, 37, 77, 1.5, dict(batch_size=700)),
+    ("f16-sph", "embedding-f16", 12_000, 768, 256, 2.0, dict(spherical=True)),
 ]
 
 
@@ -97,7 +102,8 @@ def test_train_lockstep(mm, name, gen, n, d, k, T, o):
 
 LLOYD = [("tiny", "tiny", 10_000, 16, 64, 8), ("emb-small", "embedding", 12_000, 768, 256, 4),
          ("large-small", "large", 40_000, 128, 1024, 3), ("codes", "codes", 12_000, 96, 200, 4),
-         ("ragged", "tiny", 5_003, 37, 77, 5), ("f8", "codes8", 12_000, 128, 200, 4)]
+         ("ragged", "tiny", 5_003, 37, 77, 5), ("f8", "codes8", 12_000, 128, 200, 4),
+         ("f16", "sift-f16", 12_000, 128, 200, 4)]
 
 
 @pytest.mark.parametrize("name,gen,n,d,k,iters", LLOYD, ids=[c[0] for c in LLOYD])
@@ -111,7 +117,7 @@ def test_lloyd_mode_lockstep(mm, name, gen, n, d, k, iters):
     last = {}
 
     def hook(chk):
-        C32 = chk["C32"] if X.dtype in (np.uint16, np.int8, np.uint8) else None
+        C32 = chk["C32"] if X.dtype in LOW_PRECISION else None
         check_labels(X, chk["C"], None, chk["given"], chk["oracle"], chk["d1"], chk["d2"],
                      chk["given_dist"], what=f"lloyd {name} iteration {chk['t']}", C32=C32)
         last["labels"] = chk["given"]
