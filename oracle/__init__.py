@@ -49,6 +49,11 @@ Do."):
                     compares them with the centroids rounded to codes.
 * Lloyd             blog, Lloyd section: assign all, move each centroid to
                     the exact mean of its points (the Lloyd-25 target).
+* slow EMA          blog, closing remark of the section on what e-means
+                    changes: for unseen data, finish with a second, slower
+                    EMA, a second set of centroids from the same run. The
+                    pages give no decay; read as a second pair of running
+                    statistics over the last pass at the rate alpha_t / kappa.
 
 Readings where the pages are silent (each listed in the design notes):
 power-of-two rounding in log2 space; cap = largest power of two <= n/2;
@@ -61,8 +66,8 @@ keeping the EMA centroid where that pass gave no point; labels of rows the last
 pass did not visit are -1; random streams from Philox4x64-10.
 
 Parity unpinned: the split geometry of a revival (halving, the +/-2^-10
-hashed-sign perturbation, the sequential donor draws) is this build's reading
-of "split a busy cluster in two"; the pages fix no values for it. It is pinned
+hashed-sign perturbation, the sequential donor draws) is a reading of "split
+a busy cluster in two"; the pages fix no values for it. It is pinned
 only by properties (donor frequency proportional to N, the split identities,
 fewer dead clusters than without revival).
 """
@@ -510,6 +515,8 @@ class TrainResult:
     split_log: list = field(default_factory=list)  # (t, dead j, donor i)
     dead_at_end: int = 0
     label_checks: list = field(default_factory=list)  # per step, lockstep validation results
+    slow_centroids: Optional[np.ndarray] = None        # k x d fp32 (slow_ema > 0)
+    slow_N: Optional[np.ndarray] = None                # k fp32 slow running counts
 
 
 def init_rows(n: int, k: int, seed: int) -> np.ndarray:
@@ -556,7 +563,7 @@ def train(X: np.ndarray, k: int, T: float, seed: int = 1234, *, batch_law: int =
           check_slots: Optional[Callable[[int, int], Optional[np.ndarray]]] = None,
           check_hook: Optional[Callable[[dict], None]] = None,
           nthreads: int = 0, bf16_search: bool = False,
-          spherical: bool = False) -> TrainResult:
+          spherical: bool = False, slow_ema: float = 0.0) -> TrainResult:
     """e-means on X (n x d, fp32 or bf16 bits), step by step.
 
     bf16_search: fp32 data is searched in bf16 (rows and centroids rounded to
@@ -570,6 +577,15 @@ def train(X: np.ndarray, k: int, T: float, seed: int = 1234, *, batch_law: int =
     rescales each cluster's exact mean to norm 1, and the reported error is
     the sum of 2 - 2 x similarity. In label checks a dot product s enters as
     -2 s (the squared distance up to a per-row constant for unit centroids).
+
+    slow_ema = kappa >= 1 (0: off), the second, slower EMA of the blog's
+    section on what e-means changes ("for unseen data"). Reading: when the last
+    pass begins, a second pair (N', S') starts from (N, S); every update of
+    that pass applies the same recurrence to it with the rate
+    beta_t = fl32(alpha_t / kappa); a revival in that pass restarts the
+    (N', S') of both halves from their split values; the slow centroids are
+    S' / N' (the EMA centroid where N' = 0), rescaled to norm 1 in spherical
+    mode (res.slow_centroids, res.slow_N). kappa = 1 gives the EMA centroids.
 
     labels_for_step(t, rows) may supply the labels of step t from elsewhere
     (lockstep replay). The oracle then checks them on the slots that
@@ -595,6 +611,9 @@ def train(X: np.ndarray, k: int, T: float, seed: int = 1234, *, batch_law: int =
     labels_out = np.full(n, -1, dtype=np.int32)
     res = TrainResult(centroids=C, ema_centroids=C, labels=labels_out, N=N, S=S, recipe=rc,
                       alphas=al)
+    if slow_ema and slow_ema < 1.0:
+        raise ValueError("slow_ema must be 0 (off) or >= 1")
+    N2 = S2 = None
 
     t = 0
     n_pass = len(rc["epoch_rows"])
@@ -633,6 +652,14 @@ def train(X: np.ndarray, k: int, T: float, seed: int = 1234, *, batch_law: int =
             counts, sums = group(X, rows, lab, k)
             a = al[t]
             b = np.float32(1.0) - a
+            if slow_ema and last:
+                if N2 is None:   # the slow pair starts from the running statistics
+                    N2, S2 = N.copy(), S.copy()
+                beta = np.float32(np.float64(a) / slow_ema)
+                b2 = np.float32(1.0) - beta
+                N2[:] = (b2 * N2) + (beta * counts.astype(np.float32))
+                S2[:] = (np.float64(b2) * S2.astype(np.float64)
+                         + np.float64(beta) * sums).astype(np.float32)
             # running count in fp32, fixed operation order: fl(fl(b*N) + fl(a*n))
             N[:] = (b * N) + (a * counts.astype(np.float32))
             # running sum: fp64 arithmetic, fp32 storage
@@ -646,11 +673,25 @@ def train(X: np.ndarray, k: int, T: float, seed: int = 1234, *, batch_law: int =
                 LS += sums
                 labels_out[rows] = lab
             if thr > 0 and (t + 1) % REVIVE_EVERY == 0:
+                before = len(res.split_log)
                 _revive(t, seed, thr, N, S, C, res.split_log, spherical)
+                if N2 is not None:   # both halves restart their slow statistics
+                    for _, j, i in res.split_log[before:]:
+                        N2[[i, j]] = N[[i, j]]
+                        S2[[i, j]] = S[[i, j]]
             t += 1
         res.obj.append(obj / rows_e)
 
     res.ema_centroids = C.copy()
+    if slow_ema:
+        CS = C.copy()
+        if N2 is not None:
+            pos = N2 > 0
+            CS[pos] = (S2[pos].astype(np.float64)
+                       / N2[pos].astype(np.float64)[:, None]).astype(np.float32)
+            if spherical:
+                CS[pos] = normalize(CS[pos])
+        res.slow_centroids, res.slow_N = CS, N2
     if finalize:
         pos = LN > 0
         C[pos] = (LS[pos] / LN[pos].astype(np.float64)[:, None]).astype(np.float32)

@@ -750,3 +750,55 @@ def test_revival_reduces_dead_clusters():
     dead_off = int(np.sum(off.N < th_off))
     assert on.dead_at_end <= dead_off
     assert len(on.split_log) > 0
+
+
+# Slow EMA (blog, section on what e-means changes: a second, slower EMA for
+# unseen data; its decay is a reading: beta_t = alpha_t / kappa over the last pass)
+
+def test_slow_ema_kappa_one_is_the_ema():
+    """kappa = 1 makes the slow pair the running pair itself: the slow
+    centroids equal the EMA centroids bit for bit, revivals in the last pass
+    included."""
+    X = datagen.tiny(n=3000, d=16, seed=9)
+    res = oracle.train(X, 100, 2.0, seed=5, slow_ema=1.0)
+    last0 = sum(res.recipe["steps_per_pass"][:-1])
+    assert any(t >= last0 for t, _, _ in res.split_log), "no revival in the last pass"
+    assert np.array_equal(res.slow_centroids, res.ema_centroids)
+    assert np.array_equal(res.slow_N, res.N)
+    with pytest.raises(ValueError):
+        oracle.train(X, 32, 2.0, seed=5, slow_ema=0.5)
+
+
+def test_slow_ema_closed_form_one_cluster():
+    """With one cluster every row of a step goes to it, so both averages are
+    fixed weighted sums of the batch sums: the running pair weighs step t by
+    a_t prod_{u>t} (1 - a_u) up to the last pass, and the slow pair carries
+    that on with b_u = a_u / kappa through the last pass."""
+    n, d, T, kappa, seed, B = 2000, 16, 3.0, 4.0, 7, 256
+    X = datagen.tiny(n=n, d=d, seed=3)
+    res = oracle.train(X, 1, T, seed=seed, slow_ema=kappa, batch_size=B, unused_threshold=0.0)
+    rc = res.recipe
+    al = res.alphas.astype(np.float64)
+    steps, sums, cnt, in_last = [], [], [], []
+    for e, rows_e in enumerate(rc["epoch_rows"]):
+        for s in range(rc["steps_per_pass"][e]):
+            Bt = min(B, rows_e - s * B)
+            rows = oracle.perm_range(n, seed, oracle.STREAM_PERM, e, s * B, Bt)
+            sums.append(X[rows].astype(np.float64).sum(axis=0))
+            cnt.append(float(Bt))
+            in_last.append(e == len(rc["epoch_rows"]) - 1)
+    S_tot = len(cnt)
+    t0 = in_last.index(True)
+    beta = np.array([np.float64(np.float32(al[t] / kappa)) for t in range(S_tot)])
+    w = np.zeros(S_tot)
+    for t in range(S_tot):
+        if t < t0:    # running pair up to the last pass, then the slow decay
+            w[t] = al[t] * np.prod(1.0 - al[t + 1:t0]) * np.prod(1.0 - beta[t0:])
+        else:
+            w[t] = beta[t] * np.prod(1.0 - beta[t + 1:])
+    N2 = float(np.dot(w, cnt))
+    S2 = np.dot(w, np.array(sums))
+    np.testing.assert_allclose(res.slow_N[0], N2, rtol=1e-5)
+    np.testing.assert_allclose(res.slow_centroids[0], S2 / N2, rtol=1e-5, atol=1e-6)
+    # and it differs from the EMA centroid (the slow pair forgets less)
+    assert not np.allclose(res.slow_centroids[0], res.ema_centroids[0], rtol=1e-4, atol=1e-6)
