@@ -417,6 +417,20 @@ def main() -> int:
         log(f"first crossing: {ttt['first_crossing']['first']}")
         line["s_to_lloyd25"] = ttt["seconds"]
         line["time_to_target"] = ttt
+        # the two closing choices of one run at the workload's T (untimed):
+        # the last pass's exact means, the EMA itself and the slow EMA (kappa 2)
+        r2 = mm.train(X, k, T, args.seed, slow_ema=2.0, capture_labels=False,
+                      bf16_search=bsearch)
+        r1 = mm.train(X, k, T, args.seed, slow_ema=1.0, capture_labels=False,
+                      bf16_search=bsearch)
+
+        def _ho(C):
+            return heldout_mse(mm, Xh, C if dec is None else dec(C), torch)
+
+        line["finalization"] = {"T": T, "heldout_mse": {
+            "closing_mean": _ho(r2.centroids), "ema": _ho(r1.slow_centroids),
+            "slow_ema_kappa2": _ho(r2.slow_centroids)}}
+        log(f"finalization: {line['finalization']}")
 
     if not args.no_cpu and Xhost is not None:
         C = out.centroids.cpu().numpy()

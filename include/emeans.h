@@ -143,6 +143,21 @@ typedef struct emeans_opts {
                                  assignment. n < 2^31 (the 2^24 batch limit does not
                                  apply; a cluster of more than 2^24 rows divides by
                                  its fp32-rounded count). Not with emeans_begin. */
+  double slow_ema;            /* kappa >= 1 (0: off): a second, slower EMA for unseen
+                                 data (blog "k-means Reads Your Data 25 Times. Two
+                                 Would Do.", section on what e-means changes; the
+                                 pages give no decay, so this is a reading): when the
+                                 last pass begins, a second pair (N', S') starts from
+                                 (N, S) and each update of that pass applies the same
+                                 recurrence to it with beta_t = fl32(alpha_t / kappa);
+                                 a revival in that pass restarts both halves' pair
+                                 from their split values. Requires slow_centroids;
+                                 not with lloyd. kappa = 1 gives the EMA centroids. */
+  float* slow_centroids;      /* device, k x d fp32 (with slow_ema): written by
+                                 emeans_train / emeans_finalize with S' / N' (the
+                                 EMA centroid where N' = 0, or everywhere if the last
+                                 pass never began), rescaled to norm 1 in spherical
+                                 mode; the closing mean is not applied to them */
 } emeans_opts;
 
 /* Recipe and statistics of a run (README "Settings and results": recipe, obj,

@@ -36,7 +36,7 @@ class Opts(ctypes.Structure):
         ("unused_threshold", c_dbl), ("no_finalize", c_i32), ("profile", c_i32),
         ("stream", c_vp), ("trace_labels", c_vp), ("out_counts", c_vp), ("split_log", c_vp),
         ("split_log_cap", c_i64), ("max_steps", c_i64), ("bf16_search", c_i32),
-        ("spherical", c_i32), ("lloyd", c_i32),
+        ("spherical", c_i32), ("lloyd", c_i32), ("slow_ema", c_dbl), ("slow_centroids", c_vp),
     ]
 
 
@@ -193,6 +193,7 @@ class TrainOutput:
     trace: object = None       # int32 tensor of every step's labels, or None
     counts: object = None      # k float32 running counts at the end, or None
     split_log: Optional[list] = None
+    slow_centroids: object = None  # k x d float32 slow-EMA centroids (slow_ema), or None
 
 
 def train(X, k: int, T: float = 5.0, seed: int = 1234, *, batch_law="auto", batch_size: int = 0,
@@ -200,9 +201,11 @@ def train(X, k: int, T: float = 5.0, seed: int = 1234, *, batch_law="auto", batc
           capture_labels: bool = True, trace: bool = False, counts: bool = False,
           split_log_cap: int = 0, profile: bool = False, max_steps: int = 0,
           bf16_search: bool = False, spherical: bool = False, lloyd: bool = False,
-          stream=None) -> TrainOutput:
+          slow_ema: float = 0.0, stream=None) -> TrainOutput:
     """e-means training of X (n x d tensor on the GPU). lloyd: plain Lloyd
-    iterations instead (T of them, every row each time, alpha = 1)."""
+    iterations instead (T of them, every row each time, alpha = 1).
+    slow_ema = kappa >= 1: also the centroids of a second, slower EMA over the
+    last pass (rate alpha_t / kappa), for unseen data (out.slow_centroids)."""
     import torch
     _require_device(X)
     n, d = X.shape
@@ -227,6 +230,11 @@ def train(X, k: int, T: float = 5.0, seed: int = 1234, *, batch_law="auto", batc
         o.max_steps = int(max_steps)
         o.bf16_search = 1 if bf16_search else 0
         o.spherical = 1 if spherical else 0
+        SC = None
+        if slow_ema:
+            SC = torch.empty((k, d), dtype=torch.float32, device=dev)
+            o.slow_ema = float(slow_ema)
+            o.slow_centroids = SC.data_ptr()
         s = Stats()
         _check(lib().emeans_train(X.data_ptr(), n, d, int(k), float(T), int(seed) & (2**64 - 1),
                                   C.data_ptr(), labels.data_ptr() if labels is not None else None,
@@ -236,7 +244,7 @@ def train(X, k: int, T: float = 5.0, seed: int = 1234, *, batch_law="auto", batc
         if log is not None:
             m = min(s.n_logged, split_log_cap)
             splits = [(log[3 * i], log[3 * i + 1], log[3 * i + 2]) for i in range(m)]
-        return TrainOutput(C, labels, st, tr, cn, splits)
+        return TrainOutput(C, labels, st, tr, cn, splits, SC)
 
 
 def assign(X, C, *, with_dists: bool = True, bf16_search: bool = False, spherical: bool = False,
@@ -378,7 +386,7 @@ class Stream:
                  batch_law="auto", batch_size: int = 0, alpha0: float = 0.0,
                  unused_threshold=None, finalize: bool = True, bf16_search: bool = False,
                  spherical: bool = False, profile: bool = False, counts: bool = False,
-                 split_log_cap: int = 0, stream=None):
+                 split_log_cap: int = 0, slow_ema: float = 0.0, stream=None):
         import torch
         if not (getattr(start, "is_cuda", False) and start.dtype == torch.float32
                 and start.is_contiguous() and start.dim() == 2):
@@ -408,6 +416,12 @@ class Stream:
             if self._log is not None:
                 o.split_log = ctypes.cast(self._log, c_vp)
                 o.split_log_cap = split_log_cap
+            # the slow-EMA centroids (slow_ema) are written by finalize()
+            self.slow_centroids = torch.empty((self.k, self.d), dtype=torch.float32,
+                                              device=self.device) if slow_ema else None
+            if self.slow_centroids is not None:
+                o.slow_ema = float(slow_ema)
+                o.slow_centroids = self.slow_centroids.data_ptr()
             self._opts = o
             self.recipe = recipe(self.n, self.d, self.k, T, batch_law=batch_law,
                                  batch_size=batch_size, alpha0=alpha0,

@@ -215,9 +215,24 @@ int check_dtype(int32_t d, const emeans_opts* opts) {
   return EMEANS_OK;
 }
 
+// The slow EMA's options: kappa >= 1 with an output table, not in Lloyd mode.
+int check_slow(const emeans_opts* opts) {
+  if (!opts) return EMEANS_OK;
+  const double kp = opts->slow_ema;
+  if (!(kp == 0.0 || kp >= 1.0))
+    return fail(EMEANS_EINVAL, "slow_ema must be 0 (off) or >= 1 (got %g)", kp);
+  if (kp >= 1.0 && !opts->slow_centroids)
+    return fail(EMEANS_EINVAL, "slow_ema needs slow_centroids");
+  if (kp == 0.0 && opts->slow_centroids)
+    return fail(EMEANS_EINVAL, "slow_centroids is set but slow_ema is 0");
+  if (kp >= 1.0 && opts->lloyd) return fail(EMEANS_EINVAL, "slow_ema does not apply to lloyd");
+  return EMEANS_OK;
+}
+
 int check_run_args(int64_t n, int32_t d, int32_t k, double T, const emeans_opts* opts) {
   int rc0 = check_dtype(d, opts);
   if (rc0) return rc0;
+  if ((rc0 = check_slow(opts))) return rc0;
   Recipe r;
   const int rc = make_recipe(n, d, k, T, opts, r);
   if (rc) return rc;
@@ -258,6 +273,9 @@ struct emeans_model {
   bool bf16 = false, bsearch = false, sbf = false, i8 = false, f8 = false, f16 = false,
        sph = false, profile = false;
   bool no_finalize = false;
+  double slow_k = 0.0;             // slow EMA: kappa (0 = off)
+  float* slow_out = nullptr;       // caller's table for the slow centroids
+  bool slow_started = false;       // the slow pair holds the last pass's statistics
   int32_t* trace = nullptr;
   float* out_counts = nullptr;
   int32_t* split_log = nullptr;
@@ -285,6 +303,7 @@ struct emeans_model {
   int2* ovf = nullptr;
   float *s_acc = nullptr, *S = nullptr, *N = nullptr, *LS = nullptr, *bias = nullptr,
         *n0 = nullptr, *pair_n = nullptr, *wlive = nullptr;
+  float *N2 = nullptr, *S2 = nullptr;  // slow pair (slow EMA)
   uint16_t *chat = nullptr, *xb = nullptr;  // chat: bf16 or (fp16 data) fp16 copy of C
   int8_t* cq = nullptr;   // int8 codes of C (int8 data)
   uint8_t* cf = nullptr;  // E4M3 codes of C (FP8 data)
@@ -330,7 +349,7 @@ struct emeans_model {
                       pair_i, pair_n, rv_pos, rv_head, rv_cbase, rv_clen, rv_heads, rv_list,
                       rv_nheads, counters, count_only ? nullptr : dlog,
                       count_only ? 0 : log_cap, count_only ? 1 : 0, sph ? 1 : 0, wlive,
-                      f16 ? 1 : 0};
+                      f16 ? 1 : 0, slow_started ? N2 : nullptr, slow_started ? S2 : nullptr};
   }
 
   // Recipe, options and workspace; C = external (the caller's buffer) or own.
@@ -352,6 +371,10 @@ struct emeans_model {
     if (opts && opts->trace_labels && (rc = check_device(opts->trace_labels, "trace_labels")))
       return rc;
     if (opts && opts->out_counts && (rc = check_device(opts->out_counts, "out_counts"))) return rc;
+    if ((rc = check_slow(opts))) return rc;
+    if (opts && opts->slow_centroids &&
+        (rc = check_device(opts->slow_centroids, "slow_centroids")))
+      return rc;
     if (opts && opts->split_log && opts->split_log_cap < 0)
       return fail(EMEANS_EINVAL, "split_log_cap must be >= 0");
     st = static_cast<hipStream_t>(opts ? opts->stream : nullptr);
@@ -369,6 +392,8 @@ struct emeans_model {
     out_counts = opts ? opts->out_counts : nullptr;
     split_log = (opts && opts->split_log) ? opts->split_log : nullptr;
     log_cap = split_log ? opts->split_log_cap : 0;
+    slow_k = opts ? opts->slow_ema : 0.0;
+    slow_out = slow_k >= 1.0 ? opts->slow_centroids : nullptr;
 
     const size_t kd = (size_t)k * d;
     const int64_t B = r.B;
@@ -402,6 +427,10 @@ struct emeans_model {
     ar.want(&S, kd);
     ar.want(&N, (size_t)k);
     ar.want(&LS, kd);
+    if (slow_out) {
+      ar.want(&N2, (size_t)k);
+      ar.want(&S2, kd);
+    }
     ar.want(&bias, (size_t)k);
     if (sbf || f16) ar.want(&chat, kd);
     if (i8) ar.want(&cq, kd);
@@ -466,9 +495,18 @@ struct emeans_model {
     const float a = r.lloyd ? 1.0f : alpha_at(r.alpha0, t, r.S);
     const float b = 1.0f - a;
     const bool last = e == r.npass - 1;
+    const bool slow = slow_out && last;
+    if (slow && !slow_started) {  // the slow pair starts from the running pair
+      HIP_RET(hipMemcpyAsync(N2, N, sizeof(float) * k, hipMemcpyDeviceToDevice, st));
+      HIP_RET(hipMemcpyAsync(S2, S, sizeof(float) * (size_t)k * d, hipMemcpyDeviceToDevice, st));
+      slow_started = true;
+    }
+    const float beta = slow ? (float)((double)a / slow_k) : 0.0f;
+    const float b2 = 1.0f - beta;
     HIP_RET(timed(kUpdate, [&] {
       return launch_ema(k, d, a, b, counts, s_acc, N, S, C, bias, chat, f16, cq, cf, pass_counts,
-                        last ? LS : nullptr, sph, st);
+                        last ? LS : nullptr, sph, beta, b2, slow ? N2 : nullptr,
+                        slow ? S2 : nullptr, st);
     }));
     if (r.thr > 0.0 && (t + 1) % kReviveEvery == 0) {
       const ReviveArgs ra = revive_args(false);
@@ -503,6 +541,9 @@ struct emeans_model {
     }
     if (out_counts)
       HIP_RET(hipMemcpyAsync(out_counts, N, sizeof(float) * k, hipMemcpyDeviceToDevice, st));
+    // the slow centroids come from the EMA centroids before the closing mean
+    if (slow_out)
+      HIP_RET(launch_slow_final(k, d, slow_started ? N2 : nullptr, S2, C, slow_out, sph, st));
     if (closing) HIP_RET(launch_finalize(k, d, pass_counts, LS, C, sph, st));
     if (out_C && out_C != C)
       HIP_RET(hipMemcpyAsync(out_C, C, sizeof(float) * (size_t)k * d, hipMemcpyDeviceToDevice, st));

@@ -77,9 +77,17 @@ hipError_t launch_group(int dt, const void* X, int d, const uint32_t* order,
 // pass_counts += counts; LS += s when LS is non-null; refreshes bias and the
 // search format (Chat, Cq or Cf, at most one non-null).
 // sph: the centroids are rescaled to norm 1 and the bias is 0.
+// N2 / S2 (slow pair, both or neither): the same recurrence with rate beta
+// and 1 - beta = b2.
 hipError_t launch_ema(int k, int d, float a, float b, int32_t* counts, float* s_acc, float* N,
                       float* S, float* C, float* bias, uint16_t* Chat, bool chat_f16, int8_t* Cq,
-                      uint8_t* Cf, int32_t* pass_counts, float* LS, bool sph, hipStream_t st);
+                      uint8_t* Cf, int32_t* pass_counts, float* LS, bool sph, float beta,
+                      float b2, float* N2, float* S2, hipStream_t st);
+
+// out[j] = S2[j] / N2[j] where N2[j] > 0, else C[j] (N2 NULL: out = C);
+// rescaled to norm 1 with sph where N2[j] > 0.
+hipError_t launch_slow_final(int k, int d, const float* N2, const float* S2, const float* C,
+                             float* out, bool sph, hipStream_t st);
 
 struct ReviveArgs {
   int k, d;
@@ -113,6 +121,8 @@ struct ReviveArgs {
   int sph;            // spherical e-means: split centroids rescaled to norm 1, bias 0
   float* wlive;       // live counts (0 for dead) when k > 32768; k rounded up to 4096
   int chat_f16;       // Chat holds fp16 rather than bf16
+  float* N2;          // slow pair (or NULL): a split copies both halves' N and S here
+  float* S2;
 };
 // Dead-cluster check and donor draws (one workgroup), then the splits of the
 // running sums, one wave per donor chain.

@@ -519,7 +519,8 @@ __global__ __launch_bounds__(256) void ema_kernel(int k, int d, float a, float b
                                                   int32_t* counts, float* s_acc, float* N,
                                                   float* S, float* C, float* bias,
                                                   uint16_t* Chat, int8_t* Cq, uint8_t* Cf,
-                                                  int32_t* pass_counts, float* LS, int sph) {
+                                                  int32_t* pass_counts, float* LS, int sph,
+                                                  float beta, float b2, float* N2, float* S2) {
   const int j = blockIdx.x * 4 + (threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
   if (j >= k) return;
@@ -537,6 +538,7 @@ __global__ __launch_bounds__(256) void ema_kernel(int k, int d, float a, float b
     }
     const float Sv = __fadd_rn(__fmul_rn(b, S[idx]), __fmul_rn(a, s));
     S[idx] = Sv;
+    if (S2) S2[idx] = __fadd_rn(__fmul_rn(b2, S2[idx]), __fmul_rn(beta, s));
     float c;
     if (Nn > 0.0f) {
       c = __fdiv_rn(Sv, Nn);
@@ -574,6 +576,7 @@ __global__ __launch_bounds__(256) void ema_kernel(int k, int d, float a, float b
   }
   if (lane == 0) {
     N[j] = Nn;
+    if (N2) N2[j] = __fadd_rn(__fmul_rn(b2, N2[j]), __fmul_rn(beta, (float)n));
     if constexpr (SF == 2)
       reinterpret_cast<int32_t*>(bias)[j] = -nq;
     else
@@ -581,6 +584,21 @@ __global__ __launch_bounds__(256) void ema_kernel(int k, int d, float a, float b
     pass_counts[j] += n;
     counts[j] = 0;
   }
+}
+
+// One wave per centroid: the slow centroids S2 / N2 (C where N2 = 0, or
+// everywhere without a slow pair), rescaled to norm 1 with sph.
+__global__ __launch_bounds__(256) void slow_final_kernel(int k, int d, const float* N2,
+                                                         const float* S2, const float* C,
+                                                         float* out, int sph) {
+  const int j = blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  if (j >= k) return;
+  const float nn = N2 ? N2[j] : 0.0f;
+  const size_t base = (size_t)j * d;
+  for (int e = lane; e < d; e += 64)
+    out[base + e] = nn > 0.0f ? __fdiv_rn(S2[base + e], nn) : C[base + e];
+  if (sph && nn > 0.0f) wave_normalize(out + base, d, lane);
 }
 
 // Dead-cluster revival. Mean running count m = sum N / k (fp64); dead set
@@ -885,6 +903,10 @@ __global__ __launch_bounds__(256) void split_kernel(ReviveArgs A) {
     const int i = A.pair_i[q];
     const int j = A.dead[q];
     const float Nh = A.pair_n[q];
+    if (A.N2 && lane == 0) {  // the counts are final once revive_kernel has run
+      A.N2[j] = A.N[j];
+      A.N2[i] = A.N[i];
+    }
     float ni = 0.0f, nj = 0.0f;
     int qni = 0, qnj = 0;  // |q|^2 of the int8 codes, exact
     U64x4 wd = {0, 0, 0, 0};
@@ -899,6 +921,10 @@ __global__ __launch_bounds__(256) void split_kernel(ReviveArgs A) {
       const float si = __fmul_rn(half, 1.0f - kSplitEps * sg);
       A.S[jj] = sj;
       A.S[ii] = si;
+      if (A.S2) {  // the slow pair of both halves restarts from the split values
+        A.S2[jj] = sj;
+        A.S2[ii] = si;
+      }
       float cj = __fdiv_rn(sj, Nh), ci = __fdiv_rn(si, Nh);
       A.C[jj] = cj;
       A.C[ii] = ci;
@@ -1121,12 +1147,13 @@ hipError_t launch_group(int dt, const void* X, int d, const uint32_t* order,
 
 hipError_t launch_ema(int k, int d, float a, float b, int32_t* counts, float* s_acc, float* N,
                       float* S, float* C, float* bias, uint16_t* Chat, bool chat_f16, int8_t* Cq,
-                      uint8_t* Cf, int32_t* pass_counts, float* LS, bool sph, hipStream_t st) {
+                      uint8_t* Cf, int32_t* pass_counts, float* LS, bool sph, float beta,
+                      float b2, float* N2, float* S2, hipStream_t st) {
   const dim3 grid((k + 3) / 4), block(256);
   const int sp = sph ? 1 : 0;
 #define EMK_EMA(SF)                                                                        \
   ema_kernel<SF><<<grid, block, 0, st>>>(k, d, a, b, counts, s_acc, N, S, C, bias, Chat, Cq, \
-                                         Cf, pass_counts, LS, sp)
+                                         Cf, pass_counts, LS, sp, beta, b2, N2, S2)
   if (Chat && chat_f16)
     EMK_EMA(4);
   else if (Chat)
@@ -1138,6 +1165,12 @@ hipError_t launch_ema(int k, int d, float a, float b, int32_t* counts, float* s_
   else
     EMK_EMA(0);
 #undef EMK_EMA
+  return hipGetLastError();
+}
+
+hipError_t launch_slow_final(int k, int d, const float* N2, const float* S2, const float* C,
+                             float* out, bool sph, hipStream_t st) {
+  slow_final_kernel<<<(k + 3) / 4, 256, 0, st>>>(k, d, N2, S2, C, out, sph ? 1 : 0);
   return hipGetLastError();
 }
 

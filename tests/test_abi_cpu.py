@@ -149,6 +149,28 @@ def test_train_rejects_before_device_work(L):
     assert L.emeans_train(None, 100, 4, 3, 5.0, 1, None, None, ctypes.byref(o), ctypes.byref(s)) == -1
 
 
+def test_slow_ema_options_rejected_before_device_work(L):
+    """slow_ema: kappa must be 0 or >= 1, needs an output table, and does not
+    combine with Lloyd mode; the streaming begin applies the same checks."""
+    s = mm.Stats()
+    for kappa, table, lloyd, msg in ((0.5, 8, 0, b"slow_ema must be"),
+                                     (2.0, None, 0, b"needs slow_centroids"),
+                                     (0.0, 8, 0, b"slow_ema is 0"),
+                                     (2.0, 8, 1, b"lloyd")):
+        o = mm.Opts()
+        o.slow_ema = kappa
+        o.slow_centroids = table
+        o.lloyd = lloyd
+        assert L.emeans_train(None, 100, 4, 3, 2.0, 1, None, None, ctypes.byref(o),
+                              ctypes.byref(s)) == -1
+        assert msg in L.emeans_last_error()
+    o = mm.Opts()
+    o.slow_ema = 0.5
+    h = ctypes.c_void_p()
+    assert L.emeans_begin(100, 4, 3, 2.0, 1, None, ctypes.byref(o), ctypes.byref(h)) == -1
+    assert b"slow_ema must be" in L.emeans_last_error()
+
+
 def test_assign_rejects_before_device_work(L):
     o = mm.Opts()
     assert L.emeans_assign(None, 10, 4, None, 3, None, None, ctypes.byref(o)) == -1

@@ -62,7 +62,8 @@ def _stream_run(mm, X, k, T, seed, pieces=1, **kw):
     C = em.finalize()
     torch.cuda.synchronize()
     out = SimpleNamespace(trace=torch.cat(trace), counts=em.counts, centroids=C, labels=labels,
-                          stats=em.stats, split_log=em.split_log)
+                          stats=em.stats, split_log=em.split_log,
+                          slow_centroids=em.slow_centroids)
     em.close()
     return out
 
@@ -77,6 +78,7 @@ STREAM = [
     ("codes-pieces", "codes", 12_000, 64, 256, 2.0, 2, {}),
     ("f8-pieces", "codes8", 12_000, 64, 256, 2.0, 2, {}),
     ("f16-pieces", "deep-f16", 12_000, 96, 256, 2.0, 2, {}),
+    ("slow-ema", "tiny", 3_000, 16, 100, 2.0, 2, dict(slow_ema=4.0)),
 ]
 
 
@@ -93,6 +95,8 @@ def test_stream_lockstep(mm, name, gen, n, d, k, T, pieces, o):
     tol = 1e-2 if X.dtype == np.uint16 else 1e-4
     assert rel_l2(out.centroids.cpu().numpy(), res.centroids) <= tol
     np.testing.assert_allclose(out.stats["obj"], res.obj, rtol=1e-4, atol=obj_atol(X))
+    if o.get("slow_ema"):
+        assert rel_l2(out.slow_centroids.cpu().numpy(), res.slow_centroids) <= tol
 
 
 def test_stream_rejects_rule_breaks(mm):

@@ -251,6 +251,50 @@ def test_train_repeatable(mm):
     assert abs(ma - mb) <= 1e-2 * mb
 
 
+SLOW = [
+    ("tiny-revive", "tiny", 3_000, 16, 100, 2.0, {}),
+    ("emb-small", "embedding", 12_000, 768, 256, 2.0, {}),
+    ("deep-sph", "deep", 30_000, 96, 1024, 2.5, dict(spherical=True)),
+    ("large-bf16", "large", 40_000, 128, 1024, 2.0, {}),
+    ("f16", "deep-f16", 12_000, 96, 256, 2.0, {}),
+]
+
+
+@pytest.mark.parametrize("name,gen,n,d,k,T,o", SLOW, ids=[c[0] for c in SLOW])
+def test_train_slow_ema_lockstep(mm, name, gen, n, d, k, T, o):
+    """The slow EMA (kappa = 4) against the oracle's on the adopted labels:
+    the slow centroids to 1e-4 relative L2 (1e-2 for bf16 data, as the
+    centroids), alongside the usual lockstep checks."""
+    seed, kappa = 1234, 4.0
+    X = datagen.make(gen, n, d, seed=21)
+    out = _gpu_train(mm, X, k, T, seed, slow_ema=kappa, **dict(o))
+    res, _ = lockstep(X, out, k, T, seed, slow_ema=kappa, **o)
+    assert np.array_equal(out.counts.cpu().numpy(), res.N)
+    assert out.split_log == [tuple(s) for s in res.split_log]
+    tol = 1e-2 if X.dtype == np.uint16 else 1e-4
+    SC = out.slow_centroids.cpu().numpy()
+    err = rel_l2(SC, res.slow_centroids)
+    assert err <= tol, f"slow centroids rel L2 {err:.3e}"
+    assert rel_l2(out.centroids.cpu().numpy(), res.centroids) <= tol
+    if o.get("spherical"):
+        nrm = np.linalg.norm(SC.astype(np.float64), axis=1)
+        assert np.all((np.abs(nrm - 1.0) < 1e-6) | (nrm == 0.0))
+
+
+def test_train_slow_ema_kappa_one_and_early_stop(mm):
+    """kappa = 1 runs the EMA's own recurrence: the slow centroids equal the
+    EMA centroids of the same run bit for bit (revivals in the last pass
+    included). A run stopped before its last pass returns the EMA centroids."""
+    import torch
+    X = to_device(datagen.make("tiny", 3_000, 16, seed=9))
+    out = mm.train(X, 100, 2.0, 5, slow_ema=1.0, finalize=False, split_log_cap=4096)
+    assert torch.equal(out.slow_centroids, out.centroids)
+    last0 = sum(out.stats["steps_per_pass"][:-1])
+    assert any(t >= last0 for t, _, _ in out.split_log)
+    part = mm.train(X, 100, 2.0, 5, slow_ema=3.0, finalize=False, max_steps=3)
+    assert torch.equal(part.slow_centroids, part.centroids)
+
+
 def test_train_rejects_bad_args(mm):
     import torch
     X = torch.zeros((100, 8), device="cuda")
