@@ -221,6 +221,31 @@ def codes_i8(n: int = 1_000_000, d: int = 768, m: int = 4096, spread: float = 80
     return _chunked(n, d, np.int8, fill)
 
 
+# uint8 data is handed to the oracle as `raw.view(U8)`: a one-field structured
+# dtype over the same bytes (plain numpy uint8 stands for E4M3 bit patterns).
+U8 = np.dtype([("u8", np.uint8)])
+
+
+def codes_u8(n: int = 1_000_000, d: int = 128, m: int = 4096, lo: float = 40.0,
+             hi: float = 215.0, sigma: float = 12.0, seed: int = 111,
+             split: int = 0) -> np.ndarray:
+    """uint8 data with clusters (README "Data precision", UINT8 input, e.g.
+    raw descriptor bytes): m centres uniform in [lo, hi]^d, Zipf(1.1) weights,
+    Gaussian noise of s.d. sigma, rounded and clamped to [0, 255]. Returns
+    the raw bytes (numpy uint8); `make` marks them with U8."""
+    r0 = _rng(seed, 0)
+    means = r0.uniform(lo, hi, size=(m, d)).astype(np.float32)
+    w = zipf_weights(m, 1.1)
+
+    def fill(c, lo_, hi_, out):
+        r = _rng(seed, 1 + split, c)
+        comp = r.choice(m, size=hi_ - lo_, p=w)
+        g = r.standard_normal((hi_ - lo_, d), dtype=np.float32)
+        out[:] = np.clip(np.rint(means[comp] + np.float32(sigma) * g), 0, 255).astype(np.uint8)
+
+    return _chunked(n, d, np.uint8, fill)
+
+
 def codes_e4m3(n: int = 1_000_000, d: int = 768, m: int = 1024, sigma: float = 2.0,
                seed: int = 109, split: int = 0) -> np.ndarray:
     """FP8 E4M3 codes of clustered data (README "Data precision", FP8 input),
@@ -246,9 +271,14 @@ def codes_e4m3(n: int = 1_000_000, d: int = 768, m: int = 1024, sigma: float = 2
 
 def make(gen: str, n: int, d: int, split: int = 0, **kw) -> np.ndarray:
     """Host data for a generator name at any (n, d) (fp32, bf16 bits for
-    'large', int8 for 'codes', E4M3 bits for 'codes8'). A name ending in
-    '-f16' stores that generator's rows as IEEE fp16 (numpy float16: nearest,
-    ties to even), the one-off conversion a caller makes for FP16 data."""
+    'large', int8 for 'codes', E4M3 bits for 'codes8', U8-marked bytes for
+    'codes-u8' and 'sift-u8'). A name ending in '-f16' stores that generator's
+    rows as IEEE fp16 (numpy float16: nearest, ties to even), the one-off
+    conversion a caller makes for FP16 data."""
+    if gen == "codes-u8":
+        return codes_u8(n=n, d=d, split=split, **kw).view(U8)
+    if gen == "sift-u8":   # the SIFT-like values are integers in [0, 255]
+        return sift(n=n, d=d, split=split, **kw).astype(np.uint8).view(U8)
     if gen.endswith("-f16"):
         X = make(gen[:-4], n, d, split=split, **kw)
         if X.dtype == np.uint16:

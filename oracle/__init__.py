@@ -46,7 +46,9 @@ Do."):
                     dimension and one power-of-two scale calibrated on a
                     sample, values beyond its range clamped to the edge
                     (127 / 448); training runs on the codes and the search
-                    compares them with the centroids rounded to codes.
+                    compares them with the centroids rounded to codes. UINT8
+                    data is searched exactly against the centroids rounded to
+                    uint8 values (clamped to [0, 255]).
 * Lloyd             blog, Lloyd section: assign all, move each centroid to
                     the exact mean of its points (the Lloyd-25 target).
 * slow EMA          blog, closing remark of the section on what e-means
@@ -222,7 +224,16 @@ def alphas(alpha0: float, S: int) -> np.ndarray:
 # assignment and grouping
 # ----------------------------------------------------------------------------
 
+# UINT8 data (README "Data precision": INT8 and UINT8 input numbers). Plain
+# numpy uint8 already stands for E4M3 bit patterns here, so uint8 data is
+# marked by a one-field structured dtype of the same bytes: U8 data is
+# `raw_uint8_array.view(U8)`.
+U8 = np.dtype([("u8", np.uint8)])
+
+
 def _dtype_code(X: np.ndarray) -> int:
+    if X.dtype == U8:             # uint8 values 0..255
+        return 5
     if X.dtype == np.float32:
         return 0
     if X.dtype == np.uint16:      # bf16 bit patterns
@@ -237,6 +248,8 @@ def _dtype_code(X: np.ndarray) -> int:
 
 
 def to_f32(X: np.ndarray) -> np.ndarray:
+    if X.dtype == U8:
+        return X.view(np.uint8).astype(np.float32)
     if X.dtype == np.uint16:
         return (X.astype(np.uint32) << 16).view(np.float32)
     if X.dtype == np.int8:
@@ -273,6 +286,13 @@ def int8_round(C: np.ndarray) -> np.ndarray:
     """Centroids (code space) -> nearest int8 code (ties to even), clamped to
     [-127, 127], returned as fp32 values."""
     return np.clip(np.rint(np.asarray(C, dtype=np.float32)), -127, 127).astype(np.float32)
+
+
+def u8_round(C: np.ndarray) -> np.ndarray:
+    """Centroids of uint8 data -> nearest uint8 value (ties to even), clamped
+    to [0, 255], returned as fp32 values: the search compares uint8 rows with
+    uint8 centroids exactly, as for int8 codes."""
+    return np.clip(np.rint(np.asarray(C, dtype=np.float32)), 0, 255).astype(np.float32)
 
 
 def int8_calibrate(sample: np.ndarray):
@@ -395,8 +415,11 @@ def f16_round(C: np.ndarray) -> np.ndarray:
 
 def search_centroids(C: np.ndarray, X: np.ndarray) -> np.ndarray:
     """Centroids in the search format: bf16 for bf16 data, fp16 for fp16 data,
-    int8 codes for int8 data, E4M3 values for FP8 data (README "Data
-    precision": only the search uses the smaller format), fp32 otherwise."""
+    int8 codes for int8 data, uint8 values for uint8 data, E4M3 values for FP8
+    data (README "Data precision": only the search uses the smaller format),
+    fp32 otherwise."""
+    if X.dtype == U8:
+        return u8_round(C)
     if X.dtype == np.uint16:
         return bf16_round(C)
     if X.dtype == np.int8:

@@ -105,9 +105,10 @@ void ref_perm_range(uint64_t n, uint64_t seed, uint64_t stream, uint64_t pass, u
 
 /* ------------------------------------------------------------------------ */
 /* Element access: dtype 0 = fp32, 1 = bf16 (stored as the high 16 bits of  */
-/* an fp32), 2 = int8 codes, 4 = IEEE fp16, 3 = FP8 E4M3 codes (OCP: sign, 4 exponent bits  */
-/* with bias 7, 3 mantissa bits; exponent 0 is subnormal, m * 2^-9; the     */
-/* pattern with all exponent and mantissa bits set is NaN, there is no inf). */
+/* an fp32), 2 = int8 codes, 4 = IEEE fp16, 5 = uint8 values, 3 = FP8 E4M3  */
+/* codes (OCP: sign, 4 exponent bits with bias 7, 3 mantissa bits; exponent */
+/* 0 is subnormal, m * 2^-9; the pattern with all exponent and mantissa     */
+/* bits set is NaN, there is no inf).                                       */
 /* ------------------------------------------------------------------------ */
 static inline double e4m3_value(uint8_t c) {
   const int e = (c >> 3) & 15, m = c & 7;
@@ -132,6 +133,7 @@ static inline double ref_elem(const void* X, int dtype, int64_t row, int32_t d, 
   if (dtype == 2) return (double)((const int8_t*)X)[row * (int64_t)d + t];  /* int8 codes */
   if (dtype == 3) return e4m3_value(((const uint8_t*)X)[row * (int64_t)d + t]);
   if (dtype == 4) return f16_value(((const uint16_t*)X)[row * (int64_t)d + t]);
+  if (dtype == 5) return (double)((const uint8_t*)X)[row * (int64_t)d + t];     /* uint8 */
   uint32_t bits = (uint32_t)((const uint16_t*)X)[row * (int64_t)d + t] << 16;
   float f;
   memcpy(&f, &bits, 4);

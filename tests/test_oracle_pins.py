@@ -802,3 +802,46 @@ def test_slow_ema_closed_form_one_cluster():
     np.testing.assert_allclose(res.slow_centroids[0], S2 / N2, rtol=1e-5, atol=1e-6)
     # and it differs from the EMA centroid (the slow pair forgets less)
     assert not np.allclose(res.slow_centroids[0], res.ema_centroids[0], rtol=1e-4, atol=1e-6)
+
+
+# UINT8 data (README "Data precision": INT8 and UINT8 input numbers)
+
+def test_u8_rounding_decode_and_brute_force():
+    r = oracle.u8_round(np.array([0.5, 1.5, 2.5, 254.5, 255.4, 255.6, 300.0, -3.0, -0.4, 7.49],
+                                 np.float32))
+    assert r.tolist() == [0, 2, 2, 254, 255, 255, 255, 0, 0, 7]   # ties to even, clamped
+    # the C side reads every byte as its unsigned value (distance to 0 = v^2)
+    allb = np.arange(256, dtype=np.uint8).reshape(-1, 1).view(oracle.U8)
+    _, d1, _ = oracle.assign(allb, np.zeros((1, 1), np.float32))
+    assert np.array_equal(d1, np.arange(256, dtype=np.float64) ** 2)
+    # exact integer argmin against a pure-Python loop (ties to the lowest index)
+    rng = np.random.default_rng(4)
+    raw = rng.integers(0, 256, size=(40, 5)).astype(np.uint8)
+    Q = rng.integers(0, 256, size=(9, 5)).astype(np.float32)
+    Q[3] = Q[7]                                              # a tied pair
+    raw[0] = Q[3].astype(np.uint8)                           # exact hit on the pair
+    lab, d1, _ = oracle.assign(raw.view(oracle.U8), Q)
+    for i in range(len(raw)):
+        dd = [sum((int(raw[i, t]) - int(Q[j, t])) ** 2 for t in range(5)) for j in range(len(Q))]
+        assert lab[i] == dd.index(min(dd)) and d1[i] == min(dd)
+    assert lab[0] == 3 and d1[0] == 0
+    # the GPU's form of the same search: rows and codes shifted by -128 as int8
+    s_lab, s_d1, _ = oracle.assign((raw.astype(np.int16) - 128).astype(np.int8), Q - 128)
+    assert np.array_equal(s_lab, lab) and np.array_equal(s_d1, d1)
+
+
+def test_u8_training_closing_mean_and_search():
+    X = datagen.make("codes-u8", 6000, 24, seed=5)
+    res = oracle.train(X, 48, 2.0, seed=3)
+    Xv = X.view(np.uint8).astype(np.float64)
+    for j in range(48):
+        m = res.labels == j
+        if m.any():
+            np.testing.assert_allclose(res.centroids[j], Xv[m].mean(axis=0), rtol=1e-6)
+    # the search uses the centroids rounded to uint8: x = 10 against 10.6 and
+    # 9.45: as values the second is nearer, but they round to 11 and 9, a tie
+    # that goes to the lower index
+    x = np.array([[10]], np.uint8).view(oracle.U8)
+    c2 = np.array([[10.6], [9.45]], np.float32)
+    assert oracle.assign(x, c2)[0].tolist() == [1]
+    assert oracle.assign(x, oracle.search_centroids(c2, x))[0].tolist() == [0]
