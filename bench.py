@@ -24,7 +24,8 @@ sys.path.insert(0, HERE)
 
 METRIC = "assign TFLOP/s (% MFMA peak) + s to Lloyd-25 MSE, 1M×768 k=4096"
 # MI355X dense (i8: TOP/s)
-MFMA_PEAK_TFLOPS = {"f32": 157.3, "bf16": 2516.6, "f16": 2516.6, "i8": 5033.2, "f8": 5033.2}
+MFMA_PEAK_TFLOPS = {"f32": 157.3, "bf16": 2516.6, "f16": 2516.6, "i8": 5033.2, "u8": 5033.2,
+                    "f8": 5033.2}
 HBM_PEAK_GBS = 8000.0
 
 DESCR = {
@@ -54,7 +55,7 @@ def assign_kernel_name(dtype: str, d: int) -> str:
     dtype and width (the dispatch rule of launch_assign in assign.hip)."""
     if dtype in ("bf16", "f16") and d in (32, 64, 96, 128):
         return f"assign_bf16_kernel (points resident in registers, 32x32x16 {dtype} MFMA)"
-    if d % {"bf16": 8, "f16": 8, "i8": 16, "f8": 16}.get(dtype, 4) == 0:
+    if d % {"bf16": 8, "f16": 8, "i8": 16, "u8": 16, "f8": 16}.get(dtype, 4) == 0:
         return "assign_ring_kernel (direct-to-LDS stage ring, 16x16 MFMA)"
     return "assign_kernel (register-staged stages, 16x16 MFMA)"
 
@@ -88,16 +89,28 @@ def batch_sizes(rc: dict) -> list:
     return out
 
 
-def make_data(name: str, W: dict, torch, codes: str = "", mm=None, fp16: bool = False):
+def make_data(name: str, W: dict, torch, codes: str = "", mm=None, fp16: bool = False,
+              u8: bool = False):
     """Training data, held-out data (fp32 or bf16, on the GPU) and the host
     copy of the training data (None when it is made on the GPU). codes
     ("int8" or "fp8"): the training rows as codes, calibrated on the first
     65536 rows (the data is an iid draw) and encoded on the GPU; returns the
     codes, the held-out data, the host codes (int8, or E4M3 bit patterns) and
     (shift, scale, encode seconds, decode function). fp16: the training rows
-    converted once to fp16 on the GPU (held-out rows stay fp32)."""
+    converted once to fp16 on the GPU (held-out rows stay fp32). u8: the
+    rows (integers in [0, 255]) stored as uint8 on the GPU, exactly."""
     from mini_means_amd import datagen
     t0 = time.time()
+    if u8:
+        Xf = torch.from_numpy(datagen.make(W["gen"], W["n"], W["d"])).cuda()
+        Xh = torch.from_numpy(datagen.make(W["gen"], W["heldout"], W["d"], split=1)).cuda()
+        X = Xf.to(torch.uint8)
+        if not torch.equal(X.float(), Xf):
+            raise SystemExit("--uint8 needs integer data in [0, 255] (the sift workload)")
+        del Xf
+        torch.cuda.synchronize()
+        log(f"uint8 data {tuple(X.shape)}; data in {time.time() - t0:.1f}s")
+        return X, Xh, X.cpu().numpy().view(datagen.U8), None
     if fp16:
         Xf = torch.from_numpy(datagen.make(W["gen"], W["n"], W["d"])).cuda()
         Xh = torch.from_numpy(datagen.make(W["gen"], W["heldout"], W["d"], split=1)).cuda()
@@ -195,10 +208,10 @@ def first_crossing(mm, X, Xh, k, T, rc, target, seed, torch, bf16_search=False,
     return dict(T=T, per_pass=rows, first=hit)
 
 
-def cpu_baseline(Xhost, C, k, d, budget_s: float) -> dict:
+def cpu_baseline(Xhost, C, k, d, budget_s: float, unit: str = "TFLOP/s") -> dict:
     """The CPU oracle's assignment (fp64 brute force, OpenMP over rows) on a
-    bounded sample of the workload's rows, in the metric's unit (int8 codes:
-    against the centroids' codes)."""
+    bounded sample of the workload's rows, in the metric's unit (codes and
+    uint8 data: against the centroids rounded to the search format)."""
     import numpy as np
     import oracle
     C = oracle.search_centroids(C, Xhost)
@@ -215,7 +228,7 @@ def cpu_baseline(Xhost, C, k, d, budget_s: float) -> dict:
     oracle.assign(sample, C, nthreads=cores)
     dt = time.perf_counter() - t0
     tflops = 2.0 * rows * k * d / dt / 1e12
-    return dict(value=round(tflops, 6), unit="TFLOP/s", cores=cores, kind="oracle",
+    return dict(value=round(tflops, 6), unit=unit, cores=cores, kind="oracle",
                 sample=f"{rows} random training rows x all {k} centroids (fp64 brute force, "
                        f"{dt:.1f}s)")
 
@@ -248,6 +261,9 @@ def main() -> int:
     ap.add_argument("--fp16", action="store_true",
                     help="README \"Data precision\", FP16: the rows converted once to fp16 on "
                          "the GPU (fp16 search, fp32 sums); held-out MSE in fp32")
+    ap.add_argument("--uint8", action="store_true",
+                    help="README \"Data precision\", UINT8: the SIFT-like rows (integers in "
+                         "[0, 255]) stored as uint8 (exact integer search); held-out MSE in fp32")
     ap.add_argument("--print-source-sha", action="store_true")
     args = ap.parse_args()
     if args.print_source_sha:
@@ -280,19 +296,22 @@ def main() -> int:
     codes_fmt = ("int8" if args.int8 else "fp8" if args.fp8 else "") if W["dtype"] == "f32" else ""
     i8 = codes_fmt == "int8"
     f16 = bool(args.fp16) and W["dtype"] == "f32" and not codes_fmt
-    es = 2 if (W["dtype"] == "bf16" or f16) else (1 if codes_fmt else 4)
+    u8 = bool(args.uint8) and W["dtype"] == "f32" and not codes_fmt and not f16
+    es = 2 if (W["dtype"] == "bf16" or f16) else (1 if (codes_fmt or u8) else 4)
     flops = float(sum(2.0 * b * k * d for b in sizes))
-    bsearch = bool(args.bf16_search) and W["dtype"] == "f32" and not codes_fmt and not f16
+    bsearch = (bool(args.bf16_search) and W["dtype"] == "f32" and not codes_fmt and not f16
+               and not u8)
     # arithmetic type of the search
-    sdtype = ("bf16" if bsearch else "f16" if f16
+    sdtype = ("bf16" if bsearch else "f16" if f16 else "u8" if u8
               else {"int8": "i8", "fp8": "f8"}.get(codes_fmt, W["dtype"]))
     sph = bool(args.spherical) and not codes_fmt
     tag = (args.workload + ("_bf16search" if bsearch else "") + ("_spherical" if sph else "")
-           + (f"_{codes_fmt}" if codes_fmt else "") + ("_fp16" if f16 else ""))
+           + (f"_{codes_fmt}" if codes_fmt else "") + ("_fp16" if f16 else "")
+           + ("_uint8" if u8 else ""))
     if sph:
         args.no_ttt = True   # the Lloyd-25 target is Euclidean
 
-    X, Xh, Xhost, codes = make_data(args.workload, W, torch, codes_fmt, mm, f16)
+    X, Xh, Xhost, codes = make_data(args.workload, W, torch, codes_fmt, mm, f16, u8)
 
     # warm-up (untimed)
     if Wm > 0:
@@ -325,7 +344,7 @@ def main() -> int:
     a_ms = prof["ms_assign"]
     assign_tflops = flops / (a_ms / 1e3) / 1e12 if a_ms > 0 else None
     peak = MFMA_PEAK_TFLOPS[sdtype]
-    unit = "TOP/s" if i8 else "TFLOP/s"
+    unit = "TOP/s" if (i8 or u8) else "TFLOP/s"
     group_bytes = float(sum(b * d * es + 4 * b + 4 * k * d for b in sizes))
     update_bytes = float(K * (4 * 4 * k * d))   # read s, S, C; write S, C (+ counts, small)
     g_ms = prof["ms_group"]
@@ -356,6 +375,7 @@ def main() -> int:
                    else "int8 codes (exact integer search; sums in fp32)" if i8
                    else "FP8 E4M3 codes (FP8 products, fp32 sums)" if codes_fmt == "fp8"
                    else "fp16 data (fp16 products, fp32 sums)" if f16
+                   else "uint8 data (exact integer search; sums in fp32)" if u8
                    else ("bf16" if W["dtype"] == "bf16" else "fp32 (exact)"),
                    "mode": "spherical" if sph else "euclidean"},
         "mfma_peak_frac": round(value / peak, 4),
@@ -434,7 +454,7 @@ def main() -> int:
 
     if not args.no_cpu and Xhost is not None:
         C = out.centroids.cpu().numpy()
-        line["cpu_baseline"] = cpu_baseline(Xhost, C, k, d, args.cpu_seconds)
+        line["cpu_baseline"] = cpu_baseline(Xhost, C, k, d, args.cpu_seconds, unit)
         log(f"cpu baseline {line['cpu_baseline']}")
 
     print(json.dumps(line), flush=True)

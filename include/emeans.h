@@ -21,7 +21,8 @@
  *   - X, centroids, labels and dists are DEVICE pointers (HIP device memory on
  *     the current device), row-major and contiguous, owned by the caller. The
  *     library never copies data between host and device for the caller.
- *   - X is n x d, fp32, bf16, fp16, int8 codes or FP8 E4M3 codes (opts->dtype).
+ *   - X is n x d, fp32, bf16, fp16, int8 codes, uint8 values or FP8 E4M3 codes
+ *     (opts->dtype).
  *     Centroids are always k x d fp32 (for code data: in code space). Labels
  *     are int32 in [0, k). Distances are fp32 squared L2.
  *   - Work is queued on opts->stream (a hipStream_t; NULL = the null stream).
@@ -70,12 +71,19 @@ extern "C" {
  * (nearest, ties to even, subnormals kept; magnitudes from 65520 up become
  * infinity, as the README's table of out-of-range values states), multiplying
  * in fp16 and accumulating in fp32. Running sums and centroids are fp32. */
+/* EMEANS_U8: X holds uint8 values 0..255 (README "Data precision": INT8 and
+ * UINT8 input numbers, e.g. raw descriptor bytes), used as they are. Running
+ * sums and centroids are fp32 averages of the values; the search compares
+ * each row exactly, in integers, with the centroids rounded to the nearest
+ * uint8 (ties to even, clamped to [0, 255]), so labels and distances are
+ * exact. Requires d <= 43919 and no spherical mode, as int8. */
 enum emeans_dtype {
   EMEANS_F32 = 0,
   EMEANS_BF16 = 1,
   EMEANS_I8 = 2,
   EMEANS_F8 = 3,
-  EMEANS_F16 = 4
+  EMEANS_F16 = 4,
+  EMEANS_U8 = 5
 };
 
 enum emeans_status {
@@ -119,7 +127,7 @@ typedef struct emeans_opts {
                                  nearest-centroid search only, and the distances are
                                  those of the rounded vectors; grouping, running sums
                                  and centroids use the fp32 rows. 0: fp32 X is searched
-                                 in fp32 (exact). Ignored for bf16 and int8 X. */
+                                 in fp32 (exact). Ignored for X of other types. */
   int32_t spherical;          /* 1: spherical e-means (README "Spherical e-means"):
                                  every centroid is its running average rescaled to
                                  norm 1 before use (a zero centroid stays zero), each
@@ -129,8 +137,8 @@ typedef struct emeans_opts {
                                  2 - 2 x similarity. Vectors are not normalised (nor
                                  checked): pass unit-norm rows for cosine semantics.
                                  emeans_assign: labels by the highest dot product with
-                                 C as given, dists[i] = that similarity. fp32 or
-                                 bf16 X only (EINVAL with int8 or FP8 X). */
+                                 C as given, dists[i] = that similarity. fp32, bf16
+                                 or fp16 X only (EINVAL with int8, uint8 or FP8 X). */
   int32_t lloyd;              /* 1: plain Lloyd iterations instead of e-means (the
                                  baseline of the blog's Lloyd section, the loss
                                  e-means is timed against): each of the T passes
@@ -218,7 +226,9 @@ int emeans_train(const void* X, int64_t n, int32_t d, int32_t k, double T, uint6
  * centroids with opts->bf16_search (rows and centroids rounded to bf16, the
  * distances those of the rounded vectors; workspace n x d bf16). For int8 X
  * the centroids (code space) are rounded to int8 codes and the labels and
- * distances are exact for the codes (see EMEANS_I8).
+ * distances are exact for the codes (see EMEANS_I8); likewise for uint8 X
+ * with the centroids rounded to uint8 (EMEANS_U8). fp16 X is searched with
+ * the centroids rounded to fp16 and FP8 X with them rounded to E4M3.
  *   X        device, n x d, opts->dtype      C       device, k x d fp32
  *   labels   device, n int32 output          dists   device, n fp32 output or NULL
  * Errors: EINVAL (n < 0, d < 1, k < 1, n >= 2^31, NULL pointers), EDTYPE,

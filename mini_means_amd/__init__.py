@@ -23,7 +23,7 @@ LIB_PATH = os.path.join(_PKG, "_lib", "libemeans.so")
 HEADER = os.path.join(os.path.dirname(_PKG), "include", "emeans.h")
 
 MAX_PASSES = 64
-F32, BF16, I8, F8, F16 = 0, 1, 2, 3, 4
+F32, BF16, I8, F8, F16, U8 = 0, 1, 2, 3, 4, 5
 LAWS = {"auto": 0, "throughput": 1, "quality": 2}
 STATUS = {0: "OK", -1: "EINVAL", -2: "EDTYPE", -3: "ENOMEM", -4: "EHIP", -5: "ENOTDEVICE"}
 
@@ -168,8 +168,10 @@ def _dtype_of(X) -> int:
         return F8
     if X.dtype == torch.float16:
         return F16
-    raise EmeansError(f"EDTYPE: {X.dtype} not supported (float32, bfloat16, float16, int8 or "
-                      f"float8_e4m3fn)")
+    if X.dtype == torch.uint8:
+        return U8
+    raise EmeansError(f"EDTYPE: {X.dtype} not supported (float32, bfloat16, float16, int8, "
+                      f"uint8 or float8_e4m3fn)")
 
 
 def _stream_ptr(X, stream):
@@ -395,13 +397,13 @@ class Stream:
         self.n = int(n)
         self.device = start.device
         codes = {None: F32, torch.float32: F32, torch.bfloat16: BF16, torch.int8: I8,
-                 torch.float8_e4m3fn: F8, torch.float16: F16}
+                 torch.float8_e4m3fn: F8, torch.float16: F16, torch.uint8: U8}
         code = codes.get(dtype, -1)
         if code < 0:
-            raise EmeansError(f"EDTYPE: {dtype} not supported (float32, bfloat16, float16, int8 "
-                              f"or float8_e4m3fn)")
+            raise EmeansError(f"EDTYPE: {dtype} not supported (float32, bfloat16, float16, int8, "
+                              f"uint8 or float8_e4m3fn)")
         self.dtype = {F32: torch.float32, BF16: torch.bfloat16, I8: torch.int8,
-                      F8: torch.float8_e4m3fn, F16: torch.float16}[code]
+                      F8: torch.float8_e4m3fn, F16: torch.float16, U8: torch.uint8}[code]
         self._stream = stream if stream is not None else torch.cuda.current_stream(self.device)
         with torch.cuda.device(self.device):
             o = _opts(code, batch_law, batch_size, alpha0, unused_threshold, finalize, profile,

@@ -197,20 +197,22 @@ struct Arena {
 // arguments and limits.
 constexpr int32_t kMaxDimI8 = 43919;  // int8 search: |2 x.q| + |q|^2 < 2^31
 
-// dtype supported; int8 codes: dimension limit and no spherical mode.
+// dtype supported; int8 codes and uint8 data: dimension limit and no
+// spherical mode; FP8 codes: no spherical mode.
 bool dtype_known(int32_t dtype) {
   return dtype == EMEANS_F32 || dtype == EMEANS_BF16 || dtype == EMEANS_I8 ||
-         dtype == EMEANS_F8 || dtype == EMEANS_F16;
+         dtype == EMEANS_F8 || dtype == EMEANS_F16 || dtype == EMEANS_U8;
 }
 
 int check_dtype(int32_t d, const emeans_opts* opts) {
   const int32_t dtype = opts ? opts->dtype : EMEANS_F32;
   if (!dtype_known(dtype))
     return fail(EMEANS_EDTYPE,
-                "dtype %d not supported (fp32 = 0, bf16 = 1, int8 = 2, fp8 = 3, fp16 = 4)", dtype);
-  if (dtype == EMEANS_I8 && d > kMaxDimI8)
-    return fail(EMEANS_EINVAL, "int8 data needs d <= %d (got %d)", kMaxDimI8, d);
-  if ((dtype == EMEANS_I8 || dtype == EMEANS_F8) && opts->spherical)
+                "dtype %d not supported (fp32 = 0, bf16 = 1, int8 = 2, fp8 = 3, fp16 = 4, "
+                "uint8 = 5)", dtype);
+  if ((dtype == EMEANS_I8 || dtype == EMEANS_U8) && d > kMaxDimI8)
+    return fail(EMEANS_EINVAL, "int8 and uint8 data need d <= %d (got %d)", kMaxDimI8, d);
+  if ((dtype == EMEANS_I8 || dtype == EMEANS_F8 || dtype == EMEANS_U8) && opts->spherical)
     return fail(EMEANS_EINVAL, "spherical e-means takes fp32, bf16 or fp16 data");
   return EMEANS_OK;
 }
@@ -270,8 +272,8 @@ struct emeans_model {
   Recipe r;
   hipStream_t st = nullptr;
   int dt = EMEANS_F32;  // emeans_dtype of X
-  bool bf16 = false, bsearch = false, sbf = false, i8 = false, f8 = false, f16 = false,
-       sph = false, profile = false;
+  bool bf16 = false, bsearch = false, sbf = false, i8 = false, u8 = false, f8 = false,
+       f16 = false, sph = false, profile = false;
   bool no_finalize = false;
   double slow_k = 0.0;             // slow EMA: kappa (0 = off)
   float* slow_out = nullptr;       // caller's table for the slow centroids
@@ -305,7 +307,7 @@ struct emeans_model {
         *n0 = nullptr, *pair_n = nullptr, *wlive = nullptr;
   float *N2 = nullptr, *S2 = nullptr;  // slow pair (slow EMA)
   uint16_t *chat = nullptr, *xb = nullptr;  // chat: bf16 or (fp16 data) fp16 copy of C
-  int8_t* cq = nullptr;   // int8 codes of C (int8 data)
+  int8_t* cq = nullptr;   // int8 codes of C (int8 data; shifted uint8 codes for uint8 data)
   uint8_t* cf = nullptr;  // E4M3 codes of C (FP8 data)
   // per pass: [0, P) sum of distances, [P, 3P) sum n^2 and sum n, [3P, 4P) splits (int64)
   double* dstat = nullptr;
@@ -339,7 +341,7 @@ struct emeans_model {
 
   // Centroid table the search reads for rows of type dt.
   const void* search_table() const {
-    return i8 ? (const void*)cq
+    return (i8 || u8) ? (const void*)cq
            : f8 ? (const void*)cf
            : (bf16 || f16) ? (const void*)chat : (const void*)C;
   }
@@ -349,7 +351,8 @@ struct emeans_model {
                       pair_i, pair_n, rv_pos, rv_head, rv_cbase, rv_clen, rv_heads, rv_list,
                       rv_nheads, counters, count_only ? nullptr : dlog,
                       count_only ? 0 : log_cap, count_only ? 1 : 0, sph ? 1 : 0, wlive,
-                      f16 ? 1 : 0, slow_started ? N2 : nullptr, slow_started ? S2 : nullptr};
+                      f16 ? 1 : 0, slow_started ? N2 : nullptr, slow_started ? S2 : nullptr,
+                      u8 ? 1 : 0};
   }
 
   // Recipe, options and workspace; C = external (the caller's buffer) or own.
@@ -383,6 +386,7 @@ struct emeans_model {
     bsearch = dtype == EMEANS_F32 && opts && opts->bf16_search;  // fp32 rows searched in bf16 (xb)
     sbf = bf16 || bsearch;  // the search runs in bf16 against chat
     i8 = dtype == EMEANS_I8;  // the search runs in int8 against cq
+    u8 = dtype == EMEANS_U8;  // the same integer search on rows and codes shifted by -128
     f8 = dtype == EMEANS_F8;  // the search runs in FP8 against cf
     f16 = dtype == EMEANS_F16;  // the search runs in fp16 against chat
     sph = opts && opts->spherical;
@@ -433,7 +437,7 @@ struct emeans_model {
     }
     ar.want(&bias, (size_t)k);
     if (sbf || f16) ar.want(&chat, kd);
-    if (i8) ar.want(&cq, kd);
+    if (i8 || u8) ar.want(&cq, kd);
     if (f8) ar.want(&cf, kd);
     if (bsearch) ar.want(&xb, (size_t)B * d);
     ar.want(&dstat, (size_t)4 * EMEANS_MAX_PASSES);
@@ -504,7 +508,7 @@ struct emeans_model {
     const float beta = slow ? (float)((double)a / slow_k) : 0.0f;
     const float b2 = 1.0f - beta;
     HIP_RET(timed(kUpdate, [&] {
-      return launch_ema(k, d, a, b, counts, s_acc, N, S, C, bias, chat, f16, cq, cf, pass_counts,
+      return launch_ema(k, d, a, b, counts, s_acc, N, S, C, bias, chat, f16, cq, u8, cf, pass_counts,
                         last ? LS : nullptr, sph, beta, b2, slow ? N2 : nullptr,
                         slow ? S2 : nullptr, st);
     }));
@@ -627,7 +631,8 @@ int emeans_assign(const void* X, int64_t n, int32_t d, const float* C, int32_t k
   const int32_t dtype = opts ? opts->dtype : EMEANS_F32;
   if (!dtype_known(dtype))
     return fail(EMEANS_EDTYPE,
-                "dtype %d not supported (fp32 = 0, bf16 = 1, int8 = 2, fp8 = 3, fp16 = 4)", dtype);
+                "dtype %d not supported (fp32 = 0, bf16 = 1, int8 = 2, fp8 = 3, fp16 = 4, "
+                "uint8 = 5)", dtype);
   if (n < 0 || n >= ((int64_t)1 << 31)) return fail(EMEANS_EINVAL, "n out of range (%lld)", (long long)n);
   if (d < 1) return fail(EMEANS_EINVAL, "d must be >= 1");
   if (k < 1) return fail(EMEANS_EINVAL, "k must be >= 1");
@@ -641,6 +646,7 @@ int emeans_assign(const void* X, int64_t n, int32_t d, const float* C, int32_t k
   hipStream_t st = static_cast<hipStream_t>(opts ? opts->stream : nullptr);
   const bool bf16 = dtype == EMEANS_BF16;
   const bool i8 = dtype == EMEANS_I8;
+  const bool u8 = dtype == EMEANS_U8;
   const bool f8 = dtype == EMEANS_F8;
   const bool f16 = dtype == EMEANS_F16;
   const bool bsearch = dtype == EMEANS_F32 && opts && opts->bf16_search;  // fp32 rows in bf16
@@ -654,16 +660,16 @@ int emeans_assign(const void* X, int64_t n, int32_t d, const float* C, int32_t k
   Arena ar;
   ar.want(&bias, (size_t)k);
   if (bf16 || bsearch || f16) ar.want(&chat, (size_t)k * d);
-  if (i8) ar.want(&cq, (size_t)k * d);
+  if (i8 || u8) ar.want(&cq, (size_t)k * d);
   if (f8) ar.want(&cf, (size_t)k * d);
   if (bsearch) ar.want(&xb, (size_t)n * d);
   rc = EMEANS_OK;
   HIP_TRY(ar.alloc(&base, st));
-  HIP_TRY(launch_prep(C, k, d, bias, chat, f16, cq, cf, sph, st));
+  HIP_TRY(launch_prep(C, k, d, bias, chat, f16, cq, u8, cf, sph, st));
   if (bsearch) HIP_TRY(launch_cast_rows(static_cast<const float*>(X), d, nullptr, (int)n, xb, st));
   {
     const int sdt = bsearch ? EMEANS_BF16 : dtype;
-    const void* cs = i8 ? (const void*)cq
+    const void* cs = (i8 || u8) ? (const void*)cq
                      : f8 ? (const void*)cf
                      : (bf16 || bsearch || f16) ? (const void*)chat : (const void*)C;
     HIP_TRY(launch_assign(sdt, bsearch ? (const void*)xb : X, d, nullptr, (int)n, cs, bias, k,
@@ -702,7 +708,7 @@ int emeans_train(const void* X, int64_t n, int32_t d, int32_t k, double T, uint6
   // starting centroids: k distinct rows (first k entries of the init permutation)
   HIP_RET(launch_init_centroids(m.dt, X, d, make_perm_key((uint64_t)n, seed, kStreamInit, 0), k,
                                 m.C, m.sph, st));
-  HIP_RET(launch_prep(m.C, k, d, m.bias, m.chat, m.f16, m.cq, m.cf, m.sph, st));
+  HIP_RET(launch_prep(m.C, k, d, m.bias, m.chat, m.f16, m.cq, m.u8, m.cf, m.sph, st));
 
   for (int e = 0; e < r.npass && m.t < run_steps; ++e) {
     const bool last = e == r.npass - 1;
@@ -750,7 +756,7 @@ int emeans_begin(int64_t n, int32_t d, int32_t k, double T, uint64_t seed, const
   }
   if (rc == EMEANS_OK) {
     const hipError_t e2 =
-        launch_prep(m->C, k, d, m->bias, m->chat, m->f16, m->cq, m->cf, m->sph, m->st);
+        launch_prep(m->C, k, d, m->bias, m->chat, m->f16, m->cq, m->u8, m->cf, m->sph, m->st);
     if (e2 != hipSuccess) rc = fail(EMEANS_EHIP, "centroid prep: %s", hipGetErrorString(e2));
   }
   if (rc != EMEANS_OK) {

@@ -26,6 +26,12 @@
 // array then holds -|q|^2 as int32), so labels and distances are exact.
 // With d <= 43919 no intermediate leaves the int32 range:
 // |2 x.q| + |q|^2 <= d (2 * 128 * 127 + 127^2) < 2^31.
+//
+// uint8 rows run the same integer search after a shift by -128 (u ^ 0x80
+// read as int8 is u - 128), applied to the point chunks as they leave LDS or
+// memory; the centroids' codes are stored already shifted. Distances are
+// unchanged by the shift, and per dimension the score 2 x'q' - q'^2 lies in
+// [-48896, 16384], so d <= 43919 keeps the sum inside int32 here too.
 #include "kernels.hpp"
 
 namespace emk {
@@ -38,8 +44,8 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 typedef int32_t i32x4 __attribute__((ext_vector_type(4)));
 
-// Per data type (0 fp32, 1 bf16, 2 int8, 3 FP8 E4M3, 4 fp16): element bytes,
-// the accumulator tile and the score type.
+// Per data type (0 fp32, 1 bf16, 2 int8, 3 FP8 E4M3, 4 fp16, 5 uint8):
+// element bytes, the accumulator tile and the score type.
 template <int DT>
 struct Fmt {
   static constexpr int ES = 4;
@@ -65,11 +71,25 @@ struct Fmt<3> {
   using Sc = float;
 };
 template <>
+struct Fmt<5> : Fmt<2> {};
+template <>
 struct Fmt<4> {
   static constexpr int ES = 2;
   using Acc = f32x4;
   using Sc = float;
 };
+
+// int8 and uint8 rows: the exact integer search
+template <int DT>
+constexpr bool kIntSearch = DT == 2 || DT == 5;
+
+// A 16-byte chunk of point data in the search's form: uint8 bytes shifted
+// by -128 into int8 (the centroid codes are stored shifted already).
+template <int DT>
+__device__ __forceinline__ u32x4 point_chunk(u32x4 w) {
+  if constexpr (DT == 5) return w ^ 0x80808080u;
+  return w;
+}
 
 constexpr int kWM = 4;               // waves along the centroid (M) dimension
 constexpr int kWN = 2;               // waves along the point (N) dimension
@@ -88,7 +108,8 @@ __device__ __forceinline__ u32x4 load_slab16(const unsigned char* row, int col, 
   // 16 bytes of a row starting at element `col`. With whole 16-byte chunks
   // per row (VEC) the address is clamped into the row and the caller zeroes
   // chunks past the end when it stores them, so the load stays in flight
-  // across the MFMA work; otherwise elements past the end read as zero.
+  // across the MFMA work; otherwise elements past the end read as zero (as
+  // 0x80 for uint8 rows, which point_chunk maps to zero).
   constexpr int ES = Fmt<DT>::ES;
   constexpr int EPV = 16 / ES;
   if constexpr (VEC) {
@@ -98,7 +119,7 @@ __device__ __forceinline__ u32x4 load_slab16(const unsigned char* row, int col, 
 #pragma unroll
     for (int e = 0; e < EPV; ++e) {
       const int c = col + e;
-      uint32_t v = 0u;
+      uint32_t v = DT == 5 ? 0x80u : 0u;
       if (c < d) {
         if constexpr (ES == 1)
           v = (uint32_t)row[c];
@@ -114,13 +135,14 @@ __device__ __forceinline__ u32x4 load_slab16(const unsigned char* row, int col, 
   }
 }
 
-// Sum of squares of the elements in a 16-byte chunk (exact integer for int8).
+// Sum of squares of the elements in a 16-byte chunk (exact integer for int8;
+// uint8 chunks arrive shifted into int8 by point_chunk).
 template <int DT>
 __device__ __forceinline__ typename Fmt<DT>::Sc sumsq16(u32x4 w) {
   typename Fmt<DT>::Sc s = 0;
 #pragma unroll
   for (int e = 0; e < 4; ++e) {
-    if constexpr (DT == 2) {
+    if constexpr (kIntSearch<DT>) {
 #pragma unroll
       for (int b = 0; b < 4; ++b) {
         const int v = (int)(int8_t)(w[e] >> (8 * b));
@@ -154,7 +176,7 @@ __device__ __forceinline__ typename Fmt<DT>::Sc sumsq16(u32x4 w) {
 template <int DT>
 __device__ __forceinline__ void mfma_slice(typename Fmt<DT>::Acc (&acc)[4][4], const u32x4 (&a)[4],
                                            const u32x4 (&b)[4]) {
-  if constexpr (DT == 2) {
+  if constexpr (kIntSearch<DT>) {
 #pragma unroll
     for (int mb = 0; mb < 4; ++mb)
 #pragma unroll
@@ -213,7 +235,7 @@ __device__ __forceinline__ void panel_bias(const float* bias, int k, int j0, int
 #pragma unroll
     for (int v = 0; v < 4; ++v) {
       const int j = j0 + mb * 16 + 4 * (lane >> 4) + v;
-      if constexpr (DT == 2)
+      if constexpr (kIntSearch<DT>)
         bt[mb][v] = j < k ? reinterpret_cast<const int32_t*>(bias)[j] : 0;
       else
         bt[mb][v] = j < k ? bias[j] : -__builtin_inff();
@@ -234,7 +256,7 @@ __device__ __forceinline__ void fold_panel(const typename Fmt<DT>::Acc (&acc)[4]
 #pragma unroll
       for (int v = 0; v < 4; ++v) {
         const int j = j0 + mb * 16 + 4 * (lane >> 4) + v;
-        if constexpr (DT == 2) {
+        if constexpr (kIntSearch<DT>) {
           const int sc = 2 * acc[mb][nb][v] + bt[mb][v];
           if (j < k && sc > best[nb]) {
             best[nb] = sc;
@@ -257,7 +279,7 @@ __device__ __forceinline__ void init_tile(typename Fmt<DT>::Acc (&acc)[4][4],
   for (int mb = 0; mb < 4; ++mb)
 #pragma unroll
     for (int nb = 0; nb < 4; ++nb) {
-      if constexpr (DT == 2)
+      if constexpr (kIntSearch<DT>)
         acc[mb][nb] = i32x4{0, 0, 0, 0};
       else
         acc[mb][nb] = bt[mb];
@@ -318,7 +340,7 @@ __device__ __forceinline__ double finish_points(typename Fmt<DT>::Sc (&best)[4],
     if (slot < nrows) {
       labels[slot] = j;
       if (counts) atomicAdd(&counts[j], 1);
-      if constexpr (DT == 2) {
+      if constexpr (kIntSearch<DT>) {
         const long long dist = (long long)xn_s[p] - (long long)sc;
         if (dists) dists[slot] = (float)dist;
         dsum = (double)dist;
@@ -379,11 +401,11 @@ __global__ __launch_bounds__(kThreads, 1) void assign_kernel(
     const int col = s * EPS + ch * EPV;
     colin = col < d;
 #pragma unroll
-    for (int i = 0; i < kXL; ++i) rx[i] = load_slab16<DT, false>(xrow[i], col, d);
+    for (int i = 0; i < kXL; ++i) rx[i] = point_chunk<DT>(load_slab16<DT, false>(xrow[i], col, d));
 #pragma unroll
     for (int i = 0; i < kCL; ++i) {
       const int j = min(panel * kTC + rb + kRowsPerPass * i, k - 1);
-      rc[i] = load_slab16<DT, false>(Cs + (size_t)j * rowbytes, col, d);
+      rc[i] = load_slab16<DT == 5 ? 2 : DT, false>(Cs + (size_t)j * rowbytes, col, d);
     }
   };
   auto sstore = [&](int buf) {
@@ -404,7 +426,7 @@ __global__ __launch_bounds__(kThreads, 1) void assign_kernel(
   int bidx[4];
 #pragma unroll
   for (int nb = 0; nb < 4; ++nb) {
-    best[nb] = DT == 2 ? (Sc)INT32_MIN : (Sc)-__builtin_inff();
+    best[nb] = kIntSearch<DT> ? (Sc)INT32_MIN : (Sc)-__builtin_inff();
     bidx[nb] = -1;
   }
   Sc xpart[kXL];  // |x|^2 partials of this thread's point-row slabs
@@ -631,7 +653,7 @@ __global__ __launch_bounds__(kThreads, 1) void assign_ring_kernel(
   int bidx[4];
 #pragma unroll
   for (int nb = 0; nb < 4; ++nb) {
-    best[nb] = DT == 2 ? (Sc)INT32_MIN : (Sc)-__builtin_inff();
+    best[nb] = kIntSearch<DT> ? (Sc)INT32_MIN : (Sc)-__builtin_inff();
     bidx[nb] = -1;
   }
   // |x|^2 partials: thread (rb, ch) covers chunk ch of point rows rb + kRowsPerPass i
@@ -673,8 +695,8 @@ __global__ __launch_bounds__(kThreads, 1) void assign_ring_kernel(
 #pragma unroll
       for (int i = 0; i < kXR; ++i)
         if (in)
-          xpart[i] += sumsq16<DT>(
-              *reinterpret_cast<const u32x4*>(cur + swz(rb + kRowsPerPass * i, ch)));
+          xpart[i] += sumsq16<DT>(point_chunk<DT>(
+              *reinterpret_cast<const u32x4*>(cur + swz(rb + kRowsPerPass * i, ch))));
     }
 #pragma unroll
     for (int kk = 0; kk < kSlab / 64; ++kk) {
@@ -686,7 +708,8 @@ __global__ __launch_bounds__(kThreads, 1) void assign_ring_kernel(
             cur + (kTP + wm * 64 + mb * 16 + (lane & 15)) * kSlab + pc);
 #pragma unroll
       for (int nb = 0; nb < 4; ++nb)
-        b[nb] = *reinterpret_cast<const u32x4*>(cur + (wn * 64 + nb * 16 + (lane & 15)) * kSlab + pc);
+        b[nb] = point_chunk<DT>(
+            *reinterpret_cast<const u32x4*>(cur + (wn * 64 + nb * 16 + (lane & 15)) * kSlab + pc));
       mfma_slice<DT>(acc, a, b);
       // the loads of stage t + 2, issued while the matrix core works on this
       // stage's first half
@@ -750,12 +773,17 @@ hipError_t launch_assign(int dt, const void* X, int d, const uint32_t* rows, int
   const auto* x = static_cast<const unsigned char*>(X);
   const auto* c = static_cast<const unsigned char*>(Cs);
   const bool aligned = ((uintptr_t)X % 16 == 0) && ((uintptr_t)Cs % 16 == 0);
-  const int epv = (dt == 2 || dt == 3) ? 16 : (dt == 1 || dt == 4) ? 8 : 4;  // per 16 bytes
+  const int epv = (dt == 2 || dt == 3 || dt == 5) ? 16 : (dt == 1 || dt == 4) ? 8 : 4;
   const bool ring = aligned && d % epv == 0;
   const int sm = sim ? 1 : 0;
 #define EMK_ASSIGN(KERNEL) \
   KERNEL<<<grid, block, 0, st>>>(x, d, rows, nrows, c, bias, k, labels, dists, counts, obj, sm)
-  if (dt == 4) {
+  if (dt == 5) {
+    if (ring)
+      EMK_ASSIGN(assign_ring_kernel<5>);
+    else
+      EMK_ASSIGN(assign_kernel<5>);
+  } else if (dt == 4) {
     if (ring)
       EMK_ASSIGN(assign_ring_kernel<4>);
     else

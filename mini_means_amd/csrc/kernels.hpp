@@ -12,7 +12,9 @@ namespace emk {
 // centroid by maximal score x.c - |c|^2/2 (equivalent to minimal squared
 // distance). dt is the search type of X and `Cs`: 0 fp32 (Cs = C), 1 bf16
 // (Cs = bf16 C-hat), 2 int8 (Cs = int8 codes q), 3 FP8 E4M3 (Cs = E4M3
-// codes of C, products accumulated in fp32), 4 fp16 (Cs = fp16 C-hat). `bias` = -|c|^2/2 computed
+// codes of C, products accumulated in fp32), 4 fp16 (Cs = fp16 C-hat), 5
+// uint8 (Cs = the uint8 codes of C shifted by -128 as int8; the rows are
+// shifted the same way inside the kernel, bias as for int8). `bias` = -|c|^2/2 computed
 // from Cs as fp32, except for int8, where it holds -|q|^2 as int32 and the
 // score is the exact integer 2 x.q - |q|^2. Writes labels[r], dists[r]
 // (optional), counts[label] += 1 (optional) and obj[0] += sum of distances
@@ -37,17 +39,18 @@ hipError_t launch_sample_rows_i32(const PermKey& pk, uint64_t start, int count, 
                                   hipStream_t st);
 
 // C[j] = X[pi(j)] as fp32, j < k (rescaled to norm 1 when sph); dt is the
-// data type of X: 0 fp32, 1 bf16, 2 int8, 3 FP8 E4M3, 4 fp16.
+// data type of X: 0 fp32, 1 bf16, 2 int8, 3 FP8 E4M3, 4 fp16, 5 uint8.
 hipError_t launch_init_centroids(int dt, const void* X, int d, const PermKey& pk, int k,
                                  float* C, bool sph, hipStream_t st);
 
 // bias[j] = -|c_j|^2 / 2 in the search format (0 when sph). At most one
 // search copy is non-null: Chat = bf16(C), or fp16(C) with chat_f16; Cq =
-// int8 codes q of C (nearest, clamped to +-127), and then bias[j] holds the
-// int32 -|q_j|^2 (the assign contract); Cf = E4M3 codes of C (nearest,
-// saturating at +-448).
+// int8 codes q of C (nearest, clamped to +-127; with cq_u8 the nearest uint8
+// value, clamped to [0, 255], minus 128), and then bias[j] holds the int32
+// -|q_j|^2 (the assign contract); Cf = E4M3 codes of C (nearest, saturating
+// at +-448).
 hipError_t launch_prep(const float* C, int k, int d, float* bias, uint16_t* Chat, bool chat_f16,
-                       int8_t* Cq, uint8_t* Cf, bool sph, hipStream_t st);
+                       int8_t* Cq, bool cq_u8, uint8_t* Cf, bool sph, hipStream_t st);
 
 // out[r] = bf16(X[rows[r]]) for r < nrows (rows NULL: row r), row-major.
 hipError_t launch_cast_rows(const float* X, int d, const uint32_t* rows, int nrows,
@@ -81,8 +84,8 @@ hipError_t launch_group(int dt, const void* X, int d, const uint32_t* order,
 // and 1 - beta = b2.
 hipError_t launch_ema(int k, int d, float a, float b, int32_t* counts, float* s_acc, float* N,
                       float* S, float* C, float* bias, uint16_t* Chat, bool chat_f16, int8_t* Cq,
-                      uint8_t* Cf, int32_t* pass_counts, float* LS, bool sph, float beta,
-                      float b2, float* N2, float* S2, hipStream_t st);
+                      bool cq_u8, uint8_t* Cf, int32_t* pass_counts, float* LS, bool sph,
+                      float beta, float b2, float* N2, float* S2, hipStream_t st);
 
 // out[j] = S2[j] / N2[j] where N2[j] > 0, else C[j] (N2 NULL: out = C);
 // rescaled to norm 1 with sph where N2[j] > 0.
@@ -96,7 +99,7 @@ struct ReviveArgs {
   float* C;
   float* bias;
   uint16_t* Chat;     // bf16 (fp16 with chat_f16) search copy of C, or NULL
-  int8_t* Cq;         // int8 search codes of C, or NULL
+  int8_t* Cq;         // int8 search codes of C (shifted uint8 codes with cq_u8), or NULL
   uint8_t* Cf;        // E4M3 search codes of C, or NULL
   double thr;
   uint64_t seed, step;
@@ -123,6 +126,7 @@ struct ReviveArgs {
   int chat_f16;       // Chat holds fp16 rather than bf16
   float* N2;          // slow pair (or NULL): a split copies both halves' N and S here
   float* S2;
+  int cq_u8;          // Cq holds shifted uint8 codes
 };
 // Dead-cluster check and donor draws (one workgroup), then the splits of the
 // running sums, one wave per donor chain.

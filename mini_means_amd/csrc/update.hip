@@ -91,6 +91,17 @@ __device__ __forceinline__ int8_t to_code_i8(float c) {
   return (int8_t)fminf(fmaxf(__builtin_rintf(c), -127.0f), 127.0f);
 }
 
+// Search code of a centroid of uint8 data: the nearest uint8 value (ties to
+// even, clamped to [0, 255]) shifted by -128 into int8, the form the integer
+// search compares the shifted rows with.
+__device__ __forceinline__ int8_t to_code_u8(float c) {
+  return (int8_t)((int)fminf(fmaxf(__builtin_rintf(c), 0.0f), 255.0f) - 128);
+}
+
+__device__ __forceinline__ int8_t to_code(float c, bool u8) {
+  return u8 ? to_code_u8(c) : to_code_i8(c);
+}
+
 // One wave per centroid: C[j] = X[pi(j)] converted to fp32 (rescaled to norm
 // 1 for spherical e-means).
 __global__ __launch_bounds__(256) void init_centroids_kernel(const unsigned char* X, int dt,
@@ -112,6 +123,8 @@ __global__ __launch_bounds__(256) void init_centroids_kernel(const unsigned char
       v = e4m3_to_f32(reinterpret_cast<const uint8_t*>(X)[row * (uint64_t)d + e]);
     else if (dt == 4)
       v = f16_to_f32(reinterpret_cast<const uint16_t*>(X)[row * (uint64_t)d + e]);
+    else if (dt == 5)
+      v = (float)X[row * (uint64_t)d + e];
     else
       v = reinterpret_cast<const float*>(X)[row * (uint64_t)d + e];
     C[(size_t)j * d + e] = v;
@@ -120,11 +133,11 @@ __global__ __launch_bounds__(256) void init_centroids_kernel(const unsigned char
 }
 
 // One wave per centroid: bias = -|c|^2/2 in the search format, Chat = bf16(c)
-// (bf16 search) or fp16(c) (fp16 data, hf), Cq = int8 codes of c (int8 data)
-// or Cf = E4M3 codes of c (FP8 data).
+// (bf16 search) or fp16(c) (fp16 data, hf), Cq = int8 codes of c (int8 data;
+// uint8 data, u8: the shifted uint8 codes) or Cf = E4M3 codes of c (FP8 data).
 __global__ __launch_bounds__(256) void prep_kernel(const float* C, int k, int d, float* bias,
-                                                   uint16_t* Chat, int hf, int8_t* Cq, uint8_t* Cf,
-                                                   int sph) {
+                                                   uint16_t* Chat, int hf, int8_t* Cq, int u8,
+                                                   uint8_t* Cf, int sph) {
   const int j = blockIdx.x * 4 + (threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
   if (j >= k) return;
@@ -137,7 +150,7 @@ __global__ __launch_bounds__(256) void prep_kernel(const float* C, int k, int d,
       Chat[(size_t)j * d + e] = h;
       c = half_to_f32(h, hf);
     } else if (Cq) {
-      const int8_t q = to_code_i8(c);
+      const int8_t q = to_code(c, u8);
       Cq[(size_t)j * d + e] = q;
       nq += (int)q * (int)q;
       continue;
@@ -278,15 +291,17 @@ __global__ void scatter_kernel(const int32_t* labels, const uint32_t* rows, int 
 }
 
 // Column unit `col` of a row as fp32 values: 16 bytes of fp32 / bf16 / fp16
-// (VEC), 4 bytes of int8 or E4M3 codes (VEC), or one element.
+// (VEC), 4 bytes of int8, uint8 or E4M3 codes (VEC), or one element.
 template <int DT, bool VEC>
 __device__ __forceinline__ void load_unit_dt(const unsigned char* base, int col, float* v) {
-  if constexpr (VEC && (DT == 2 || DT == 3)) {
+  if constexpr (VEC && (DT == 2 || DT == 3 || DT == 5)) {
     const uint32_t q = *reinterpret_cast<const uint32_t*>(base + (size_t)col * 4);
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
       if constexpr (DT == 3)
         v[e] = e4m3_to_f32((q >> (8 * e)) & 0xFFu);
+      else if constexpr (DT == 5)
+        v[e] = (float)((q >> (8 * e)) & 0xFFu);
       else
         v[e] = (float)(int8_t)(q >> (8 * e));
     }
@@ -318,6 +333,8 @@ __device__ __forceinline__ void load_unit_dt(const unsigned char* base, int col,
       v[0] = e4m3_to_f32(base[col]);
     else if constexpr (DT == 4)
       v[0] = f16_to_f32(reinterpret_cast<const uint16_t*>(base)[col]);
+    else if constexpr (DT == 5)
+      v[0] = (float)base[col];
     else
       v[0] = reinterpret_cast<const float*>(base)[col];
   }
@@ -337,9 +354,9 @@ __global__ __launch_bounds__(256) void group_kernel(const unsigned char* __restr
                                                     const int2* __restrict__ ovf,
                                                     const int32_t* __restrict__ ovf_n, int k,
                                                     int R, float* __restrict__ s_acc, int add) {
-  // element bytes: fp32 4, bf16 / fp16 2, int8 / E4M3 1; a column unit is 16
-  // bytes (4 for the 1-byte codes, which keeps the rows in flight within the
-  // register budget)
+  // element bytes: fp32 4, bf16 / fp16 2, int8 / uint8 / E4M3 1; a column
+  // unit is 16 bytes (4 for the 1-byte types, which keeps the rows in flight
+  // within the register budget)
   constexpr int ES = DT == 0 ? 4 : (DT == 1 || DT == 4) ? 2 : 1;
   constexpr int UB = ES == 1 ? 4 : 16;
   constexpr int EPV = VEC ? UB / ES : 1;  // elements per column unit
@@ -440,9 +457,9 @@ __global__ __launch_bounds__(256) void group_wave_kernel(const unsigned char* __
                                                          const int32_t* __restrict__ ovf_n,
                                                          int k, int R, float* __restrict__ s_acc,
                                                          int add) {
-  // element bytes: fp32 4, bf16 / fp16 2, int8 / E4M3 1; a column unit is 16
-  // bytes (4 for the 1-byte codes, which keeps the rows in flight within the
-  // register budget)
+  // element bytes: fp32 4, bf16 / fp16 2, int8 / uint8 / E4M3 1; a column
+  // unit is 16 bytes (4 for the 1-byte types, which keeps the rows in flight
+  // within the register budget)
   constexpr int ES = DT == 0 ? 4 : (DT == 1 || DT == 4) ? 2 : 1;
   constexpr int UB = ES == 1 ? 4 : 16;
   constexpr int EPV = VEC ? UB / ES : 1;  // elements per column unit
@@ -513,7 +530,7 @@ __global__ __launch_bounds__(256) void group_wave_kernel(const unsigned char* __
 // One wave per cluster: EMA of the running count and sum, centroid S/N,
 // search-format refresh, last-pass accumulation; resets counts and s_acc.
 // search format kept beside C: 0 none, 1 bf16 (Chat), 2 int8 (Cq), 3 E4M3 (Cf),
-// 4 fp16 (Chat)
+// 4 fp16 (Chat), 5 shifted uint8 (Cq)
 template <int SF>
 __global__ __launch_bounds__(256) void ema_kernel(int k, int d, float a, float b,
                                                   int32_t* counts, float* s_acc, float* N,
@@ -552,8 +569,8 @@ __global__ __launch_bounds__(256) void ema_kernel(int k, int d, float a, float b
       const uint16_t h = to_half_rne(c, SF == 4);
       Chat[idx] = h;
       c = half_to_f32(h, SF == 4);
-    } else if constexpr (SF == 2) {
-      const int8_t q = to_code_i8(c);
+    } else if constexpr (SF == 2 || SF == 5) {
+      const int8_t q = to_code(c, SF == 5);
       Cq[idx] = q;
       nq += (int)q * (int)q;
       continue;
@@ -564,7 +581,7 @@ __global__ __launch_bounds__(256) void ema_kernel(int k, int d, float a, float b
     }
     nrm += c * c;
   }
-  if constexpr (SF == 2) nq = wave_sum(nq);
+  if constexpr (SF == 2 || SF == 5) nq = wave_sum(nq);
   if (sph) {
     // spherical e-means: the running average rescaled to norm 1 (a centroid
     // without a count keeps its unit-norm value); the score is x.c, bias 0
@@ -577,7 +594,7 @@ __global__ __launch_bounds__(256) void ema_kernel(int k, int d, float a, float b
   if (lane == 0) {
     N[j] = Nn;
     if (N2) N2[j] = __fadd_rn(__fmul_rn(b2, N2[j]), __fmul_rn(beta, (float)n));
-    if constexpr (SF == 2)
+    if constexpr (SF == 2 || SF == 5)
       reinterpret_cast<int32_t*>(bias)[j] = -nq;
     else
       bias[j] = sph ? 0.0f : -0.5f * nrm;
@@ -942,7 +959,7 @@ __global__ __launch_bounds__(256) void split_kernel(ReviveArgs A) {
         cj = e4m3_to_f32(fj);
         ci = e4m3_to_f32(fi);
       } else if (A.Cq) {
-        const int8_t qj = to_code_i8(cj), qi = to_code_i8(ci);
+        const int8_t qj = to_code(cj, A.cq_u8), qi = to_code(ci, A.cq_u8);
         A.Cq[jj] = qj;
         A.Cq[ii] = qi;
         qni += (int)qi * (int)qi;
@@ -1076,9 +1093,9 @@ hipError_t launch_init_centroids(int dt, const void* X, int d, const PermKey& pk
 }
 
 hipError_t launch_prep(const float* C, int k, int d, float* bias, uint16_t* Chat, bool chat_f16,
-                       int8_t* Cq, uint8_t* Cf, bool sph, hipStream_t st) {
-  prep_kernel<<<(k + 3) / 4, 256, 0, st>>>(C, k, d, bias, Chat, chat_f16 ? 1 : 0, Cq, Cf,
-                                           sph ? 1 : 0);
+                       int8_t* Cq, bool cq_u8, uint8_t* Cf, bool sph, hipStream_t st) {
+  prep_kernel<<<(k + 3) / 4, 256, 0, st>>>(C, k, d, bias, Chat, chat_f16 ? 1 : 0, Cq,
+                                           cq_u8 ? 1 : 0, Cf, sph ? 1 : 0);
   return hipGetLastError();
 }
 
@@ -1128,7 +1145,7 @@ hipError_t launch_group(int dt, const void* X, int d, const uint32_t* order,
   const long long items = (long long)k + nb / R;
   const auto* x = static_cast<const unsigned char*>(X);
   // a vector unit is 16 B (4 fp32, 8 bf16 / fp16) or, for int8 / E4M3 codes, 4 B
-  const bool codes = dt == 2 || dt == 3;
+  const bool codes = dt == 2 || dt == 3 || dt == 5;
   const int per = (dt == 1 || dt == 4) ? 8 : 4;
   const bool aligned = (uintptr_t)X % (codes ? 4 : 16) == 0;
   const bool vec = aligned && d % per == 0;
@@ -1142,13 +1159,15 @@ hipError_t launch_group(int dt, const void* X, int d, const uint32_t* order,
     return launch_group_dt<3>(x, d, vec, ncol, order, off, ovf, ovf_n, k, R, items, s_acc, a, st);
   if (dt == 4)
     return launch_group_dt<4>(x, d, vec, ncol, order, off, ovf, ovf_n, k, R, items, s_acc, a, st);
+  if (dt == 5)
+    return launch_group_dt<5>(x, d, vec, ncol, order, off, ovf, ovf_n, k, R, items, s_acc, a, st);
   return launch_group_dt<0>(x, d, vec, ncol, order, off, ovf, ovf_n, k, R, items, s_acc, a, st);
 }
 
 hipError_t launch_ema(int k, int d, float a, float b, int32_t* counts, float* s_acc, float* N,
                       float* S, float* C, float* bias, uint16_t* Chat, bool chat_f16, int8_t* Cq,
-                      uint8_t* Cf, int32_t* pass_counts, float* LS, bool sph, float beta,
-                      float b2, float* N2, float* S2, hipStream_t st) {
+                      bool cq_u8, uint8_t* Cf, int32_t* pass_counts, float* LS, bool sph,
+                      float beta, float b2, float* N2, float* S2, hipStream_t st) {
   const dim3 grid((k + 3) / 4), block(256);
   const int sp = sph ? 1 : 0;
 #define EMK_EMA(SF)                                                                        \
@@ -1158,6 +1177,8 @@ hipError_t launch_ema(int k, int d, float a, float b, int32_t* counts, float* s_
     EMK_EMA(4);
   else if (Chat)
     EMK_EMA(1);
+  else if (Cq && cq_u8)
+    EMK_EMA(5);
   else if (Cq)
     EMK_EMA(2);
   else if (Cf)

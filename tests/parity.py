@@ -31,8 +31,8 @@ F8_TOL = 5e-4
 
 # search formats whose centroids are the running centroids rounded (the
 # band then covers coordinates on a rounding boundary): bf16 bits, int8
-# codes, E4M3 bits, fp16
-LOW_PRECISION = (np.uint16, np.int8, np.uint8, np.float16)
+# codes, E4M3 bits, fp16, uint8 data
+LOW_PRECISION = (np.uint16, np.int8, np.uint8, np.float16, oracle.U8)
 
 
 def _tol(X, base):
@@ -51,6 +51,8 @@ def obj_atol(X) -> float:
 
 def to_device(X: np.ndarray, device="cuda"):
     import torch
+    if X.dtype == oracle.U8:       # uint8 data
+        return torch.from_numpy(X.view(np.uint8)).to(device)
     if X.dtype == np.uint16:
         return torch.from_numpy(X.view(np.int16)).to(device).view(torch.bfloat16)
     if X.dtype == np.uint8:        # FP8 E4M3 bit patterns
@@ -130,6 +132,11 @@ def e4m3_flip_bound(X, rows, C32, labels, rel=1e-5):
     return _round_flip_bound(X, rows, C32, labels, oracle.e4m3_round, rel)
 
 
+def u8_flip_bound(X, rows, C32, labels, rel=1e-5):
+    """The uint8 analogue of int8_flip_bound (centroids rounded to [0, 255])."""
+    return _round_flip_bound(X, rows, C32, labels, oracle.u8_round, rel)
+
+
 def f16_flip_bound(X, rows, C32, labels, rel=1e-5, dot=False):
     """The fp16 analogue of bf16_flip_bound (fp16 data: the search centroids
     are the running centroids rounded to fp16)."""
@@ -155,6 +162,8 @@ def check_labels(X, Cs, rows, given, olab, d1, d2, given_dist=None, what="", C32
         band = (band + int8_flip_bound(X, rows, C32, olab) + int8_flip_bound(X, rows, C32, given))
     elif C32 is not None and X.dtype == np.uint8:
         band = (band + e4m3_flip_bound(X, rows, C32, olab) + e4m3_flip_bound(X, rows, C32, given))
+    elif C32 is not None and X.dtype == oracle.U8:
+        band = (band + u8_flip_bound(X, rows, C32, olab) + u8_flip_bound(X, rows, C32, given))
     elif C32 is not None and X.dtype == np.float16:
         band = (band + f16_flip_bound(X, rows, C32, olab, dot=dot)
                 + f16_flip_bound(X, rows, C32, given, dot=dot))

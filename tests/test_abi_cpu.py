@@ -176,7 +176,7 @@ def test_assign_rejects_before_device_work(L):
     assert L.emeans_assign(None, 10, 4, None, 3, None, None, ctypes.byref(o)) == -1
     assert L.emeans_assign(None, 10, 0, None, 3, None, None, ctypes.byref(o)) == -1
     assert L.emeans_assign(None, -1, 4, None, 3, None, None, ctypes.byref(o)) == -1
-    o.dtype = 5   # 0..4 are fp32, bf16, int8, FP8, fp16
+    o.dtype = 6   # 0..5 are fp32, bf16, int8, FP8, fp16, uint8
     assert L.emeans_assign(None, 10, 4, None, 3, None, None, ctypes.byref(o)) == -2
     assert L.emeans_batch_rows(10, 1, 0, 5, 6, None, None) == -1
     assert L.emeans_batch_rows(0, 1, 0, 0, 0, None, None) == -1

@@ -177,6 +177,70 @@ def test_assign_int8_rules(mm):
         mm.assign(X[:, :16].contiguous(), C[:, :16].contiguous(), spherical=True)
 
 
+CASES_U8 = [(2000, 768, 300), (1000, 64, 129), (777, 48, 50), (500, 37, 20), (300, 256, 1),
+            (600, 1040, 257), (3000, 128, 1000)]
+
+
+def _u8_centroids(X, k, seed):
+    """Centroids near data rows, a few coordinates outside [0, 255] (clamped)
+    and at exact half-integers (ties to even)."""
+    C = _centroids(X, k, seed)
+    d = C.shape[1]
+    C[0, : min(d, 4)] = np.array([300.0, -20.0, 254.5, 0.5], np.float32)[: min(d, 4)]
+    if k > 1:
+        C[1, : min(d, 2)] = np.array([2.5, 255.5], np.float32)[: min(d, 2)]
+    return C
+
+
+@pytest.mark.parametrize("n,d,k", CASES_U8)
+def test_assign_uint8(mm, n, d, k):
+    """uint8 data: the search is exact in integers, so labels (lowest index on
+    ties) and distances equal the oracle's exactly."""
+    X = datagen.codes_u8(n, d, m=64, seed=37).view(oracle.U8)
+    C = _u8_centroids(X, k, 15)
+    lab, dist = _run(mm, X, C)
+    olab, d1, _ = oracle.assign(X, oracle.u8_round(C))
+    assert np.array_equal(lab, olab), f"{int(np.sum(lab != olab))} labels differ"
+    assert np.array_equal(dist, d1.astype(np.float32))
+
+
+@pytest.mark.parametrize("d", [43919, 43904])
+def test_assign_uint8_extremes_at_the_dimension_limit(mm, d):
+    """Rows of 0s, 255s and 128s against centroids of 0s and 255s at the
+    largest d: the losing score of a 255-row against the 0-centroid is
+    -48896 d, one step from the int32 limit; labels and distances stay exact
+    (d = 43904: whole 16-byte rows; 43919: the unaligned tail)."""
+    raw = np.zeros((3, d), np.uint8)
+    raw[1] = 255
+    raw[2] = 128
+    C = np.zeros((2, d), np.float32)
+    C[1] = 255.0
+    X = raw.view(oracle.U8)
+    lab, dist = _run(mm, X, C)
+    olab, d1, _ = oracle.assign(X, oracle.u8_round(C))
+    assert lab.tolist() == [0, 1, 1] and np.array_equal(lab, olab)   # 128 is nearer 255
+    assert np.array_equal(dist, d1.astype(np.float32))
+
+
+def test_assign_uint8_misaligned_and_rules(mm):
+    import torch
+    n, d, k = 700, 64, 90
+    X = datagen.codes_u8(n, d, m=32, seed=39).view(oracle.U8)
+    C = _u8_centroids(X, k, 16)
+    buf = torch.empty(n * d + 1, dtype=torch.uint8, device="cuda")
+    Xd = buf[1:].view(n, d)
+    Xd.copy_(torch.from_numpy(X.view(np.uint8)).cuda())
+    lab, dist = mm.assign(Xd, torch.from_numpy(C).cuda())
+    olab, d1, _ = oracle.assign(X, oracle.u8_round(C))
+    assert np.array_equal(lab.cpu().numpy(), olab)
+    assert np.array_equal(dist.cpu().numpy(), d1.astype(np.float32))
+    Z = torch.zeros((10, 43920), dtype=torch.uint8, device="cuda")
+    with pytest.raises(mm.EmeansError, match="EINVAL"):
+        mm.assign(Z, torch.zeros((2, 43920), device="cuda"))
+    with pytest.raises(mm.EmeansError, match="EINVAL"):
+        mm.assign(Xd, torch.from_numpy(C).cuda(), spherical=True)
+
+
 CASES_F8 = [(2000, 768, 300), (1000, 64, 129), (777, 48, 50), (500, 37, 20), (300, 256, 1),
             (600, 1040, 257), (3000, 128, 1000)]
 

@@ -79,6 +79,7 @@ STREAM = [
     ("f8-pieces", "codes8", 12_000, 64, 256, 2.0, 2, {}),
     ("f16-pieces", "deep-f16", 12_000, 96, 256, 2.0, 2, {}),
     ("slow-ema", "tiny", 3_000, 16, 100, 2.0, 2, dict(slow_ema=4.0)),
+    ("u8-pieces", "codes-u8", 12_000, 64, 256, 2.0, 2, {}),
 ]
 
 

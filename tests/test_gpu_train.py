@@ -68,6 +68,10 @@ LOCKSTEP = [
     ("f16-deep", "deep-f16", 30_000, 96, 1024, 3.0, {}),
     ("f16-ragged", "tiny-f16", 5_003, 37, 77, 1.5, dict(batch_size=700)),
     ("f16-sph", "embedding-f16", 12_000, 768, 256, 2.0, dict(spherical=True)),
+    # uint8 data (README "Data precision", UINT8): exact integer search
+    ("u8-small", "codes-u8", 12_000, 128, 256, 2.0, {}),
+    ("u8-ragged", "codes-u8", 5_003, 37, 77, 1.5, dict(batch_size=700)),
+    ("u8-sift", "sift-u8", 20_000, 128, 1024, 2.0, {}),
 ]
 
 
@@ -103,7 +107,7 @@ def test_train_lockstep(mm, name, gen, n, d, k, T, o):
 LLOYD = [("tiny", "tiny", 10_000, 16, 64, 8), ("emb-small", "embedding", 12_000, 768, 256, 4),
          ("large-small", "large", 40_000, 128, 1024, 3), ("codes", "codes", 12_000, 96, 200, 4),
          ("ragged", "tiny", 5_003, 37, 77, 5), ("f8", "codes8", 12_000, 128, 200, 4),
-         ("f16", "sift-f16", 12_000, 128, 200, 4)]
+         ("f16", "sift-f16", 12_000, 128, 200, 4), ("u8", "codes-u8", 12_000, 64, 200, 4)]
 
 
 @pytest.mark.parametrize("name,gen,n,d,k,iters", LLOYD, ids=[c[0] for c in LLOYD])
