@@ -242,34 +242,47 @@ __device__ __forceinline__ void panel_bias(const float* bias, int k, int j0, int
     }
 }
 
-// Folds a finished panel into the running best of each point column
-// (centroids in increasing order; the first strict maximum is kept).
+// Folds a finished panel into the running best of each point column. A lane
+// holds 16 scores per point column, in increasing centroid order (slot
+// (mb, v) is centroid j0 + 16 mb + 4 (lane / 16) + v). It first takes their
+// maximum m; only where m beats the running best does it look for the first
+// slot holding m, the lowest such index, which is what an ordered walk that
+// keeps the first strict maximum finds. Past k the int8 scores are masked
+// (float scores are -inf there through the bias).
 template <int DT>
 __device__ __forceinline__ void fold_panel(const typename Fmt<DT>::Acc (&acc)[4][4],
                                            const typename Fmt<DT>::Acc (&bt)[4], int j0, int k,
                                            int lane, typename Fmt<DT>::Sc (&best)[4],
                                            int (&bidx)[4]) {
+  using Sc = typename Fmt<DT>::Sc;
+  const int jl = j0 + 4 * (lane >> 4);
+  const bool tail = j0 + 64 > k;  // some slot of this wave is past k
 #pragma unroll
-  for (int nb = 0; nb < 4; ++nb)
+  for (int nb = 0; nb < 4; ++nb) {
+    Sc sc[16];
 #pragma unroll
     for (int mb = 0; mb < 4; ++mb)
 #pragma unroll
       for (int v = 0; v < 4; ++v) {
-        const int j = j0 + mb * 16 + 4 * (lane >> 4) + v;
         if constexpr (kIntSearch<DT>) {
-          const int sc = 2 * acc[mb][nb][v] + bt[mb][v];
-          if (j < k && sc > best[nb]) {
-            best[nb] = sc;
-            bidx[nb] = j;
-          }
+          const int x = 2 * acc[mb][nb][v] + bt[mb][v];
+          sc[4 * mb + v] = (tail && jl + 16 * mb + v >= k) ? INT32_MIN : x;
         } else {
-          const float sc = acc[mb][nb][v];
-          if (sc > best[nb]) {
-            best[nb] = sc;
-            bidx[nb] = j;
-          }
+          sc[4 * mb + v] = acc[mb][nb][v];
         }
       }
+    Sc m = sc[0];
+#pragma unroll
+    for (int q = 1; q < 16; ++q) m = sc[q] > m ? sc[q] : m;
+    if (m > best[nb]) {
+      int jb = -1;
+#pragma unroll
+      for (int q = 15; q >= 0; --q)
+        if (sc[q] == m) jb = jl + 16 * (q >> 2) + (q & 3);
+      best[nb] = m;
+      bidx[nb] = jb;
+    }
+  }
 }
 
 template <int DT>
