@@ -273,15 +273,6 @@ def bf16_bits(X: np.ndarray) -> np.ndarray:
     return (bf16_round(X).view(np.uint32) >> 16).astype(np.uint16)
 
 
-def search_data(X: np.ndarray, bf16_search: bool) -> np.ndarray:
-    """Data in the search format. README "Data precision": on a GPU, fp32 data
-    may be converted to bf16 for the nearest-centroid search only (the pages'
-    GPU default, opt-in here); bf16 data is searched as stored."""
-    if bf16_search and X.dtype == np.float32:
-        return bf16_bits(X)
-    return X
-
-
 def int8_round(C: np.ndarray) -> np.ndarray:
     """Centroids (code space) -> nearest int8 code (ties to even), clamped to
     [-127, 127], returned as fp32 values."""
@@ -411,6 +402,66 @@ def f16_round(C: np.ndarray) -> np.ndarray:
     values (numpy's conversion)."""
     with np.errstate(over="ignore"):
         return np.asarray(C, dtype=np.float32).astype(np.float16).astype(np.float32)
+
+
+@dataclass
+class Converter:
+    """README "Data precision", "keep FP32, convert on the fly": fp32 rows and
+    centroids are converted, batch by batch, to a smaller format for the
+    nearest-centroid search only, v -> fmt((v - shift) * scale) in fp32 (the
+    product by a power of two is exact). fmt 'bf16' or 'f16' is the cast
+    (scale 1; a shift is the optional centering, "subtracts your data's mean
+    before rounding to 16 bits"); 'f8' is the calibrated FP8 converter (shift
+    and scale from fp8_calibrate). Sums and centroids stay fp32 in data units,
+    and distances in the converted units are divided by scale^2 ("the
+    centroids and distances come back in your original FP32 units")."""
+    fmt: str
+    shift: Optional[np.ndarray] = None
+    scale: float = 1.0
+
+    def __post_init__(self):
+        if self.fmt not in ("bf16", "f16", "f8"):
+            raise ValueError(f"unknown search format {self.fmt}")
+        if self.fmt == "f8" and self.shift is None:
+            raise ValueError("the FP8 converter needs a shift and a scale")
+
+    @property
+    def scale2(self) -> float:
+        return float(self.scale) ** 2
+
+    def unrounded(self, A: np.ndarray) -> np.ndarray:
+        """(A - shift) * scale in fp32, before rounding to the format."""
+        y = np.asarray(A, dtype=np.float32)
+        if self.shift is not None:
+            y = y - np.asarray(self.shift, dtype=np.float32)
+        return (y * np.float32(self.scale)).astype(np.float32)
+
+    def rows(self, X: np.ndarray) -> np.ndarray:
+        """The rows in the search's storage type: bf16 bits (uint16), IEEE fp16
+        or E4M3 bits (uint8)."""
+        y = self.unrounded(X)
+        if self.fmt == "bf16":
+            return bf16_bits(y)
+        if self.fmt == "f16":
+            with np.errstate(over="ignore"):
+                return y.astype(np.float16)
+        return e4m3_bits(e4m3_round(y))
+
+    def centroids(self, C: np.ndarray) -> np.ndarray:
+        """The search centroids, as fp32 values in the converted units."""
+        y = self.unrounded(C)
+        return {"bf16": bf16_round, "f16": f16_round, "f8": e4m3_round}[self.fmt](y)
+
+
+def converter(bf16_search: bool = False, search: Optional[str] = None,
+              search_shift: Optional[np.ndarray] = None,
+              search_scale: float = 1.0) -> Optional[Converter]:
+    """The converter of a run's options (bf16_search = the bf16 cast)."""
+    if search is None and bf16_search:
+        search = "bf16"
+    if search is None:
+        return None
+    return Converter(search, search_shift, search_scale)
 
 
 def search_centroids(C: np.ndarray, X: np.ndarray) -> np.ndarray:
@@ -586,13 +637,18 @@ def train(X: np.ndarray, k: int, T: float, seed: int = 1234, *, batch_law: int =
           check_slots: Optional[Callable[[int, int], Optional[np.ndarray]]] = None,
           check_hook: Optional[Callable[[dict], None]] = None,
           nthreads: int = 0, bf16_search: bool = False,
-          spherical: bool = False, slow_ema: float = 0.0) -> TrainResult:
+          spherical: bool = False, slow_ema: float = 0.0, search: Optional[str] = None,
+          search_shift: Optional[np.ndarray] = None,
+          search_scale: float = 1.0) -> TrainResult:
     """e-means on X (n x d, fp32 or bf16 bits), step by step.
 
     bf16_search: fp32 data is searched in bf16 (rows and centroids rounded to
     bf16), while the grouping, the running sums and the centroids use the
     fp32 rows (README "Data precision": only the search uses the smaller
-    format).
+    format). search / search_shift / search_scale: the general form, a
+    Converter of fp32 data ('bf16' or 'f16' with optional centering, 'f8'
+    with the calibrated shift and scale); the reported error is in data
+    units.
 
     spherical (README "Spherical e-means"): every centroid is its running
     average rescaled to norm 1 before use (a zero centroid stays zero), each
@@ -622,7 +678,13 @@ def train(X: np.ndarray, k: int, T: float, seed: int = 1234, *, batch_law: int =
     S_tot = rc["total_steps"]
     al = alphas(rc["alpha0"], S_tot)
     thr = rc["unused_threshold"]
-    Xf = search_data(X, bf16_search)  # the search reads this; grouping reads X
+    conv = converter(bf16_search, search, search_shift, search_scale)
+    if conv is not None and X.dtype != np.float32:
+        raise ValueError("a search converter takes fp32 data")
+    if conv is not None and spherical and (conv.shift is not None or conv.fmt == "f8"):
+        raise ValueError("spherical mode takes the plain bf16 / fp16 casts only")
+    Xf = conv.rows(X) if conv is not None else X  # the search reads this; grouping reads X
+    unit2 = conv.scale2 if conv is not None else 1.0
 
     C = np.ascontiguousarray(to_f32(X[init_rows(n, k, seed)]), dtype=np.float32)
     if spherical:
@@ -646,7 +708,8 @@ def train(X: np.ndarray, k: int, T: float, seed: int = 1234, *, batch_law: int =
         for s in range(rc["steps_per_pass"][e]):
             Bt = min(B, rows_e - s * B)
             rows = perm_range(n, seed, STREAM_PERM, e, s * B, Bt)
-            Cs = search_centroids(C, Xf)
+            Cs = conv.centroids(C) if conv is not None else search_centroids(C, Xf)
+            C32 = conv.unrounded(C) if conv is not None else C.copy()
             if spherical:
                 find = lambda r: (lambda l, a, b: (l, -2.0 * a, -2.0 * b))(*assign_ip(Xf, Cs, r, nthreads))
                 score_of = lambda l, r: -2.0 * dot_to(Xf, Cs, l, r)
@@ -664,14 +727,14 @@ def train(X: np.ndarray, k: int, T: float, seed: int = 1234, *, batch_law: int =
                 glab = lab if slots is None else lab[slots]
                 gd = score_of(glab, sel)
                 chk = dict(t=t, slots=slots, oracle=olab, d1=od1, d2=od2, given=glab,
-                           given_dist=gd, rows=sel, C=Cs, C32=C.copy(), spherical=spherical)
+                           given_dist=gd, rows=sel, C=Cs, C32=C32, spherical=spherical)
                 if check_hook is not None:
                     check_hook(chk)
                 else:
                     res.label_checks.append(chk)
                 dist = score_of(lab, rows)
             # spherical: sum of 2 - 2 x similarity (dist holds -2 x similarity)
-            obj += float(np.sum(dist)) + (2.0 * len(rows) if spherical else 0.0)
+            obj += float(np.sum(dist)) / unit2 + (2.0 * len(rows) if spherical else 0.0)
             counts, sums = group(X, rows, lab, k)
             a = al[t]
             b = np.float32(1.0) - a

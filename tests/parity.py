@@ -210,7 +210,9 @@ def lockstep(X: np.ndarray, out, k: int, T: float, seed: int, sample: int = 0,
     checking them (all slots, or `sample` random slots per step), and return
     the oracle's result and the check summary."""
     trace = out.trace.cpu().numpy()
-    Xs = oracle.search_data(X, opts.get("bf16_search", False))  # what the search reads
+    conv = oracle.converter(opts.get("bf16_search", False), opts.get("search"),
+                            opts.get("search_shift"), opts.get("search_scale", 1.0))
+    Xs = conv.rows(X) if conv is not None else X  # what the search reads
     rc = oracle.recipe(X.shape[0], X.shape[1], k, T, opts.get("batch_law", 0),
                        opts.get("batch_size", 0), opts.get("alpha0", 0.0),
                        opts.get("unused_threshold", -1.0))

@@ -845,3 +845,60 @@ def test_u8_training_closing_mean_and_search():
     c2 = np.array([[10.6], [9.45]], np.float32)
     assert oracle.assign(x, c2)[0].tolist() == [1]
     assert oracle.assign(x, oracle.search_centroids(c2, x))[0].tolist() == [0]
+
+
+# On-the-fly converters of fp32 data (README "Data precision": keep FP32,
+# convert on the fly; centering)
+
+def test_converter_centering_is_the_search_of_the_offset_free_data():
+    """Centering subtracts the shift before rounding: data 1000 + y with y
+    and the shift exact in fp32 is searched exactly as y itself, while the
+    plain bf16 cast of 1000 + y loses y's low digits."""
+    rng = np.random.default_rng(8)
+    Y = (rng.integers(-512, 512, size=(600, 12)) / 256.0).astype(np.float32)
+    CY = (rng.integers(-512, 512, size=(40, 12)) / 256.0).astype(np.float32)
+    shift = np.full(12, 1000.0, np.float32)
+    X, C = Y + shift, CY + shift                  # exact in fp32
+    cen = oracle.Converter("bf16", shift)
+    lab, d1, _ = oracle.assign(cen.rows(X), cen.centroids(C))
+    ref, r1, _ = oracle.assign(oracle.bf16_bits(Y), oracle.bf16_round(CY))
+    assert np.array_equal(lab, ref) and np.array_equal(d1, r1)
+    plain = oracle.Converter("bf16")
+    lab2, _, _ = oracle.assign(plain.rows(X), plain.centroids(C))
+    assert not np.array_equal(lab2, ref)          # the offset costs the cast its digits
+    # fp16 centering, same identity
+    c16 = oracle.Converter("f16", shift)
+    lab3, e1, _ = oracle.assign(c16.rows(X), c16.centroids(C))
+    ref3, s1, _ = oracle.assign(Y.astype(np.float16), oracle.f16_round(CY))
+    assert np.array_equal(lab3, ref3) and np.array_equal(e1, s1)
+
+
+def test_fp8_converter_on_grid_data_is_exact():
+    """Data and centroids on the FP8 converter's grid (shift + E4M3 value /
+    scale, exact in fp32 for a shift in quarters) convert without loss: the
+    rows become the codes, and the search in code units finds the exact fp32
+    labels, its distances divided by scale^2 equal to the data-space ones."""
+    codes = datagen.codes_e4m3(3000, 16, m=32, seed=13)
+    shift = (np.arange(16, dtype=np.float32) - 8.0) / 4.0
+    scale = 64.0
+    X = (shift + oracle.to_f32(codes) / np.float32(scale)).astype(np.float32)
+    conv = oracle.Converter("f8", shift, scale)
+    assert np.array_equal(conv.rows(X), codes)
+    C = X[np.random.default_rng(3).choice(len(X), 40, replace=False)].copy()
+    assert np.array_equal(conv.centroids(C), conv.unrounded(C))     # on the grid
+    lab, d1, _ = oracle.assign(conv.rows(X), conv.centroids(C))
+    ref, r1, _ = oracle.assign(X, C)
+    assert np.array_equal(lab, ref)
+    assert np.array_equal(d1 / scale ** 2, r1)
+    # training with the converter reports its error in data units: one Lloyd-
+    # like step (B = n, alpha = 1) from the same rows matches the fp32 search
+    a = oracle.train(X, 24, 1.0, seed=4, batch_size=len(X), alpha0=1.0, unused_threshold=0.0,
+                     search="f8", search_shift=shift, search_scale=scale)
+    b = oracle.train(X, 24, 1.0, seed=4, batch_size=len(X), alpha0=1.0, unused_threshold=0.0)
+    assert np.array_equal(a.labels, b.labels)
+    np.testing.assert_allclose(a.obj, b.obj, rtol=1e-12)
+    # the alias: bf16_search is the plain bf16 converter
+    Z = datagen.tiny(n=2000, d=8, seed=2)
+    r1 = oracle.train(Z, 16, 2.0, seed=1, bf16_search=True)
+    r2 = oracle.train(Z, 16, 2.0, seed=1, search="bf16")
+    assert np.array_equal(r1.labels, r2.labels) and np.array_equal(r1.centroids, r2.centroids)
