@@ -83,7 +83,7 @@ def test_assign_bf16_search(mm, gen, n, d, k):
     C = _centroids(X, k, 8)
     lab, dist = mm.assign(to_device(X), torch.from_numpy(C).cuda(), bf16_search=True)
     lab, dist = lab.cpu().numpy(), dist.cpu().numpy()
-    Xs = oracle.search_data(X, True)
+    Xs = oracle.Converter("bf16").rows(X)
     Cs = oracle.bf16_round(C)
     olab, d1, d2 = oracle.assign(Xs, Cs)
     check_labels(Xs, Cs, None, lab, olab, d1, d2, what=f"bf16-search {gen} {n}x{d} k={k}")
