@@ -157,11 +157,11 @@ def heldout_mse(mm, Xh, C, torch) -> float:
     return float(dist.double().mean().item())
 
 
-def time_to_target(mm, X, Xh, k, target, seeds, Ts, torch, bf16_search=False,
-                   decode=None) -> dict:
+def time_to_target(mm, X, Xh, k, target, seeds, Ts, torch, tkw=None, decode=None) -> dict:
     """Smallest median wall-clock among pass counts whose finalised held-out MSE
     reaches the Lloyd-25 held-out MSE (median over training seeds). decode:
-    code-space centroids to data space (int8 codes), outside the clock."""
+    code-space centroids to data space (int8 codes), outside the clock. tkw:
+    the run's search options."""
     import statistics
     rows = []
     best = None
@@ -170,7 +170,7 @@ def time_to_target(mm, X, Xh, k, target, seeds, Ts, torch, bf16_search=False,
         for s in seeds:
             torch.cuda.synchronize()
             t0 = time.perf_counter()
-            out = mm.train(X, k, T, s, capture_labels=True, bf16_search=bf16_search)
+            out = mm.train(X, k, T, s, capture_labels=True, **(tkw or {}))
             torch.cuda.synchronize()
             walls.append(time.perf_counter() - t0)
             C = out.centroids if decode is None else decode(out.centroids)
@@ -185,8 +185,7 @@ def time_to_target(mm, X, Xh, k, target, seeds, Ts, torch, bf16_search=False,
                 T=None if best is None else best["T"])
 
 
-def first_crossing(mm, X, Xh, k, T, rc, target, seed, torch, bf16_search=False,
-                   decode=None) -> dict:
+def first_crossing(mm, X, Xh, k, T, rc, target, seed, torch, tkw=None, decode=None) -> dict:
     """Secondary time-to-target: the T-pass run's EMA centroids at the end of
     each pass (finalisation off), each prefix timed on its own and evaluated
     outside the clock; the first pass whose held-out MSE reaches the target."""
@@ -197,7 +196,7 @@ def first_crossing(mm, X, Xh, k, T, rc, target, seed, torch, bf16_search=False,
         torch.cuda.synchronize()
         t0 = time.perf_counter()
         out = mm.train(X, k, T, seed, max_steps=steps, finalize=False, capture_labels=False,
-                       bf16_search=bf16_search)
+                       **(tkw or {}))
         torch.cuda.synchronize()
         w = time.perf_counter() - t0
         C = out.centroids if decode is None else decode(out.centroids)
@@ -246,6 +245,13 @@ def main() -> int:
     ap.add_argument("--ttt-seeds", type=int, default=5)
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
                     help="also run a plain device copy of BYTES (counter calibration)")
+    ap.add_argument("--search", choices=["bf16", "f16", "f8"], default=None,
+                    help="README \"Data precision\", keep FP32 and convert on the fly: the rows "
+                         "converted batch by batch for the search (f8: the FP8 converter "
+                         "calibrated on the first 65536 rows)")
+    ap.add_argument("--center", action="store_true",
+                    help="with --search bf16 / f16: subtract the mean of the first 65536 rows "
+                         "before rounding (centering)")
     ap.add_argument("--bf16-search", action="store_true",
                     help="search fp32 data in bf16 (README \"Data precision\": the pages' GPU "
                          "default); the held-out MSE is still evaluated in fp32")
@@ -299,29 +305,48 @@ def main() -> int:
     u8 = bool(args.uint8) and W["dtype"] == "f32" and not codes_fmt and not f16
     es = 2 if (W["dtype"] == "bf16" or f16) else (1 if (codes_fmt or u8) else 4)
     flops = float(sum(2.0 * b * k * d for b in sizes))
-    bsearch = (bool(args.bf16_search) and W["dtype"] == "f32" and not codes_fmt and not f16
-               and not u8)
+    # fp32 rows converted on the fly for the search (--search, --bf16-search)
+    search = args.search or ("bf16" if args.bf16_search else None)
+    if W["dtype"] != "f32" or codes_fmt or f16 or u8:
+        search = None
+    center = bool(args.center) and search is not None
     # arithmetic type of the search
-    sdtype = ("bf16" if bsearch else "f16" if f16 else "u8" if u8
+    sdtype = (search if search else "f16" if f16 else "u8" if u8
               else {"int8": "i8", "fp8": "f8"}.get(codes_fmt, W["dtype"]))
     sph = bool(args.spherical) and not codes_fmt
-    tag = (args.workload + ("_bf16search" if bsearch else "") + ("_spherical" if sph else "")
-           + (f"_{codes_fmt}" if codes_fmt else "") + ("_fp16" if f16 else "")
-           + ("_uint8" if u8 else ""))
+    tag = (args.workload + (f"_{search}search" if search else "") + ("_centered" if center else "")
+           + ("_spherical" if sph else "") + (f"_{codes_fmt}" if codes_fmt else "")
+           + ("_fp16" if f16 else "") + ("_uint8" if u8 else ""))
     if sph:
         args.no_ttt = True   # the Lloyd-25 target is Euclidean
 
     X, Xh, Xhost, codes = make_data(args.workload, W, torch, codes_fmt, mm, f16, u8)
+    # the run's search options: the converter's shift and scale come from the
+    # first 65536 rows (FP8: calibrated; casts with --center: their mean)
+    tkw, conv_info = {}, None
+    if search:
+        tkw["search"] = search
+        t1 = time.perf_counter()
+        if search == "f8":
+            shift, scale = mm.fp8_calibrate(X[:65536])
+            tkw.update(search_shift=shift, search_scale=scale)
+            conv_info = {"calibration_rows": 65536, "scale": scale}
+        elif center:
+            tkw["search_shift"] = X[:65536].double().mean(dim=0).float().contiguous()
+            conv_info = {"centering_rows": 65536}
+        torch.cuda.synchronize()
+        if conv_info is not None:
+            conv_info["setup_s"] = round(time.perf_counter() - t1, 4)
 
     # warm-up (untimed)
     if Wm > 0:
-        mm.train(X, k, T, args.seed, max_steps=Wm, bf16_search=bsearch, spherical=sph)
+        mm.train(X, k, T, args.seed, max_steps=Wm, spherical=sph, **tkw)
         torch.cuda.synchronize()
 
     # timed: exactly K steps of the schedule
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    out = mm.train(X, k, T, args.seed, max_steps=K, bf16_search=bsearch, spherical=sph)
+    out = mm.train(X, k, T, args.seed, max_steps=K, spherical=sph, **tkw)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     value = flops / wall / 1e12
@@ -338,7 +363,7 @@ def main() -> int:
         log(f"copied {args.copy_calibration} bytes x3 for counter calibration")
 
     # profiled run: device time per kernel class (HIP events on the launch stream)
-    prof = mm.train(X, k, T, args.seed, max_steps=K, profile=True, bf16_search=bsearch,
+    prof = mm.train(X, k, T, args.seed, max_steps=K, profile=True, **tkw,
                     spherical=sph).stats
     torch.cuda.synchronize()
     a_ms = prof["ms_assign"]
@@ -371,7 +396,8 @@ def main() -> int:
         "config": {"workload": DESCR[args.workload], "n": n, "d": d, "k": k, "T": T,
                    "batch": rc["batch_size"], "alpha0": round(rc["alpha0"], 6),
                    "steps_per_run": S,
-                   "search": "bf16 (fp32 rows rounded for the search; sums in fp32)" if bsearch
+                   "search": (f"{search} (fp32 rows converted on the fly"
+                              + (", centered" if center else "") + "; sums in fp32)") if search
                    else "int8 codes (exact integer search; sums in fp32)" if i8
                    else "FP8 E4M3 codes (FP8 products, fp32 sums)" if codes_fmt == "fp8"
                    else "fp16 data (fp16 products, fp32 sums)" if f16
@@ -404,6 +430,8 @@ def main() -> int:
     if codes is not None:
         line["config"][codes_fmt] = {"calibration_rows": 65536, "scale": codes[1],
                                      "calibrate_encode_s": round(codes[2], 4)}
+    if conv_info is not None:
+        line["config"]["converter"] = conv_info
 
     if not args.no_ttt:
         dec = codes[3] if codes is not None else None
@@ -413,7 +441,7 @@ def main() -> int:
         torch.cuda.synchronize()
         t0 = time.perf_counter()
         lout = mm.train(X, k, 25.0, args.seed, lloyd=True, capture_labels=False,
-                        bf16_search=bsearch)
+                        **tkw)
         torch.cuda.synchronize()
         lloyd_s = time.perf_counter() - t0
         lloyd_mse = heldout_mse(mm, Xh, lout.centroids if dec is None else dec(lout.centroids),
@@ -429,20 +457,20 @@ def main() -> int:
             source = "GPU Lloyd mode, 25 iterations (parity-tested against the oracle's Lloyd)"
         seeds = [args.seed + i for i in range(args.ttt_seeds)]
         Ts = [1.0, 1.5, 2.0, 2.5, 3.0] if T <= 3.0 else [1.0, 1.25, 1.5, 2.0, 2.5, 3.0, 5.0]
-        ttt = time_to_target(mm, X, Xh, k, target, seeds, Ts, torch, bsearch, dec)
+        ttt = time_to_target(mm, X, Xh, k, target, seeds, Ts, torch, tkw, dec)
         ttt.update(target_source=source, gpu_lloyd25_seconds=round(lloyd_s, 4),
                    gpu_lloyd25_heldout_mse=lloyd_mse)
         ttt["first_crossing"] = first_crossing(mm, X, Xh, k, T, rc, target, args.seed, torch,
-                                               bsearch, dec)
+                                               tkw, dec)
         log(f"first crossing: {ttt['first_crossing']['first']}")
         line["s_to_lloyd25"] = ttt["seconds"]
         line["time_to_target"] = ttt
         # the two closing choices of one run at the workload's T (untimed):
         # the last pass's exact means, the EMA itself and the slow EMA (kappa 2)
         r2 = mm.train(X, k, T, args.seed, slow_ema=2.0, capture_labels=False,
-                      bf16_search=bsearch)
+                      **tkw)
         r1 = mm.train(X, k, T, args.seed, slow_ema=1.0, capture_labels=False,
-                      bf16_search=bsearch)
+                      **tkw)
 
         def _ho(C):
             return heldout_mse(mm, Xh, C if dec is None else dec(C), torch)

@@ -166,6 +166,24 @@ typedef struct emeans_opts {
                                  EMA centroid where N' = 0, or everywhere if the last
                                  pass never began), rescaled to norm 1 in spherical
                                  mode; the closing mean is not applied to them */
+  int32_t search;             /* fp32 X only: convert the rows on the fly, batch by
+                                 batch, for the nearest-centroid search (README "Data
+                                 precision", keep FP32 and convert on the fly; the
+                                 rows and the centroids become
+                                 fmt((v - search_shift) * search_scale) in fp32):
+                                 EMEANS_BF16 or EMEANS_F16 (the casts; a shift is
+                                 the optional centering, scale 0 or 1) or EMEANS_F8
+                                 (the FP8 converter: shift and scale from
+                                 emeans_fp8_calibrate). Sums and centroids stay
+                                 fp32 in data units, and distances and obj are
+                                 given in data units (divided by scale^2).
+                                 0: none, or bf16 when bf16_search is set (the same
+                                 cast). Workspace B x d bytes (FP8) or 2 B x d. No
+                                 centering or FP8 converter in spherical mode. */
+  const float* search_shift;  /* device, d fp32, or NULL (0); owned by the caller and
+                                 read until emeans_train returns, or until
+                                 emeans_free for a model from emeans_begin */
+  double search_scale;        /* EMEANS_F8: power of two in [2^-126, 2^126] */
 } emeans_opts;
 
 /* Recipe and statistics of a run (README "Settings and results": recipe, obj,

@@ -37,6 +37,7 @@ class Opts(ctypes.Structure):
         ("stream", c_vp), ("trace_labels", c_vp), ("out_counts", c_vp), ("split_log", c_vp),
         ("split_log_cap", c_i64), ("max_steps", c_i64), ("bf16_search", c_i32),
         ("spherical", c_i32), ("lloyd", c_i32), ("slow_ema", c_dbl), ("slow_centroids", c_vp),
+        ("search", c_i32), ("search_shift", c_vp), ("search_scale", c_dbl),
     ]
 
 
@@ -136,6 +137,29 @@ def _opts(dtype=F32, batch_law="auto", batch_size=0, alpha0=0.0, unused_threshol
     return o
 
 
+SEARCH = {"bf16": BF16, "f16": F16, "fp16": F16, "f8": F8, "fp8": F8}
+
+
+def _set_search(o: Opts, search, search_shift, search_scale, d: int):
+    """On-the-fly search converter of fp32 data: search = 'bf16' | 'f16' |
+    'f8' (None: none), search_shift = d float32 GPU tensor or None (centering
+    for the casts, the FP8 converter's shift), search_scale (the FP8
+    converter's power-of-two scale)."""
+    if search is None:
+        if search_shift is not None or search_scale is not None:
+            raise EmeansError("EINVAL: search_shift / search_scale need search=")
+        return
+    if search not in SEARCH:
+        raise EmeansError(f"EINVAL: search must be one of {sorted(SEARCH)} (got {search!r})")
+    o.search = SEARCH[search]
+    if search_shift is not None:
+        _f32_device(search_shift, "search_shift")
+        if search_shift.numel() != d:
+            raise EmeansError(f"EINVAL: search_shift must have {d} values")
+        o.search_shift = search_shift.data_ptr()
+    o.search_scale = float(search_scale) if search_scale is not None else 0.0
+
+
 def _stats_dict(s: Stats) -> dict:
     P = s.n_passes
     return dict(batch_size=s.batch_size, alpha0=s.alpha0, law=s.law, total_steps=s.total_steps,
@@ -203,11 +227,15 @@ def train(X, k: int, T: float = 5.0, seed: int = 1234, *, batch_law="auto", batc
           capture_labels: bool = True, trace: bool = False, counts: bool = False,
           split_log_cap: int = 0, profile: bool = False, max_steps: int = 0,
           bf16_search: bool = False, spherical: bool = False, lloyd: bool = False,
-          slow_ema: float = 0.0, stream=None) -> TrainOutput:
+          slow_ema: float = 0.0, search=None, search_shift=None, search_scale=None,
+          stream=None) -> TrainOutput:
     """e-means training of X (n x d tensor on the GPU). lloyd: plain Lloyd
     iterations instead (T of them, every row each time, alpha = 1).
     slow_ema = kappa >= 1: also the centroids of a second, slower EMA over the
-    last pass (rate alpha_t / kappa), for unseen data (out.slow_centroids)."""
+    last pass (rate alpha_t / kappa), for unseen data (out.slow_centroids).
+    search = 'bf16' | 'f16' | 'f8' with search_shift / search_scale: fp32 rows
+    converted batch by batch for the search (casts with optional centering,
+    or the calibrated FP8 converter); results stay in data units."""
     import torch
     _require_device(X)
     n, d = X.shape
@@ -232,6 +260,7 @@ def train(X, k: int, T: float = 5.0, seed: int = 1234, *, batch_law="auto", batc
         o.max_steps = int(max_steps)
         o.bf16_search = 1 if bf16_search else 0
         o.spherical = 1 if spherical else 0
+        _set_search(o, search, search_shift, search_scale, d)
         SC = None
         if slow_ema:
             SC = torch.empty((k, d), dtype=torch.float32, device=dev)
@@ -250,9 +279,10 @@ def train(X, k: int, T: float = 5.0, seed: int = 1234, *, batch_law="auto", batc
 
 
 def assign(X, C, *, with_dists: bool = True, bf16_search: bool = False, spherical: bool = False,
-           stream=None):
+           search=None, search_shift=None, search_scale=None, stream=None):
     """Nearest centroid (int32 labels) and squared distance (float32) of each row.
     bf16_search: search fp32 rows in bf16 (rows and centroids rounded).
+    search / search_shift / search_scale: the general converter (as train).
     spherical: the centroid with the highest dot product, and that similarity."""
     import torch
     _require_device(X)
@@ -268,6 +298,7 @@ def assign(X, C, *, with_dists: bool = True, bf16_search: bool = False, spherica
         o = _opts(_dtype_of(X), stream=_stream_ptr(X, stream))
         o.bf16_search = 1 if bf16_search else 0
         o.spherical = 1 if spherical else 0
+        _set_search(o, search, search_shift, search_scale, d)
         if n:
             _check(lib().emeans_assign(X.data_ptr(), n, d, C.data_ptr(), k, labels.data_ptr(),
                                        dists.data_ptr() if dists is not None else None,
@@ -388,7 +419,8 @@ class Stream:
                  batch_law="auto", batch_size: int = 0, alpha0: float = 0.0,
                  unused_threshold=None, finalize: bool = True, bf16_search: bool = False,
                  spherical: bool = False, profile: bool = False, counts: bool = False,
-                 split_log_cap: int = 0, slow_ema: float = 0.0, stream=None):
+                 split_log_cap: int = 0, slow_ema: float = 0.0, search=None, search_shift=None,
+                 search_scale=None, stream=None):
         import torch
         if not (getattr(start, "is_cuda", False) and start.dtype == torch.float32
                 and start.is_contiguous() and start.dim() == 2):
@@ -410,6 +442,8 @@ class Stream:
                       ctypes.c_void_p(self._stream.cuda_stream))
             o.bf16_search = 1 if bf16_search else 0
             o.spherical = 1 if spherical else 0
+            _set_search(o, search, search_shift, search_scale, self.d)
+            self._search_shift = search_shift   # read by the library until close()
             self._counts = torch.empty((self.k,), dtype=torch.float32, device=self.device) \
                 if counts else None
             self._log = (ctypes.c_int32 * (3 * split_log_cap))() if split_log_cap > 0 else None

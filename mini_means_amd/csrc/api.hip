@@ -217,6 +217,58 @@ int check_dtype(int32_t d, const emeans_opts* opts) {
   return EMEANS_OK;
 }
 
+// A converter scale: a power of two that fp32 holds with room to spare.
+bool pow2_scale(double s) {
+  if (!(s >= 0x1p-126 && s <= 0x1p126)) return false;
+  int e;
+  return frexp(s, &e) == 0.5;
+}
+
+// The search format of fp32 data converted on the fly (README "Data
+// precision", keep FP32 and convert on the fly): opts->search, or bf16 for
+// bf16_search; 0 for other data types (bf16_search is ignored there).
+int32_t search_format(const emeans_opts* opts) {
+  if (!opts || opts->dtype != EMEANS_F32) return 0;
+  if (opts->search) return opts->search;
+  return opts->bf16_search ? EMEANS_BF16 : 0;
+}
+
+// The converter's options: a known format for fp32 data; the FP8 converter
+// with its calibrated shift and power-of-two scale; the casts with an optional
+// centering shift and scale 1; no centering or FP8 converter in spherical mode.
+int check_search(const emeans_opts* opts) {
+  if (!opts) return EMEANS_OK;
+  const int32_t sf = opts->search;
+  if (sf != 0 && sf != EMEANS_BF16 && sf != EMEANS_F16 && sf != EMEANS_F8)
+    return fail(EMEANS_EINVAL, "search must be 0, bf16 (1), fp8 (3) or fp16 (4) (got %d)", sf);
+  if (sf != 0 && opts->dtype != EMEANS_F32)
+    return fail(EMEANS_EINVAL, "a search converter takes fp32 data");
+  if (sf != 0 && opts->bf16_search && sf != EMEANS_BF16)
+    return fail(EMEANS_EINVAL, "bf16_search conflicts with search = %d", sf);
+  const int32_t f = search_format(opts);
+  const double sc = opts->search_scale;
+  if (f == 0) {
+    if (opts->search_shift) return fail(EMEANS_EINVAL, "search_shift needs a search converter");
+    if (!(sc == 0.0 || sc == 1.0))
+      return fail(EMEANS_EINVAL, "search_scale needs the FP8 search converter");
+    return EMEANS_OK;
+  }
+  if (f == EMEANS_F8) {
+    if (!opts->search_shift)
+      return fail(EMEANS_EINVAL, "the FP8 converter needs search_shift and search_scale "
+                                 "(emeans_fp8_calibrate)");
+    if (!pow2_scale(sc))
+      return fail(EMEANS_EINVAL, "search_scale must be a power of two in [2^-126, 2^126] (got %g)",
+                  sc);
+  } else if (!(sc == 0.0 || sc == 1.0)) {
+    return fail(EMEANS_EINVAL, "the bf16 and fp16 casts take search_scale 0 or 1 (got %g)", sc);
+  }
+  if (opts->spherical && (f == EMEANS_F8 || opts->search_shift))
+    return fail(EMEANS_EINVAL, "spherical mode takes the plain bf16 and fp16 casts only "
+                               "(no centering, no FP8 converter)");
+  return EMEANS_OK;
+}
+
 // The slow EMA's options: kappa >= 1 with an output table, not in Lloyd mode.
 int check_slow(const emeans_opts* opts) {
   if (!opts) return EMEANS_OK;
@@ -235,6 +287,7 @@ int check_run_args(int64_t n, int32_t d, int32_t k, double T, const emeans_opts*
   int rc0 = check_dtype(d, opts);
   if (rc0) return rc0;
   if ((rc0 = check_slow(opts))) return rc0;
+  if ((rc0 = check_search(opts))) return rc0;
   Recipe r;
   const int rc = make_recipe(n, d, k, T, opts, r);
   if (rc) return rc;
@@ -272,8 +325,14 @@ struct emeans_model {
   Recipe r;
   hipStream_t st = nullptr;
   int dt = EMEANS_F32;  // emeans_dtype of X
-  bool bf16 = false, bsearch = false, sbf = false, i8 = false, u8 = false, f8 = false,
-       f16 = false, sph = false, profile = false;
+  bool bf16 = false, i8 = false, u8 = false, f8 = false, f16 = false, sph = false,
+       profile = false;
+  // fp32 rows converted on the fly for the search (0: none; else the format,
+  // 1 bf16, 4 fp16, 3 E4M3): fmt((x - sshift) * sscale) into xb each batch
+  int32_t conv = 0;
+  const float* sshift = nullptr;
+  float sscale = 1.0f;
+  bool hf = false;  // chat holds fp16 (fp16 data or the fp16 cast)
   bool no_finalize = false;
   double slow_k = 0.0;             // slow EMA: kappa (0 = off)
   float* slow_out = nullptr;       // caller's table for the slow centroids
@@ -306,7 +365,8 @@ struct emeans_model {
   float *s_acc = nullptr, *S = nullptr, *N = nullptr, *LS = nullptr, *bias = nullptr,
         *n0 = nullptr, *pair_n = nullptr, *wlive = nullptr;
   float *N2 = nullptr, *S2 = nullptr;  // slow pair (slow EMA)
-  uint16_t *chat = nullptr, *xb = nullptr;  // chat: bf16 or (fp16 data) fp16 copy of C
+  uint16_t* chat = nullptr;      // bf16 or fp16 search copy of C
+  unsigned char* xb = nullptr;   // the batch rows converted for the search
   int8_t* cq = nullptr;   // int8 codes of C (int8 data; shifted uint8 codes for uint8 data)
   uint8_t* cf = nullptr;  // E4M3 codes of C (FP8 data)
   // per pass: [0, P) sum of distances, [P, 3P) sum n^2 and sum n, [3P, 4P) splits (int64)
@@ -342,8 +402,8 @@ struct emeans_model {
   // Centroid table the search reads for rows of type dt.
   const void* search_table() const {
     return (i8 || u8) ? (const void*)cq
-           : f8 ? (const void*)cf
-           : (bf16 || f16) ? (const void*)chat : (const void*)C;
+           : (f8 || conv == EMEANS_F8) ? (const void*)cf
+           : chat ? (const void*)chat : (const void*)C;
   }
 
   ReviveArgs revive_args(bool count_only) {
@@ -351,8 +411,8 @@ struct emeans_model {
                       pair_i, pair_n, rv_pos, rv_head, rv_cbase, rv_clen, rv_heads, rv_list,
                       rv_nheads, counters, count_only ? nullptr : dlog,
                       count_only ? 0 : log_cap, count_only ? 1 : 0, sph ? 1 : 0, wlive,
-                      f16 ? 1 : 0, slow_started ? N2 : nullptr, slow_started ? S2 : nullptr,
-                      u8 ? 1 : 0};
+                      hf ? 1 : 0, slow_started ? N2 : nullptr, slow_started ? S2 : nullptr,
+                      u8 ? 1 : 0, sshift, sscale};
   }
 
   // Recipe, options and workspace; C = external (the caller's buffer) or own.
@@ -375,6 +435,9 @@ struct emeans_model {
       return rc;
     if (opts && opts->out_counts && (rc = check_device(opts->out_counts, "out_counts"))) return rc;
     if ((rc = check_slow(opts))) return rc;
+    if ((rc = check_search(opts))) return rc;
+    if (opts && opts->search_shift && (rc = check_device(opts->search_shift, "search_shift")))
+      return rc;
     if (opts && opts->slow_centroids &&
         (rc = check_device(opts->slow_centroids, "slow_centroids")))
       return rc;
@@ -383,12 +446,14 @@ struct emeans_model {
     st = static_cast<hipStream_t>(opts ? opts->stream : nullptr);
     dt = dtype;
     bf16 = dtype == EMEANS_BF16;
-    bsearch = dtype == EMEANS_F32 && opts && opts->bf16_search;  // fp32 rows searched in bf16 (xb)
-    sbf = bf16 || bsearch;  // the search runs in bf16 against chat
+    conv = search_format(opts);  // fp32 rows converted into xb for the search
+    sshift = conv ? opts->search_shift : nullptr;
+    sscale = conv == EMEANS_F8 ? (float)opts->search_scale : 1.0f;
     i8 = dtype == EMEANS_I8;  // the search runs in int8 against cq
     u8 = dtype == EMEANS_U8;  // the same integer search on rows and codes shifted by -128
     f8 = dtype == EMEANS_F8;  // the search runs in FP8 against cf
     f16 = dtype == EMEANS_F16;  // the search runs in fp16 against chat
+    hf = f16 || conv == EMEANS_F16;
     sph = opts && opts->spherical;
     profile = opts && opts->profile;
     no_finalize = opts && opts->no_finalize;
@@ -436,10 +501,10 @@ struct emeans_model {
       ar.want(&S2, kd);
     }
     ar.want(&bias, (size_t)k);
-    if (sbf || f16) ar.want(&chat, kd);
+    if (bf16 || f16 || conv == EMEANS_BF16 || conv == EMEANS_F16) ar.want(&chat, kd);
     if (i8 || u8) ar.want(&cq, kd);
-    if (f8) ar.want(&cf, kd);
-    if (bsearch) ar.want(&xb, (size_t)B * d);
+    if (f8 || conv == EMEANS_F8) ar.want(&cf, kd);
+    if (conv) ar.want(&xb, (size_t)B * d * (conv == EMEANS_F8 ? 1 : 2));
     ar.want(&dstat, (size_t)4 * EMEANS_MAX_PASSES);
     ar.want(&counters, 4);
     if (log_cap > 0) ar.want(&dlog, (size_t)3 * log_cap);
@@ -464,13 +529,14 @@ struct emeans_model {
   int accumulate(const void* X, const uint32_t* rws, int nb, int32_t* out_labels) {
     if (nb <= 0) return EMEANS_OK;
     const bool add = rows_step > 0;
-    if (bsearch)
+    if (conv)
       HIP_RET(timed(kSample, [&] {
-        return launch_cast_rows(static_cast<const float*>(X), d, rws, nb, xb, st);
+        return launch_convert_rows(static_cast<const float*>(X), d, rws, nb, conv, sshift, sscale,
+                                   xb, st);
       }));
     HIP_RET(timed(kAssign, [&] {
-      if (bsearch)
-        return launch_assign(EMEANS_BF16, xb, d, nullptr, nb, chat, bias, k, blab, nullptr,
+      if (conv)
+        return launch_assign(conv, xb, d, nullptr, nb, search_table(), bias, k, blab, nullptr,
                              pcounts, dstat + e, sph, st);
       return launch_assign(dt, X, d, rws, nb, search_table(), bias, k, blab, nullptr, pcounts,
                            dstat + e, sph, st);
@@ -508,9 +574,9 @@ struct emeans_model {
     const float beta = slow ? (float)((double)a / slow_k) : 0.0f;
     const float b2 = 1.0f - beta;
     HIP_RET(timed(kUpdate, [&] {
-      return launch_ema(k, d, a, b, counts, s_acc, N, S, C, bias, chat, f16, cq, u8, cf, pass_counts,
+      return launch_ema(k, d, a, b, counts, s_acc, N, S, C, bias, chat, hf, cq, u8, cf, pass_counts,
                         last ? LS : nullptr, sph, beta, b2, slow ? N2 : nullptr,
-                        slow ? S2 : nullptr, st);
+                        slow ? S2 : nullptr, sshift, sscale, st);
     }));
     if (r.thr > 0.0 && (t + 1) % kReviveEvery == 0) {
       const ReviveArgs ra = revive_args(false);
@@ -560,7 +626,9 @@ struct emeans_model {
     if (!stats) return EMEANS_OK;
     fill_stats(r, stats);
     for (int q = 0; q < r.npass; ++q) {
-      stats->obj[q] = r.rows[q] ? host_stat[q] / (double)r.rows[q] : 0.0;
+      // distances of converted rows are in converted units: back to data units
+      const double u2 = (double)sscale * (double)sscale;
+      stats->obj[q] = r.rows[q] ? host_stat[q] / (double)r.rows[q] / u2 : 0.0;
       const double s2 = host_stat[EMEANS_MAX_PASSES + 2 * q];
       const double s1 = host_stat[EMEANS_MAX_PASSES + 2 * q + 1];
       stats->imbalance[q] = s1 > 0 ? (double)k * s2 / (s1 * s1) : 0.0;
@@ -639,6 +707,7 @@ int emeans_assign(const void* X, int64_t n, int32_t d, const float* C, int32_t k
   if (!X || !C || !labels) return fail(EMEANS_EINVAL, "X, C and labels must not be NULL");
   int rc;
   if ((rc = check_dtype(d, opts))) return rc;
+  if ((rc = check_search(opts))) return rc;
   if (n == 0) return EMEANS_OK;
   if ((rc = check_device(X, "X")) || (rc = check_device(C, "C")) ||
       (rc = check_device(labels, "labels")) || (dists && (rc = check_device(dists, "dists"))))
@@ -649,31 +718,41 @@ int emeans_assign(const void* X, int64_t n, int32_t d, const float* C, int32_t k
   const bool u8 = dtype == EMEANS_U8;
   const bool f8 = dtype == EMEANS_F8;
   const bool f16 = dtype == EMEANS_F16;
-  const bool bsearch = dtype == EMEANS_F32 && opts && opts->bf16_search;  // fp32 rows in bf16
+  if (opts && opts->search_shift && (rc = check_device(opts->search_shift, "search_shift")))
+    return rc;
+  const int32_t conv = search_format(opts);  // fp32 rows converted for the search
+  const float* sshift = conv ? opts->search_shift : nullptr;
+  const float sscale = conv == EMEANS_F8 ? (float)opts->search_scale : 1.0f;
+  const bool hf = f16 || conv == EMEANS_F16;
   const bool sph = opts && opts->spherical;  // highest dot product, similarity out
   void* base = nullptr;
   float* bias = nullptr;
   uint16_t* chat = nullptr;
-  uint16_t* xb = nullptr;
+  unsigned char* xb = nullptr;
   int8_t* cq = nullptr;
   uint8_t* cf = nullptr;
   Arena ar;
   ar.want(&bias, (size_t)k);
-  if (bf16 || bsearch || f16) ar.want(&chat, (size_t)k * d);
+  if (bf16 || f16 || conv == EMEANS_BF16 || conv == EMEANS_F16) ar.want(&chat, (size_t)k * d);
   if (i8 || u8) ar.want(&cq, (size_t)k * d);
-  if (f8) ar.want(&cf, (size_t)k * d);
-  if (bsearch) ar.want(&xb, (size_t)n * d);
+  if (f8 || conv == EMEANS_F8) ar.want(&cf, (size_t)k * d);
+  if (conv) ar.want(&xb, (size_t)n * d * (conv == EMEANS_F8 ? 1 : 2));
   rc = EMEANS_OK;
   HIP_TRY(ar.alloc(&base, st));
-  HIP_TRY(launch_prep(C, k, d, bias, chat, f16, cq, u8, cf, sph, st));
-  if (bsearch) HIP_TRY(launch_cast_rows(static_cast<const float*>(X), d, nullptr, (int)n, xb, st));
+  HIP_TRY(launch_prep(C, k, d, bias, chat, hf, cq, u8, cf, sshift, sscale, sph, st));
+  if (conv)
+    HIP_TRY(launch_convert_rows(static_cast<const float*>(X), d, nullptr, (int)n, conv, sshift,
+                                sscale, xb, st));
   {
-    const int sdt = bsearch ? EMEANS_BF16 : dtype;
+    const int sdt = conv ? conv : dtype;
     const void* cs = (i8 || u8) ? (const void*)cq
-                     : f8 ? (const void*)cf
-                     : (bf16 || bsearch || f16) ? (const void*)chat : (const void*)C;
-    HIP_TRY(launch_assign(sdt, bsearch ? (const void*)xb : X, d, nullptr, (int)n, cs, bias, k,
+                     : (f8 || conv == EMEANS_F8) ? (const void*)cf
+                     : chat ? (const void*)chat : (const void*)C;
+    HIP_TRY(launch_assign(sdt, conv ? (const void*)xb : X, d, nullptr, (int)n, cs, bias, k,
                           labels, dists, nullptr, nullptr, sph, st));
+    // distances of converted rows are in converted units: back to data units
+    if (dists && sscale != 1.0f)
+      HIP_TRY(launch_scale(dists, n, 1.0f / (sscale * sscale), st));
   }
 done:
   if (base) {
@@ -708,7 +787,8 @@ int emeans_train(const void* X, int64_t n, int32_t d, int32_t k, double T, uint6
   // starting centroids: k distinct rows (first k entries of the init permutation)
   HIP_RET(launch_init_centroids(m.dt, X, d, make_perm_key((uint64_t)n, seed, kStreamInit, 0), k,
                                 m.C, m.sph, st));
-  HIP_RET(launch_prep(m.C, k, d, m.bias, m.chat, m.f16, m.cq, m.u8, m.cf, m.sph, st));
+  HIP_RET(launch_prep(m.C, k, d, m.bias, m.chat, m.hf, m.cq, m.u8, m.cf, m.sshift, m.sscale, m.sph,
+                      st));
 
   for (int e = 0; e < r.npass && m.t < run_steps; ++e) {
     const bool last = e == r.npass - 1;
@@ -756,7 +836,8 @@ int emeans_begin(int64_t n, int32_t d, int32_t k, double T, uint64_t seed, const
   }
   if (rc == EMEANS_OK) {
     const hipError_t e2 =
-        launch_prep(m->C, k, d, m->bias, m->chat, m->f16, m->cq, m->u8, m->cf, m->sph, m->st);
+        launch_prep(m->C, k, d, m->bias, m->chat, m->hf, m->cq, m->u8, m->cf, m->sshift, m->sscale,
+                    m->sph, m->st);
     if (e2 != hipSuccess) rc = fail(EMEANS_EHIP, "centroid prep: %s", hipGetErrorString(e2));
   }
   if (rc != EMEANS_OK) {
@@ -822,13 +903,6 @@ int emeans_finalize(emeans_model* m, float* centroids, emeans_stats* stats) {
 void emeans_free(emeans_model* m) { delete m; }
 
 // README "Data precision", INT8: calibration, encoding and decoding of codes.
-namespace {
-bool pow2_scale(double s) {
-  if (!(s >= 0x1p-126 && s <= 0x1p126)) return false;
-  int e;
-  return frexp(s, &e) == 0.5;
-}
-}  // namespace
 
 namespace {
 

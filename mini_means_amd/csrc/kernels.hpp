@@ -48,13 +48,17 @@ hipError_t launch_init_centroids(int dt, const void* X, int d, const PermKey& pk
 // int8 codes q of C (nearest, clamped to +-127; with cq_u8 the nearest uint8
 // value, clamped to [0, 255], minus 128), and then bias[j] holds the int32
 // -|q_j|^2 (the assign contract); Cf = E4M3 codes of C (nearest, saturating
-// at +-448).
+// at +-448). Chat and Cf round (c - sshift) * sscale (sshift NULL: c * sscale),
+// fp32 data converted on the fly; sshift = NULL and sscale = 1 otherwise.
 hipError_t launch_prep(const float* C, int k, int d, float* bias, uint16_t* Chat, bool chat_f16,
-                       int8_t* Cq, bool cq_u8, uint8_t* Cf, bool sph, hipStream_t st);
+                       int8_t* Cq, bool cq_u8, uint8_t* Cf, const float* sshift, float sscale,
+                       bool sph, hipStream_t st);
 
-// out[r] = bf16(X[rows[r]]) for r < nrows (rows NULL: row r), row-major.
-hipError_t launch_cast_rows(const float* X, int d, const uint32_t* rows, int nrows,
-                            uint16_t* out, hipStream_t st);
+// out[r] = fmt((X[rows[r]] - shift) * scale) for r < nrows (rows NULL: row r;
+// shift NULL: 0), row-major: fmt 1 bf16 bits, 4 fp16 bits (both nearest, ties
+// to even), 3 E4M3 codes (nearest, saturating at +-448).
+hipError_t launch_convert_rows(const float* X, int d, const uint32_t* rows, int nrows, int fmt,
+                               const float* shift, float scale, void* out, hipStream_t st);
 
 // off = exclusive scan of counts (k+1 entries), cursor = off[0..k); ovf lists
 // the grouping work items beyond the first R rows of each cluster as
@@ -78,14 +82,19 @@ hipError_t launch_group(int dt, const void* X, int d, const uint32_t* order,
 
 // EMA update of every cluster; resets counts and s_acc for the next step;
 // pass_counts += counts; LS += s when LS is non-null; refreshes bias and the
-// search format (Chat, Cq or Cf, at most one non-null).
+// search format (Chat, Cq or Cf, at most one non-null; Chat and Cf of
+// (c - sshift) * sscale as in launch_prep).
 // sph: the centroids are rescaled to norm 1 and the bias is 0.
 // N2 / S2 (slow pair, both or neither): the same recurrence with rate beta
 // and 1 - beta = b2.
 hipError_t launch_ema(int k, int d, float a, float b, int32_t* counts, float* s_acc, float* N,
                       float* S, float* C, float* bias, uint16_t* Chat, bool chat_f16, int8_t* Cq,
                       bool cq_u8, uint8_t* Cf, int32_t* pass_counts, float* LS, bool sph,
-                      float beta, float b2, float* N2, float* S2, hipStream_t st);
+                      float beta, float b2, float* N2, float* S2, const float* sshift,
+                      float sscale, hipStream_t st);
+
+// a[i] *= f for i < n.
+hipError_t launch_scale(float* a, int64_t n, float f, hipStream_t st);
 
 // out[j] = S2[j] / N2[j] where N2[j] > 0, else C[j] (N2 NULL: out = C);
 // rescaled to norm 1 with sph where N2[j] > 0.
@@ -127,6 +136,8 @@ struct ReviveArgs {
   float* N2;          // slow pair (or NULL): a split copies both halves' N and S here
   float* S2;
   int cq_u8;          // Cq holds shifted uint8 codes
+  const float* sshift;  // the search copy rounds (c - sshift) * sscale (launch_prep)
+  float sscale;
 };
 // Dead-cluster check and donor draws (one workgroup), then the splits of the
 // running sums, one wave per donor chain.

@@ -42,32 +42,76 @@ __global__ void sample_rows_i32_kernel(PermKey pk, uint64_t start, int count, in
   if (r < count) rows[r] = (int32_t)perm_at(start + (uint64_t)r, pk);
 }
 
-// out[r] = bf16(X[rows[r]]) (nearest, ties to even): the batch rows in the
-// bf16 search format, contiguous. Eight elements per thread when rows are
+// A value in a search format of fp32 data (README "Data precision", convert
+// on the fly): y = (x - shift) * scale in fp32, the product by a power of two
+// exact, then the nearest bf16 (FMT 1) or fp16 (FMT 4) bits, or the nearest
+// E4M3 code (FMT 3, saturating).
+template <int FMT>
+__device__ __forceinline__ uint32_t to_search_fmt(float y) {
+  if constexpr (FMT == 3) return f32_to_e4m3(y);
+  else if constexpr (FMT == 4) return f32_to_f16_rne(y);
+  else return f32_to_bf16_rne(y);
+}
+
+// out[r] = the batch row X[rows[r]] in search format FMT (rows NULL: row r),
+// contiguous; shift NULL means 0. Eight elements per thread when rows are
 // whole 32-byte chunks, else one.
-template <bool VEC>
-__global__ __launch_bounds__(256) void cast_rows_kernel(const float* __restrict__ X, int d,
-                                                        const uint32_t* __restrict__ rows,
-                                                        int nrows, uint16_t* __restrict__ out) {
+template <int FMT, bool VEC>
+__global__ __launch_bounds__(256) void convert_rows_kernel(const float* __restrict__ X, int d,
+                                                           const uint32_t* __restrict__ rows,
+                                                           int nrows,
+                                                           const float* __restrict__ shift,
+                                                           float scale,
+                                                           unsigned char* __restrict__ out) {
   constexpr int E = VEC ? 8 : 1;
+  constexpr int OB = FMT == 3 ? 1 : 2;  // output bytes per element
   const int per = d / E;
   const int64_t q = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (q >= (int64_t)nrows * per) return;
   const int r = (int)(q / per), c = (int)(q - (int64_t)r * per) * E;
   const size_t src = (size_t)(rows ? rows[r] : (uint32_t)r) * d + c;
-  const size_t dst = (size_t)r * d + c;
+  const size_t dst = ((size_t)r * d + c) * OB;
   if constexpr (VEC) {
     const float4 a = *reinterpret_cast<const float4*>(X + src);
     const float4 b = *reinterpret_cast<const float4*>(X + src + 4);
-    const float f[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
-    uint32_t w[4];
+    float f[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+    if (shift) {
+      const float4 sa = *reinterpret_cast<const float4*>(shift + c);
+      const float4 sb = *reinterpret_cast<const float4*>(shift + c + 4);
+      const float sv[8] = {sa.x, sa.y, sa.z, sa.w, sb.x, sb.y, sb.z, sb.w};
 #pragma unroll
-    for (int e = 0; e < 4; ++e)
-      w[e] = (uint32_t)f32_to_bf16_rne(f[2 * e]) | ((uint32_t)f32_to_bf16_rne(f[2 * e + 1]) << 16);
-    *reinterpret_cast<uint4*>(out + dst) = make_uint4(w[0], w[1], w[2], w[3]);
+      for (int e = 0; e < 8; ++e) f[e] = f[e] - sv[e];
+    }
+    uint32_t h[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) h[e] = to_search_fmt<FMT>(f[e] * scale);
+    if constexpr (FMT == 3) {
+      uint32_t w0 = 0, w1 = 0;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        w0 |= h[e] << (8 * e);
+        w1 |= h[e + 4] << (8 * e);
+      }
+      *reinterpret_cast<uint2*>(out + dst) = make_uint2(w0, w1);
+    } else {
+      uint32_t w[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) w[e] = h[2 * e] | (h[2 * e + 1] << 16);
+      *reinterpret_cast<uint4*>(out + dst) = make_uint4(w[0], w[1], w[2], w[3]);
+    }
   } else {
-    out[dst] = f32_to_bf16_rne(X[src]);
+    const float y = (shift ? X[src] - shift[c] : X[src]) * scale;
+    if constexpr (FMT == 3)
+      out[dst] = (unsigned char)to_search_fmt<FMT>(y);
+    else
+      *reinterpret_cast<uint16_t*>(out + dst) = (uint16_t)to_search_fmt<FMT>(y);
   }
+}
+
+// The search copy of a centroid coordinate c of fp32 data converted on the
+// fly: (c - shift[e]) * scale (shift NULL: c * scale), before rounding.
+__device__ __forceinline__ float conv_in(float c, const float* sshift, float sscale, size_t e) {
+  return (sshift ? c - sshift[e] : c) * sscale;
 }
 
 // Spherical e-means: rescale a row of length d to norm 1 in place, the norm
@@ -137,7 +181,8 @@ __global__ __launch_bounds__(256) void init_centroids_kernel(const unsigned char
 // uint8 data, u8: the shifted uint8 codes) or Cf = E4M3 codes of c (FP8 data).
 __global__ __launch_bounds__(256) void prep_kernel(const float* C, int k, int d, float* bias,
                                                    uint16_t* Chat, int hf, int8_t* Cq, int u8,
-                                                   uint8_t* Cf, int sph) {
+                                                   uint8_t* Cf, const float* sshift,
+                                                   float sscale, int sph) {
   const int j = blockIdx.x * 4 + (threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
   if (j >= k) return;
@@ -146,7 +191,7 @@ __global__ __launch_bounds__(256) void prep_kernel(const float* C, int k, int d,
   for (int e = lane; e < d; e += 64) {
     float c = C[(size_t)j * d + e];
     if (Chat) {
-      const uint16_t h = to_half_rne(c, hf);
+      const uint16_t h = to_half_rne(conv_in(c, sshift, sscale, e), hf);
       Chat[(size_t)j * d + e] = h;
       c = half_to_f32(h, hf);
     } else if (Cq) {
@@ -155,7 +200,7 @@ __global__ __launch_bounds__(256) void prep_kernel(const float* C, int k, int d,
       nq += (int)q * (int)q;
       continue;
     } else if (Cf) {
-      const uint32_t q = f32_to_e4m3(c);
+      const uint32_t q = f32_to_e4m3(conv_in(c, sshift, sscale, e));
       Cf[(size_t)j * d + e] = (uint8_t)q;
       c = e4m3_to_f32(q);
     }
@@ -537,7 +582,8 @@ __global__ __launch_bounds__(256) void ema_kernel(int k, int d, float a, float b
                                                   float* S, float* C, float* bias,
                                                   uint16_t* Chat, int8_t* Cq, uint8_t* Cf,
                                                   int32_t* pass_counts, float* LS, int sph,
-                                                  float beta, float b2, float* N2, float* S2) {
+                                                  float beta, float b2, float* N2, float* S2,
+                                                  const float* sshift, float sscale) {
   const int j = blockIdx.x * 4 + (threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
   if (j >= k) return;
@@ -566,7 +612,7 @@ __global__ __launch_bounds__(256) void ema_kernel(int k, int d, float a, float b
     if (LS && n) LS[idx] += s;
     if (sph) continue;  // rescaled (and rounded to Chat) below, once the norm is known
     if constexpr (SF == 1 || SF == 4) {
-      const uint16_t h = to_half_rne(c, SF == 4);
+      const uint16_t h = to_half_rne(conv_in(c, sshift, sscale, e), SF == 4);
       Chat[idx] = h;
       c = half_to_f32(h, SF == 4);
     } else if constexpr (SF == 2 || SF == 5) {
@@ -575,7 +621,7 @@ __global__ __launch_bounds__(256) void ema_kernel(int k, int d, float a, float b
       nq += (int)q * (int)q;
       continue;
     } else if constexpr (SF == 3) {
-      const uint32_t q = f32_to_e4m3(c);
+      const uint32_t q = f32_to_e4m3(conv_in(c, sshift, sscale, e));
       Cf[idx] = (uint8_t)q;
       c = e4m3_to_f32(q);
     }
@@ -947,13 +993,15 @@ __global__ __launch_bounds__(256) void split_kernel(ReviveArgs A) {
       A.C[ii] = ci;
       if (A.Chat) {
         const bool hf = A.chat_f16;
-        const uint16_t hj = to_half_rne(cj, hf), hi = to_half_rne(ci, hf);
+        const uint16_t hj = to_half_rne(conv_in(cj, A.sshift, A.sscale, e), hf),
+                       hi = to_half_rne(conv_in(ci, A.sshift, A.sscale, e), hf);
         A.Chat[jj] = hj;
         A.Chat[ii] = hi;
         cj = half_to_f32(hj, hf);
         ci = half_to_f32(hi, hf);
       } else if (A.Cf) {
-        const uint32_t fj = f32_to_e4m3(cj), fi = f32_to_e4m3(ci);
+        const uint32_t fj = f32_to_e4m3(conv_in(cj, A.sshift, A.sscale, e)),
+                       fi = f32_to_e4m3(conv_in(ci, A.sshift, A.sscale, e));
         A.Cf[jj] = (uint8_t)fj;
         A.Cf[ii] = (uint8_t)fi;
         cj = e4m3_to_f32(fj);
@@ -1065,16 +1113,28 @@ hipError_t launch_sample_rows(const PermKey& pk, uint64_t start, int count, uint
   return hipGetLastError();
 }
 
-hipError_t launch_cast_rows(const float* X, int d, const uint32_t* rows, int nrows,
-                            uint16_t* out, hipStream_t st) {
+hipError_t launch_convert_rows(const float* X, int d, const uint32_t* rows, int nrows, int fmt,
+                               const float* shift, float scale, void* out, hipStream_t st) {
   if (nrows <= 0) return hipSuccess;
-  const bool vec = d % 8 == 0 && (uintptr_t)X % 16 == 0 && (uintptr_t)out % 16 == 0;
+  auto* o = static_cast<unsigned char*>(out);
+  const bool vec = d % 8 == 0 && (uintptr_t)X % 16 == 0 && (uintptr_t)o % 16 == 0 &&
+                   (uintptr_t)shift % 16 == 0;
   const int64_t work = (int64_t)nrows * (vec ? d / 8 : d);
   const unsigned grid = (unsigned)((work + 255) / 256);
-  if (vec)
-    cast_rows_kernel<true><<<grid, 256, 0, st>>>(X, d, rows, nrows, out);
+#define EMK_CONV(F)                                                                              \
+  do {                                                                                           \
+    if (vec)                                                                                     \
+      convert_rows_kernel<F, true><<<grid, 256, 0, st>>>(X, d, rows, nrows, shift, scale, o);   \
+    else                                                                                         \
+      convert_rows_kernel<F, false><<<grid, 256, 0, st>>>(X, d, rows, nrows, shift, scale, o);  \
+  } while (0)
+  if (fmt == 3)
+    EMK_CONV(3);
+  else if (fmt == 4)
+    EMK_CONV(4);
   else
-    cast_rows_kernel<false><<<grid, 256, 0, st>>>(X, d, rows, nrows, out);
+    EMK_CONV(1);
+#undef EMK_CONV
   return hipGetLastError();
 }
 
@@ -1093,9 +1153,10 @@ hipError_t launch_init_centroids(int dt, const void* X, int d, const PermKey& pk
 }
 
 hipError_t launch_prep(const float* C, int k, int d, float* bias, uint16_t* Chat, bool chat_f16,
-                       int8_t* Cq, bool cq_u8, uint8_t* Cf, bool sph, hipStream_t st) {
+                       int8_t* Cq, bool cq_u8, uint8_t* Cf, const float* sshift, float sscale,
+                       bool sph, hipStream_t st) {
   prep_kernel<<<(k + 3) / 4, 256, 0, st>>>(C, k, d, bias, Chat, chat_f16 ? 1 : 0, Cq,
-                                           cq_u8 ? 1 : 0, Cf, sph ? 1 : 0);
+                                           cq_u8 ? 1 : 0, Cf, sshift, sscale, sph ? 1 : 0);
   return hipGetLastError();
 }
 
@@ -1167,12 +1228,13 @@ hipError_t launch_group(int dt, const void* X, int d, const uint32_t* order,
 hipError_t launch_ema(int k, int d, float a, float b, int32_t* counts, float* s_acc, float* N,
                       float* S, float* C, float* bias, uint16_t* Chat, bool chat_f16, int8_t* Cq,
                       bool cq_u8, uint8_t* Cf, int32_t* pass_counts, float* LS, bool sph,
-                      float beta, float b2, float* N2, float* S2, hipStream_t st) {
+                      float beta, float b2, float* N2, float* S2, const float* sshift,
+                      float sscale, hipStream_t st) {
   const dim3 grid((k + 3) / 4), block(256);
   const int sp = sph ? 1 : 0;
 #define EMK_EMA(SF)                                                                        \
   ema_kernel<SF><<<grid, block, 0, st>>>(k, d, a, b, counts, s_acc, N, S, C, bias, Chat, Cq, \
-                                         Cf, pass_counts, LS, sp, beta, b2, N2, S2)
+                                         Cf, pass_counts, LS, sp, beta, b2, N2, S2, sshift, sscale)
   if (Chat && chat_f16)
     EMK_EMA(4);
   else if (Chat)
@@ -1186,6 +1248,17 @@ hipError_t launch_ema(int k, int d, float a, float b, int32_t* counts, float* s_
   else
     EMK_EMA(0);
 #undef EMK_EMA
+  return hipGetLastError();
+}
+
+__global__ void scale_kernel(float* a, int64_t n, float f) {
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < n) a[i] *= f;
+}
+
+hipError_t launch_scale(float* a, int64_t n, float f, hipStream_t st) {
+  if (n <= 0) return hipSuccess;
+  scale_kernel<<<(unsigned)((n + 255) / 256), 256, 0, st>>>(a, n, f);
   return hipGetLastError();
 }
 

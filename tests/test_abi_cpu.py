@@ -171,6 +171,30 @@ def test_slow_ema_options_rejected_before_device_work(L):
     assert b"slow_ema must be" in L.emeans_last_error()
 
 
+def test_search_converter_options_rejected_before_device_work(L):
+    """opts.search: a known format, fp32 data only, the FP8 converter with a
+    shift and a power-of-two scale, the casts with scale 0 or 1, no centering
+    or FP8 converter in spherical mode, no stray shift or scale."""
+    s = mm.Stats()
+    fake = 4096   # never dereferenced: the checks run before any device work
+    cases = [dict(search=7), dict(search=4, dtype=1), dict(search=3),
+             dict(search=3, search_shift=fake, search_scale=3.0),
+             dict(search=1, search_scale=2.0), dict(search=4, bf16_search=1),
+             dict(search=1, search_shift=fake, spherical=1),
+             dict(search=3, search_shift=fake, search_scale=4.0, spherical=1),
+             dict(search_shift=fake), dict(search_scale=8.0)]
+    for c in cases:
+        o = mm.Opts()
+        for key, val in c.items():
+            setattr(o, key, val)
+        assert L.emeans_train(None, 100, 4, 3, 2.0, 1, None, None, ctypes.byref(o),
+                              ctypes.byref(s)) == -1, c
+        assert b"NULL" not in L.emeans_last_error()
+        # assign: non-NULL pointers so that the option check is what answers
+        assert L.emeans_assign(fake, 10, 4, fake, 3, fake, None, ctypes.byref(o)) == -1, c
+        assert b"NULL" not in L.emeans_last_error() and b"device" not in L.emeans_last_error()
+
+
 def test_assign_rejects_before_device_work(L):
     o = mm.Opts()
     assert L.emeans_assign(None, 10, 4, None, 3, None, None, ctypes.byref(o)) == -1
