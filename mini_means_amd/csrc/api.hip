@@ -39,7 +39,7 @@ int fail(int code, const char* fmt, ...) {
     }                                                                                     \
   } while (0)
 
-constexpr int kGroupRows = 64;   // rows per grouping work item
+constexpr int kGroupRowsMin = 64;  // the smallest rows per grouping work item (group_rows)
 constexpr int kReviveEvery = 5;  // blog: dead clusters are checked every five batches
 
 struct Recipe {
@@ -475,7 +475,7 @@ struct emeans_model {
     ar.want(&counts, (size_t)k);
     ar.want(&cursor, (size_t)k);
     ar.want(&off, (size_t)k + 1);
-    ar.want(&ovf, (size_t)(B / kGroupRows) + 1);
+    ar.want(&ovf, (size_t)(B / kGroupRowsMin) + 1);
     ar.want(&ovf_n, 1);
     ar.want(&pass_counts, (size_t)k);
     ar.want(&flags, (size_t)k);
@@ -547,12 +547,14 @@ struct emeans_model {
       trace_off += nb;
     }
     HIP_RET(timed(kBucket, [&] {
-      hipError_t er = launch_scan(pcounts, k, kGroupRows, off, cursor, ovf, ovf_n, counts, st);
+      hipError_t er = launch_scan(pcounts, k, group_rows(dt, d), off, cursor, ovf, ovf_n, counts,
+                                  st);
       if (er != hipSuccess) return er;
       return launch_scatter(blab, rws, nb, cursor, order, out_labels, st);
     }));
     HIP_RET(timed(kGroup, [&] {
-      return launch_group(dt, X, d, order, off, ovf, ovf_n, k, kGroupRows, nb, s_acc, add, st);
+      return launch_group(dt, X, d, order, off, ovf, ovf_n, k, group_rows(dt, d), nb, s_acc, add,
+                          st);
     }));
     rows_step += nb;
     rows_pass += nb;

@@ -73,6 +73,10 @@ hipError_t launch_scan(int32_t* counts, int k, int R, int32_t* off, int32_t* cur
 hipError_t launch_scatter(const int32_t* labels, const uint32_t* rows, int nb, int32_t* cursor,
                           uint32_t* order, int32_t* out_labels, hipStream_t st);
 
+// Rows per grouping work item (R of launch_scan and launch_group) for rows of
+// d elements of type dt: 64, or more for rows of at most 1 KB.
+int group_rows(int dt, int d);
+
 // s_acc[j] += sum of X rows of cluster j (work items of at most R rows). A
 // cluster held by one work item is stored, assuming s_acc[j] = 0, unless
 // `add` (a later piece of the same update).
