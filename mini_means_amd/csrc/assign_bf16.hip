@@ -3,11 +3,14 @@
 // streamed. The two 16-bit formats differ only in the decode of |x|^2 and in
 // the MFMA (v_mfma_f32_32x32x16_bf16 or _f16, same operand layout).
 //
-// At d = 128 a bf16 point row is 256 bytes, so a wave can keep 64 points as
-// MFMA B operands in registers (64 VGPRs) for the whole sweep over the
+// At d = 128 a bf16 point row is 256 bytes, so a wave can keep 96 points as
+// MFMA B operands in registers (96 VGPRs) for the whole sweep over the
 // centroids, and the only streamed data are the bf16 centroid panels, shared
 // by the eight waves of the workgroup through LDS (two waves per SIMD, so one
-// wave's argmax work overlaps the other's MFMAs). v_mfma_f32_32x32x16_bf16
+// wave's argmax work overlaps the other's MFMAs). Each centroid fragment read
+// from LDS feeds three MFMAs, and it is read one k-step ahead of them (a
+// whole block ahead would not fit the registers beside 96 points; deeper
+// lookahead measured no faster). v_mfma_f32_32x32x16_bf16
 // tiles put 32 centroids on M and 32 points on N: after the KS k-steps each
 // lane holds 16 centroid scores x.c - |c|^2/2 (the bias is the accumulator's
 // initial value) of one point. The argmax first reduces the 16 scores to
@@ -26,7 +29,7 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 
-constexpr int kPB = 2;                  // 32-point blocks per wave
+constexpr int kPB = 3;                  // 32-point blocks per wave (96 points resident)
 constexpr int kWaves = 8;               // two waves per SIMD: one folds while the other multiplies
 constexpr int kThreads = 64 * kWaves;
 constexpr int kTPw = 32 * kPB;          // points per wave
@@ -117,44 +120,6 @@ __global__ __launch_bounds__(kThreads, 1) void assign_bf16_kernel(
   sstore(0);
   __syncthreads();
 
-  // A operands and biases of one 32-centroid block, read from LDS.
-  struct BlockOps {
-    u32x4 a[KS];
-    f32x16 init;
-  };
-  auto block_load = [&](int buf, int cb, BlockOps& o) {
-#pragma unroll
-    for (int ks = 0; ks < KS; ++ks)
-      o.a[ks] = *reinterpret_cast<const u32x4*>(
-          &lc[buf][(cb * 32 + (lane & 31)) * kStride + 32 * ks + 16 * half]);
-#pragma unroll
-    for (int g = 0; g < 4; ++g) {
-      // rows 8g + 4*half + 0..3 of the block: four consecutive biases
-      const float4 b4 = *reinterpret_cast<const float4*>(&lb[buf][cb * 32 + 8 * g + 4 * half]);
-      o.init[4 * g + 0] = b4.x;
-      o.init[4 * g + 1] = b4.y;
-      o.init[4 * g + 2] = b4.z;
-      o.init[4 * g + 3] = b4.w;
-    }
-  };
-  // KS x kPB MFMAs with the bias as the accumulators' initial value.
-  auto block_mfma = [&](const BlockOps& o, f32x16* acc) {
-#pragma unroll
-    for (int pb = 0; pb < kPB; ++pb) acc[pb] = o.init;
-#pragma unroll
-    for (int ks = 0; ks < KS; ++ks)
-#pragma unroll
-      for (int pb = 0; pb < kPB; ++pb) {
-        if constexpr (F16)
-          acc[pb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, o.a[ks]),
-                                                           __builtin_bit_cast(f16x8, pB[pb][ks]),
-                                                           acc[pb], 0, 0, 0);
-        else
-          acc[pb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, o.a[ks]),
-                                                            __builtin_bit_cast(bf16x8, pB[pb][ks]),
-                                                            acc[pb], 0, 0, 0);
-      }
-  };
   // Fold a finished block into the running best: the max m of the 16 scores
   // per point; only when some lane of the wave improves on its best does the
   // wave locate, on those lanes, the first of the 16 slots holding m (slots
@@ -190,14 +155,43 @@ __global__ __launch_bounds__(kThreads, 1) void assign_bf16_kernel(
     const int buf = panel & 1;
     const bool more = panel + 1 < npan;
     if (more) gload(panel + 1);
-    // the next block's operands are read from LDS before this block's MFMAs
-    BlockOps ops[2];
-    block_load(buf, 0, ops[0]);
 #pragma unroll
     for (int cb = 0; cb < kTC / 32; ++cb) {
-      if (cb + 1 < kTC / 32) block_load(buf, cb + 1, ops[(cb + 1) & 1]);
+      // biases of the block's 32 centroids: the accumulators' initial values
       f32x16 acc[kPB];
-      block_mfma(ops[cb & 1], acc);
+      {
+        f32x16 init;
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const float4 b4 = *reinterpret_cast<const float4*>(&lb[buf][cb * 32 + 8 * g + 4 * half]);
+          init[4 * g + 0] = b4.x;
+          init[4 * g + 1] = b4.y;
+          init[4 * g + 2] = b4.z;
+          init[4 * g + 3] = b4.w;
+        }
+#pragma unroll
+        for (int pb = 0; pb < kPB; ++pb) acc[pb] = init;
+      }
+      // A operands one k-step ahead of the MFMAs that use them
+      const unsigned char* arow = &lc[buf][(cb * 32 + (lane & 31)) * kStride + 16 * half];
+      u32x4 a_cur = *reinterpret_cast<const u32x4*>(arow);
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+        u32x4 a_nxt = a_cur;
+        if (ks + 1 < KS) a_nxt = *reinterpret_cast<const u32x4*>(arow + 32 * (ks + 1));
+#pragma unroll
+        for (int pb = 0; pb < kPB; ++pb) {
+          if constexpr (F16)
+            acc[pb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, a_cur),
+                                                             __builtin_bit_cast(f16x8, pB[pb][ks]),
+                                                             acc[pb], 0, 0, 0);
+          else
+            acc[pb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+                __builtin_bit_cast(bf16x8, a_cur), __builtin_bit_cast(bf16x8, pB[pb][ks]), acc[pb],
+                0, 0, 0);
+        }
+        a_cur = a_nxt;
+      }
       fold(acc, panel * kTC + cb * 32 + 4 * half);
     }
     if (more) {
