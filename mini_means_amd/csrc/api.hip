@@ -754,7 +754,7 @@ int emeans_assign(const void* X, int64_t n, int32_t d, const float* C, int32_t k
                           labels, dists, nullptr, nullptr, sph, st));
     // distances of converted rows are in converted units: back to data units
     if (dists && sscale != 1.0f)
-      HIP_TRY(launch_scale(dists, n, 1.0f / (sscale * sscale), st));
+      HIP_TRY(launch_scale(dists, n, (float)(1.0 / ((double)sscale * (double)sscale)), st));
   }
 done:
   if (base) {
