@@ -44,7 +44,8 @@ def kernel_source_sha() -> str:
     """Hash of the assign kernels' sources: counter readings are only reused
     while it is unchanged."""
     h = hashlib.sha256()
-    for f in ("assign.hip", "assign_bf16.hip", "common.hpp", "kernels.hpp"):  # assign kernels
+    for f in ("assign.hip", "assign_bf16.hip", "assign_i8r.hip", "common.hpp",
+              "kernels.hpp"):  # assign kernels
         with open(os.path.join(HERE, "mini_means_amd", "csrc", f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()
@@ -55,6 +56,8 @@ def assign_kernel_name(dtype: str, d: int) -> str:
     dtype and width (the dispatch rule of launch_assign in assign.hip)."""
     if dtype in ("bf16", "f16") and d in (32, 64, 96, 128):
         return f"assign_bf16_kernel (points resident in registers, 32x32x16 {dtype} MFMA)"
+    if dtype in ("i8", "u8") and d % 32 == 0 and 32 <= d <= 256:
+        return "assign_i8r_kernel (points resident in registers, 32x32x32 int8 MFMA)"
     if d % {"bf16": 8, "f16": 8, "i8": 16, "u8": 16, "f8": 16}.get(dtype, 4) == 0:
         return "assign_ring_kernel (direct-to-LDS stage ring, 16x16 MFMA)"
     return "assign_kernel (register-staged stages, 16x16 MFMA)"

@@ -782,6 +782,9 @@ hipError_t launch_assign(int dt, const void* X, int d, const uint32_t* rows, int
   if ((dt == 1 || dt == 4) && assign_bf16_resident_ok(d, X, Cs))
     return launch_assign_bf16_resident(X, d, rows, nrows, Cs, bias, k, labels, dists, counts, obj,
                                        sim, dt == 4, st);
+  if ((dt == 2 || dt == 5) && !sim && assign_i8_resident_ok(d, X, Cs))
+    return launch_assign_i8_resident(X, d, rows, nrows, Cs, bias, k, labels, dists, counts, obj,
+                                     dt == 5, st);
   const dim3 grid((nrows + kTP - 1) / kTP), block(kThreads);
   const auto* x = static_cast<const unsigned char*>(X);
   const auto* c = static_cast<const unsigned char*>(Cs);

@@ -32,6 +32,15 @@ hipError_t launch_assign_bf16_resident(const void* X, int d, const uint32_t* row
                                        int32_t* labels, float* dists, int32_t* counts,
                                        double* obj, bool sim, bool f16, hipStream_t st);
 
+// int8 codes (u8 false) or uint8 data of dimension 32 * KS <= 256: points
+// resident in registers, 32x32x32 int8 MFMA tiles, exact integer scores
+// (same contract as launch_assign with dt 2 or 5; bias holds -|q|^2 as int32).
+bool assign_i8_resident_ok(int d, const void* X, const void* Cq);
+hipError_t launch_assign_i8_resident(const void* X, int d, const uint32_t* rows, int nrows,
+                                     const void* Cq, const float* bias, int k, int32_t* labels,
+                                     float* dists, int32_t* counts, double* obj, bool u8,
+                                     hipStream_t st);
+
 // rows[r] = pi(start + r) for the keyed permutation pk.
 hipError_t launch_sample_rows(const PermKey& pk, uint64_t start, int count, uint32_t* rows,
                               hipStream_t st);

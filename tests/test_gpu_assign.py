@@ -124,7 +124,12 @@ def test_assign_spherical(mm, gen, n, d, k, bf16):
 
 
 CASES_I8 = [(2000, 768, 300), (1000, 64, 129), (777, 48, 50), (500, 37, 20), (300, 256, 1),
-            (900, 520, 300), (600, 1040, 257), (3000, 128, 1000)]
+            (900, 520, 300), (600, 1040, 257), (3000, 128, 1000),
+            # d = 32..256 in steps of 32 take the register-resident kernel:
+            # every k-step count, several workgroups with a ragged last one,
+            # k past one 256-centroid panel and not a multiple of 32
+            (1500, 32, 513), (2049, 96, 300), (2500, 160, 700), (1100, 192, 33),
+            (2100, 224, 290), (1700, 256, 600)]
 
 
 def _int8_centroids(X, k, seed):
@@ -178,7 +183,9 @@ def test_assign_int8_rules(mm):
 
 
 CASES_U8 = [(2000, 768, 300), (1000, 64, 129), (777, 48, 50), (500, 37, 20), (300, 256, 1),
-            (600, 1040, 257), (3000, 128, 1000)]
+            (600, 1040, 257), (3000, 128, 1000),
+            (1500, 32, 513), (2049, 96, 300), (2500, 160, 700), (1100, 192, 33),
+            (2100, 224, 290), (1700, 256, 600)]
 
 
 def _u8_centroids(X, k, seed):
@@ -404,3 +411,51 @@ def test_batch_rows_bit_exact(mm, n):
     if n <= 65536:
         full = mm.batch_rows(n, seed, 1, 0, n).cpu().numpy()
         assert np.array_equal(np.sort(full), np.arange(n))
+
+
+@pytest.mark.parametrize("u8", [False, True])
+@pytest.mark.parametrize("d", [64, 160])
+def test_assign_integer_ties_take_the_lowest_index(mm, u8, d):
+    """Copies of one centroid at indices that fall in the two lane halves of a
+    32-centroid block, in different blocks and in different 256-centroid
+    panels: every point nearest to that centroid takes its lowest index."""
+    n, k = 1200, 700
+    if u8:
+        X = datagen.codes_u8(n, d, m=16, seed=41).view(oracle.U8)
+        C = _u8_centroids(X, k, 16)
+    else:
+        X = datagen.codes_i8(n, d, m=16, seed=41)
+        C = _int8_centroids(X, k, 16)
+    Xf = oracle.to_f32(X)
+    for src, dups in ((3, (7, 12, 40, 300, 699)), (5, (4,)), (600, (601, 33))):
+        C[list(dups)] = C[src]
+    for j, row in ((20, 0), (21, 1), (290, 2)):  # centroids on data rows: exact hits
+        C[j] = Xf[row]
+    C[[520, 260, 9]] = Xf[0]
+    lab, dist = _run(mm, X, C)
+    Cs = oracle.u8_round(C) if u8 else oracle.int8_round(C)
+    olab, d1, _ = oracle.assign(X, Cs)
+    assert np.array_equal(lab, olab), f"{int(np.sum(lab != olab))} labels differ"
+    assert np.array_equal(dist, d1.astype(np.float32))
+
+
+@pytest.mark.parametrize("u8", [False, True])
+@pytest.mark.parametrize("n", [70_000, 140_000, 270_000])
+def test_assign_integer_batch_sizes(mm, u8, n):
+    """The register-resident integer kernel splits the 32-centroid blocks of
+    a panel among 8 waves for small batches (the cases above), among 4 and 2
+    waves at 70000 and 140000 rows of d = 64, and not at all at 270000 rows:
+    every split gives the same exact result."""
+    d, k = 64, 333
+    if u8:
+        X = datagen.codes_u8(n, d, m=64, seed=43).view(oracle.U8)
+        C = _u8_centroids(X, k, 17)
+        Cs = oracle.u8_round(C)
+    else:
+        X = datagen.codes_i8(n, d, m=64, seed=43)
+        C = _int8_centroids(X, k, 17)
+        Cs = oracle.int8_round(C)
+    lab, dist = _run(mm, X, C)
+    olab, d1, _ = oracle.assign(X, Cs)
+    assert np.array_equal(lab, olab), f"{int(np.sum(lab != olab))} labels differ"
+    assert np.array_equal(dist, d1.astype(np.float32))
