@@ -707,16 +707,16 @@ __global__ __launch_bounds__(1024) void revive_kernel(ReviveArgs A) {
   __shared__ double dtmp[16];
   __shared__ int itmp[16];
   __shared__ double csum[64];
-  __shared__ __attribute__((aligned(16))) float wN[kRvLdsN];
+  // live counts in LDS exactly when VT <= 8 (k <= 32768); a compile-time
+  // choice keeps global loads, and waits on the draw's global stores, out of
+  // the LDS variant's draw loop
+  constexpr bool lds_n = VT >= 1 && VT <= 8;
+  __shared__ __attribute__((aligned(16))) float wN[lds_n ? 4096 * VT : 4];
   __shared__ int s_ndead, s_last;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
   const int k = A.k;
-  // live counts in LDS exactly when VT <= 8 (k <= 32768); a compile-time
-  // choice keeps global loads, and waits on the draw's global stores, out of
-  // the LDS variant's draw loop
-  constexpr bool lds_n = VT >= 1 && VT <= 8;
   static_assert(8 * 4096 <= kRvLdsN, "VT <= 8 must fit the LDS counts");
   const int V = VT > 0 ? VT : (k + 4095) / 4096;  // clusters per lane per chunk
   const int CS = 64 * V;  // clusters per chunk; chunk c = [c CS, (c + 1) CS)
@@ -798,6 +798,13 @@ __global__ __launch_bounds__(1024) void revive_kernel(ReviveArgs A) {
     int64_t logc = A.counters[1];
     int dl = 0;
     double ul = 0.0;
+    // With the counts in LDS the draws of a batch of 64 touch no global
+    // memory: lane ql keeps draw ql's donor and count, and one coalesced
+    // flush per batch writes them (vector stores and loads share one
+    // completion counter, so a store inside the loop would make the next
+    // batch load wait for it, once per draw).
+    int bi = 0;
+    float bn = 0.0f;
     for (int q = 0; q < ndead; ++q) {
       const int ql = q & 63;
       if (ql == 0) {
@@ -888,24 +895,44 @@ __global__ __launch_bounds__(1024) void revive_kernel(ReviveArgs A) {
       }
       const int i = donor;
       const float Nh = nvd * 0.5f;
-      if (lane == 0) {
-        A.N[i] = Nh;
-        A.N[j] = Nh;
-        A.pair_i[q] = i;
-        A.pair_n[q] = Nh;
-        if constexpr (lds_n)
-          wN[i] = Nh;
-        else
-          A.wlive[i] = Nh;
-        if (A.log && logc < A.log_cap) {
-          A.log[3 * logc] = (int32_t)A.step;
-          A.log[3 * logc + 1] = j;
-          A.log[3 * logc + 2] = i;
-          ++logc;
+      if constexpr (lds_n) {
+        if (lane == 0) wN[i] = Nh;
+        if (lane == ql) {
+          bi = i;
+          bn = Nh;
         }
+        if (ql == 63 || q + 1 == ndead) {
+          // flush draws q - ql .. q: lane l holds draw q - ql + l (dead cluster dl)
+          const int q0 = q - ql;
+          if (lane <= ql) {
+            A.N[dl] = bn;
+            A.pair_i[q0 + lane] = bi;
+            A.pair_n[q0 + lane] = bn;
+            if (A.log && logc + lane < A.log_cap) {
+              A.log[3 * (logc + lane)] = (int32_t)A.step;
+              A.log[3 * (logc + lane) + 1] = dl;
+              A.log[3 * (logc + lane) + 2] = bi;
+            }
+          }
+          if (A.log) logc = min(A.log_cap, logc + ql + 1);
+        }
+      } else {
+        if (lane == 0) {
+          A.N[i] = Nh;
+          A.N[j] = Nh;
+          A.pair_i[q] = i;
+          A.pair_n[q] = Nh;
+          A.wlive[i] = Nh;
+          if (A.log && logc < A.log_cap) {
+            A.log[3 * logc] = (int32_t)A.step;
+            A.log[3 * logc + 1] = j;
+            A.log[3 * logc + 2] = i;
+            ++logc;
+          }
+        }
+        // counts read from global memory by the next draw must see these stores
+        __threadfence_block();
       }
-      // counts read from global memory by the next draw must see these stores
-      if constexpr (!lds_n) __threadfence_block();
       // the donor's chunk lost Nh of live count: update the prefix state
       const int Lo = i / CS;
       if (lane == Lo) lsum -= (double)Nh;
@@ -916,6 +943,13 @@ __global__ __launch_bounds__(1024) void revive_kernel(ReviveArgs A) {
   }
   __threadfence_block();
   __syncthreads();
+  if constexpr (lds_n) {
+    // the donors' halved counts, from LDS (dead clusters were written by the flushes)
+    for (int j = tid; j < k; j += 1024)
+      if (!A.flags[j]) A.N[j] = wN[j];
+    __threadfence_block();
+    __syncthreads();
+  }
 
   // ---- C: chain bookkeeping -------------------------------------------------
   // per thread a contiguous run of splits; chain starts are counted with a
