@@ -7,6 +7,9 @@
 //   fp32 X: v_mfma_f32_16x16x4_f32     bf16 X: v_mfma_f32_16x16x32_bf16
 //   int8 X: v_mfma_i32_16x16x64_i8     FP8 E4M3 X: v_mfma_f32_16x16x32_fp8_fp8
 //   fp16 X: v_mfma_f32_16x16x32_f16.
+// The stage ring (16-byte aligned rows) takes FP8 through the gfx950
+// v_mfma_scale_f32_16x16x128_f8f6f4 (scales 1) instead: one instruction per
+// 128-byte stage, each lane holding its 16-byte piece of both 64-byte slices.
 // Centroids sit on the MFMA M dimension and points on N, so after a tile each
 // lane holds four centroid scores of a single point; the running best score
 // and its index stay in registers across all panels and are merged across the
@@ -168,6 +171,28 @@ __device__ __forceinline__ typename Fmt<DT>::Sc sumsq16(u32x4 w) {
     }
   }
   return s;
+}
+
+typedef int32_t i32x8 __attribute__((ext_vector_type(8)));
+
+// FP8 E4M3: both 64-byte slices of a 128-byte stage for a 64 x 64 score block
+// (a[s][mb], b[s][nb]: slice s, 16 bytes per lane, lane / 16 selecting the
+// piece), one 16x16x128 MFMA per tile. A and B pair the same bytes with the
+// same lanes, so every product meets its partner.
+__device__ __forceinline__ void mfma_stage_f8(f32x4 (&acc)[4][4], const u32x4 (&a)[2][4],
+                                              const u32x4 (&b)[2][4]) {
+#pragma unroll
+  for (int mb = 0; mb < 4; ++mb)
+#pragma unroll
+    for (int nb = 0; nb < 4; ++nb) {
+      const i32x8 av = {(int)a[0][mb][0], (int)a[0][mb][1], (int)a[0][mb][2], (int)a[0][mb][3],
+                        (int)a[1][mb][0], (int)a[1][mb][1], (int)a[1][mb][2], (int)a[1][mb][3]};
+      const i32x8 bv = {(int)b[0][nb][0], (int)b[0][nb][1], (int)b[0][nb][2], (int)b[0][nb][3],
+                        (int)b[1][nb][0], (int)b[1][nb][1], (int)b[1][nb][2], (int)b[1][nb][3]};
+      // formats 0, 0: E4M3 operands; scales 127: 2^0
+      acc[mb][nb] =
+          __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(av, bv, acc[mb][nb], 0, 0, 0, 127, 0, 127);
+    }
 }
 
 // One 64-byte slice of K for a 64 x 64 score block: a[mb] holds 16 centroid
@@ -711,22 +736,42 @@ __global__ __launch_bounds__(kThreads, 1) void assign_ring_kernel(
           xpart[i] += sumsq16<DT>(point_chunk<DT>(
               *reinterpret_cast<const u32x4*>(cur + swz(rb + kRowsPerPass * i, ch))));
     }
+    if constexpr (DT == 3) {
+      static_assert(kSlab == 128, "one 16x16x128 FP8 MFMA per stage");
+      u32x4 a[2][4], b[2][4];
 #pragma unroll
-    for (int kk = 0; kk < kSlab / 64; ++kk) {
-      const int pc = swz_pos(lane & 15, kk * 4 + (lane >> 4)) << 4;  // rows are 16-aligned + lane % 16
-      u32x4 a[4], b[4];
+      for (int kk = 0; kk < 2; ++kk) {
+        const int pc = swz_pos(lane & 15, kk * 4 + (lane >> 4)) << 4;
 #pragma unroll
-      for (int mb = 0; mb < 4; ++mb)
-        a[mb] = *reinterpret_cast<const u32x4*>(
-            cur + (kTP + wm * 64 + mb * 16 + (lane & 15)) * kSlab + pc);
+        for (int mb = 0; mb < 4; ++mb)
+          a[kk][mb] = *reinterpret_cast<const u32x4*>(
+              cur + (kTP + wm * 64 + mb * 16 + (lane & 15)) * kSlab + pc);
 #pragma unroll
-      for (int nb = 0; nb < 4; ++nb)
-        b[nb] = point_chunk<DT>(
-            *reinterpret_cast<const u32x4*>(cur + (wn * 64 + nb * 16 + (lane & 15)) * kSlab + pc));
-      mfma_slice<DT>(acc, a, b);
-      // the loads of stage t + 2, issued while the matrix core works on this
-      // stage's first half
-      if (kk == 0) issue_next();
+        for (int nb = 0; nb < 4; ++nb)
+          b[kk][nb] = *reinterpret_cast<const u32x4*>(
+              cur + (wn * 64 + nb * 16 + (lane & 15)) * kSlab + pc);
+      }
+      mfma_stage_f8(acc, a, b);
+      // the loads of stage t + 2, issued while the matrix core works on this stage
+      issue_next();
+    } else {
+#pragma unroll
+      for (int kk = 0; kk < kSlab / 64; ++kk) {
+        const int pc = swz_pos(lane & 15, kk * 4 + (lane >> 4)) << 4;  // rows are 16-aligned + lane % 16
+        u32x4 a[4], b[4];
+#pragma unroll
+        for (int mb = 0; mb < 4; ++mb)
+          a[mb] = *reinterpret_cast<const u32x4*>(
+              cur + (kTP + wm * 64 + mb * 16 + (lane & 15)) * kSlab + pc);
+#pragma unroll
+        for (int nb = 0; nb < 4; ++nb)
+          b[nb] = point_chunk<DT>(
+              *reinterpret_cast<const u32x4*>(cur + (wn * 64 + nb * 16 + (lane & 15)) * kSlab + pc));
+        mfma_slice<DT>(acc, a, b);
+        // the loads of stage t + 2, issued while the matrix core works on this
+        // stage's first half
+        if (kk == 0) issue_next();
+      }
     }
     if (last_s) {
       // panel complete: fold it into the running best (centroids in increasing order)
