@@ -40,6 +40,7 @@ int fail(int code, const char* fmt, ...) {
   } while (0)
 
 constexpr int kGroupRowsMin = 64;  // the smallest rows per grouping work item (group_rows)
+constexpr int64_t kSampleRows = 1 << 20;  // sampled rows drawn per launch, at most
 constexpr int kReviveEvery = 5;  // blog: dead clusters are checked every five batches
 
 struct Recipe {
@@ -355,6 +356,10 @@ struct emeans_model {
   void* base = nullptr;
   float* C = nullptr;  // working centroids (the caller's output buffer in emeans_train)
   uint32_t *rows = nullptr, *order = nullptr;
+  // steps whose sampled rows one launch produces (rows holds sample_steps
+  // batches): a 65536-row launch keeps one wave per SIMD, each waiting on its
+  // own Feistel chain, so the rows of up to 2^20 slots are drawn at once
+  int64_t sample_steps = 1;
   int32_t *blab = nullptr, *pcounts = nullptr, *counts = nullptr, *cursor = nullptr,
           *off = nullptr, *ovf_n = nullptr, *pass_counts = nullptr, *flags = nullptr,
           *dead = nullptr, *dlog = nullptr, *pair_i = nullptr, *rv_pos = nullptr,
@@ -468,7 +473,8 @@ struct emeans_model {
     const int64_t B = r.B;
     Arena ar;
     if (!external_C) ar.want(&C, kd);
-    ar.want(&rows, r.lloyd ? (size_t)1 : (size_t)B);
+    sample_steps = r.lloyd ? 1 : (B < kSampleRows ? kSampleRows / B : 1);
+    ar.want(&rows, r.lloyd ? (size_t)1 : (size_t)(B * sample_steps));
     ar.want(&order, (size_t)B);
     ar.want(&blab, (size_t)B);
     ar.want(&pcounts, (size_t)k);
@@ -799,12 +805,18 @@ int emeans_train(const void* X, int64_t n, int32_t d, int32_t k, double T, uint6
     for (int64_t s = 0; s < r.steps[e] && m.t < run_steps; ++s) {
       const int64_t rem = r.rows[e] - s * B;
       const int nb = (int)(rem < B ? rem : B);
-      // Lloyd iterations visit the rows in their own order (rows = NULL)
-      if (!r.lloyd)
+      // Lloyd iterations visit the rows in their own order (rows = NULL); the
+      // sampler fills the rows of sample_steps steps at a time
+      const int64_t g = s % m.sample_steps;
+      if (!r.lloyd && g == 0) {
+        const int64_t left = r.rows[e] - s * B;
+        const int64_t cnt = left < B * m.sample_steps ? left : B * m.sample_steps;
         HIP_RET(m.timed(emeans_model::kSample, [&] {
-          return launch_sample_rows(pk, (uint64_t)(s * B), nb, m.rows, st);
+          return launch_sample_rows(pk, (uint64_t)(s * B), (int)cnt, m.rows, st);
         }));
-      if ((rc = m.accumulate(X, r.lloyd ? nullptr : m.rows, nb, (last && labels) ? labels : nullptr)))
+      }
+      if ((rc = m.accumulate(X, r.lloyd ? nullptr : m.rows + g * B, nb,
+                             (last && labels) ? labels : nullptr)))
         return rc;
       if ((rc = m.update())) return rc;
     }
