@@ -73,7 +73,7 @@ hipError_t launch_convert_rows(const float* X, int d, const uint32_t* rows, int 
 // the grouping work items beyond the first R rows of each cluster as
 // (cluster, part) pairs, *ovf_n of them (room for rows / R pairs). With acc:
 // acc += counts, then counts = 0 (the counts of one piece of a batch join the
-// update's totals).
+// update's totals). R must be a power of two (hipErrorInvalidValue otherwise).
 hipError_t launch_scan(int32_t* counts, int k, int R, int32_t* off, int32_t* cursor,
                        int2* ovf, int32_t* ovf_n, int32_t* acc, hipStream_t st);
 

@@ -227,7 +227,7 @@ __global__ __launch_bounds__(256) void prep_kernel(const float* C, int k, int d,
 // in the high word, overflow items in the low word) serves both sums, and the
 // row offsets go back through LDS to be stored coalesced.
 __global__ __launch_bounds__(1024) void scan_kernel(int32_t* __restrict__ counts, int k,
-                                                    int R, int32_t* __restrict__ off,
+                                                    int R, int rsh, int32_t* __restrict__ off,
                                                     int32_t* __restrict__ cursor,
                                                     int2* __restrict__ ovf,
                                                     int32_t* __restrict__ ovf_n,
@@ -270,7 +270,7 @@ __global__ __launch_bounds__(1024) void scan_kernel(int32_t* __restrict__ counts
     uint64_t loc = 0;
 #pragma unroll
     for (int v = 0; v < V; ++v)
-      loc += ((uint64_t)(uint32_t)n[v] << 32) | (uint32_t)(n[v] > R ? (n[v] - 1) / R : 0);
+      loc += ((uint64_t)(uint32_t)n[v] << 32) | (uint32_t)(n[v] > R ? (n[v] - 1) >> rsh : 0);
     // ends with a barrier: every thread has read its counts from lds
     const uint64_t incl = block_incl_scan<uint64_t, 1024>(loc, tmp);
     const uint64_t total = tmp[15];
@@ -279,7 +279,7 @@ __global__ __launch_bounds__(1024) void scan_kernel(int32_t* __restrict__ counts
 #pragma unroll
     for (int v = 0; v < V; ++v) {
       lds[at(tid * V + v)] = oc;
-      const int extra = n[v] > R ? (n[v] - 1) / R : 0;
+      const int extra = n[v] > R ? (n[v] - 1) >> rsh : 0;  // R = 2^rsh
       for (int q = 0; q < extra; ++q) ovf[ov + q] = make_int2(t0 + tid * V + v, q + 1);
       oc += n[v];
       ov += extra;
@@ -1198,7 +1198,10 @@ hipError_t launch_prep(const float* C, int k, int d, float* bias, uint16_t* Chat
 
 hipError_t launch_scan(int32_t* counts, int k, int R, int32_t* off, int32_t* cursor,
                        int2* ovf, int32_t* ovf_n, int32_t* acc, hipStream_t st) {
-  scan_kernel<<<1, 1024, 0, st>>>(counts, k, R, off, cursor, ovf, ovf_n, acc);
+  // items of R rows, R a power of two: the kernel divides by shifting
+  if (R <= 0 || (R & (R - 1)) != 0) return hipErrorInvalidValue;
+  const int rsh = __builtin_ctz((unsigned)R);
+  scan_kernel<<<1, 1024, 0, st>>>(counts, k, R, rsh, off, cursor, ovf, ovf_n, acc);
   return hipGetLastError();
 }
 
