@@ -51,6 +51,11 @@ Do."):
                     uint8 values (clamped to [0, 255]).
 * Lloyd             blog, Lloyd section: assign all, move each centroid to
                     the exact mean of its points (the Lloyd-25 target).
+* closing replay    README "Several GPUs", paragraph on final_closing_mean:
+                    the closing mean taken after the last pass from a second
+                    look at the rows, with the labels the last pass saved
+                    (-1 rows left out) or, without them, a fresh assignment
+                    against the final EMA centroids.
 * slow EMA          blog, closing remark of the section on what e-means
                     changes: for unseen data, finish with a second, slower
                     EMA, a second set of centroids from the same run. The
@@ -822,6 +827,59 @@ def lloyd(X: np.ndarray, k: int, iters: int, seed: int = 1234, nthreads: int = 0
         pos = counts > 0
         C[pos] = (sums[pos] / counts[pos].astype(np.float64)[:, None]).astype(np.float32)
     return C, hist
+
+
+def final_closing_mean(batches, C_ema: np.ndarray, assignments: Optional[np.ndarray] = None,
+                       spherical: bool = False, nthreads: int = 0):
+    """The closing mean taken from a second look at the rows after the last
+    pass (README "Several GPUs", the paragraph on final_closing_mean for
+    callers who write their own batch loop).
+
+    `batches` is a sequence of row blocks that together go over the rows in
+    one fixed order. `assignments`, when given, holds one label per row in
+    that same order: the cluster the last pass gave it, or -1 for a row that
+    pass did not visit (such rows are left out). Without it, every row is
+    assigned once more to its nearest centroid among C_ema, the final EMA
+    centroids, compared in the data's search format (highest dot product when
+    spherical). Each centroid that receives at least one row becomes the exact
+    mean of its rows (fp64 sums, stored fp32; rescaled to norm 1 when
+    spherical); a centroid that receives none keeps its C_ema value.
+
+    Returns (centroids, labels): the k x d fp32 result and the label each row
+    was counted under (int32, -1 for rows left out)."""
+    C_ema = np.ascontiguousarray(C_ema, dtype=np.float32)
+    k, d = C_ema.shape
+    counts = np.zeros(k, dtype=np.int64)
+    sums = np.zeros((k, d), dtype=np.float64)
+    used = []
+    pos = 0
+    for X in batches:
+        X = np.ascontiguousarray(X)
+        m = X.shape[0]
+        if assignments is not None:
+            lab = np.asarray(assignments[pos:pos + m], dtype=np.int64)
+            if len(lab) != m:
+                raise ValueError("assignments hold fewer labels than the batches have rows")
+            if np.any((lab < -1) | (lab >= k)):
+                raise ValueError("labels must be -1 or in [0, k)")
+        elif spherical:
+            lab = assign_ip(X, search_centroids(C_ema, X), nthreads=nthreads)[0].astype(np.int64)
+        else:
+            lab = assign(X, search_centroids(C_ema, X), nthreads=nthreads)[0].astype(np.int64)
+        keep = np.nonzero(lab >= 0)[0]
+        c, s = group(X, keep, lab[keep].astype(np.int32), k)
+        counts += c
+        sums += s
+        used.append(lab.astype(np.int32))
+        pos += m
+    if assignments is not None and pos != len(assignments):
+        raise ValueError("assignments hold more labels than the batches have rows")
+    C = C_ema.copy()
+    have = counts > 0
+    C[have] = (sums[have] / counts[have].astype(np.float64)[:, None]).astype(np.float32)
+    if spherical:
+        C[have] = normalize(C[have])
+    return C, (np.concatenate(used) if used else np.zeros(0, dtype=np.int32))
 
 
 def rel_gap(X: np.ndarray, C: np.ndarray, rows: Optional[np.ndarray], labels: np.ndarray,

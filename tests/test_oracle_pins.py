@@ -362,6 +362,73 @@ def test_finalisation_is_exact_mean_of_last_pass():
             assert np.array_equal(res.centroids[j], res.ema_centroids[j])
 
 
+def _closing_case():
+    import json
+    with open(os.path.join(GOLDEN, "closing_mean_hand.json")) as f:
+        g = json.load(f)
+    C = np.array(g["C_ema"], dtype=np.float32)
+    batches = [np.array(b, dtype=np.float32) for b in g["batches"]]
+    return g, C, batches
+
+
+def test_final_closing_mean_hand_example():
+    """README "Several GPUs", final_closing_mean: a hand-evaluated replay
+    (tests/golden/closing_mean_hand.json). With labels, the -1 row is left
+    out and the centroid without rows keeps its value; without labels, each
+    row first goes to its nearest final EMA centroid (the far row then pulls
+    cluster 1)."""
+    g, C, batches = _closing_case()
+    Cw, lw = oracle.final_closing_mean(batches, C, np.array(g["assignments"]))
+    assert np.array_equal(Cw, np.array(g["with_labels"]["centroids"], dtype=np.float32))
+    assert lw.tolist() == g["with_labels"]["labels"]
+    Cn, ln = oracle.final_closing_mean(batches, C)
+    assert np.array_equal(Cn, np.array(g["without_labels"]["centroids"], dtype=np.float32))
+    assert ln.tolist() == g["without_labels"]["labels"]
+    Cs, ls = oracle.final_closing_mean(batches, C, spherical=True)
+    assert ls.tolist() == g["without_labels_spherical"]["labels"]
+    m1 = np.array([113.0, 117.0]) / 4.0
+    np.testing.assert_allclose(Cs[1], m1 / np.linalg.norm(m1), rtol=1e-7)
+    assert np.array_equal(Cs[2], np.array([-1.0, 0.0], dtype=np.float32))
+    assert np.array_equal(Cs[0], C[0])
+    with pytest.raises(ValueError):
+        oracle.final_closing_mean(batches, C, np.array(g["assignments"][:-1]))
+
+
+def test_final_closing_mean_without_labels_is_a_lloyd_step():
+    """Without labels the replay is one Lloyd step from the EMA centroids:
+    scipy's vector quantiser (nearest code by Euclidean distance) gives the
+    labels and pandas' group-by mean the centroids, whatever the batch cut."""
+    import pandas as pd
+    from scipy.cluster.vq import vq
+    rng = np.random.default_rng(4)
+    X = rng.standard_normal((3000, 7)).astype(np.float32)
+    C = rng.standard_normal((40, 7)).astype(np.float32)
+    code, _ = vq(X.astype(np.float64), C.astype(np.float64))
+    means = pd.DataFrame(X.astype(np.float64)).groupby(code).mean()
+    want = C.copy()
+    want[means.index.values] = means.values.astype(np.float32)
+    for cut in ([3000], [1, 999, 2000], [700] * 4 + [200]):
+        edges = np.concatenate([[0], np.cumsum(cut)])
+        batches = [X[a:b] for a, b in zip(edges[:-1], edges[1:])]
+        got, lab = oracle.final_closing_mean(batches, C)
+        assert np.array_equal(lab, code.astype(np.int32))
+        np.testing.assert_allclose(got, want, rtol=0, atol=1e-6)
+
+
+def test_final_closing_mean_from_last_pass_labels_is_the_closing_step():
+    """Replaying the rows in row order with the labels the last pass saved
+    gives the closing mean of the run itself (the exact last-pass mean,
+    pinned above), also for a fractional last pass whose unvisited rows carry
+    -1."""
+    X = datagen.tiny(n=4000, d=16, seed=11)
+    res = oracle.train(X, 48, 2.5, seed=3)
+    assert np.sum(res.labels < 0) == 2000
+    batches = [X[a:a + 512] for a in range(0, 4000, 512)]
+    got, lab = oracle.final_closing_mean(batches, res.ema_centroids, res.labels)
+    assert np.array_equal(lab, res.labels)
+    np.testing.assert_allclose(got, res.centroids, rtol=0, atol=1e-6)
+
+
 def test_bf16_search_on_bf16_exact_values_is_the_bf16_data_path():
     """README "Data precision": converting fp32 data to bf16 for the search is
     the same search as storing the data in bf16. On fp32 data whose values are
@@ -741,15 +808,23 @@ def test_revival_donor_frequency_is_size_proportional():
 
 
 def test_revival_reduces_dead_clusters():
-    """Qualitative trend of the blog's ablation: with revival far fewer
-    clusters end up dead than without."""
-    X = datagen.deep(n=20000, d=96, seed=3)
-    on = oracle.train(X, 1024, 3.0, seed=1)
-    off = oracle.train(X, 1024, 3.0, seed=1, unused_threshold=0.0)
-    th_off = 0.1 * float(np.sum(off.N.astype(np.float64))) / 1024
-    dead_off = int(np.sum(off.N < th_off))
-    assert on.dead_at_end <= dead_off
-    assert len(on.split_log) > 0
+    """The trend of the blog's revival ablation (third change, the table for
+    DEEP at k = 16,384 over 5 passes: a few dozen dead clusters with revival
+    against thousands without, and a lower test loss with it), at a
+    deep-like shape with the same rows per cluster (n / k = 64, 5 passes):
+    without revival a few percent of the clusters end under the threshold,
+    with it at least ten times fewer, and the loss is lower."""
+    k = 1024
+    X = datagen.deep(n=65536, d=96, seed=3)
+    on = oracle.train(X, k, 5.0, seed=1)
+    off = oracle.train(X, k, 5.0, seed=1, unused_threshold=0.0)
+    assert off.split_log == []
+    th_off = 0.1 * float(np.sum(off.N.astype(np.float64))) / k
+    dead_off = int(np.sum(off.N.astype(np.float64) < th_off))
+    assert dead_off >= 16, dead_off
+    assert 10 * on.dead_at_end <= dead_off, (on.dead_at_end, dead_off)
+    assert len(on.split_log) >= dead_off
+    assert oracle.mse(X, on.centroids) < oracle.mse(X, off.centroids)
 
 
 # Slow EMA (blog, section on what e-means changes: a second, slower EMA for
