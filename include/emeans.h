@@ -305,14 +305,43 @@ int emeans_end_epoch(emeans_model* m);
  * valid. Errors: EINVAL, ENOTDEVICE, EHIP. */
 int emeans_finalize(emeans_model* m, float* centroids, emeans_stats* stats);
 
+/* Closing mean from a second look at the rows (README "Several GPUs", the
+ * paragraph on final_closing_mean, for callers who run their own batch loop):
+ * once every pass has ended and before emeans_finalize, the caller may send
+ * all rows once more, in any blocks of at most stats.batch_size rows, in one
+ * fixed order.
+ *   batch       device, rows x d, the dtype of emeans_begin
+ *   labels      device, rows int32, or NULL. Given: the label the last pass
+ *               gave each row (saved from emeans_accumulate); -1 marks a row
+ *               that pass skipped, which is left out. NULL: each row is
+ *               assigned once more to its nearest current centroid (the final
+ *               EMA centroids, searched in the run's format) and counted there.
+ *   labels_out  device, rows int32 output or NULL: the label each row was
+ *               counted under (the given one, or the search's).
+ * The first call discards the closing statistics the last pass gathered;
+ * emeans_finalize then makes each centroid that received rows their exact
+ * mean (rescaled to norm 1 in spherical mode) and keeps the EMA centroid of
+ * every other cluster; with opts->no_finalize the replay has no effect. The
+ * model keeps its EMA centroids throughout (emeans_finalize writes only the
+ * caller's table), and the calls after an emeans_finalize start a new replay
+ * from zero. A
+ * given label outside [-1, k) is left out as well, and emeans_finalize then
+ * fails with EINVAL. Errors: EINVAL (NULL model or batch, rows < 1 or above
+ * the batch size, a pass still open), ENOTDEVICE, EHIP. Asynchronous on
+ * opts->stream. */
+int emeans_closing_add(emeans_model* m, const void* batch, int64_t rows, const int32_t* labels,
+                       int32_t* labels_out);
+
 /* Release the model and its device workspace (NULL is accepted). */
 void emeans_free(emeans_model* m);
 
 /* Rows visited by batch slots [start, start + count) of pass `pass` of a
  * training run with this seed (README "Data too big for memory": a fresh
- * order every pass, every vector once). rows_out: device, count int32.
- * Errors: EINVAL (n < 1, n >= 2^31, start + count > n, NULL), ENOTDEVICE, EHIP.
- * Asynchronous on `stream`. */
+ * order every pass, every vector once). pass = -1 gives the order whose first
+ * k entries are the starting rows emeans_train takes for k clusters.
+ * rows_out: device, count int32.
+ * Errors: EINVAL (n < 1, n >= 2^31, pass < -1, start + count > n, NULL),
+ * ENOTDEVICE, EHIP. Asynchronous on `stream`. */
 int emeans_batch_rows(int64_t n, uint64_t seed, int32_t pass, int64_t start, int64_t count,
                       int32_t* rows_out, void* stream);
 

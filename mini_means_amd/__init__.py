@@ -83,6 +83,7 @@ def lib() -> ctypes.CDLL:
         L.emeans_update.argtypes = [c_vp]
         L.emeans_end_epoch.argtypes = [c_vp]
         L.emeans_finalize.argtypes = [c_vp, c_vp, ctypes.POINTER(Stats)]
+        L.emeans_closing_add.argtypes = [c_vp, c_vp, c_i64, c_vp, c_vp]
         L.emeans_free.argtypes = [c_vp]
         L.emeans_free.restype = None
         L.emeans_int8_calibrate.argtypes = [c_vp, c_i64, c_i32, c_vp, ctypes.POINTER(c_dbl), c_vp]
@@ -96,7 +97,8 @@ def lib() -> ctypes.CDLL:
         L.emeans_version.argtypes = []
         for f in ("emeans_recipe", "emeans_train", "emeans_assign", "emeans_batch_rows",
                   "emeans_version", "emeans_begin", "emeans_accumulate", "emeans_update",
-                  "emeans_end_epoch", "emeans_finalize", "emeans_int8_calibrate",
+                  "emeans_end_epoch", "emeans_finalize", "emeans_closing_add",
+                  "emeans_int8_calibrate",
                   "emeans_int8_encode", "emeans_int8_decode"):
             getattr(L, f).restype = ctypes.c_int
         _lib = L
@@ -389,7 +391,8 @@ def fp8_decode(C, shift, scale: float, stream=None):
 
 
 def batch_rows(n: int, seed: int, pass_: int, start: int, count: int, device="cuda", stream=None):
-    """Rows visited by slots [start, start+count) of a pass of a training run."""
+    """Rows visited by slots [start, start+count) of a pass of a training run
+    (pass_ = -1: the order whose first k entries are train()'s starting rows)."""
     import torch
     out = torch.empty((count,), dtype=torch.int32, device=device)
     with torch.cuda.device(out.device):
@@ -402,18 +405,16 @@ def batch_rows(n: int, seed: int, pass_: int, start: int, count: int, device="cu
 
 
 class Stream:
-    """README "Data too big for memory": the training loop of train(), fed
-    batch by batch by the caller (the model lives on the GPU; every batch is a
-    device tensor of the recipe's batch size, the last of each pass the rest).
-
-        em = mini_means_amd.begin(n, start, T)          # start: k x d fp32, on the GPU
-        B = em.recipe["batch_size"]
-        for rows in em.recipe["epoch_rows"]:
-            ...                                          # a fresh order of `rows` vectors
-            em.update(em.accumulate(batch))              # or accumulate pieces, then update
-            em.end_epoch()
-        centroids = em.finalize()
-    """
+    """Streaming training (README "Data too big for memory"): the step loop of
+    train() with the rows supplied by the caller, for data that stays off the
+    device. The model (centroids and running statistics) lives on the device
+    of the start centroids. Pass e takes recipe["epoch_rows"][e] rows in
+    batches of recipe["batch_size"] rows (the pass's last batch holds the
+    rest); each batch goes in through one or more accumulate() calls followed
+    by one update(), and end_epoch() closes the pass. finalize() returns the
+    centroids; final_closing_mean() may first replace the closing statistics
+    with a second look at the rows. All library work runs on `stream` (the
+    current stream of the start centroids' device by default)."""
 
     def __init__(self, n: int, start, T: float = 5.0, seed: int = 1234, *, dtype=None,
                  batch_law="auto", batch_size: int = 0, alpha0: float = 0.0,
@@ -479,8 +480,9 @@ class Stream:
         _require_device(batch)
         if batch.dtype != self.dtype or batch.dim() != 2 or batch.shape[1] != self.d:
             raise EmeansError(f"EINVAL: batch must be rows x {self.d} {self.dtype}")
-        out = torch.empty((batch.shape[0],), dtype=torch.int32, device=self.device) \
-            if labels else None
+        with torch.cuda.stream(self._stream):   # allocated where the library writes it
+            out = torch.empty((batch.shape[0],), dtype=torch.int32, device=self.device) \
+                if labels else None
         _check(lib().emeans_accumulate(self._handle(), batch.data_ptr(), int(batch.shape[0]),
                                        out.data_ptr() if out is not None else None))
         return out
@@ -490,6 +492,63 @@ class Stream:
 
     def end_epoch(self) -> None:
         _check(lib().emeans_end_epoch(self._handle()))
+
+    def final_closing_mean(self, batches, assignments=None, labels_out: bool = False):
+        """Replace the closing statistics with a second look at the rows
+        (README "Several GPUs", final_closing_mean), after the last
+        end_epoch() and before finalize().
+
+        batches: device tensors (rows x d, the model's dtype, row-major) that
+        together go over the rows in one fixed order. assignments: None, or
+        one label per row in that same order (int32 or int64, host or device;
+        -1 for a row the last pass skipped): the labels saved during the last
+        pass, so that no search is needed. Without them every row is assigned
+        once more against the final EMA centroids. Blocks larger than the
+        batch size are sent in pieces. finalize() then gives each centroid the
+        exact mean of the rows counted under it (the EMA centroid where none
+        was). With labels_out, returns the labels used (int32, device, the
+        concatenation over the batches)."""
+        import torch
+        B = int(self.recipe["batch_size"])
+        lab_all = None
+        if assignments is not None:
+            lab_all = torch.as_tensor(assignments)
+            if lab_all.dim() != 1 or lab_all.dtype not in (torch.int32, torch.int64):
+                raise EmeansError("EINVAL: assignments must be one int32 or int64 label per row")
+        used = []
+        pos = 0
+        with torch.cuda.device(self.device), torch.cuda.stream(self._stream):
+            for batch in batches:
+                _require_device(batch)
+                if (batch.dtype != self.dtype or batch.dim() != 2 or batch.shape[1] != self.d
+                        or not batch.is_contiguous()):
+                    raise EmeansError(f"EINVAL: batches must be contiguous rows x {self.d} "
+                                      f"{self.dtype} tensors")
+                m = int(batch.shape[0])
+                for a in range(0, m, B):
+                    piece = batch[a:a + B]
+                    nb = int(piece.shape[0])
+                    lab = None
+                    if lab_all is not None:
+                        if pos + a + nb > lab_all.numel():
+                            raise EmeansError("EINVAL: assignments hold fewer labels than the "
+                                              "batches have rows")
+                        lab = lab_all[pos + a:pos + a + nb].to(self.device, torch.int32)
+                    out = torch.empty((nb,), dtype=torch.int32, device=self.device) \
+                        if labels_out else None
+                    _check(lib().emeans_closing_add(
+                        self._handle(), piece.data_ptr(), nb,
+                        lab.data_ptr() if lab is not None else None,
+                        out.data_ptr() if out is not None else None))
+                    if out is not None:
+                        used.append(out)
+                pos += m
+        if lab_all is not None and pos != lab_all.numel():
+            raise EmeansError("EINVAL: assignments hold more labels than the batches have rows")
+        if labels_out:
+            return torch.cat(used) if used else torch.zeros(0, dtype=torch.int32,
+                                                             device=self.device)
+        return None
 
     def finalize(self):
         """Centroids (k x d float32): the closing mean once every pass ended."""
@@ -537,13 +596,22 @@ class HostTrainOutput:
 
 def train_from_host(Xh, k: int, T: float = 5.0, seed: int = 1234, *, start=None,
                     labels: bool = True, trace: bool = False, order=None, device="cuda",
-                    order_seed: int = 0, **kw) -> HostTrainOutput:
-    """Train on a host array (numpy, any row-major n x d float32 array or
-    memory map) that need not fit on the device: every pass visits a fresh
-    order of the rows (order(e, rows) or a seeded random permutation); each
-    batch is gathered into one of two pinned host buffers and copied on a
-    second stream while the device works on the previous batch (default
-    stream priorities)."""
+                    **kw) -> HostTrainOutput:
+    """Train on a host array (numpy, row-major n x d float32, e.g. a memory
+    map) that need not fit on the device, through a Stream model.
+
+    Visiting order: order(e, rows) gives the host row ids of pass e; by
+    default the library's own sampler (batch_rows), i.e. the very rows
+    emeans_train visits with this seed. Starting centroids: `start` (k x d
+    float32 on the device), by default the rows emeans_train starts from
+    (batch_rows with pass -1). With both defaults a host run sees the same
+    batches as train() on resident data.
+
+    Transfer: each batch is gathered on the host into one of two pinned
+    buffers, which take turns; a copy stream moves it to the device while
+    the model's stream still computes on the other one. One event per buffer
+    says the copy has landed, another that the model is done reading it
+    (both streams keep the default priority)."""
     import numpy as np
     import torch
     Xh = np.asarray(Xh)
@@ -551,60 +619,61 @@ def train_from_host(Xh, k: int, T: float = 5.0, seed: int = 1234, *, start=None,
         raise EmeansError("EINVAL: Xh must be an n x d float32 array")
     n, d = Xh.shape
     dev = torch.device(device)
-    rng = np.random.default_rng(order_seed)
     if start is None:
-        start = torch.from_numpy(np.ascontiguousarray(
-            Xh[np.sort(rng.choice(n, k, replace=False))])).to(dev)
+        first = batch_rows(n, seed, -1, 0, k, device=dev).cpu().numpy()
+        start = torch.from_numpy(np.ascontiguousarray(Xh[first])).to(dev)
+    if order is None:
+        def order(e, rows):
+            return batch_rows(n, seed, e, 0, rows, device=dev).cpu().numpy()
     em = Stream(n, start, T, seed, **kw)
-    B = em.recipe["batch_size"]
-    pinned = [torch.empty((B, d), dtype=torch.float32).pin_memory() for _ in range(2)]
-    dbuf = [torch.empty((B, d), dtype=torch.float32, device=dev) for _ in range(2)]
-    copy_stream = torch.cuda.Stream(device=dev)
-    ready = [torch.cuda.Event() for _ in range(2)]
-    used = [torch.cuda.Event() for _ in range(2)]
-    for e in used:
-        e.record(em._stream)
-    out_labels = np.full(n, -1, dtype=np.int32) if labels else None
-    jobs = []
-    for e, rows_e in enumerate(em.recipe["epoch_rows"]):
-        perm = np.asarray(order(e, rows_e)) if order is not None else rng.permutation(n)[:rows_e]
-        for i in range(0, rows_e, B):
-            jobs.append((e, perm[i:i + B]))
-    last_e = len(em.recipe["epoch_rows"]) - 1
+    B = int(em.recipe["batch_size"])
+    passes = em.recipe["epoch_rows"]
+    # (pass, host rows) of every update step, in schedule order
+    steps = [(e, ids[a:a + B]) for e, rows_e in enumerate(passes)
+             for ids in [np.asarray(order(e, rows_e))] for a in range(0, rows_e, B)]
+    host = [torch.empty((B, d), dtype=torch.float32).pin_memory() for _ in range(2)]
+    staged = [torch.empty((B, d), dtype=torch.float32, device=dev) for _ in range(2)]
+    mover = torch.cuda.Stream(device=dev)
+    landed = [torch.cuda.Event() for _ in range(2)]
+    released = [torch.cuda.Event() for _ in range(2)]
+    for ev in released:
+        ev.record(em._stream)
 
-    def stage(j):
-        """Gather job j's rows into its pinned buffer and start the copy."""
-        slot = j % 2
-        rows = jobs[j][1]
-        used[slot].synchronize()          # the device is done with this slot's buffer
-        np.take(Xh, rows, axis=0, out=pinned[slot].numpy()[:len(rows)])
-        with torch.cuda.stream(copy_stream):
-            copy_stream.wait_event(used[slot])
-            dbuf[slot][:len(rows)].copy_(pinned[slot][:len(rows)], non_blocking=True)
-            ready[slot].record(copy_stream)
+    def send(j):
+        """Gather step j's rows into buffer j % 2 and queue its upload."""
+        buf = j % 2
+        ids = steps[j][1]
+        released[buf].synchronize()      # the model no longer reads this buffer
+        np.take(Xh, ids, axis=0, out=host[buf].numpy()[:len(ids)])
+        mover.wait_event(released[buf])
+        with torch.cuda.stream(mover):
+            staged[buf][:len(ids)].copy_(host[buf][:len(ids)], non_blocking=True)
+        landed[buf].record(mover)
 
-    pending = []
-    if jobs:
-        stage(0)
-    for j, (e, rows) in enumerate(jobs):
-        slot = j % 2
-        if j + 1 < len(jobs):
-            stage(j + 1)                  # overlaps the copy with this batch's compute
-        em._stream.wait_event(ready[slot])
-        want = trace or (labels and e == last_e)
-        lab = em.accumulate(dbuf[slot][:len(rows)], labels=want)
-        used[slot].record(em._stream)
-        em.update(lab)
+    final = len(passes) - 1
+    kept = []                              # (pass, rows, device labels)
+    if steps:
+        send(0)
+    for j, (e, ids) in enumerate(steps):
+        buf = j % 2
+        if j + 1 < len(steps):
+            send(j + 1)                  # the next upload overlaps this step
+        em._stream.wait_event(landed[buf])
+        want = trace or (labels and e == final)
+        lab = em.accumulate(staged[buf][:len(ids)], labels=want)
+        released[buf].record(em._stream)
+        em.update()
         if lab is not None:
-            pending.append((e, rows, lab.to("cpu", non_blocking=True)))
-        if j + 1 == len(jobs) or jobs[j + 1][0] != e:
+            kept.append((e, ids, lab))
+        if j + 1 == len(steps) or steps[j + 1][0] != e:
             em.end_epoch()
-    C = em.finalize()
+    C = em.finalize()                    # synchronises the model's stream
+    out_labels = np.full(n, -1, dtype=np.int32) if labels else None
     tr = []
-    for e, rows, lab in pending:
-        if labels and e == last_e:
-            out_labels[rows] = lab.numpy()
+    for e, ids, lab in kept:
+        h = lab.cpu().numpy()
+        if labels and e == final:
+            out_labels[ids] = h
         if trace:
-            tr.append(lab.numpy())
+            tr.append(h)
     return HostTrainOutput(C, out_labels, em, np.concatenate(tr) if trace and tr else None)
-

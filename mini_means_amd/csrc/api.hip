@@ -351,6 +351,7 @@ struct emeans_model {
   int64_t rows_step = 0;  // rows accumulated since the last update
   int64_t trace_off = 0;
   bool last_begun = false;
+  bool replay = false;    // the closing statistics come from emeans_closing_add
 
   // workspace
   void* base = nullptr;
@@ -377,6 +378,7 @@ struct emeans_model {
   // per pass: [0, P) sum of distances, [P, 3P) sum n^2 and sum n, [3P, 4P) splits (int64)
   double* dstat = nullptr;
   int64_t* counters = nullptr;  // [0] splits, [1] logged, [2] dead count, [3] splits this pass
+  int32_t* bad_labels = nullptr;  // labels outside [-1, k) sent to emeans_closing_add
   std::vector<Span> spans;
 
   ~emeans_model() {
@@ -513,6 +515,7 @@ struct emeans_model {
     if (conv) ar.want(&xb, (size_t)B * d * (conv == EMEANS_F8 ? 1 : 2));
     ar.want(&dstat, (size_t)4 * EMEANS_MAX_PASSES);
     ar.want(&counters, 4);
+  ar.want(&bad_labels, 1);
     if (log_cap > 0) ar.want(&dlog, (size_t)3 * log_cap);
     HIP_RET(ar.alloc(&base, st));
     if (external_C) C = external_C;
@@ -526,6 +529,40 @@ struct emeans_model {
     HIP_RET(hipMemsetAsync(LS, 0, sizeof(float) * kd, st));
     HIP_RET(hipMemsetAsync(dstat, 0, sizeof(double) * 4 * EMEANS_MAX_PASSES, st));
     HIP_RET(hipMemsetAsync(counters, 0, sizeof(int64_t) * 4, st));
+    HIP_RET(hipMemsetAsync(bad_labels, 0, sizeof(int32_t), st));
+    return EMEANS_OK;
+  }
+
+  // Closing replay (README "Several GPUs", final_closing_mean): nb rows of X
+  // in the caller's order with their last-pass labels (given; -1 = left out)
+  // or, when given is NULL, labels from a search against the current (final
+  // EMA) centroids. The first call replaces the closing statistics the last
+  // pass gathered. labels_out, when non-null, receives the labels used.
+  int closing_add(const void* X, int nb, const int32_t* given, int32_t* labels_out) {
+    if (!replay) {
+      HIP_RET(hipMemsetAsync(pass_counts, 0, sizeof(int32_t) * k, st));
+      HIP_RET(hipMemsetAsync(LS, 0, sizeof(float) * (size_t)k * d, st));
+      HIP_RET(hipMemsetAsync(bad_labels, 0, sizeof(int32_t), st));
+      replay = true;
+    }
+    const int32_t* lab = given;
+    if (given) {
+      HIP_RET(launch_label_hist(given, nb, k, pcounts, bad_labels, st));
+    } else {
+      if (conv)
+        HIP_RET(launch_convert_rows(static_cast<const float*>(X), d, nullptr, nb, conv, sshift,
+                                    sscale, xb, st));
+      HIP_RET(launch_assign(conv ? conv : dt, conv ? (const void*)xb : X, d, nullptr, nb,
+                            search_table(), bias, k, blab, nullptr, pcounts, nullptr, sph, st));
+      lab = blab;
+    }
+    if (labels_out)
+      HIP_RET(hipMemcpyAsync(labels_out, lab, sizeof(int32_t) * nb, hipMemcpyDeviceToDevice, st));
+    HIP_RET(launch_scan(pcounts, k, group_rows(dt, d), off, cursor, ovf, ovf_n, counts, st));
+    HIP_RET(launch_scatter(lab, nullptr, nb, k, cursor, order, nullptr, st));
+    HIP_RET(launch_group(dt, X, d, order, off, ovf, ovf_n, k, group_rows(dt, d), nb, s_acc, false,
+                         st));
+    HIP_RET(launch_closing_add(k, d, counts, s_acc, pass_counts, LS, st));
     return EMEANS_OK;
   }
 
@@ -556,7 +593,7 @@ struct emeans_model {
       hipError_t er = launch_scan(pcounts, k, group_rows(dt, d), off, cursor, ovf, ovf_n, counts,
                                   st);
       if (er != hipSuccess) return er;
-      return launch_scatter(blab, rws, nb, cursor, order, out_labels, st);
+      return launch_scatter(blab, rws, nb, k, cursor, order, out_labels, st);
     }));
     HIP_RET(timed(kGroup, [&] {
       return launch_group(dt, X, d, order, off, ovf, ovf_n, k, group_rows(dt, d), nb, s_acc, add,
@@ -622,15 +659,26 @@ struct emeans_model {
     // the slow centroids come from the EMA centroids before the closing mean
     if (slow_out)
       HIP_RET(launch_slow_final(k, d, slow_started ? N2 : nullptr, S2, C, slow_out, sph, st));
-    if (closing) HIP_RET(launch_finalize(k, d, pass_counts, LS, C, sph, st));
-    if (out_C && out_C != C)
-      HIP_RET(hipMemcpyAsync(out_C, C, sizeof(float) * (size_t)k * d, hipMemcpyDeviceToDevice, st));
+    // the closing mean goes into the caller's table; the model's own working
+    // centroids stay the EMA centroids (a later closing replay searches them)
+    float* dst = out_C ? out_C : C;
+    if (dst != C)
+      HIP_RET(hipMemcpyAsync(dst, C, sizeof(float) * (size_t)k * d, hipMemcpyDeviceToDevice, st));
+    if (closing) HIP_RET(launch_finalize(k, d, pass_counts, LS, dst, sph, st));
     HIP_RET(hipMemcpyAsync(host_stat, dstat, sizeof host_stat, hipMemcpyDeviceToHost, st));
     HIP_RET(hipMemcpyAsync(host_counters, counters, sizeof host_counters, hipMemcpyDeviceToHost, st));
     if (log_cap > 0)
       HIP_RET(hipMemcpyAsync(split_log, dlog, sizeof(int32_t) * 3 * (size_t)log_cap,
                              hipMemcpyDeviceToHost, st));
+    int32_t host_bad = 0;
+    if (replay)
+      HIP_RET(hipMemcpyAsync(&host_bad, bad_labels, sizeof host_bad, hipMemcpyDeviceToHost, st));
     HIP_RET(hipStreamSynchronize(st));
+    replay = false;  // the next emeans_closing_add starts a new replay
+    if (host_bad)
+      return fail(EMEANS_EINVAL,
+                  "emeans_closing_add received %d labels outside [-1, k); those rows were left "
+                  "out of the closing mean", host_bad);
     if (!stats) return EMEANS_OK;
     fill_stats(r, stats);
     for (int q = 0; q < r.npass; ++q) {
@@ -671,7 +719,7 @@ extern "C" {
 
 const char* emeans_last_error(void) { return g_err.c_str(); }
 
-int emeans_version(void) { return 100; }
+int emeans_version(void) { return 101; }
 
 int emeans_recipe(int64_t n, int32_t d, int32_t k, double T, const emeans_opts* opts,
                   emeans_stats* out) {
@@ -688,13 +736,16 @@ int emeans_batch_rows(int64_t n, uint64_t seed, int32_t pass, int64_t start, int
                       int32_t* rows_out, void* stream) {
   g_err.clear();
   if (n < 1 || n >= ((int64_t)1 << 31)) return fail(EMEANS_EINVAL, "n out of range");
-  if (pass < 0 || start < 0 || count < 0 || start + count > n)
+  if (pass < -1) return fail(EMEANS_EINVAL, "pass must be >= -1 (got %d)", pass);
+  if (start < 0 || count < 0 || start + count > n)
     return fail(EMEANS_EINVAL, "slot range [%lld, %lld) outside [0, %lld)", (long long)start,
                 (long long)(start + count), (long long)n);
   if (!rows_out) return fail(EMEANS_EINVAL, "rows_out is NULL");
   int rc = check_device(rows_out, "rows_out");
   if (rc) return rc;
-  const PermKey pk = make_perm_key((uint64_t)n, seed, kStreamPerm, (uint64_t)pass);
+  // pass -1: the order whose first k entries are emeans_train's starting rows
+  const PermKey pk = pass < 0 ? make_perm_key((uint64_t)n, seed, kStreamInit, 0)
+                              : make_perm_key((uint64_t)n, seed, kStreamPerm, (uint64_t)pass);
   const hipError_t e = launch_sample_rows_i32(pk, (uint64_t)start, (int)count, rows_out,
                                               static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return fail(EMEANS_EHIP, "sampler launch: %s", hipGetErrorString(e));
@@ -912,6 +963,24 @@ int emeans_finalize(emeans_model* m, float* centroids, emeans_stats* stats) {
   if (!centroids) return fail(EMEANS_EINVAL, "centroids must not be NULL");
   if ((rc = check_device(centroids, "centroids"))) return rc;
   return m->finish(centroids, stats, !m->no_finalize && m->e == m->r.npass);
+}
+
+int emeans_closing_add(emeans_model* m, const void* batch, int64_t rows, const int32_t* labels,
+                       int32_t* labels_out) {
+  g_err.clear();
+  int rc;
+  if (!m) return fail(EMEANS_EINVAL, "model is NULL");
+  if (!batch) return fail(EMEANS_EINVAL, "batch is NULL");
+  if (m->e < m->r.npass)
+    return fail(EMEANS_EINVAL, "the closing replay starts after the last pass has ended "
+                "(pass %d of %d is open)", m->e, m->r.npass);
+  if (rows < 1 || rows > m->r.B)
+    return fail(EMEANS_EINVAL, "rows must be in [1, %lld] (the batch size), got %lld",
+                (long long)m->r.B, (long long)rows);
+  if ((rc = check_device(batch, "batch")) || (labels && (rc = check_device(labels, "labels"))) ||
+      (labels_out && (rc = check_device(labels_out, "labels_out"))))
+    return rc;
+  return m->closing_add(batch, (int)rows, labels, labels_out);
 }
 
 void emeans_free(emeans_model* m) { delete m; }

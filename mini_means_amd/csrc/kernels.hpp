@@ -78,9 +78,20 @@ hipError_t launch_scan(int32_t* counts, int k, int R, int32_t* off, int32_t* cur
                        int2* ovf, int32_t* ovf_n, int32_t* acc, hipStream_t st);
 
 // Bucket the batch by label: order[cursor[label]++] = rows[r] (r when rows is
-// NULL); when out_labels is non-null also out_labels[rows[r]] = label.
-hipError_t launch_scatter(const int32_t* labels, const uint32_t* rows, int nb, int32_t* cursor,
-                          uint32_t* order, int32_t* out_labels, hipStream_t st);
+// NULL); when out_labels is non-null also out_labels[rows[r]] = label. Rows
+// whose label lies outside [0, k) are skipped.
+hipError_t launch_scatter(const int32_t* labels, const uint32_t* rows, int nb, int k,
+                          int32_t* cursor, uint32_t* order, int32_t* out_labels, hipStream_t st);
+
+// counts[labels[r]] += 1 for labels in [0, k); *bad += 1 for each label that is
+// neither in [0, k) nor -1.
+hipError_t launch_label_hist(const int32_t* labels, int nb, int k, int32_t* counts,
+                             int32_t* bad, hipStream_t st);
+
+// pass_counts += counts and LS += s_acc for every cluster with a count; counts
+// and s_acc are reset.
+hipError_t launch_closing_add(int k, int d, int32_t* counts, float* s_acc, int32_t* pass_counts,
+                              float* LS, hipStream_t st);
 
 // Rows per grouping work item (R of launch_scan and launch_group) for rows of
 // d elements of type dt: 64, or more for rows of at most 1 KB.

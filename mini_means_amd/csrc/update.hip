@@ -326,15 +326,53 @@ __device__ __forceinline__ bool group_item(int w, int k, int R, const int32_t* _
   return true;
 }
 
-__global__ void scatter_kernel(const int32_t* labels, const uint32_t* rows, int nb,
+// A label outside [0, k) (a row a closing replay leaves out) is not bucketed;
+// the counts of launch_label_hist skip the same rows.
+__global__ void scatter_kernel(const int32_t* labels, const uint32_t* rows, int nb, int k,
                                int32_t* cursor, uint32_t* order, int32_t* out_labels) {
   const int r = blockIdx.x * blockDim.x + threadIdx.x;
   if (r >= nb) return;
   const int j = labels[r];
+  if ((unsigned)j >= (unsigned)k) return;
   const uint32_t row = rows ? rows[r] : (uint32_t)r;
   const int pos = atomicAdd(&cursor[j], 1);
   order[pos] = row;
   if (out_labels) out_labels[row] = j;
+}
+
+// Counts of the labels a caller supplies (the closing replay): labels in
+// [0, k) are counted, -1 marks a row to leave out, and any other value is
+// left out too and counted in *bad (reported on the host).
+__global__ void label_hist_kernel(const int32_t* __restrict__ labels, int nb, int k,
+                                  int32_t* __restrict__ counts, int32_t* __restrict__ bad) {
+  const int r = blockIdx.x * blockDim.x + threadIdx.x;
+  if (r >= nb) return;
+  const int j = labels[r];
+  if ((unsigned)j < (unsigned)k)
+    atomicAdd(&counts[j], 1);
+  else if (j != -1)
+    atomicAdd(bad, 1);
+}
+
+// One wave per cluster: the replayed rows' counts and sums join the closing
+// statistics (pass_counts, LS); counts and s_acc are reset for the next call.
+__global__ __launch_bounds__(256) void closing_add_kernel(int k, int d, int32_t* counts,
+                                                          float* s_acc, int32_t* pass_counts,
+                                                          float* LS) {
+  const int j = blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  if (j >= k) return;
+  const int n = counts[j];
+  if (n == 0) return;
+  const size_t base = (size_t)j * d;
+  for (int e = lane; e < d; e += 64) {
+    LS[base + e] += s_acc[base + e];
+    s_acc[base + e] = 0.0f;
+  }
+  if (lane == 0) {
+    pass_counts[j] += n;
+    counts[j] = 0;
+  }
 }
 
 // Column unit `col` of a row as fp32 values: 16 bytes of fp32 / bf16 / fp16
@@ -1205,10 +1243,24 @@ hipError_t launch_scan(int32_t* counts, int k, int R, int32_t* off, int32_t* cur
   return hipGetLastError();
 }
 
-hipError_t launch_scatter(const int32_t* labels, const uint32_t* rows, int nb, int32_t* cursor,
-                          uint32_t* order, int32_t* out_labels, hipStream_t st) {
+hipError_t launch_scatter(const int32_t* labels, const uint32_t* rows, int nb, int k,
+                          int32_t* cursor, uint32_t* order, int32_t* out_labels, hipStream_t st) {
   if (nb <= 0) return hipSuccess;
-  scatter_kernel<<<(nb + 255) / 256, 256, 0, st>>>(labels, rows, nb, cursor, order, out_labels);
+  scatter_kernel<<<(nb + 255) / 256, 256, 0, st>>>(labels, rows, nb, k, cursor, order,
+                                                   out_labels);
+  return hipGetLastError();
+}
+
+hipError_t launch_label_hist(const int32_t* labels, int nb, int k, int32_t* counts,
+                             int32_t* bad, hipStream_t st) {
+  if (nb <= 0) return hipSuccess;
+  label_hist_kernel<<<(nb + 255) / 256, 256, 0, st>>>(labels, nb, k, counts, bad);
+  return hipGetLastError();
+}
+
+hipError_t launch_closing_add(int k, int d, int32_t* counts, float* s_acc, int32_t* pass_counts,
+                              float* LS, hipStream_t st) {
+  closing_add_kernel<<<(k + 3) / 4, 256, 0, st>>>(k, d, counts, s_acc, pass_counts, LS);
   return hipGetLastError();
 }
 

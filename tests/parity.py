@@ -207,10 +207,13 @@ def step_offsets(rc: dict) -> np.ndarray:
 
 
 def lockstep(X: np.ndarray, out, k: int, T: float, seed: int, sample: int = 0,
-             rng_seed: int = 0, progress: int = 0, **opts):
+             rng_seed: int = 0, progress: int = 0, full=None, **opts):
     """Replay a GPU training run in the oracle, adopting the GPU's labels after
     checking them (all slots, or `sample` random slots per step), and return
-    the oracle's result and the check summary."""
+    the oracle's result and the check summary.
+
+    full: {step: count} checks the first `count` slots of that step (every
+    slot when count is None), i.e. one assign launch slot by slot."""
     trace = out.trace.cpu().numpy()
     conv = oracle.converter(opts.get("bf16_search", False), opts.get("search"),
                             opts.get("search_shift"), opts.get("search_scale", 1.0))
@@ -227,6 +230,13 @@ def lockstep(X: np.ndarray, out, k: int, T: float, seed: int, sample: int = 0,
         return trace[offs[t]:offs[t + 1]]
 
     def check_slots(t, Bt):
+        if full and t in full:
+            cnt = full[t]
+            if cnt is None or cnt >= Bt:
+                summary["full_slots"] = summary.get("full_slots", 0) + Bt
+                return None
+            summary["full_slots"] = summary.get("full_slots", 0) + cnt
+            return np.arange(cnt)
         if not sample or sample >= Bt:
             return None
         return np.sort(rng.choice(Bt, size=sample, replace=False))

@@ -7,7 +7,9 @@ times (emeans_train with the scaling-law recipe, seed 1234).
   of slots per step against its own fp64 assignment, adopts the GPU labels,
   and the final states are compared (running counts bit for bit, revival log
   exactly, centroids to 1e-4 relative L2 for fp32 data and 1e-2 for bf16,
-  final MSE on a sample of rows to 1e-3).
+  final MSE on a sample of rows to 1e-3). One step mid-run is checked slot
+  by slot: every one of its 65,536 slots (one whole assign launch), and the
+  first 262,144 slots of a 4M-row step on the large workload.
 
 The workloads: embedding-like 1M x 768 (k 4096), deep-like 1M x 96 (k 16384),
 SIFT-like 1M x 128 (k 16384), fp32, 5 passes; large 100M x 128 bf16
@@ -85,9 +87,12 @@ def test_fullsize_train_lockstep(mm, name):
     torch.cuda.synchronize()
     log(f"{name}: GPU train {time.time() - t0:.2f}s, {out.stats['n_splits']} revivals")
     t0 = time.time()
-    res, summ = lockstep(X, out, k, T, seed, sample=192, rng_seed=3, progress=16)
+    mid = oracle.recipe(len(X), X.shape[1], k, T)["total_steps"] // 2
+    res, summ = lockstep(X, out, k, T, seed, sample=192, rng_seed=3, progress=16,
+                         full={mid: None})
     log(f"{name}: oracle replay {time.time() - t0:.1f}s {summ}")
     assert summ["steps"] == res.recipe["total_steps"]
+    assert summ["full_slots"] == res.recipe["batch_size"]
     assert np.array_equal(out.counts.cpu().numpy(), res.N)
     assert out.stats["n_splits"] == len(res.split_log)
     assert out.split_log == [tuple(s) for s in res.split_log]
@@ -142,6 +147,11 @@ def test_fullsize_large_assign(mm, large):
     check_dists(X, Cs, rows, lab[rows], dist[rows], what="large assign")
 
 
+def res_mid(k, T):
+    W = datagen.WORKLOADS["large"]
+    return oracle.recipe(W["n"], W["d"], k, T)["total_steps"] // 2
+
+
 def test_fullsize_large_train_lockstep(mm, large):
     import torch
     W = datagen.WORKLOADS["large"]
@@ -152,8 +162,10 @@ def test_fullsize_large_train_lockstep(mm, large):
     torch.cuda.synchronize()
     log(f"large: GPU train {time.time() - t0:.2f}s, {out.stats['n_splits']} revivals")
     t0 = time.time()
-    res, summ = lockstep(X, out, k, T, seed, sample=96, rng_seed=4, progress=8)
+    res, summ = lockstep(X, out, k, T, seed, sample=96, rng_seed=4, progress=8,
+                         full={res_mid(k, T): 1 << 18})
     log(f"large: oracle replay {time.time() - t0:.1f}s {summ}")
+    assert summ["full_slots"] == 1 << 18
     assert np.array_equal(out.counts.cpu().numpy(), res.N)
     assert out.split_log == [tuple(s) for s in res.split_log]
     assert np.array_equal(out.labels.cpu().numpy(), res.labels)
