@@ -254,6 +254,24 @@ int emeans_train(const void* X, int64_t n, int32_t d, int32_t k, double T, uint6
 int emeans_assign(const void* X, int64_t n, int32_t d, const float* C, int32_t k,
                   int32_t* labels, float* dists, const emeans_opts* opts);
 
+/* Nearest centroid of each row, as emeans_assign, with no memory allocation:
+ * for callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc). Arguments,
+ * results and errors are those of emeans_assign. The working memory (the
+ * centroid bias, the search copy of the centroids, and the converted rows
+ * when opts->search or bf16_search converts fp32 rows) comes from one device
+ * array of EMEANS_STATIC_SCRATCH_BYTES per GPU, held from the library's load
+ * until the process ends. The need is 4k bytes, plus 2kd for a bf16/fp16
+ * search copy or kd for int8/uint8/E4M3 codes, plus 2nd (nd for FP8) for
+ * converted rows, each part rounded up to 256 bytes; sizes that need more
+ * fail with EINVAL before any device work. Every call on one GPU uses the same array, so calls
+ * that overlap on one GPU (on different streams, or from several threads
+ * without ordering) race and give undefined results; calls queued on one
+ * stream are ordered. Asynchronous on opts->stream. */
+#define EMEANS_STATIC_SCRATCH_BYTES (32u << 20)
+int emeans_assign_static(const void* X, int64_t n, int32_t d, const float* C, int32_t k,
+                         int32_t* labels, float* dists, const emeans_opts* opts);
+
 /* ---------------------------------------------------------------------------
  * Streaming training (README "Data too big for memory"): the loop that
  * emeans_train runs, fed batch by batch by the caller, for data that does not

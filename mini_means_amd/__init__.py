@@ -76,6 +76,7 @@ def lib() -> ctypes.CDLL:
                                    ctypes.POINTER(Opts), ctypes.POINTER(Stats)]
         L.emeans_assign.argtypes = [c_vp, c_i64, c_i32, c_vp, c_i32, c_vp, c_vp,
                                     ctypes.POINTER(Opts)]
+        L.emeans_assign_static.argtypes = L.emeans_assign.argtypes
         L.emeans_batch_rows.argtypes = [c_i64, ctypes.c_uint64, c_i32, c_i64, c_i64, c_vp, c_vp]
         L.emeans_begin.argtypes = [c_i64, c_i32, c_i32, c_dbl, ctypes.c_uint64, c_vp,
                                    ctypes.POINTER(Opts), ctypes.POINTER(c_vp)]
@@ -95,7 +96,8 @@ def lib() -> ctypes.CDLL:
         L.emeans_last_error.restype = ctypes.c_char_p
         L.emeans_last_error.argtypes = []
         L.emeans_version.argtypes = []
-        for f in ("emeans_recipe", "emeans_train", "emeans_assign", "emeans_batch_rows",
+        for f in ("emeans_recipe", "emeans_train", "emeans_assign", "emeans_assign_static",
+                  "emeans_batch_rows",
                   "emeans_version", "emeans_begin", "emeans_accumulate", "emeans_update",
                   "emeans_end_epoch", "emeans_finalize", "emeans_closing_add",
                   "emeans_int8_calibrate",
@@ -281,11 +283,15 @@ def train(X, k: int, T: float = 5.0, seed: int = 1234, *, batch_law="auto", batc
 
 
 def assign(X, C, *, with_dists: bool = True, bf16_search: bool = False, spherical: bool = False,
-           search=None, search_shift=None, search_scale=None, stream=None):
+           search=None, search_shift=None, search_scale=None, stream=None, no_alloc: bool = False,
+           out=None):
     """Nearest centroid (int32 labels) and squared distance (float32) of each row.
     bf16_search: search fp32 rows in bf16 (rows and centroids rounded).
     search / search_shift / search_scale: the general converter (as train).
-    spherical: the centroid with the highest dot product, and that similarity."""
+    spherical: the centroid with the highest dot product, and that similarity.
+    no_alloc: call emeans_assign_static (the library allocates nothing; its
+    working memory is one fixed device array per GPU, shared by every call).
+    out: (labels, dists or None) tensors to write into instead of new ones."""
     import torch
     _require_device(X)
     if not (getattr(C, "is_cuda", False) and C.dtype == torch.float32 and C.is_contiguous()):
@@ -295,16 +301,26 @@ def assign(X, C, *, with_dists: bool = True, bf16_search: bool = False, spherica
     if C.shape[1] != d:
         raise EmeansError("EINVAL: C and X differ in dimension")
     with torch.cuda.device(X.device):
-        labels = torch.empty((n,), dtype=torch.int32, device=X.device)
-        dists = torch.empty((n,), dtype=torch.float32, device=X.device) if with_dists else None
+        if out is not None:
+            labels, dists = out
+            if not (getattr(labels, "is_cuda", False) and labels.dtype == torch.int32
+                    and labels.is_contiguous() and labels.numel() >= n):
+                raise EmeansError("EINVAL: out labels must be a contiguous int32 GPU tensor of n")
+            if dists is not None and not (getattr(dists, "is_cuda", False)
+                                          and dists.dtype == torch.float32
+                                          and dists.is_contiguous() and dists.numel() >= n):
+                raise EmeansError("EINVAL: out dists must be a contiguous float32 GPU tensor of n")
+        else:
+            labels = torch.empty((n,), dtype=torch.int32, device=X.device)
+            dists = torch.empty((n,), dtype=torch.float32, device=X.device) if with_dists else None
         o = _opts(_dtype_of(X), stream=_stream_ptr(X, stream))
         o.bf16_search = 1 if bf16_search else 0
         o.spherical = 1 if spherical else 0
         _set_search(o, search, search_shift, search_scale, d)
+        fn = lib().emeans_assign_static if no_alloc else lib().emeans_assign
         if n:
-            _check(lib().emeans_assign(X.data_ptr(), n, d, C.data_ptr(), k, labels.data_ptr(),
-                                       dists.data_ptr() if dists is not None else None,
-                                       ctypes.byref(o)))
+            _check(fn(X.data_ptr(), n, d, C.data_ptr(), k, labels.data_ptr(),
+                      dists.data_ptr() if dists is not None else None, ctypes.byref(o)))
     return labels, dists
 
 

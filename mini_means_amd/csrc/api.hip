@@ -6,6 +6,7 @@
 #include <string.h>
 
 #include <chrono>
+#include <mutex>
 #include <new>
 #include <string>
 #include <vector>
@@ -14,6 +15,10 @@
 #include "kernels.hpp"
 
 using namespace emk;
+
+// Device scratch of the allocation-free assignment (emeans_assign_static); host
+// code reaches it only through the address hipGetSymbolAddress gives per device.
+static __device__ __align__(256) unsigned char scratch[EMEANS_STATIC_SCRATCH_BYTES];
 
 namespace {
 
@@ -176,21 +181,56 @@ struct Arena {
   void want(T** p, size_t count) {
     wants.push_back({reinterpret_cast<void**>(p), count * sizeof(T)});
   }
-  hipError_t alloc(void** base, hipStream_t st) {
-    size_t total = 0;
-    for (auto& w : wants) total += (w.second + 255) & ~(size_t)255;
-    if (total == 0) total = 256;
-    hipError_t e = hipMallocAsync(base, total, st);
-    if (e != hipSuccess) return e;
+  size_t total() const {
+    size_t t = 0;
+    for (auto& w : wants) t += (w.second + 255) & ~(size_t)255;
+    return t == 0 ? 256 : t;
+  }
+  // Carve the buffers out of `base` (256-byte aligned, at least total() bytes).
+  void place(void* base) {
     size_t off = 0;
     for (auto& w : wants) {
-      *w.first = static_cast<char*>(*base) + off;
+      *w.first = static_cast<char*>(base) + off;
       off += (w.second + 255) & ~(size_t)255;
     }
-    used = total;
+    used = total();
+  }
+  hipError_t alloc(void** base, hipStream_t st) {
+    hipError_t e = hipMallocAsync(base, total(), st);
+    if (e != hipSuccess) return e;
+    place(*base);
     return hipSuccess;
   }
 };
+
+// Device scratch of the allocation-free assignment (emeans_assign_static):
+// bias and search copies of the centroids, and the converted rows when a
+// search converter is used. Every GPU the library runs on holds its own copy
+// from the module's load until the process ends.
+constexpr size_t kScratchBytes = EMEANS_STATIC_SCRATCH_BYTES;
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_addr[kMaxDevices] = {};
+
+// Device address of the current device's copy of `scratch`, looked up once
+// per device (the array's host-side name is not a device address).
+int scratch_address(void** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return fail(EMEANS_EHIP, "hipGetDevice: %s", hipGetErrorString(e));
+  if (dev < 0 || dev >= kMaxDevices) return fail(EMEANS_EINVAL, "device %d out of range", dev);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_addr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !p)
+      return fail(EMEANS_EHIP, "hipGetSymbolAddress(scratch): %s", hipGetErrorString(e));
+    g_scratch_addr[dev] = p;
+  }
+  *out = g_scratch_addr[dev];
+  return EMEANS_OK;
+}
 
 }  // namespace
 
@@ -752,8 +792,11 @@ int emeans_batch_rows(int64_t n, uint64_t seed, int32_t pass, int64_t start, int
   return EMEANS_OK;
 }
 
-int emeans_assign(const void* X, int64_t n, int32_t d, const float* C, int32_t k,
-                  int32_t* labels, float* dists, const emeans_opts* opts) {
+// emeans_assign and emeans_assign_static: the same checks and kernels; the
+// workspace is allocated stream-ordered (use_scratch false) or carved out of
+// the device array `scratch` (use_scratch true, nothing allocated).
+static int assign_impl(const void* X, int64_t n, int32_t d, const float* C, int32_t k,
+                       int32_t* labels, float* dists, const emeans_opts* opts, bool use_scratch) {
   g_err.clear();
   const int32_t dtype = opts ? opts->dtype : EMEANS_F32;
   if (!dtype_known(dtype))
@@ -767,23 +810,12 @@ int emeans_assign(const void* X, int64_t n, int32_t d, const float* C, int32_t k
   int rc;
   if ((rc = check_dtype(d, opts))) return rc;
   if ((rc = check_search(opts))) return rc;
-  if (n == 0) return EMEANS_OK;
-  if ((rc = check_device(X, "X")) || (rc = check_device(C, "C")) ||
-      (rc = check_device(labels, "labels")) || (dists && (rc = check_device(dists, "dists"))))
-    return rc;
-  hipStream_t st = static_cast<hipStream_t>(opts ? opts->stream : nullptr);
   const bool bf16 = dtype == EMEANS_BF16;
   const bool i8 = dtype == EMEANS_I8;
   const bool u8 = dtype == EMEANS_U8;
   const bool f8 = dtype == EMEANS_F8;
   const bool f16 = dtype == EMEANS_F16;
-  if (opts && opts->search_shift && (rc = check_device(opts->search_shift, "search_shift")))
-    return rc;
   const int32_t conv = search_format(opts);  // fp32 rows converted for the search
-  const float* sshift = conv ? opts->search_shift : nullptr;
-  const float sscale = conv == EMEANS_F8 ? (float)opts->search_scale : 1.0f;
-  const bool hf = f16 || conv == EMEANS_F16;
-  const bool sph = opts && opts->spherical;  // highest dot product, similarity out
   void* base = nullptr;
   float* bias = nullptr;
   uint16_t* chat = nullptr;
@@ -796,8 +828,30 @@ int emeans_assign(const void* X, int64_t n, int32_t d, const float* C, int32_t k
   if (i8 || u8) ar.want(&cq, (size_t)k * d);
   if (f8 || conv == EMEANS_F8) ar.want(&cf, (size_t)k * d);
   if (conv) ar.want(&xb, (size_t)n * d * (conv == EMEANS_F8 ? 1 : 2));
+  if (use_scratch && ar.total() > kScratchBytes)
+    return fail(EMEANS_EINVAL,
+                "emeans_assign_static needs %zu bytes of scratch for these sizes (at most %zu: "
+                "centroid bias and search copy, plus the converted rows with a search "
+                "converter)", ar.total(), kScratchBytes);
+  if (n == 0) return EMEANS_OK;
+  if ((rc = check_device(X, "X")) || (rc = check_device(C, "C")) ||
+      (rc = check_device(labels, "labels")) || (dists && (rc = check_device(dists, "dists"))))
+    return rc;
+  hipStream_t st = static_cast<hipStream_t>(opts ? opts->stream : nullptr);
+  if (opts && opts->search_shift && (rc = check_device(opts->search_shift, "search_shift")))
+    return rc;
+  const float* sshift = conv ? opts->search_shift : nullptr;
+  const float sscale = conv == EMEANS_F8 ? (float)opts->search_scale : 1.0f;
+  const bool hf = f16 || conv == EMEANS_F16;
+  const bool sph = opts && opts->spherical;  // highest dot product, similarity out
   rc = EMEANS_OK;
-  HIP_TRY(ar.alloc(&base, st));
+  if (use_scratch) {
+    void* sp = nullptr;
+    if ((rc = scratch_address(&sp))) return rc;
+    ar.place(sp);  // every buffer is written before it is read: nothing to clear
+  } else {
+    HIP_TRY(ar.alloc(&base, st));
+  }
   HIP_TRY(launch_prep(C, k, d, bias, chat, hf, cq, u8, cf, sshift, sscale, sph, st));
   if (conv)
     HIP_TRY(launch_convert_rows(static_cast<const float*>(X), d, nullptr, (int)n, conv, sshift,
@@ -820,6 +874,16 @@ done:
       rc = fail(EMEANS_EHIP, "hipFreeAsync: %s", hipGetErrorString(e));
   }
   return rc;
+}
+
+int emeans_assign(const void* X, int64_t n, int32_t d, const float* C, int32_t k,
+                  int32_t* labels, float* dists, const emeans_opts* opts) {
+  return assign_impl(X, n, d, C, k, labels, dists, opts, false);
+}
+
+int emeans_assign_static(const void* X, int64_t n, int32_t d, const float* C, int32_t k,
+                         int32_t* labels, float* dists, const emeans_opts* opts) {
+  return assign_impl(X, n, d, C, k, labels, dists, opts, true);
 }
 
 int emeans_train(const void* X, int64_t n, int32_t d, int32_t k, double T, uint64_t seed,

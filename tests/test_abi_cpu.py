@@ -206,6 +206,32 @@ def test_assign_rejects_before_device_work(L):
     assert L.emeans_batch_rows(0, 1, 0, 0, 0, None, None) == -1
 
 
+def test_static_assign_rejects_sizes_beyond_its_array(L):
+    """emeans_assign_static checks its working-memory need against the fixed
+    array (EMEANS_STATIC_SCRATCH_BYTES) before touching any pointer: a bf16
+    search copy of k x d elements needs 2kd bytes."""
+    import re
+    with open(mm.HEADER) as f:
+        cap = int(eval(re.search(r"#define EMEANS_STATIC_SCRATCH_BYTES \((.*)\)", f.read())
+                       .group(1).replace("u", "")))
+    assert cap == 32 << 20
+    x = np.zeros(4, np.float32)
+    o = mm.Opts()
+    o.dtype = 1                      # bf16 rows: a bf16 copy of the centroids
+    d = 128
+    k = cap // (2 * d)               # the copy alone fills the array; the bias does not fit
+    p = x.ctypes.data
+    assert L.emeans_assign_static(p, 16, d, p, k, p, None, ctypes.byref(o)) == -1
+    assert "scratch" in L.emeans_last_error().decode()
+    # a size that fits passes the size check and reaches the pointer checks
+    assert L.emeans_assign_static(p, 16, d, p, 1000, p, None, ctypes.byref(o)) == -5
+    o.dtype = 0
+    o.search = 4                     # the fp16 cast of fp32 rows: 2nd bytes of converted rows
+    n = cap // (2 * d)
+    assert L.emeans_assign_static(p, n, d, p, 8, p, None, ctypes.byref(o)) == -1
+    assert L.emeans_assign_static(p, n // 2, d, p, 8, p, None, ctypes.byref(o)) == -5
+
+
 def test_host_pointer_is_not_device(L):
     """A host buffer is refused with ENOTDEVICE (no GPU needed to tell)."""
     x = np.zeros((16, 4), np.float32)
