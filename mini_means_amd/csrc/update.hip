@@ -612,6 +612,200 @@ __global__ __launch_bounds__(256) void group_wave_kernel(const unsigned char* __
   }
 }
 
+// UB bytes of a row (UB = 4, 8 or 16) as fp32 values: EPV = UB / element size.
+template <int DT, int UB>
+__device__ __forceinline__ void load_span_unit(const unsigned char* p, float* v) {
+  if constexpr (DT == 2 || DT == 3 || DT == 5) {  // 1-byte codes / values
+#pragma unroll
+    for (int h = 0; h < UB / 4; ++h) {
+      const uint32_t q = reinterpret_cast<const uint32_t*>(p)[h];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const uint32_t b = (q >> (8 * e)) & 0xFFu;
+        if constexpr (DT == 3)
+          v[4 * h + e] = e4m3_to_f32(b);
+        else if constexpr (DT == 5)
+          v[4 * h + e] = (float)b;
+        else
+          v[4 * h + e] = (float)(int8_t)b;
+      }
+    }
+  } else if constexpr (DT == 1 || DT == 4) {  // bf16 / fp16
+#pragma unroll
+    for (int h = 0; h < UB / 4; ++h) {
+      const uint32_t q = reinterpret_cast<const uint32_t*>(p)[h];
+      if constexpr (DT == 1) {
+        v[2 * h] = __uint_as_float(q << 16);
+        v[2 * h + 1] = __uint_as_float(q & 0xFFFF0000u);
+      } else {
+        v[2 * h] = f16_to_f32((uint16_t)(q & 0xFFFFu));
+        v[2 * h + 1] = f16_to_f32((uint16_t)(q >> 16));
+      }
+    }
+  } else {  // fp32
+    if constexpr (UB == 16) {
+      typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+      const u32x4 q = *reinterpret_cast<const u32x4*>(p);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) v[e] = __uint_as_float(q[e]);
+    } else if constexpr (UB == 8) {
+      typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+      const u32x2 q = *reinterpret_cast<const u32x2*>(p);
+      v[0] = __uint_as_float(q[0]);
+      v[1] = __uint_as_float(q[1]);
+    } else {
+      v[0] = *reinterpret_cast<const float*>(p);
+    }
+  }
+}
+
+// Grouping of narrow rows (a row is at most 64 units of UB bytes): one wave
+// per span of C consecutive clusters, whose rows occupy one contiguous run of
+// the bucketed order. Each lane owns one UB-byte column unit of every row.
+// The wave reads the span's C + 1 offsets in one load and the run's row ids in
+// 64-slot chunks (one load each), then issues the row loads U at a time,
+// summing in slot order and storing each cluster's sum when its last slot
+// has been added, so the dependent chain per wave is offsets -> row ids ->
+// rows however many clusters the span holds. A span holding a cluster of
+// more than R rows (rare for the mixtures these rows come from) takes the
+// per-cluster path: part 0 of each cluster here, parts >= 1 as the overflow
+// items that follow the spans (waves nA and up), with atomic adds for
+// clusters split over items. Without `add` the sums are stored (s_acc of a
+// cluster with rows need not be zero); with `add` (a later piece of one
+// update) every span takes the per-cluster path and adds them.
+template <int DT, int UB>
+__global__ __launch_bounds__(256) void group_span_kernel(const unsigned char* __restrict__ X,
+                                                         int d, const uint32_t* __restrict__ order,
+                                                         const int32_t* __restrict__ off,
+                                                         const int2* __restrict__ ovf,
+                                                         const int32_t* __restrict__ ovf_n,
+                                                         int k, int R, int C, int nA,
+                                                         float* __restrict__ s_acc, int add) {
+  constexpr int ES = DT == 0 ? 4 : (DT == 1 || DT == 4) ? 2 : 1;
+  constexpr int EPV = UB / ES;  // elements per lane per row
+  constexpr int U = 16;         // row loads in flight per lane
+  const int lane = threadIdx.x & 63;
+  const int w = blockIdx.x * 4 + (threadIdx.x >> 6);
+  const size_t rowbytes = (size_t)d * ES;
+  const int ncol = (int)(rowbytes / UB);
+  const bool active = lane < ncol;
+  // idle lanes read their row's first unit (a valid address; never stored),
+  // so the loads below need no lane mask and stay in flight together
+  const unsigned char* xcol = X + (active ? (size_t)lane * UB : 0);
+
+  float acc[EPV];
+#pragma unroll
+  for (int e = 0; e < EPV; ++e) acc[e] = 0.0f;
+
+  auto flush = [&](int j, bool single) {
+    if (active) {
+      float* dst = s_acc + (size_t)j * d + (size_t)lane * EPV;
+#pragma unroll
+      for (int e = 0; e < EPV; ++e) {
+        if (single && !add)
+          dst[e] = acc[e];
+        else if (single)
+          dst[e] += acc[e];
+        else
+          atomicAdd(&dst[e], acc[e]);
+        acc[e] = 0.0f;
+      }
+    }
+  };
+
+  // slots [beg, end) of the order, all of cluster j, into acc
+  auto sum_run = [&](int beg, int end) {
+    for (int t = beg; t < end; t += 64) {
+      const int m = min(64, end - t);
+      const int ord = lane < m ? (int)order[t + lane] : 0;
+      for (int u = 0; u < m; u += U) {
+        float v[U][EPV];
+#pragma unroll
+        for (int q = 0; q < U; ++q) {  // slots past m re-read the last row (not added)
+          const uint32_t row = (uint32_t)__builtin_amdgcn_readlane(ord, min(u + q, m - 1));
+          load_span_unit<DT, UB>(xcol + (size_t)row * rowbytes, v[q]);
+        }
+#pragma unroll
+        for (int q = 0; q < U; ++q)
+          if (u + q < m)
+#pragma unroll
+            for (int e = 0; e < EPV; ++e) acc[e] += v[q][e];
+      }
+    }
+  };
+
+  if (w >= nA) {  // overflow item: part p >= 1 of a cluster of more than R rows
+    const int it = w - nA;
+    if (it >= *ovf_n) return;
+    const int2 o = ovf[it];
+    const int b = off[o.x], e = off[o.x + 1];
+    const int beg = b + o.y * R;
+    if (beg >= e) return;
+    sum_run(beg, min(e, beg + R));
+    flush(o.x, false);
+    return;
+  }
+
+  const int j0 = w * C;
+  const int nc = min(C, k - j0);
+  const int my_off = lane <= nc ? off[j0 + lane] : 0;
+  const int nxt = __shfl_down(my_off, 1, 64);
+  const bool big = lane < nc && nxt - my_off > R;
+  // per cluster (part 0 of each, atomics where split) when the span holds a
+  // cluster of more than R rows or the sums are added to earlier pieces
+  if (add || __ballot(big) != 0ull) {
+    for (int jj = 0; jj < nc; ++jj) {
+      const int b = __builtin_amdgcn_readlane(my_off, jj);
+      const int e = __builtin_amdgcn_readlane(my_off, jj + 1);
+      if (b == e) continue;
+      sum_run(b, min(e, b + R));
+      flush(j0 + jj, e - b <= R);
+    }
+    return;
+  }
+
+  // the span's slots in order, each cluster stored when its last slot is in
+  const int S0 = __builtin_amdgcn_readlane(my_off, 0);
+  const int S1 = __builtin_amdgcn_readlane(my_off, nc);
+  int jc = 0;  // current cluster (relative to j0); its rows end at bnd
+  int bnd = __builtin_amdgcn_readlane(my_off, 1);
+  while (bnd == S0 && jc + 1 < nc) bnd = __builtin_amdgcn_readlane(my_off, ++jc + 1);
+  for (int t = S0; t < S1; t += 64) {
+    const int m = min(64, S1 - t);
+    const int ord = lane < m ? (int)order[t + lane] : 0;
+    for (int u = 0; u < m; u += U) {
+      float v[U][EPV];
+#pragma unroll
+      for (int q = 0; q < U; ++q) {  // slots past m re-read the last row (not added)
+        const uint32_t row = (uint32_t)__builtin_amdgcn_readlane(ord, min(u + q, m - 1));
+        load_span_unit<DT, UB>(xcol + (size_t)row * rowbytes, v[q]);
+      }
+#pragma unroll
+      for (int q = 0; q < U; ++q) {
+        if (u + q < m) {
+#pragma unroll
+          for (int e = 0; e < EPV; ++e) acc[e] += v[q][e];
+          const int slot = t + u + q;
+          if (slot + 1 == bnd) {  // last row of cluster jc: store, move to the next with rows
+            if (active) {
+              float* dst = s_acc + (size_t)(j0 + jc) * d + (size_t)lane * EPV;
+#pragma unroll
+              for (int e = 0; e < EPV; ++e) {
+                dst[e] = acc[e];
+                acc[e] = 0.0f;
+              }
+            }
+            do {
+              ++jc;
+              bnd = jc < nc ? __builtin_amdgcn_readlane(my_off, jc + 1) : 0x7FFFFFFF;
+            } while (bnd == slot + 1);
+          }
+        }
+      }
+    }
+  }
+}
+
 // One wave per cluster: EMA of the running count and sum, centroid S/N,
 // search-format refresh, last-pass accumulation; resets counts and s_acc.
 // search format kept beside C: 0 none, 1 bf16 (Chat), 2 int8 (Cq), 3 E4M3 (Cf),
@@ -1268,7 +1462,36 @@ template <int DT>
 static hipError_t launch_group_dt(const unsigned char* x, int d, bool vec, int ncol,
                                   const uint32_t* order, const int32_t* off, const int2* ovf,
                                   const int32_t* ovf_n, int k, int R, long long items,
-                                  float* s_acc, int add, hipStream_t st) {
+                                  float* s_acc, int add, int nb, hipStream_t st) {
+  // narrow rows: spans of consecutive clusters, one lane per 4-, 8- or 16-byte unit
+  constexpr int ES = DT == 0 ? 4 : (DT == 1 || DT == 4) ? 2 : 1;
+  const size_t rowbytes = (size_t)d * ES;
+  int ub = 0;
+  for (int cand = 4; cand <= 16; cand *= 2)  // at most 4 elements per lane per row
+    if (!ub && cand / ES <= 4 && rowbytes % cand == 0 && rowbytes / cand <= 64 &&
+        (uintptr_t)x % cand == 0)
+      ub = cand;
+  if (ub) {
+    // about 16 rows per span: C clusters of nb / k rows on average
+    const double avg = (double)nb / (double)k;
+    int C = (int)(16.0 / (avg > 1.0 ? avg : 1.0));
+    C = C < 1 ? 1 : (C > 32 ? 32 : C);
+    const int nA = (k + C - 1) / C;
+    const long long waves = (long long)nA + nb / R;
+    const dim3 grid((unsigned)((waves + 3) / 4)), block(256);
+    if (ub == 4)
+      group_span_kernel<DT, 4><<<grid, block, 0, st>>>(x, d, order, off, ovf, ovf_n, k, R, C, nA,
+                                                        s_acc, add);
+    if constexpr (ES >= 2)
+      if (ub == 8)
+        group_span_kernel<DT, 8><<<grid, block, 0, st>>>(x, d, order, off, ovf, ovf_n, k, R, C,
+                                                          nA, s_acc, add);
+    if constexpr (ES >= 4)
+      if (ub == 16)
+        group_span_kernel<DT, 16><<<grid, block, 0, st>>>(x, d, order, off, ovf, ovf_n, k, R, C,
+                                                           nA, s_acc, add);
+    return hipGetLastError();
+  }
   if (ncol <= 64) {
     const dim3 wgrid((unsigned)((items + 3) / 4)), wblock(256);
     if (vec)
@@ -1314,16 +1537,16 @@ hipError_t launch_group(int dt, const void* X, int d, const uint32_t* order,
   const int ncol = vec ? d / per : d;
   const int a = add ? 1 : 0;
   if (dt == 1)
-    return launch_group_dt<1>(x, d, vec, ncol, order, off, ovf, ovf_n, k, R, items, s_acc, a, st);
+    return launch_group_dt<1>(x, d, vec, ncol, order, off, ovf, ovf_n, k, R, items, s_acc, a, nb, st);
   if (dt == 2)
-    return launch_group_dt<2>(x, d, vec, ncol, order, off, ovf, ovf_n, k, R, items, s_acc, a, st);
+    return launch_group_dt<2>(x, d, vec, ncol, order, off, ovf, ovf_n, k, R, items, s_acc, a, nb, st);
   if (dt == 3)
-    return launch_group_dt<3>(x, d, vec, ncol, order, off, ovf, ovf_n, k, R, items, s_acc, a, st);
+    return launch_group_dt<3>(x, d, vec, ncol, order, off, ovf, ovf_n, k, R, items, s_acc, a, nb, st);
   if (dt == 4)
-    return launch_group_dt<4>(x, d, vec, ncol, order, off, ovf, ovf_n, k, R, items, s_acc, a, st);
+    return launch_group_dt<4>(x, d, vec, ncol, order, off, ovf, ovf_n, k, R, items, s_acc, a, nb, st);
   if (dt == 5)
-    return launch_group_dt<5>(x, d, vec, ncol, order, off, ovf, ovf_n, k, R, items, s_acc, a, st);
-  return launch_group_dt<0>(x, d, vec, ncol, order, off, ovf, ovf_n, k, R, items, s_acc, a, st);
+    return launch_group_dt<5>(x, d, vec, ncol, order, off, ovf, ovf_n, k, R, items, s_acc, a, nb, st);
+  return launch_group_dt<0>(x, d, vec, ncol, order, off, ovf, ovf_n, k, R, items, s_acc, a, nb, st);
 }
 
 hipError_t launch_ema(int k, int d, float a, float b, int32_t* counts, float* s_acc, float* N,

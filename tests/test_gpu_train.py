@@ -45,6 +45,9 @@ LOCKSTEP = [
     ("sift-small", "sift", 20_000, 128, 1024, 2.0, {}),
     ("large-small", "large", 40_000, 128, 1024, 2.0, {}),
     ("ragged", "tiny", 5_003, 37, 77, 1.5, dict(batch_size=700)),
+    # narrow rows with Zipf-heavy clusters: spans holding a cluster of more
+    # than 256 rows in a batch take the per-cluster grouping path plus overflow items
+    ("zipf-narrow", "embedding", 20_000, 64, 64, 2.0, dict(batch_size=8192)),
     ("no-revival", "deep", 8_000, 96, 300, 2.0, dict(unused_threshold=0.0)),
     ("alpha1-lloyd", "tiny", 4_000, 16, 32, 1.0, dict(batch_size=4000, alpha0=1.0)),
     # fp32 data searched in bf16 (README "Data precision", the pages' GPU default)
