@@ -44,8 +44,8 @@ def kernel_source_sha() -> str:
     """Hash of the assign kernels' sources: counter readings are only reused
     while it is unchanged."""
     h = hashlib.sha256()
-    for f in ("assign.hip", "assign_bf16.hip", "assign_i8r.hip", "common.hpp",
-              "kernels.hpp"):  # assign kernels
+    for f in ("assign.hip", "assign_bf16.hip", "assign_i8r.hip",
+              "common.hpp"):  # the sources that define the assign kernels
         with open(os.path.join(HERE, "mini_means_amd", "csrc", f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()

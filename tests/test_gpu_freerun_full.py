@@ -30,7 +30,7 @@ from mini_means_amd import datagen
 pytestmark = pytest.mark.gpu
 
 GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
-WORKLOADS = ["tiny"]
+WORKLOADS = ["tiny", "deep", "sift"]
 MSE_TOL = 1e-3
 
 
