@@ -8,7 +8,7 @@
  *     N_j <- (1 - alpha) N_j + alpha n_j,   S_j <- (1 - alpha) S_j + alpha s_j,
  *     c_j  = S_j / N_j,
  * where n_j, s_j are the count and sum of the batch's vectors assigned to j.
- * The batch size and the starting step alpha0 come from the README's scaling
+ * B and alpha0 follow the README's scaling
  * laws ("Scaling laws", equations (1)-(3)); alpha decays along a cosine to
  * alpha0/10; clusters whose running count falls under a fraction of the mean
  * are revived every 5 batches by splitting a cluster drawn in proportion to
@@ -129,10 +129,10 @@ typedef struct emeans_opts {
                                  and centroids use the fp32 rows. 0: fp32 X is searched
                                  in fp32 (exact). Ignored for X of other types. */
   int32_t spherical;          /* 1: spherical e-means (README "Spherical e-means"):
-                                 every centroid is its running average rescaled to
-                                 norm 1 before use (a zero centroid stays zero), each
-                                 vector goes to the centroid with the highest dot
-                                 product, the closing step rescales each cluster's
+                                 each centroid is kept at norm 1 (S / N rescaled after
+                                 every change; an all-zero centroid is left as is),
+                                 a vector is assigned where its dot product is
+                                 largest, the closing step rescales each cluster's
                                  mean to norm 1, and stats->obj is the mean of
                                  2 - 2 x similarity. Vectors are not normalised (nor
                                  checked): pass unit-norm rows for cosine semantics.
@@ -168,7 +168,7 @@ typedef struct emeans_opts {
                                  mode; the closing mean is not applied to them */
   int32_t search;             /* fp32 X only: convert the rows on the fly, batch by
                                  batch, for the nearest-centroid search (README "Data
-                                 precision", keep FP32 and convert on the fly; the
+                                 precision", fp32 data converted batch by batch; the
                                  rows and the centroids become
                                  fmt((v - search_shift) * search_scale) in fp32):
                                  EMEANS_BF16 or EMEANS_F16 (the casts; a shift is
@@ -227,9 +227,9 @@ int emeans_recipe(int64_t n, int32_t d, int32_t k, double T, const emeans_opts* 
  * `seed`.
  *   X          device, n x d, opts->dtype
  *   centroids  device, k x d fp32, output (also the working centroids)
- *   labels     device, n int32, output or NULL: each vector's label from the
- *              last pass (README "Quick start"); -1 for vectors that pass
- *              did not visit
+ *   labels     device, n int32, output or NULL: the label the final pass gave
+ *              each row (README "Quick start"); -1 for rows that pass did
+ *              not visit
  *   stats      host, output or NULL
  * Errors: EINVAL (sizes as for emeans_recipe, n >= 2^31, NULL X/centroids),
  * EDTYPE, ENOTDEVICE, ENOMEM, EHIP. Synchronises opts->stream. */
@@ -364,8 +364,8 @@ int emeans_batch_rows(int64_t n, uint64_t seed, int32_t pass, int64_t start, int
                       int32_t* rows_out, void* stream);
 
 /* ---------------------------------------------------------------------------
- * int8 codes (README "Data precision", INT8: a shift per dimension and one
- * power-of-two scale, calibrated from a sample, map fp32 data to int8 codes
+ * int8 codes (README "Data precision", INT8: a per-dimension offset and a
+ * single power-of-two factor, calibrated from a sample, map fp32 data to codes
  * that training and assignment take with opts->dtype = EMEANS_I8).
  * ------------------------------------------------------------------------- */
 

@@ -288,7 +288,7 @@ def assign(X, C, *, with_dists: bool = True, bf16_search: bool = False, spherica
     """Nearest centroid (int32 labels) and squared distance (float32) of each row.
     bf16_search: search fp32 rows in bf16 (rows and centroids rounded).
     search / search_shift / search_scale: the general converter (as train).
-    spherical: the centroid with the highest dot product, and that similarity.
+    spherical: the centroid of largest dot product, and that similarity.
     no_alloc: call emeans_assign_static (the library allocates nothing; its
     working memory is one fixed device array per GPU, shared by every call).
     out: (labels, dists or None) tensors to write into instead of new ones."""
@@ -517,7 +517,7 @@ class Stream:
         batches: device tensors (rows x d, the model's dtype, row-major) that
         together go over the rows in one fixed order. assignments: None, or
         one label per row in that same order (int32 or int64, host or device;
-        -1 for a row the last pass skipped): the labels saved during the last
+        -1 for a row the last pass skipped): the labels kept from the final
         pass, so that no search is needed. Without them every row is assigned
         once more against the final EMA centroids. Blocks larger than the
         batch size are sent in pieces. finalize() then gives each centroid the

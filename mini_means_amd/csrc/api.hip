@@ -266,7 +266,7 @@ bool pow2_scale(double s) {
 }
 
 // The search format of fp32 data converted on the fly (README "Data
-// precision", keep FP32 and convert on the fly): opts->search, or bf16 for
+// precision", fp32 rows converted batch by batch): opts->search, or bf16 for
 // bf16_search; 0 for other data types (bf16_search is ignored there).
 int32_t search_format(const emeans_opts* opts) {
   if (!opts || opts->dtype != EMEANS_F32) return 0;

@@ -863,8 +863,8 @@ __global__ __launch_bounds__(256) void ema_kernel(int k, int d, float a, float b
   }
   if constexpr (SF == 2 || SF == 5) nq = wave_sum(nq);
   if (sph) {
-    // spherical e-means: the running average rescaled to norm 1 (a centroid
-    // without a count keeps its unit-norm value); the score is x.c, bias 0
+    // spherical e-means: S / N rescaled to norm 1 (a centroid without a
+    // count keeps its unit-norm value); the score is x.c, bias 0
     if (Nn > 0.0f) wave_normalize(C + base, d, lane);
     if constexpr (SF == 1 || SF == 4)
       for (int e = lane; e < d; e += 64) Chat[base + e] = to_half_rne(C[base + e], SF == 4);

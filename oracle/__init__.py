@@ -20,11 +20,12 @@ Do."):
                     N_j <- (1-a) N_j + a n_j,  S_j <- (1-a) S_j + a s_j,
                     c_j = S_j / N_j.
 * cosine schedule   blog, second item; README "How the centroid updates
-                    work": the step decays along a cosine to a tenth of its
-                    starting value.
-* revival           blog, third item (every five batches, clusters below 10%
-                    of the mean count are refilled by splitting a big
-                    cluster); README "Settings" (unused_threshold).
+                    work": a cosine takes the step from alpha0 down to
+                    alpha0 / 10.
+* revival           blog, third item (checked every five batches; a cluster
+                    whose running count falls under a tenth of the mean is
+                    refilled by splitting a big one); README "Settings"
+                    (unused_threshold).
 * batch order       README "Data too big for memory": fresh random order every
                     pass, batches of exactly B except the last of each pass,
                     every vector once per pass.
@@ -32,20 +33,20 @@ Do."):
                     centroid becomes the exact mean of the points the last pass
                     assigned to it; README "Quick start": labels come from the
                     last pass.
-* spherical         README "Spherical e-means": centroids rescaled to norm 1
-                    before every use (zero stays zero), assignment by the
-                    highest dot product (``emeans_ref.c``, fp64 brute force),
+* spherical         README "Spherical e-means": centroids kept at norm 1
+                    (an all-zero one left as is), assignment by the
+                    largest dot product (``emeans_ref.c``, fp64 brute force),
                     closing mean rescaled to norm 1, error = sum of
                     2 - 2 x similarity.
 * precision         README "Data precision": centroids and running sums are
-                    stored in fp32; only the nearest-centroid search uses the
-                    smaller format: for bf16 data, and for fp32 data when
+                    stored in fp32; the smaller format serves the search
+                    alone: for bf16 data, and for fp32 data when
                     bf16_search asks for the pages' GPU default (rows and
                     centroids rounded to bf16 for the search, fp32 rows
-                    grouped). INT8 and FP8 (E4M3) codes: a shift per
-                    dimension and one power-of-two scale calibrated on a
-                    sample, values beyond its range clamped to the edge
-                    (127 / 448); training runs on the codes and the search
+                    grouped). INT8 and FP8 (E4M3) codes: a per-dimension
+                    offset and a single power-of-two factor calibrated on a
+                    sample, values beyond its range limited to the extreme
+                    code (127 / 448); training runs on the codes and the search
                     compares them with the centroids rounded to codes. UINT8
                     data is searched exactly against the centroids rounded to
                     uint8 values (clamped to [0, 255]).
@@ -57,8 +58,9 @@ Do."):
                     (-1 rows left out) or, without them, a fresh assignment
                     against the final EMA centroids.
 * slow EMA          blog, closing remark of the section on what e-means
-                    changes: for unseen data, finish with a second, slower
-                    EMA, a second set of centroids from the same run. The
+                    changes: a second running average at a lower rate gives
+                    centroids meant for data outside the training set, from
+                    the same run. The
                     pages give no decay; read as a second pair of running
                     statistics over the last pass at the rate alpha_t / kappa.
 
@@ -292,8 +294,8 @@ def u8_round(C: np.ndarray) -> np.ndarray:
 
 
 def int8_calibrate(sample: np.ndarray):
-    """README "Data precision", INT8: a shift per dimension and one power-of-two
-    scale from a sample. Readings: the shift is the sample's midrange per
+    """README "Data precision", INT8: a per-dimension offset and a single
+    power-of-two factor from a sample. Readings: the shift is the sample's midrange per
     dimension (fp64, stored fp32); the scale is the largest power of two that
     maps every sample value within [-127, 127] (1 for a constant sample)."""
     return _calibrate(sample, 127.0)
@@ -411,15 +413,15 @@ def f16_round(C: np.ndarray) -> np.ndarray:
 
 @dataclass
 class Converter:
-    """README "Data precision", "keep FP32, convert on the fly": fp32 rows and
-    centroids are converted, batch by batch, to a smaller format for the
-    nearest-centroid search only, v -> fmt((v - shift) * scale) in fp32 (the
-    product by a power of two is exact). fmt 'bf16' or 'f16' is the cast
-    (scale 1; a shift is the optional centering, "subtracts your data's mean
-    before rounding to 16 bits"); 'f8' is the calibrated FP8 converter (shift
-    and scale from fp8_calibrate). Sums and centroids stay fp32 in data units,
-    and distances in the converted units are divided by scale^2 ("the
-    centroids and distances come back in your original FP32 units")."""
+    """README "Data precision", fp32 data converted batch by batch: rows and
+    centroids are converted to a smaller format for the nearest-centroid
+    search only, v -> fmt((v - shift) * scale) in fp32 (the product by a
+    power of two is exact). fmt 'bf16' or 'f16' is the cast (scale 1; a shift
+    is the optional centering, the data's mean taken out before the 16-bit
+    rounding); 'f8' is the calibrated FP8 converter (shift and scale from
+    fp8_calibrate). Sums and centroids stay fp32 in data units, and distances
+    in the converted units are divided by scale^2, so that they are reported
+    in the data's own units, as the README states for converters."""
     fmt: str
     shift: Optional[np.ndarray] = None
     scale: float = 1.0
@@ -508,7 +510,7 @@ def assign(X: np.ndarray, C: np.ndarray, rows: Optional[np.ndarray] = None, nthr
 
 def assign_ip(X: np.ndarray, C: np.ndarray, rows: Optional[np.ndarray] = None,
               nthreads: int = 0):
-    """README "Spherical e-means": centroid with the highest dot product (lowest
+    """README "Spherical e-means": the centroid of largest dot product (lowest
     index on ties): labels, best and runner-up dot product (fp64)."""
     X = np.ascontiguousarray(X)
     C = np.ascontiguousarray(C, dtype=np.float32)
@@ -655,11 +657,11 @@ def train(X: np.ndarray, k: int, T: float, seed: int = 1234, *, batch_law: int =
     with the calibrated shift and scale); the reported error is in data
     units.
 
-    spherical (README "Spherical e-means"): every centroid is its running
-    average rescaled to norm 1 before use (a zero centroid stays zero), each
-    vector goes to the centroid with the highest dot product, the closing step
-    rescales each cluster's exact mean to norm 1, and the reported error is
-    the sum of 2 - 2 x similarity. In label checks a dot product s enters as
+    spherical (README "Spherical e-means"): S / N of each centroid is
+    rescaled to norm 1 after every change (an all-zero centroid is left as
+    is), a vector is assigned where its dot product is largest, the closing
+    step rescales each cluster's exact mean to norm 1, and the error summed
+    over the rows is 2 - 2 x similarity. In label checks a dot product s enters as
     -2 s (the squared distance up to a per-row constant for unit centroids).
 
     slow_ema = kappa >= 1 (0: off), the second, slower EMA of the blog's

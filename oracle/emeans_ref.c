@@ -227,7 +227,7 @@ void ref_dist_to(const void* X, int dtype, int64_t nrows, const int64_t* rows, i
 }
 
 /* Spherical e-means (README "Spherical e-means"): each row goes to the      */
-/* centroid with the highest dot product, the lowest index on ties. Returns  */
+/* centroid of largest dot product, the lowest index on ties. Returns       */
 /* the label, the best and the runner-up dot product (fp64, summed over t in */
 /* order).                                                                    */
 void ref_assign_ip(const void* X, int dtype, int64_t nrows, const int64_t* rows, int32_t d,

@@ -102,7 +102,7 @@ def _unit_rows(A):
 
 @pytest.mark.parametrize("gen,n,d,k,bf16", CASES_SPHERICAL)
 def test_assign_spherical(mm, gen, n, d, k, bf16):
-    """README "Spherical e-means": the centroid with the highest dot product and
+    """README "Spherical e-means": the centroid of largest dot product and
     that similarity (a zero centroid included, which scores 0)."""
     import torch
     X = datagen.make(gen, n, d, seed=19)

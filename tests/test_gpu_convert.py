@@ -1,5 +1,5 @@
-"""fp32 data converted on the fly for the search (README "Data precision":
-keep FP32, convert on the fly): the bf16 and fp16 casts, with and without
+"""fp32 data converted on the fly for the search (README "Data precision",
+the column for fp32 rows converted batch by batch): the bf16 and fp16 casts, with and without
 centering, and the calibrated FP8 converter, against the oracle's Converter.
 Labels are checked within the band of the search format, distances in data
 units (the converted-unit distance divided by scale^2)."""

@@ -293,8 +293,8 @@ def test_lloyd_mse_never_increases():
 
 
 def test_convex_hull_invariant():
-    """Without revival, every EMA centroid stays in the convex hull of the
-    points ever assigned to it (blog, on the rejected gradient update)."""
+    """Without revival, every EMA centroid stays inside the hull spanned by
+    all rows it was ever given (blog, on the rejected gradient update)."""
     rng = np.random.default_rng(6)
     X = rng.standard_normal((400, 3)).astype(np.float32)
     k = 6
@@ -347,8 +347,9 @@ def _train_recording(X, k, T, seed, B, record):
 
 
 def test_finalisation_is_exact_mean_of_last_pass():
-    """README: at the end of the last pass each centroid is the exact mean of
-    the points that pass assigned to it; labels come from that pass."""
+    """README "How the centroid updates work": after the final pass every
+    centroid equals the plain average of the rows that pass gave it; the
+    labels returned are that pass's."""
     X = datagen.tiny(n=5000, d=16, seed=9)
     res = oracle.train(X, 64, 3.0, seed=5)
     lab = res.labels
@@ -518,9 +519,9 @@ def test_normalize_keeps_zero_rows():
 def test_spherical_one_step_is_spherical_kmeans():
     """B = n, alpha = 1, no revival: one step is one spherical k-means step
     (assign by the highest cosine to the unit-norm starting centroids, then
-    each centroid is its cluster's mean rescaled to norm 1); the reported
-    error is the mean of 2 - 2 x cosine, i.e. the mean squared distance on
-    the sphere."""
+    each centroid is its cluster's mean rescaled to norm 1); the error
+    reported per row is 2 - 2 x cosine on average, i.e. the mean squared
+    distance on the sphere."""
     X = _unit(datagen.tiny(n=3000, d=16, seed=4))
     k = 40
     res = oracle.train(X, k, 1.0, seed=9, batch_size=3000, alpha0=1.0, unused_threshold=0,
@@ -553,7 +554,7 @@ def test_spherical_closing_step_is_normalised_mean():
         if m.any():
             mu = X[m].astype(np.float64).mean(axis=0)
             np.testing.assert_allclose(res.centroids[j], mu / np.linalg.norm(mu), rtol=0, atol=2e-6)
-    # the EMA centroids are unit-norm too (rescaled before every use)
+    # the EMA centroids are unit-norm too (rescaled after every change)
     en = np.linalg.norm(res.ema_centroids.astype(np.float64), axis=1)
     np.testing.assert_allclose(en[en > 0], 1.0, atol=1e-6)
 
@@ -617,7 +618,7 @@ def test_f16_rounding_and_decode():
     r = oracle.f16_round(np.array([65504.0, 65519.99, 65520.0, -70000.0, 1.0 + 2.0 ** -11,
                                    1.0 + 3 * 2.0 ** -11, 2.0 ** -24, 2.0 ** -25, 3 * 2.0 ** -25],
                                   np.float32))
-    # the pages: values of 65,520 and above become infinity, silently
+    # the pages: from 65,520 up, fp16 gives infinity without any error
     assert r[0] == 65504.0 and r[1] == 65504.0 and np.isinf(r[2]) and r[3] == -np.inf
     # ties to even: 1 + 2^-11 -> 1; 1 + 3 2^-11 -> 1 + 2^-9; 2^-25 -> 0; 3 2^-25 -> 2^-23
     assert r[4] == 1.0 and r[5] == 1.0 + 2.0 ** -9
@@ -922,8 +923,8 @@ def test_u8_training_closing_mean_and_search():
     assert oracle.assign(x, oracle.search_centroids(c2, x))[0].tolist() == [0]
 
 
-# On-the-fly converters of fp32 data (README "Data precision": keep FP32,
-# convert on the fly; centering)
+# On-the-fly converters of fp32 data (README "Data precision", fp32 rows
+# converted batch by batch; centering)
 
 def test_converter_centering_is_the_search_of_the_offset_free_data():
     """Centering subtracts the shift before rounding: data 1000 + y with y
