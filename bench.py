@@ -210,29 +210,76 @@ def first_crossing(mm, X, Xh, k, T, rc, target, seed, torch, tkw=None, decode=No
     return dict(T=T, per_pass=rows, first=hit)
 
 
-def cpu_baseline(Xhost, C, k, d, budget_s: float, unit: str = "TFLOP/s") -> dict:
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def cpu_baseline(Xhost, C, k, d, budget_s: float, unit: str = "TFLOP/s", workload: str = "",
+                 T: float = 5.0) -> dict:
     """The CPU oracle's assignment (fp64 brute force, OpenMP over rows) on a
     bounded sample of the workload's rows, in the metric's unit (codes and
-    uint8 data: against the centroids rounded to the search format)."""
+    uint8 data: against the centroids rounded to the search format), on all
+    the machine's cores and on one core. The oracle's whole e-means run (T passes)
+    and Lloyd-25 run are extrapolated from the multi-core rate (their cost is
+    the assignment of every row once per pass or iteration, plus the final
+    MSE evaluations) and labelled as such; the times the stored targets took
+    when they were made are given beside them."""
     import numpy as np
     import oracle
     C = oracle.search_centroids(C, Xhost)
     rng = np.random.default_rng(0)
     cores = int(os.environ.get("OMP_NUM_THREADS", "0")) or len(os.sched_getaffinity(0))
+    n = len(Xhost)
     npr = 2048
-    probe = Xhost[rng.choice(len(Xhost), npr, replace=False)]
+    probe = Xhost[rng.choice(n, npr, replace=False)]
     t0 = time.perf_counter()
     oracle.assign(probe, C, nthreads=cores)
     per_row = (time.perf_counter() - t0) / npr
-    rows = int(max(256, min(len(Xhost), budget_s / max(per_row, 1e-9))))
-    sample = Xhost[rng.choice(len(Xhost), rows, replace=False)]
+    rows = int(max(256, min(n, budget_s / max(per_row, 1e-9))))
+    sample = Xhost[rng.choice(n, rows, replace=False)]
     t0 = time.perf_counter()
     oracle.assign(sample, C, nthreads=cores)
     dt = time.perf_counter() - t0
     tflops = 2.0 * rows * k * d / dt / 1e12
-    return dict(value=round(tflops, 6), unit=unit, cores=cores, kind="oracle",
-                sample=f"{rows} random training rows x all {k} centroids (fp64 brute force, "
-                       f"{dt:.1f}s)")
+    # one core, on a sample about a tenth of a second long at that rate
+    r1 = int(max(64, min(n, 0.1 * cores / max(dt / rows, 1e-12) / cores)))
+    one = sample[:min(r1, rows)]
+    t0 = time.perf_counter()
+    oracle.assign(one, C, nthreads=1)
+    dt1 = time.perf_counter() - t0
+    sec_per_row = dt / rows
+    out = dict(value=round(tflops, 6), unit=unit, cores=cores, kind="oracle",
+               sample=f"{rows} random training rows x all {k} centroids (fp64 brute force, "
+                      f"{dt:.1f}s)",
+               cpu_model=cpu_model(),
+               single_thread={"value": round(2.0 * len(one) * k * d / dt1 / 1e12, 6),
+                              "unit": unit, "rows": len(one), "seconds": round(dt1, 3)},
+               extrapolated={
+                   "emeans_seconds": round((T + 1.0) * n * sec_per_row, 1),
+                   "lloyd25_seconds": round(26.0 * n * sec_per_row, 1),
+                   "basis": f"{n} rows assigned once per pass ({T:g} passes) or per Lloyd "
+                            "iteration (25), plus one final MSE pass, at the sampled "
+                            "multi-core rate; grouping and the held-out MSE are left out"})
+    measured = {}
+    for kind, fname, key in (("emeans", f"freerun_{workload}.json", "oracle_train_seconds"),
+                             ("lloyd25", f"lloyd25_{workload}.json", "cpu_seconds")):
+        path = os.path.join(HERE, "tests", "golden", fname)
+        if workload and os.path.exists(path):
+            with open(path) as f:
+                g = json.load(f)
+            measured[kind] = {"seconds": round(g[key], 1),
+                              "threads": g.get("threads"),
+                              "where": "when the stored target was written (another host)"}
+    if measured:
+        out["target_runs"] = measured
+    return out
 
 
 def main() -> int:
@@ -485,7 +532,8 @@ def main() -> int:
 
     if not args.no_cpu and Xhost is not None:
         C = out.centroids.cpu().numpy()
-        line["cpu_baseline"] = cpu_baseline(Xhost, C, k, d, args.cpu_seconds, unit)
+        line["cpu_baseline"] = cpu_baseline(Xhost, C, k, d, args.cpu_seconds, unit,
+                                            args.workload, T)
         log(f"cpu baseline {line['cpu_baseline']}")
 
     print(json.dumps(line), flush=True)

@@ -39,6 +39,7 @@ def main(name: str, threads: int = 0, iters: int = 25, seed: int = 1234) -> None
                init="first k entries of the init permutation (same as e-means)",
                train_mse_history=hist, train_mse=train_mse, heldout_rows=W["heldout"],
                heldout_mse=held_mse, cpu_seconds=time.time() - t0,
+               threads=threads or os.cpu_count(),
                source="oracle.lloyd (CPU, fp64), written by tests/golden/make_lloyd_targets.py")
     path = os.path.join(HERE, f"lloyd25_{name}.json")
     with open(path, "w") as f:
