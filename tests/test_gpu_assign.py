@@ -129,7 +129,12 @@ CASES_I8 = [(2000, 768, 300), (1000, 64, 129), (777, 48, 50), (500, 37, 20), (30
             # every k-step count, several workgroups with a ragged last one,
             # k past one 256-centroid panel and not a multiple of 32
             (1500, 32, 513), (2049, 96, 300), (2500, 160, 700), (1100, 192, 33),
-            (2100, 224, 290), (1700, 256, 600)]
+            (2100, 224, 290), (1700, 256, 600),
+            # d = 512 and 768 take the wide resident kernel (64 points per
+            # wave, 64-centroid panels): one panel, a ragged panel and point
+            # tile, k = 1, several workgroups with a ragged last one
+            (256, 512, 64), (777, 512, 65), (4097, 768, 1025), (300, 768, 1),
+            (1300, 768, 129)]
 
 
 def _int8_centroids(X, k, seed):
@@ -185,7 +190,8 @@ def test_assign_int8_rules(mm):
 CASES_U8 = [(2000, 768, 300), (1000, 64, 129), (777, 48, 50), (500, 37, 20), (300, 256, 1),
             (600, 1040, 257), (3000, 128, 1000),
             (1500, 32, 513), (2049, 96, 300), (2500, 160, 700), (1100, 192, 33),
-            (2100, 224, 290), (1700, 256, 600)]
+            (2100, 224, 290), (1700, 256, 600),
+            (777, 512, 65), (4097, 768, 1025), (300, 768, 1)]
 
 
 def _u8_centroids(X, k, seed):
