@@ -9,7 +9,15 @@ Times. Two Would Do.", the MSE of the section on Lloyd's algorithm, taken after
 the closing mean of the faiss README's "How the centroid updates work"). The
 two runs need not pass through the same labels: a near-tie resolved
 differently in fp32 and fp64 sends them onto different trajectories, and the
-test asks that both still land on the same loss to 1e-3.
+test asks that both still land on the same loss.
+
+On the embedding-like set (k = 4096 heavily overlapping unit-norm clusters)
+the final loss itself is not reproducible to 1e-3: five runs with the same
+seed that differ only in the fp32 summation order of the per-cluster sums
+end 1.5e-3 (held-out) and 2.0e-3 (train) apart in relative standard
+deviation (seeds 1234-1238: 1.8e-3 and 2.1e-3). That workload is held to
+5e-3, about three of those standard deviations; the deep- and SIFT-like
+sets (same-seed spreads below 1e-4) keep 1e-3.
 
 MSE of the GPU's centroids: on the held-out rows by the oracle (fp64 brute
 force); on the training rows from the GPU's own assignment of every row (its
@@ -30,8 +38,8 @@ from mini_means_amd import datagen
 pytestmark = pytest.mark.gpu
 
 GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
-WORKLOADS = ["tiny", "deep", "sift"]
-MSE_TOL = 1e-3
+WORKLOADS = ["tiny", "deep", "sift", "embedding"]
+MSE_TOL = {"tiny": 1e-3, "deep": 1e-3, "sift": 1e-3, "embedding": 5e-3}
 
 
 def log(msg):
@@ -84,6 +92,7 @@ def test_freerun_final_mse_matches_oracle(mm, name):
         f"held-out gpu {h_gpu:.6f} oracle {g['heldout_mse']:.6f} (rel {rel_h:.2e})")
     # the GPU's own MSE of its centroids agrees with the oracle's on a sample
     assert abs(float(d_rows.double().mean().item()) - m_smp) <= 1e-5 * m_smp
-    assert rel_m <= MSE_TOL, (m_gpu, g["train_mse"])
-    assert rel_h <= MSE_TOL, (h_gpu, g["heldout_mse"])
-    np.testing.assert_allclose(st["obj"][-1], g["obj_per_pass"][-1], rtol=MSE_TOL)
+    tol = MSE_TOL[name]
+    assert rel_m <= tol, (m_gpu, g["train_mse"])
+    assert rel_h <= tol, (h_gpu, g["heldout_mse"])
+    np.testing.assert_allclose(st["obj"][-1], g["obj_per_pass"][-1], rtol=tol)
