@@ -44,7 +44,7 @@ def kernel_source_sha() -> str:
     """Hash of the assign kernels' sources: counter readings are only reused
     while it is unchanged."""
     h = hashlib.sha256()
-    for f in ("assign.hip", "assign_bf16.hip", "assign_i8r.hip", "assign_i8w.hip",
+    for f in ("assign.hip", "assign_bf16.hip", "assign_i8r.hip", "assign_wide.hip",
               "common.hpp"):  # the sources that define the assign kernels
         with open(os.path.join(HERE, "mini_means_amd", "csrc", f), "rb") as fh:
             h.update(fh.read())
@@ -60,6 +60,8 @@ def assign_kernel_name(dtype: str, d: int) -> str:
         return "assign_i8r_kernel (points resident in registers, 32x32x32 int8 MFMA)"
     if dtype in ("i8", "u8") and d in (512, 768):
         return "assign_i8w_kernel (64 points per wave resident, 16x16x64 int8 MFMA)"
+    if dtype == "f8" and d in (512, 768):
+        return "assign_f8w_kernel (64 points per wave resident, 16x16x128 FP8 MFMA)"
     if d % {"bf16": 8, "f16": 8, "i8": 16, "u8": 16, "f8": 16}.get(dtype, 4) == 0:
         return "assign_ring_kernel (direct-to-LDS stage ring, 16x16 MFMA)"
     return "assign_kernel (register-staged stages, 16x16 MFMA)"

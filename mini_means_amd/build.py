@@ -15,7 +15,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 OUT_DIR = os.path.join(PKG, "_lib")
 LIB = os.path.join(OUT_DIR, "libemeans.so")
-SOURCES = ["assign.hip", "assign_bf16.hip", "assign_i8r.hip", "assign_i8w.hip", "update.hip",
+SOURCES = ["assign.hip", "assign_bf16.hip", "assign_i8r.hip", "assign_wide.hip", "update.hip",
            "codes.hip", "api.hip"]
 
 HIPCC = os.environ.get("HIPCC", shutil.which("hipcc") or "/opt/rocm/bin/hipcc")

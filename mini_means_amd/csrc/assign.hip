@@ -827,6 +827,8 @@ hipError_t launch_assign(int dt, const void* X, int d, const uint32_t* rows, int
   if ((dt == 1 || dt == 4) && assign_bf16_resident_ok(d, X, Cs))
     return launch_assign_bf16_resident(X, d, rows, nrows, Cs, bias, k, labels, dists, counts, obj,
                                        sim, dt == 4, st);
+  if (dt == 3 && !sim && assign_f8_wide_ok(d, X, Cs))
+    return launch_assign_f8_wide(X, d, rows, nrows, Cs, bias, k, labels, dists, counts, obj, st);
   if ((dt == 2 || dt == 5) && !sim && assign_i8_wide_ok(d, X, Cs))
     return launch_assign_i8_wide(X, d, rows, nrows, Cs, bias, k, labels, dists, counts, obj,
                                  dt == 5, st);

@@ -51,6 +51,14 @@ hipError_t launch_assign_i8_wide(const void* X, int d, const uint32_t* rows, int
                                  float* dists, int32_t* counts, double* obj, bool u8,
                                  hipStream_t st);
 
+// FP8 E4M3 codes of dimension 512 or 768: the same structure with 16x16x128
+// FP8 MFMA tiles and fp32 scores (same contract as launch_assign with dt 3,
+// which has no similarity mode; bias holds -|c|^2 / 2).
+bool assign_f8_wide_ok(int d, const void* X, const void* Cf);
+hipError_t launch_assign_f8_wide(const void* X, int d, const uint32_t* rows, int nrows,
+                                 const void* Cf, const float* bias, int k, int32_t* labels,
+                                 float* dists, int32_t* counts, double* obj, hipStream_t st);
+
 // rows[r] = pi(start + r) for the keyed permutation pk.
 hipError_t launch_sample_rows(const PermKey& pk, uint64_t start, int count, uint32_t* rows,
                               hipStream_t st);

@@ -255,7 +255,10 @@ def test_assign_uint8_misaligned_and_rules(mm):
 
 
 CASES_F8 = [(2000, 768, 300), (1000, 64, 129), (777, 48, 50), (500, 37, 20), (300, 256, 1),
-            (600, 1040, 257), (3000, 128, 1000)]
+            (600, 1040, 257), (3000, 128, 1000),
+            # the register-resident kernel of d = 512 and 768: ragged point
+            # tiles (256 per workgroup) and ragged 64-row centroid panels
+            (4097, 512, 1025), (300, 512, 1), (1300, 768, 129), (257, 768, 64)]
 
 
 @pytest.mark.parametrize("n,d,k", CASES_F8)
