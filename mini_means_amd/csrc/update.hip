@@ -905,6 +905,7 @@ __global__ __launch_bounds__(256) void slow_final_kernel(int k, int d, const flo
 // sum, cluster j takes the other half, and both sums are perturbed by
 // -/+ 2^-10 * sign per coordinate.
 //
+// Up to k = 16384, revive_spec_kernel (below) draws the donors; beyond it
 // revive_kernel (one workgroup):
 //  A. all threads: threshold, dead list, uniform draws, live counts (in LDS
 //     when k <= kRvLdsN), fp64 live sum of each of 64 chunks of CS = 64 V
@@ -919,6 +920,7 @@ __global__ __launch_bounds__(256) void slow_final_kernel(int k, int d, const flo
 //  C. all threads: chain bookkeeping. A donor picked r times before split q
 //     had its count halved r times, so the recorded count after split q fixes
 //     q's place in the donor's chain and the final count the chain's length.
+// Both end with the same chain bookkeeping (revive_chains), and then
 // split_kernel (many workgroups): one wave per chain applies its splits of the
 // running sums in order (chains are independent: donors are never dead).
 constexpr int kRvLdsN = 32768;  // live counts kept in LDS up to this k
@@ -930,6 +932,94 @@ __device__ __forceinline__ int halvings(float from, float to) {
     ++m;
   }
   return m;
+}
+
+// Chain bookkeeping after the draws (all 1024 threads of the revival
+// workgroup): a donor picked r times before split q had its count halved r
+// times, so the recorded count after split q fixes q's place in the donor's
+// chain and the final count the chain's length. Per thread a contiguous run
+// of splits; chain starts are counted with a block scan (chain lengths) and a
+// second one (number of chains).
+__device__ __forceinline__ void revive_chains(const ReviveArgs& A, int ndead, int* itmp) {
+  constexpr int G = 8;  // splits per batch: their loads are issued together
+  const int tid = threadIdx.x;
+  const int qper = (ndead + 1023) / 1024;
+  const int q0 = min(ndead, tid * qper), q1 = min(ndead, q0 + qper);
+  int lensum = 0, hcnt = 0;
+  for (int qb = q0; qb < q1; qb += G) {
+    int iv[G];
+    float pn[G], n0v[G], nfv[G];
+#pragma unroll
+    for (int e = 0; e < G; ++e) {
+      const int q = min(qb + e, q1 - 1);
+      iv[e] = A.pair_i[q];
+      pn[e] = A.pair_n[q];
+    }
+#pragma unroll
+    for (int e = 0; e < G; ++e) {
+      n0v[e] = A.n0[iv[e]];
+      nfv[e] = A.N[iv[e]];
+    }
+#pragma unroll
+    for (int e = 0; e < G; ++e) {
+      const int q = qb + e;
+      if (q < q1) {
+        const int ps = halvings(n0v[e] * 0.5f, pn[e]);
+        A.pos[q] = ps;
+        if (ps == 0) {
+          const int len = 1 + halvings(n0v[e] * 0.5f, nfv[e]);
+          A.head_of[iv[e]] = q;
+          A.clen[q] = len;
+          lensum += len;
+          ++hcnt;
+        }
+      }
+    }
+  }
+  const int lincl = block_incl_scan<int, 1024>(lensum, itmp);
+  const int hincl = block_incl_scan<int, 1024>(hcnt, itmp);
+  int lb = lincl - lensum, hb = hincl - hcnt;
+  for (int qb = q0; qb < q1; qb += G) {
+    int pv[G], cl[G];
+#pragma unroll
+    for (int e = 0; e < G; ++e) {
+      const int q = min(qb + e, q1 - 1);
+      pv[e] = A.pos[q];
+      cl[e] = A.clen[q];
+    }
+#pragma unroll
+    for (int e = 0; e < G; ++e) {
+      const int q = qb + e;
+      if (q < q1 && pv[e] == 0) {
+        A.cbase[q] = lb;
+        lb += cl[e];
+        A.heads[hb++] = q;
+      }
+    }
+  }
+  if (tid == 1023) A.nheads[0] = hincl;
+  __threadfence_block();
+  __syncthreads();
+  for (int qb = q0; qb < q1; qb += G) {
+    int iv[G], pv[G], hv[G], cb[G];
+#pragma unroll
+    for (int e = 0; e < G; ++e) {
+      const int q = min(qb + e, q1 - 1);
+      iv[e] = A.pair_i[q];
+      pv[e] = A.pos[q];
+    }
+#pragma unroll
+    for (int e = 0; e < G; ++e) hv[e] = A.head_of[iv[e]];
+#pragma unroll
+    for (int e = 0; e < G; ++e) cb[e] = A.cbase[hv[e]];
+#pragma unroll
+    for (int e = 0; e < G; ++e)
+      if (qb + e < q1) A.list[cb[e] + pv[e]] = qb + e;
+  }
+  if (tid == 0) {
+    A.counters[0] += ndead;
+    A.counters[3] += ndead;
+  }
 }
 
 // VT > 0: VT clusters per lane per chunk (a power of two >= k / 4096), held in
@@ -1184,41 +1274,313 @@ __global__ __launch_bounds__(1024) void revive_kernel(ReviveArgs A) {
   }
 
   // ---- C: chain bookkeeping -------------------------------------------------
-  // per thread a contiguous run of splits; chain starts are counted with a
-  // block scan (chain lengths) and a second one (number of chains)
-  const int qper = (ndead + 1023) / 1024;
-  const int q0 = min(ndead, tid * qper), q1 = min(ndead, q0 + qper);
-  int lensum = 0, hcnt = 0;
-  for (int q = q0; q < q1; ++q) {
-    const int i = A.pair_i[q];
-    const int ps = halvings(A.n0[i] * 0.5f, A.pair_n[q]);
-    A.pos[q] = ps;
-    if (ps == 0) {
-      const int len = 1 + halvings(A.n0[i] * 0.5f, A.N[i]);
-      A.head_of[i] = q;
-      A.clen[q] = len;
-      lensum += len;
-      ++hcnt;
+  revive_chains(A, ndead, itmp);
+}
+
+// Donor draws for k <= kSpecK, speculated a round of 64 at a time.
+//
+// The draws are sequential (each halves its donor's count, which moves every
+// later target and prefix sum), but one draw moves them little: the donor of
+// draw q is usually at or next to the cluster it would get from the counts at
+// the start of its round. So each round of 64 dead clusters (lane q = draw q)
+//  1. speculates in parallel: lane q searches the round-start prefix sums for
+//     u_q T (T = the live total at the round's start) and keeps its candidate
+//     m_q with the exact current prefix sums around it, L_q = cum(m_q - 1)
+//     and H_q = cum(m_q), and the candidate's current count;
+//  2. settles the draws in order: draw q's exact target is u_q T_q (T_q =
+//     the live total after the round's earlier draws); if L_q <= u_q T_q <
+//     H_q the candidate is the donor (the first cluster whose prefix sum
+//     exceeds the target); otherwise a walk from m_q over the current counts,
+//     16 clusters per step, finds it. Each settled draw halves its donor's
+//     count, and every lane subtracts the lost half from L, H (where the donor
+//     lies at or before its candidate) and from T;
+//  3. folds the round's halvings into the prefix tree.
+// Live clusters are compacted in index order (dead ones carry no weight), and
+// the prefix sums come from a tree of sums of 8 (levels of 2048, 256, 32 and
+// 4 fp64 sums over 16384 counts). Every sum is of fp32 counts in fp64 and is
+// exact, so its value does not depend on the order of the additions, and the
+// donors are those of the one-by-one definition bit for bit.
+// The settle loop is one wave's dependent chain (fp64 multiply, compares,
+// ballot, lane reads, fp64 updates), a few hundred cycles per draw; about a
+// third of the candidates are right at the first SIFT-like check, and a miss
+// costs one 16-cluster walk step (an LDS read and a 16-lane fp64 scan).
+constexpr int kSpecK = 16384;
+
+// First of N consecutive sums whose running total from acc exceeds t (N if
+// none); acc becomes the running total before it.
+template <int N>
+__device__ __forceinline__ int pick_child(const double* s, double t, double& acc) {
+  double v[N];
+#pragma unroll
+  for (int i = 0; i < N; i += 2) {
+    const double2 p = *reinterpret_cast<const double2*>(s + i);
+    v[i] = p.x;
+    v[i + 1] = p.y;
+  }
+  double run[N];
+  run[0] = acc + v[0];
+#pragma unroll
+  for (int i = 1; i < N; ++i) run[i] = run[i - 1] + v[i];
+  int r = N;
+  double before = acc;
+#pragma unroll
+  for (int i = N - 1; i >= 0; --i)
+    if (run[i] > t) {
+      r = i;
+      before = i > 0 ? run[i - 1] : acc;
+    }
+  acc = before;
+  return r;
+}
+
+// Inclusive fp64 scan within each row of 16 lanes.
+__device__ __forceinline__ double row_scan16_f64(double v) {
+  v += dpp_move_f64<0x111, 0xF>(v);  // row_shr:1
+  v += dpp_move_f64<0x112, 0xF>(v);  // row_shr:2
+  v += dpp_move_f64<0x114, 0xF>(v);  // row_shr:4
+  v += dpp_move_f64<0x118, 0xF>(v);  // row_shr:8
+  return v;
+}
+
+__global__ __launch_bounds__(1024) void revive_spec_kernel(ReviveArgs A) {
+  constexpr int RV = kSpecK / 1024;  // clusters per thread in the set-up
+  __shared__ double dtmp[16];
+  __shared__ int itmp[16];
+  __shared__ __attribute__((aligned(16))) float wc[kSpecK + 64];  // live counts, compacted
+  __shared__ int lidx[kSpecK];                                      // their clusters
+  __shared__ __attribute__((aligned(16))) double t1[kSpecK / 8];  // sums of 8 counts
+  __shared__ __attribute__((aligned(16))) double t2[kSpecK / 64];
+  __shared__ __attribute__((aligned(16))) double t3[kSpecK / 512];
+  __shared__ __attribute__((aligned(16))) double t4[kSpecK / 4096];
+  __shared__ float sink[64];  // target of the stores of lanes that do not write
+  __shared__ int s_ndead;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int k = A.k;
+  if (tid == 0) A.nheads[0] = 0;
+
+  // ---- threshold, dead list, compacted live counts ---------------------------
+  // thread tid owns clusters RV tid .. RV tid + RV - 1, read once
+  float nv[RV];
+#pragma unroll
+  for (int e = 0; e < RV; ++e) {
+    const int j = RV * tid + e;
+    nv[e] = j < k ? A.N[j] : 0.0f;
+  }
+  double loc = 0.0;
+#pragma unroll
+  for (int e = 0; e < RV; ++e) loc += (double)nv[e];
+  const double total = block_sum<double, 1024>(loc, dtmp);
+  const double th = A.thr * (total / (double)k);
+  unsigned deadm = 0;
+  int cnt = 0;
+#pragma unroll
+  for (int e = 0; e < RV; ++e) {
+    const int j = RV * tid + e;
+    if (j < k) {
+      const int dd = ((double)nv[e] < th) ? 1 : 0;
+      A.flags[j] = dd;
+      A.n0[j] = nv[e];
+      deadm |= (unsigned)dd << e;
+      cnt += dd;
     }
   }
-  const int lincl = block_incl_scan<int, 1024>(lensum, itmp);
-  const int hincl = block_incl_scan<int, 1024>(hcnt, itmp);
-  int lb = lincl - lensum, hb = hincl - hcnt;
-  for (int q = q0; q < q1; ++q) {
-    if (A.pos[q] == 0) {
-      A.cbase[q] = lb;
-      lb += A.clen[q];
-      A.heads[hb++] = q;
+  const int incl = block_incl_scan<int, 1024>(cnt, itmp);
+  if (tid == 1023) s_ndead = incl;
+  int wpos = incl - cnt;                   // dead clusters before this thread's
+  int lpos = min(k, RV * tid) - wpos;      // live clusters before this thread's
+#pragma unroll
+  for (int e = 0; e < RV; ++e) {
+    const int j = RV * tid + e;
+    if (j < k) {
+      if ((deadm >> e) & 1u) {
+        A.dead[wpos++] = j;
+      } else {
+        wc[lpos] = nv[e];
+        lidx[lpos] = j;
+        ++lpos;
+      }
     }
   }
-  if (tid == 1023) A.nheads[0] = hincl;
   __threadfence_block();
   __syncthreads();
-  for (int q = q0; q < q1; ++q) A.list[A.cbase[A.head_of[A.pair_i[q]]] + A.pos[q]] = q;
-  if (tid == 0) {
-    A.counters[0] += ndead;
-    A.counters[3] += ndead;
+  const int ndead = s_ndead;
+  const int M = k - ndead;  // live clusters
+  if (A.count_only) {
+    if (tid == 0) A.counters[2] = ndead;
+    return;
   }
+  if (ndead == 0 || M == 0) return;  // nothing to revive, or no donor exists
+  for (int q = tid; q < ndead; q += 1024)
+    A.udraw[q] = revive_uniform(A.seed, A.step, (uint64_t)A.dead[q]);
+  for (int m = M + tid; m < kSpecK + 64; m += 1024) wc[m] = 0.0f;
+  __threadfence_block();
+  __syncthreads();
+  for (int i = tid; i < kSpecK / 8; i += 1024) {
+    const float4 a = *reinterpret_cast<const float4*>(&wc[8 * i]);
+    const float4 b = *reinterpret_cast<const float4*>(&wc[8 * i + 4]);
+    t1[i] = (((double)a.x + (double)a.y) + ((double)a.z + (double)a.w)) +
+            (((double)b.x + (double)b.y) + ((double)b.z + (double)b.w));
+  }
+  __syncthreads();
+  auto sum8 = [](const double* s) {
+    return ((s[0] + s[1]) + (s[2] + s[3])) + ((s[4] + s[5]) + (s[6] + s[7]));
+  };
+  for (int i = tid; i < kSpecK / 64; i += 1024) t2[i] = sum8(&t1[8 * i]);
+  __syncthreads();
+  if (tid < kSpecK / 512) t3[tid] = sum8(&t2[8 * tid]);
+  __syncthreads();
+  if (tid < kSpecK / 4096) t4[tid] = sum8(&t3[8 * tid]);
+  __syncthreads();
+
+  // ---- draws (wave 0) ---------------------------------------------------------
+  if (wave == 0) {
+    double T = (t4[0] + t4[1]) + (t4[2] + t4[3]);  // live total
+    int64_t logc = A.counters[1];
+    // the first round's dead clusters and draws; later rounds load theirs one
+    // round ahead
+    int dl = lane < ndead ? A.dead[lane] : 0;
+    double u = lane < ndead ? A.udraw[lane] : 0.0;
+    for (int d0 = 0; d0 < ndead; d0 += 64) {
+      const int nb = min(64, ndead - d0);
+      const bool act = lane < nb;
+      const int dn = d0 + 64 + lane;
+      const int dl_next = dn < ndead ? A.dead[dn] : 0;
+      const double u_next = dn < ndead ? A.udraw[dn] : 0.0;
+      // 1. candidate from the round-start sums; a target at or past the total
+      // (no cluster exceeds it) takes position M, with L = H = T
+      const double t0 = u * T;
+      double acc = 0.0;
+      int m = M;
+      double L = T, H = T;
+      const int i4 = pick_child<4>(t4, t0, acc);
+      if (i4 < 4) {
+        const int n3 = 8 * i4 + min(pick_child<8>(&t3[8 * i4], t0, acc), 7);
+        const int n2 = 8 * n3 + min(pick_child<8>(&t2[8 * n3], t0, acc), 7);
+        const int n1 = 8 * n2 + min(pick_child<8>(&t1[8 * n2], t0, acc), 7);
+        double w8[8];
+        const float4 a = *reinterpret_cast<const float4*>(&wc[8 * n1]);
+        const float4 b = *reinterpret_cast<const float4*>(&wc[8 * n1 + 4]);
+        w8[0] = a.x; w8[1] = a.y; w8[2] = a.z; w8[3] = a.w;
+        w8[4] = b.x; w8[5] = b.y; w8[6] = b.z; w8[7] = b.w;
+        const int i0 = min(pick_child<8>(w8, t0, acc), 7);
+        m = 8 * n1 + i0;
+        L = acc;
+        H = acc + w8[i0];
+      }
+      // half the candidate's current count (0 at position M), as the split
+      // would take it, in fp32 and fp64
+      float half = wc[m] * 0.5f;
+      double halfd = (double)half;
+      // waited for here, so that the loop below never waits for its own stores
+      __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
+      double Tq = T;
+      int rec_m = 0;
+      float rec_n = 0.0f;
+      // 2. settle the draws in order
+      for (int q = 0; q < nb; ++q) {
+        const double t = u * Tq;
+        const uint64_t okm = __ballot((L <= t) & (t < H));
+        int ms;
+        float nh;
+        double nhd;
+        if ((okm >> q) & 1ull) {
+          ms = __builtin_amdgcn_readlane(m, q);
+          nh = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(half), q));
+          nhd = readlane_f64(halfd, q);
+        } else {
+          const uint64_t rightm = __ballot(t >= H);
+          const double tq = readlane_f64(t, q);
+          const int mq = __builtin_amdgcn_readlane(m, q);
+          ms = -1;
+          float cn = 0.0f;
+          if ((rightm >> q) & 1ull) {
+            // right of the candidate: cum(p0 - 1) = c <= tq
+            double c = readlane_f64(H, q);
+            for (int p0 = mq + 1; p0 < M; p0 += 16) {
+              const float w = wc[p0 + (lane & 15)];  // zero past M
+              const double v = row_scan16_f64((double)w);
+              const uint64_t hm = __ballot((lane < 16) & (c + v > tq));
+              if (hm) {
+                const int i = __ffsll((unsigned long long)hm) - 1;
+                ms = p0 + i;
+                cn = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(w), i));
+                break;
+              }
+              c += readlane_f64(v, 15);
+            }
+            if (ms < 0) {  // the target reaches the total: the last live cluster
+              ms = M - 1;
+              cn = wc[M - 1];
+            }
+          } else {
+            // left of the candidate: cum(p0) = c > tq
+            double c = readlane_f64(L, q);
+            for (int p0 = mq - 1; p0 >= 0; p0 -= 16) {
+              const int pos = p0 - (lane & 15);
+              const float w = pos >= 0 ? wc[max(pos, 0)] : 0.0f;
+              const double v = row_scan16_f64((double)w);
+              const uint64_t hm = __ballot((lane < 16) & (pos >= 0) & (c - v <= tq));
+              if (hm) {
+                const int i = __ffsll((unsigned long long)hm) - 1;
+                ms = p0 - i;
+                cn = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(w), i));
+                break;
+              }
+              c -= readlane_f64(v, 15);
+            }
+            if (ms < 0) {  // not reachable with exact sums: cum(-1) = 0 <= tq
+              ms = 0;
+              cn = wc[0];
+            }
+          }
+          __builtin_amdgcn_s_waitcnt(0xC07F);  // its LDS reads are done before the join
+          nh = cn * 0.5f;
+          nhd = (double)nh;
+        }
+        // the donor's count halves (lane 0 stores it; the others store to the sink)
+        *(lane == 0 ? &wc[ms] : &sink[lane]) = nh;
+        Tq -= nhd;
+        H -= ms <= m ? nhd : 0.0;
+        L -= ms < m ? nhd : 0.0;
+        const bool hit = ms == m;
+        const float hh = half * 0.5f;
+        half = hit ? hh : half;
+        halfd = hit ? (double)hh : halfd;
+        rec_m = lane == q ? ms : rec_m;
+        rec_n = lane == q ? nh : rec_n;
+      }
+      // 3. the tree learns the round's halvings; outputs of the round
+      if (act) {
+        const double nd = (double)rec_n;
+        atomicAdd(&t1[rec_m >> 3], -nd);
+        atomicAdd(&t2[rec_m >> 6], -nd);
+        atomicAdd(&t3[rec_m >> 9], -nd);
+        atomicAdd(&t4[rec_m >> 12], -nd);
+        const int ci = lidx[rec_m];
+        A.N[dl] = rec_n;
+        A.pair_i[d0 + lane] = ci;
+        A.pair_n[d0 + lane] = rec_n;
+        if (A.log && logc + lane < A.log_cap) {
+          A.log[3 * (logc + lane)] = (int32_t)A.step;
+          A.log[3 * (logc + lane) + 1] = dl;
+          A.log[3 * (logc + lane) + 2] = ci;
+        }
+      }
+      if (A.log) logc = min(A.log_cap, logc + nb);
+      T = Tq;
+      dl = dl_next;
+      u = u_next;
+    }
+    if (lane == 0) A.counters[1] = logc;
+  }
+  __syncthreads();
+  // the donors' halved counts (dead clusters were written by the rounds)
+  for (int m = tid; m < M; m += 1024) A.N[lidx[m]] = wc[m];
+  __threadfence_block();
+  __syncthreads();
+  revive_chains(A, ndead, itmp);
 }
 
 // One wave per donor chain: apply its splits of the running sums in order.
@@ -1594,7 +1956,9 @@ hipError_t launch_slow_final(int k, int d, const float* N2, const float* S2, con
 
 hipError_t launch_revive(const ReviveArgs& a, hipStream_t st) {
   const int v = (a.k + 4095) / 4096;
-  if (v <= 1)
+  if (a.k <= kSpecK)
+    revive_spec_kernel<<<1, 1024, 0, st>>>(a);
+  else if (v <= 1)
     revive_kernel<1><<<1, 1024, 0, st>>>(a);
   else if (v <= 2)
     revive_kernel<2><<<1, 1024, 0, st>>>(a);

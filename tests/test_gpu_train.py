@@ -141,11 +141,14 @@ def test_lloyd_mode_lockstep(mm, name, gen, n, d, k, iters):
     assert out.stats["n_splits"] == 0
 
 
-# Revival draws at larger k: 64 chunks of 64 V clusters, V = 2, 8, 16 (live
-# counts in global memory) and the generic path (k > 65536), each with
-# thousands of revivals.
+# Revival draws at larger k, each with thousands of revivals: the speculated
+# rounds up to k = 16384 (k6000, and k16384 with the full prefix tree), then
+# 64 chunks of 64 V clusters, V = 8 just past it, V = 8 and 16 (live counts in
+# global memory), and the generic path (k > 65536).
 REVIVAL_K = [
     ("k6000", 24_000, 8, 6_000, 4_096),
+    ("k16384", 50_000, 8, 16_384, 8_192),
+    ("k16385", 50_000, 8, 16_385, 8_192),
     ("k20000", 60_000, 8, 20_000, 8_192),
     ("k40000", 100_000, 4, 40_000, 16_384),
     ("k66000", 140_000, 4, 66_000, 16_384),
