@@ -75,6 +75,10 @@ LOCKSTEP = [
     ("u8-small", "codes-u8", 12_000, 128, 256, 2.0, {}),
     ("u8-ragged", "codes-u8", 5_003, 37, 77, 1.5, dict(batch_size=700)),
     ("u8-sift", "sift-u8", 20_000, 128, 1024, 2.0, {}),
+    # rows of 16-byte grouping units: 768 code bytes, 384 bf16 and fp16 values
+    ("u8-wide", "codes-u8", 12_000, 768, 256, 2.0, {}),
+    ("large-384", "large", 20_000, 384, 512, 2.0, {}),
+    ("f16-384", "embedding-f16", 12_000, 384, 256, 2.0, {}),
 ]
 
 
