@@ -67,7 +67,7 @@ def test_assign_fp32(mm, gen, n, d, k):
 
 
 CASES_BF16 = [(2000, 128, 300), (1000, 64, 129), (777, 40, 50), (500, 37, 20), (300, 256, 1),
-              (900, 520, 300), (600, 1024, 257)]
+              (900, 520, 300), (600, 1024, 257), (4097, 768, 1025), (300, 768, 1)]
 
 
 CASES_BF16_SEARCH = [("sift", 2000, 128, 300), ("embedding", 1000, 768, 257),
@@ -92,7 +92,8 @@ def test_assign_bf16_search(mm, gen, n, d, k):
 
 CASES_SPHERICAL = [("embedding", 1500, 768, 300, False), ("deep", 3000, 96, 1000, False),
                    ("tiny", 700, 16, 40, False), ("large", 2000, 128, 300, True),
-                   ("large", 900, 64, 129, True), ("large", 600, 256, 70, True)]
+                   ("large", 900, 64, 129, True), ("large", 600, 256, 70, True),
+                   ("large", 1100, 768, 65, True)]
 
 
 def _unit_rows(A):
@@ -304,7 +305,8 @@ def test_assign_bf16(mm, n, d, k):
 
 CASES_F16 = [("embedding", 2000, 768, 300), ("deep", 1000, 96, 129), ("sift", 1500, 128, 257),
              ("tiny", 777, 40, 50), ("tiny", 500, 37, 20), ("embedding", 300, 256, 1),
-             ("deep", 600, 32, 70), ("sift", 900, 64, 1000), ("embedding", 513, 1040, 257)]
+             ("deep", 600, 32, 70), ("sift", 900, 64, 1000), ("embedding", 513, 1040, 257),
+             ("embedding", 4097, 768, 1025)]
 
 
 @pytest.mark.parametrize("gen,n,d,k", CASES_F16)
