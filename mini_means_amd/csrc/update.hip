@@ -1470,9 +1470,12 @@ __global__ __launch_bounds__(1024) void revive_spec_kernel(ReviveArgs A) {
         H = acc + w8[i0];
       }
       // half the candidate's current count (0 at position M), as the split
-      // would take it, in fp32 and fp64
+      // would take it, in fp32 and fp64; the current counts of its two
+      // neighbours on each side (0 before position 0 and past M)
       float half = wc[m] * 0.5f;
       double halfd = (double)half;
+      float wl1 = m >= 1 ? wc[max(m - 1, 0)] : 0.0f, wl2 = m >= 2 ? wc[max(m - 2, 0)] : 0.0f;
+      float wr1 = wc[m + 1], wr2 = wc[m + 2];  // m + 2 <= M + 2: zero padding
       // waited for here, so that the loop below never waits for its own stores
       __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
       double Tq = T;
@@ -1496,9 +1499,24 @@ __global__ __launch_bounds__(1024) void revive_spec_kernel(ReviveArgs A) {
           ms = -1;
           float cn = 0.0f;
           if ((rightm >> q) & 1ull) {
-            // right of the candidate: cum(p0 - 1) = c <= tq
+            // right of the candidate: cum(p0 - 1) = c <= tq; first its two
+            // neighbours (a count of 0 is padding past M and never taken)
             double c = readlane_f64(H, q);
-            for (int p0 = mq + 1; p0 < M; p0 += 16) {
+            const float r1 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(wr1), q));
+            const float r2 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(wr2), q));
+            const double c1 = c + (double)r1, c2 = c1 + (double)r2;
+            int p0 = mq + 3;
+            if (tq < c1) {
+              ms = mq + 1;
+              cn = r1;
+              p0 = M;  // found
+            } else if (tq < c2) {
+              ms = mq + 2;
+              cn = r2;
+              p0 = M;
+            }
+            c = c2;
+            for (; p0 < M; p0 += 16) {
               const float w = wc[p0 + (lane & 15)];  // zero past M
               const double v = row_scan16_f64((double)w);
               const uint64_t hm = __ballot((lane < 16) & (c + v > tq));
@@ -1515,9 +1533,23 @@ __global__ __launch_bounds__(1024) void revive_spec_kernel(ReviveArgs A) {
               cn = wc[M - 1];
             }
           } else {
-            // left of the candidate: cum(p0) = c > tq
+            // left of the candidate: cum(p0) = c > tq; first its two neighbours
             double c = readlane_f64(L, q);
-            for (int p0 = mq - 1; p0 >= 0; p0 -= 16) {
+            const float l1 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(wl1), q));
+            const float l2 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(wl2), q));
+            const double c1 = c - (double)l1, c2 = c1 - (double)l2;
+            int p0 = mq - 3;
+            if (c1 <= tq) {
+              ms = mq - 1;
+              cn = l1;
+              p0 = -1;  // found
+            } else if (c2 <= tq) {
+              ms = mq - 2;
+              cn = l2;
+              p0 = -1;
+            }
+            c = c2;
+            for (; p0 >= 0; p0 -= 16) {
               const int pos = p0 - (lane & 15);
               const float w = pos >= 0 ? wc[max(pos, 0)] : 0.0f;
               const double v = row_scan16_f64((double)w);
@@ -1548,6 +1580,11 @@ __global__ __launch_bounds__(1024) void revive_spec_kernel(ReviveArgs A) {
         const float hh = half * 0.5f;
         half = hit ? hh : half;
         halfd = hit ? (double)hh : halfd;
+        const int dm = ms - m;  // the neighbours' counts halve too
+        wl2 = dm == -2 ? nh : wl2;
+        wl1 = dm == -1 ? nh : wl1;
+        wr1 = dm == 1 ? nh : wr1;
+        wr2 = dm == 2 ? nh : wr2;
         rec_m = lane == q ? ms : rec_m;
         rec_n = lane == q ? nh : rec_n;
       }
