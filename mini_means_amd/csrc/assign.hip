@@ -562,8 +562,6 @@ __global__ __launch_bounds__(kThreads, 1) void assign_kernel(
 // ragged row the chunks past the row end are zeroed in LDS before use, and
 // the loads for them read the row's first chunk (in bounds, finite).
 // ---------------------------------------------------------------------------
-typedef __attribute__((address_space(3))) void* lds_ptr_t;
-
 constexpr int kRing = 3;                         // stage buffers
 constexpr int kRowsStage = kTP + kTC;            // point rows, then centroid rows
 constexpr int kStageBytes = kRowsStage * kSlab;  // 48 KB
@@ -575,34 +573,6 @@ constexpr int kLoadsPerWave = kRowsStage / 8 / (kThreads / 64);  // 8-row wave l
 // banks) of a 16-byte read per cycle.
 __device__ __forceinline__ int swz_pos(int r, int c) { return c ^ (r & 7) ^ ((r >> 3) & 1); }
 __device__ __forceinline__ int swz(int r, int c) { return r * kSlab + (swz_pos(r, c) << 4); }
-
-// One wave-wide direct load: lane i's 16 bytes at src go to LDS bytes
-// [lds + 16 i, lds + 16 i + 16); lds must be wave-uniform. Written as asm so
-// that the compiler does not treat every later LDS read as aliasing the load
-// (it would wait for all loads in flight before each one); the asm has no
-// register outputs, and completion is waited for with EMK_WAIT_VMCNT.
-// M0 is clobbered: the backend reserves it and sets it right before any
-// instruction that reads it, so no value of its own is live across the asm.
-#pragma clang diagnostic push
-#pragma clang diagnostic ignored "-Winline-asm"
-__device__ __forceinline__ void load_lds16(const void* src, void* lds) {
-  const uint32_t m0 = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(lds_ptr_t)lds);
-  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off" ::"s"(m0), "v"(src)
-               : "memory", "m0");
-}
-#pragma clang diagnostic pop
-
-// s_waitcnt immediate that waits for vmcnt <= n only (gfx9 encoding).
-#define EMK_WAIT_VMCNT(n) __builtin_amdgcn_s_waitcnt(((n) & 15) | (((n) >> 4) << 14) | (7 << 4) | (15 << 8))
-
-// Workgroup barrier that orders LDS accesses only. __syncthreads() also
-// orders global memory, which waits for every load in flight, the ring loads
-// of later stages included; their completion is waited for explicitly.
-__device__ __forceinline__ void lds_barrier() {
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
-  __builtin_amdgcn_s_barrier();
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
-}
 
 template <int DT>
 __global__ __launch_bounds__(kThreads, 1) void assign_ring_kernel(
@@ -666,7 +636,7 @@ __global__ __launch_bounds__(kThreads, 1) void assign_ring_kernel(
     for (int i = 0; i < kLoadsPerWave; ++i) {
       const int col = is * EPS + pcol[i];
       const int c = ragged && col >= d ? 0 : col;
-      load_lds16(rowp[i] + (size_t)c * ES, dst + 1024 * (wv * kLoadsPerWave + i));
+      lds_load16(rowp[i] + (size_t)c * ES, dst + 1024 * (wv * kLoadsPerWave + i));
     }
     islot = islot + 1 == kRing ? 0 : islot + 1;
     if (issued + 1 < total) {  // past the end the last stage is loaded again

@@ -57,7 +57,6 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef int32_t i32x4 __attribute__((ext_vector_type(4)));
 typedef int32_t i32x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
-typedef __attribute__((address_space(3))) void* lds_ptr_t;
 
 constexpr int kWaves = 4;            // one wave per SIMD
 constexpr int kThreads = 64 * kWaves;
@@ -68,37 +67,6 @@ constexpr int kPan = 64;             // centroid rows per panel
 constexpr int kBlk = kPan / 16;      // 16-row blocks per panel
 constexpr int kRing = 3;             // panels in flight
 constexpr int kMasked = -(1 << 30);  // packed value of a row past k
-
-// One wave-wide direct load of 16 bytes per lane into 1 KB of consecutive LDS
-// starting at `lds` (wave-uniform). Written as asm so that the compiler does
-// not make later LDS reads wait for it; completion is waited for with
-// EMK_I8W_WAIT. M0 is set right before the load and declared clobbered.
-#pragma clang diagnostic push
-#pragma clang diagnostic ignored "-Winline-asm"
-__device__ __forceinline__ void lds_load16(const void* src, void* lds) {
-  const uint32_t m0 = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(lds_ptr_t)lds);
-  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off" ::"s"(m0), "v"(src)
-               : "memory", "m0");
-}
-// The same with 4 bytes per lane into 256 consecutive bytes.
-__device__ __forceinline__ void lds_load4(const void* src, void* lds) {
-  const uint32_t m0 = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(lds_ptr_t)lds);
-  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dword %1, off" ::"s"(m0), "v"(src)
-               : "memory", "m0");
-}
-#pragma clang diagnostic pop
-
-// s_waitcnt that waits for vmcnt <= n only (gfx9 encoding)
-#define EMK_I8W_WAIT(n) \
-  __builtin_amdgcn_s_waitcnt(((n) & 15) | (((n) >> 4) << 14) | (7 << 4) | (15 << 8))
-
-// Barrier that orders LDS accesses only (loads still in flight are waited
-// for explicitly).
-__device__ __forceinline__ void lds_sync() {
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
-  __builtin_amdgcn_s_barrier();
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
-}
 
 // The direct loads of one panel of 64 centroid rows of D bytes (rows past k
 // repeat row k - 1) into lc, chunk position p of row r holding the row's
@@ -127,12 +95,12 @@ __device__ __forceinline__ void issue_panel(const unsigned char* C, const uint32
 template <int LPW>
 __device__ __forceinline__ void wait_panel(int panel, int npan, int wave) {
   if (panel + 1 < npan) {
-    EMK_I8W_WAIT(LPW + 1);
-    if (wave != 0) EMK_I8W_WAIT(LPW);
+    EMK_WAIT_VMCNT(LPW + 1);
+    if (wave != 0) EMK_WAIT_VMCNT(LPW);
   } else {
-    EMK_I8W_WAIT(0);
+    EMK_WAIT_VMCNT(0);
   }
-  lds_sync();
+  lds_barrier();
 }
 
 template <int KS, bool U8>  // KS = d / 64 k-steps of 64 bytes

@@ -251,4 +251,45 @@ __device__ __forceinline__ double readlane_f64(double v, int lane) {
   return __longlong_as_double((long long)(((uint64_t)hi << 32) | lo));
 }
 
+// ---------------------------------------------------------------------------
+// Direct global-to-LDS loads (gfx950 global_load_lds_dword / _dwordx4).
+// One wave-wide load: lane i's 16 (or 4) bytes at src go to LDS bytes
+// [lds + 16 i, lds + 16 i + 16) (or 4 i ...); lds must be wave-uniform.
+// Written as asm so that the compiler does not treat every later LDS read as
+// aliasing the load (it would wait for all loads in flight before each one);
+// the asm has no register outputs, and completion is waited for with
+// EMK_WAIT_VMCNT. M0 is clobbered: the backend reserves it and sets it right
+// before any instruction that reads it, so no value of its own is live
+// across the asm.
+// ---------------------------------------------------------------------------
+typedef __attribute__((address_space(3))) void* lds_ptr_t;
+
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+__device__ __forceinline__ void lds_load16(const void* src, void* lds) {
+  const uint32_t m0 = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(lds_ptr_t)lds);
+  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off" ::"s"(m0), "v"(src)
+               : "memory", "m0");
+}
+__device__ __forceinline__ void lds_load4(const void* src, void* lds) {
+  const uint32_t m0 = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(lds_ptr_t)lds);
+  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dword %1, off" ::"s"(m0), "v"(src)
+               : "memory", "m0");
+}
+#pragma clang diagnostic pop
+
+// s_waitcnt immediate that waits for vmcnt <= n only (gfx9 encoding).
+#define EMK_WAIT_VMCNT(n) \
+  __builtin_amdgcn_s_waitcnt(((n) & 15) | (((n) >> 4) << 14) | (7 << 4) | (15 << 8))
+
+// Workgroup barrier that orders LDS accesses only. __syncthreads() also
+// orders global memory, which waits for every load in flight, direct loads
+// of later panels or stages included; their completion is waited for
+// explicitly.
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
 }  // namespace emk

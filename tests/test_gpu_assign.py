@@ -303,6 +303,38 @@ def test_assign_bf16(mm, n, d, k):
     check_dists(X, Cs, None, lab, dist, what=f"bf16 {n}x{d} k={k}")
 
 
+@pytest.mark.parametrize("n,k,sph", [((1 << 20) + 77, 1000, False), (1 << 20, 129, True)])
+def test_assign_bf16_large_batch(mm, n, k, sph):
+    """A batch of more than 2^20 bf16 rows of d = 128 (the 100M-row set's
+    batch scale) in the register-resident kernel: a ragged last point tile
+    and a ragged last centroid panel, checked on a sample of rows and on the
+    last rows of the batch (and in spherical mode, the similarity)."""
+    import torch
+    X = datagen.large_host(n, d=128, m=64, seed=17)
+    C = _centroids(X[:65536], k, 8)
+    if sph:
+        C = (C / np.linalg.norm(C.astype(np.float64), axis=1, keepdims=True)).astype(np.float32)
+    lab, dist = mm.assign(to_device(X), torch.from_numpy(C).cuda(), spherical=sph)
+    lab, dist = lab.cpu().numpy(), dist.cpu().numpy()
+    rows = np.unique(np.concatenate([np.random.default_rng(3).choice(n, 3000, replace=False),
+                                     np.arange(n - 300, n)]))
+    Cs = oracle.bf16_round(C)
+    what = f"bf16 large batch {n}x128 k={k}{' spherical' if sph else ''}"
+    if sph:
+        olab, s1, s2 = oracle.assign_ip(X, Cs, rows)
+        ref = oracle.dot_to(X, Cs, lab[rows], rows)
+        check_labels(X, Cs, rows, lab[rows], olab, -2.0 * s1, -2.0 * s2, given_dist=-2.0 * ref,
+                     what=what)
+        Xf = oracle.to_f32(X[rows]).astype(np.float64)
+        scale = np.einsum("ij,ij->i", Xf, Xf) + np.sum(Cs[lab[rows]].astype(np.float64) ** 2, axis=1)
+        assert np.all(np.abs(dist[rows] - ref) <= 1e-5 * scale)
+    else:
+        olab, d1, d2 = oracle.assign(X, Cs, rows)
+        check_labels(X, Cs, rows, lab[rows], olab, d1, d2, what=what)
+        check_dists(X, Cs, rows, lab[rows], dist[rows], what=what)
+    assert lab.min() >= 0 and lab.max() < k
+
+
 CASES_F16 = [("embedding", 2000, 768, 300), ("deep", 1000, 96, 129), ("sift", 1500, 128, 257),
              ("tiny", 777, 40, 50), ("tiny", 500, 37, 20), ("embedding", 300, 256, 1),
              ("deep", 600, 32, 70), ("sift", 900, 64, 1000), ("embedding", 513, 1040, 257),
