@@ -212,6 +212,10 @@ typedef struct emeans_stats {
                                        /* ms_sample includes, with bf16_search, the
                                           gather and bf16 rounding of the batch rows */
   int64_t steps_run;                   /* update steps executed */
+  /* with opts->profile: device time of each pass, from an event recorded on
+     opts->stream before the pass's first launch to one after its statistics
+     (0 for a pass that did not run); entries past n_passes are 0 */
+  double pass_ms[EMEANS_MAX_PASSES];
 } emeans_stats;
 
 /* Scaling-law recipe for (n, d, k, T) and the given options; host only, no

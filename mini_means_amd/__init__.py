@@ -52,6 +52,7 @@ class Stats(ctypes.Structure):
         ("ms_total", c_dbl), ("ms_assign", c_dbl), ("ms_bucket", c_dbl), ("ms_group", c_dbl),
         ("ms_update", c_dbl),
         ("ms_revive", c_dbl), ("ms_sample", c_dbl), ("steps_run", c_i64),
+        ("pass_ms", c_dbl * MAX_PASSES),
     ]
 
 
@@ -173,7 +174,8 @@ def _stats_dict(s: Stats) -> dict:
                 n_splits=s.n_splits, dead_at_end=s.dead_at_end, ms_total=s.ms_total,
                 ms_assign=s.ms_assign, ms_bucket=s.ms_bucket, ms_group=s.ms_group,
                 ms_update=s.ms_update,
-                ms_revive=s.ms_revive, ms_sample=s.ms_sample, steps_run=s.steps_run)
+                ms_revive=s.ms_revive, ms_sample=s.ms_sample, steps_run=s.steps_run,
+                pass_ms=list(s.pass_ms[:P]))
 
 
 def recipe(n: int, d: int, k: int, T: float = 5.0, **kw) -> dict:

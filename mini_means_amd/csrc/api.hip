@@ -420,11 +420,19 @@ struct emeans_model {
   int64_t* counters = nullptr;  // [0] splits, [1] logged, [2] dead count, [3] splits this pass
   int32_t* bad_labels = nullptr;  // labels outside [-1, k) sent to emeans_closing_add
   std::vector<Span> spans;
+  // with profile: events around each pass (pass_a at its first launch, pass_b
+  // after its statistics); pass_open while pass e's start is recorded
+  hipEvent_t pass_a[EMEANS_MAX_PASSES] = {}, pass_b[EMEANS_MAX_PASSES] = {};
+  bool pass_open = false;
 
   ~emeans_model() {
     for (const Span& sp : spans) {
       (void)hipEventDestroy(sp.a);
       (void)hipEventDestroy(sp.b);
+    }
+    for (int q = 0; q < EMEANS_MAX_PASSES; ++q) {
+      if (pass_a[q]) (void)hipEventDestroy(pass_a[q]);
+      if (pass_b[q]) (void)hipEventDestroy(pass_b[q]);
     }
     if (base) {
       (void)hipFreeAsync(base, st);
@@ -444,6 +452,16 @@ struct emeans_model {
     if ((er = hipEventRecord(sp.a, st)) != hipSuccess) return er;
     if ((er = launch()) != hipSuccess) return er;
     return hipEventRecord(sp.b, st);
+  }
+
+  // Start of pass e's device time (with profile; once per pass).
+  hipError_t mark_pass_start() {
+    if (!profile || pass_open || e >= EMEANS_MAX_PASSES) return hipSuccess;
+    hipError_t er = hipEventCreate(&pass_a[e]);
+    if (er == hipSuccess) er = hipEventCreate(&pass_b[e]);
+    if (er == hipSuccess) er = hipEventRecord(pass_a[e], st);
+    if (er == hipSuccess) pass_open = true;
+    return er;
   }
 
   // Centroid table the search reads for rows of type dt.
@@ -680,6 +698,10 @@ struct emeans_model {
     HIP_RET(hipMemcpyAsync(dstat + 3 * EMEANS_MAX_PASSES + e, counters + 3, sizeof(int64_t),
                            hipMemcpyDeviceToDevice, st));
     HIP_RET(hipMemsetAsync(counters + 3, 0, sizeof(int64_t), st));
+    if (pass_open) {
+      HIP_RET(hipEventRecord(pass_b[e], st));
+      pass_open = false;
+    }
     ++e;
     rows_pass = 0;
     return EMEANS_OK;
@@ -747,6 +769,13 @@ struct emeans_model {
       stats->ms_update = cls_ms[kUpdate];
       stats->ms_revive = cls_ms[kRevive];
       stats->ms_sample = cls_ms[kSample];
+      for (int q = 0; q < EMEANS_MAX_PASSES; ++q) {
+        float ms = 0.0f;
+        stats->pass_ms[q] = (pass_a[q] && pass_b[q] && q < e &&
+                             hipEventElapsedTime(&ms, pass_a[q], pass_b[q]) == hipSuccess)
+                                ? ms
+                                : 0.0;
+      }
     }
     stats->steps_run = t;
     stats->ms_total =
@@ -759,7 +788,7 @@ extern "C" {
 
 const char* emeans_last_error(void) { return g_err.c_str(); }
 
-int emeans_version(void) { return 101; }
+int emeans_version(void) { return 102; }
 
 int emeans_recipe(int64_t n, int32_t d, int32_t k, double T, const emeans_opts* opts,
                   emeans_stats* out) {
@@ -917,6 +946,7 @@ int emeans_train(const void* X, int64_t n, int32_t d, int32_t k, double T, uint6
     const bool last = e == r.npass - 1;
     m.last_begun = last;
     const PermKey pk = make_perm_key((uint64_t)n, seed, kStreamPerm, (uint64_t)e);
+    HIP_RET(m.mark_pass_start());
     for (int64_t s = 0; s < r.steps[e] && m.t < run_steps; ++s) {
       const int64_t rem = r.rows[e] - s * B;
       const int nb = (int)(rem < B ? rem : B);
@@ -994,6 +1024,7 @@ int emeans_accumulate(emeans_model* m, const void* batch, int64_t rows, int32_t*
   if ((rc = check_device(batch, "batch")) || (labels && (rc = check_device(labels, "labels"))))
     return rc;
   if (m->e == m->r.npass - 1) m->last_begun = true;
+  HIP_RET(m->mark_pass_start());
   return m->accumulate(batch, nullptr, (int)rows, labels);
 }
 

@@ -35,7 +35,7 @@ def test_exports_every_declared_symbol(L):
     exported = {line.split()[-1] for line in out.splitlines() if line.strip()}
     for name in names:
         assert name in exported, name
-    assert L.emeans_version() == 101
+    assert L.emeans_version() == 102
 
 
 def _c_layout(struct, fields):

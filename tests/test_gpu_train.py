@@ -265,6 +265,25 @@ def test_train_repeatable(mm):
     assert abs(ma - mb) <= 1e-2 * mb
 
 
+def test_train_profile_per_pass_times(mm):
+    """With profile set, each pass reports its device time; the passes cover the
+    timed kernel classes, and a run cut short reports the passes it began."""
+    X = datagen.deep(n=20_000, d=96, seed=8)
+    out = _gpu_train(mm, X, 256, 2.5, 3, profile=True)
+    st = out.stats
+    assert st["n_passes"] == 3 and len(st["pass_ms"]) == 3
+    assert all(v > 0.0 for v in st["pass_ms"])
+    classes = sum(st[c] for c in ("ms_assign", "ms_bucket", "ms_group", "ms_update",
+                                  "ms_revive", "ms_sample"))
+    assert classes > 0.0
+    assert classes <= 1.02 * sum(st["pass_ms"]) + 0.05
+    assert sum(st["pass_ms"]) <= st["ms_total"] + 0.05
+    cut = _gpu_train(mm, X, 256, 2.5, 3, profile=True, max_steps=1)
+    assert cut.stats["pass_ms"][0] > 0.0 and cut.stats["pass_ms"][1:] == [0.0, 0.0]
+    plain = _gpu_train(mm, X, 256, 2.5, 3)
+    assert plain.stats["pass_ms"] == [0.0, 0.0, 0.0]
+
+
 SLOW = [
     ("tiny-revive", "tiny", 3_000, 16, 100, 2.0, {}),
     ("emb-small", "embedding", 12_000, 768, 256, 2.0, {}),
