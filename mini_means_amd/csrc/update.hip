@@ -672,8 +672,10 @@ __device__ __forceinline__ void load_span_unit(const unsigned char* p, float* v)
 // items that follow the spans (waves nA and up), with atomic adds for
 // clusters split over items. Without `add` the sums are stored (s_acc of a
 // cluster with rows need not be zero); with `add` (a later piece of one
-// update) every span takes the per-cluster path and adds them.
-template <int DT, int UB>
+// update) every span takes the per-cluster path and adds them. U row loads
+// are in flight per lane: 16 for spans of a few short clusters, 32 where a
+// span is one cluster of tens of rows (fewer dependent rounds per wave).
+template <int DT, int UB, int U = 16>
 __global__ __launch_bounds__(256) void group_span_kernel(const unsigned char* __restrict__ X,
                                                          int d, const uint32_t* __restrict__ order,
                                                          const int32_t* __restrict__ off,
@@ -683,7 +685,6 @@ __global__ __launch_bounds__(256) void group_span_kernel(const unsigned char* __
                                                          float* __restrict__ s_acc, int add) {
   constexpr int ES = DT == 0 ? 4 : (DT == 1 || DT == 4) ? 2 : 1;
   constexpr int EPV = UB / ES;  // elements per lane per row
-  constexpr int U = 16;         // row loads in flight per lane
   const int lane = threadIdx.x & 63;
   const int w = blockIdx.x * 4 + (threadIdx.x >> 6);
   const size_t rowbytes = (size_t)d * ES;
@@ -1878,7 +1879,10 @@ static hipError_t launch_group_dt(const unsigned char* x, int d, bool vec, int n
     const int nA = (k + C - 1) / C;
     const long long waves = (long long)nA + nb / R;
     const dim3 grid((unsigned)((waves + 3) / 4)), block(256);
-    if (ub == 4)
+    if (ub == 4 && C == 1)  // clusters of 16 rows or more on average
+      group_span_kernel<DT, 4, 32><<<grid, block, 0, st>>>(x, d, order, off, ovf, ovf_n, k, R, C,
+                                                            nA, s_acc, add);
+    else if (ub == 4)
       group_span_kernel<DT, 4><<<grid, block, 0, st>>>(x, d, order, off, ovf, ovf_n, k, R, C, nA,
                                                         s_acc, add);
     if constexpr (ES >= 2)
