@@ -249,6 +249,42 @@ __device__ __forceinline__ void mfma_slice(typename Fmt<DT>::Acc (&acc)[4][4], c
   }
 }
 
+// Part [P0, P1) of mfma_slice: fp32 k-steps P0..P1-1 of the slice (each
+// lane's chunk holds four consecutive k values); other types the MFMAs of
+// centroid blocks P0..P1-1.
+template <int DT, int P0, int P1>
+__device__ __forceinline__ void mfma_part(typename Fmt<DT>::Acc (&acc)[4][4], const u32x4 (&a)[4],
+                                          const u32x4 (&b)[4]) {
+  if constexpr (DT == 0) {
+#pragma unroll
+    for (int q = P0; q < P1; ++q)
+#pragma unroll
+      for (int mb = 0; mb < 4; ++mb)
+#pragma unroll
+        for (int nb = 0; nb < 4; ++nb)
+          acc[mb][nb] = __builtin_amdgcn_mfma_f32_16x16x4f32(
+              __uint_as_float(a[mb][q]), __uint_as_float(b[nb][q]), acc[mb][nb], 0, 0, 0);
+  } else {
+#pragma unroll
+    for (int mb = P0; mb < P1; ++mb)
+#pragma unroll
+      for (int nb = 0; nb < 4; ++nb) {
+        if constexpr (kIntSearch<DT>)
+          acc[mb][nb] = __builtin_amdgcn_mfma_i32_16x16x64_i8(__builtin_bit_cast(i32x4, a[mb]),
+                                                              __builtin_bit_cast(i32x4, b[nb]),
+                                                              acc[mb][nb], 0, 0, 0);
+        else if constexpr (DT == 1)
+          acc[mb][nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+              __builtin_bit_cast(bf16x8, a[mb]), __builtin_bit_cast(bf16x8, b[nb]), acc[mb][nb], 0,
+              0, 0);
+        else
+          acc[mb][nb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, a[mb]),
+                                                               __builtin_bit_cast(f16x8, b[nb]),
+                                                               acc[mb][nb], 0, 0, 0);
+      }
+  }
+}
+
 // Bias tile of a panel: lane-group g holds centroids 4 g .. 4 g + 3 of each
 // 16-row block. fp32 / bf16: -|c|^2/2, -inf past k (the accumulator's initial
 // value). int8: -|q|^2 (added at the fold; centroids past k are skipped).
@@ -683,30 +719,29 @@ __global__ __launch_bounds__(kThreads, 1) void assign_ring_kernel(
   EMK_WAIT_VMCNT(kLoadsPerWave);
   lds_barrier();
 
-  int panel = 0, s = 0, cslot = 0;
-  for (int t = 0; t < total; ++t) {
-    const bool last_s = s == nst - 1;
-    const bool more_p = panel + 1 < npan;
-    if (last_s && more_p) load_bias(panel + 1);  // before the ring loads: retired by the stage wait
-    unsigned char* cur = ring + cslot * kStageBytes;
-    if (ragged && last_s) {
-      // zero the chunks past the row end (points and centroids)
-      const u32x4 z = {0u, 0u, 0u, 0u};
-      for (int q = tid; q < kRowsStage * kChunks; q += kThreads) {
-        const int r = q >> 3, c = q & 7;
-        if (s * EPS + c * EPV >= d) *reinterpret_cast<u32x4*>(cur + swz(r, c)) = z;
+  if constexpr (DT == 3) {
+    int panel = 0, s = 0, cslot = 0;
+    for (int t = 0; t < total; ++t) {
+      const bool last_s = s == nst - 1;
+      const bool more_p = panel + 1 < npan;
+      if (last_s && more_p) load_bias(panel + 1);  // before the ring loads: retired by the stage wait
+      unsigned char* cur = ring + cslot * kStageBytes;
+      if (ragged && last_s) {
+        const u32x4 z = {0u, 0u, 0u, 0u};
+        for (int q = tid; q < kRowsStage * kChunks; q += kThreads) {
+          const int r = q >> 3, c = q & 7;
+          if (s * EPS + c * EPV >= d) *reinterpret_cast<u32x4*>(cur + swz(r, c)) = z;
+        }
+        lds_barrier();
       }
-      lds_barrier();
-    }
-    if (panel == 0) {
-      const bool in = s * EPS + ch * EPV < d;
+      if (panel == 0) {
+        const bool in = s * EPS + ch * EPV < d;
 #pragma unroll
-      for (int i = 0; i < kXR; ++i)
-        if (in)
-          xpart[i] += sumsq16<DT>(point_chunk<DT>(
-              *reinterpret_cast<const u32x4*>(cur + swz(rb + kRowsPerPass * i, ch))));
-    }
-    if constexpr (DT == 3) {
+        for (int i = 0; i < kXR; ++i)
+          if (in)
+            xpart[i] += sumsq16<DT>(point_chunk<DT>(
+                *reinterpret_cast<const u32x4*>(cur + swz(rb + kRowsPerPass * i, ch))));
+      }
       static_assert(kSlab == 128, "one 16x16x128 FP8 MFMA per stage");
       u32x4 a[2][4], b[2][4];
 #pragma unroll
@@ -724,43 +759,102 @@ __global__ __launch_bounds__(kThreads, 1) void assign_ring_kernel(
       mfma_stage_f8(acc, a, b);
       // the loads of stage t + 2, issued while the matrix core works on this stage
       issue_next();
-    } else {
+      if (last_s) {
+        fold_panel<DT>(acc, bcur, panel * kTC + wm * 64, k, lane, best, bidx);
+        if (more_p) {
 #pragma unroll
-      for (int kk = 0; kk < kSlab / 64; ++kk) {
-        const int pc = swz_pos(lane & 15, kk * 4 + (lane >> 4)) << 4;  // rows are 16-aligned + lane % 16
-        u32x4 a[4], b[4];
-#pragma unroll
-        for (int mb = 0; mb < 4; ++mb)
-          a[mb] = *reinterpret_cast<const u32x4*>(
-              cur + (kTP + wm * 64 + mb * 16 + (lane & 15)) * kSlab + pc);
-#pragma unroll
-        for (int nb = 0; nb < 4; ++nb)
-          b[nb] = point_chunk<DT>(
-              *reinterpret_cast<const u32x4*>(cur + (wn * 64 + nb * 16 + (lane & 15)) * kSlab + pc));
-        mfma_slice<DT>(acc, a, b);
-        // the loads of stage t + 2, issued while the matrix core works on this
-        // stage's first half
-        if (kk == 0) issue_next();
+          for (int mb = 0; mb < 4; ++mb) bcur[mb] = bnext[mb];
+          init_tile<DT>(acc, bcur);
+        }
+      }
+      // the next stage's loads have landed in LDS for this wave, then for all
+      EMK_WAIT_VMCNT(kLoadsPerWave);
+      lds_barrier();
+      cslot = cslot + 1 == kRing ? 0 : cslot + 1;
+      if (last_s) {
+        s = 0;
+        ++panel;
+      } else {
+        ++s;
       }
     }
-    if (last_s) {
-      // panel complete: fold it into the running best (centroids in increasing order)
-      fold_panel<DT>(acc, bcur, panel * kTC + wm * 64, k, lane, best, bidx);
-      if (more_p) {
+  } else {
+    // Each stage: the MFMAs of its first 64-byte slice, the loads of stage
+    // t + 2, then part of the second slice's MFMAs before the stage's wait and
+    // barrier and the rest after it, while the fragments of the next stage's
+    // first slice are read (they cover that read's latency, which otherwise
+    // idles every wave at once after each barrier). The panel's fold follows
+    // its last MFMAs.
+    const int pc0 = swz_pos(lane & 15, lane >> 4) << 4;  // rows are 16-aligned + lane % 16
+    const int pc1 = swz_pos(lane & 15, 4 + (lane >> 4)) << 4;
+    auto read_frags = [&](const unsigned char* base, int pc, u32x4 (&a)[4], u32x4 (&b)[4]) {
 #pragma unroll
-        for (int mb = 0; mb < 4; ++mb) bcur[mb] = bnext[mb];
-        init_tile<DT>(acc, bcur);
+      for (int mb = 0; mb < 4; ++mb)
+        a[mb] = *reinterpret_cast<const u32x4*>(base + (kTP + wm * 64 + mb * 16 + (lane & 15)) * kSlab + pc);
+#pragma unroll
+      for (int nb = 0; nb < 4; ++nb)
+        b[nb] = point_chunk<DT>(
+            *reinterpret_cast<const u32x4*>(base + (wn * 64 + nb * 16 + (lane & 15)) * kSlab + pc));
+    };
+    static_assert(kSlab == 128, "two 64-byte slices per stage");
+    // MFMAs of the second slice run before the barrier: fp32 k-steps 0..2 of
+    // 4 (48 of 64); the others none of their 16
+    constexpr int kSplit = DT == 0 ? 3 : 0;
+    u32x4 fa0[4], fb0[4], fa1[4], fb1[4];
+    read_frags(ring, pc0, fa0, fb0);
+    int panel = 0, s = 0, cslot = 0;
+    for (int t = 0; t < total; ++t) {
+      const bool last_s = s == nst - 1;
+      const bool more_p = panel + 1 < npan;
+      if (last_s && more_p) load_bias(panel + 1);  // before the ring loads: retired by the stage wait
+      unsigned char* cur = ring + cslot * kStageBytes;
+      if (ragged && last_s) {
+        // zero the chunks past the row end (points and centroids), then read
+        // the first slice again
+        const u32x4 z = {0u, 0u, 0u, 0u};
+        for (int q = tid; q < kRowsStage * kChunks; q += kThreads) {
+          const int r = q >> 3, c = q & 7;
+          if (s * EPS + c * EPV >= d) *reinterpret_cast<u32x4*>(cur + swz(r, c)) = z;
+        }
+        lds_barrier();
+        read_frags(cur, pc0, fa0, fb0);
       }
-    }
-    // the next stage's loads have landed in LDS for this wave, then for all
-    EMK_WAIT_VMCNT(kLoadsPerWave);
-    lds_barrier();
-    cslot = cslot + 1 == kRing ? 0 : cslot + 1;
-    if (last_s) {
-      s = 0;
-      ++panel;
-    } else {
-      ++s;
+      if (panel == 0) {
+        const bool in = s * EPS + ch * EPV < d;
+#pragma unroll
+        for (int i = 0; i < kXR; ++i)
+          if (in)
+            xpart[i] += sumsq16<DT>(point_chunk<DT>(
+                *reinterpret_cast<const u32x4*>(cur + swz(rb + kRowsPerPass * i, ch))));
+      }
+      read_frags(cur, pc1, fa1, fb1);
+      mfma_slice<DT>(acc, fa0, fb0);
+      // the loads of stage t + 2, into the buffer of stage t - 1 (its reads
+      // all ended before the barrier that opened this stage)
+      issue_next();
+      mfma_part<DT, 0, kSplit>(acc, fa1, fb1);
+      // the next stage's loads have landed in LDS for this wave, then for all
+      __builtin_amdgcn_sched_barrier(0);
+      EMK_WAIT_VMCNT(kLoadsPerWave);
+      __builtin_amdgcn_sched_barrier(0);
+      lds_barrier();
+      __builtin_amdgcn_sched_barrier(0);
+      cslot = cslot + 1 == kRing ? 0 : cslot + 1;
+      if (t + 1 < total) read_frags(ring + cslot * kStageBytes, pc0, fa0, fb0);
+      mfma_part<DT, kSplit, 4>(acc, fa1, fb1);
+      if (last_s) {
+        // panel complete: fold it into the running best (centroids in increasing order)
+        fold_panel<DT>(acc, bcur, panel * kTC + wm * 64, k, lane, best, bidx);
+        if (more_p) {
+#pragma unroll
+          for (int mb = 0; mb < 4; ++mb) bcur[mb] = bnext[mb];
+          init_tile<DT>(acc, bcur);
+        }
+        s = 0;
+        ++panel;
+      } else {
+        ++s;
+      }
     }
   }
 
