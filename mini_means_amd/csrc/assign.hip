@@ -332,9 +332,22 @@ __device__ __forceinline__ void fold_panel(const typename Fmt<DT>::Acc (&acc)[4]
           sc[4 * mb + v] = acc[mb][nb][v];
         }
       }
-    Sc m = sc[0];
+    // the largest of the 16: integers by compare and select, floats in a
+    // tree of max3 (eight instructions instead of thirty; the scores are
+    // finite or -inf, and equal values give the same index below)
+    Sc m;
+    if constexpr (kIntSearch<DT>) {
+      m = sc[0];
 #pragma unroll
-    for (int q = 1; q < 16; ++q) m = sc[q] > m ? sc[q] : m;
+      for (int q = 1; q < 16; ++q) m = sc[q] > m ? sc[q] : m;
+    } else {
+      Sc t[8];
+#pragma unroll
+      for (int q = 0; q < 5; ++q) t[q] = __builtin_fmaxf(__builtin_fmaxf(sc[3 * q], sc[3 * q + 1]), sc[3 * q + 2]);
+      t[5] = __builtin_fmaxf(__builtin_fmaxf(t[0], t[1]), t[2]);
+      t[6] = __builtin_fmaxf(__builtin_fmaxf(t[3], t[4]), sc[15]);
+      m = __builtin_fmaxf(t[5], t[6]);
+    }
     if (m > best[nb]) {
       int jb = -1;
 #pragma unroll
