@@ -477,7 +477,7 @@ struct emeans_model {
                       rv_nheads, counters, count_only ? nullptr : dlog,
                       count_only ? 0 : log_cap, count_only ? 1 : 0, sph ? 1 : 0, wlive,
                       hf ? 1 : 0, slow_started ? N2 : nullptr, slow_started ? S2 : nullptr,
-                      u8 ? 1 : 0, sshift, sscale};
+                      u8 ? 1 : 0, sshift, sscale, r.lloyd ? 1 : 0};
   }
 
   // Recipe, options and workspace; C = external (the caller's buffer) or own.
@@ -681,7 +681,9 @@ struct emeans_model {
                         last ? LS : nullptr, sph, beta, b2, slow ? N2 : nullptr,
                         slow ? S2 : nullptr, sshift, sscale, st);
     }));
-    if (r.thr > 0.0 && (t + 1) % kReviveEvery == 0) {
+    // Lloyd: clusters left without a row are split off donors after every
+    // update but the last (the last one's means are the result)
+    if ((r.thr > 0.0 && (t + 1) % kReviveEvery == 0) || (r.lloyd && t + 1 < r.S)) {
       const ReviveArgs ra = revive_args(false);
       HIP_RET(timed(kRevive, [&] { return launch_revive(ra, st); }));
     }
@@ -712,7 +714,7 @@ struct emeans_model {
   int finish(float* out_C, emeans_stats* stats, bool closing) {
     double host_stat[4 * EMEANS_MAX_PASSES];
     int64_t host_counters[4] = {0, 0, 0, 0};
-    if (r.thr > 0.0) {
+    if (r.thr > 0.0 || r.lloyd) {
       const ReviveArgs ra = revive_args(true);
       HIP_RET(launch_revive(ra, st));
     }
@@ -756,7 +758,7 @@ struct emeans_model {
     }
     stats->n_splits = host_counters[0];
     stats->n_logged = host_counters[1] < log_cap ? host_counters[1] : log_cap;
-    stats->dead_at_end = r.thr > 0.0 ? host_counters[2] : 0;
+    stats->dead_at_end = (r.thr > 0.0 || r.lloyd) ? host_counters[2] : 0;
     if (profile) {
       double cls_ms[kClasses] = {};
       for (const Span& sp : spans) {

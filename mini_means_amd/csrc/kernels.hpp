@@ -180,6 +180,7 @@ struct ReviveArgs {
   int cq_u8;          // Cq holds shifted uint8 codes
   const float* sshift;  // the search copy rounds (c - sshift) * sscale (launch_prep)
   float sscale;
+  int empty_only;     // Lloyd: dead = clusters with no row (N < 0.5) instead of N < thr * mean
 };
 // Dead-cluster check and donor draws (one workgroup), then the splits of the
 // running sums, one wave per donor chain.

@@ -900,7 +900,8 @@ __global__ __launch_bounds__(256) void slow_final_kernel(int k, int d, const flo
 }
 
 // Dead-cluster revival. Mean running count m = sum N / k (fp64); dead set
-// D = {j : N_j < thr * m} in index order. For each dead j in turn: u from
+// D = {j : N_j < thr * m} in index order (Lloyd's empty-cluster split:
+// D = {j : N_j = 0}, the counts being whole numbers). For each dead j in turn: u from
 // Philox, donor i = first live index whose fp64 prefix sum of N over live
 // clusters exceeds u * (sum of live N); the donor keeps half of its count and
 // sum, cluster j takes the other half, and both sums are perturbed by
@@ -1049,7 +1050,7 @@ __global__ __launch_bounds__(1024) void revive_kernel(ReviveArgs A) {
   double loc = 0.0;
   for (int j = tid; j < k; j += 1024) loc += (double)A.N[j];
   const double total = block_sum<double, 1024>(loc, dtmp);
-  const double th = A.thr * (total / (double)k);
+  const double th = A.empty_only ? 0.5 : A.thr * (total / (double)k);
 
   const int per = (k + 1023) / 1024;
   const int j0 = min(k, tid * per), j1 = min(k, j0 + per);
@@ -1373,7 +1374,7 @@ __global__ __launch_bounds__(1024) void revive_spec_kernel(ReviveArgs A) {
 #pragma unroll
   for (int e = 0; e < RV; ++e) loc += (double)nv[e];
   const double total = block_sum<double, 1024>(loc, dtmp);
-  const double th = A.thr * (total / (double)k);
+  const double th = A.empty_only ? 0.5 : A.thr * (total / (double)k);
   unsigned deadm = 0;
   int cnt = 0;
 #pragma unroll

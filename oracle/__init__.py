@@ -606,10 +606,13 @@ def init_rows(n: int, k: int, seed: int) -> np.ndarray:
 
 
 def _revive(t: int, seed: int, thr: float, N: np.ndarray, S: np.ndarray, C: np.ndarray,
-            log: list, spherical: bool = False) -> None:
+            log: list, spherical: bool = False, empty_only: bool = False) -> None:
     k, d = S.shape
-    total = float(np.sum(N.astype(np.float64)))
-    th = thr * (total / k)
+    if empty_only:
+        th = 0.5  # Lloyd: the clusters that received no row (N holds whole row counts)
+    else:
+        total = float(np.sum(N.astype(np.float64)))
+        th = thr * (total / k)
     dead = np.nonzero(N.astype(np.float64) < th)[0]
     if len(dead) == 0:
         return
@@ -800,9 +803,20 @@ def train(X: np.ndarray, k: int, T: float, seed: int = 1234, *, batch_law: int =
 def lloyd(X: np.ndarray, k: int, iters: int, seed: int = 1234, nthreads: int = 0,
           progress: Optional[Callable[[int, float], None]] = None,
           labels_for_step: Optional[Callable[[int, np.ndarray], np.ndarray]] = None,
-          check_hook: Optional[Callable[[dict], None]] = None):
-    """Plain Lloyd from the same k starting rows: assign all rows, move each
-    centroid to the exact mean of its rows (a centroid with no row stays).
+          check_hook: Optional[Callable[[dict], None]] = None, split_empty: bool = True,
+          split_log: Optional[list] = None):
+    """Lloyd's algorithm from the same k starting rows (blog, Lloyd section,
+    run as Faiss's k-means): assign all rows, move each centroid to the exact
+    mean of its rows. After every update but the last, each centroid that
+    received no row is split off a donor, as Faiss does with empty clusters:
+    the revival step of train with the dead set {j : n_j = 0} and the step
+    number i of the iteration, on N = the row counts and S = the row sums in
+    fp32 (donors drawn one by one in index order, in proportion to N; each
+    donor's count and sum halved between the two, the halves perturbed by
+    -/+ 2^-10 per coordinate). The last update's means are the result; a
+    centroid that never received a row keeps its value. split_empty=False
+    gives plain Lloyd (a centroid with no row stays where it is); split_log
+    receives (iteration, empty cluster, donor).
     Returns the centroids after `iters` updates and the MSE seen at each assign.
 
     labels_for_step(i, None) may supply the labels of iteration i from
@@ -828,6 +842,11 @@ def lloyd(X: np.ndarray, k: int, iters: int, seed: int = 1234, nthreads: int = 0
         counts, sums = group(X, None, lab, k)
         pos = counts > 0
         C[pos] = (sums[pos] / counts[pos].astype(np.float64)[:, None]).astype(np.float32)
+        if split_empty and i < iters - 1 and not np.all(pos):
+            N = counts.astype(np.float32)
+            S = sums.astype(np.float32)
+            _revive(i, seed, 0.0, N, S, C, split_log if split_log is not None else [],
+                    empty_only=True)
     return C, hist
 
 

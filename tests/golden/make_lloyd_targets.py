@@ -2,7 +2,9 @@
 
 Lloyd's algorithm with the Faiss default of 25 iterations (blog "k-means Reads
 Your Data 25 Times", section on Lloyd's algorithm and Faiss's niter = 25),
-from the same k starting rows as e-means with the same seed. The result file
+from the same k starting rows as e-means with the same seed, splitting the
+clusters an iteration leaves without rows as Faiss's k-means does (oracle.lloyd;
+the splits are recorded). The result file
 tests/golden/lloyd25_<workload>.json holds the training MSE after every
 assignment and the held-out MSE of the final centroids; the benchmark's
 time-to-target measurement reads the held-out value.
@@ -32,13 +34,17 @@ def main(name: str, threads: int = 0, iters: int = 25, seed: int = 1234) -> None
     def progress(i, m):
         print(f"[{name}] iter {i}/{iters} train mse {m:.6f} ({time.time() - t0:.0f}s)", flush=True)
 
-    C, hist = oracle.lloyd(X, W["k"], iters, seed, nthreads=threads, progress=progress)
+    splits = []
+    C, hist = oracle.lloyd(X, W["k"], iters, seed, nthreads=threads, progress=progress,
+                           split_log=splits)
     train_mse = oracle.mse(X, C, nthreads=threads)
     held_mse = oracle.mse(Xh, C, nthreads=threads)
     out = dict(workload=name, n=W["n"], d=W["d"], k=W["k"], iters=iters, seed=seed,
                init="first k entries of the init permutation (same as e-means)",
                train_mse_history=hist, train_mse=train_mse, heldout_rows=W["heldout"],
-               heldout_mse=held_mse, cpu_seconds=time.time() - t0,
+               heldout_mse=held_mse, empty_cluster_splits=len(splits),
+               splits_per_iteration=[sum(1 for t, _, _ in splits if t == i) for i in range(iters)],
+               cpu_seconds=time.time() - t0,
                threads=threads or os.cpu_count(),
                source="oracle.lloyd (CPU, fp64), written by tests/golden/make_lloyd_targets.py")
     path = os.path.join(HERE, f"lloyd25_{name}.json")

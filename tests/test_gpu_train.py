@@ -120,7 +120,8 @@ LLOYD = [("tiny", "tiny", 10_000, 16, 64, 8), ("emb-small", "embedding", 12_000,
 @pytest.mark.parametrize("name,gen,n,d,k,iters", LLOYD, ids=[c[0] for c in LLOYD])
 def test_lloyd_mode_lockstep(mm, name, gen, n, d, k, iters):
     """GPU Lloyd mode against the oracle's Lloyd, adopting the band-checked
-    GPU labels every iteration: per-iteration MSE, final counts and centroids."""
+    GPU labels every iteration: per-iteration MSE, the empty-cluster splits
+    (identical decisions), final counts and centroids."""
     from parity import check_labels
     X = datagen.make(gen, n, d, seed=23)
     out = _gpu_train(mm, X, k, float(iters), 1234, lloyd=True)
@@ -133,8 +134,9 @@ def test_lloyd_mode_lockstep(mm, name, gen, n, d, k, iters):
                      chk["given_dist"], what=f"lloyd {name} iteration {chk['t']}", C32=C32)
         last["labels"] = chk["given"]
 
+    splits = []
     C, hist = oracle.lloyd(X, k, iters, 1234, labels_for_step=lambda i, _: trace[i],
-                           check_hook=hook)
+                           check_hook=hook, split_log=splits)
     np.testing.assert_allclose(out.stats["obj"], hist, rtol=1e-4, atol=obj_atol(X))
     counts = np.bincount(last["labels"], minlength=k).astype(np.float32)
     assert np.array_equal(out.counts.cpu().numpy(), counts)
@@ -142,7 +144,11 @@ def test_lloyd_mode_lockstep(mm, name, gen, n, d, k, iters):
     tol = 1e-2 if X.dtype == np.uint16 else 1e-4
     err = rel_l2(out.centroids.cpu().numpy(), C)
     assert err <= tol, f"centroids rel L2 {err:.3e}"
-    assert out.stats["n_splits"] == 0
+    assert out.split_log == [tuple(v) for v in splits]
+    assert out.stats["n_splits"] == len(splits)
+    assert out.stats["dead_at_end"] == int(np.sum(counts == 0))
+    if name == "emb-small":
+        assert len(splits) > 10  # this case does leave clusters empty
 
 
 # Revival draws at larger k, each with thousands of revivals: the speculated

@@ -978,3 +978,94 @@ def test_fp8_converter_on_grid_data_is_exact():
     r1 = oracle.train(Z, 16, 2.0, seed=1, bf16_search=True)
     r2 = oracle.train(Z, 16, 2.0, seed=1, search="bf16")
     assert np.array_equal(r1.labels, r2.labels) and np.array_equal(r1.centroids, r2.centroids)
+
+
+# ---------------------------------------------------------------------------
+# Lloyd's empty-cluster split (Faiss's k-means splits a cluster left without
+# rows off a large one; reading R9)
+
+
+def test_lloyd_without_empty_clusters_is_plain_lloyd():
+    """When no cluster is ever left without rows the split never fires: the
+    result equals plain Lloyd, which a brute-force loop over scipy's cdist
+    reproduces (nearest centroid, lowest index on ties, exact means)."""
+    X = datagen.tiny(n=4000, d=16, seed=5)
+    k, iters = 64, 6
+    log = []
+    C, hist = oracle.lloyd(X, k, iters, seed=3, split_log=log)
+    Cp, hp = oracle.lloyd(X, k, iters, seed=3, split_empty=False)
+    assert log == []
+    assert np.array_equal(C, Cp) and hist == hp
+    W = X[oracle.init_rows(len(X), k, 3)].astype(np.float64)
+    for _ in range(iters):
+        lab = np.argmin(cdist(X.astype(np.float64), W, "sqeuclidean"), axis=1)
+        assert np.bincount(lab, minlength=k).min() > 0
+        for j in range(k):
+            W[j] = X[lab == j].astype(np.float64).mean(axis=0)
+    np.testing.assert_allclose(C, W, rtol=0, atol=2e-6)
+
+
+def test_lloyd_splits_every_empty_cluster_off_the_live_ones():
+    """Six copies of one row and k = 3: every starting centroid is that row,
+    the first takes all six rows (lowest index on ties) and the other two are
+    empty. Both are refilled from the only live cluster, one after the other
+    in index order, so the donor's half is halved again; the second iteration
+    then gives all rows to the nearest of the three split centroids and that
+    one returns to the row itself. The last iteration is not split."""
+    a = np.array([3.0, -1.5, 0.25, 8.0, 2.0], dtype=np.float32)
+    X = np.tile(a, (6, 1))
+    d = len(a)
+    log = []
+    C, hist = oracle.lloyd(X, 3, 2, seed=7, split_log=log)
+    assert [(t, j) for t, j, _ in log] == [(0, 1), (0, 2)]
+    assert [i for _, _, i in log] == [0, 0]
+    e = 2.0 ** -10
+    s1 = oracle.split_signs(7, 0, 1, d).astype(np.float64)
+    s2 = oracle.split_signs(7, 0, 2, d).astype(np.float64)
+    a64 = a.astype(np.float64)
+    after = np.stack([a64 * (1 - e * s1) * (1 - e * s2), a64 * (1 + e * s1),
+                      a64 * (1 - e * s1) * (1 + e * s2)])
+    win = int(np.argmin(((after - a64) ** 2).sum(axis=1)))
+    want = after.copy()
+    want[win] = a64
+    np.testing.assert_allclose(C, want, rtol=1e-6, atol=0)
+    assert hist[0] == 0.0 and hist[1] > 0.0
+
+
+def test_lloyd_split_keeps_the_donor_mean_and_lowers_the_loss():
+    """On the embedding-like mixture (Zipf weights) plain Lloyd leaves
+    clusters empty; here every row also appears twice, so that starting
+    centroids drawn from both copies of a row leave the second one empty from
+    the first iteration on. The clusters split after the first iteration are
+    exactly those the brute-force assignment (scipy's cdist, lowest index on
+    ties) leaves without rows, in index order, each refilled from a cluster
+    that has rows; a donor split once sits with its new cluster symmetrically
+    about its mean, (c_i + c_j) / 2 = mean_i; and with the splits the loss
+    ends lower."""
+    X0 = datagen.make("embedding", 6_000, 768, seed=23)
+    X = np.concatenate([X0, X0])
+    k = 256
+    W = X[oracle.init_rows(len(X), k, 1234)].astype(np.float64)
+    lab0 = np.argmin(cdist(X.astype(np.float64), W, "sqeuclidean"), axis=1).astype(np.int32)
+    cnt = np.bincount(lab0, minlength=k)
+    seen = {}
+    log = []
+    oracle.lloyd(X, k, 2, 1234, split_log=log,
+                 labels_for_step=lambda i, _: lab0 if i == 0 else np.zeros(len(X), np.int32),
+                 check_hook=lambda chk: seen.__setitem__(chk["t"], chk["C32"].copy()))
+    assert all(t == 0 for t, _, _ in log)
+    assert [j for _, j, _ in log] == list(np.nonzero(cnt == 0)[0]) and len(log) > 0
+    donors = [i for _, _, i in log]
+    assert all(cnt[i] > 0 for i in donors)
+    Cs = seen[1].astype(np.float64)  # the centroids the second iteration searched
+    checked = 0
+    for _, j, i in log:
+        if donors.count(i) == 1:
+            mean_i = X[lab0 == i].astype(np.float64).mean(axis=0)
+            np.testing.assert_allclose((Cs[i] + Cs[j]) / 2, mean_i, rtol=0, atol=1e-6)
+            checked += 1
+    assert checked > 0
+    iters = 4
+    C, _ = oracle.lloyd(X, k, iters, 1234)
+    Cp, _ = oracle.lloyd(X, k, iters, 1234, split_empty=False)
+    assert oracle.mse(X, C) < oracle.mse(X, Cp)
