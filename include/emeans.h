@@ -139,13 +139,16 @@ typedef struct emeans_opts {
                                  emeans_assign: labels by the highest dot product with
                                  C as given, dists[i] = that similarity. fp32, bf16
                                  or fp16 X only (EINVAL with int8, uint8 or FP8 X). */
-  int32_t lloyd;              /* 1: plain Lloyd iterations instead of e-means (the
-                                 baseline of the blog's Lloyd section, the loss
-                                 e-means is timed against): each of the T passes
-                                 (T a whole number) is one step over all n rows in
-                                 row order with alpha = 1, so every centroid becomes
-                                 the exact mean of its rows and a centroid with no
-                                 row stays where it is; no revival. batch_size,
+  int32_t lloyd;              /* 1: Lloyd iterations instead of e-means (the
+                                 baseline of the blog's Lloyd section, Faiss's
+                                 k-means, the loss e-means is timed against): each
+                                 of the T passes (T a whole number) is one step over
+                                 all n rows in row order with alpha = 1, so every
+                                 centroid becomes the exact mean of its rows; after
+                                 every pass but the last, the centroids left without
+                                 a row are split off donors drawn in proportion to
+                                 the row counts (the revival split, as Faiss
+                                 refills empty clusters; no other revival). batch_size,
                                  alpha0 and unused_threshold are ignored; stats->obj
                                  holds the mean squared distance of every iteration's
                                  assignment. n < 2^31 (the 2^24 batch limit does not

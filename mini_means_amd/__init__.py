@@ -235,8 +235,10 @@ def train(X, k: int, T: float = 5.0, seed: int = 1234, *, batch_law="auto", batc
           bf16_search: bool = False, spherical: bool = False, lloyd: bool = False,
           slow_ema: float = 0.0, search=None, search_shift=None, search_scale=None,
           stream=None) -> TrainOutput:
-    """e-means training of X (n x d tensor on the GPU). lloyd: plain Lloyd
-    iterations instead (T of them, every row each time, alpha = 1).
+    """e-means training of X (n x d tensor on the GPU). lloyd: Lloyd
+    iterations instead (T of them, every row each time, alpha = 1; clusters
+    left without rows are split off donors after every iteration but the
+    last, as Faiss's k-means does).
     slow_ema = kappa >= 1: also the centroids of a second, slower EMA over the
     last pass (rate alpha_t / kappa), for unseen data (out.slow_centroids).
     search = 'bf16' | 'f16' | 'f8' with search_shift / search_scale: fp32 rows
