@@ -98,3 +98,32 @@ def test_freerun_final_mse_matches_oracle(mm, name):
     assert rel_m <= tol, (m_gpu, g["train_mse"])
     assert rel_h <= tol, (h_gpu, g["heldout_mse"])
     np.testing.assert_allclose(st["obj"][-1], g["obj_per_pass"][-1], rtol=tol)
+
+
+@pytest.mark.parametrize("name", ["embedding", "deep", "sift"])
+def test_gpu_lloyd25_matches_oracle_target(mm, name):
+    """The baseline e-means is timed against: 25 Lloyd iterations on the GPU
+    (its own labels, Faiss-style splits of empty clusters) end at the
+    held-out MSE of the oracle's own Lloyd-25 run from the same starting rows
+    (tests/golden/lloyd25_<workload>.json), to the same relative bar as the
+    free run, and split as many empty clusters."""
+    import torch
+    with open(os.path.join(GOLDEN, f"lloyd25_{name}.json")) as f:
+        g = json.load(f)
+    W = datagen.WORKLOADS[name]
+    assert (g["n"], g["d"], g["k"], g["iters"], g["seed"]) == (W["n"], W["d"], W["k"], 25, 1234)
+    X = datagen.make(W["gen"], W["n"], W["d"])
+    Xh = datagen.make(W["gen"], W["heldout"], W["d"], split=1)
+    t0 = time.time()
+    out = mm.train(torch.from_numpy(X).cuda(), W["k"], 25.0, 1234, lloyd=True)
+    torch.cuda.synchronize()
+    log(f"lloyd25 {name}: GPU {time.time() - t0:.2f}s, {out.stats['n_splits']} splits "
+        f"(oracle {g.get('empty_cluster_splits', 'not recorded')})")
+    h_gpu = oracle.mse(Xh, out.centroids.cpu().numpy())
+    rel = abs(h_gpu - g["heldout_mse"]) / g["heldout_mse"]
+    log(f"lloyd25 {name}: held-out gpu {h_gpu:.6f} oracle {g['heldout_mse']:.6f} (rel {rel:.2e})")
+    assert rel <= MSE_TOL[name]
+    np.testing.assert_allclose(out.stats["obj"], g["train_mse_history"], rtol=MSE_TOL[name])
+    if "empty_cluster_splits" in g:
+        ns = g["empty_cluster_splits"]
+        assert abs(out.stats["n_splits"] - ns) <= max(5, 0.1 * ns)
