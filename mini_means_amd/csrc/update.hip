@@ -813,12 +813,17 @@ __global__ __launch_bounds__(256) void group_span_kernel(const unsigned char* __
 // 4 fp16 (Chat), 5 shifted uint8 (Cq)
 template <int SF>
 __global__ __launch_bounds__(256) void ema_kernel(int k, int d, float a, float b,
-                                                  int32_t* counts, float* s_acc, float* N,
-                                                  float* S, float* C, float* bias,
-                                                  uint16_t* Chat, int8_t* Cq, uint8_t* Cf,
-                                                  int32_t* pass_counts, float* LS, int sph,
-                                                  float beta, float b2, float* N2, float* S2,
-                                                  const float* sshift, float sscale) {
+                                                  int32_t* __restrict__ counts,
+                                                  float* __restrict__ s_acc, float* __restrict__ N,
+                                                  float* __restrict__ S, float* __restrict__ C,
+                                                  float* __restrict__ bias,
+                                                  uint16_t* __restrict__ Chat,
+                                                  int8_t* __restrict__ Cq, uint8_t* __restrict__ Cf,
+                                                  int32_t* __restrict__ pass_counts,
+                                                  float* __restrict__ LS, int sph, float beta,
+                                                  float b2, float* __restrict__ N2,
+                                                  float* __restrict__ S2,
+                                                  const float* __restrict__ sshift, float sscale) {
   const int j = blockIdx.x * 4 + (threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
   if (j >= k) return;
@@ -827,40 +832,62 @@ __global__ __launch_bounds__(256) void ema_kernel(int k, int d, float a, float b
   float nrm = 0.0f;
   int nq = 0;  // |q|^2 of the int8 codes, exact
   const size_t base = (size_t)j * d;
-  for (int e = lane; e < d; e += 64) {
-    const size_t idx = base + e;
-    float s = 0.0f;
-    if (n) {
-      s = s_acc[idx];
-      s_acc[idx] = 0.0f;
+  // G elements per lane at a time: all their loads first, then the
+  // arithmetic and the stores, so that a wave waits for memory once per G
+  // elements instead of once per element
+  constexpr int G = 8;
+  for (int e0 = lane; e0 < d; e0 += 64 * G) {
+    float sv[G], Sv[G], S2v[G], Cv[G], LSv[G];
+#pragma unroll
+    for (int g = 0; g < G; ++g) {
+      const int e = e0 + 64 * g;
+      sv[g] = 0.0f;
+      S2v[g] = Cv[g] = LSv[g] = 0.0f;
+      Sv[g] = 0.0f;
+      if (e < d) {
+        const size_t idx = base + e;
+        if (n) sv[g] = s_acc[idx];
+        Sv[g] = S[idx];
+        if (S2) S2v[g] = S2[idx];
+        if (!(Nn > 0.0f)) Cv[g] = C[idx];
+        if (LS && n) LSv[g] = LS[idx];
+      }
     }
-    const float Sv = __fadd_rn(__fmul_rn(b, S[idx]), __fmul_rn(a, s));
-    S[idx] = Sv;
-    if (S2) S2[idx] = __fadd_rn(__fmul_rn(b2, S2[idx]), __fmul_rn(beta, s));
-    float c;
-    if (Nn > 0.0f) {
-      c = __fdiv_rn(Sv, Nn);
-      C[idx] = c;
-    } else {
-      c = C[idx];
+#pragma unroll
+    for (int g = 0; g < G; ++g) {
+      const int e = e0 + 64 * g;
+      if (e >= d) continue;
+      const size_t idx = base + e;
+      const float s = sv[g];
+      if (n) s_acc[idx] = 0.0f;
+      const float Snew = __fadd_rn(__fmul_rn(b, Sv[g]), __fmul_rn(a, s));
+      S[idx] = Snew;
+      if (S2) S2[idx] = __fadd_rn(__fmul_rn(b2, S2v[g]), __fmul_rn(beta, s));
+      float c;
+      if (Nn > 0.0f) {
+        c = __fdiv_rn(Snew, Nn);
+        C[idx] = c;
+      } else {
+        c = Cv[g];
+      }
+      if (LS && n) LS[idx] = LSv[g] + s;
+      if (sph) continue;  // rescaled (and rounded to Chat) below, once the norm is known
+      if constexpr (SF == 1 || SF == 4) {
+        const uint16_t h = to_half_rne(conv_in(c, sshift, sscale, e), SF == 4);
+        Chat[idx] = h;
+        c = half_to_f32(h, SF == 4);
+      } else if constexpr (SF == 2 || SF == 5) {
+        const int8_t q = to_code(c, SF == 5);
+        Cq[idx] = q;
+        nq += (int)q * (int)q;
+        continue;
+      } else if constexpr (SF == 3) {
+        const uint32_t q = f32_to_e4m3(conv_in(c, sshift, sscale, e));
+        Cf[idx] = (uint8_t)q;
+        c = e4m3_to_f32(q);
+      }
+      nrm += c * c;
     }
-    if (LS && n) LS[idx] += s;
-    if (sph) continue;  // rescaled (and rounded to Chat) below, once the norm is known
-    if constexpr (SF == 1 || SF == 4) {
-      const uint16_t h = to_half_rne(conv_in(c, sshift, sscale, e), SF == 4);
-      Chat[idx] = h;
-      c = half_to_f32(h, SF == 4);
-    } else if constexpr (SF == 2 || SF == 5) {
-      const int8_t q = to_code(c, SF == 5);
-      Cq[idx] = q;
-      nq += (int)q * (int)q;
-      continue;
-    } else if constexpr (SF == 3) {
-      const uint32_t q = f32_to_e4m3(conv_in(c, sshift, sscale, e));
-      Cf[idx] = (uint8_t)q;
-      c = e4m3_to_f32(q);
-    }
-    nrm += c * c;
   }
   if constexpr (SF == 2 || SF == 5) nq = wave_sum(nq);
   if (sph) {
