@@ -397,6 +397,7 @@ struct emeans_model {
   void* base = nullptr;
   float* C = nullptr;  // working centroids (the caller's output buffer in emeans_train)
   uint32_t *rows = nullptr, *order = nullptr;
+  int32_t* olab = nullptr;  // labels in bucketed order
   // steps whose sampled rows one launch produces (rows holds sample_steps
   // batches): a 65536-row launch keeps one wave per SIMD, each waiting on its
   // own Feistel chain, so the rows of up to 2^20 slots are drawn at once
@@ -536,6 +537,7 @@ struct emeans_model {
     sample_steps = r.lloyd ? 1 : (B < kSampleRows ? kSampleRows / B : 1);
     ar.want(&rows, r.lloyd ? (size_t)1 : (size_t)(B * sample_steps));
     ar.want(&order, (size_t)B);
+    ar.want(&olab, (size_t)B);
     ar.want(&blab, (size_t)B);
     ar.want(&pcounts, (size_t)k);
     ar.want(&counts, (size_t)k);
@@ -617,8 +619,8 @@ struct emeans_model {
     if (labels_out)
       HIP_RET(hipMemcpyAsync(labels_out, lab, sizeof(int32_t) * nb, hipMemcpyDeviceToDevice, st));
     HIP_RET(launch_scan(pcounts, k, group_rows(dt, d), off, cursor, ovf, ovf_n, counts, st));
-    HIP_RET(launch_scatter(lab, nullptr, nb, k, cursor, order, nullptr, st));
-    HIP_RET(launch_group(dt, X, d, order, off, ovf, ovf_n, k, group_rows(dt, d), nb, s_acc, false,
+    HIP_RET(launch_scatter(lab, nullptr, nb, k, cursor, order, olab, nullptr, st));
+    HIP_RET(launch_group(dt, X, d, order, olab, off, ovf, ovf_n, k, group_rows(dt, d), nb, s_acc, false,
                          st));
     HIP_RET(launch_closing_add(k, d, counts, s_acc, pass_counts, LS, st));
     return EMEANS_OK;
@@ -651,10 +653,10 @@ struct emeans_model {
       hipError_t er = launch_scan(pcounts, k, group_rows(dt, d), off, cursor, ovf, ovf_n, counts,
                                   st);
       if (er != hipSuccess) return er;
-      return launch_scatter(blab, rws, nb, k, cursor, order, out_labels, st);
+      return launch_scatter(blab, rws, nb, k, cursor, order, olab, out_labels, st);
     }));
     HIP_RET(timed(kGroup, [&] {
-      return launch_group(dt, X, d, order, off, ovf, ovf_n, k, group_rows(dt, d), nb, s_acc, add,
+      return launch_group(dt, X, d, order, olab, off, ovf, ovf_n, k, group_rows(dt, d), nb, s_acc, add,
                           st);
     }));
     rows_step += nb;

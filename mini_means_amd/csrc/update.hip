@@ -329,7 +329,8 @@ __device__ __forceinline__ bool group_item(int w, int k, int R, const int32_t* _
 // A label outside [0, k) (a row a closing replay leaves out) is not bucketed;
 // the counts of launch_label_hist skip the same rows.
 __global__ void scatter_kernel(const int32_t* labels, const uint32_t* rows, int nb, int k,
-                               int32_t* cursor, uint32_t* order, int32_t* out_labels) {
+                               int32_t* cursor, uint32_t* order, int32_t* olab,
+                               int32_t* out_labels) {
   const int r = blockIdx.x * blockDim.x + threadIdx.x;
   if (r >= nb) return;
   const int j = labels[r];
@@ -337,6 +338,7 @@ __global__ void scatter_kernel(const int32_t* labels, const uint32_t* rows, int 
   const uint32_t row = rows ? rows[r] : (uint32_t)r;
   const int pos = atomicAdd(&cursor[j], 1);
   order[pos] = row;
+  if (olab) olab[pos] = j;
   if (out_labels) out_labels[row] = j;
 }
 
@@ -805,6 +807,182 @@ __global__ __launch_bounds__(256) void group_span_kernel(const unsigned char* __
       }
     }
   }
+}
+
+// UB raw bytes of a row (UB = 4, 8 or 16) into UB / 4 dwords, and their
+// values as fp32 (the element types of load_span_unit). Split so that a batch
+// of row loads is issued before any of them is converted.
+template <int UB>
+__device__ __forceinline__ void load_unit_raw(const unsigned char* p, uint32_t* r) {
+  if constexpr (UB == 16) {
+    typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+    const u32x4 q = *reinterpret_cast<const u32x4*>(p);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) r[e] = q[e];
+  } else if constexpr (UB == 8) {
+    typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+    const u32x2 q = *reinterpret_cast<const u32x2*>(p);
+    r[0] = q[0];
+    r[1] = q[1];
+  } else {
+    r[0] = *reinterpret_cast<const uint32_t*>(p);
+  }
+}
+
+template <int DT, int UB>
+__device__ __forceinline__ void unit_to_f32(const uint32_t* r, float* v) {
+#pragma unroll
+  for (int h = 0; h < UB / 4; ++h) {
+    const uint32_t q = r[h];
+    if constexpr (DT == 2 || DT == 3 || DT == 5) {  // 1-byte codes / values
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const uint32_t b = (q >> (8 * e)) & 0xFFu;
+        if constexpr (DT == 3)
+          v[4 * h + e] = e4m3_to_f32(b);
+        else if constexpr (DT == 5)
+          v[4 * h + e] = (float)b;
+        else
+          v[4 * h + e] = (float)(int8_t)b;
+      }
+    } else if constexpr (DT == 1) {  // bf16
+      v[2 * h] = __uint_as_float(q << 16);
+      v[2 * h + 1] = __uint_as_float(q & 0xFFFF0000u);
+    } else if constexpr (DT == 4) {  // fp16
+      v[2 * h] = f16_to_f32((uint16_t)(q & 0xFFFFu));
+      v[2 * h + 1] = f16_to_f32((uint16_t)(q >> 16));
+    } else {  // fp32
+      v[h] = __uint_as_float(q);
+    }
+  }
+}
+
+// Grouping of narrow rows by windows of the bucketed order, for batches of
+// small clusters (a few rows each on average). Wave w owns the clusters whose
+// first slot lies in [W w, W w + W). It reads the row ids and labels of slots
+// W w .. W w + 63 with one load each (lanes W..63 are a look-ahead that
+// normally holds the rest of its last cluster), then the rows of its
+// clusters, U loads in flight per lane, so its dependent chain is
+// labels -> rows -> stores (the span kernel's read of the cluster offsets is
+// gone). Each cluster with rows is summed by exactly one wave, in slot order,
+// and stored (added with `add`); a last cluster that runs past the look-ahead
+// is finished in further 64-slot chunks. Each lane owns one UB-byte column
+// unit of every row. Slots past the owned ones in a batch of U loads re-read
+// the last owned row (a cache hit, not added), so the loads need no branch.
+template <int DT, int UB, int U, int W>
+__global__ __launch_bounds__(256) void group_win_kernel(const unsigned char* __restrict__ X,
+                                                        int d, const uint32_t* __restrict__ order,
+                                                        const int32_t* __restrict__ olab,
+                                                        const int32_t* __restrict__ off, int k,
+                                                        int nb, float* __restrict__ s_acc,
+                                                        int add) {
+  constexpr int ES = DT == 0 ? 4 : (DT == 1 || DT == 4) ? 2 : 1;
+  constexpr int EPV = UB / ES;  // elements per lane per row
+  constexpr int RW = UB / 4;    // dwords per lane per row
+  const int lane = threadIdx.x & 63;
+  const int s0 = (blockIdx.x * 4 + (threadIdx.x >> 6)) * W;
+  if (s0 >= nb) return;
+  const size_t rowbytes = (size_t)d * ES;
+  const int ncol = (int)(rowbytes / UB);
+  const bool active = lane < ncol;
+  const unsigned char* xcol = X + (active ? (size_t)lane * UB : 0);
+
+  // one round of independent loads: this lane's slot, the slot before it, and
+  // the number of bucketed slots (addresses clamped into the nb-slot buffers;
+  // slots at or past ns are masked below)
+  const int sl = s0 + lane;
+  const int sc = min(sl, nb - 1);
+  const int lab = olab[sc];
+  const int labp = olab[max(sc - 1, 0)];
+  const uint32_t ord = order[sc];
+  const int ns = off[k];
+  const bool valid = sl < ns;
+  const bool start = valid && (sl == 0 || lab != labp);
+  const uint64_t own = __ballot(start && lane < W);
+  if (own == 0ull) return;  // the window lies inside a cluster that began earlier
+  // the owned slots are lanes [a, e): e is the first slot past the end of the
+  // bucketed order or the first cluster start in the look-ahead
+  const uint64_t endm = __ballot(!valid || (lane >= W && start));
+  const int a = __builtin_ctzll(own);
+  const int e = endm ? __builtin_ctzll(endm) : 64;
+
+  float acc[EPV];
+#pragma unroll
+  for (int q = 0; q < EPV; ++q) acc[q] = 0.0f;
+  auto flush = [&](int j) {
+    if (active) {
+      float* dst = s_acc + (size_t)j * d + (size_t)lane * EPV;
+      if (add) {
+#pragma unroll
+        for (int q = 0; q < EPV; ++q) dst[q] += acc[q];
+      } else if constexpr (EPV % 4 == 0) {
+        typedef float f32x4 __attribute__((ext_vector_type(4)));
+#pragma unroll
+        for (int q = 0; q < EPV; q += 4)
+          *reinterpret_cast<f32x4*>(dst + q) = f32x4{acc[q], acc[q + 1], acc[q + 2], acc[q + 3]};
+      } else if constexpr (EPV == 2) {
+        typedef float f32x2 __attribute__((ext_vector_type(2)));
+        *reinterpret_cast<f32x2*>(dst) = f32x2{acc[0], acc[1]};
+      } else {
+        dst[0] = acc[0];
+      }
+    }
+#pragma unroll
+    for (int q = 0; q < EPV; ++q) acc[q] = 0.0f;
+  };
+
+  for (int t = a; t < e; t += U) {
+    uint32_t raw[U][RW];
+#pragma unroll
+    for (int q = 0; q < U; ++q) {
+      const uint32_t row = (uint32_t)__builtin_amdgcn_readlane((int)ord, min(t + q, e - 1));
+      load_unit_raw<UB>(xcol + (size_t)row * rowbytes, raw[q]);
+    }
+#pragma unroll
+    for (int q = 0; q < U; ++q) {
+      const int sq = t + q;
+      if (sq < e) {
+        float v[EPV];
+        unit_to_f32<DT, UB>(raw[q], v);
+#pragma unroll
+        for (int c = 0; c < EPV; ++c) acc[c] += v[c];
+        // a cluster ends at slot sq when the next slot holds another label,
+        // or at e unless e is the end of the look-ahead (the cluster goes on)
+        const int lq = __builtin_amdgcn_readlane(lab, sq);
+        const bool last = sq + 1 < e ? __builtin_amdgcn_readlane(lab, sq + 1) != lq : e < 64;
+        if (last) flush(lq);
+      }
+    }
+  }
+  if (e < 64) return;
+  // the last cluster runs past the look-ahead: its rows in 64-slot chunks
+  const int lc = __builtin_amdgcn_readlane(lab, 63);
+  for (int t0 = s0 + 64;; t0 += 64) {
+    const int sl2 = t0 + lane;
+    const int sc2 = min(sl2, nb - 1);
+    const int lab2 = olab[sc2];
+    const uint32_t ord2 = order[sc2];
+    const uint64_t stop = __ballot(sl2 >= ns || lab2 != lc);
+    const int m = stop ? __builtin_ctzll(stop) : 64;
+    for (int t = 0; t < m; t += U) {
+      uint32_t raw[U][RW];
+#pragma unroll
+      for (int q = 0; q < U; ++q) {
+        const uint32_t row = (uint32_t)__builtin_amdgcn_readlane((int)ord2, min(t + q, m - 1));
+        load_unit_raw<UB>(xcol + (size_t)row * rowbytes, raw[q]);
+      }
+#pragma unroll
+      for (int q = 0; q < U; ++q)
+        if (t + q < m) {
+          float v[EPV];
+          unit_to_f32<DT, UB>(raw[q], v);
+#pragma unroll
+          for (int c = 0; c < EPV; ++c) acc[c] += v[c];
+        }
+    }
+    if (m < 64) break;
+  }
+  flush(lc);
 }
 
 // One wave per cluster: EMA of the running count and sum, centroid S/N,
@@ -1306,12 +1484,12 @@ __global__ __launch_bounds__(1024) void revive_kernel(ReviveArgs A) {
   revive_chains(A, ndead, itmp);
 }
 
-// Donor draws for k <= kSpecK, speculated a round of 64 at a time.
+// Donor draws for k <= kSpecK, speculated a round of kSpecRound at a time.
 //
 // The draws are sequential (each halves its donor's count, which moves every
 // later target and prefix sum), but one draw moves them little: the donor of
 // draw q is usually at or next to the cluster it would get from the counts at
-// the start of its round. So each round of 64 dead clusters (lane q = draw q)
+// the start of its round. So each round of kSpecRound dead clusters (lane q = draw q)
 //  1. speculates in parallel: lane q searches the round-start prefix sums for
 //     u_q T (T = the live total at the round's start) and keeps its candidate
 //     m_q with the exact current prefix sums around it, L_q = cum(m_q - 1)
@@ -1334,6 +1512,11 @@ __global__ __launch_bounds__(1024) void revive_kernel(ReviveArgs A) {
 // third of the candidates are right at the first SIFT-like check, and a miss
 // costs one 16-cluster walk step (an LDS read and a 16-lane fp64 scan).
 constexpr int kSpecK = 16384;
+// Draws speculated per round (lanes 0 .. kSpecRound - 1 of wave 0). Rounds of
+// 8, 16, 32 and 64 draws cost within 4% of each other over whole runs (the
+// fresher candidates of short rounds hit more often, but each round starts
+// with its own tree search); 32 was the fastest.
+constexpr int kSpecRound = 32;
 
 // First of N consecutive sums whose running total from acc exceeds t (N if
 // none); acc becomes the running total before it.
@@ -1372,6 +1555,7 @@ __device__ __forceinline__ double row_scan16_f64(double v) {
 }
 
 __global__ __launch_bounds__(1024) void revive_spec_kernel(ReviveArgs A) {
+  constexpr int RR = kSpecRound;
   constexpr int RV = kSpecK / 1024;  // clusters per thread in the set-up
   __shared__ double dtmp[16];
   __shared__ int itmp[16];
@@ -1471,10 +1655,10 @@ __global__ __launch_bounds__(1024) void revive_spec_kernel(ReviveArgs A) {
     // round ahead
     int dl = lane < ndead ? A.dead[lane] : 0;
     double u = lane < ndead ? A.udraw[lane] : 0.0;
-    for (int d0 = 0; d0 < ndead; d0 += 64) {
-      const int nb = min(64, ndead - d0);
+    for (int d0 = 0; d0 < ndead; d0 += RR) {
+      const int nb = min(RR, ndead - d0);
       const bool act = lane < nb;
-      const int dn = d0 + 64 + lane;
+      const int dn = d0 + RR + lane;
       const int dl_next = dn < ndead ? A.dead[dn] : 0;
       const double u_next = dn < ndead ? A.udraw[dn] : 0.0;
       // 1. candidate from the round-start sums; a target at or past the total
@@ -1866,9 +2050,10 @@ hipError_t launch_scan(int32_t* counts, int k, int R, int32_t* off, int32_t* cur
 }
 
 hipError_t launch_scatter(const int32_t* labels, const uint32_t* rows, int nb, int k,
-                          int32_t* cursor, uint32_t* order, int32_t* out_labels, hipStream_t st) {
+                          int32_t* cursor, uint32_t* order, int32_t* olab, int32_t* out_labels,
+                          hipStream_t st) {
   if (nb <= 0) return hipSuccess;
-  scatter_kernel<<<(nb + 255) / 256, 256, 0, st>>>(labels, rows, nb, k, cursor, order,
+  scatter_kernel<<<(nb + 255) / 256, 256, 0, st>>>(labels, rows, nb, k, cursor, order, olab,
                                                    out_labels);
   return hipGetLastError();
 }
@@ -1888,9 +2073,10 @@ hipError_t launch_closing_add(int k, int d, int32_t* counts, float* s_acc, int32
 
 template <int DT>
 static hipError_t launch_group_dt(const unsigned char* x, int d, bool vec, int ncol,
-                                  const uint32_t* order, const int32_t* off, const int2* ovf,
-                                  const int32_t* ovf_n, int k, int R, long long items,
-                                  float* s_acc, int add, int nb, hipStream_t st) {
+                                  const uint32_t* order, const int32_t* olab, const int32_t* off,
+                                  const int2* ovf, const int32_t* ovf_n, int k, int R,
+                                  long long items, float* s_acc, int add, int nb,
+                                  hipStream_t st) {
   // narrow rows: spans of consecutive clusters, one lane per 4-, 8- or 16-byte unit
   constexpr int ES = DT == 0 ? 4 : (DT == 1 || DT == 4) ? 2 : 1;
   const size_t rowbytes = (size_t)d * ES;
@@ -1899,6 +2085,24 @@ static hipError_t launch_group_dt(const unsigned char* x, int d, bool vec, int n
     if (!ub && cand / ES <= 4 && rowbytes % cand == 0 && rowbytes / cand <= 64 &&
         (uintptr_t)x % cand == 0)
       ub = cand;
+  if (ub && olab && (long long)nb <= 8LL * k) {
+    // at most 8 rows per cluster on average: windows of 8 slots, one wave each
+    // (8.3 -> 7.3 us on 65536 rows of 96 fp32 against 16384 clusters, 10.6 ->
+    // 9.4 us at 128; windows of 4, 16 and 32 slots were slower)
+    const dim3 grid((unsigned)((((long long)nb + 7) / 8 + 3) / 4)), block(256);
+    if (ub == 4)
+      group_win_kernel<DT, 4, 8, 8><<<grid, block, 0, st>>>(x, d, order, olab, off, k, nb, s_acc,
+                                                             add);
+    if constexpr (ES >= 2)
+      if (ub == 8)
+        group_win_kernel<DT, 8, 8, 8><<<grid, block, 0, st>>>(x, d, order, olab, off, k, nb,
+                                                               s_acc, add);
+    if constexpr (ES >= 4)
+      if (ub == 16)
+        group_win_kernel<DT, 16, 8, 8><<<grid, block, 0, st>>>(x, d, order, olab, off, k, nb,
+                                                                s_acc, add);
+    return hipGetLastError();
+  }
   if (ub) {
     // about 16 rows per span: C clusters of nb / k rows on average
     const double avg = (double)nb / (double)k;
@@ -1954,8 +2158,9 @@ int group_rows(int dt, int d) {
 }
 
 hipError_t launch_group(int dt, const void* X, int d, const uint32_t* order,
-                        const int32_t* off, const int2* ovf, const int32_t* ovf_n, int k, int R,
-                        int nb, float* s_acc, bool add, hipStream_t st) {
+                        const int32_t* olab, const int32_t* off, const int2* ovf,
+                        const int32_t* ovf_n, int k, int R, int nb, float* s_acc, bool add,
+                        hipStream_t st) {
   if (nb <= 0) return hipSuccess;
   // work items: one per cluster plus at most nb / R overflow items
   const long long items = (long long)k + nb / R;
@@ -1968,16 +2173,22 @@ hipError_t launch_group(int dt, const void* X, int d, const uint32_t* order,
   const int ncol = vec ? d / per : d;
   const int a = add ? 1 : 0;
   if (dt == 1)
-    return launch_group_dt<1>(x, d, vec, ncol, order, off, ovf, ovf_n, k, R, items, s_acc, a, nb, st);
+    return launch_group_dt<1>(x, d, vec, ncol, order, olab, off, ovf, ovf_n, k, R, items, s_acc, a,
+                              nb, st);
   if (dt == 2)
-    return launch_group_dt<2>(x, d, vec, ncol, order, off, ovf, ovf_n, k, R, items, s_acc, a, nb, st);
+    return launch_group_dt<2>(x, d, vec, ncol, order, olab, off, ovf, ovf_n, k, R, items, s_acc, a,
+                              nb, st);
   if (dt == 3)
-    return launch_group_dt<3>(x, d, vec, ncol, order, off, ovf, ovf_n, k, R, items, s_acc, a, nb, st);
+    return launch_group_dt<3>(x, d, vec, ncol, order, olab, off, ovf, ovf_n, k, R, items, s_acc, a,
+                              nb, st);
   if (dt == 4)
-    return launch_group_dt<4>(x, d, vec, ncol, order, off, ovf, ovf_n, k, R, items, s_acc, a, nb, st);
+    return launch_group_dt<4>(x, d, vec, ncol, order, olab, off, ovf, ovf_n, k, R, items, s_acc, a,
+                              nb, st);
   if (dt == 5)
-    return launch_group_dt<5>(x, d, vec, ncol, order, off, ovf, ovf_n, k, R, items, s_acc, a, nb, st);
-  return launch_group_dt<0>(x, d, vec, ncol, order, off, ovf, ovf_n, k, R, items, s_acc, a, nb, st);
+    return launch_group_dt<5>(x, d, vec, ncol, order, olab, off, ovf, ovf_n, k, R, items, s_acc, a,
+                              nb, st);
+  return launch_group_dt<0>(x, d, vec, ncol, order, olab, off, ovf, ovf_n, k, R, items, s_acc, a,
+                              nb, st);
 }
 
 hipError_t launch_ema(int k, int d, float a, float b, int32_t* counts, float* s_acc, float* N,
