@@ -397,7 +397,7 @@ struct emeans_model {
   void* base = nullptr;
   float* C = nullptr;  // working centroids (the caller's output buffer in emeans_train)
   uint32_t *rows = nullptr, *order = nullptr;
-  int32_t* olab = nullptr;  // labels in bucketed order
+  int2* olab = nullptr;  // (row id, label) of each slot in bucketed order
   // steps whose sampled rows one launch produces (rows holds sample_steps
   // batches): a 65536-row launch keeps one wave per SIMD, each waiting on its
   // own Feistel chain, so the rows of up to 2^20 slots are drawn at once

@@ -96,11 +96,12 @@ hipError_t launch_scan(int32_t* counts, int k, int R, int32_t* off, int32_t* cur
                        int2* ovf, int32_t* ovf_n, int32_t* acc, hipStream_t st);
 
 // Bucket the batch by label: pos = cursor[label]++, order[pos] = rows[r] (r
-// when rows is NULL) and, when olab is non-null, olab[pos] = label; when
+// when rows is NULL) and, when olab is non-null, olab[pos] = (that row,
+// label); when
 // out_labels is non-null also out_labels[rows[r]] = label. Rows whose label
 // lies outside [0, k) are skipped.
 hipError_t launch_scatter(const int32_t* labels, const uint32_t* rows, int nb, int k,
-                          int32_t* cursor, uint32_t* order, int32_t* olab, int32_t* out_labels,
+                          int32_t* cursor, uint32_t* order, int2* olab, int32_t* out_labels,
                           hipStream_t st);
 
 // counts[labels[r]] += 1 for labels in [0, k); *bad += 1 for each label that is
@@ -119,11 +120,11 @@ int group_rows(int dt, int d);
 
 // s_acc[j] += sum of X rows of cluster j (work items of at most R rows). A
 // cluster held by one work item is stored, assuming s_acc[j] = 0, unless
-// `add` (a later piece of the same update). olab (the labels in bucketed
-// order, from launch_scatter) may be NULL; with it, batches of small clusters
+// `add` (a later piece of the same update). olab (row ids and labels in
+// bucketed order, from launch_scatter) may be NULL; with it, batches of small clusters
 // of narrow rows are grouped by windows of the order.
 hipError_t launch_group(int dt, const void* X, int d, const uint32_t* order,
-                        const int32_t* olab, const int32_t* off, const int2* ovf,
+                        const int2* olab, const int32_t* off, const int2* ovf,
                         const int32_t* ovf_n, int k, int R, int nb, float* s_acc, bool add,
                         hipStream_t st);
 

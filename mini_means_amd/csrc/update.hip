@@ -329,7 +329,7 @@ __device__ __forceinline__ bool group_item(int w, int k, int R, const int32_t* _
 // A label outside [0, k) (a row a closing replay leaves out) is not bucketed;
 // the counts of launch_label_hist skip the same rows.
 __global__ void scatter_kernel(const int32_t* labels, const uint32_t* rows, int nb, int k,
-                               int32_t* cursor, uint32_t* order, int32_t* olab,
+                               int32_t* cursor, uint32_t* order, int2* olab,
                                int32_t* out_labels) {
   const int r = blockIdx.x * blockDim.x + threadIdx.x;
   if (r >= nb) return;
@@ -338,7 +338,7 @@ __global__ void scatter_kernel(const int32_t* labels, const uint32_t* rows, int 
   const uint32_t row = rows ? rows[r] : (uint32_t)r;
   const int pos = atomicAdd(&cursor[j], 1);
   order[pos] = row;
-  if (olab) olab[pos] = j;
+  if (olab) olab[pos] = make_int2((int)row, j);
   if (out_labels) out_labels[row] = j;
 }
 
@@ -812,21 +812,13 @@ __global__ __launch_bounds__(256) void group_span_kernel(const unsigned char* __
 // UB raw bytes of a row (UB = 4, 8 or 16) into UB / 4 dwords, and their
 // values as fp32 (the element types of load_span_unit). Split so that a batch
 // of row loads is issued before any of them is converted.
+// The rows are read once per step: non-temporal loads (slightly faster than
+// plain ones on the deep- and SIFT-like batches).
 template <int UB>
 __device__ __forceinline__ void load_unit_raw(const unsigned char* p, uint32_t* r) {
-  if constexpr (UB == 16) {
-    typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-    const u32x4 q = *reinterpret_cast<const u32x4*>(p);
 #pragma unroll
-    for (int e = 0; e < 4; ++e) r[e] = q[e];
-  } else if constexpr (UB == 8) {
-    typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
-    const u32x2 q = *reinterpret_cast<const u32x2*>(p);
-    r[0] = q[0];
-    r[1] = q[1];
-  } else {
-    r[0] = *reinterpret_cast<const uint32_t*>(p);
-  }
+  for (int e = 0; e < UB / 4; ++e)
+    r[e] = __builtin_nontemporal_load(reinterpret_cast<const uint32_t*>(p) + e);
 }
 
 template <int DT, int UB>
@@ -859,9 +851,10 @@ __device__ __forceinline__ void unit_to_f32(const uint32_t* r, float* v) {
 
 // Grouping of narrow rows by windows of the bucketed order, for batches of
 // small clusters (a few rows each on average). Wave w owns the clusters whose
-// first slot lies in [W w, W w + W). It reads the row ids and labels of slots
-// W w .. W w + 63 with one load each (lanes W..63 are a look-ahead that
-// normally holds the rest of its last cluster), then the rows of its
+// first slot lies in [W w, W w + W). It reads the (row id, label) pairs of
+// slots W w .. W w + 63, one 8-byte load per lane (lanes W..63 are a
+// look-ahead that normally holds the rest of its last cluster; the label of
+// the slot before each lane's comes from a lane shift), then the rows of its
 // clusters, U loads in flight per lane, so its dependent chain is
 // labels -> rows -> stores (the span kernel's read of the cluster offsets is
 // gone). Each cluster with rows is summed by exactly one wave, in slot order,
@@ -871,8 +864,7 @@ __device__ __forceinline__ void unit_to_f32(const uint32_t* r, float* v) {
 // the last owned row (a cache hit, not added), so the loads need no branch.
 template <int DT, int UB, int U, int W>
 __global__ __launch_bounds__(256) void group_win_kernel(const unsigned char* __restrict__ X,
-                                                        int d, const uint32_t* __restrict__ order,
-                                                        const int32_t* __restrict__ olab,
+                                                        int d, const int2* __restrict__ olab,
                                                         const int32_t* __restrict__ off, int k,
                                                         int nb, float* __restrict__ s_acc,
                                                         int add) {
@@ -892,10 +884,13 @@ __global__ __launch_bounds__(256) void group_win_kernel(const unsigned char* __r
   // slots at or past ns are masked below)
   const int sl = s0 + lane;
   const int sc = min(sl, nb - 1);
-  const int lab = olab[sc];
-  const int labp = olab[max(sc - 1, 0)];
-  const uint32_t ord = order[sc];
+  const int2 pr = olab[sc];
+  const int lab = pr.y;
+  const uint32_t ord = (uint32_t)pr.x;
+  const int lab0 = olab[max(s0 - 1, 0)].y;  // the slot before the window
   const int ns = off[k];
+  // label of the slot before this lane's: lane - 1's (wave_shr:1), lab0 on lane 0
+  const int labp = __builtin_amdgcn_update_dpp(lab0, lab, 0x138, 0xF, 0xF, false);
   const bool valid = sl < ns;
   const bool start = valid && (sl == 0 || lab != labp);
   const uint64_t own = __ballot(start && lane < W);
@@ -960,8 +955,9 @@ __global__ __launch_bounds__(256) void group_win_kernel(const unsigned char* __r
   for (int t0 = s0 + 64;; t0 += 64) {
     const int sl2 = t0 + lane;
     const int sc2 = min(sl2, nb - 1);
-    const int lab2 = olab[sc2];
-    const uint32_t ord2 = order[sc2];
+    const int2 pr2 = olab[sc2];
+    const int lab2 = pr2.y;
+    const uint32_t ord2 = (uint32_t)pr2.x;
     const uint64_t stop = __ballot(sl2 >= ns || lab2 != lc);
     const int m = stop ? __builtin_ctzll(stop) : 64;
     for (int t = 0; t < m; t += U) {
@@ -2050,7 +2046,7 @@ hipError_t launch_scan(int32_t* counts, int k, int R, int32_t* off, int32_t* cur
 }
 
 hipError_t launch_scatter(const int32_t* labels, const uint32_t* rows, int nb, int k,
-                          int32_t* cursor, uint32_t* order, int32_t* olab, int32_t* out_labels,
+                          int32_t* cursor, uint32_t* order, int2* olab, int32_t* out_labels,
                           hipStream_t st) {
   if (nb <= 0) return hipSuccess;
   scatter_kernel<<<(nb + 255) / 256, 256, 0, st>>>(labels, rows, nb, k, cursor, order, olab,
@@ -2073,7 +2069,7 @@ hipError_t launch_closing_add(int k, int d, int32_t* counts, float* s_acc, int32
 
 template <int DT>
 static hipError_t launch_group_dt(const unsigned char* x, int d, bool vec, int ncol,
-                                  const uint32_t* order, const int32_t* olab, const int32_t* off,
+                                  const uint32_t* order, const int2* olab, const int32_t* off,
                                   const int2* ovf, const int32_t* ovf_n, int k, int R,
                                   long long items, float* s_acc, int add, int nb,
                                   hipStream_t st) {
@@ -2087,20 +2083,16 @@ static hipError_t launch_group_dt(const unsigned char* x, int d, bool vec, int n
       ub = cand;
   if (ub && olab && (long long)nb <= 8LL * k) {
     // at most 8 rows per cluster on average: windows of 8 slots, one wave each
-    // (8.3 -> 7.3 us on 65536 rows of 96 fp32 against 16384 clusters, 10.6 ->
-    // 9.4 us at 128; windows of 4, 16 and 32 slots were slower)
     const dim3 grid((unsigned)((((long long)nb + 7) / 8 + 3) / 4)), block(256);
     if (ub == 4)
-      group_win_kernel<DT, 4, 8, 8><<<grid, block, 0, st>>>(x, d, order, olab, off, k, nb, s_acc,
-                                                             add);
+      group_win_kernel<DT, 4, 8, 8><<<grid, block, 0, st>>>(x, d, olab, off, k, nb, s_acc, add);
     if constexpr (ES >= 2)
       if (ub == 8)
-        group_win_kernel<DT, 8, 8, 8><<<grid, block, 0, st>>>(x, d, order, olab, off, k, nb,
-                                                               s_acc, add);
+        group_win_kernel<DT, 8, 8, 8><<<grid, block, 0, st>>>(x, d, olab, off, k, nb, s_acc, add);
     if constexpr (ES >= 4)
       if (ub == 16)
-        group_win_kernel<DT, 16, 8, 8><<<grid, block, 0, st>>>(x, d, order, olab, off, k, nb,
-                                                                s_acc, add);
+        group_win_kernel<DT, 16, 8, 8><<<grid, block, 0, st>>>(x, d, olab, off, k, nb, s_acc,
+                                                                add);
     return hipGetLastError();
   }
   if (ub) {
@@ -2158,7 +2150,7 @@ int group_rows(int dt, int d) {
 }
 
 hipError_t launch_group(int dt, const void* X, int d, const uint32_t* order,
-                        const int32_t* olab, const int32_t* off, const int2* ovf,
+                        const int2* olab, const int32_t* off, const int2* ovf,
                         const int32_t* ovf_n, int k, int R, int nb, float* s_acc, bool add,
                         hipStream_t st) {
   if (nb <= 0) return hipSuccess;
