@@ -155,30 +155,45 @@ __global__ __launch_bounds__(kThreads, 1) void assign_bf16_kernel(
     const int buf = panel & 1;
     const bool more = panel + 1 < npan;
     if (more) gload(panel + 1);
+    // biases of a block's 32 centroids (the accumulators' initial values) and
+    // the row of its A operands
+    auto block_init = [&](int cb) {
+      f32x16 init;
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const float4 b4 = *reinterpret_cast<const float4*>(&lb[buf][cb * 32 + 8 * g + 4 * half]);
+        init[4 * g + 0] = b4.x;
+        init[4 * g + 1] = b4.y;
+        init[4 * g + 2] = b4.z;
+        init[4 * g + 3] = b4.w;
+      }
+      return init;
+    };
+    auto block_row = [&](int cb) {
+      return &lc[buf][(cb * 32 + (lane & 31)) * kStride + 16 * half];
+    };
+    f32x16 init = block_init(0);
+    u32x4 a_cur = *reinterpret_cast<const u32x4*>(block_row(0));
 #pragma unroll
     for (int cb = 0; cb < kTC / 32; ++cb) {
-      // biases of the block's 32 centroids: the accumulators' initial values
       f32x16 acc[kPB];
-      {
-        f32x16 init;
 #pragma unroll
-        for (int g = 0; g < 4; ++g) {
-          const float4 b4 = *reinterpret_cast<const float4*>(&lb[buf][cb * 32 + 8 * g + 4 * half]);
-          init[4 * g + 0] = b4.x;
-          init[4 * g + 1] = b4.y;
-          init[4 * g + 2] = b4.z;
-          init[4 * g + 3] = b4.w;
-        }
-#pragma unroll
-        for (int pb = 0; pb < kPB; ++pb) acc[pb] = init;
-      }
-      // A operands one k-step ahead of the MFMAs that use them
-      const unsigned char* arow = &lc[buf][(cb * 32 + (lane & 31)) * kStride + 16 * half];
-      u32x4 a_cur = *reinterpret_cast<const u32x4*>(arow);
+      for (int pb = 0; pb < kPB; ++pb) acc[pb] = init;
+      // A operands one k-step ahead of the MFMAs that use them; during the
+      // last k-step, the next block's first operands and its biases
+      const unsigned char* arow = block_row(cb);
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) {
         u32x4 a_nxt = a_cur;
-        if (ks + 1 < KS) a_nxt = *reinterpret_cast<const u32x4*>(arow + 32 * (ks + 1));
+        if (ks + 1 < KS) {
+          a_nxt = *reinterpret_cast<const u32x4*>(arow + 32 * (ks + 1));
+        } else if (cb + 1 < kTC / 32) {
+          a_nxt = *reinterpret_cast<const u32x4*>(block_row(cb + 1));
+          init = block_init(cb + 1);
+        }
+        // keep these reads above this step's MFMAs (the scheduler would
+        // otherwise sink them to just before their first use)
+        __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int pb = 0; pb < kPB; ++pb) {
           if constexpr (F16)
