@@ -102,6 +102,24 @@ def test_stream_lockstep(mm, name, gen, n, d, k, T, pieces, o):
         assert rel_l2(out.slow_centroids.cpu().numpy(), res.slow_centroids) <= tol
 
 
+def test_stream_window_grouping_in_pieces(mm):
+    """The window grouping adds each later piece of an update to the sums of
+    the earlier ones: three pieces per 4096-row batch of narrow rows (a few
+    rows per cluster on average), one cluster holding hundreds of rows."""
+    n, d, k, T, seed, bs = 24_000, 64, 1024, 2.0, 1234, 4096
+    X = datagen.make("tiny", n, d, seed=5)
+    rng = np.random.default_rng(5)
+    X[rng.choice(n, n // 4, replace=False)] = X[0]
+    out = _stream_run(mm, X, k, T, seed, pieces=3, batch_size=bs)
+    res, summ = lockstep(X, out, k, T, seed, batch_size=bs)
+    assert summ["steps"] == res.recipe["total_steps"]
+    assert np.array_equal(out.counts.cpu().numpy(), res.N)
+    assert out.split_log == [tuple(s) for s in res.split_log]
+    assert np.array_equal(out.labels.cpu().numpy(), res.labels)
+    assert rel_l2(out.centroids.cpu().numpy(), res.centroids) <= 1e-4
+    np.testing.assert_allclose(out.stats["obj"], res.obj, rtol=1e-4, atol=obj_atol(X))
+
+
 def test_stream_rejects_rule_breaks(mm):
     """README "Data too big for memory" rules: batches of exactly the recipe's
     size except the last of a pass, every pass visits its rows, begin before

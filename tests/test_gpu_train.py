@@ -111,6 +111,37 @@ def test_train_lockstep(mm, name, gen, n, d, k, T, o):
         assert np.all((np.abs(nrm - 1.0) < 1e-6) | (nrm == 0.0))
 
 
+def _dup_heavy(n, d, frac, seed):
+    """Seeded rows of the 64-centre mixture with a share `frac` of them replaced
+    by one repeated row, so that one cluster holds hundreds of rows of every
+    batch while the average cluster holds a few."""
+    X = datagen.make("tiny", n, d, seed=seed)
+    rng = np.random.default_rng(seed)
+    X[rng.choice(n, int(frac * n), replace=False)] = X[0]
+    return X
+
+
+def test_train_lockstep_window_grouping_long_cluster(mm):
+    """Narrow rows in batches of at most 8 rows per cluster on average are
+    grouped by 8-slot windows of the bucketed order, each wave reading 64
+    slots ahead; here one cluster holds about 700 rows of each 4096-row batch,
+    so its wave finishes it in further 64-slot chunks."""
+    X = _dup_heavy(24_000, 64, 0.25, 5)
+    k, T, seed, bs = 1024, 2.0, 1234, 4096
+    out = _gpu_train(mm, X, k, T, seed, batch_size=bs)
+    trace = out.trace.cpu().numpy()
+    assert bs <= 8 * k
+    assert max(np.bincount(trace[s:s + bs], minlength=k).max()
+               for s in range(0, len(trace), bs)) > 3 * 64
+    res, summ = lockstep(X, out, k, T, seed, batch_size=bs)
+    assert summ["steps"] == res.recipe["total_steps"]
+    assert np.array_equal(out.counts.cpu().numpy(), res.N)
+    assert out.split_log == [tuple(s) for s in res.split_log]
+    assert np.array_equal(out.labels.cpu().numpy(), res.labels)
+    assert rel_l2(out.centroids.cpu().numpy(), res.centroids) <= 1e-4
+    np.testing.assert_allclose(out.stats["obj"], res.obj, rtol=1e-4, atol=obj_atol(X))
+
+
 LLOYD = [("tiny", "tiny", 10_000, 16, 64, 8), ("emb-small", "embedding", 12_000, 768, 256, 4),
          ("large-small", "large", 40_000, 128, 1024, 3), ("codes", "codes", 12_000, 96, 200, 4),
          ("ragged", "tiny", 5_003, 37, 77, 5), ("f8", "codes8", 12_000, 128, 200, 4),
