@@ -1693,7 +1693,9 @@ __global__ __launch_bounds__(1024) void revive_spec_kernel(ReviveArgs A) {
       // 2. settle the draws in order
       for (int q = 0; q < nb; ++q) {
         const double t = u * Tq;
-        const uint64_t okm = __ballot((L <= t) & (t < H));
+        // two ballots and a scalar AND: a ballot of the combined predicate
+        // goes through a vector select and compare on the draw's chain
+        const uint64_t okm = __ballot(L <= t) & __ballot(t < H);
         int ms;
         float nh;
         double nhd;
@@ -1728,7 +1730,7 @@ __global__ __launch_bounds__(1024) void revive_spec_kernel(ReviveArgs A) {
             for (; p0 < M; p0 += 16) {
               const float w = wc[p0 + (lane & 15)];  // zero past M
               const double v = row_scan16_f64((double)w);
-              const uint64_t hm = __ballot((lane < 16) & (c + v > tq));
+              const uint64_t hm = __ballot(c + v > tq) & 0xFFFFull;
               if (hm) {
                 const int i = __ffsll((unsigned long long)hm) - 1;
                 ms = p0 + i;
@@ -1762,7 +1764,7 @@ __global__ __launch_bounds__(1024) void revive_spec_kernel(ReviveArgs A) {
               const int pos = p0 - (lane & 15);
               const float w = pos >= 0 ? wc[max(pos, 0)] : 0.0f;
               const double v = row_scan16_f64((double)w);
-              const uint64_t hm = __ballot((lane < 16) & (pos >= 0) & (c - v <= tq));
+              const uint64_t hm = __ballot(pos >= 0) & __ballot(c - v <= tq) & 0xFFFFull;
               if (hm) {
                 const int i = __ffsll((unsigned long long)hm) - 1;
                 ms = p0 - i;
