@@ -130,6 +130,13 @@ def lib():
                                     ctypes.c_int]
         L.ref_dot_to.argtypes = [vp, ctypes.c_int, i64, vp, i32, vp, vp, vp]
         L.ref_group.argtypes = [vp, ctypes.c_int, i64, vp, vp, i32, i32, vp, vp]
+        f64 = ctypes.c_double
+        L.emeans_ref_recipe.argtypes = [i64, i32, i32, f64, vp, vp, vp, vp, vp]
+        L.emeans_ref_recipe.restype = ctypes.c_int
+        L.emeans_ref_assign.argtypes = [vp, i64, i32, vp, i32, vp, vp]
+        L.emeans_ref_assign.restype = ctypes.c_int
+        L.emeans_ref_train.argtypes = [vp, i64, i32, i32, f64, u64, vp, vp, vp]
+        L.emeans_ref_train.restype = ctypes.c_int
         _lib = L
     return _lib
 
@@ -571,6 +578,44 @@ def group(X: np.ndarray, rows: Optional[np.ndarray], labels: np.ndarray, k: int)
     counts = np.zeros(k, dtype=np.int64)
     lib().ref_group(_p(X), _dtype_code(X), m, _p(r), _p(labels), d, k, _p(sums), _p(counts))
     return counts, sums
+
+
+def abi_recipe(n: int, d: int, k: int, T: float) -> dict:
+    """emeans_ref_recipe: the C mirror of the library's recipe call (default
+    options): batch size, alpha0, passes, total steps, revival threshold."""
+    B, S = np.zeros(1, np.int64), np.zeros(1, np.int64)
+    a0, thr = np.zeros(1, np.float64), np.zeros(1, np.float64)
+    npass = np.zeros(1, np.int32)
+    rc = lib().emeans_ref_recipe(n, d, k, T, _p(B), _p(a0), _p(npass), _p(S), _p(thr))
+    if rc:
+        raise ValueError("emeans_ref_recipe rejected its arguments")
+    return dict(batch_size=int(B[0]), alpha0=float(a0[0]), passes=int(npass[0]),
+                total_steps=int(S[0]), unused_threshold=float(thr[0]))
+
+
+def abi_assign(X: np.ndarray, C: np.ndarray):
+    """emeans_ref_assign: labels and fp32 squared distances of fp32 rows."""
+    X = np.ascontiguousarray(X, dtype=np.float32)
+    C = np.ascontiguousarray(C, dtype=np.float32)
+    lab = np.empty(len(X), np.int32)
+    dist = np.empty(len(X), np.float32)
+    rc = lib().emeans_ref_assign(_p(X), len(X), X.shape[1], _p(C), len(C), _p(lab), _p(dist))
+    if rc:
+        raise ValueError("emeans_ref_assign rejected its arguments")
+    return lab, dist
+
+
+def abi_train(X: np.ndarray, k: int, T: float, seed: int = 1234):
+    """emeans_ref_train: the whole run in C (fp32 rows, default options):
+    centroids, last-pass labels and the number of revivals."""
+    X = np.ascontiguousarray(X, dtype=np.float32)
+    C = np.empty((k, X.shape[1]), np.float32)
+    lab = np.empty(len(X), np.int32)
+    ns = np.zeros(1, np.int64)
+    rc = lib().emeans_ref_train(_p(X), len(X), X.shape[1], k, T, seed, _p(C), _p(lab), _p(ns))
+    if rc:
+        raise ValueError("emeans_ref_train rejected its arguments")
+    return C, lab, int(ns[0])
 
 
 def mse(X: np.ndarray, C: np.ndarray, nthreads: int = 0) -> float:

@@ -305,3 +305,207 @@ void ref_group(const void* X, int dtype, int64_t nrows, const int64_t* rows,
   free(cursor);
   free(start);
 }
+
+/* ======================================================================== */
+/* Host-pointer mirrors of the library's boundary: emeans_ref_recipe,       */
+/* emeans_ref_assign and emeans_ref_train. They take the same steps as the  */
+/* Python oracle (oracle/__init__.py: recipe, assign, train with default    */
+/* options) for fp32 data, in the same arithmetic:                          */
+/*   recipe  - scaling laws (faiss e_means README, "Scaling laws"): batch   */
+/*             size c * k^0.134749 * n^0.876473 * T^0.813344 rounded to the */
+/*             nearest power of two and capped at the largest power of two  */
+/*             <= n / 2; alpha0 = 0.8244 k^-0.4617 B^0.9003 n^-0.4498       */
+/*             T^-0.1057 clamped to [1e-4, 1]; floor(T) full passes plus    */
+/*             floor(frac(T) n) rows; revival threshold 0.1 (0 for d <= 2); */
+/*   assign  - the nearest centroid in fp64, ties to the lowest index;      */
+/*   train   - the batch loop of the README's "Data too big for memory"     */
+/*             rules: a fresh keyed order every pass, N <- fl(fl(b N) +      */
+/*             fl(a n)) in fp32 with b = fl(1 - a), S <- (b S + a s) in     */
+/*             fp64 stored fp32, c = S / N where N > 0, revival after every */
+/*             fifth step (blog, third change), and the closing exact mean  */
+/*             of the last pass (README "How the centroid updates work").   */
+/* Return 0, or -1 for arguments outside the library's own bounds (the      */
+/* outputs are then untouched).                                             */
+/* ======================================================================== */
+enum { REF_LAW_THROUGHPUT = 1, REF_LAW_QUALITY = 2 };
+
+int emeans_ref_recipe(int64_t n, int32_t d, int32_t k, double T, int64_t* batch_size,
+                      double* alpha0, int32_t* passes, int64_t* total_steps, double* threshold) {
+  if (n < 1 || d < 1 || k < 1 || k > n || !(T > 0.0)) return -1;
+  const int law = d <= 16 ? REF_LAW_QUALITY : REF_LAW_THROUGHPUT;
+  const double c = law == REF_LAW_QUALITY ? 0.00439175 : 0.035134;
+  const double braw = c * pow((double)k, 0.134749) * pow((double)n, 0.876473) * pow(T, 0.813344);
+  int64_t B = (int64_t)ldexp(1.0, (int)floor(log2(braw) + 0.5));
+  const int64_t cap = n >= 2 ? (int64_t)ldexp(1.0, (int)floor(log2((double)n / 2.0))) : 1;
+  if (B > cap) B = cap;
+  if (B < 1) B = 1;
+  double a0 = 0.8244 * pow((double)k, -0.4617) * pow((double)B, 0.9003) *
+              pow((double)n, -0.4498) * pow(T, -0.1057);
+  if (a0 < 1e-4) a0 = 1e-4;
+  if (a0 > 1.0) a0 = 1.0;
+  const int full = (int)floor(T);
+  const int64_t frac_rows = (int64_t)floor((T - full) * (double)n);
+  int np_ = full + (frac_rows > 0 ? 1 : 0);
+  int64_t steps = (int64_t)full * ((n + B - 1) / B) + (frac_rows > 0 ? (frac_rows + B - 1) / B : 0);
+  if (batch_size) *batch_size = B;
+  if (alpha0) *alpha0 = a0;
+  if (passes) *passes = np_;
+  if (total_steps) *total_steps = steps;
+  if (threshold) *threshold = d <= 2 ? 0.0 : 0.1;
+  return 0;
+}
+
+int emeans_ref_assign(const float* X, int64_t n, int32_t d, const float* C, int32_t k,
+                      int32_t* labels, float* dists) {
+  if (n < 0 || d < 1 || k < 1 || !X || !C || !labels) return -1;
+  double* d1 = (double*)malloc(sizeof(double) * (size_t)(n > 0 ? n : 1));
+  ref_assign(X, 0, n, NULL, d, C, k, labels, d1, NULL, 0);
+  if (dists)
+    for (int64_t i = 0; i < n; ++i) dists[i] = (float)d1[i];
+  free(d1);
+  return 0;
+}
+
+/* Revival after step t (the Python oracle's _revive, euclidean mode). */
+static int64_t ref_revive(int64_t t, uint64_t seed, double thr, int32_t k, int32_t d, float* N,
+                          float* S, float* C) {
+  double total = 0.0;
+  for (int32_t j = 0; j < k; ++j) total += (double)N[j];
+  const double th = thr * (total / (double)k);
+  unsigned char* live = (unsigned char*)malloc((size_t)k);
+  double* cum = (double*)malloc(sizeof(double) * (size_t)k);
+  int32_t last_live = -1;
+  for (int32_t j = 0; j < k; ++j) {
+    live[j] = !((double)N[j] < th);
+    if (live[j]) last_live = j;
+  }
+  int64_t splits = 0;
+  const float eps = (float)ldexp(1.0, -10);
+  for (int32_t j = 0; j < k; ++j) {
+    if (live[j]) continue;
+    /* u from Philox stream 3: 53 random bits in [0, 1) */
+    const uint64_t ctr[4] = {(uint64_t)j, (uint64_t)t, 0, 3}, key[2] = {seed, 0};
+    uint64_t w[4];
+    ref_philox4x64(ctr, key, w);
+    const double u = (double)(w[0] >> 11) * ldexp(1.0, -53);
+    double run = 0.0;
+    for (int32_t q = 0; q < k; ++q) {
+      run += live[q] ? (double)N[q] : 0.0;
+      cum[q] = run;
+    }
+    const double target = u * cum[k - 1];
+    int32_t i = k;
+    for (int32_t q = 0; q < k; ++q)
+      if (cum[q] > target) {
+        i = q;
+        break;
+      }
+    if (i >= k || !live[i]) i = last_live;
+    const float* si = S + (int64_t)i * d;
+    float* sj = S + (int64_t)j * d;
+    float* sim = S + (int64_t)i * d;
+    N[i] = N[i] * 0.5f;
+    N[j] = N[i];
+    for (int32_t e = 0; e < d; ++e) {
+      /* sign of coordinate e: bit e % 64 of word (e / 64) % 4 of the Philox
+         stream-4 block with counter word 2 = e / 256; a set bit means -1 */
+      const uint64_t c4[4] = {(uint64_t)j, (uint64_t)t, (uint64_t)(e / 256), 4};
+      uint64_t sw[4];
+      ref_philox4x64(c4, key, sw);
+      const float sg = ((sw[(e / 64) % 4] >> (e % 64)) & 1ULL) ? -1.0f : 1.0f;
+      const float half = si[e] * 0.5f;
+      const float pe = eps * sg;
+      sj[e] = half * (1.0f + pe);
+      sim[e] = half * (1.0f - pe);
+    }
+    for (int32_t e = 0; e < d; ++e) {
+      C[(int64_t)i * d + e] = (float)((double)S[(int64_t)i * d + e] / (double)N[i]);
+      C[(int64_t)j * d + e] = (float)((double)S[(int64_t)j * d + e] / (double)N[j]);
+    }
+    ++splits;
+  }
+  free(cum);
+  free(live);
+  return splits;
+}
+
+int emeans_ref_train(const float* X, int64_t n, int32_t d, int32_t k, double T, uint64_t seed,
+                     float* centroids, int32_t* labels, int64_t* n_splits) {
+  int64_t B, S_tot;
+  double a0, thr;
+  int32_t npass;
+  if (!X || !centroids || emeans_ref_recipe(n, d, k, T, &B, &a0, &npass, &S_tot, &thr)) return -1;
+  const size_t kd = (size_t)k * (size_t)d;
+  float* C = centroids;
+  float* N = (float*)calloc((size_t)k, sizeof(float));
+  float* S = (float*)calloc(kd, sizeof(float));
+  int64_t* LN = (int64_t*)calloc((size_t)k, sizeof(int64_t));
+  double* LS = (double*)calloc(kd, sizeof(double));
+  int64_t* counts = (int64_t*)malloc(sizeof(int64_t) * (size_t)k);
+  double* sums = (double*)malloc(sizeof(double) * kd);
+  int64_t* rows = (int64_t*)malloc(sizeof(int64_t) * (size_t)B);
+  int32_t* lab = (int32_t*)malloc(sizeof(int32_t) * (size_t)B);
+  double* d1 = (double*)malloc(sizeof(double) * (size_t)B);
+  /* starting centroids: the first k entries of the init order (stream 1) */
+  int64_t* init = (int64_t*)malloc(sizeof(int64_t) * (size_t)k);
+  ref_perm_range((uint64_t)n, seed, 1, 0, 0, (uint64_t)k, init);
+  for (int32_t j = 0; j < k; ++j) memcpy(C + (size_t)j * d, X + (size_t)init[j] * d, sizeof(float) * d);
+  free(init);
+  if (labels)
+    for (int64_t r = 0; r < n; ++r) labels[r] = -1;
+  const int full = (int)floor(T);
+  int64_t t = 0, splits = 0;
+  for (int32_t e = 0; e < npass; ++e) {
+    const int64_t rows_e = e < full ? n : (int64_t)floor((T - full) * (double)n);
+    const int last = e == npass - 1;
+    for (int64_t s0 = 0; s0 < rows_e; s0 += B) {
+      const int64_t Bt = rows_e - s0 < B ? rows_e - s0 : B;
+      ref_perm_range((uint64_t)n, seed, 2, (uint64_t)e, (uint64_t)s0, (uint64_t)Bt, rows);
+      ref_assign(X, 0, Bt, rows, d, C, k, lab, d1, NULL, 0);
+      ref_group(X, 0, Bt, rows, lab, d, k, sums, counts);
+      /* cosine step: alpha0 (0.1 + 0.45 (1 + cos(pi t / (S - 1)))), in fp32 */
+      const float a = S_tot == 1 ? (float)a0
+                                 : (float)(a0 * (0.1 + 0.45 * (1.0 + cos(M_PI * (double)t /
+                                                                          (double)(S_tot - 1)))));
+      const float b = 1.0f - a;
+      for (int32_t j = 0; j < k; ++j) {
+        N[j] = (b * N[j]) + (a * (float)counts[j]);
+        for (int32_t q = 0; q < d; ++q) {
+          const size_t ix = (size_t)j * d + q;
+          S[ix] = (float)((double)b * (double)S[ix] + (double)a * sums[ix]);
+        }
+        if (N[j] > 0.0f)
+          for (int32_t q = 0; q < d; ++q) {
+            const size_t ix = (size_t)j * d + q;
+            C[ix] = (float)((double)S[ix] / (double)N[j]);
+          }
+      }
+      if (last) {
+        for (int32_t j = 0; j < k; ++j) LN[j] += counts[j];
+        for (size_t ix = 0; ix < kd; ++ix) LS[ix] += sums[ix];
+        if (labels)
+          for (int64_t r = 0; r < Bt; ++r) labels[rows[r]] = lab[r];
+      }
+      if (thr > 0.0 && (t + 1) % 5 == 0) splits += ref_revive(t, seed, thr, k, d, N, S, C);
+      ++t;
+    }
+  }
+  /* closing step: the exact mean of each cluster's rows in the last pass */
+  for (int32_t j = 0; j < k; ++j)
+    if (LN[j] > 0)
+      for (int32_t q = 0; q < d; ++q) {
+        const size_t ix = (size_t)j * d + q;
+        C[ix] = (float)(LS[ix] / (double)LN[j]);
+      }
+  if (n_splits) *n_splits = splits;
+  free(d1);
+  free(lab);
+  free(rows);
+  free(sums);
+  free(counts);
+  free(LS);
+  free(LN);
+  free(S);
+  free(N);
+  return 0;
+}
