@@ -614,13 +614,27 @@ __global__ __launch_bounds__(256) void group_wave_kernel(const unsigned char* __
   }
 }
 
-// UB bytes of a row (UB = 4, 8 or 16) as fp32 values: EPV = UB / element size.
-template <int DT, int UB>
-__device__ __forceinline__ void load_span_unit(const unsigned char* p, float* v) {
-  if constexpr (DT == 2 || DT == 3 || DT == 5) {  // 1-byte codes / values
+// UB raw bytes of a row (UB = 4, 8 or 16) into UB / 4 dwords, and their
+// values as fp32 (fp32, bf16, fp16, int8 codes, E4M3 codes or uint8 values).
+// Split so that a batch of row loads is issued before any of them is
+// converted.
+// The rows are read once per step: non-temporal loads, which keep the
+// gathered rows from displacing the rest of L2 (the 4M-row bf16 batches:
+// 255 -> 208 us per grouping launch; the deep- and SIFT-like batches about
+// 1.5% faster).
+template <int UB>
+__device__ __forceinline__ void load_unit_raw(const unsigned char* p, uint32_t* r) {
 #pragma unroll
-    for (int h = 0; h < UB / 4; ++h) {
-      const uint32_t q = reinterpret_cast<const uint32_t*>(p)[h];
+  for (int e = 0; e < UB / 4; ++e)
+    r[e] = __builtin_nontemporal_load(reinterpret_cast<const uint32_t*>(p) + e);
+}
+
+template <int DT, int UB>
+__device__ __forceinline__ void unit_to_f32(const uint32_t* r, float* v) {
+#pragma unroll
+  for (int h = 0; h < UB / 4; ++h) {
+    const uint32_t q = r[h];
+    if constexpr (DT == 2 || DT == 3 || DT == 5) {  // 1-byte codes / values
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const uint32_t b = (q >> (8 * e)) & 0xFFu;
@@ -631,32 +645,14 @@ __device__ __forceinline__ void load_span_unit(const unsigned char* p, float* v)
         else
           v[4 * h + e] = (float)(int8_t)b;
       }
-    }
-  } else if constexpr (DT == 1 || DT == 4) {  // bf16 / fp16
-#pragma unroll
-    for (int h = 0; h < UB / 4; ++h) {
-      const uint32_t q = reinterpret_cast<const uint32_t*>(p)[h];
-      if constexpr (DT == 1) {
-        v[2 * h] = __uint_as_float(q << 16);
-        v[2 * h + 1] = __uint_as_float(q & 0xFFFF0000u);
-      } else {
-        v[2 * h] = f16_to_f32((uint16_t)(q & 0xFFFFu));
-        v[2 * h + 1] = f16_to_f32((uint16_t)(q >> 16));
-      }
-    }
-  } else {  // fp32
-    if constexpr (UB == 16) {
-      typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-      const u32x4 q = *reinterpret_cast<const u32x4*>(p);
-#pragma unroll
-      for (int e = 0; e < 4; ++e) v[e] = __uint_as_float(q[e]);
-    } else if constexpr (UB == 8) {
-      typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
-      const u32x2 q = *reinterpret_cast<const u32x2*>(p);
-      v[0] = __uint_as_float(q[0]);
-      v[1] = __uint_as_float(q[1]);
-    } else {
-      v[0] = *reinterpret_cast<const float*>(p);
+    } else if constexpr (DT == 1) {  // bf16
+      v[2 * h] = __uint_as_float(q << 16);
+      v[2 * h + 1] = __uint_as_float(q & 0xFFFF0000u);
+    } else if constexpr (DT == 4) {  // fp16
+      v[2 * h] = f16_to_f32((uint16_t)(q & 0xFFFFu));
+      v[2 * h + 1] = f16_to_f32((uint16_t)(q >> 16));
+    } else {  // fp32
+      v[h] = __uint_as_float(q);
     }
   }
 }
@@ -722,17 +718,20 @@ __global__ __launch_bounds__(256) void group_span_kernel(const unsigned char* __
       const int m = min(64, end - t);
       const int ord = lane < m ? (int)order[t + lane] : 0;
       for (int u = 0; u < m; u += U) {
-        float v[U][EPV];
+        uint32_t raw[U][UB / 4];
 #pragma unroll
         for (int q = 0; q < U; ++q) {  // slots past m re-read the last row (not added)
           const uint32_t row = (uint32_t)__builtin_amdgcn_readlane(ord, min(u + q, m - 1));
-          load_span_unit<DT, UB>(xcol + (size_t)row * rowbytes, v[q]);
+          load_unit_raw<UB>(xcol + (size_t)row * rowbytes, raw[q]);
         }
 #pragma unroll
         for (int q = 0; q < U; ++q)
-          if (u + q < m)
+          if (u + q < m) {
+            float v[EPV];
+            unit_to_f32<DT, UB>(raw[q], v);
 #pragma unroll
-            for (int e = 0; e < EPV; ++e) acc[e] += v[q][e];
+            for (int e = 0; e < EPV; ++e) acc[e] += v[e];
+          }
       }
     }
   };
@@ -777,17 +776,19 @@ __global__ __launch_bounds__(256) void group_span_kernel(const unsigned char* __
     const int m = min(64, S1 - t);
     const int ord = lane < m ? (int)order[t + lane] : 0;
     for (int u = 0; u < m; u += U) {
-      float v[U][EPV];
+      uint32_t raw[U][UB / 4];
 #pragma unroll
       for (int q = 0; q < U; ++q) {  // slots past m re-read the last row (not added)
         const uint32_t row = (uint32_t)__builtin_amdgcn_readlane(ord, min(u + q, m - 1));
-        load_span_unit<DT, UB>(xcol + (size_t)row * rowbytes, v[q]);
+        load_unit_raw<UB>(xcol + (size_t)row * rowbytes, raw[q]);
       }
 #pragma unroll
       for (int q = 0; q < U; ++q) {
         if (u + q < m) {
+          float v[EPV];
+          unit_to_f32<DT, UB>(raw[q], v);
 #pragma unroll
-          for (int e = 0; e < EPV; ++e) acc[e] += v[q][e];
+          for (int e = 0; e < EPV; ++e) acc[e] += v[e];
           const int slot = t + u + q;
           if (slot + 1 == bnd) {  // last row of cluster jc: store, move to the next with rows
             if (active) {
@@ -805,46 +806,6 @@ __global__ __launch_bounds__(256) void group_span_kernel(const unsigned char* __
           }
         }
       }
-    }
-  }
-}
-
-// UB raw bytes of a row (UB = 4, 8 or 16) into UB / 4 dwords, and their
-// values as fp32 (the element types of load_span_unit). Split so that a batch
-// of row loads is issued before any of them is converted.
-// The rows are read once per step: non-temporal loads (slightly faster than
-// plain ones on the deep- and SIFT-like batches).
-template <int UB>
-__device__ __forceinline__ void load_unit_raw(const unsigned char* p, uint32_t* r) {
-#pragma unroll
-  for (int e = 0; e < UB / 4; ++e)
-    r[e] = __builtin_nontemporal_load(reinterpret_cast<const uint32_t*>(p) + e);
-}
-
-template <int DT, int UB>
-__device__ __forceinline__ void unit_to_f32(const uint32_t* r, float* v) {
-#pragma unroll
-  for (int h = 0; h < UB / 4; ++h) {
-    const uint32_t q = r[h];
-    if constexpr (DT == 2 || DT == 3 || DT == 5) {  // 1-byte codes / values
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const uint32_t b = (q >> (8 * e)) & 0xFFu;
-        if constexpr (DT == 3)
-          v[4 * h + e] = e4m3_to_f32(b);
-        else if constexpr (DT == 5)
-          v[4 * h + e] = (float)b;
-        else
-          v[4 * h + e] = (float)(int8_t)b;
-      }
-    } else if constexpr (DT == 1) {  // bf16
-      v[2 * h] = __uint_as_float(q << 16);
-      v[2 * h + 1] = __uint_as_float(q & 0xFFFF0000u);
-    } else if constexpr (DT == 4) {  // fp16
-      v[2 * h] = f16_to_f32((uint16_t)(q & 0xFFFFu));
-      v[2 * h + 1] = f16_to_f32((uint16_t)(q >> 16));
-    } else {  // fp32
-      v[h] = __uint_as_float(q);
     }
   }
 }
